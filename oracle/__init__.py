@@ -1,0 +1,15 @@
+"""fp64 CPU oracle for the GlowQ group-shared low-rank correction path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import or run anything in this package.  It shares
+no code with the HIP library (``rank_error_compensation_amd``), which never imports it.
+
+  glowq_ref : inference definitions (dequantisation, group / solo / layerwise forward,
+              the layer path with the restore mask, brute-force loops)
+  solve     : the offline factor solve and restore scores, used to build exact factors
+              for the tiny workload and to pin the inference oracle end to end
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against closed forms, exact
+arithmetic, brute force or special cases; none is marked "parity unpinned".
+"""
+from . import glowq_ref, solve  # noqa: F401

@@ -1,0 +1,423 @@
+"""Checks that pin the fp64 oracle to facts outside itself: exact rational arithmetic,
+hand-worked fixtures, closed forms (Eckart-Young-Mirsky), special cases that reduce to a
+textbook SVD, brute-force loops and invariants.
+
+Each check takes the oracle as a namespace (``ref`` for the inference definitions,
+``sol`` for the factor solve) so that ``test_oracle_mutations.py`` can hand it a copy
+with a planted mistake and confirm that some check fails.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+from fractions import Fraction
+from types import SimpleNamespace
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def oracle_namespaces():
+    from oracle import glowq_ref, solve
+    ref = SimpleNamespace(**{k: getattr(glowq_ref, k) for k in dir(glowq_ref) if not k.startswith("__")})
+    sol = SimpleNamespace(**{k: getattr(solve, k) for k in dir(solve) if not k.startswith("__")})
+    return ref, sol
+
+
+# ------------------------------------------------------------------ helpers (test side)
+def pack_words(q: np.ndarray) -> np.ndarray:
+    """uint values [O][K] -> int32 words, input 8w+j in bits 4j..4j+3 (python ints)."""
+    O, K = q.shape
+    out = np.zeros((O, K // 8), dtype=np.int64)
+    for o in range(O):
+        for w in range(K // 8):
+            v = 0
+            for j in range(8):
+                v |= int(q[o, 8 * w + j]) << (4 * j)
+            out[o, w] = v - (1 << 32) if v >= (1 << 31) else v
+    return out.astype(np.int32)
+
+
+def fp16_from_bits(h: int) -> np.float16:
+    return np.array([h], dtype=np.uint16).view(np.float16)[0]
+
+
+# ------------------------------------------------------------------ P1: dequantisation
+S_SWEEP_BITS = [0x0001, 0x0003, 0x0200, 0x0400, 0x1F60, 0x2E66, 0x3800, 0x3C00, 0x3E00,
+                0x4248, 0x63D0, 0x7800, 0x7BFF]
+
+
+def check_dequant_exhaustive(ref):
+    """Every q in 0..15, every z in -16..31 and a sweep of fp16 scales (subnormal, min
+    normal, 1, max): the oracle's fp64 value equals the exact rational (q - z) * s and is
+    exactly representable in fp32."""
+    zs = list(range(-16, 32))
+    rows = [(z, sb) for z in zs for sb in S_SWEEP_BITS]
+    O, K = len(rows), 256
+    q = np.zeros((O, K), dtype=np.int64)
+    s = np.zeros((O, 2), dtype=np.float16)
+    z = np.zeros((O, 2), dtype=np.float16)
+    for o, (zz, sb) in enumerate(rows):
+        for k in range(K):
+            q[o, k] = (k + o) % 16
+        s[o, 0] = fp16_from_bits(sb)
+        s[o, 1] = fp16_from_bits(S_SWEEP_BITS[(S_SWEEP_BITS.index(sb) + 5) % len(S_SWEEP_BITS)])
+        z[o, 0] = zz
+        z[o, 1] = -zz + 7
+    words = pack_words(q)
+    W = ref.dequant(words, s, z, O, K)
+    assert W.shape == (O, K) and W.dtype == np.float64
+    for o in range(O):
+        for k in range(K):
+            g = k // 128
+            exact = (Fraction(int(q[o, k])) - Fraction(float(z[o, g]))) * Fraction(float(s[o, g]))
+            assert Fraction(float(W[o, k])) == exact, (o, k)
+            assert float(np.float32(W[o, k])) == float(W[o, k]), (o, k)
+
+
+def check_dequant_golden(ref):
+    """Hand-worked rows of the canonical format (tests/golden/dequant_nibbles.txt)."""
+    rows, expects = {}, {}
+    with open(os.path.join(GOLDEN, "dequant_nibbles.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            tok = line.split()
+            if tok[0] == "row":
+                r = int(tok[1])
+                sb = int(tok[2].split("=")[1], 16)
+                zz = int(tok[3].split("=")[1])
+                words = [int(tok[4].split("=")[1], 16)] + [int(t, 16) for t in tok[5:]]
+                rows[r] = (sb, zz, words)
+            elif tok[0] == "expect":
+                r = int(tok[1])
+                expects[r] = [(int(p.split(":")[0]), float(p.split(":")[1])) for p in tok[2:]]
+    assert rows and set(rows) == set(expects)
+    for r, (sb, zz, words) in rows.items():
+        w = np.array([[v - (1 << 32) if v >= (1 << 31) else v for v in words]], dtype=np.int64).astype(np.int32)
+        s = np.array([[fp16_from_bits(sb)]], dtype=np.float16)
+        z = np.array([[zz]], dtype=np.float16)
+        W = ref.dequant(w, s, z, 1, 128)
+        listed = dict(expects[r])
+        for k in range(128):
+            want = listed.get(k, (0 - zz) * float(s[0, 0]))
+            assert float(W[0, k]) == want, (r, k, float(W[0, k]), want)
+
+
+# ------------------------------------------------------------------ tiny random problem
+def tiny_problem(seed=0, T=3, d=256, n_outs=(24, 40, 16), r=5, z_range=(0, 16)):
+    rng = np.random.default_rng(seed)
+    G = d // 128
+    qs, ss, zs, words = [], [], [], []
+    for O in n_outs:
+        q = rng.integers(0, 16, size=(O, d))
+        s = (rng.uniform(0.002, 0.05, size=(O, G))).astype(np.float16)
+        z = rng.integers(z_range[0], z_range[1], size=(O, G)).astype(np.float16)
+        qs.append(q)
+        ss.append(s)
+        zs.append(z)
+        words.append(pack_words(q))
+    x = rng.standard_normal((T, d)).astype(np.float16)
+    b = (rng.standard_normal((r, d)) / math.sqrt(d)).astype(np.float16)
+    a = [(rng.standard_normal((O, r)) * 0.05).astype(np.float16) for O in n_outs]
+    return SimpleNamespace(x=x, b=b, a=a, q=qs, s=ss, z=zs, words=words, n_outs=list(n_outs), d=d,
+                           T=T, r=r)
+
+
+def _w_hats(ref, p):
+    return [ref.dequant(w, s, z, O, p.d) for w, s, z, O in zip(p.words, p.s, p.z, p.n_outs)]
+
+
+# ------------------------------------------------------------------ P3: restore off / r = 0
+def check_restore_off(ref):
+    p = tiny_problem(1)
+    wh = _w_hats(ref, p)
+    bf = ref.bruteforce_group(p.x, p.words, p.s, p.z, p.n_outs, p.d, None, p.a, restore=False)
+    for restore, b in ((False, p.b), (True, None), (True, p.b[:0])):
+        ys = ref.group_forward(p.x, wh, b, p.a, restore=restore)
+        for y, w, yb in zip(ys, wh, bf):
+            base = p.x.astype(np.float64) @ w.T
+            assert np.array_equal(y, base)
+            assert np.max(np.abs(y - yb)) <= 1e-15 * max(1.0, np.max(np.abs(yb)))
+
+
+# ------------------------------------------------------------------ P4: associativity
+def check_associativity_small_int(ref):
+    """Small integers make every product and sum exact in fp64, so
+    X W_hat^T + (X B^T) A^T must equal X (W_hat + A B)^T bit for bit; unequal
+    dimensions expose a transposed operand, a wrong sign or a dropped term."""
+    rng = np.random.default_rng(7)
+    T, d, r = 5, 256, 3
+    n_outs = [16, 32]
+    words, ss, zs, qs = [], [], [], []
+    for O in n_outs:
+        q = rng.integers(0, 16, size=(O, d))
+        qs.append(q)
+        words.append(pack_words(q))
+        ss.append(np.ones((O, 2), dtype=np.float16))
+        zs.append(rng.integers(0, 16, size=(O, 2)).astype(np.float16))
+    x = rng.integers(-3, 4, size=(T, d)).astype(np.float16)
+    b = rng.integers(-2, 3, size=(r, d)).astype(np.float16)
+    a = [rng.integers(-2, 3, size=(O, r)).astype(np.float16) for O in n_outs]
+    wh = [ref.dequant(w, s, z, O, d) for w, s, z, O in zip(words, ss, zs, n_outs)]
+    ys = ref.group_forward(x, wh, b, a, restore=True)
+    for i, O in enumerate(n_outs):
+        g = np.arange(d) // 128
+        w_int = qs[i] - zs[i].astype(np.int64)[:, g]
+        merged = w_int + a[i].astype(np.int64) @ b.astype(np.int64)
+        want = x.astype(np.int64) @ merged.T
+        assert ys[i].shape == (T, O)
+        assert np.array_equal(ys[i], want.astype(np.float64)), i
+    # solo = group of one with its private B; layerwise = one solo per module
+    ysolo = ref.solo_forward(x, wh[1], b, a[1], restore=True)
+    assert np.array_equal(ysolo, ys[1])
+    ylw = ref.layerwise_forward(x, wh, [b, b], a, restore=True)
+    for u, v in zip(ylw, ys):
+        assert np.array_equal(u, v)
+
+
+# ------------------------------------------------------------------ P11: brute force
+def check_bruteforce(ref):
+    for seed, kw in ((2, {}), (3, dict(T=2, d=128, n_outs=(8,), r=2, z_range=(-5, 20)))):
+        p = tiny_problem(seed, **kw)
+        wh = _w_hats(ref, p)
+        ys = ref.group_forward(p.x, wh, p.b, p.a, restore=True)
+        bf = ref.bruteforce_group(p.x, p.words, p.s, p.z, p.n_outs, p.d, p.b, p.a, restore=True)
+        for y, yb in zip(ys, bf):
+            scale = float(np.max(np.abs(yb)))
+            assert np.max(np.abs(y - yb)) <= 1e-13 * scale, np.max(np.abs(y - yb)) / scale
+
+
+# ------------------------------------------------------------------ P12: row independence
+def check_row_independence(ref):
+    p = tiny_problem(4, T=6)
+    wh = _w_hats(ref, p)
+    y_all = ref.group_forward(p.x, wh, p.b, p.a, restore=True)
+    y_1 = ref.group_forward(p.x[:2], wh, p.b, p.a, restore=True)
+    y_2 = ref.group_forward(p.x[2:], wh, p.b, p.a, restore=True)
+    for ya, y1, y2 in zip(y_all, y_1, y_2):
+        scale = float(np.max(np.abs(ya)))
+        assert np.max(np.abs(ya - np.vstack([y1, y2]))) <= 1e-14 * scale
+
+
+# ------------------------------------------------------------------ mask path
+def check_path_mask(ref):
+    """A layer outside the restore set returns the quantised product alone; a restored
+    layer gets the correction; units run in the stated order."""
+    units = {}
+    for l in range(3):
+        us = []
+        for u, n_outs in enumerate(((24, 16, 16), (32,))):
+            p = tiny_problem(10 + 3 * l + u, n_outs=n_outs)
+            us.append(SimpleNamespace(x=p.x, b=p.b, a=p.a, weights=[
+                SimpleNamespace(q_packed=w, s=s, z=z, n_out=O, k_in=p.d)
+                for w, s, z, O in zip(p.words, p.s, p.z, p.n_outs)], p=p))
+        units[l] = us
+    mask = [True, False, True]
+    out = ref.path_forward(units, mask)
+    for l, us in units.items():
+        for ui, u in enumerate(us):
+            wh = _w_hats(ref, u.p)
+            for i, w in enumerate(wh):
+                base = u.x.astype(np.float64) @ w.T
+                y = out[l][ui][i]
+                if mask[l]:
+                    corr = (u.x.astype(np.float64) @ u.b.astype(np.float64).T) @ u.a[i].astype(np.float64).T
+                    assert np.max(np.abs(y - base - corr)) <= 1e-14 * np.max(np.abs(y))
+                    assert np.max(np.abs(corr)) > 0
+                else:
+                    assert np.array_equal(y, base)
+
+
+# ------------------------------------------------------------------ solver pins
+def _cov(d, alpha, seed, n_zero=0):
+    rng = np.random.default_rng(seed)
+    Q, R = np.linalg.qr(rng.standard_normal((d, d)))
+    Q = Q * np.sign(np.diag(R))
+    lam = np.arange(1, d + 1, dtype=np.float64) ** (-alpha)
+    lam *= d / lam.sum()
+    if n_zero:
+        lam[-n_zero:] = 0.0
+    return Q, lam
+
+
+def check_exact_rank(ref, sol, singular=False):
+    """E_cat exactly rank r, W_i = W_hat_i + E_i: the covariance-aligned shared factors make
+    the inference output reproduce X W_i^T to 1e-10 (full-rank or singular Sigma_x)."""
+    rng = np.random.default_rng(11 + singular)
+    d, r, T = 128, 6, 7
+    n_outs = [40, 24, 16]
+    m = sum(n_outs)
+    Q, lam = _cov(d, 1.19, 5, n_zero=20 if singular else 0)
+    U0, _ = np.linalg.qr(rng.standard_normal((m, r)))
+    V0, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    if singular:  # restrict E to range(Sigma_x)
+        P = (Q[:, :d - 20]) @ Q[:, :d - 20].T
+        V0, _ = np.linalg.qr(P @ V0)
+    sig = np.linspace(2.0, 0.3, r)
+    E_cat = (U0 * sig) @ V0.T
+    E_list = sol.split_rows(E_cat, n_outs)
+    S_half = sol.sqrt_psd(Q, lam)
+    S_lift = sol.pinv_sqrt_psd(Q, lam)
+    A_list, B, _ = sol.whitened_factors(E_list, S_half, S_lift, r)
+    p = tiny_problem(21, T=T, d=d, n_outs=tuple(n_outs), r=r)
+    wh = _w_hats(ref, p)
+    Z = rng.standard_normal((T, d))
+    X = (Z * np.sqrt(lam)) @ Q.T  # rows in range(Sigma_x)
+    ys = ref.group_forward(X, wh, B, A_list, restore=True)
+    for y, w, E in zip(ys, wh, E_list):
+        want = X @ (w + E).T
+        assert np.linalg.norm(y - want) <= 1e-10 * np.linalg.norm(want)
+    # the QR-reduced core route gives the same product
+    A2, B2 = sol.core_factors(E_list, S_half, S_lift, r)
+    AB1 = np.vstack(A_list) @ B
+    AB2 = np.vstack(A2) @ B2
+    assert np.linalg.norm(AB1 - AB2) <= 1e-10 * np.linalg.norm(AB1)
+
+
+def check_eckart_young(sol):
+    """Whitened residual of the shared factors equals sum_{j>r} sigma_j^2 of the whitened
+    error (closed form), and no other rank-r pair tried does better."""
+    rng = np.random.default_rng(31)
+    d, r = 96, 5
+    n_outs = [30, 20, 50]
+    E_list = [rng.standard_normal((O, d)) * (1 + 0.3 * i) for i, O in enumerate(n_outs)]
+    Q, lam = _cov(d, 0.77, 6)
+    S_half = sol.sqrt_psd(Q, lam)
+    S_lift = sol.pinv_sqrt_psd(Q, lam)
+    A_list, B, S = sol.whitened_factors(E_list, S_half, S_lift, r)
+    E_cat = np.vstack(E_list)
+    resid = np.linalg.norm((E_cat - np.vstack(A_list) @ B) @ S_half) ** 2
+    s_ref = np.linalg.svd(E_cat @ S_half, compute_uv=False)
+    closed = float(np.sum(s_ref[r:] ** 2))
+    assert abs(resid - closed) <= 1e-12 * closed
+    for t in range(20):
+        A_alt = np.vstack(A_list) + 0.05 * rng.standard_normal((sum(n_outs), r))
+        B_alt = B + 0.05 * rng.standard_normal(B.shape)
+        alt = np.linalg.norm((E_cat - A_alt @ B_alt) @ S_half) ** 2
+        assert alt >= resid * (1 - 1e-12)
+    # per-module right factors add nothing: the best per-module fit with the shared row
+    # space B is what the shared solve already gives (A_i = E_i S B^T (B S B^T)^-1 ...)
+    Bw = B @ S_half  # whitened shared basis
+    for Ei, Ai in zip(E_list, A_list):
+        Ai_ls = (Ei @ S_half) @ np.linalg.pinv(Bw)
+        assert np.linalg.norm(Ai_ls - Ai) <= 1e-9 * np.linalg.norm(Ai)
+
+
+def check_isotropic(sol):
+    """Sigma_x = c I: the covariance-aligned product equals the plain stacked-SVD product."""
+    rng = np.random.default_rng(41)
+    d, r = 64, 4
+    E_list = [rng.standard_normal((O, d)) for O in (20, 30)]
+    c = 2.5
+    S_half = np.sqrt(c) * np.eye(d)
+    S_lift = np.eye(d) / np.sqrt(c)
+    A_list, B, _ = sol.whitened_factors(E_list, S_half, S_lift, r)
+    E_cat = np.vstack(E_list)
+    U, S, Vt = np.linalg.svd(E_cat, full_matrices=False)
+    plain = (U[:, :r] * S[:r]) @ Vt[:r]
+    got = np.vstack(A_list) @ B
+    assert np.linalg.norm(got - plain) <= 1e-12 * np.linalg.norm(plain)
+
+
+def check_usage_weighted_risk(sol):
+    """E||M x||^2 = tr(M Sigma M^T) = ||M Sigma^{1/2}||_F^2, algebraically and by Monte Carlo."""
+    rng = np.random.default_rng(51)
+    d, o = 32, 12
+    Q, lam = _cov(d, 1.19, 8)
+    Sigma = (Q * lam) @ Q.T
+    S_half = sol.sqrt_psd(Q, lam)
+    assert np.linalg.norm(S_half @ S_half - Sigma) <= 1e-12 * np.linalg.norm(Sigma)
+    M = rng.standard_normal((o, d))
+    lhs = float(np.trace(M @ Sigma @ M.T))
+    rhs = float(np.linalg.norm(M @ S_half) ** 2)
+    assert abs(lhs - rhs) <= 1e-12 * lhs
+    n = 200000
+    X = (rng.standard_normal((n, d)) * np.sqrt(lam)) @ Q.T
+    v = np.sum((X @ M.T) ** 2, axis=1)
+    mc, se = float(v.mean()), float(v.std() / math.sqrt(n))
+    assert abs(mc - lhs) <= 4 * se
+
+
+def check_qr_core(sol):
+    """sigma(R_e Sigma^{1/2}) = sigma(E_cat Sigma^{1/2}) (left-orthogonal invariance)."""
+    rng = np.random.default_rng(61)
+    d = 48
+    E_cat = rng.standard_normal((150, d))
+    Q, lam = _cov(d, 1.19, 9)
+    S_half = sol.sqrt_psd(Q, lam)
+    Qe, M = sol.qr_core(E_cat, S_half)
+    assert M.shape == (d, d)
+    assert np.linalg.norm(Qe.T @ Qe - np.eye(d)) <= 1e-12 * d
+    s1 = np.linalg.svd(M, compute_uv=False)
+    s2 = np.linalg.svd(E_cat @ S_half, compute_uv=False)
+    assert np.max(np.abs(s1 - s2)) <= 1e-12 * s2[0]
+
+
+def check_cholesky_vs_symmetric(sol):
+    """The lifted product A B does not depend on which square root of Sigma_x is used."""
+    rng = np.random.default_rng(71)
+    d, r = 64, 6
+    E_list = [rng.standard_normal((O, d)) for O in (30, 34)]
+    Q, lam = _cov(d, 0.77, 10)
+    Sigma = (Q * lam) @ Q.T
+    L = np.linalg.cholesky(Sigma)
+    A1, B1, _ = sol.whitened_factors(E_list, sol.sqrt_psd(Q, lam), sol.pinv_sqrt_psd(Q, lam), r)
+    A2, B2, _ = sol.whitened_factors(E_list, L, np.linalg.inv(L), r)
+    P1 = np.vstack(A1) @ B1
+    P2 = np.vstack(A2) @ B2
+    assert np.linalg.norm(P1 - P2) <= 1e-10 * np.linalg.norm(P1)
+
+
+def check_randomized_svd(sol):
+    """Randomized SVD: exact on an exactly rank-r core with p = q = 0; with oversampling and
+    power iterations it reaches the exact top-r subspace of a decaying spectrum."""
+    rng = np.random.default_rng(81)
+    d, r = 80, 6
+    U0, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    V0, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    M = (U0 * np.linspace(3, 1, r)) @ V0.T
+    U, S, Vt = sol.randomized_svd(M, r, 0, 0, np.random.default_rng(1))
+    P = (U[:, :r] * S[:r]) @ Vt[:r]
+    assert np.linalg.norm(P - M) <= 1e-12 * np.linalg.norm(M)
+    sv = 1.0 / np.arange(1, d + 1) ** 1.5
+    Ua, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    Va, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    M2 = (Ua * sv) @ Va.T
+    U, S, Vt = sol.randomized_svd(M2, r, 10, 3, np.random.default_rng(2))
+    assert np.max(np.abs(S[:r] - sv[:r]) / sv[:r]) <= 1e-6
+    best = np.sqrt(np.sum(sv[r:] ** 2))
+    got = np.linalg.norm(M2 - (U[:, :r] * S[:r]) @ Vt[:r])
+    assert got <= best * (1 + 1e-6)
+
+
+def check_scores(sol):
+    """g_ec is 1 for a core of rank <= r and the captured fraction otherwise; g_ner is the
+    error-to-weight energy ratio; top-k matches exhaustive search with index tie-break."""
+    rng = np.random.default_rng(91)
+    M = (rng.standard_normal((20, 3))) @ rng.standard_normal((3, 20))
+    assert abs(sol.g_ec(M, 3) - 1.0) <= 1e-12
+    D = np.diag([4.0, 3.0, 2.0, 1.0])
+    assert abs(sol.g_ec(D, 2) - (16 + 9) / 30.0) <= 1e-15
+    W = np.full((3, 4), 2.0)
+    E = np.full((3, 4), 0.5)
+    assert abs(sol.g_ner(E, W) - 0.0625) <= 1e-15
+    scores = [0.3, 0.9, 0.3, 0.1, 0.9, 0.5]
+    for k in range(len(scores) + 1):
+        best = None
+        for comb in itertools.combinations(range(len(scores)), k):
+            key = (sum(scores[i] for i in comb), [-i for i in sorted(comb)])
+            if best is None or key > best[0]:
+                best = (key, comb)
+        want = [u in best[1] for u in range(len(scores))]
+        assert sol.topk_restore(scores, k) == want, k
+
+
+ALL_REF_CHECKS = [check_dequant_exhaustive, check_dequant_golden, check_restore_off,
+                  check_associativity_small_int, check_bruteforce, check_row_independence,
+                  check_path_mask]
+ALL_SOL_CHECKS = [check_eckart_young, check_isotropic, check_usage_weighted_risk, check_qr_core,
+                  check_cholesky_vs_symmetric, check_randomized_svd, check_scores]

@@ -1,0 +1,323 @@
+"""Seeded synthetic workloads for the GlowQ group-shared low-rank correction path.
+
+This module draws every random input that both the fp64 oracle (``oracle/``) and the
+HIP library consume: activations X with a power-law covariance spectrum, fp16 weights
+with outlier input columns, the round-to-nearest INT4-g128 base quantisation of those
+weights (packed in the library's canonical nibble format), seeded Gaussian low-rank
+factors rescaled to the size of the quantisation error, and the GlowQ-S restore mask.
+
+It holds none of the correction method's arithmetic: no shared projection, no
+correction epilogue and no factor solve (the whitened SVD that yields exact factors
+lives in the oracle).  The base quantiser here is the W4A16 "INT4, g128" weight format
+that the correction is applied on top of (GlowQ paper note, "Experimental setup";
+GlowQ arXiv page, Table 1 header "INT4, g128"); its rounding rules are the workload
+recipe and are listed in the design doc.
+
+All functions take a ``device`` so that large workloads can be drawn directly on the
+GPU (random streams then differ from the CPU ones; both sides of a parity test always
+read the same tensors).
+"""
+from __future__ import annotations
+
+import functools
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+GROUP = 128  # inputs per quantisation group (INT4 "g128")
+
+# stable integer codes for seed keys
+KIND = {"x": 1, "w": 2, "outlier": 3, "a": 4, "b": 5, "basis": 6, "mask": 7, "z": 8}
+
+
+def seed_of(*keys: int) -> int:
+    """64-bit seed from a tuple of non-negative integer keys (numpy SeedSequence)."""
+    ss = np.random.SeedSequence([int(k) for k in keys])
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def generator(device, *keys: int) -> torch.Generator:
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(seed_of(*keys))
+    return g
+
+
+# ----------------------------------------------------------------------------------
+# activations: rows ~ N(0, Sigma_x), Sigma_x = Q diag(lam) Q^T, lam_k ∝ k^-alpha
+# (GlowQ paper note, key design 2: input covariance spectra decay as a power law with
+#  exponent about 0.77 for MLP inputs and 1.19 for QKV inputs; GlowQ arXiv page, Fig. 2)
+# ----------------------------------------------------------------------------------
+def powerlaw_spectrum(d: int, alpha: float) -> torch.Tensor:
+    """lam_k = k^-alpha for k = 1..d, rescaled so that sum(lam) = d (fp64, CPU)."""
+    k = torch.arange(1, d + 1, dtype=torch.float64)
+    lam = k.pow(-alpha)
+    return lam * (d / lam.sum())
+
+
+@functools.lru_cache(maxsize=8)
+def _haar_basis_cpu(d: int, seed: int, dtype_name: str) -> torch.Tensor:
+    dtype = getattr(torch, dtype_name)
+    g = torch.Generator().manual_seed(seed)
+    a = torch.randn(d, d, generator=g, dtype=dtype)
+    q, r = torch.linalg.qr(a)
+    sgn = torch.sign(torch.diagonal(r))
+    sgn[sgn == 0] = 1
+    return (q * sgn.unsqueeze(0)).contiguous()
+
+
+def haar_basis(d: int, *keys: int) -> torch.Tensor:
+    """Seeded Haar-random orthogonal d x d matrix (QR of a Gaussian, column signs fixed
+    by sign(diag R)).  fp64 for d <= 4096, fp32 above (only the activation distribution
+    depends on it).  Always built on the CPU and cached per process."""
+    return _haar_basis_cpu(d, seed_of(*keys), "float64" if d <= 4096 else "float32")
+
+
+def make_x(T: int, d: int, alpha: float, keys: Sequence[int], device="cpu",
+           basis: Optional[torch.Tensor] = None, lam: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp16 [T][d]: fp16_RNE(Z diag(sqrt lam) Q^T), Z ~ N(0,1)."""
+    if lam is None:
+        lam = powerlaw_spectrum(d, alpha)
+    if basis is None:
+        basis = haar_basis(d, *keys, KIND["basis"])
+    g = generator(device, *keys, KIND["x"])
+    z = torch.randn(T, d, generator=g, device=device, dtype=torch.float32)
+    dt = basis.dtype
+    zs = z.to(dt) * lam.to(device=device, dtype=dt).sqrt().unsqueeze(0)
+    x = zs @ basis.to(device).t()
+    return x.to(torch.float16).contiguous()
+
+
+# ----------------------------------------------------------------------------------
+# weights: W ~ N(0, 0.02^2), four outlier input columns x10, rounded to fp16
+# ----------------------------------------------------------------------------------
+def outlier_columns(d: int, keys: Sequence[int], n: int = 4) -> torch.Tensor:
+    g = generator("cpu", *keys, KIND["outlier"])
+    return torch.randperm(d, generator=g)[:n].sort().values
+
+
+def make_w(O: int, d: int, keys: Sequence[int], cols: torch.Tensor, device="cpu",
+           std: float = 0.02, outlier_gain: float = 10.0) -> torch.Tensor:
+    g = generator(device, *keys, KIND["w"])
+    w = torch.randn(O, d, generator=g, device=device, dtype=torch.float32) * std
+    if cols.numel():
+        w[:, cols.to(device)] *= outlier_gain
+    return w.to(torch.float16).contiguous()
+
+
+# ----------------------------------------------------------------------------------
+# base quantiser: asymmetric round-to-nearest INT4 per 128-input group
+#   s = fp16_RNE((max - min) / 15), z = RNE(-min / s), q = clip(RNE(w / s) + z, 0, 15)
+# (RNE = round half to even; z from the fp16-rounded s; z is not clamped)
+# ----------------------------------------------------------------------------------
+@dataclass
+class QuantWeight:
+    q: torch.Tensor        # uint8 [O][d], values 0..15
+    s: torch.Tensor        # fp16 [O][d/128]
+    z: torch.Tensor        # fp16 [O][d/128], integer valued
+    q_packed: torch.Tensor  # int32 [O][d/8], canonical nibble packing
+    err_sq: float          # ||W - W_hat||_F^2 (fp64)
+    w_sq: float            # ||W||_F^2 (fp64)
+
+    @property
+    def n_out(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def k_in(self) -> int:
+        return int(self.q.shape[1])
+
+
+def rtn_quantize(w: torch.Tensor) -> QuantWeight:
+    O, d = w.shape
+    assert d % GROUP == 0
+    wg = w.to(torch.float64).reshape(O, d // GROUP, GROUP)
+    mn = wg.amin(dim=2)
+    mx = wg.amax(dim=2)
+    s = ((mx - mn) / 15.0).to(torch.float16).to(torch.float64)
+    degenerate = s == 0
+    s = torch.where(degenerate, torch.ones_like(s), s)
+    z = torch.round(-mn / s)
+    q = torch.clamp(torch.round(wg / s.unsqueeze(2)) + z.unsqueeze(2), 0, 15)
+    w_hat = (q - z.unsqueeze(2)) * s.unsqueeze(2)
+    err_sq = float(((wg - w_hat) ** 2).sum())
+    w_sq = float((wg ** 2).sum())
+    q8 = q.reshape(O, d).to(torch.uint8).contiguous()
+    return QuantWeight(q=q8, s=s.to(torch.float16).contiguous(), z=z.to(torch.float16).contiguous(),
+                       q_packed=pack_canonical(q8), err_sq=err_sq, w_sq=w_sq)
+
+
+def pack_canonical(q: torch.Tensor) -> torch.Tensor:
+    """uint8 [O][d] (0..15) -> int32 [O][d/8]; nibble j (bits 4j..4j+3) of word w holds
+    q[o][8w + j] (low nibble first).  The int32 holds the uint32 bit pattern."""
+    O, d = q.shape
+    assert d % 8 == 0
+    v = q.to(torch.int64).reshape(O, d // 8, 8)
+    shifts = torch.arange(0, 32, 4, device=q.device, dtype=torch.int64)
+    word = (v << shifts).sum(dim=2)  # < 2^32
+    word = torch.where(word >= 2 ** 31, word - 2 ** 32, word)
+    return word.to(torch.int32).contiguous()
+
+
+# ----------------------------------------------------------------------------------
+# seeded Gaussian factors rescaled so that ||A_i B||_F = ||E_i||_F
+# ----------------------------------------------------------------------------------
+def gaussian_factors(n_outs: Sequence[int], d: int, r: int, err_sq: Sequence[float],
+                     keys: Sequence[int], device="cpu", per_module_b: bool = False):
+    """Returns (A list fp16 [O_i][r], B fp16 [r][d]) or, with per_module_b, a list of B_i.
+    B <- B / sqrt(d); A_i <- A_i * ||E_i||_F / ||A_i B||_F (product norm in fp64)."""
+    def draw_b(tag):
+        gb = generator(device, *keys, KIND["b"], tag)
+        return torch.randn(r, d, generator=gb, device=device, dtype=torch.float64) / math.sqrt(d)
+
+    b_shared = draw_b(0)
+    A, Bs = [], []
+    for i, (O, e2) in enumerate(zip(n_outs, err_sq)):
+        b = draw_b(1 + i) if per_module_b else b_shared
+        ga = generator(device, *keys, KIND["a"], i)
+        a = torch.randn(O, r, generator=ga, device=device, dtype=torch.float64)
+        # ||A B||_F^2 = sum((A^T A) * (B B^T))
+        nrm2 = float(((a.t() @ a) * (b @ b.t())).sum())
+        scale = math.sqrt(e2 / nrm2) if nrm2 > 0 else 0.0
+        A.append((a * scale).to(torch.float16).contiguous())
+        Bs.append(b.to(torch.float16).contiguous())
+    if per_module_b:
+        return A, Bs
+    return A, Bs[0]
+
+
+def restore_mask(n_units: int, n_restore: int, keys: Sequence[int]) -> List[bool]:
+    """GlowQ-S restore set drawn from a seeded score: one uniform score per unit, the
+    n_restore highest are restored; equal scores go to the lower index."""
+    g = generator("cpu", *keys, KIND["mask"])
+    score = torch.rand(n_units, generator=g, dtype=torch.float64)
+    order = sorted(range(n_units), key=lambda u: (-float(score[u]), u))
+    chosen = set(order[:n_restore])
+    return [u in chosen for u in range(n_units)]
+
+
+# ----------------------------------------------------------------------------------
+# workload descriptions
+# ----------------------------------------------------------------------------------
+@dataclass
+class Unit:
+    """One call of the path: an input-sharing group (m >= 1 modules with one shared B,
+    module 0 the anchor) or a solo module (m == 1, private B)."""
+    name: str
+    kind: str                 # "group" | "solo"
+    x: torch.Tensor           # fp16 [T][d]
+    weights: List[QuantWeight]
+    a: List[torch.Tensor]     # fp16 [O_i][r]
+    b: torch.Tensor           # fp16 [r][d]
+    r: int
+    restore: bool = True
+    b_layerwise: Optional[List[torch.Tensor]] = None  # per-module B_i for the baseline
+    extra: Dict = field(default_factory=dict)
+
+    @property
+    def T(self) -> int:
+        return int(self.x.shape[0])
+
+    @property
+    def d(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def n_outs(self) -> List[int]:
+        return [w.n_out for w in self.weights]
+
+
+def make_unit(name: str, kind: str, x: torch.Tensor, n_outs: Sequence[int], r: int,
+              keys: Sequence[int], device="cpu", restore: bool = True,
+              layerwise: bool = False, w_override: Optional[List[torch.Tensor]] = None) -> Unit:
+    d = x.shape[1]
+    cols = outlier_columns(d, keys)  # shared by the modules of one group (an input property)
+    weights = []
+    for i, O in enumerate(n_outs):
+        w = w_override[i] if w_override is not None else make_w(O, d, list(keys) + [i], cols, device)
+        weights.append(rtn_quantize(w))
+    a, b = gaussian_factors(n_outs, d, r, [q.err_sq for q in weights], keys, device)
+    b_lw = None
+    if layerwise:
+        _, b_lw = gaussian_factors(n_outs, d, r, [q.err_sq for q in weights], keys, device,
+                                   per_module_b=True)
+    return Unit(name=name, kind=kind, x=x, weights=weights, a=a, b=b, r=r, restore=restore,
+                b_layerwise=b_lw)
+
+
+ALPHA_QKV = 1.19
+ALPHA_MLP = 0.77
+
+
+def config0_inputs(device="cpu"):
+    """Tiny QKV group, d = 256, 3 x 256 outputs, T = 8, r = 16.  Returns the fp16
+    weights before quantisation, the quantised weights, X and the covariance (Q, lam)
+    so that exact whitened factors can be solved by the caller."""
+    keys = (0, 0, 0, 0)
+    d, T = 256, 8
+    lam = powerlaw_spectrum(d, ALPHA_QKV)
+    Q = haar_basis(d, *keys, KIND["basis"])
+    x = make_x(T, d, ALPHA_QKV, keys, device, basis=Q, lam=lam)
+    cols = outlier_columns(d, keys)
+    w16 = [make_w(256, d, list(keys) + [i], cols, device) for i in range(3)]
+    qw = [rtn_quantize(w) for w in w16]
+    return dict(x=x, w16=w16, qw=qw, Q=Q, lam=lam, r=16, d=d, T=T)
+
+
+def config1_unit(T: int, device="cpu", layerwise=False) -> Unit:
+    keys = (0, 1, 0, 0)
+    x = make_x(T, 4096, ALPHA_QKV, keys, device)
+    return make_unit("qkv", "group", x, [4096, 4096, 4096], 64, keys, device, layerwise=layerwise)
+
+
+def config2_unit(T: int = 2048, device="cpu", layerwise=False) -> Unit:
+    keys = (0, 2, 0, 0)
+    x = make_x(T, 4096, ALPHA_MLP, keys, device)
+    return make_unit("gateup", "group", x, [11008, 11008], 64, keys, device, layerwise=layerwise)
+
+
+LLAMA2_7B = dict(d=4096, inter=11008, n_layers=32)
+
+
+def config3_inputs(T: int, device="cpu", layers: Optional[Sequence[int]] = None, r: int = 64,
+                   layerwise=False):
+    """32-layer LLaMA-2-7B linear path.  One activation per input kind, shared by all
+    layers (the layers are not chained).  Returns (units per layer, mask per layer)."""
+    d, inter, L = LLAMA2_7B["d"], LLAMA2_7B["inter"], LLAMA2_7B["n_layers"]
+    x_attn = make_x(T, d, ALPHA_QKV, (0, 3, 100, 0), device)
+    x_o = make_x(T, d, ALPHA_QKV, (0, 3, 101, 0), device)
+    x_mlp = make_x(T, d, ALPHA_MLP, (0, 3, 102, 0), device)
+    x_down = make_x(T, inter, ALPHA_MLP, (0, 3, 103, 0), device)
+    mask = restore_mask(L, 16, (0, 3, 0, 0))
+    layers = range(L) if layers is None else layers
+    out = {}
+    for l in layers:
+        rs = mask[l]
+        out[l] = [
+            make_unit("qkv", "group", x_attn, [d, d, d], r, (0, 3, l, 0), device, rs, layerwise),
+            make_unit("o_proj", "solo", x_o, [d], r, (0, 3, l, 1), device, rs, layerwise),
+            make_unit("gateup", "group", x_mlp, [inter, inter], r, (0, 3, l, 2), device, rs, layerwise),
+            make_unit("down_proj", "solo", x_down, [d], r, (0, 3, l, 3), device, rs, layerwise),
+        ]
+    return out, mask
+
+
+def config4_units(T: int, r: int, device="cpu", layerwise=False, which=("qkv", "gateup", "down")):
+    """LLaMA-3.1-8B GQA shapes: QKV 4096 -> 4096 + 1024 + 1024, gate/up 4096 -> 2 x 14336,
+    solo down 14336 -> 4096."""
+    units = []
+    if "qkv" in which:
+        x = make_x(T, 4096, ALPHA_QKV, (0, 4, 0, 0), device)
+        units.append(make_unit("qkv", "group", x, [4096, 1024, 1024], r, (0, 4, 0, r), device,
+                               layerwise=layerwise))
+    if "gateup" in which:
+        x = make_x(T, 4096, ALPHA_MLP, (0, 4, 1, 0), device)
+        units.append(make_unit("gateup", "group", x, [14336, 14336], r, (0, 4, 1, r), device,
+                               layerwise=layerwise))
+    if "down" in which:
+        x = make_x(T, 14336, ALPHA_MLP, (0, 4, 2, 0), device)
+        units.append(make_unit("down_proj", "solo", x, [4096], r, (0, 4, 2, r), device,
+                               layerwise=layerwise))
+    return units
