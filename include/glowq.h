@@ -1,0 +1,171 @@
+/*
+ * glowq.h -- C ABI of the MI355X (gfx950) library for the inference path of group-shared
+ * low-rank quantisation-error correction ("GlowQ: Group-Shared LOw-Rank Approximation for
+ * Quantized LLMs").
+ *
+ * What the path computes (token-major: X is T x d, outputs are T x O_i):
+ *   W4A16 weights: 4-bit integers q in groups of 128 inputs with one fp16 scale s and one
+ *   fp16 zero point z per (row, group); the dequantised weight is (q - z) * s
+ *   (GlowQ paper note, "Experimental setup": W4A16, INT4 weights, g128).
+ *   Low-rank compensation of the quantisation error W - W_q ~ A B adds A (B X) to the
+ *   quantised product (paper note, "Research background and motivation").
+ *   For an input-sharing group (Q/K/V on the attention input, gate/up on the MLP input)
+ *   one right factor B_shared serves every module; the anchor (Q, or gate) forms
+ *   R = X B_shared^T once and every module i, the anchor included, returns
+ *   y_i = X W_hat_i^T + R A_i^T (paper note, key design 4 and the flowchart's last node).
+ *   Solo modules (o_proj, down_proj) share no input and correct on the fly with a private B
+ *   (key design 4).  GlowQ-S applies the correction only on selected units (restore bit).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev, and every tensor pointer of the forward calls, are DEVICE
+ *     pointers on the current HIP device; the caller allocates and owns all memory.  The
+ *     forward calls allocate nothing and keep no state between calls.
+ *   - fp16 means IEEE binary16; tensors are dense row-major.
+ *   - Tensor pointers must be 16-byte aligned; the workspace 256-byte aligned.
+ *   - Every argument is validated on the host BEFORE any HIP call; a rejected call makes
+ *     no HIP call and returns a negative status.  Kernels are launched asynchronously on
+ *     `stream`; launch failures return GLOWQ_ERR_HIP; execution faults surface at the
+ *     caller's next synchronisation.
+ *   - Outputs must not alias inputs or the workspace.  One workspace must not be used by
+ *     two calls that may run concurrently.
+ */
+#ifndef GLOWQ_H
+#define GLOWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status codes */
+#define GLOWQ_OK 0
+#define GLOWQ_ERR_INVALID_ARG (-1) /* null pointer, bad enum value                         */
+#define GLOWQ_ERR_SHAPE (-2)       /* a size out of range (d % 128, T < 0, n_out < 1, ...)  */
+#define GLOWQ_ERR_ALIGN (-3)       /* pointer not 16-byte (workspace: 256-byte) aligned    */
+#define GLOWQ_ERR_UNSUPPORTED (-4) /* r > 256, r % 8 != 0, more than 8 modules            */
+#define GLOWQ_ERR_WORKSPACE (-5)   /* workspace missing or smaller than required          */
+#define GLOWQ_ERR_HIP (-6)         /* a HIP runtime call or kernel launch failed           */
+#define GLOWQ_ERR_RANGE (-7)       /* repack: a zero point is not an integer in [-1024,1024]
+                                      or a scale is not finite                           */
+
+#define GLOWQ_MAX_MODULES 8
+#define GLOWQ_MAX_RANK 256
+
+#define GLOWQ_DTYPE_F32 0
+#define GLOWQ_DTYPE_F16 1
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* glowq_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int glowq_version(void);
+
+/* ---------------------------------------------------------------- weight format
+ * Canonical interchange format of one INT4-g128 module (n_out x k_in, k_in % 128 == 0):
+ *   q_canon : uint32 [n_out][k_in / 8]; word w of row o holds input 8w + j in bits
+ *             4j..4j+3 (low nibble first), values 0..15;
+ *   scales  : fp16 [n_out][k_in / 128];
+ *   zeros   : fp16 [n_out][k_in / 128], integer valued, in [-1024, 1024].
+ * The device layout (opaque to callers) interleaves nibbles for 128-bit loads in the
+ * matrix-core operand order and pairs each zero with its scale; rows are padded to a
+ * multiple of 16 with zero weights.
+ */
+typedef struct glowq_qweight {
+    const void* q;  /* device layout words, glowq_q_bytes(n_out, k_in) bytes           */
+    const void* sz; /* device layout zero/scale pairs, glowq_sz_bytes(n_out, k_in) bytes */
+    int64_t n_out;  /* output rows O_i >= 1                                            */
+    int64_t k_in;   /* input columns d, a positive multiple of 128                      */
+} glowq_qweight;
+
+/* Bytes of the device-layout buffers of one module (0 if the shape is invalid). */
+size_t glowq_q_bytes(int64_t n_out, int64_t k_in);
+size_t glowq_sz_bytes(int64_t n_out, int64_t k_in);
+
+/* Convert one module from the canonical format (device pointers q_canon_dev, scales_dev,
+ * zeros_dev) into the device layout (q_dev, sz_dev).  flag_dev is a caller-provided device
+ * int32 used to report out-of-range zero points or non-finite scales.  This is the
+ * offline load step: it SYNCHRONISES `stream` and returns GLOWQ_ERR_RANGE if any zero point
+ * is not an integer in [-1024, 1024] or any scale is not finite (the layout is written
+ * regardless).  Shape rules: n_out >= 1, k_in % 128 == 0. */
+int glowq_repack(const void* q_canon_dev, const void* scales_dev, const void* zeros_dev,
+                 int64_t n_out, int64_t k_in, void* q_dev, void* sz_dev, int32_t* flag_dev,
+                 hipStream_t stream);
+
+/* Export the dequantised weight (q - z) * s of one module to out_dev [n_out][k_in] as fp32
+ * (exact: the product of a 5-bit integer difference and an fp16 scale fits in 24 bits) or
+ * fp16 (the exact value rounded once to nearest-even).  It runs the same in-register
+ * dequantisation routine as the forward kernels.  Asynchronous on `stream`. */
+int glowq_dequant(const glowq_qweight* w, void* out_dev, int32_t out_dtype, hipStream_t stream);
+
+/* ---------------------------------------------------------------- forward
+ * Workspace bytes for a call with T tokens, rank r and n_proj right projections (1 for a
+ * group or solo call, m for the layerwise baseline).  Holds the projection R = X B^T and
+ * synchronisation words.  Zero-fill it once after allocation; every call leaves it
+ * reusable.  Returns 0 when no workspace is needed (r == 0 or T == 0).
+ */
+size_t glowq_workspace_bytes(int64_t T, int32_t r, int32_t n_proj);
+
+/* Input-sharing group of m modules (1 <= m <= 8), w[0] the anchor.
+ *   x        : fp16 [T][d], the group's shared input (T >= 0; T == 0 is a no-op)
+ *   w        : host array of m module descriptors, every w[i].k_in == d
+ *   b_shared : fp16 [r][d] shared right factor
+ *   a        : host array of m device pointers, a[i] fp16 [w[i].n_out][r]
+ *   r        : rank, 0 <= r <= 256, r % 8 == 0
+ *   restore  : GlowQ-S bit of this group; restore == 0 or r == 0 computes the quantised
+ *              product alone, and then b_shared, a and the workspace may be NULL
+ *   y        : host array of m device pointers, y[i] fp16 [T][w[i].n_out]
+ * Result: y[i] = fp16_RNE(X W_hat_i^T + (X b_shared^T) a[i]^T), accumulated in fp32; the
+ * projection is formed once per call. */
+int glowq_group_forward(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
+                        const void* b_shared, const void* const* a, int32_t r, int32_t restore,
+                        void* workspace, size_t workspace_bytes, void* const* y,
+                        hipStream_t stream);
+
+/* Solo module (o_proj, down_proj): y = X W_hat^T + (X b^T) a^T with its private b fp16
+ * [r][d], a fp16 [n_out][r] and y fp16 [T][n_out]; nothing is kept after the call.  Same
+ * rules as glowq_group_forward. */
+int glowq_solo_forward(const void* x, int64_t T, int64_t d, const glowq_qweight* w, const void* b,
+                       const void* a, int32_t r, int32_t restore, void* workspace,
+                       size_t workspace_bytes, void* y, hipStream_t stream);
+
+/* Layerwise baseline (the comparison of the paper's latency table): every module i has
+ * its own right factor b[i] fp16 [r][d] and its own projection X b[i]^T, computed in the
+ * same kernels.  workspace_bytes >= glowq_workspace_bytes(T, r, m). */
+int glowq_layerwise_forward(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
+                            const void* const* b, const void* const* a, int32_t r, int32_t restore,
+                            void* workspace, size_t workspace_bytes, void* const* y,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------- decoder-layer schedule
+ * A sequence of units run in order on one stream: per decoder layer the QKV group, the
+ * o_proj solo, the gate/up group and the down_proj solo, each with the restore bit of the
+ * GlowQ-S mask (paper note, key design 4).  Every unit is validated before the first
+ * launch; the workspace is reused unit after unit and must hold the largest unit.
+ */
+#define GLOWQ_UNIT_GROUP 0
+#define GLOWQ_UNIT_SOLO 1
+
+typedef struct glowq_unit {
+    int32_t kind;             /* GLOWQ_UNIT_GROUP or GLOWQ_UNIT_SOLO (then m == 1) */
+    int32_t m;                /* modules                                        */
+    const void* x;            /* fp16 [T][d]                                    */
+    int64_t T, d;
+    const glowq_qweight* w;   /* host array of m descriptors                      */
+    const void* b;            /* fp16 [r][d]                                    */
+    const void* const* a;     /* host array of m device pointers                */
+    int32_t r;
+    int32_t restore;          /* this unit's GlowQ-S bit                        */
+    void* const* y;           /* host array of m device pointers                */
+} glowq_unit;
+
+int glowq_path_forward(const glowq_unit* units, int32_t n_units, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GLOWQ_H */

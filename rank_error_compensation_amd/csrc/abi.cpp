@@ -1,0 +1,313 @@
+// C ABI of libglowq: host-side validation (before any HIP call), planning and launches.
+//
+// The schedule follows the pages' inference form (GlowQ paper note, key design 4): per call the
+// projection R = X B^T is formed once for the group (or once per module for the layerwise
+// baseline), then one launch computes every module's quantised product and adds R A_i^T.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "glowq.h"
+#include "glowq_internal.h"
+
+using namespace glowq;
+
+namespace {
+
+constexpr int64_t kMaxT = 1 << 20;
+constexpr int64_t kMaxD = 1 << 20;
+constexpr int64_t kMaxRows = 1 << 24;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline int64_t r_pad_of(int32_t r) { return ceil_div(r, 32) * 32; }
+
+// Everything needed to launch one group / solo / layerwise call.
+struct Call {
+    const void* x;
+    int64_t T, d;
+    int32_t m;
+    const glowq_qweight* w;
+    const void* const* b;  // n_proj pointers (1 for shared)
+    const void* b_one;     // storage for the shared pointer
+    int32_t n_proj;
+    const void* const* a;
+    int32_t r;
+    bool correct;
+    void* const* y;
+};
+
+int validate(const Call& c, void* workspace, size_t ws_bytes) {
+    if (c.m < 1) return GLOWQ_ERR_SHAPE;
+    if (c.m > GLOWQ_MAX_MODULES) return GLOWQ_ERR_UNSUPPORTED;
+    if (c.T < 0 || c.d < kGroup || c.d % kGroup != 0) return GLOWQ_ERR_SHAPE;
+    if (c.T > kMaxT || c.d > kMaxD) return GLOWQ_ERR_UNSUPPORTED;
+    if (c.r < 0) return GLOWQ_ERR_SHAPE;
+    if (c.r > GLOWQ_MAX_RANK || c.r % 8 != 0) return GLOWQ_ERR_UNSUPPORTED;
+    if (c.w == nullptr || c.y == nullptr) return GLOWQ_ERR_INVALID_ARG;
+    if (c.T > 0 && c.x == nullptr) return GLOWQ_ERR_INVALID_ARG;
+    for (int i = 0; i < c.m; ++i) {
+        const glowq_qweight& w = c.w[i];
+        if (w.q == nullptr || w.sz == nullptr) return GLOWQ_ERR_INVALID_ARG;
+        if (c.T > 0 && c.y[i] == nullptr) return GLOWQ_ERR_INVALID_ARG;
+        if (w.n_out < 1 || w.k_in != c.d) return GLOWQ_ERR_SHAPE;
+        if (w.n_out > kMaxRows) return GLOWQ_ERR_UNSUPPORTED;
+        if (!aligned(w.q, 16) || !aligned(w.sz, 16) || !aligned(c.y[i], 16)) return GLOWQ_ERR_ALIGN;
+    }
+    if (c.x != nullptr && !aligned(c.x, 16)) return GLOWQ_ERR_ALIGN;
+    if (c.correct) {
+        if (c.a == nullptr || c.b == nullptr) return GLOWQ_ERR_INVALID_ARG;
+        for (int i = 0; i < c.m; ++i)
+            if (c.a[i] == nullptr) return GLOWQ_ERR_INVALID_ARG;
+        for (int p = 0; p < c.n_proj; ++p)
+            if (c.b[p] == nullptr) return GLOWQ_ERR_INVALID_ARG;
+        for (int i = 0; i < c.m; ++i)
+            if (!aligned(c.a[i], 16)) return GLOWQ_ERR_ALIGN;
+        for (int p = 0; p < c.n_proj; ++p)
+            if (!aligned(c.b[p], 16)) return GLOWQ_ERR_ALIGN;
+        if (c.T > 0) {
+            const size_t need = glowq_workspace_bytes(c.T, c.r, c.n_proj);
+            if (workspace == nullptr || ws_bytes < need) return GLOWQ_ERR_WORKSPACE;
+            if (!aligned(workspace, 256)) return GLOWQ_ERR_ALIGN;
+        }
+    }
+    return GLOWQ_OK;
+}
+
+// Choose the prefill tile shape: the largest tile that still yields at least two workgroups per
+// CU (256 CUs); otherwise the shape with the most workgroups.
+void choose_prefill_shape(const Call& c, int& tt, int& rr) {
+    const int64_t want = 2 * 256;
+    int64_t best_n = -1;
+    int best_tt = 4, best_rr = 2;
+    for (const auto& sh : kPrefillShapes) {
+        const int64_t mt = ceil_div(c.T, 16 * sh[0]);
+        int64_t nb = 0;
+        for (int i = 0; i < c.m; ++i) nb += ceil_div(ceil_div(c.w[i].n_out, 16), 4 * sh[1]);
+        const int64_t n = mt * nb;
+        if (n >= want) {
+            tt = sh[0];
+            rr = sh[1];
+            return;
+        }
+        if (n > best_n) {
+            best_n = n;
+            best_tt = sh[0];
+            best_rr = sh[1];
+        }
+    }
+    tt = best_tt;
+    rr = best_rr;
+}
+
+int run(const Call& c, void* workspace, hipStream_t stream) {
+    if (c.T == 0) return GLOWQ_OK;
+    const bool prefill = c.T > kDecodeMaxT;
+    const int32_t rp = (int32_t)r_pad_of(c.r);
+    void* R = c.correct ? static_cast<uint8_t*>(workspace) + kWsHeader : nullptr;
+
+    if (c.correct) {
+        ProjArgs p;
+        std::memset(&p, 0, sizeof(p));
+        p.x = static_cast<const _Float16*>(c.x);
+        p.T = (int32_t)c.T;
+        p.d = (int32_t)c.d;
+        p.r = c.r;
+        p.r_pad = rp;
+        p.n_proj = c.n_proj;
+        for (int i = 0; i < c.n_proj; ++i) p.b[i] = static_cast<const _Float16*>(c.b[i]);
+        p.R = R;
+        const hipError_t e = prefill ? launch_proj_prefill(p, stream) : launch_proj_decode(p, stream);
+        if (e != hipSuccess) return GLOWQ_ERR_HIP;
+    }
+
+    ForwardArgs f;
+    std::memset(&f, 0, sizeof(f));
+    f.x = static_cast<const _Float16*>(c.x);
+    f.T = (int32_t)c.T;
+    f.d = (int32_t)c.d;
+    f.G = (int32_t)(c.d / kGroup);
+    f.r = c.correct ? c.r : 0;
+    f.r_pad = c.correct ? rp : 0;
+    f.n_mod = c.m;
+    f.R = R;
+    int tt = 0, rr = 0;
+    if (prefill) choose_prefill_shape(c, tt, rr);
+    f.tile_tt = tt;
+    f.tile_rr = rr;
+    int64_t tiles = 0;
+    for (int i = 0; i < c.m; ++i) {
+        ModuleArgs& M = f.mod[i];
+        M.q = static_cast<const uint8_t*>(c.w[i].q);
+        M.sz = static_cast<const uint8_t*>(c.w[i].sz);
+        M.a = c.correct ? static_cast<const _Float16*>(c.a[i]) : nullptr;
+        M.y = static_cast<_Float16*>(c.y[i]);
+        M.n_out = (int32_t)c.w[i].n_out;
+        M.n_tiles16 = (int32_t)ceil_div(c.w[i].n_out, 16);
+        M.tile_begin = (int32_t)tiles;
+        M.proj = c.n_proj > 1 ? i : 0;
+        tiles += prefill ? ceil_div(M.n_tiles16, 4 * rr) : M.n_tiles16;
+    }
+    hipError_t e;
+    if (prefill) {
+        f.m_tiles = (int32_t)ceil_div(c.T, 16 * tt);
+        f.n_tiles = (int32_t)(tiles * f.m_tiles);
+        e = launch_prefill(f, stream);
+    } else {
+        f.m_tiles = 1;
+        f.n_tiles = (int32_t)tiles;
+        e = launch_decode(f, stream);
+    }
+    return e == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
+}
+
+Call make_group(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
+                const void* const* b, int32_t n_proj, const void* const* a, int32_t r, int32_t restore,
+                void* const* y) {
+    Call c;
+    c.x = x;
+    c.T = T;
+    c.d = d;
+    c.m = m;
+    c.w = w;
+    c.b = b;
+    c.b_one = nullptr;
+    c.n_proj = n_proj;
+    c.a = a;
+    c.r = r;
+    c.correct = restore != 0 && r > 0;
+    c.y = y;
+    return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* glowq_status_string(int status) {
+    switch (status) {
+        case GLOWQ_OK: return "GLOWQ_OK";
+        case GLOWQ_ERR_INVALID_ARG: return "GLOWQ_ERR_INVALID_ARG: null pointer or bad enum value";
+        case GLOWQ_ERR_SHAPE: return "GLOWQ_ERR_SHAPE: size out of range";
+        case GLOWQ_ERR_ALIGN: return "GLOWQ_ERR_ALIGN: pointer misaligned";
+        case GLOWQ_ERR_UNSUPPORTED: return "GLOWQ_ERR_UNSUPPORTED: configuration not supported";
+        case GLOWQ_ERR_WORKSPACE: return "GLOWQ_ERR_WORKSPACE: workspace missing or too small";
+        case GLOWQ_ERR_HIP: return "GLOWQ_ERR_HIP: HIP runtime or launch failure";
+        case GLOWQ_ERR_RANGE: return "GLOWQ_ERR_RANGE: zero point or scale out of range";
+        default: return "GLOWQ_ERR_UNKNOWN";
+    }
+}
+
+int glowq_version(void) { return 100; }
+
+size_t glowq_q_bytes(int64_t n_out, int64_t k_in) {
+    if (n_out < 1 || k_in < kGroup || k_in % kGroup != 0 || n_out > kMaxRows || k_in > kMaxD) return 0;
+    return (size_t)ceil_div(n_out, 16) * (size_t)(k_in / kGroup) * 1024u;
+}
+
+size_t glowq_sz_bytes(int64_t n_out, int64_t k_in) {
+    if (n_out < 1 || k_in < kGroup || k_in % kGroup != 0 || n_out > kMaxRows || k_in > kMaxD) return 0;
+    return (size_t)ceil_div(n_out, 16) * (size_t)(k_in / kGroup) * 64u;
+}
+
+size_t glowq_workspace_bytes(int64_t T, int32_t r, int32_t n_proj) {
+    if (T <= 0 || r <= 0 || n_proj <= 0) return 0;
+    const size_t per_dec = (size_t)T * (size_t)r * 4u;
+    const size_t per_pre = (size_t)T * (size_t)r_pad_of(r) * 2u;
+    const size_t per = per_dec > per_pre ? per_dec : per_pre;
+    const size_t body = ((per * (size_t)n_proj) + 255u) / 256u * 256u;
+    return kWsHeader + body;
+}
+
+int glowq_repack(const void* q_canon_dev, const void* scales_dev, const void* zeros_dev, int64_t n_out,
+                 int64_t k_in, void* q_dev, void* sz_dev, int32_t* flag_dev, hipStream_t stream) {
+    if (!q_canon_dev || !scales_dev || !zeros_dev || !q_dev || !sz_dev || !flag_dev)
+        return GLOWQ_ERR_INVALID_ARG;
+    if (n_out < 1 || k_in < kGroup || k_in % kGroup != 0) return GLOWQ_ERR_SHAPE;
+    if (n_out > kMaxRows || k_in > kMaxD) return GLOWQ_ERR_UNSUPPORTED;
+    if (!aligned(q_canon_dev, 4) || !aligned(scales_dev, 2) || !aligned(zeros_dev, 2) ||
+        !aligned(q_dev, 16) || !aligned(sz_dev, 16) || !aligned(flag_dev, 4))
+        return GLOWQ_ERR_ALIGN;
+    if (launch_flag_clear(flag_dev, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    if (launch_repack(static_cast<const uint32_t*>(q_canon_dev), static_cast<const _Float16*>(scales_dev),
+                      static_cast<const _Float16*>(zeros_dev), n_out, k_in, static_cast<uint8_t*>(q_dev),
+                      static_cast<uint8_t*>(sz_dev), flag_dev, stream) != hipSuccess)
+        return GLOWQ_ERR_HIP;
+    int32_t flag = 0;
+    if (hipMemcpyAsync(&flag, flag_dev, sizeof(flag), hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return GLOWQ_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    return flag ? GLOWQ_ERR_RANGE : GLOWQ_OK;
+}
+
+int glowq_dequant(const glowq_qweight* w, void* out_dev, int32_t out_dtype, hipStream_t stream) {
+    if (!w || !out_dev || !w->q || !w->sz) return GLOWQ_ERR_INVALID_ARG;
+    if (out_dtype != GLOWQ_DTYPE_F32 && out_dtype != GLOWQ_DTYPE_F16) return GLOWQ_ERR_INVALID_ARG;
+    if (w->n_out < 1 || w->k_in < kGroup || w->k_in % kGroup != 0) return GLOWQ_ERR_SHAPE;
+    if (w->n_out > kMaxRows || w->k_in > kMaxD) return GLOWQ_ERR_UNSUPPORTED;
+    if (!aligned(w->q, 16) || !aligned(w->sz, 16) || !aligned(out_dev, 16)) return GLOWQ_ERR_ALIGN;
+    const hipError_t e = launch_dequant(static_cast<const uint8_t*>(w->q), static_cast<const uint8_t*>(w->sz),
+                                        w->n_out, w->k_in, out_dev, out_dtype == GLOWQ_DTYPE_F32 ? 0 : 1,
+                                        stream);
+    return e == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
+}
+
+int glowq_group_forward(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
+                        const void* b_shared, const void* const* a, int32_t r, int32_t restore,
+                        void* workspace, size_t workspace_bytes, void* const* y, hipStream_t stream) {
+    const void* bp[1] = {b_shared};
+    const Call c = make_group(x, T, d, m, w, bp, 1, a, r, restore, y);
+    const int v = validate(c, workspace, workspace_bytes);
+    if (v != GLOWQ_OK) return v;
+    return run(c, workspace, stream);
+}
+
+int glowq_solo_forward(const void* x, int64_t T, int64_t d, const glowq_qweight* w, const void* b,
+                       const void* a, int32_t r, int32_t restore, void* workspace, size_t workspace_bytes,
+                       void* y, hipStream_t stream) {
+    const void* bp[1] = {b};
+    const void* ap[1] = {a};
+    void* yp[1] = {y};
+    const Call c = make_group(x, T, d, 1, w, bp, 1, ap, r, restore, yp);
+    const int v = validate(c, workspace, workspace_bytes);
+    if (v != GLOWQ_OK) return v;
+    return run(c, workspace, stream);
+}
+
+int glowq_layerwise_forward(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
+                            const void* const* b, const void* const* a, int32_t r, int32_t restore,
+                            void* workspace, size_t workspace_bytes, void* const* y, hipStream_t stream) {
+    if (m < 1) return GLOWQ_ERR_SHAPE;
+    if (m > GLOWQ_MAX_MODULES) return GLOWQ_ERR_UNSUPPORTED;
+    const Call c = make_group(x, T, d, m, w, b, m, a, r, restore, y);
+    const int v = validate(c, workspace, workspace_bytes);
+    if (v != GLOWQ_OK) return v;
+    return run(c, workspace, stream);
+}
+
+int glowq_path_forward(const glowq_unit* units, int32_t n_units, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    if (n_units < 0) return GLOWQ_ERR_SHAPE;
+    if (n_units > 0 && units == nullptr) return GLOWQ_ERR_INVALID_ARG;
+    // validate every unit first: a rejected schedule launches nothing
+    for (int32_t u = 0; u < n_units; ++u) {
+        const glowq_unit& U = units[u];
+        if (U.kind != GLOWQ_UNIT_GROUP && U.kind != GLOWQ_UNIT_SOLO) return GLOWQ_ERR_INVALID_ARG;
+        if (U.kind == GLOWQ_UNIT_SOLO && U.m != 1) return GLOWQ_ERR_SHAPE;
+        const void* bp[1] = {U.b};
+        const Call c = make_group(U.x, U.T, U.d, U.m, U.w, bp, 1, U.a, U.r, U.restore, U.y);
+        const int v = validate(c, workspace, workspace_bytes);
+        if (v != GLOWQ_OK) return v;
+    }
+    for (int32_t u = 0; u < n_units; ++u) {
+        const glowq_unit& U = units[u];
+        const void* bp[1] = {U.b};
+        const Call c = make_group(U.x, U.T, U.d, U.m, U.w, bp, 1, U.a, U.r, U.restore, U.y);
+        const int v = run(c, workspace, stream);
+        if (v != GLOWQ_OK) return v;
+    }
+    return GLOWQ_OK;
+}
+
+}  // extern "C"

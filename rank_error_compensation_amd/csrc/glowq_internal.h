@@ -1,0 +1,129 @@
+// Internal definitions shared by the HIP translation units of libglowq (not installed).
+//
+// Device layout of one INT4-g128 module (n_out x k_in, G = k_in / 128 groups, NT = ceil(n_out/16)
+// row tiles of 16 rows):
+//   q  : NT x G blocks of 1024 bytes, block (rt, g) at byte (rt * G + g) * 1024.  Lane l (0..63)
+//        of a wavefront owns the 16 bytes at l * 16: four 32-bit words, word j (0..3) holding the
+//        eight inputs k = 128 g + 32 j + 8 (l / 16) + e, e = 0..7, of row 16 rt + (l % 16).  This
+//        is exactly the A/B operand of v_mfma_f32_16x16x32_f16 (lane l: row l % 16, k-slice
+//        8 (l / 16) .. +8) for the j-th 32-wide slice of the group, so one 128-bit load per lane
+//        brings a whole group's operands for four matrix-core steps.  Inside a word, nibble slot
+//        p (bits 4p..4p+3) holds e = 2p for p < 4 and e = 2(p - 4) + 1 for p >= 4, so that
+//        masking with 0x000F000F / 0x00F000F0 (after a shift by 0 or 8) yields the fp16 pairs
+//        (e0, e1), (e2, e3), (e4, e5), (e6, e7) with the 0x6400 exponent trick.
+//   sz : NT x G blocks of 64 bytes, block (rt, g) at byte (rt * G + g) * 64: sixteen (z, s) fp16
+//        pairs, pair i for row 16 rt + i.
+//   Rows >= n_out are zero (q = 0, z = 0, s = 0).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace glowq {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 128;
+constexpr int kMaxModules = 8;
+constexpr int kMaxRank = 256;
+constexpr size_t kWsHeader = 256;  // workspace bytes reserved for synchronisation words
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// --------------------------------------------------------------------- device helpers
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Eight nibbles of one device-layout word -> the eight integer differences (q - z) as fp16,
+// exact for integer z in [-1024, 1024]: 0x6400 | q is the fp16 value 1024 + q, 0x6400 | (q << 4)
+// is 1024 + 16 q; subtracting 1024 + z (resp. scaling by 1/16 and subtracting 64 + z) is exact.
+__device__ __forceinline__ h8 nib8_minus_z(uint32_t w, h2 zc1024, h2 zc64) {
+    const uint32_t lo = w, hi = w >> 8;
+    const h2 p0 = as_h2((lo & 0x000F000Fu) | 0x64006400u);
+    const h2 p1 = as_h2((lo & 0x00F000F0u) | 0x64006400u);
+    const h2 p2 = as_h2((hi & 0x000F000Fu) | 0x64006400u);
+    const h2 p3 = as_h2((hi & 0x00F000F0u) | 0x64006400u);
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 d0 = p0 - zc1024;
+    const h2 d1 = p1 * sixteenth - zc64;
+    const h2 d2 = p2 - zc1024;
+    const h2 d3 = p3 * sixteenth - zc64;
+    h8 r;
+    r[0] = d0[0]; r[1] = d0[1]; r[2] = d1[0]; r[3] = d1[1];
+    r[4] = d2[0]; r[5] = d2[1]; r[6] = d3[0]; r[7] = d3[1];
+    return r;
+}
+
+// (1024 + z, 1024 + z) and (64 + z, 64 + z) from the (z, s) pair word of a row.
+__device__ __forceinline__ void zero_consts(uint32_t zs, h2& zc1024, h2& zc64) {
+    const _Float16 z = as_h2(zs)[0];
+    const _Float16 a = (_Float16)1024.0f + z;
+    const _Float16 b = (_Float16)64.0f + z;
+    zc1024 = h2{a, a};
+    zc64 = h2{b, b};
+}
+
+__device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ h8 load_h8(const void* p) {
+    return __builtin_bit_cast(h8, *reinterpret_cast<const u4*>(p));
+}
+
+// --------------------------------------------------------------------- launch arguments
+struct ModuleArgs {
+    const uint8_t* q;    // device layout
+    const uint8_t* sz;   // device layout
+    const _Float16* a;   // [n_out][r] (may be null when no correction)
+    _Float16* y;         // [T][n_out]
+    int32_t n_out;
+    int32_t n_tiles16;   // ceil(n_out / 16)
+    int32_t tile_begin;  // first work tile of this module in the launch's tile numbering
+    int32_t proj;        // which projection R_p this module adds (0 for shared B)
+};
+
+struct ForwardArgs {
+    const _Float16* x;   // [T][d]
+    int32_t T, d, G;     // G = d / 128
+    int32_t r;           // rank (0 = no correction)
+    int32_t r_pad;       // r rounded up to 32 (prefill R row stride)
+    int32_t n_mod;
+    int32_t n_tiles;     // total work tiles of the launch
+    int32_t m_tiles;     // token tiles (prefill)
+    int32_t tile_tt;     // prefill tile shape: 16-token tiles per wave
+    int32_t tile_rr;     // prefill tile shape: 16-row tiles per wave (4 waves side by side)
+    const void* R;       // projections: decode fp32 [n_proj][T][r]; prefill fp16 [n_proj][T][r_pad]
+    ModuleArgs mod[kMaxModules];
+};
+
+struct ProjArgs {
+    const _Float16* x;   // [T][d]
+    int32_t T, d, r, r_pad, n_proj;
+    const _Float16* b[kMaxModules];  // [r][d] per projection
+    void* R;             // output
+};
+
+// --------------------------------------------------------------------- launchers
+hipError_t launch_repack(const uint32_t* qc, const _Float16* s, const _Float16* z, int64_t n_out,
+                         int64_t k_in, uint8_t* q_dev, uint8_t* sz_dev, int32_t* flag,
+                         hipStream_t stream);
+hipError_t launch_flag_clear(int32_t* flag, hipStream_t stream);
+hipError_t launch_dequant(const uint8_t* q, const uint8_t* sz, int64_t n_out, int64_t k_in, void* out,
+                          int dtype, hipStream_t stream);
+hipError_t launch_proj_decode(const ProjArgs& p, hipStream_t stream);
+hipError_t launch_proj_prefill(const ProjArgs& p, hipStream_t stream);
+hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
+
+// Token count above which the prefill (dequant-to-register MFMA GEMM) kernels are used.
+constexpr int kDecodeMaxT = 64;
+
+// Prefill tile shapes compiled, largest first: (TT, RR) token-tile x row-tile counts per wave.
+constexpr int kPrefillShapes[3][2] = {{8, 2}, {4, 4}, {4, 2}};
+
+}  // namespace glowq

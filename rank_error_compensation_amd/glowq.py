@@ -1,0 +1,268 @@
+"""Thin ctypes binding of libglowq (include/glowq.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.  torch is
+used for device memory and the current stream (plumbing); tensors are passed as raw pointers.
+There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libglowq.so")
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_SHAPE = -2
+ERR_ALIGN = -3
+ERR_UNSUPPORTED = -4
+ERR_WORKSPACE = -5
+ERR_HIP = -6
+ERR_RANGE = -7
+
+DTYPE_F32 = 0
+DTYPE_F16 = 1
+UNIT_GROUP = 0
+UNIT_SOLO = 1
+MAX_MODULES = 8
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+
+class QWeightC(ctypes.Structure):
+    _fields_ = [("q", _vp), ("sz", _vp), ("n_out", _i64), ("k_in", _i64)]
+
+
+class UnitC(ctypes.Structure):
+    _fields_ = [("kind", _i32), ("m", _i32), ("x", _vp), ("T", _i64), ("d", _i64),
+                ("w", ctypes.POINTER(QWeightC)), ("b", _vp), ("a", ctypes.POINTER(_vp)),
+                ("r", _i32), ("restore", _i32), ("y", ctypes.POINTER(_vp))]
+
+
+EXPORTS = {
+    "glowq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "glowq_version": (ctypes.c_int, []),
+    "glowq_q_bytes": (_sz, [_i64, _i64]),
+    "glowq_sz_bytes": (_sz, [_i64, _i64]),
+    "glowq_repack": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "glowq_dequant": (ctypes.c_int, [ctypes.POINTER(QWeightC), _vp, _i32, _vp]),
+    "glowq_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "glowq_group_forward": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(QWeightC), _vp,
+                                           ctypes.POINTER(_vp), _i32, _i32, _vp, _sz,
+                                           ctypes.POINTER(_vp), _vp]),
+    "glowq_solo_forward": (ctypes.c_int, [_vp, _i64, _i64, ctypes.POINTER(QWeightC), _vp, _vp, _i32,
+                                          _i32, _vp, _sz, _vp, _vp]),
+    "glowq_layerwise_forward": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(QWeightC),
+                                               ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i32,
+                                               _vp, _sz, ctypes.POINTER(_vp), _vp]),
+    "glowq_path_forward": (ctypes.c_int, [ctypes.POINTER(UnitC), _i32, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libglowq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(python -m rank_error_compensation_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+class GlowQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().glowq_status_string(status).decode()} ({status})")
+
+
+def check(status: int, what: str) -> None:
+    if status != OK:
+        raise GlowQError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# --------------------------------------------------------------------------- weights
+@dataclass
+class QWeight:
+    """One INT4-g128 module in the library's device layout."""
+    q: torch.Tensor     # uint8, glowq_q_bytes
+    sz: torch.Tensor    # uint8, glowq_sz_bytes
+    n_out: int
+    k_in: int
+
+    def c(self) -> QWeightC:
+        return QWeightC(self.q.data_ptr(), self.sz.data_ptr(), self.n_out, self.k_in)
+
+    @staticmethod
+    def from_canonical(q_packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                       device=None, stream=None) -> "QWeight":
+        """Repack canonical (q_packed int32 [n_out][k_in/8], scales/zeros fp16 [n_out][k_in/128])
+        into the device layout (glowq_repack; synchronises the stream)."""
+        device = device or torch.device("cuda")
+        n_out, kw = q_packed.shape
+        k_in = kw * 8
+        qc = q_packed.to(device).contiguous()
+        s = scales.to(device=device, dtype=torch.float16).contiguous()
+        z = zeros.to(device=device, dtype=torch.float16).contiguous()
+        L = lib()
+        qb, zb = L.glowq_q_bytes(n_out, k_in), L.glowq_sz_bytes(n_out, k_in)
+        if qb == 0 or zb == 0:
+            raise GlowQError(ERR_SHAPE, "glowq_q_bytes")
+        q_dev = torch.empty(qb, dtype=torch.uint8, device=device)
+        sz_dev = torch.empty(zb, dtype=torch.uint8, device=device)
+        flag = torch.empty(1, dtype=torch.int32, device=device)
+        check(L.glowq_repack(_ptr(qc), _ptr(s), _ptr(z), n_out, k_in, _ptr(q_dev), _ptr(sz_dev),
+                             _ptr(flag), _stream(stream)), "glowq_repack")
+        return QWeight(q_dev, sz_dev, int(n_out), int(k_in))
+
+    @staticmethod
+    def from_workload(qw, device=None, stream=None) -> "QWeight":
+        return QWeight.from_canonical(qw.q_packed, qw.s, qw.z, device, stream)
+
+
+def dequant(w: QWeight, dtype=torch.float32, stream=None) -> torch.Tensor:
+    out = torch.empty(w.n_out, w.k_in, dtype=dtype, device=w.q.device)
+    code = DTYPE_F32 if dtype == torch.float32 else DTYPE_F16
+    wc = w.c()
+    check(lib().glowq_dequant(ctypes.byref(wc), _ptr(out), code, _stream(stream)), "glowq_dequant")
+    return out
+
+
+# --------------------------------------------------------------------------- forward
+def workspace_bytes(T: int, r: int, n_proj: int = 1) -> int:
+    return int(lib().glowq_workspace_bytes(T, r, n_proj))
+
+
+def make_workspace(T: int, r: int, n_proj: int = 1, device=None) -> Optional[torch.Tensor]:
+    n = workspace_bytes(T, r, n_proj)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device or torch.device("cuda"))
+
+
+def _arr(kind, items):
+    return (kind * max(1, len(items)))(*items)
+
+
+def _outs(x: torch.Tensor, weights: Sequence[QWeight], y):
+    if y is None:
+        y = [torch.empty(x.shape[0], w.n_out, dtype=torch.float16, device=x.device) for w in weights]
+    return y
+
+
+def group_forward(x: torch.Tensor, weights: Sequence[QWeight], b: Optional[torch.Tensor],
+                  a: Sequence[torch.Tensor], r: int, restore: bool = True,
+                  workspace: Optional[torch.Tensor] = None, y: Optional[List[torch.Tensor]] = None,
+                  stream=None) -> List[torch.Tensor]:
+    m = len(weights)
+    y = _outs(x, weights, y)
+    if workspace is None and restore and r > 0:
+        workspace = make_workspace(x.shape[0], r, 1, x.device)
+    wc = _arr(QWeightC, [w.c() for w in weights])
+    ac = _arr(_vp, [t.data_ptr() for t in a]) if a else None
+    yc = _arr(_vp, [t.data_ptr() for t in y])
+    ws_n = 0 if workspace is None else workspace.numel()
+    check(lib().glowq_group_forward(_ptr(x), x.shape[0], x.shape[1], m, wc, _ptr(b), ac, r,
+                                    int(bool(restore)), _ptr(workspace), ws_n, yc, _stream(stream)),
+          "glowq_group_forward")
+    return y
+
+
+def solo_forward(x: torch.Tensor, w: QWeight, b: Optional[torch.Tensor], a: Optional[torch.Tensor],
+                 r: int, restore: bool = True, workspace: Optional[torch.Tensor] = None,
+                 y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if y is None:
+        y = torch.empty(x.shape[0], w.n_out, dtype=torch.float16, device=x.device)
+    if workspace is None and restore and r > 0:
+        workspace = make_workspace(x.shape[0], r, 1, x.device)
+    wc = w.c()
+    ws_n = 0 if workspace is None else workspace.numel()
+    check(lib().glowq_solo_forward(_ptr(x), x.shape[0], x.shape[1], ctypes.byref(wc), _ptr(b), _ptr(a),
+                                   r, int(bool(restore)), _ptr(workspace), ws_n, _ptr(y), _stream(stream)),
+          "glowq_solo_forward")
+    return y
+
+
+def layerwise_forward(x: torch.Tensor, weights: Sequence[QWeight], b: Sequence[torch.Tensor],
+                      a: Sequence[torch.Tensor], r: int, restore: bool = True,
+                      workspace: Optional[torch.Tensor] = None, y: Optional[List[torch.Tensor]] = None,
+                      stream=None) -> List[torch.Tensor]:
+    m = len(weights)
+    y = _outs(x, weights, y)
+    if workspace is None and restore and r > 0:
+        workspace = make_workspace(x.shape[0], r, m, x.device)
+    wc = _arr(QWeightC, [w.c() for w in weights])
+    bc = _arr(_vp, [t.data_ptr() for t in b]) if b else None
+    ac = _arr(_vp, [t.data_ptr() for t in a]) if a else None
+    yc = _arr(_vp, [t.data_ptr() for t in y])
+    ws_n = 0 if workspace is None else workspace.numel()
+    check(lib().glowq_layerwise_forward(_ptr(x), x.shape[0], x.shape[1], m, wc, bc, ac, r,
+                                        int(bool(restore)), _ptr(workspace), ws_n, yc, _stream(stream)),
+          "glowq_layerwise_forward")
+    return y
+
+
+@dataclass
+class PathUnit:
+    """One unit of a decoder-layer schedule (a group or a solo module) with its restore bit."""
+    kind: int
+    x: torch.Tensor
+    weights: List[QWeight]
+    b: Optional[torch.Tensor]
+    a: List[torch.Tensor]
+    r: int
+    restore: bool
+    y: List[torch.Tensor]
+
+
+class PathPlan:
+    """Marshalled glowq_unit array for repeated glowq_path_forward calls (keeps the ctypes
+    arrays alive)."""
+
+    def __init__(self, units: Sequence[PathUnit]):
+        self.units = list(units)
+        self._keep = []
+        arr = (UnitC * max(1, len(self.units)))()
+        for i, u in enumerate(self.units):
+            wc = _arr(QWeightC, [w.c() for w in u.weights])
+            ac = _arr(_vp, [t.data_ptr() for t in u.a]) if u.a else None
+            yc = _arr(_vp, [t.data_ptr() for t in u.y])
+            self._keep += [wc, ac, yc]
+            arr[i] = UnitC(u.kind, len(u.weights), u.x.data_ptr(), u.x.shape[0], u.x.shape[1],
+                           ctypes.cast(wc, ctypes.POINTER(QWeightC)),
+                           None if u.b is None else u.b.data_ptr(),
+                           None if ac is None else ctypes.cast(ac, ctypes.POINTER(_vp)),
+                           u.r, int(bool(u.restore)), ctypes.cast(yc, ctypes.POINTER(_vp)))
+        self.arr = arr
+        need = max([workspace_bytes(u.x.shape[0], u.r, 1) for u in self.units if u.restore] + [0])
+        dev = self.units[0].x.device if self.units else torch.device("cuda")
+        self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def run(self, stream=None) -> None:
+        check(lib().glowq_path_forward(self.arr, len(self.units), _ptr(self.workspace),
+                                       self.workspace.numel(), _stream(stream)), "glowq_path_forward")

@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: the library loads, exports every function that include/glowq.h
+declares, sizes its buffers as documented and rejects invalid arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_error_compensation_amd import glowq as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "glowq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(glowq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = g.lib()
+    names = header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(g.EXPORTS), set(names) ^ set(g.EXPORTS)
+
+
+def test_status_strings_and_version():
+    L = g.lib()
+    assert L.glowq_version() == 100
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert L.glowq_status_string(code).startswith(b"GLOWQ_")
+    assert L.glowq_status_string(12345) == b"GLOWQ_ERR_UNKNOWN"
+
+
+def test_buffer_sizes():
+    L = g.lib()
+    assert L.glowq_q_bytes(4096, 4096) == 4096 * 4096 // 2
+    assert L.glowq_sz_bytes(4096, 4096) == 4096 * 32 * 4
+    assert L.glowq_q_bytes(17, 256) == 2 * 2 * 1024  # rows padded to 32
+    assert L.glowq_q_bytes(16, 100) == 0 and L.glowq_q_bytes(0, 128) == 0
+    assert L.glowq_workspace_bytes(0, 64, 1) == 0
+    assert L.glowq_workspace_bytes(4, 0, 1) == 0
+    assert L.glowq_workspace_bytes(1, 64, 1) == 256 + 256
+    assert L.glowq_workspace_bytes(2048, 64, 1) == 256 + 2048 * 64 * 4
+    assert L.glowq_workspace_bytes(100, 8, 3) == 256 + ((100 * 32 * 2 * 3 + 255) // 256) * 256
+
+
+FAKE = 0x10000  # 64 KiB-aligned fake device address: never dereferenced, validation fails first
+
+
+def _w(n_out=32, k_in=256, q=FAKE, sz=FAKE):
+    return g.QWeightC(q, sz, n_out, k_in)
+
+
+def call_group(x=FAKE, T=4, d=256, m=1, w=None, b=FAKE, a=None, r=8, restore=1, ws=FAKE,
+               ws_bytes=1 << 20, y=None):
+    L = g.lib()
+    w = w if w is not None else [_w() for _ in range(m)]
+    wc = (g.QWeightC * max(1, len(w)))(*w)
+    a = a if a is not None else [FAKE] * m
+    y = y if y is not None else [FAKE] * m
+    ac = (ctypes.c_void_p * max(1, len(a)))(*a)
+    yc = (ctypes.c_void_p * max(1, len(y)))(*y)
+    return L.glowq_group_forward(x, T, d, m, wc, b, ac, r, restore, ws, ws_bytes, yc, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=0), g.ERR_SHAPE),
+    (dict(m=9), g.ERR_UNSUPPORTED),
+    (dict(T=-1), g.ERR_SHAPE),
+    (dict(d=100), g.ERR_SHAPE),
+    (dict(d=0), g.ERR_SHAPE),
+    (dict(r=-8), g.ERR_SHAPE),
+    (dict(r=264), g.ERR_UNSUPPORTED),
+    (dict(r=12), g.ERR_UNSUPPORTED),
+    (dict(x=None), g.ERR_INVALID_ARG),
+    (dict(w=[_w(q=0)]), g.ERR_INVALID_ARG),
+    (dict(w=[_w(n_out=0)]), g.ERR_SHAPE),
+    (dict(w=[_w(k_in=384)]), g.ERR_SHAPE),
+    (dict(b=None), g.ERR_INVALID_ARG),
+    (dict(a=[0]), g.ERR_INVALID_ARG),
+    (dict(y=[0]), g.ERR_INVALID_ARG),
+    (dict(x=FAKE + 8), g.ERR_ALIGN),
+    (dict(y=[FAKE + 2]), g.ERR_ALIGN),
+    (dict(a=[FAKE + 4]), g.ERR_ALIGN),
+    (dict(w=[_w(q=FAKE + 8)]), g.ERR_ALIGN),
+    (dict(ws=None), g.ERR_WORKSPACE),
+    (dict(ws_bytes=100), g.ERR_WORKSPACE),
+    (dict(ws=FAKE + 16), g.ERR_ALIGN),
+])
+def test_group_validation_rejects_before_any_hip_call(kw, code):
+    assert call_group(**kw) == code
+
+
+def test_restore_off_needs_no_factors_and_t0_is_noop():
+    # restore off with null b / a / workspace validates; T = 0 returns OK without launching
+    assert call_group(T=0, b=None, a=[0], ws=None, restore=0) == g.OK
+    assert call_group(T=0, r=0, b=None, a=[0], ws=None) == g.OK
+    assert call_group(T=0, x=None, y=[0]) == g.OK
+
+
+def test_other_entry_points_validate():
+    L = g.lib()
+    wc = _w()
+    assert L.glowq_solo_forward(FAKE, 4, 256, ctypes.byref(wc), None, FAKE, 8, 1, FAKE, 1 << 20, FAKE,
+                                None) == g.ERR_INVALID_ARG
+    assert L.glowq_solo_forward(FAKE, 4, 256, None, FAKE, FAKE, 8, 1, FAKE, 1 << 20, FAKE, None) == g.ERR_INVALID_ARG
+    ws = (g.QWeightC * 2)(_w(), _w())
+    bc = (ctypes.c_void_p * 2)(FAKE, 0)
+    ac = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    yc = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    assert L.glowq_layerwise_forward(FAKE, 4, 256, 2, ws, bc, ac, 8, 1, FAKE, 1 << 20, yc, None) == g.ERR_INVALID_ARG
+    bc2 = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    need = L.glowq_workspace_bytes(4, 8, 2)
+    assert L.glowq_layerwise_forward(FAKE, 4, 256, 2, ws, bc2, ac, 8, 1, FAKE, need - 1, yc, None) == g.ERR_WORKSPACE
+    assert L.glowq_dequant(None, FAKE, 0, None) == g.ERR_INVALID_ARG
+    assert L.glowq_dequant(ctypes.byref(wc), FAKE, 7, None) == g.ERR_INVALID_ARG
+    bad = _w(k_in=200)
+    assert L.glowq_dequant(ctypes.byref(bad), FAKE, 0, None) == g.ERR_SHAPE
+    assert L.glowq_repack(FAKE, FAKE, FAKE, 16, 100, FAKE, FAKE, FAKE, None) == g.ERR_SHAPE
+    assert L.glowq_repack(None, FAKE, FAKE, 16, 128, FAKE, FAKE, FAKE, None) == g.ERR_INVALID_ARG
+    assert L.glowq_repack(FAKE, FAKE, FAKE, 16, 128, FAKE + 4, FAKE, FAKE, None) == g.ERR_ALIGN
+
+
+def test_path_validates_every_unit_first():
+    L = g.lib()
+    wq = (g.QWeightC * 1)(_w())
+    ac = (ctypes.c_void_p * 1)(FAKE)
+    yc = (ctypes.c_void_p * 1)(FAKE)
+    P = ctypes.POINTER
+    good = g.UnitC(g.UNIT_GROUP, 1, FAKE, 0, 256, ctypes.cast(wq, P(g.QWeightC)), FAKE,
+                   ctypes.cast(ac, P(ctypes.c_void_p)), 8, 1, ctypes.cast(yc, P(ctypes.c_void_p)))
+    bad = g.UnitC(g.UNIT_SOLO, 2, FAKE, 0, 256, ctypes.cast(wq, P(g.QWeightC)), FAKE,
+                  ctypes.cast(ac, P(ctypes.c_void_p)), 8, 1, ctypes.cast(yc, P(ctypes.c_void_p)))
+    arr = (g.UnitC * 2)(good, bad)
+    assert L.glowq_path_forward(arr, 2, FAKE, 1 << 20, None) == g.ERR_SHAPE
+    arr2 = (g.UnitC * 2)(good, good)
+    assert L.glowq_path_forward(arr2, 2, FAKE, 1 << 20, None) == g.OK  # T = 0 units
+    bad_kind = g.UnitC(7, 1, FAKE, 0, 256, ctypes.cast(wq, P(g.QWeightC)), FAKE,
+                       ctypes.cast(ac, P(ctypes.c_void_p)), 8, 1, ctypes.cast(yc, P(ctypes.c_void_p)))
+    assert L.glowq_path_forward((g.UnitC * 1)(bad_kind), 1, FAKE, 1 << 20, None) == g.ERR_INVALID_ARG
+    assert L.glowq_path_forward(None, 3, FAKE, 1 << 20, None) == g.ERR_INVALID_ARG
