@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Benchmark of the group-shared low-rank corrected W4A16 linear path on one MI355X.
+
+A step is one pass of the whole path over one batch: the 32-layer LLaMA-2-7B-shaped decoder's
+linear units (per layer the QKV group, the o_proj solo, the gate/up group and the down_proj solo)
+at decode T = 1, rank 64, with the restore mask switching the correction on in 16 of the 32
+layers, run through one glowq_path_forward call.  Inputs and weights are seeded synthetic data
+generated on the GPU and resident in HBM before the timed region.
+
+The JSON line also carries the dominant kernel's roofline (the fused decode kernel, measured with
+HIP events on the launch stream), the fp64 CPU oracle timed on a bounded sample, and extra
+measurements: the prefill pass (T = 512), the QKV decode group alone (T = 1, HBM TB/s) and the
+gate/up prefill group (T = 2048, matrix-core TFLOP/s), plus the layerwise baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "corrected-W4 group fwd: tokens/s, HBM TB/s (T=1), MFMA TFLOP/s (T=2048)"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ algorithmic work
+def unit_bytes(T, d, n_outs, r, restore, n_proj=1):
+    """Bytes the path must move for one unit: packed W + (s, z), A_i and B once (or once per
+    module for the layerwise form), X once, Y in fp16."""
+    so = sum(n_outs)
+    b = so * d // 2 + so * (d // 128) * 4 + T * d * 2 + T * so * 2
+    if restore and r > 0:
+        b += so * r * 2 + n_proj * r * d * 2
+    return b
+
+
+def unit_flops(T, d, n_outs, r, restore, n_proj=1):
+    so = sum(n_outs)
+    f = 2 * T * d * so
+    if restore and r > 0:
+        f += n_proj * 2 * T * d * r + 2 * T * r * so
+    return f
+
+
+# ------------------------------------------------------------------ workload on the GPU
+def build_path(T, device, keep_layers=(), layerwise=False):
+    import torch
+    import workload as W
+    from rank_error_compensation_amd import glowq as g
+
+    units, descr, keep = [], [], {}
+    mask = None
+    t0 = time.time()
+    for l in range(W.LLAMA2_7B["n_layers"]):
+        layer_units, mask = W.config3_inputs(T, device=device, layers=[l], layerwise=layerwise)
+        for u in layer_units[l]:
+            qws = [g.QWeight.from_workload(q, device=device) for q in u.weights]
+            ys = [torch.empty(T, q.n_out, dtype=torch.float16, device=device) for q in u.weights]
+            kind = g.UNIT_GROUP if u.kind == "group" else g.UNIT_SOLO
+            pu = g.PathUnit(kind, u.x, qws, u.b, u.a, u.r, u.restore, ys)
+            pu.b_layerwise = u.b_layerwise
+            units.append(pu)
+            descr.append((u.name, T, u.d, u.n_outs, u.r, u.restore))
+        if l in keep_layers:
+            keep[l] = layer_units[l]
+        else:
+            del layer_units
+    torch.cuda.synchronize()
+    log(f"[bench] built T={T} path: {len(units)} units in {time.time() - t0:.1f}s")
+    return units, descr, mask, keep
+
+
+def time_steps(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def call_unit(u, g, ws, layerwise=False):
+    if layerwise and u.kind == g.UNIT_GROUP:
+        return g.layerwise_forward(u.x, u.weights, u.b_layerwise, u.a, u.r, u.restore, workspace=ws, y=u.y)
+    if u.kind == g.UNIT_SOLO:
+        return g.solo_forward(u.x, u.weights[0], u.b, u.a[0], u.r, u.restore, workspace=ws, y=u.y[0])
+    return g.group_forward(u.x, u.weights, u.b, u.a, u.r, u.restore, workspace=ws, y=u.y)
+
+
+def per_launch_events(units, descr, g, reps, layerwise=False):
+    """Average device time of each unit's launch, from HIP events recorded on the launch stream
+    around every call (one kernel per decode call)."""
+    import torch
+    n_proj = max(len(u.weights) for u in units) if layerwise else 1
+    ws = g.make_workspace(max(u.x.shape[0] for u in units), max(u.r for u in units), n_proj)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in units]
+    tot = [0.0] * len(units)
+    for _ in range(2):
+        for u in units:
+            call_unit(u, g, ws, layerwise)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        for (e0, e1), u in zip(ev, units):
+            e0.record(stream)
+            call_unit(u, g, ws, layerwise)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        for i, (e0, e1) in enumerate(ev):
+            tot[i] += e0.elapsed_time(e1) * 1e-3
+    return [t / reps for t in tot]
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+def cpu_baseline(keep, mask):
+    """The fp64 oracle on a bounded sample of the same workload: one restored and one
+    unrestored layer of the T = 1 path (weights copied from the GPU), scaled to 32 layers."""
+    from oracle import glowq_ref as G
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas_threads = 1
+    import torch
+    t_layers = []
+    for l, units in keep.items():
+        cpu_units = []
+        for u in units:
+            for q in u.weights:
+                q.q_packed = q.q_packed.cpu()
+                q.s = q.s.cpu()
+                q.z = q.z.cpu()
+            u.x = u.x.cpu()
+            u.a = [a.cpu() for a in u.a]
+            u.b = u.b.cpu()
+            cpu_units.append(u)
+        t0 = time.perf_counter()
+        G.path_forward({l: cpu_units}, mask)
+        t_layers.append(time.perf_counter() - t0)
+    t_pair = sum(t_layers)
+    per_token = t_pair * (32 / len(t_layers))
+    return {"value": round(1.0 / per_token, 4), "unit": "tokens/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle on layers {sorted(keep)} (restored {[bool(mask[l]) for l in sorted(keep)]}) "
+                      f"of the T=1 path, {t_pair:.1f}s, scaled x{32 // len(t_layers)} to the 32-layer step; "
+                      f"BLAS threads {blas_threads}, dequantisation single-threaded numpy"}
+
+
+# ------------------------------------------------------------------ extra measurements
+def rotating_group(T, copies, g, device):
+    """Config-1 QKV group with `copies` weight copies at distinct addresses (more than twice the
+    256 MB last-level cache), cycled so that each call streams its weights from HBM."""
+    import torch
+    import workload as W
+    u = W.config1_unit(T, device=device)
+    base = [g.QWeight.from_workload(q, device=device) for q in u.weights]
+    sets = [base] + [[g.QWeight(w.q.clone(), w.sz.clone(), w.n_out, w.k_in) for w in base]
+                     for _ in range(copies - 1)]
+    a_sets = [u.a] + [[a.clone() for a in u.a] for _ in range(copies - 1)]
+    ys = [torch.empty(T, w.n_out, dtype=torch.float16, device=device) for w in base]
+    return u, sets, a_sets, ys
+
+
+def extra_decode_qkv(g, reps=50):
+    import torch
+    T, copies = 1, 20
+    u, sets, a_sets, ys = rotating_group(T, copies, g, "cuda")
+    ws = g.make_workspace(T, u.r)
+    stream = torch.cuda.current_stream()
+    for i in range(copies):
+        g.group_forward(u.x, sets[i], u.b, a_sets[i], u.r, True, workspace=ws, y=ys)
+    torch.cuda.synchronize()
+    evs = []
+    for k in range(reps * copies):
+        i = k % copies
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.group_forward(u.x, sets[i], u.b, a_sets[i], u.r, True, workspace=ws, y=ys)
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ts = [e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs]
+    t = statistics.median(ts)
+    nb = unit_bytes(T, 4096, u.n_outs, u.r, True)
+    return {"workload": "llama2-7b QKV group decode T=1 r=64 (20 rotating weight copies)",
+            "us_median": round(t * 1e6, 3), "tokens_per_s": round(T / t, 1),
+            "alg_bytes": nb, "TB_per_s": round(nb / t / 1e12, 4), "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4)}
+
+
+def extra_prefill_gateup(g, reps=20):
+    import torch
+    import workload as W
+    T = 2048
+    u = W.config2_unit(T, device="cuda", layerwise=True)
+    w = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
+    ws = g.make_workspace(T, u.r, 2)
+    ys = [torch.empty(T, q.n_out, dtype=torch.float16, device="cuda") for q in w]
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, fn in (("group", lambda: g.group_forward(u.x, w, u.b, u.a, u.r, True, workspace=ws, y=ys)),
+                     ("layerwise", lambda: g.layerwise_forward(u.x, w, u.b_layerwise, u.a, u.r, True,
+                                                               workspace=ws, y=ys))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        fl = unit_flops(T, 4096, u.n_outs, u.r, True, 1 if name == "group" else 2)
+        out[name] = {"us": round(t * 1e6, 2), "tokens_per_s": round(T / t, 1),
+                     "alg_TFLOP_per_s": round(unit_flops(T, 4096, u.n_outs, u.r, True) / t / 1e12, 2),
+                     "frac_mfma_f16_peak": round(unit_flops(T, 4096, u.n_outs, u.r, True) / t / 1e12 / 2500.0, 4),
+                     "flops_executed": fl}
+    out["workload"] = "llama2-7b gate/up group prefill T=2048 r=64 (one call: projection + grouped GEMM)"
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--event-reps", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from rank_error_compensation_amd import glowq as g
+    g.lib()
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    # ---- headline: 32-layer path, decode T = 1
+    T = 1
+    units, descr, mask, keep = build_path(T, dev, keep_layers=())
+    first_off = next(l for l in range(32) if not mask[l])
+    first_on = next(l for l in range(32) if mask[l])
+    plan = g.PathPlan(units)
+    elapsed = time_steps(plan.run, args.steps, args.warmup)
+    ms = elapsed / args.steps * 1e3
+    value = T * args.steps / elapsed
+    log(f"[bench] decode path: {ms * 1e3:.1f} us/step, {value:.1f} tokens/s")
+
+    # ---- dominant kernel: the fused decode kernel, one launch per unit
+    durs = per_launch_events(units, descr, g, args.event_reps)
+    nbytes = [unit_bytes(t, d, no, r, rs) for (_, t, d, no, r, rs) in descr]
+    achieved = sum(nbytes) / sum(durs) / 1e9
+    kernel_sum_ms = sum(durs) * 1e3
+    per_kind = {}
+    for (name, t, d, no, r, rs), du, nb in zip(descr, durs, nbytes):
+        k = f"{name}{'' if rs else '(no-restore)'}"
+        e = per_kind.setdefault(k, {"launches": 0, "us": 0.0, "bytes": nb})
+        e["launches"] += 1
+        e["us"] += du * 1e6
+    for k, e in per_kind.items():
+        e["us"] = round(e["us"] / e["launches"], 3)
+        e["GB_per_s"] = round(e["bytes"] / (e["us"] * 1e-6) / 1e9, 1)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "glowq::decode_kernel<1>",
+                "per_launch_alg_bytes_mean": int(sum(nbytes) / len(nbytes)),
+                "per_launch_us_mean": round(sum(durs) / len(durs) * 1e6, 3),
+                "kernel_sum_ms_per_step": round(kernel_sum_ms, 4), "per_unit": per_kind}
+    log(f"[bench] decode kernel: {achieved:.0f} GB/s over {len(durs)} launches, kernel sum {kernel_sum_ms:.3f} ms")
+
+    # ---- layerwise baseline on the same path
+    extra = {}
+    if not args.no_extras:
+        del plan
+        units_lw, descr_lw, _, _ = build_path(T, dev, layerwise=True)
+        ws_lw = g.make_workspace(T, 64, 3)
+
+        def run_lw():
+            for u in units_lw:
+                call_unit(u, g, ws_lw, layerwise=True)
+
+        def run_grp():
+            for u in units_lw:
+                call_unit(u, g, ws_lw, layerwise=False)
+
+        t_lw = time_steps(run_lw, args.steps, args.warmup) / args.steps
+        t_gr = time_steps(run_grp, args.steps, args.warmup) / args.steps
+        d_lw = sum(per_launch_events(units_lw, descr_lw, g, args.event_reps, layerwise=True))
+        d_gr = sum(per_launch_events(units_lw, descr_lw, g, args.event_reps, layerwise=False))
+        extra["layerwise_vs_group_T1_path"] = {
+            "group_us_per_step_percall": round(t_gr * 1e6, 1), "layerwise_us_per_step_percall": round(t_lw * 1e6, 1),
+            "group_kernel_sum_us": round(d_gr * 1e6, 1), "layerwise_kernel_sum_us": round(d_lw * 1e6, 1),
+            "kernel_speedup": round(d_lw / d_gr, 4)}
+        del units_lw
+        torch.cuda.empty_cache()
+        log(f"[bench] layerwise {d_lw * 1e6:.1f} us vs group {d_gr * 1e6:.1f} us (kernel sums)")
+
+        # prefill pass
+        units_p, descr_p, _, _ = build_path(512, dev)
+        plan_p = g.PathPlan(units_p)
+        ksteps = max(3, args.steps // 10)
+        ep = time_steps(plan_p.run, ksteps, 2)
+        tp = ep / ksteps
+        fl = sum(unit_flops(t, d, no, r, rs) for (_, t, d, no, r, rs) in descr_p)
+        extra["prefill_path_T512"] = {"ms_per_step": round(tp * 1e3, 3), "tokens_per_s": round(512 / tp, 1),
+                                      "alg_TFLOP_per_s": round(fl / tp / 1e12, 2),
+                                      "frac_mfma_f16_peak": round(fl / tp / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+        log(f"[bench] prefill path T=512: {tp * 1e3:.3f} ms, {fl / tp / 1e12:.1f} TFLOP/s")
+        del plan_p, units_p
+        torch.cuda.empty_cache()
+        extra["decode_qkv_T1"] = extra_decode_qkv(g)
+        log(f"[bench] QKV decode T=1: {extra['decode_qkv_T1']}")
+        extra["prefill_gateup_T2048"] = extra_prefill_gateup(g)
+        log(f"[bench] gate/up prefill T=2048: {extra['prefill_gateup_T2048']}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import glowq_ref  # noqa: F401  (oracle only in the CPU-baseline leg)
+        _, _, mask2, keep = build_path_keep(T, dev, [first_on, first_off])
+        cpu = cpu_baseline(keep, mask2)
+        log(f"[bench] cpu oracle: {cpu}")
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "llama2-7b-32-layer-linear-path decode T=1 r=64 restore=16/32 layers",
+                   "T": 1, "r": 64, "layers": 32, "d": 4096, "inter": 11008,
+                   "units_per_step": len(descr), "weights": "INT4-g128 fp16 scale/zero"},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def build_path_keep(T, device, layers):
+    """Only the requested layers of the path (for the CPU oracle sample)."""
+    import workload as W
+    keep, mask = {}, None
+    for l in layers:
+        lu, mask = W.config3_inputs(T, device=device, layers=[l])
+        keep[l] = lu[l]
+    return None, None, mask, keep
+
+
+if __name__ == "__main__":
+    main()

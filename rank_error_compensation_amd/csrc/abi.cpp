@@ -107,7 +107,7 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
     const int32_t rp = (int32_t)r_pad_of(c.r);
     void* R = c.correct ? static_cast<uint8_t*>(workspace) + kWsHeader : nullptr;
 
-    if (c.correct) {
+    if (c.correct && prefill) {
         ProjArgs p;
         std::memset(&p, 0, sizeof(p));
         p.x = static_cast<const _Float16*>(c.x);
@@ -118,8 +118,7 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
         p.n_proj = c.n_proj;
         for (int i = 0; i < c.n_proj; ++i) p.b[i] = static_cast<const _Float16*>(c.b[i]);
         p.R = R;
-        const hipError_t e = prefill ? launch_proj_prefill(p, stream) : launch_proj_decode(p, stream);
-        if (e != hipSuccess) return GLOWQ_ERR_HIP;
+        if (launch_proj_prefill(p, stream) != hipSuccess) return GLOWQ_ERR_HIP;
     }
 
     ForwardArgs f;
@@ -132,6 +131,14 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
     f.r_pad = c.correct ? rp : 0;
     f.n_mod = c.m;
     f.R = R;
+    f.sync = c.correct ? static_cast<int32_t*>(workspace) : nullptr;
+    f.n_proj = c.n_proj;
+    for (int i = 0; i < c.n_proj; ++i) f.b[i] = c.correct ? static_cast<const _Float16*>(c.b[i]) : nullptr;
+    if (c.correct && !prefill) {
+        const int64_t total = (int64_t)c.n_proj * c.r;
+        f.prod_rows = (int32_t)ceil_div(total, kMaxProducers);
+        f.n_prod = (int32_t)ceil_div(total, f.prod_rows);
+    }
     int tt = 0, rr = 0;
     if (prefill) choose_prefill_shape(c, tt, rr);
     f.tile_tt = tt;

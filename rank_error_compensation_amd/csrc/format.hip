@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
     const uint32_t zs = szd[blk * 16 + (l & 15)];
     h2 c1024, c64;
     zero_consts(zs, c1024, c64);
-    const h8 dq = nib8_minus_z(qd[idx], c1024, c64);
+    const h8 dq = nib8_minus_z(qd[idx], c1024, c64, nib_consts());
     const _Float16 s = as_h2(zs)[1];
     if (DTYPE == 0) {
         float* o = reinterpret_cast<float*>(out) + row * k_in + k0;

@@ -30,7 +30,20 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 constexpr int kGroup = 128;
 constexpr int kMaxModules = 8;
 constexpr int kMaxRank = 256;
-constexpr size_t kWsHeader = 256;  // workspace bytes reserved for synchronisation words
+constexpr size_t kWsHeader = 2048;  // workspace bytes reserved for synchronisation words
+// Synchronisation words of the decode hand-off, int32 offsets into the workspace header.  One
+// ready/done pair per XCD (workgroup b polls the pair of XCD b % 8), each on its own 64-byte line,
+// so that no single address is hammered by every workgroup of the launch.
+constexpr int kXcds = 8;
+constexpr int kSyncReady = 0;    // ready[x] at word kSyncReady + 16 x: producers done, as seen by XCD x
+constexpr int kSyncDone = 128;   // done[x]  at word kSyncDone + 16 x: consumers of XCD x past the epilogue
+constexpr int kSyncError = 256;  // nonzero when a bounded wait expired (results invalid)
+constexpr int kSpinLimit = 1 << 20;
+constexpr int kMaxProducers = 64;
+// Largest activation block (T x d fp16 bytes) the decode kernel stages in LDS, and the matching
+// number of 16-byte staging loads per thread.
+constexpr size_t kDecodeXLdsMax = 32 * 1024;
+constexpr int kDecodeXChunks = kDecodeXLdsMax / 16 / 256;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -38,15 +51,28 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Bit masks of the nibble unpacking, held in VGPRs so that each mask-and-or is one v_and_or_b32
+// (a VALU instruction can read only one scalar constant on this architecture).
+struct NibConsts {
+    uint32_t lo, hi, magic;
+};
+__device__ __forceinline__ NibConsts nib_consts() {
+    NibConsts n;
+    asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(n.lo));
+    asm volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(n.hi));
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(n.magic));
+    return n;
+}
+
 // Eight nibbles of one device-layout word -> the eight integer differences (q - z) as fp16,
 // exact for integer z in [-1024, 1024]: 0x6400 | q is the fp16 value 1024 + q, 0x6400 | (q << 4)
 // is 1024 + 16 q; subtracting 1024 + z (resp. scaling by 1/16 and subtracting 64 + z) is exact.
-__device__ __forceinline__ h8 nib8_minus_z(uint32_t w, h2 zc1024, h2 zc64) {
+__device__ __forceinline__ h8 nib8_minus_z(uint32_t w, h2 zc1024, h2 zc64, const NibConsts& n) {
     const uint32_t lo = w, hi = w >> 8;
-    const h2 p0 = as_h2((lo & 0x000F000Fu) | 0x64006400u);
-    const h2 p1 = as_h2((lo & 0x00F000F0u) | 0x64006400u);
-    const h2 p2 = as_h2((hi & 0x000F000Fu) | 0x64006400u);
-    const h2 p3 = as_h2((hi & 0x00F000F0u) | 0x64006400u);
+    const h2 p0 = as_h2((lo & n.lo) | n.magic);
+    const h2 p1 = as_h2((lo & n.hi) | n.magic);
+    const h2 p2 = as_h2((hi & n.lo) | n.magic);
+    const h2 p3 = as_h2((hi & n.hi) | n.magic);
     const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     const h2 d0 = p0 - zc1024;
     const h2 d1 = p1 * sixteenth - zc64;
@@ -97,7 +123,13 @@ struct ForwardArgs {
     int32_t m_tiles;     // token tiles (prefill)
     int32_t tile_tt;     // prefill tile shape: 16-token tiles per wave
     int32_t tile_rr;     // prefill tile shape: 16-row tiles per wave (4 waves side by side)
-    const void* R;       // projections: decode fp32 [n_proj][T][r]; prefill fp16 [n_proj][T][r_pad]
+    void* R;             // projections: decode fp32 [n_proj][T][r]; prefill fp16 [n_proj][T][r_pad]
+    int32_t* sync;       // workspace header (decode)
+    int32_t n_proj;      // projections (1 shared, m layerwise)
+    int32_t n_prod;      // decode: producer workgroups forming R (0 without correction)
+    int32_t prod_rows;   // decode: stacked projection rows per producer
+    int32_t r_lds_off;   // decode: byte offset of the R copy in dynamic LDS (set by the launcher)
+    const _Float16* b[kMaxModules];  // [r][d] right factors, one per projection
     ModuleArgs mod[kMaxModules];
 };
 
@@ -115,7 +147,6 @@ hipError_t launch_repack(const uint32_t* qc, const _Float16* s, const _Float16* 
 hipError_t launch_flag_clear(int32_t* flag, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sz, int64_t n_out, int64_t k_in, void* out,
                           int dtype, hipStream_t stream);
-hipError_t launch_proj_decode(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_proj_prefill(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);

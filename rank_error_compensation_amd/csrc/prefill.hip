@@ -48,8 +48,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const ForwardArgs args)
     pick_module_p(args, nbl, M);
     const int nb = nbl - M.tile_begin;
     const int m0 = mb * BM;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = args.T, d = args.d, G = args.G;
+    const NibConsts nc = nib_consts();
     const int kofs = 8 * (lane >> 4);
     const int rt0 = nb * 4 * RR + wave * RR;
 
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const ForwardArgs args)
         for (int j = 0; j < 4; ++j) {
             h8 a[RR];
 #pragma unroll
-            for (int rr = 0; rr < RR; ++rr) a[rr] = nib8_minus_z(qv[rr][j], c1024[rr], c64[rr]) * s8[rr];
+            for (int rr = 0; rr < RR; ++rr) a[rr] = nib8_minus_z(qv[rr][j], c1024[rr], c64[rr], nc) * s8[rr];
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
                 const h8 b = *reinterpret_cast<const h8*>(xb + tt * 16 * LS + 32 * j);

@@ -42,9 +42,10 @@ def test_buffer_sizes():
     assert L.glowq_q_bytes(16, 100) == 0 and L.glowq_q_bytes(0, 128) == 0
     assert L.glowq_workspace_bytes(0, 64, 1) == 0
     assert L.glowq_workspace_bytes(4, 0, 1) == 0
-    assert L.glowq_workspace_bytes(1, 64, 1) == 256 + 256
-    assert L.glowq_workspace_bytes(2048, 64, 1) == 256 + 2048 * 64 * 4
-    assert L.glowq_workspace_bytes(100, 8, 3) == 256 + ((100 * 32 * 2 * 3 + 255) // 256) * 256
+    hdr = 2048  # synchronisation words of the decode hand-off
+    assert L.glowq_workspace_bytes(1, 64, 1) == hdr + 256
+    assert L.glowq_workspace_bytes(2048, 64, 1) == hdr + 2048 * 64 * 4
+    assert L.glowq_workspace_bytes(100, 8, 3) == hdr + ((100 * 32 * 2 * 3 + 255) // 256) * 256
 
 
 FAKE = 0x10000  # 64 KiB-aligned fake device address: never dereferenced, validation fails first

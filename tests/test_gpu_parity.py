@@ -207,3 +207,23 @@ def test_config2_prefill():
     for i, (a, b) in enumerate(zip(yd, ys)):
         e = G.parity_errors(a.float().cpu().numpy(), b[:64].float().cpu().numpy().astype(np.float64))
         assert e["rel_fro"] <= 1e-3, (i, e)
+
+
+def test_decode_workspace_left_clean():
+    """The fused decode kernel's producer/consumer words are back to zero after every call and
+    no bounded wait expired (the 2 KiB workspace header is all zero)."""
+    g = glowq()
+    keys = (10,)
+    for T, lw in ((1, False), (7, True), (64, False)):
+        x = W.make_x(T, 512, 1.19, keys)
+        unit = W.make_unit("g", "group", x, [64, 40, 32], 24, keys, layerwise=True)
+        du = DevUnit(unit, layerwise=True)
+        ws = g.make_workspace(T, 24, 3)
+        for _ in range(3):
+            if lw:
+                g.layerwise_forward(du.x, du.w, du.b_lw, du.a, 24, True, workspace=ws)
+            else:
+                g.group_forward(du.x, du.w, du.b, du.a, 24, True, workspace=ws)
+        torch.cuda.synchronize()
+        hdr = ws[:2048].view(torch.int32).cpu()
+        assert int(hdr.abs().sum()) == 0, hdr.nonzero()
