@@ -23,6 +23,17 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 
 inline int64_t r_pad_of(int32_t r) { return ceil_div(r, 32) * 32; }
 
+// Workspace after the header: the decode projection as (fp32, tag) pairs, then the prefill
+// projection in fp16 with rows padded to 32.  The two never share bytes, so tags left by a decode
+// call can never be confused with a prefill call's data.
+inline size_t round256(size_t n) { return (n + 255u) / 256u * 256u; }
+inline size_t decode_r_bytes(int64_t T, int32_t r, int32_t n_proj) {
+    return round256((size_t)T * (size_t)r * 8u * (size_t)n_proj);
+}
+inline size_t prefill_r_bytes(int64_t T, int32_t r, int32_t n_proj) {
+    return round256((size_t)T * (size_t)r_pad_of(r) * 2u * (size_t)n_proj);
+}
+
 // Everything needed to launch one group / solo / layerwise call.
 struct Call {
     const void* x;
@@ -105,7 +116,11 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
     if (c.T == 0) return GLOWQ_OK;
     const bool prefill = c.T > kDecodeMaxT;
     const int32_t rp = (int32_t)r_pad_of(c.r);
-    void* R = c.correct ? static_cast<uint8_t*>(workspace) + kWsHeader : nullptr;
+    void* R = nullptr;
+    if (c.correct) {
+        uint8_t* base = static_cast<uint8_t*>(workspace) + kWsHeader;
+        R = prefill ? base + decode_r_bytes(c.T, c.r, c.n_proj) : base;
+    }
 
     if (c.correct && prefill) {
         ProjArgs p;
@@ -143,6 +158,15 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
     if (prefill) choose_prefill_shape(c, tt, rr);
     f.tile_tt = tt;
     f.tile_rr = rr;
+    int dec_rt = 1;
+    if (!prefill) {
+        int64_t total16 = 0;
+        for (int i = 0; i < c.m; ++i) total16 += ceil_div(c.w[i].n_out, 16);
+        const bool xlds = c.T <= 16 && (size_t)(c.T + 1) * (size_t)c.d * 2u <= kDecodeXLdsMax;
+        f.dec_kw = (total16 <= kDecodeWide8Tiles && f.G >= kDecodeWide8Groups) ? 8 : 4;
+        dec_rt = (f.dec_kw == 4 && xlds && total16 > kDecodeRt2Tiles) ? 2 : 1;
+        f.dec_rt = dec_rt;
+    }
     int64_t tiles = 0;
     for (int i = 0; i < c.m; ++i) {
         ModuleArgs& M = f.mod[i];
@@ -154,7 +178,7 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
         M.n_tiles16 = (int32_t)ceil_div(c.w[i].n_out, 16);
         M.tile_begin = (int32_t)tiles;
         M.proj = c.n_proj > 1 ? i : 0;
-        tiles += prefill ? ceil_div(M.n_tiles16, 4 * rr) : M.n_tiles16;
+        tiles += prefill ? ceil_div(M.n_tiles16, 4 * rr) : ceil_div(M.n_tiles16, dec_rt);
     }
     hipError_t e;
     if (prefill) {
@@ -220,11 +244,7 @@ size_t glowq_sz_bytes(int64_t n_out, int64_t k_in) {
 
 size_t glowq_workspace_bytes(int64_t T, int32_t r, int32_t n_proj) {
     if (T <= 0 || r <= 0 || n_proj <= 0) return 0;
-    const size_t per_dec = (size_t)T * (size_t)r * 4u;
-    const size_t per_pre = (size_t)T * (size_t)r_pad_of(r) * 2u;
-    const size_t per = per_dec > per_pre ? per_dec : per_pre;
-    const size_t body = ((per * (size_t)n_proj) + 255u) / 256u * 256u;
-    return kWsHeader + body;
+    return kWsHeader + decode_r_bytes(T, r, n_proj) + prefill_r_bytes(T, r, n_proj);
 }
 
 int glowq_repack(const void* q_canon_dev, const void* scales_dev, const void* zeros_dev, int64_t n_out,

@@ -5,15 +5,15 @@
 //   y_i = X W_hat_i^T + R_p A_i^T,   R_p = X B_p^T  (p = 0 for the shared factor)
 // (GlowQ paper note, key design 4 and the flowchart's last node: the anchor forms R once, every
 // module consumes it).  In this launch the anchor's role is played by the first n_prod
-// workgroups ("producers"): they compute R in fp32 into the workspace and publish it with an
-// agent-scope release.  The other workgroups ("consumers") each own one 16-row tile of the
-// concatenated modules: they stream their INT4 weights first and look at R only for the
-// epilogue, so the projection overlaps the weight stream.  Producers have the lowest workgroup
-// ids and never wait, so they are dispatched before any consumer and always finish; every wait is
-// bounded and raises a flag in the workspace header if it expires.  The hand-off counters are
-// replicated per XCD (consumer b uses copy b % 8) so that polls and arrivals spread over eight
-// addresses; the last consumer of each copy resets it, leaving the workspace ready for the next
-// call without a memset.
+// workgroups ("producers"): they compute R in fp32 and write it to the workspace as (value, tag)
+// pairs, each pair one 64-bit store, the tag being the call's epoch + 1.  The other workgroups
+// ("consumers") each own one 16-row tile of the concatenated modules: they stream their INT4
+// weights first and read R only for the epilogue, polling the pairs themselves until every tag is
+// current -- one coherent read both waits for and fetches R, and producers need no fence or
+// counter.  Producers have the lowest workgroup ids and never wait, so they are dispatched before
+// any consumer and always finish; every wait is bounded and raises a flag in the workspace header
+// if it expires.  The last consumer of the call advances the epoch (arrival counters replicated
+// per XCD, then one counter over the XCDs), so stale pairs never match and no memset is needed.
 //
 // Main loop: the K dimension (input groups of 128) is split across the 4 wavefronts of a tile
 // (group g goes to wave g % 4).  Each wave keeps a ring of U groups in flight: one 16-byte load
@@ -48,17 +48,45 @@ __device__ __forceinline__ int count_mod8(int lo, int hi, int x) {
     return first < hi ? (hi - 1 - first) / 8 + 1 : 0;
 }
 
+typedef unsigned long long u64;
+
+__device__ __forceinline__ uint32_t load_epoch(const ForwardArgs& a) {
+    return (uint32_t)__hip_atomic_load(a.sync + kSyncEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_pair(u64* p, float v, uint32_t tag) {
+    const u64 w = ((u64)tag << 32) | (u64)__builtin_bit_cast(uint32_t, v);
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait (bounded) until pair p carries `tag`, then return its value.
+__device__ __forceinline__ float load_pair(const ForwardArgs& a, const u64* p, uint32_t tag) {
+    u64 w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int spins = 0;
+    while ((uint32_t)(w >> 32) != tag) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+            __hip_atomic_fetch_or(a.sync + kSyncError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return __builtin_bit_cast(float, (uint32_t)w);
+}
+
 // Producer workgroup: rows [p * prod_rows, (p+1) * prod_rows) of the stacked projections
 // (row jj = projection jj / r, rank index jj % r), all tokens; fp32 accumulation of exact fp16
-// products, fixed-order block reduction.  Only wave 0 stores R (threads 0..15), so only wave 0
-// issues the agent-scope release before the counters are bumped.
+// products, fixed-order block reduction, each value stored as a tagged pair.
+template <int KW>
 __device__ void produce(const ForwardArgs& a, int p) {
     constexpr int C = 4;  // 8-input chunks per thread in flight
-    __shared__ float part[4][16];
+    constexpr int NTH = 64 * KW;
+    __shared__ float part[KW][16];
+    const uint32_t tag = load_epoch(a) + 1u;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int T = a.T, d = a.d, r = a.r;
-    float* R = reinterpret_cast<float*>(a.R);
+    u64* R = reinterpret_cast<u64*>(a.R);
     const int total = a.n_proj * r;
     const int j0 = p * a.prod_rows;
     const int j1 = min(j0 + a.prod_rows, total);
@@ -71,11 +99,11 @@ __device__ void produce(const ForwardArgs& a, int p) {
             float acc[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) acc[t] = 0.f;
-            for (int c0 = threadIdx.x; c0 < n8; c0 += 256 * C) {
+            for (int c0 = threadIdx.x; c0 < n8; c0 += NTH * C) {
                 h8 bv[C];
 #pragma unroll
                 for (int k = 0; k < C; ++k) {
-                    const int c = min(c0 + 256 * k, n8 - 1);
+                    const int c = min(c0 + NTH * k, n8 - 1);
                     bv[k] = load_h8(brow + 8 * c);
                 }
 #pragma unroll
@@ -84,13 +112,13 @@ __device__ void produce(const ForwardArgs& a, int p) {
                         h8 xv[C];
 #pragma unroll
                         for (int k = 0; k < C; ++k) {
-                            const int c = min(c0 + 256 * k, n8 - 1);
+                            const int c = min(c0 + NTH * k, n8 - 1);
                             xv[k] = load_h8(a.x + (size_t)(t0 + t) * d + 8 * c);
                         }
                         float s = acc[t];
 #pragma unroll
                         for (int k = 0; k < C; ++k) {
-                            if (c0 + 256 * k < n8) {
+                            if (c0 + NTH * k < n8) {
 #pragma unroll
                                 for (int e = 0; e < 8; ++e) s = fmaf((float)bv[k][e], (float)xv[k][e], s);
                             }
@@ -115,93 +143,84 @@ __device__ void produce(const ForwardArgs& a, int p) {
             __syncthreads();
             if (threadIdx.x < 16 && (int)threadIdx.x < nt) {
                 const int t = threadIdx.x;
-                R[((size_t)pi * T + t0 + t) * r + j] = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+                float v = part[0][t];
+#pragma unroll
+                for (int w = 1; w < KW; ++w) v += part[w][t];
+                store_pair(R + ((size_t)pi * T + t0 + t) * r + j, v, tag);
             }
             __syncthreads();
         }
     }
-    if (wave == 0) {
-        // R stores of this wave become visible at agent scope before the counters move
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        if (lane == 0) {
-            const int lo = a.n_prod, hi = a.n_prod + a.n_tiles;
-#pragma unroll
-            for (int x = 0; x < kXcds; ++x)
-                if (count_mod8(lo, hi, x) > 0)
-                    __hip_atomic_fetch_add(a.sync + kSyncReady + 16 * x, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
 }
 
-// Consumer side of the hand-off.  Thread 0 polls its XCD's counter with agent-scope relaxed loads
-// (coherent loads, no cache maintenance per poll); R is then read with agent-scope relaxed atomic
-// loads, which are served from the coherence point, so no workgroup invalidates its caches.  The
-// R loads are issued only after the counter value has come back (control dependence; a wavefront
-// issues its memory operations in order), and every producer made its R stores visible at agent
-// scope before incrementing the counters.
-__device__ __forceinline__ void wait_ready(const ForwardArgs& a) {
-    if (threadIdx.x == 0) {
-        const int* ready = a.sync + kSyncReady + 16 * (blockIdx.x & 7);
-        int spins = 0;
-        while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_prod) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins > kSpinLimit) {
-                __hip_atomic_fetch_or(a.sync + kSyncError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-        }
-    }
-    __syncthreads();
-}
-
-__device__ __forceinline__ float load_r(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
+// End of a consumer: count arrivals per XCD, then over XCDs; the very last consumer of the call
+// resets the counters and advances the epoch.  Every consumer has read the epoch and every
+// producer has written its pairs before the last arrival, so the advance is seen by no one in
+// this call.
 __device__ __forceinline__ void signal_done(const ForwardArgs& a) {
     __syncthreads();
     if (threadIdx.x == 0) {
+        const int lo = a.n_prod, hi = a.n_prod + a.n_tiles;
         const int x = blockIdx.x & 7;
-        const int n = count_mod8(a.n_prod, a.n_prod + a.n_tiles, x);
+        const int n = count_mod8(lo, hi, x);
         const int prev = __hip_atomic_fetch_add(a.sync + kSyncDone + 16 * x, 1, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == n - 1) {  // last consumer of this copy: every wait on it is over
-            __hip_atomic_store(a.sync + kSyncReady + 16 * x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == n - 1) {
             __hip_atomic_store(a.sync + kSyncDone + 16 * x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            int n_x = 0;
+#pragma unroll
+            for (int k = 0; k < kXcds; ++k) n_x += count_mod8(lo, hi, k) > 0;
+            const int top = __hip_atomic_fetch_add(a.sync + kSyncTop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (top == n_x - 1) {
+                __hip_atomic_store(a.sync + kSyncTop, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(a.sync + kSyncEpoch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
 }
 
-// NTT: 16-token tiles.  XC > 0: the tokens' activations (T x d fp16, at most kDecodeXLdsMax bytes)
-// are staged once in LDS with XC 16-byte loads per thread, issued before the weight loads so that
-// waiting for them does not wait for the weights; lanes of padding tokens read an all-zero LDS row,
-// so the B operand needs no masking.  XC == 0: each group's B operand is loaded from global memory
-// together with the group's weights.
-template <int NTT, int XC>
-__global__ __launch_bounds__(256) void decode_kernel(const ForwardArgs args) {
+// NTT: 16-token tiles.  RT: 16-row tiles per workgroup, multiplied side by side against the same
+// activation operand (one workgroup per RT tiles of one module).  KW: waves per workgroup; K (the
+// 128-input groups) is split across them, group g going to wave g % KW.
+// XC > 0: the tokens' activations (T x d fp16, at most kDecodeXLdsMax bytes) are staged once in
+// LDS with XC 16-byte loads per thread, issued before the weight loads so that waiting for them
+// does not wait for the weights; lanes of padding tokens read an all-zero LDS row, so the B operand
+// needs no masking.  XC == 0: each group's B operand is loaded from global memory together with
+// the group's weights.
+template <int NTT, int XC, int KW, int RT>
+__global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0 && KW == 4) ? (RT == 2 ? 3 : 4) : 1))) void decode_kernel(const ForwardArgs args) {
     constexpr bool XLDS = XC > 0;
-    constexpr int U = XLDS ? 8 : (NTT == 1 ? 4 : (NTT == 2 ? 2 : 1));  // ring of groups per wave
-    __shared__ f4 red[4][NTT][64];
+    constexpr int NTH = 64 * KW;
+    constexpr int U = XLDS ? 8 / RT : (NTT == 1 ? 4 / RT : 1);  // ring of groups per wave
+    static_assert(U >= 1, "ring");
+    __shared__ f4 red[KW][RT][NTT][64];
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
 
     if ((int)blockIdx.x < args.n_prod) {
-        produce(args, blockIdx.x);
+        produce<KW>(args, blockIdx.x);
         return;
     }
     const int tile = blockIdx.x - args.n_prod;
     ModuleArgs M;
     pick_module(args, tile, M);
-    const int rt = tile - M.tile_begin;
+    const int rt0 = (tile - M.tile_begin) * RT;  // first 16-row tile of this workgroup
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
     const int G = args.G, T = args.T, d = args.d;
-    const uint8_t* qbase = M.q + (size_t)rt * G * 1024 + lane * 16;
-    const uint8_t* szbase = M.sz + (size_t)rt * G * 64;
+    const uint8_t* qbase[RT];
+    const uint8_t* szbase[RT];
+#pragma unroll
+    for (int rr = 0; rr < RT; ++rr) {
+        const int rt = min(rt0 + rr, M.n_tiles16 - 1);  // a tile past the module end rereads the last
+        qbase[rr] = M.q + (size_t)rt * G * 1024 + lane * 16;
+        szbase[rr] = M.sz + (size_t)rt * G * 64;
+    }
     const int kofs = 8 * (lane >> 4);
     const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     const NibConsts nc = nib_consts();
-    const int n_my = G > wave ? (G - wave + 3) / 4 : 0;  // groups of this wave: g = wave + 4 i
+    const int n_my = G > wave ? (G - wave + KW - 1) / KW : 0;  // groups of this wave: g = wave + KW i
+    const bool correct = args.r > 0 && M.a != nullptr;
+    const uint32_t tag = correct ? load_epoch(args) + 1u : 0u;  // read before this call can end
 
     const _Float16* xrow[NTT];
     bool tok_ok[NTT];
@@ -215,25 +234,25 @@ __global__ __launch_bounds__(256) void decode_kernel(const ForwardArgs args) {
             xrow[tt] = args.x + (size_t)(tok_ok[tt] ? t : 0) * d + kofs;
     }
 
-    // activations first: slot c * 256 + tid of the (T + 1) x d LDS block, clamped to the last slot
+    // activations first: slot c * NTH + tid of the (T + 1) x d LDS block, clamped to the last slot
     // (the tail rewrites a slot with its own value); slots past T x d are the zero row.
     const int n8x = T * d / 8, n8 = (T + 1) * d / 8;
     u4 xst[XLDS ? XC : 1];
     if (XLDS) {
 #pragma unroll
         for (int c = 0; c < XC; ++c) {
-            const int idx = min(c * 256 + (int)threadIdx.x, n8 - 1);
+            const int idx = min(c * NTH + (int)threadIdx.x, n8 - 1);
             const u4 v = reinterpret_cast<const u4*>(args.x)[min(idx, n8x - 1)];
             xst[c] = idx < n8x ? v : u4{0u, 0u, 0u, 0u};
         }
     }
 
-    u4 qv[U];
-    uint32_t zso[U];
-    u4 zs4[U];
+    u4 qv[U][RT];
+    uint32_t zso[U][RT];
+    u4 zs4[U][RT];
     h8 bx[XLDS ? 1 : U][NTT][4];
     auto issue = [&](int u, int i) {
-        const int g = min(wave + 4 * i, G - 1);  // always a valid group of this row tile
+        const int g = min(wave + KW * i, G - 1);  // always a valid group of this row tile
         if (!XLDS) {
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt)
@@ -243,33 +262,46 @@ __global__ __launch_bounds__(256) void decode_kernel(const ForwardArgs args) {
                     bx[XLDS ? 0 : u][tt][j] = tok_ok[tt] ? v : zero8;
                 }
         }
-        qv[u] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(qbase + (size_t)g * 1024));
-        zso[u] = *reinterpret_cast<const uint32_t*>(szbase + (size_t)g * 64 + (lane & 15) * 4);
-        zs4[u] = *reinterpret_cast<const u4*>(szbase + (size_t)g * 64 + (lane >> 4) * 16);
+#pragma unroll
+        for (int rr = 0; rr < RT; ++rr) {
+            qv[u][rr] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(qbase[rr] + (size_t)g * 1024));
+            zso[u][rr] = *reinterpret_cast<const uint32_t*>(szbase[rr] + (size_t)g * 64 + (lane & 15) * 4);
+            zs4[u][rr] = *reinterpret_cast<const u4*>(szbase[rr] + (size_t)g * 64 + (lane >> 4) * 16);
+        }
     };
 
-    f4 acc[NTT];
+    f4 acc[RT][NTT];
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) acc[tt] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int rr = 0; rr < RT; ++rr)
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) acc[rr][tt] = f4{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int u, int i) {
-        const int g = wave + 4 * i;
-        h2 c1024, c64;
-        zero_consts(zso[u], c1024, c64);
-        h8 aop[4];
+        const int g = wave + KW * i;
+        h8 aop[RT][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) aop[j] = nib8_minus_z(qv[u][j], c1024, c64, nc);
+        for (int rr = 0; rr < RT; ++rr) {
+            h2 c1024, c64;
+            zero_consts(zso[u][rr], c1024, c64);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) aop[rr][j] = nib8_minus_z(qv[u][rr][j], c1024, c64, nc);
+        }
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
-            f4 part = f4{0.f, 0.f, 0.f, 0.f};
+            f4 part[RT];
+#pragma unroll
+            for (int rr = 0; rr < RT; ++rr) part[rr] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const h8 b = XLDS ? *reinterpret_cast<const h8*>(xrow[tt] + (size_t)g * kGroup + 32 * j)
                                   : bx[XLDS ? 0 : u][tt][j];
-                part = mfma16(aop[j], b, part);
+#pragma unroll
+                for (int rr = 0; rr < RT; ++rr) part[rr] = mfma16(aop[rr][j], b, part[rr]);
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) acc[tt][k] += (float)as_h2(zs4[u][k])[1] * part[k];
+            for (int rr = 0; rr < RT; ++rr)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) acc[rr][tt][k] += (float)as_h2(zs4[u][rr][k])[1] * part[rr][k];
         }
     };
 
@@ -279,7 +311,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const ForwardArgs args) {
     if (XLDS) {
 #pragma unroll
         for (int c = 0; c < XC; ++c) {
-            const int idx = min(c * 256 + (int)threadIdx.x, n8 - 1);
+            const int idx = min(c * NTH + (int)threadIdx.x, n8 - 1);
             reinterpret_cast<u4*>(xs)[idx] = xst[c];
         }
         __syncthreads();
@@ -300,45 +332,47 @@ __global__ __launch_bounds__(256) void decode_kernel(const ForwardArgs args) {
             if (i0 + u < n_my) compute(u, i0 + u);
     }
 
-    // correction epilogue: this wave adds R[t][8c..8c+8) . A[row][8c..8c+8) for chunks c = wave mod 4.
-    // The first A chunks are loaded before waiting for R; with one token tile R is copied once into
-    // LDS (one coherent 4-byte load per thread) and read from there.
-    const bool correct = args.r > 0 && M.a != nullptr;
+    // correction epilogue: this wave adds R[t][8c..8c+8) . A[row][8c..8c+8) for chunks c = wave mod KW.
+    // The first A chunks are loaded before R is needed; with one token tile R is copied once into
+    // LDS (one coherent 8-byte pair load per element, which also waits for the producers) and read
+    // from there.
     if (correct) {
         const int r = args.r;
-        const int row0 = rt * 16 + 4 * (lane >> 4);
         const int nc8 = r / 8;
-        constexpr int PF = 2;  // A chunks prefetched per wave
-        h8 apf[PF][4];
+        constexpr int PF = RT == 1 ? 2 : 1;  // A chunks prefetched per wave
+        h8 apf[PF][RT][4];
 #pragma unroll
         for (int k = 0; k < PF; ++k) {
-            const int c = wave + 4 * k;
+            const int c = wave + KW * k;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = row0 + i;
-                apf[k][i] = (c < nc8 && row < M.n_out) ? load_h8(M.a + (size_t)row * r + 8 * c) : zero8;
-            }
+            for (int rr = 0; rr < RT; ++rr)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = (rt0 + rr) * 16 + 4 * (lane >> 4) + i;
+                    apf[k][rr][i] = (c < nc8 && row < M.n_out) ? load_h8(M.a + (size_t)row * r + 8 * c) : zero8;
+                }
         }
-        wait_ready(args);
-        const float* R = reinterpret_cast<const float*>(args.R) + (size_t)M.proj * T * r;
+        const u64* R = reinterpret_cast<const u64*>(args.R) + (size_t)M.proj * T * r;
         float* rl = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(xs) + args.r_lds_off);
         if (NTT == 1) {
-            for (int k = threadIdx.x; k < T * r; k += 256) rl[k] = load_r(R + k);
+            for (int k = threadIdx.x; k < T * r; k += NTH) rl[k] = load_pair(args, R + k, tag);
             __syncthreads();
         }
-        for (int c = wave, k = 0; c < nc8; c += 4, ++k) {
-            h8 a8[4];
+        for (int c = wave, k = 0; c < nc8; c += KW, ++k) {
+            h8 a8[RT][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (k < PF) {
+            for (int rr = 0; rr < RT; ++rr)
 #pragma unroll
-                    for (int kk = 0; kk < PF; ++kk)
-                        if (kk == k) a8[i] = apf[kk][i];
-                } else {
-                    const int row = row0 + i;
-                    a8[i] = row < M.n_out ? load_h8(M.a + (size_t)row * r + 8 * c) : zero8;
+                for (int i = 0; i < 4; ++i) {
+                    if (k < PF) {
+#pragma unroll
+                        for (int kk = 0; kk < PF; ++kk)
+                            if (kk == k) a8[rr][i] = apf[kk][rr][i];
+                    } else {
+                        const int row = (rt0 + rr) * 16 + 4 * (lane >> 4) + i;
+                        a8[rr][i] = row < M.n_out ? load_h8(M.a + (size_t)row * r + 8 * c) : zero8;
+                    }
                 }
-            }
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
                 const int t = 16 * tt + (lane & 15);
@@ -351,32 +385,39 @@ __global__ __launch_bounds__(256) void decode_kernel(const ForwardArgs args) {
                         rv[4] = r1[0]; rv[5] = r1[1]; rv[6] = r1[2]; rv[7] = r1[3];
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) rv[e] = load_r(R + (size_t)t * r + 8 * c + e);
+                        for (int e = 0; e < 8; ++e) rv[e] = load_pair(args, R + (size_t)t * r + 8 * c + e, tag);
                     }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float s = acc[tt][i];
+                    for (int rr = 0; rr < RT; ++rr)
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) s = fmaf((float)a8[i][e], rv[e], s);
-                        acc[tt][i] = s;
-                    }
+                        for (int i = 0; i < 4; ++i) {
+                            float s = acc[rr][tt][i];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) s = fmaf((float)a8[rr][i][e], rv[e], s);
+                            acc[rr][tt][i] = s;
+                        }
                 }
             }
         }
     }
 
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) red[wave][tt][lane] = acc[tt];
+    for (int rr = 0; rr < RT; ++rr)
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) red[wave][rr][tt][lane] = acc[rr][tt];
     __syncthreads();
-    if (wave < NTT) {  // wave w stores token tile w
-        const int tt = wave;
-        const f4 v0 = red[0][tt][lane], v1 = red[1][tt][lane], v2 = red[2][tt][lane], v3 = red[3][tt][lane];
+    // wave w stores (row tile, token tile) pairs w, w + KW, ...
+    for (int job = wave; job < RT * NTT; job += KW) {
+        const int rr = job / NTT, tt = job % NTT;
+        f4 v = red[0][rr][tt][lane];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) v += red[w][rr][tt][lane];  // fixed order: deterministic
         const int t = 16 * tt + (lane & 15);
-        const int row0 = rt * 16 + 4 * (lane >> 4);
-        if (t < T) {
+        const int row0 = (rt0 + rr) * 16 + 4 * (lane >> 4);
+        if (t < T && rt0 + rr < M.n_tiles16) {
             _Float16 o[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (_Float16)(((v0[i] + v1[i]) + v2[i]) + v3[i]);
+            for (int i = 0; i < 4; ++i) o[i] = (_Float16)v[i];
             _Float16* yp = M.y + (size_t)t * M.n_out + row0;
             if ((M.n_out & 3) == 0 && row0 + 3 < M.n_out) {
                 h2 lo = {o[0], o[1]}, hi = {o[2], o[3]};
@@ -391,34 +432,45 @@ __global__ __launch_bounds__(256) void decode_kernel(const ForwardArgs args) {
     if (correct) signal_done(args);
 }
 
-hipError_t launch_decode(const ForwardArgs& a_in, hipStream_t stream) {
-    ForwardArgs a = a_in;
+template <int KW, int RT>
+static hipError_t launch_decode_kw(const ForwardArgs& a, hipStream_t stream) {
+    constexpr int NTH = 64 * KW;
     const int ntt = (int)ceil_div(a.T, 16);
-    const dim3 grid(a.n_prod + a.n_tiles), block(256);
+    const dim3 grid(a.n_prod + a.n_tiles), block(NTH);
     const size_t xbytes = (size_t)(a.T + 1) * a.d * 2;  // tokens + one zero row
     const bool xlds = ntt == 1 && xbytes <= kDecodeXLdsMax;
     const size_t xarea = xlds ? (xbytes + 15) / 16 * 16 : 0;
     const size_t rarea = (ntt == 1 && a.r > 0) ? (size_t)a.T * a.r * 4 : 0;
-    a.r_lds_off = (int32_t)xarea;
+    ForwardArgs b = a;
+    b.r_lds_off = (int32_t)xarea;
     const size_t shmem = xarea + rarea;
     if (xlds) {
-        const int chunks = (int)ceil_div((int64_t)xbytes / 16, 256);
+        const int chunks = (int)ceil_div((int64_t)xbytes / 16, NTH);
         if (chunks <= 2)
-            hipLaunchKernelGGL((decode_kernel<1, 2>), grid, block, shmem, stream, a);
+            hipLaunchKernelGGL((decode_kernel<1, 2, KW, RT>), grid, block, shmem, stream, b);
         else if (chunks <= 4)
-            hipLaunchKernelGGL((decode_kernel<1, 4>), grid, block, shmem, stream, a);
+            hipLaunchKernelGGL((decode_kernel<1, 4, KW, RT>), grid, block, shmem, stream, b);
+        else if (chunks <= 8)
+            hipLaunchKernelGGL((decode_kernel<1, 8, KW, RT>), grid, block, shmem, stream, b);
         else
-            hipLaunchKernelGGL((decode_kernel<1, kDecodeXChunks>), grid, block, shmem, stream, a);
+            hipLaunchKernelGGL((decode_kernel<1, (int)(kDecodeXLdsMax / 16 / NTH), KW, RT>), grid, block, shmem,
+                               stream, b);
         return hipGetLastError();
     }
+    if (RT != 1) return hipErrorInvalidValue;
     switch (ntt) {
-        case 1: hipLaunchKernelGGL((decode_kernel<1, 0>), grid, block, shmem, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<2, 0>), grid, block, shmem, stream, a); break;
-        case 3: hipLaunchKernelGGL((decode_kernel<3, 0>), grid, block, shmem, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<4, 0>), grid, block, shmem, stream, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<1, 0, KW, 1>), grid, block, shmem, stream, b); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<2, 0, KW, 1>), grid, block, shmem, stream, b); break;
+        case 3: hipLaunchKernelGGL((decode_kernel<3, 0, KW, 1>), grid, block, shmem, stream, b); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<4, 0, KW, 1>), grid, block, shmem, stream, b); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream) {
+    if (a.dec_kw == 8) return launch_decode_kw<8, 1>(a, stream);
+    return a.dec_rt == 2 ? launch_decode_kw<4, 2>(a, stream) : launch_decode_kw<4, 1>(a, stream);
 }
 
 }  // namespace glowq

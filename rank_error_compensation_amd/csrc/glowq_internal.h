@@ -31,19 +31,26 @@ constexpr int kGroup = 128;
 constexpr int kMaxModules = 8;
 constexpr int kMaxRank = 256;
 constexpr size_t kWsHeader = 2048;  // workspace bytes reserved for synchronisation words
-// Synchronisation words of the decode hand-off, int32 offsets into the workspace header.  One
-// ready/done pair per XCD (workgroup b polls the pair of XCD b % 8), each on its own 64-byte line,
-// so that no single address is hammered by every workgroup of the launch.
+// Synchronisation words of the decode hand-off, int32 offsets into the workspace header, each on
+// its own 64-byte line.  The projection R travels as (value, tag) pairs written with single 64-bit
+// stores; a pair is current when its tag equals epoch + 1, where epoch is the header word read by
+// every workgroup at start.  The last consumer of a call (per-XCD arrival counters, then a counter
+// over the XCDs) advances the epoch, so no memset is ever needed and stale pairs never match.
 constexpr int kXcds = 8;
-constexpr int kSyncReady = 0;    // ready[x] at word kSyncReady + 16 x: producers done, as seen by XCD x
-constexpr int kSyncDone = 128;   // done[x]  at word kSyncDone + 16 x: consumers of XCD x past the epilogue
-constexpr int kSyncError = 256;  // nonzero when a bounded wait expired (results invalid)
+constexpr int kSyncEpoch = 0;     // epoch of the call in flight
+constexpr int kSyncDone = 16;     // done[x] at word kSyncDone + 16 x: consumers of XCD x finished
+constexpr int kSyncTop = 160;     // XCDs whose consumers all finished
+constexpr int kSyncError = 176;   // nonzero when a bounded wait expired (results invalid)
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kMaxProducers = 64;
-// Largest activation block (T x d fp16 bytes) the decode kernel stages in LDS, and the matching
-// number of 16-byte staging loads per thread.
-constexpr size_t kDecodeXLdsMax = 32 * 1024;
-constexpr int kDecodeXChunks = kDecodeXLdsMax / 16 / 256;
+// Largest activation block ((T + 1) x d fp16 bytes) the decode kernel stages in LDS.
+constexpr size_t kDecodeXLdsMax = 48 * 1024;
+// Decode workgroup shape: 8 waves when a launch has at most kDecodeWide8Tiles 16-row tiles and
+// long rows (at least kDecodeWide8Groups input groups); two row tiles per workgroup when it has
+// more than kDecodeRt2Tiles (so that every workgroup is resident at once).
+constexpr int kDecodeWide8Tiles = 512;
+constexpr int kDecodeWide8Groups = 64;
+constexpr int kDecodeRt2Tiles = 1024;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -123,12 +130,14 @@ struct ForwardArgs {
     int32_t m_tiles;     // token tiles (prefill)
     int32_t tile_tt;     // prefill tile shape: 16-token tiles per wave
     int32_t tile_rr;     // prefill tile shape: 16-row tiles per wave (4 waves side by side)
-    void* R;             // projections: decode fp32 [n_proj][T][r]; prefill fp16 [n_proj][T][r_pad]
+    void* R;             // projections: decode (fp32, tag) pairs [n_proj][T][r]; prefill fp16 [n_proj][T][r_pad]
     int32_t* sync;       // workspace header (decode)
     int32_t n_proj;      // projections (1 shared, m layerwise)
     int32_t n_prod;      // decode: producer workgroups forming R (0 without correction)
     int32_t prod_rows;   // decode: stacked projection rows per producer
     int32_t r_lds_off;   // decode: byte offset of the R copy in dynamic LDS (set by the launcher)
+    int32_t dec_kw;      // decode: waves per workgroup (4 or 8)
+    int32_t dec_rt;      // decode: 16-row tiles per workgroup (1 or 2)
     const _Float16* b[kMaxModules];  // [r][d] right factors, one per projection
     ModuleArgs mod[kMaxModules];
 };

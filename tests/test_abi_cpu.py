@@ -43,9 +43,11 @@ def test_buffer_sizes():
     assert L.glowq_workspace_bytes(0, 64, 1) == 0
     assert L.glowq_workspace_bytes(4, 0, 1) == 0
     hdr = 2048  # synchronisation words of the decode hand-off
-    assert L.glowq_workspace_bytes(1, 64, 1) == hdr + 256
-    assert L.glowq_workspace_bytes(2048, 64, 1) == hdr + 2048 * 64 * 4
-    assert L.glowq_workspace_bytes(100, 8, 3) == hdr + ((100 * 32 * 2 * 3 + 255) // 256) * 256
+    r256 = lambda n: (n + 255) // 256 * 256
+    # decode projection as (fp32, tag) pairs, then the prefill projection in fp16 (r padded to 32)
+    assert L.glowq_workspace_bytes(1, 64, 1) == hdr + r256(64 * 8) + r256(64 * 2)
+    assert L.glowq_workspace_bytes(2048, 64, 1) == hdr + 2048 * 64 * 8 + 2048 * 64 * 2
+    assert L.glowq_workspace_bytes(100, 8, 3) == hdr + r256(100 * 8 * 8 * 3) + r256(100 * 32 * 2 * 3)
 
 
 FAKE = 0x10000  # 64 KiB-aligned fake device address: never dereferenced, validation fails first

@@ -209,21 +209,42 @@ def test_config2_prefill():
         assert e["rel_fro"] <= 1e-3, (i, e)
 
 
-def test_decode_workspace_left_clean():
-    """The fused decode kernel's producer/consumer words are back to zero after every call and
-    no bounded wait expired (the 2 KiB workspace header is all zero)."""
+def test_decode_workspace_state_after_calls():
+    """After every decode call the hand-off's arrival counters are back to zero, no bounded wait
+    expired, and the epoch word has advanced once per call that applied the correction."""
     g = glowq()
     keys = (10,)
-    for T, lw in ((1, False), (7, True), (64, False)):
-        x = W.make_x(T, 512, 1.19, keys)
+    calls = 0
+    T_max = 64
+    ws = g.make_workspace(T_max, 24, 3)
+    for T, lw in ((1, False), (7, True), (64, False), (3, True)):
+        x = W.make_x(T, 512, 1.19, keys + (T,))
         unit = W.make_unit("g", "group", x, [64, 40, 32], 24, keys, layerwise=True)
         du = DevUnit(unit, layerwise=True)
-        ws = g.make_workspace(T, 24, 3)
         for _ in range(3):
             if lw:
                 g.layerwise_forward(du.x, du.w, du.b_lw, du.a, 24, True, workspace=ws)
             else:
                 g.group_forward(du.x, du.w, du.b, du.a, 24, True, workspace=ws)
+            calls += 1
+        g.group_forward(du.x, du.w, du.b, du.a, 24, False, workspace=ws)  # restore off: no hand-off
         torch.cuda.synchronize()
         hdr = ws[:2048].view(torch.int32).cpu()
-        assert int(hdr.abs().sum()) == 0, hdr.nonzero()
+        assert int(hdr[0]) == calls, (int(hdr[0]), calls)          # epoch
+        assert int(hdr[1:].abs().sum()) == 0, hdr[1:].nonzero()     # counters and error flag
+
+
+def test_workspace_reuse_across_calls_and_paths():
+    """One workspace reused by consecutive decode and prefill calls with different inputs: every
+    result matches the oracle (no stale projection is ever consumed)."""
+    g = glowq()
+    ws = g.make_workspace(200, 32, 1)
+    for i, T in enumerate((1, 1, 150, 1, 16, 200, 2, 2)):
+        keys = (11, i)
+        x = W.make_x(T, 384, 0.77, keys)
+        unit = W.make_unit("g", "group", x, [48, 32], 32, keys)
+        du = DevUnit(unit)
+        ys = g.group_forward(du.x, du.w, du.b, du.a, 32, True, workspace=ws)
+        ref = oracle_unit(unit)
+        for j, (y, yr) in enumerate(zip(ys, ref)):
+            assert_parity(y, yr, f"reuse call {i} T={T} module {j}")
