@@ -33,6 +33,10 @@ inline size_t decode_r_bytes(int64_t T, int32_t r, int32_t n_proj) {
 inline size_t prefill_r_bytes(int64_t T, int32_t r, int32_t n_proj) {
     return round256((size_t)T * (size_t)r_pad_of(r) * 2u * (size_t)n_proj);
 }
+// fp32 split-K partials of the prefill projection, after the fp16 projection
+inline size_t prefill_part_bytes(int64_t T, int32_t r, int32_t n_proj) {
+    return round256((size_t)kProjMaxSplit * (size_t)T * (size_t)r_pad_of(r) * 4u * (size_t)n_proj);
+}
 
 // Everything needed to launch one group / solo / layerwise call.
 struct Call {
@@ -133,6 +137,11 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
         p.n_proj = c.n_proj;
         for (int i = 0; i < c.n_proj; ++i) p.b[i] = static_cast<const _Float16*>(c.b[i]);
         p.R = R;
+        const int64_t G = c.d / kGroup;
+        p.ks = (int32_t)(G < kProjMaxSplit ? G : kProjMaxSplit);
+        p.k_per = (int32_t)(ceil_div(G, p.ks) * kGroup);
+        p.ks = (int32_t)ceil_div(c.d, p.k_per);
+        p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(R) + prefill_r_bytes(c.T, c.r, c.n_proj));
         if (launch_proj_prefill(p, stream) != hipSuccess) return GLOWQ_ERR_HIP;
     }
 
@@ -244,7 +253,8 @@ size_t glowq_sz_bytes(int64_t n_out, int64_t k_in) {
 
 size_t glowq_workspace_bytes(int64_t T, int32_t r, int32_t n_proj) {
     if (T <= 0 || r <= 0 || n_proj <= 0) return 0;
-    return kWsHeader + decode_r_bytes(T, r, n_proj) + prefill_r_bytes(T, r, n_proj);
+    return kWsHeader + decode_r_bytes(T, r, n_proj) + prefill_r_bytes(T, r, n_proj) +
+           prefill_part_bytes(T, r, n_proj);
 }
 
 int glowq_repack(const void* q_canon_dev, const void* scales_dev, const void* zeros_dev, int64_t n_out,

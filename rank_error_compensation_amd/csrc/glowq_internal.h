@@ -145,6 +145,8 @@ struct ForwardArgs {
 struct ProjArgs {
     const _Float16* x;   // [T][d]
     int32_t T, d, r, r_pad, n_proj;
+    int32_t ks, k_per;   // K split: ks ranges of k_per inputs (a multiple of 128)
+    float* part;         // fp32 partials [ks][n_proj][T][r_pad]
     const _Float16* b[kMaxModules];  // [r][d] per projection
     void* R;             // output
 };
@@ -159,6 +161,9 @@ hipError_t launch_dequant(const uint8_t* q, const uint8_t* sz, int64_t n_out, in
 hipError_t launch_proj_prefill(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
+
+// Largest K split of the prefill projection.
+constexpr int kProjMaxSplit = 8;
 
 // Token count above which the prefill (dequant-to-register MFMA GEMM) kernels are used.
 constexpr int kDecodeMaxT = 64;
