@@ -125,6 +125,36 @@ def per_launch_events(units, descr, g, reps, layerwise=False):
     return [t / reps for t in tot]
 
 
+# ------------------------------------------------------------------ measured HBM traffic
+def source_digest():
+    """sha256 over the decode kernel's sources: counter readings are only valid for this code."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode.hip", "glowq_internal.h"):
+        with open(os.path.join(ROOT, "rank_error_compensation_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None when the kernel
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "decode_path_T1_counters.txt")
+    try:
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic_bytes_per_launch=") or line.startswith("source_sha256="):
+                    k, v = line.strip().split("=", 1)
+                    kv[k] = v
+        if kv.get("source_sha256") != source_digest():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 def cpu_baseline(keep, mask):
     """The fp64 oracle on a bounded sample of the same workload: one restored and one
@@ -241,6 +271,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--event-reps", type=int, default=10)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after the timed region, copy a buffer of this many MiB 5 times with a plain "
+                         "device copy (a reference kernel of known traffic for hardware counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
@@ -259,16 +292,29 @@ def main():
     first_off = next(l for l in range(32) if not mask[l])
     first_on = next(l for l in range(32) if mask[l])
     plan = g.PathPlan(units)
-    elapsed = time_steps(plan.run, args.steps, args.warmup)
+    nbytes = [unit_bytes(t, d, no, r, rs) for (_, t, d, no, r, rs) in descr]
+    # timed region: K steps between two HIP events on the stream the library launches on
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        plan.run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    elapsed = ev0.elapsed_time(ev1) * 1e-3
     ms = elapsed / args.steps * 1e3
     value = T * args.steps / elapsed
-    log(f"[bench] decode path: {ms * 1e3:.1f} us/step, {value:.1f} tokens/s")
+    log(f"[bench] decode path: {ms * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), {value:.1f} tokens/s")
 
-    # ---- dominant kernel: the fused decode kernel, one launch per unit
-    durs = per_launch_events(units, descr, g, args.event_reps)
-    nbytes = [unit_bytes(t, d, no, r, rs) for (_, t, d, no, r, rs) in descr]
-    achieved = sum(nbytes) / sum(durs) / 1e9
-    kernel_sum_ms = sum(durs) * 1e3
+    # ---- dominant kernel: the fused decode kernel, one launch per unit (every launch of the step)
+    launch_us = elapsed / args.steps / len(descr) * 1e6
+    achieved = sum(nbytes) / (elapsed / args.steps) / 1e9
+    durs = per_launch_events(units, descr, g, args.event_reps)  # per unit, single launch between events
     per_kind = {}
     for (name, t, d, no, r, rs), du, nb in zip(descr, durs, nbytes):
         k = f"{name}{'' if rs else '(no-restore)'}"
@@ -279,12 +325,13 @@ def main():
         e["us"] = round(e["us"] / e["launches"], 3)
         e["GB_per_s"] = round(e["bytes"] / (e["us"] * 1e-6) / 1e9, 1)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "glowq::decode_kernel<1>",
-                "per_launch_alg_bytes_mean": int(sum(nbytes) / len(nbytes)),
-                "per_launch_us_mean": round(sum(durs) / len(durs) * 1e6, 3),
-                "kernel_sum_ms_per_step": round(kernel_sum_ms, 4), "per_unit": per_kind}
-    log(f"[bench] decode kernel: {achieved:.0f} GB/s over {len(durs)} launches, kernel sum {kernel_sum_ms:.3f} ms")
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "kernel": "glowq::decode_kernel (fused projection + INT4 product + correction)",
+                "launches_per_step": len(descr),
+                "alg_bytes_per_launch_mean": int(sum(nbytes) / len(nbytes)),
+                "launch_us_mean": round(launch_us, 3),
+                "per_unit_single_launch_event_us": per_kind}
+    log(f"[bench] decode kernel: {achieved:.0f} GB/s, {launch_us:.2f} us per launch over {len(descr)} launches")
 
     # ---- layerwise baseline on the same path
     extra = {}
@@ -337,6 +384,22 @@ def main():
         _, _, mask2, keep = build_path_keep(T, dev, [first_on, first_off])
         cpu = cpu_baseline(keep, mask2)
         log(f"[bench] cpu oracle: {cpu}")
+
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 5
+        extra["copy_probe"] = {"bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                               "GB_per_s_read_plus_write": round(2 * n / t / 1e9, 1)}
+        log(f"[bench] copy probe: {extra['copy_probe']}")
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
