@@ -212,9 +212,10 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
 #pragma unroll
     for (int rr = 0; rr < RT; ++rr) {
         const int rt = min(rt0 + rr, M.n_tiles16 - 1);  // a tile past the module end rereads the last
-        qbase[rr] = M.q + (size_t)rt * G * 1024 + lane * 16;
-        szbase[rr] = M.sz + (size_t)rt * G * 64;
+        qbase[rr] = M.q + (size_t)rt * 1024 + lane * 16;
+        szbase[rr] = M.sz + (size_t)rt * 64;
     }
+    const size_t qstride = (size_t)M.n_tiles16 * 1024, szstride = (size_t)M.n_tiles16 * 64;  // per group
     const int kofs = 8 * (lane >> 4);
     const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     const NibConsts nc = nib_consts();
@@ -264,9 +265,9 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
         }
 #pragma unroll
         for (int rr = 0; rr < RT; ++rr) {
-            qv[u][rr] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(qbase[rr] + (size_t)g * 1024));
-            zso[u][rr] = *reinterpret_cast<const uint32_t*>(szbase[rr] + (size_t)g * 64 + (lane & 15) * 4);
-            zs4[u][rr] = *reinterpret_cast<const u4*>(szbase[rr] + (size_t)g * 64 + (lane >> 4) * 16);
+            qv[u][rr] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(qbase[rr] + (size_t)g * qstride));
+            zso[u][rr] = *reinterpret_cast<const uint32_t*>(szbase[rr] + (size_t)g * szstride + (lane & 15) * 4);
+            zs4[u][rr] = *reinterpret_cast<const u4*>(szbase[rr] + (size_t)g * szstride + (lane >> 4) * 16);
         }
     };
 

@@ -16,11 +16,11 @@ __global__ __launch_bounds__(256) void repack_q_kernel(const uint32_t* __restric
                                                        uint32_t* __restrict__ qd) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= n_words) return;
-    const int64_t G = k_in / kGroup;
-    const int64_t blk = idx >> 8;
+    const int64_t NT = ceil_div(n_out, 16);
+    const int64_t blk = idx >> 8;  // block g * NT + rt
     const int within = (int)(idx & 255);
     const int l = within >> 2, j = within & 3;
-    const int64_t rt = blk / G, g = blk - rt * G;
+    const int64_t g = blk / NT, rt = blk - g * NT;
     const int64_t row = rt * 16 + (l & 15);
     const int64_t k0 = g * kGroup + 32 * j + 8 * (l >> 4);
     uint32_t v = 0;
@@ -42,9 +42,10 @@ __global__ __launch_bounds__(256) void repack_sz_kernel(const _Float16* __restri
                                                         int32_t* __restrict__ flag) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= n_pairs) return;
-    const int64_t blk = idx >> 4;
+    const int64_t NT = ceil_div(n_out, 16);
+    const int64_t blk = idx >> 4;  // block g * NT + rt
     const int i = (int)(idx & 15);
-    const int64_t rt = blk / G, g = blk - rt * G;
+    const int64_t g = blk / NT, rt = blk - g * NT;
     const int64_t row = rt * 16 + i;
     h2 pair = {(_Float16)0.0f, (_Float16)0.0f};
     if (row < n_out) {
@@ -67,11 +68,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
                                                       int64_t k_in, int64_t n_words, void* __restrict__ out) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= n_words) return;
-    const int64_t G = k_in / kGroup;
-    const int64_t blk = idx >> 8;
+    const int64_t NT = ceil_div(n_out, 16);
+    const int64_t blk = idx >> 8;  // block g * NT + rt
     const int within = (int)(idx & 255);
     const int l = within >> 2, j = within & 3;
-    const int64_t rt = blk / G, g = blk - rt * G;
+    const int64_t g = blk / NT, rt = blk - g * NT;
     const int64_t row = rt * 16 + (l & 15);
     if (row >= n_out) return;
     const int64_t k0 = g * kGroup + 32 * j + 8 * (l >> 4);

@@ -2,7 +2,9 @@
 //
 // Device layout of one INT4-g128 module (n_out x k_in, G = k_in / 128 groups, NT = ceil(n_out/16)
 // row tiles of 16 rows):
-//   q  : NT x G blocks of 1024 bytes, block (rt, g) at byte (rt * G + g) * 1024.  Lane l (0..63)
+//   q  : G x NT blocks of 1024 bytes, block (rt, g) at byte (g * NT + rt) * 1024 (group-major: the
+//        blocks of one input group are adjacent for all row tiles, so workgroups that stream their
+//        tiles in step read one contiguous region of memory at a time).  Lane l (0..63)
 //        of a wavefront owns the 16 bytes at l * 16: four 32-bit words, word j (0..3) holding the
 //        eight inputs k = 128 g + 32 j + 8 (l / 16) + e, e = 0..7, of row 16 rt + (l % 16).  This
 //        is exactly the A/B operand of v_mfma_f32_16x16x32_f16 (lane l: row l % 16, k-slice
@@ -11,7 +13,7 @@
 //        p (bits 4p..4p+3) holds e = 2p for p < 4 and e = 2(p - 4) + 1 for p >= 4, so that
 //        masking with 0x000F000F / 0x00F000F0 (after a shift by 0 or 8) yields the fp16 pairs
 //        (e0, e1), (e2, e3), (e4, e5), (e6, e7) with the 0x6400 exponent trick.
-//   sz : NT x G blocks of 64 bytes, block (rt, g) at byte (rt * G + g) * 64: sixteen (z, s) fp16
+//   sz : G x NT blocks of 64 bytes, block (rt, g) at byte (g * NT + rt) * 64: sixteen (z, s) fp16
 //        pairs, pair i for row 16 rt + i.
 //   Rows >= n_out are zero (q = 0, z = 0, s = 0).
 #pragma once

@@ -54,6 +54,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const ForwardArgs args)
     const NibConsts nc = nib_consts();
     const int kofs = 8 * (lane >> 4);
     const int rt0 = nb * 4 * RR + wave * RR;
+    const size_t qstride = (size_t)M.n_tiles16 * 1024, szstride = (size_t)M.n_tiles16 * 64;  // per group
 
     const uint8_t* qp[RR];
     const uint8_t* zp[RR];
@@ -62,8 +63,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const ForwardArgs args)
     for (int rr = 0; rr < RR; ++rr) {
         const int rt = rt0 + rr;
         w_ok[rr] = rt < M.n_tiles16;
-        qp[rr] = M.q + (size_t)(w_ok[rr] ? rt : 0) * G * 1024 + lane * 16;
-        zp[rr] = M.sz + (size_t)(w_ok[rr] ? rt : 0) * G * 64 + (lane & 15) * 4;
+        qp[rr] = M.q + (size_t)(w_ok[rr] ? rt : 0) * 1024 + lane * 16;
+        zp[rr] = M.sz + (size_t)(w_ok[rr] ? rt : 0) * 64 + (lane & 15) * 4;
     }
     const _Float16* xsrc[NCH];
     bool x_ok[NCH];
@@ -110,8 +111,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const ForwardArgs args)
                 st[c] = x_ok[c] ? *reinterpret_cast<const u4*>(xsrc[c] + (size_t)(g + 1) * kGroup) : zero4;
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr) {
-                qn[rr] = w_ok[rr] ? *reinterpret_cast<const u4*>(qp[rr] + (size_t)(g + 1) * 1024) : zero4;
-                zn[rr] = w_ok[rr] ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)(g + 1) * 64) : 0u;
+                qn[rr] = w_ok[rr] ? *reinterpret_cast<const u4*>(qp[rr] + (size_t)(g + 1) * qstride) : zero4;
+                zn[rr] = w_ok[rr] ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)(g + 1) * szstride) : 0u;
             }
         }
         h2 c1024[RR], c64[RR];
