@@ -3,7 +3,10 @@
     python -m rank_error_compensation_amd.build        # or __graft_entry__.build()
 
 Every translation unit is compiled for gfx950 only, with packed-fp32 instruction selection
-disabled (-Xclang -target-feature -Xclang -packed-fp32-ops).
+disabled (-Xclang -target-feature -Xclang -packed-fp32-ops) and without the compiler's
+wave-aggregation of atomics (-mllvm -amdgpu-atomic-optimizer-strategy=None): the kernels issue
+their atomics from one lane and read the returned value much later, which the aggregated form
+(it broadcasts the result at once) would turn into a wait for every load in flight.
 """
 from __future__ import annotations
 
@@ -34,6 +37,7 @@ def hipcc() -> str:
 def common_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 

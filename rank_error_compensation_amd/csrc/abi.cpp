@@ -23,12 +23,12 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 
 inline int64_t r_pad_of(int32_t r) { return ceil_div(r, 32) * 32; }
 
-// Workspace after the header: the decode projection as (fp32, tag) pairs, then the prefill
-// projection in fp16 with rows padded to 32.  The two never share bytes, so tags left by a decode
-// call can never be confused with a prefill call's data.
+// Workspace after the header: the decode projection as (fp32, tag) pairs in kRReplicas copies,
+// then the prefill projection in fp16 with rows padded to 32.  The two never share bytes, so tags
+// left by a decode call can never be confused with a prefill call's data.
 inline size_t round256(size_t n) { return (n + 255u) / 256u * 256u; }
 inline size_t decode_r_bytes(int64_t T, int32_t r, int32_t n_proj) {
-    return round256((size_t)T * (size_t)r * 8u * (size_t)n_proj);
+    return round256((size_t)T * (size_t)r * 8u * (size_t)n_proj * (size_t)kRReplicas);
 }
 inline size_t prefill_r_bytes(int64_t T, int32_t r, int32_t n_proj) {
     return round256((size_t)T * (size_t)r_pad_of(r) * 2u * (size_t)n_proj);
@@ -186,6 +186,7 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
         M.n_out = (int32_t)c.w[i].n_out;
         M.n_tiles16 = (int32_t)ceil_div(c.w[i].n_out, 16);
         M.tile_begin = (int32_t)tiles;
+        f.tile_begin[i] = (int32_t)tiles;
         M.proj = c.n_proj > 1 ? i : 0;
         tiles += prefill ? ceil_div(M.n_tiles16, 4 * rr) : ceil_div(M.n_tiles16, dec_rt);
     }

@@ -12,13 +12,18 @@
 // current -- one coherent read both waits for and fetches R, and producers need no fence or
 // counter.  Producers have the lowest workgroup ids and never wait, so they are dispatched before
 // any consumer and always finish; every wait is bounded and raises a flag in the workspace header
-// if it expires.  The last consumer of the call advances the epoch (arrival counters replicated
-// per XCD, then one counter over the XCDs), so stale pairs never match and no memset is needed.
-//
+// if it expires.
+// Epoch: every workgroup reads it as its first load and then "arrives" (per-XCD counters, then one
+// counter over the XCDs); the last arrival of the launch resets the counters and advances the
+// epoch, so stale pairs never match and no memset is ever needed.  Consumers arrive right after
+// their first loads are issued, so the counting overlaps the weight stream instead of lengthening
+// the launch's tail; producers arrive when their pairs are written.
+
 // Main loop: the K dimension (input groups of 128) is split across the 4 wavefronts of a tile
-// (group g goes to wave g % 4).  Each wave keeps a ring of U groups in flight: one 16-byte load
-// per lane brings a whole group (16 rows x 128 inputs) in matrix-core operand order; after a
-// group is consumed its slot is refilled with the group U ahead.  Nibbles become exact fp16
+// (group g goes to wave g % 4).  Each wave keeps a ring of U groups in flight (4 per row tile;
+// deeper rings measured slower: the registers they take cost more than the extra loads gain):
+// one 16-byte load per lane brings a whole group (16 rows x 128 inputs) in matrix-core operand
+// order; after a group is consumed its slot is refilled with the group U ahead.  Nibbles become exact fp16
 // (q - z) values in registers; four v_mfma_f32_16x16x32_f16 accumulate the group's partial sums
 // against the tokens (padded to 16 per tile); the per-(row, group) scale is applied once per group
 // in fp32.  The four waves' partial sums, each carrying its share of the correction terms, are
@@ -26,13 +31,6 @@
 #include "glowq_internal.h"
 
 namespace glowq {
-
-__device__ __forceinline__ void pick_module(const ForwardArgs& a, int tile, ModuleArgs& m) {
-    m = a.mod[0];
-#pragma unroll
-    for (int i = 1; i < kMaxModules; ++i)
-        if (i < a.n_mod && tile >= a.mod[i].tile_begin) m = a.mod[i];
-}
 
 __device__ __forceinline__ const _Float16* pick_bp(const ForwardArgs& a, int i) {
     const _Float16* b = a.b[0];
@@ -72,6 +70,31 @@ __device__ __forceinline__ float load_pair(const ForwardArgs& a, const u64* p, u
         w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return __builtin_bit_cast(float, (uint32_t)w);
+}
+
+// Hand-off arrival of this workgroup (thread 0), made after its epoch read has completed.
+__device__ __forceinline__ int arrive(const ForwardArgs& a) {
+    return __hip_atomic_fetch_add(a.sync + kSyncDone + 16 * (blockIdx.x & 7), 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// With the result of arrive(): the last arrival of its XCD resets that XCD's counter and counts
+// the XCD; returns the previous XCD count, or -1 for every other workgroup.
+__device__ __forceinline__ int arrive_xcd(const ForwardArgs& a, int prev) {
+    const int x = blockIdx.x & 7;
+    if (prev != count_mod8(0, a.n_prod + a.n_tiles, x) - 1) return -1;
+    __hip_atomic_store(a.sync + kSyncDone + 16 * x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_fetch_add(a.sync + kSyncTop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// With the result of arrive_xcd(): the launch's very last arrival resets the XCD counter and
+// advances the epoch.  Every workgroup read the epoch before arriving, so no one in this launch
+// sees the new value.
+__device__ __forceinline__ void finish(const ForwardArgs& a, int top_prev) {
+    const int grid = a.n_prod + a.n_tiles;
+    if (top_prev != (grid < kXcds ? grid : kXcds) - 1) return;
+    __hip_atomic_store(a.sync + kSyncTop, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(a.sync + kSyncEpoch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Producer workgroup: rows [p * prod_rows, (p+1) * prod_rows) of the stacked projections
@@ -146,37 +169,14 @@ __device__ void produce(const ForwardArgs& a, int p) {
                 float v = part[0][t];
 #pragma unroll
                 for (int w = 1; w < KW; ++w) v += part[w][t];
-                store_pair(R + ((size_t)pi * T + t0 + t) * r + j, v, tag);
+                const size_t off = ((size_t)pi * T + t0 + t) * r + j, copy = (size_t)a.n_proj * T * r;
+#pragma unroll
+                for (int c = 0; c < kRReplicas; ++c) store_pair(R + c * copy + off, v, tag);
             }
             __syncthreads();
         }
     }
-}
-
-// End of a consumer: count arrivals per XCD, then over XCDs; the very last consumer of the call
-// resets the counters and advances the epoch.  Every consumer has read the epoch and every
-// producer has written its pairs before the last arrival, so the advance is seen by no one in
-// this call.
-__device__ __forceinline__ void signal_done(const ForwardArgs& a) {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int lo = a.n_prod, hi = a.n_prod + a.n_tiles;
-        const int x = blockIdx.x & 7;
-        const int n = count_mod8(lo, hi, x);
-        const int prev = __hip_atomic_fetch_add(a.sync + kSyncDone + 16 * x, 1, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == n - 1) {
-            __hip_atomic_store(a.sync + kSyncDone + 16 * x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            int n_x = 0;
-#pragma unroll
-            for (int k = 0; k < kXcds; ++k) n_x += count_mod8(lo, hi, k) > 0;
-            const int top = __hip_atomic_fetch_add(a.sync + kSyncTop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (top == n_x - 1) {
-                __hip_atomic_store(a.sync + kSyncTop, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_fetch_add(a.sync + kSyncEpoch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-    }
+    if (threadIdx.x == 0) finish(a, arrive_xcd(a, arrive(a)));
 }
 
 // NTT: 16-token tiles.  RT: 16-row tiles per workgroup, multiplied side by side against the same
@@ -191,7 +191,7 @@ template <int NTT, int XC, int KW, int RT>
 __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0 && KW == 4) ? (RT == 2 ? 3 : 4) : 1))) void decode_kernel(const ForwardArgs args) {
     constexpr bool XLDS = XC > 0;
     constexpr int NTH = 64 * KW;
-    constexpr int U = XLDS ? 8 / RT : (NTT == 1 ? 4 / RT : 1);  // ring of groups per wave
+    constexpr int U = NTT == 1 ? 4 / RT : 1;  // ring of groups per wave
     static_assert(U >= 1, "ring");
     __shared__ f4 red[KW][RT][NTT][64];
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
@@ -201,8 +201,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
         return;
     }
     const int tile = blockIdx.x - args.n_prod;
-    ModuleArgs M;
-    pick_module(args, tile, M);
+    const ModuleArgs M = args.mod[module_of(args, tile)];
     const int rt0 = (tile - M.tile_begin) * RT;  // first 16-row tile of this workgroup
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
@@ -220,8 +219,15 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
     const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     const NibConsts nc = nib_consts();
     const int n_my = G > wave ? (G - wave + KW - 1) / KW : 0;  // groups of this wave: g = wave + KW i
-    const bool correct = args.r > 0 && M.a != nullptr;
-    const uint32_t tag = correct ? load_epoch(args) + 1u : 0u;  // read before this call can end
+    const bool hand = args.n_prod > 0;  // correcting launch: R hand-off and epoch protocol
+    const bool correct = hand && M.a != nullptr;
+    const int r = args.r;
+    // the epoch: one read per workgroup, the first load of thread 0 (so that waiting for it never
+    // waits for weights), handed to the other waves through LDS
+    __shared__ uint32_t tag_lds;
+    uint32_t epoch0 = 0;
+    if (hand && threadIdx.x == 0)
+        epoch0 = (uint32_t)__hip_atomic_load(args.sync + kSyncEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     const _Float16* xrow[NTT];
     bool tok_ok[NTT];
@@ -279,6 +285,16 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
 
     auto compute = [&](int u, int i) {
         const int g = wave + KW * i;
+        // activation operands first: the LDS reads complete while the weights are unpacked
+        h8 bl[XLDS ? NTT : 1][4];
+        if (XLDS) {
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bl[XLDS ? tt : 0][j] = *reinterpret_cast<const h8*>(xrow[tt] + (size_t)g * kGroup + 32 * j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         h8 aop[RT][4];
 #pragma unroll
         for (int rr = 0; rr < RT; ++rr) {
@@ -294,8 +310,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
             for (int rr = 0; rr < RT; ++rr) part[rr] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const h8 b = XLDS ? *reinterpret_cast<const h8*>(xrow[tt] + (size_t)g * kGroup + 32 * j)
-                                  : bx[XLDS ? 0 : u][tt][j];
+                const h8 b = XLDS ? bl[XLDS ? tt : 0][j] : bx[XLDS ? 0 : u][tt][j];
 #pragma unroll
                 for (int rr = 0; rr < RT; ++rr) part[rr] = mfma16(aop[rr][j], b, part[rr]);
             }
@@ -315,8 +330,18 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
             const int idx = min(c * NTH + (int)threadIdx.x, n8 - 1);
             reinterpret_cast<u4*>(xs)[idx] = xst[c];
         }
+    }
+    // the workgroup arrives once thread 0 holds the epoch (every wave reads it after the barrier)
+    int arrived = 0;
+    if (hand) {
+        if (threadIdx.x == 0) tag_lds = epoch0 + 1u;
+        __syncthreads();
+        if (threadIdx.x == 0) arrived = arrive(args);
+    } else if (XLDS) {
         __syncthreads();
     }
+    const uint32_t tag = hand ? tag_lds : 0u;
+
     if (n_my > 0) {
         int i0 = 0;
         // steady state: consume slot u, refill it with the group U ahead (clamped)
@@ -333,13 +358,17 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
             if (i0 + u < n_my) compute(u, i0 + u);
     }
 
+    int top_prev = -1;
+    if (hand && threadIdx.x == 0) top_prev = arrive_xcd(args, arrived);
+
     // correction epilogue: this wave adds R[t][8c..8c+8) . A[row][8c..8c+8) for chunks c = wave mod KW.
     // The first A chunks are loaded before R is needed; with one token tile R is copied once into
-    // LDS (one coherent 8-byte pair load per element, which also waits for the producers) and read
-    // from there.
+    // LDS (coherent 8-byte pair reads of this workgroup's copy, which also wait for the producers)
+    // and read from there; otherwise each element is read as a pair.
     if (correct) {
-        const int r = args.r;
         const int nc8 = r / 8;
+        const u64* Rp = reinterpret_cast<const u64*>(args.R) +
+                        (size_t)(blockIdx.x & (kRReplicas - 1)) * args.n_proj * T * r + (size_t)M.proj * T * r;
         constexpr int PF = RT == 1 ? 2 : 1;  // A chunks prefetched per wave
         h8 apf[PF][RT][4];
 #pragma unroll
@@ -353,10 +382,9 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
                     apf[k][rr][i] = (c < nc8 && row < M.n_out) ? load_h8(M.a + (size_t)row * r + 8 * c) : zero8;
                 }
         }
-        const u64* R = reinterpret_cast<const u64*>(args.R) + (size_t)M.proj * T * r;
         float* rl = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(xs) + args.r_lds_off);
         if (NTT == 1) {
-            for (int k = threadIdx.x; k < T * r; k += NTH) rl[k] = load_pair(args, R + k, tag);
+            for (int k = threadIdx.x; k < T * r; k += NTH) rl[k] = load_pair(args, Rp + k, tag);
             __syncthreads();
         }
         for (int c = wave, k = 0; c < nc8; c += KW, ++k) {
@@ -386,7 +414,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
                         rv[4] = r1[0]; rv[5] = r1[1]; rv[6] = r1[2]; rv[7] = r1[3];
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) rv[e] = load_pair(args, R + (size_t)t * r + 8 * c + e, tag);
+                        for (int e = 0; e < 8; ++e) rv[e] = load_pair(args, Rp + (size_t)t * r + 8 * c + e, tag);
                     }
 #pragma unroll
                     for (int rr = 0; rr < RT; ++rr)
@@ -430,7 +458,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
             }
         }
     }
-    if (correct) signal_done(args);
+    if (hand && threadIdx.x == 0) finish(args, top_prev);
 }
 
 template <int KW, int RT>

@@ -44,6 +44,9 @@ constexpr int kSyncDone = 16;     // done[x] at word kSyncDone + 16 x: consumers
 constexpr int kSyncTop = 160;     // XCDs whose consumers all finished
 constexpr int kSyncError = 176;   // nonzero when a bounded wait expired (results invalid)
 constexpr int kSpinLimit = 1 << 20;
+// The decode projection is written in kRReplicas copies, one per XCD (copy b % 8 is read by
+// workgroup b), so that the consumers polling it spread over eight sets of cache lines.
+constexpr int kRReplicas = 8;
 constexpr int kMaxProducers = 64;
 // Largest activation block ((T + 1) x d fp16 bytes) the decode kernel stages in LDS.
 constexpr size_t kDecodeXLdsMax = 48 * 1024;
@@ -128,6 +131,7 @@ struct ForwardArgs {
     int32_t r;           // rank (0 = no correction)
     int32_t r_pad;       // r rounded up to 32 (prefill R row stride)
     int32_t n_mod;
+    int32_t tile_begin[kMaxModules];  // first work tile of each module (contiguous: one scalar load)
     int32_t n_tiles;     // total work tiles of the launch
     int32_t m_tiles;     // token tiles (prefill)
     int32_t tile_tt;     // prefill tile shape: 16-token tiles per wave
@@ -152,6 +156,15 @@ struct ProjArgs {
     const _Float16* b[kMaxModules];  // [r][d] per projection
     void* R;             // output
 };
+
+// Module owning work tile `tile` (uniform across the workgroup): one contiguous scalar load of the
+// tile_begin table, so the module's own arguments are fetched with a single dependent load.
+__device__ __forceinline__ int module_of(const ForwardArgs& a, int tile) {
+    int i = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxModules; ++k) i += (k < a.n_mod && tile >= a.tile_begin[k]) ? 1 : 0;
+    return __builtin_amdgcn_readfirstlane(i);
+}
 
 // --------------------------------------------------------------------- launchers
 hipError_t launch_repack(const uint32_t* qc, const _Float16* s, const _Float16* z, int64_t n_out,

@@ -20,13 +20,6 @@
 
 namespace glowq {
 
-__device__ __forceinline__ void pick_module_p(const ForwardArgs& a, int nbl, ModuleArgs& m) {
-    m = a.mod[0];
-#pragma unroll
-    for (int i = 1; i < kMaxModules; ++i)
-        if (i < a.n_mod && nbl >= a.mod[i].tile_begin) m = a.mod[i];
-}
-
 // Physical workgroup id -> logical tile id such that XCD x (workgroups b with b % 8 == x)
 // receives a contiguous range of logical tiles.
 __device__ __forceinline__ int xcd_remap(int b, int n) {
@@ -44,8 +37,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const ForwardArgs args)
 
     const int L = xcd_remap(blockIdx.x, args.n_tiles);
     const int mb = L % args.m_tiles, nbl = L / args.m_tiles;
-    ModuleArgs M;
-    pick_module_p(args, nbl, M);
+    const ModuleArgs M = args.mod[module_of(args, nbl)];
     const int nb = nbl - M.tile_begin;
     const int m0 = mb * BM;
     const int tid = threadIdx.x, lane = tid & 63;

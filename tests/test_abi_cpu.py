@@ -44,12 +44,13 @@ def test_buffer_sizes():
     assert L.glowq_workspace_bytes(4, 0, 1) == 0
     hdr = 2048  # synchronisation words of the decode hand-off
     r256 = lambda n: (n + 255) // 256 * 256
-    # decode projection as (fp32, tag) pairs, the prefill projection in fp16 (r padded to 32), then
-    # the prefill projection's fp32 split-K partials (up to 8 splits)
-    ws = lambda T, r, p: hdr + r256(T * r * 8 * p) + r256(T * ((r + 31) // 32 * 32) * 2 * p) + \
+    # decode projection as (fp32, tag) pairs in 8 copies (one per XCD), the prefill projection in
+    # fp16 (r padded to 32), then the prefill projection's fp32 split-K partials (up to 8 splits)
+    ws = lambda T, r, p: hdr + r256(8 * T * r * 8 * p) + r256(T * ((r + 31) // 32 * 32) * 2 * p) + \
         r256(8 * T * ((r + 31) // 32 * 32) * 4 * p)
     assert L.glowq_workspace_bytes(1, 64, 1) == ws(1, 64, 1)
-    assert L.glowq_workspace_bytes(2048, 64, 1) == hdr + 2048 * 64 * 8 + 2048 * 64 * 2 + 8 * 2048 * 64 * 4
+    assert L.glowq_workspace_bytes(2048, 64, 1) == \
+        hdr + 8 * 2048 * 64 * 8 + 2048 * 64 * 2 + 8 * 2048 * 64 * 4
     assert L.glowq_workspace_bytes(100, 8, 3) == ws(100, 8, 3)
 
 
