@@ -23,13 +23,12 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 
 inline int64_t r_pad_of(int32_t r) { return ceil_div(r, 32) * 32; }
 
-// Workspace after the header: the decode projection as (fp32, tag) pairs in kRReplicas copies,
-// then the prefill projection in fp16 with rows padded to 32.  The two never share bytes, so tags
-// left by a decode call can never be confused with a prefill call's data.
+// Workspace after the header: the fixed decode area (the projection as (fp32, tag) pairs in
+// kRReplicas copies, sized for any decode call), then the prefill projection in fp16 with rows
+// padded to 32 and its split-K partials.  No call ever writes anything but pairs into the decode
+// area, so tags can never be confused with other data.
 inline size_t round256(size_t n) { return (n + 255u) / 256u * 256u; }
-inline size_t decode_r_bytes(int64_t T, int32_t r, int32_t n_proj) {
-    return round256((size_t)T * (size_t)r * 8u * (size_t)n_proj * (size_t)kRReplicas);
-}
+constexpr size_t kDecodeAreaBytes = kDecodeAreaPairs * 8u;
 inline size_t prefill_r_bytes(int64_t T, int32_t r, int32_t n_proj) {
     return round256((size_t)T * (size_t)r_pad_of(r) * 2u * (size_t)n_proj);
 }
@@ -123,7 +122,7 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
     void* R = nullptr;
     if (c.correct) {
         uint8_t* base = static_cast<uint8_t*>(workspace) + kWsHeader;
-        R = prefill ? base + decode_r_bytes(c.T, c.r, c.n_proj) : base;
+        R = prefill ? base + kDecodeAreaBytes : base;
     }
 
     if (c.correct && prefill) {
@@ -254,8 +253,9 @@ size_t glowq_sz_bytes(int64_t n_out, int64_t k_in) {
 
 size_t glowq_workspace_bytes(int64_t T, int32_t r, int32_t n_proj) {
     if (T <= 0 || r <= 0 || n_proj <= 0) return 0;
-    return kWsHeader + decode_r_bytes(T, r, n_proj) + prefill_r_bytes(T, r, n_proj) +
-           prefill_part_bytes(T, r, n_proj);
+    if (T > kDecodeMaxT) return kWsHeader + kDecodeAreaBytes + prefill_r_bytes(T, r, n_proj) +
+                                prefill_part_bytes(T, r, n_proj);
+    return kWsHeader + kDecodeAreaBytes;
 }
 
 int glowq_repack(const void* q_canon_dev, const void* scales_dev, const void* zeros_dev, int64_t n_out,

@@ -16,8 +16,8 @@
 // Epoch: every workgroup reads it as its first load and then "arrives" (per-XCD counters, then one
 // counter over the XCDs); the last arrival of the launch resets the counters and advances the
 // epoch, so stale pairs never match and no memset is ever needed.  Consumers arrive right after
-// their first loads are issued, so the counting overlaps the weight stream instead of lengthening
-// the launch's tail; producers arrive when their pairs are written.
+// their first loads are issued and producers when their first sums are ready, so the counting
+// overlaps the weight stream instead of lengthening the launch's tail.
 
 // Main loop: the K dimension (input groups of 128) is split across the 4 wavefronts of a tile
 // (group g goes to wave g % 4).  Each wave keeps a ring of U groups in flight (4 per row tile;
@@ -87,14 +87,16 @@ __device__ __forceinline__ int arrive_xcd(const ForwardArgs& a, int prev) {
     return __hip_atomic_fetch_add(a.sync + kSyncTop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// With the result of arrive_xcd(): the launch's very last arrival resets the XCD counter and
-// advances the epoch.  Every workgroup read the epoch before arriving, so no one in this launch
-// sees the new value.
-__device__ __forceinline__ void finish(const ForwardArgs& a, int top_prev) {
+// With the result of arrive_xcd(): the launch's very last arrival resets the top counter and
+// advances the epoch (read as `epoch` by this thread), skipping 2^32 - 1 so that the tag epoch + 1
+// is never 0.  Every workgroup read the epoch before arriving, so no one in this launch sees the
+// new value.
+__device__ __forceinline__ void finish(const ForwardArgs& a, int top_prev, uint32_t epoch) {
     const int grid = a.n_prod + a.n_tiles;
     if (top_prev != (grid < kXcds ? grid : kXcds) - 1) return;
+    const uint32_t next = epoch + 1u == 0xFFFFFFFFu ? 0u : epoch + 1u;
     __hip_atomic_store(a.sync + kSyncTop, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_add(a.sync + kSyncEpoch, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.sync + kSyncEpoch, (int32_t)next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Producer workgroup: rows [p * prod_rows, (p+1) * prod_rows) of the stacked projections
@@ -105,7 +107,13 @@ __device__ void produce(const ForwardArgs& a, int p) {
     constexpr int C = 4;  // 8-input chunks per thread in flight
     constexpr int NTH = 64 * KW;
     __shared__ float part[KW][16];
-    const uint32_t tag = load_epoch(a) + 1u;
+    __shared__ uint32_t ptag;
+    // the epoch is thread 0's first load; the workgroup arrives (once) when its first partial sums
+    // are ready, by which time the read has long completed
+    uint32_t epoch0 = 0;
+    if (threadIdx.x == 0) epoch0 = load_epoch(a);
+    int arrived = 0;
+    bool first = true, scrub = true;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int T = a.T, d = a.d, r = a.r;
@@ -163,7 +171,24 @@ __device__ void produce(const ForwardArgs& a, int p) {
 #pragma unroll
                 for (int t = 0; t < 16; ++t) part[wave][t] = acc[t];
             }
+            if (first) {
+                if (threadIdx.x == 0) {
+                    ptag = epoch0 + 1u;
+                    arrived = arrive(a);
+                }
+                first = false;
+            }
             __syncthreads();
+            const uint32_t tag = ptag;
+            if (scrub && tag == 1u) {
+                // first call after the zero fill or after the epoch wrapped: clear every pair of
+                // the decode area outside this call's range (no one reads them in this call)
+                const size_t from = (size_t)kRReplicas * a.n_proj * T * r;
+                for (size_t k = from + (size_t)p * NTH + threadIdx.x; k < kDecodeAreaPairs;
+                     k += (size_t)a.n_prod * NTH)
+                    R[k] = 0ull;
+            }
+            scrub = false;
             if (threadIdx.x < 16 && (int)threadIdx.x < nt) {
                 const int t = threadIdx.x;
                 float v = part[0][t];
@@ -176,7 +201,7 @@ __device__ void produce(const ForwardArgs& a, int p) {
             __syncthreads();
         }
     }
-    if (threadIdx.x == 0) finish(a, arrive_xcd(a, arrive(a)));
+    if (threadIdx.x == 0) finish(a, arrive_xcd(a, arrived), epoch0);
 }
 
 // NTT: 16-token tiles.  RT: 16-row tiles per workgroup, multiplied side by side against the same
@@ -332,7 +357,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
         }
     }
     // the workgroup arrives once thread 0 holds the epoch (every wave reads it after the barrier)
-    int arrived = 0;
+    int arrived = 0, top_prev = -1;
     if (hand) {
         if (threadIdx.x == 0) tag_lds = epoch0 + 1u;
         __syncthreads();
@@ -352,14 +377,16 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
                 issue(u, min(i0 + U + u, n_my - 1));
             }
         }
+        // the arrival's count has returned by now: the XCD's last arrival counts the XCD before
+        // the drain rather than at the tail
+        if (hand && threadIdx.x == 0) top_prev = arrive_xcd(args, arrived);
         // drain
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (i0 + u < n_my) compute(u, i0 + u);
+    } else if (hand && threadIdx.x == 0) {
+        top_prev = arrive_xcd(args, arrived);
     }
-
-    int top_prev = -1;
-    if (hand && threadIdx.x == 0) top_prev = arrive_xcd(args, arrived);
 
     // correction epilogue: this wave adds R[t][8c..8c+8) . A[row][8c..8c+8) for chunks c = wave mod KW.
     // The first A chunks are loaded before R is needed; with one token tile R is copied once into
@@ -458,7 +485,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
             }
         }
     }
-    if (hand && threadIdx.x == 0) finish(args, top_prev);
+    if (hand && threadIdx.x == 0) finish(args, top_prev, epoch0);
 }
 
 template <int KW, int RT>

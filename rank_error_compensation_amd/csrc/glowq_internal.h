@@ -36,8 +36,11 @@ constexpr size_t kWsHeader = 2048;  // workspace bytes reserved for synchronisat
 // Synchronisation words of the decode hand-off, int32 offsets into the workspace header, each on
 // its own 64-byte line.  The projection R travels as (value, tag) pairs written with single 64-bit
 // stores; a pair is current when its tag equals epoch + 1, where epoch is the header word read by
-// every workgroup at start.  The last consumer of a call (per-XCD arrival counters, then a counter
-// over the XCDs) advances the epoch, so no memset is ever needed and stale pairs never match.
+// every workgroup at start.  The last arrival of a call (per-XCD arrival counters, then a counter
+// over the XCDs) advances the epoch, so no memset is ever needed and stale pairs never match:
+// tags run 1 .. 2^32 - 1 (the epoch skips 2^32 - 1), and a call with tag 1 (the first after the
+// zero fill or after a wrap) clears every pair outside its own range, so that a pair written
+// 2^32 - 1 calls earlier cannot be mistaken for a current one.
 constexpr int kXcds = 8;
 constexpr int kSyncEpoch = 0;     // epoch of the call in flight
 constexpr int kSyncDone = 16;     // done[x] at word kSyncDone + 16 x: consumers of XCD x finished
@@ -47,6 +50,13 @@ constexpr int kSpinLimit = 1 << 20;
 // The decode projection is written in kRReplicas copies, one per XCD (copy b % 8 is read by
 // workgroup b), so that the consumers polling it spread over eight sets of cache lines.
 constexpr int kRReplicas = 8;
+// Token count above which the prefill (dequant-to-register MFMA GEMM) kernels are used.
+constexpr int kDecodeMaxT = 64;
+// The decode pairs live in a fixed area right after the header, sized for the largest decode
+// call (T <= kDecodeMaxT, r <= kMaxRank, up to kMaxModules projections, kRReplicas copies), so
+// that no other data (the prefill projection of an earlier call) ever lies where a later decode
+// call polls for its tags.
+constexpr size_t kDecodeAreaPairs = (size_t)kDecodeMaxT * kMaxRank * kMaxModules * kRReplicas;
 constexpr int kMaxProducers = 64;
 // Largest activation block ((T + 1) x d fp16 bytes) the decode kernel stages in LDS.
 constexpr size_t kDecodeXLdsMax = 48 * 1024;
@@ -179,9 +189,6 @@ hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 
 // Largest K split of the prefill projection.
 constexpr int kProjMaxSplit = 8;
-
-// Token count above which the prefill (dequant-to-register MFMA GEMM) kernels are used.
-constexpr int kDecodeMaxT = 64;
 
 // Prefill tile shapes compiled, largest first: (TT, RR) token-tile x row-tile counts per wave.
 constexpr int kPrefillShapes[3][2] = {{8, 2}, {4, 4}, {4, 2}};

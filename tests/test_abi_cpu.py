@@ -44,13 +44,16 @@ def test_buffer_sizes():
     assert L.glowq_workspace_bytes(4, 0, 1) == 0
     hdr = 2048  # synchronisation words of the decode hand-off
     r256 = lambda n: (n + 255) // 256 * 256
-    # decode projection as (fp32, tag) pairs in 8 copies (one per XCD), the prefill projection in
-    # fp16 (r padded to 32), then the prefill projection's fp32 split-K partials (up to 8 splits)
-    ws = lambda T, r, p: hdr + r256(8 * T * r * 8 * p) + r256(T * ((r + 31) // 32 * 32) * 2 * p) + \
-        r256(8 * T * ((r + 31) // 32 * 32) * 4 * p)
-    assert L.glowq_workspace_bytes(1, 64, 1) == ws(1, 64, 1)
-    assert L.glowq_workspace_bytes(2048, 64, 1) == \
-        hdr + 8 * 2048 * 64 * 8 + 2048 * 64 * 2 + 8 * 2048 * 64 * 4
+    # the fixed decode area ((fp32, tag) pairs for T <= 64, r <= 256, 8 projections, 8 copies),
+    # then for prefill calls the projection in fp16 (r padded to 32) and its fp32 split-K
+    # partials (up to 8 splits)
+    area = 64 * 256 * 8 * 8 * 8
+    ws = lambda T, r, p: hdr + area + (0 if T <= 64 else
+                                       r256(T * ((r + 31) // 32 * 32) * 2 * p) +
+                                       r256(8 * T * ((r + 31) // 32 * 32) * 4 * p))
+    assert L.glowq_workspace_bytes(1, 64, 1) == hdr + area
+    assert L.glowq_workspace_bytes(64, 256, 8) == hdr + area
+    assert L.glowq_workspace_bytes(2048, 64, 1) == hdr + area + 2048 * 64 * 2 + 8 * 2048 * 64 * 4
     assert L.glowq_workspace_bytes(100, 8, 3) == ws(100, 8, 3)
 
 
@@ -62,7 +65,7 @@ def _w(n_out=32, k_in=256, q=FAKE, sz=FAKE):
 
 
 def call_group(x=FAKE, T=4, d=256, m=1, w=None, b=FAKE, a=None, r=8, restore=1, ws=FAKE,
-               ws_bytes=1 << 20, y=None):
+               ws_bytes=1 << 24, y=None):
     L = g.lib()
     w = w if w is not None else [_w() for _ in range(m)]
     wc = (g.QWeightC * max(1, len(w)))(*w)

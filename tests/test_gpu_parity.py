@@ -234,6 +234,43 @@ def test_decode_workspace_state_after_calls():
         assert int(hdr[1:].abs().sum()) == 0, hdr[1:].nonzero()     # counters and error flag
 
 
+def test_epoch_wrap_clears_stale_pairs():
+    """The epoch skips 2^32 - 1 (tags are never 0), and the first call after a wrap (tag 1)
+    clears every pair outside its own range: a pair planted there with the tag a later, larger
+    call will use is gone before that call runs, and every result matches the oracle."""
+    g = glowq()
+    keys = (11,)
+    r, n_out = 16, [48, 32]
+    ws = g.make_workspace(4, r, 1)
+    pairs = ws[2048:].view(torch.int64)  # the decode area: (fp32 value, u32 tag) pairs
+    hdr = ws[:2048].view(torch.int32)
+    hdr[0] = -2  # epoch 2^32 - 2: the next call uses tag 2^32 - 1
+    # pair index 8 * 1 * 1 * r (first slot past a T=1 call's range) is inside a T=4 call's range;
+    # plant a pair carrying tag 2 (what the T=4 call below will wait for) and a huge value
+    planted = 8 * r + 5
+    pairs[planted] = (2 << 32) | 0x7F000000
+    units = {T: W.make_unit("w", "group", W.make_x(T, 256, 1.19, keys + (T,)), n_out, r, keys) for T in (1, 4)}
+    devs = {T: DevUnit(u) for T, u in units.items()}
+    def run(T):
+        d = devs[T]
+        return g.group_forward(d.x, d.w, d.b, d.a, r, True, workspace=ws)
+
+    run(1)  # tag 2^32 - 1
+    torch.cuda.synchronize()
+    assert int(hdr[0]) == 0, int(hdr[0])  # 2^32 - 1 skipped
+    ys = run(1)  # tag 1: clears the area outside its range
+    torch.cuda.synchronize()
+    assert int(hdr[0]) == 1
+    assert int(pairs[planted]) == 0
+    for y, yr in zip(ys, oracle_unit(units[1])):
+        assert_parity(y, yr, "T=1 after wrap")
+    ys = run(4)  # tag 2
+    torch.cuda.synchronize()
+    for y, yr in zip(ys, oracle_unit(units[4])):
+        assert_parity(y, yr, "T=4 after wrap")
+    assert int(hdr[1:].abs().sum()) == 0
+
+
 def test_workspace_reuse_across_calls_and_paths():
     """One workspace reused by consecutive decode and prefill calls with different inputs: every
     result matches the oracle (no stale projection is ever consumed)."""
