@@ -191,6 +191,6 @@ hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 constexpr int kProjMaxSplit = 8;
 
 // Prefill tile shapes compiled, largest first: (TT, RR) token-tile x row-tile counts per wave.
-constexpr int kPrefillShapes[3][2] = {{8, 2}, {4, 4}, {4, 2}};
+constexpr int kPrefillShapes[4][2] = {{8, 4}, {8, 2}, {4, 4}, {4, 2}};
 
 }  // namespace glowq

@@ -185,8 +185,199 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const ForwardArgs args)
     }
 }
 
+// Wide tile for large grids: BM = 128 tokens x BN = 256 rows, wave w owning 4 row tiles of 16
+// rows and all 8 token tiles, so every activation operand read from LDS feeds 4 matrix-core
+// steps and every dequantised weight operand 8.  The activation tile of a 128-input group is
+// copied HBM/L2 -> LDS by the load unit itself (16-byte global_load_lds, no registers), whole
+// 256-byte rows per four lanes; in LDS row r keeps its 16-byte chunk c at position c ^ (r % 16),
+// so that the operand reads (16 rows, one chunk each) hit 16 different bank groups.  Two LDS
+// buffers (2 x 32 KiB): the copy of group g + 1 and the next weight blocks (registers) are in
+// flight while group g is multiplied.  Inside a group the 32 (slice, token tile) steps are issued
+// in a fixed order: operand reads two steps ahead, the next slice's unpacking spread between the
+// matrix-core steps.  Tokens past T read row T - 1 and row tiles past the module read its last
+// tile; neither is stored.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs args) {
+    constexpr int TT = 8, RR = 4, BM = 128;
+    extern __shared__ __attribute__((aligned(16))) u4 xw[];  // [2][TT * 4][64]
+
+    const int L = xcd_remap(blockIdx.x, args.n_tiles);
+    const int mb = L % args.m_tiles, nbl = L / args.m_tiles;
+    const ModuleArgs M = args.mod[module_of(args, nbl)];
+    const int nb = nbl - M.tile_begin;
+    const int m0 = mb * BM;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = args.T, d = args.d, G = args.G;
+    const NibConsts nc = nib_consts();
+    const int rt0 = nb * 4 * RR + wave * RR;
+    const int NT = M.n_tiles16;
+
+    // weight blocks: uniform byte offsets of this wave's row tiles (clamped to the module's last
+    // tile) plus one per-lane 32-bit offset; activations: per-lane 32-bit byte offsets of the two
+    // token rows this lane copies (the launcher keeps T d 2 below 2^31)
+    uint32_t rtc[RR];
+#pragma unroll
+    for (int rr = 0; rr < RR; ++rr) rtc[rr] = (uint32_t)min(rt0 + rr, NT - 1);
+    const uint32_t qlane = lane * 16, zlane = (lane & 15) * 4;
+    auto qaddr = [&](int g, int rr) {
+        return reinterpret_cast<const u4*>(M.q + ((size_t)g * NT + rtc[rr]) * 1024 + qlane);
+    };
+    auto zaddr = [&](int g, int rr) {
+        return reinterpret_cast<const uint32_t*>(M.sz + ((size_t)g * NT + rtc[rr]) * 64 + zlane);
+    };
+    // activation copy: instruction i of wave w fills tile rows 32 w + 4 i .. + 3 (256 bytes each,
+    // whole cache lines); lane l lands at LDS slot 16 l, i.e. row 32 w + 4 i + l / 16, 16-byte
+    // position l % 16, which holds input chunk (l % 16) ^ (row % 16) of that row (XOR swizzle)
+    uint32_t xoff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 32 * wave + 4 * i + (lane >> 4);
+        const int t = min(m0 + row, T - 1);
+        xoff[i] = (uint32_t)(t * d + 8 * ((lane & 15) ^ (row & 15))) * 2u;
+    }
+    const char* xbase = reinterpret_cast<const char*>(args.x);
+    auto copy_x = [&](int g, int buf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(xbase + (size_t)g * kGroup * 2 + xoff[i]),
+                                             (lds_void*)(xw + ((size_t)buf * BM + 32 * wave + 4 * i) * 16), 16, 0, 0);
+    };
+    // operand read of slice j: lane l takes row 16 tt + l % 16, chunk 4 j + l / 16, swizzled
+    uint32_t bofs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bofs[j] = (uint32_t)((lane & 15) * 16 + ((4 * j + (lane >> 4)) ^ (lane & 15)));
+
+    u4 qv[RR];
+    uint32_t zs[RR];
+    copy_x(0, 0);
+#pragma unroll
+    for (int rr = 0; rr < RR; ++rr) {
+        qv[rr] = *qaddr(0, rr);
+        zs[rr] = *zaddr(0, rr);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    f4 acc[TT][RR];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = f4{0.f, 0.f, 0.f, 0.f};
+
+    for (int g = 0; g < G; ++g) {
+        const int buf = g & 1;
+        const bool more = g + 1 < G;
+        u4 qn[RR];
+        uint32_t zn[RR];
+        if (more) {
+            copy_x(g + 1, buf ^ 1);
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) {
+                qn[rr] = *qaddr(g + 1, rr);
+                zn[rr] = *zaddr(g + 1, rr);
+            }
+        }
+        h2 c1024[RR], c64[RR];
+        h8 s8[RR];
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr) {
+            zero_consts(zs[rr], c1024[rr], c64[rr]);
+            const _Float16 s = as_h2(zs[rr])[1];
+            s8[rr] = h8{s, s, s, s, s, s, s, s};
+        }
+        const u4* xb = xw + (size_t)buf * BM * 16;
+        {
+            // 32 steps (slice j, token tile tt): the activation operand of step st is read two
+            // steps ahead, and the weight operands of slice j + 1 are unpacked during slice j, one
+            // row tile every other step, so that the unpacking issues while the matrix cores run
+            constexpr int NS = 4 * TT;
+            h8 bq[3];
+            auto bread = [&](int st) { return __builtin_bit_cast(h8, xb[(st % TT) * 256 + bofs[st / TT]]); };
+            bq[0] = bread(0);
+            bq[1] = bread(1);
+            h8 aj[4][RR];
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) aj[0][rr] = nib8_minus_z(qv[rr][0], c1024[rr], c64[rr], nc) * s8[rr];
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const int j = st / TT, tt = st % TT;
+                if (st + 2 < NS) bq[(st + 2) % 3] = bread(st + 2);
+                if (j < 3 && (tt & 1) == 0) {
+                    const int rr = tt >> 1;
+                    aj[j + 1][rr] = nib8_minus_z(qv[rr][j + 1], c1024[rr], c64[rr], nc) * s8[rr];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = mfma16(aj[j][rr], bq[st % 3], acc[tt][rr]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (more) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) {
+                qv[rr] = qn[rr];
+                zs[rr] = zn[rr];
+            }
+        }
+        __syncthreads();
+    }
+
+    // correction: r_pad / 32 more K steps, A-operand A_i rows, B-operand R tokens
+    if (args.r > 0 && M.a != nullptr) {
+        const int r = args.r, rp = args.r_pad;
+        const _Float16* R = reinterpret_cast<const _Float16*>(args.R) + (size_t)M.proj * T * rp;
+        const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+        const int kofs = 8 * (lane >> 4);
+        for (int kb = 0; kb < rp / 32; ++kb) {
+            const int col = 32 * kb + kofs;
+            h8 a[RR];
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) {
+                const int row = (rt0 + rr) * 16 + (lane & 15);
+                a[rr] = (row < M.n_out && col < r) ? load_h8(M.a + (size_t)row * r + col) : zero8;
+            }
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const int t = m0 + 16 * tt + (lane & 15);
+                const h8 b = t < T ? load_h8(R + (size_t)t * rp + col) : zero8;
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = mfma16(a[rr], b, acc[tt][rr]);
+            }
+        }
+    }
+
+    const bool vec = (M.n_out & 3) == 0;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const int t = m0 + 16 * tt + (lane & 15);
+        if (t >= T) continue;
+        _Float16* yrow = M.y + (size_t)t * M.n_out;
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr) {
+            const int row0 = (rt0 + rr) * 16 + 4 * (lane >> 4);
+            if (rt0 + rr >= NT) continue;
+            const f4 v = acc[tt][rr];
+            if (vec && row0 + 3 < M.n_out) {
+                const h2 lo = {(_Float16)v[0], (_Float16)v[1]}, hi = {(_Float16)v[2], (_Float16)v[3]};
+                *reinterpret_cast<u2*>(yrow + row0) = u2{as_u32(lo), as_u32(hi)};
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (row0 + i < M.n_out) yrow[row0 + i] = (_Float16)v[i];
+            }
+        }
+    }
+}
+
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
     const dim3 grid(a.n_tiles), block(256);
+    if (a.tile_tt == 8 && a.tile_rr == 4) {
+        hipLaunchKernelGGL(prefill_wide_kernel, grid, block, 2 * 8 * 4 * 64 * sizeof(u4), stream, a);
+        return hipGetLastError();
+    }
     if (a.tile_tt == 4 && a.tile_rr == 4)
         hipLaunchKernelGGL((prefill_kernel<4, 4>), grid, block, 0, stream, a);
     else if (a.tile_tt == 8 && a.tile_rr == 2)
