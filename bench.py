@@ -241,19 +241,25 @@ def extra_prefill_gateup(g, reps=20):
     ys = [torch.empty(T, q.n_out, dtype=torch.float16, device="cuda") for q in w]
     stream = torch.cuda.current_stream()
     out = {}
-    for name, fn in (("group", lambda: g.group_forward(u.x, w, u.b, u.a, u.r, True, workspace=ws, y=ys)),
-                     ("layerwise", lambda: g.layerwise_forward(u.x, w, u.b_layerwise, u.a, u.r, True,
-                                                               workspace=ws, y=ys))):
-        for _ in range(3):
+    fns = (("group", lambda: g.group_forward(u.x, w, u.b, u.a, u.r, True, workspace=ws, y=ys)),
+           ("layerwise", lambda: g.layerwise_forward(u.x, w, u.b_layerwise, u.a, u.r, True, workspace=ws, y=ys)))
+    # the two are timed call by call, alternating, so that both see the same clock and power state
+    # (the GEMM runs power-limited and the clock drifts over a run); median of the calls
+    for _ in range(3):
+        for _, fn in fns:
             fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
+    torch.cuda.synchronize()
+    evs = {name: [] for name, _ in fns}
+    for _ in range(reps):
+        for name, fn in fns:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
             fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / reps
+            e1.record(stream)
+            evs[name].append((e0, e1))
+    torch.cuda.synchronize()
+    for name, _ in fns:
+        t = statistics.median(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs[name])
         fl = unit_flops(T, 4096, u.n_outs, u.r, True, 1 if name == "group" else 2)
         out[name] = {"us": round(t * 1e6, 2), "tokens_per_s": round(T / t, 1),
                      "alg_TFLOP_per_s": round(unit_flops(T, 4096, u.n_outs, u.r, True) / t / 1e12, 2),
@@ -348,10 +354,22 @@ def main():
             for u in units_lw:
                 call_unit(u, g, ws_lw, layerwise=False)
 
-        t_lw = time_steps(run_lw, args.steps, args.warmup) / args.steps
-        t_gr = time_steps(run_grp, args.steps, args.warmup) / args.steps
-        d_lw = sum(per_launch_events(units_lw, descr_lw, g, args.event_reps, layerwise=True))
-        d_gr = sum(per_launch_events(units_lw, descr_lw, g, args.event_reps, layerwise=False))
+        # alternate the two schedules step by step (same clock and power state for both)
+        t_lw = t_gr = 0.0
+        for _ in range(args.warmup):
+            run_lw()
+            run_grp()
+        for _ in range(args.steps):
+            t_lw += time_steps(run_lw, 1, 0)
+            t_gr += time_steps(run_grp, 1, 0)
+        t_lw /= args.steps
+        t_gr /= args.steps
+        d_lw = d_gr = 0.0
+        for _ in range(2):
+            d_lw += sum(per_launch_events(units_lw, descr_lw, g, max(1, args.event_reps // 2), layerwise=True))
+            d_gr += sum(per_launch_events(units_lw, descr_lw, g, max(1, args.event_reps // 2), layerwise=False))
+        d_lw /= 2
+        d_gr /= 2
         extra["layerwise_vs_group_T1_path"] = {
             "group_us_per_step_percall": round(t_gr * 1e6, 1), "layerwise_us_per_step_percall": round(t_lw * 1e6, 1),
             "group_kernel_sum_us": round(d_gr * 1e6, 1), "layerwise_kernel_sum_us": round(d_lw * 1e6, 1),
