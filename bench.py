@@ -63,7 +63,7 @@ def build_path(T, device, keep_layers=(), layerwise=False):
     mask = None
     t0 = time.time()
     for l in range(W.LLAMA2_7B["n_layers"]):
-        layer_units, mask = W.config3_inputs(T, device=device, layers=[l], layerwise=layerwise)
+        layer_units, mask = W.llama2_path_inputs(T, device=device, layers=[l], layerwise=layerwise)
         for u in layer_units[l]:
             qws = [g.QWeight.from_workload(q, device=device) for q in u.weights]
             ys = [torch.empty(T, q.n_out, dtype=torch.float16, device=device) for q in u.weights]
@@ -192,11 +192,11 @@ def cpu_baseline(keep, mask):
 
 # ------------------------------------------------------------------ extra measurements
 def rotating_group(T, copies, g, device):
-    """Config-1 QKV group with `copies` weight copies at distinct addresses (more than twice the
+    """LLaMA-2-7B QKV group (d = 4096, 3 x 4096) with `copies` weight copies at distinct addresses (more than twice the
     256 MB last-level cache), cycled so that each call streams its weights from HBM."""
     import torch
     import workload as W
-    u = W.config1_unit(T, device=device)
+    u = W.llama2_qkv_unit(T, device=device)
     base = [g.QWeight.from_workload(q, device=device) for q in u.weights]
     sets = [base] + [[g.QWeight(w.q.clone(), w.sz.clone(), w.n_out, w.k_in) for w in base]
                      for _ in range(copies - 1)]
@@ -235,7 +235,7 @@ def extra_prefill_gateup(g, reps=20):
     import torch
     import workload as W
     T = 2048
-    u = W.config2_unit(T, device="cuda", layerwise=True)
+    u = W.llama2_gateup_unit(T, device="cuda", layerwise=True)
     w = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
     ws = g.make_workspace(T, u.r, 2)
     ys = [torch.empty(T, q.n_out, dtype=torch.float16, device="cuda") for q in w]
@@ -437,7 +437,7 @@ def build_path_keep(T, device, layers):
     import workload as W
     keep, mask = {}, None
     for l in layers:
-        lu, mask = W.config3_inputs(T, device=device, layers=[l])
+        lu, mask = W.llama2_path_inputs(T, device=device, layers=[l])
         keep[l] = lu[l]
     return None, None, mask, keep
 

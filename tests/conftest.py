@@ -11,4 +11,4 @@ if HERE not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    config.addinivalue_line("markers", "slow: full-size parity cases (GPU box)")
+    config.addinivalue_line("markers", "slow: full-size parity cases (long on the GPU)")

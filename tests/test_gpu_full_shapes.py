@@ -37,13 +37,13 @@ def _sample_rows(T, n, seed):
 
 
 @pytest.mark.parametrize("T", [1, 512])
-def test_config3_path_window(T):
+def test_llama2_path_window(T):
     """Layers 0..3 of the path run as one schedule (QKV group, o_proj solo, gate/up group,
     down_proj solo per layer) with the restore mask of the full 32-layer path."""
     g = glowq()
     layers = [0, 1, 2, 3]
-    log(f"generating config 3 layers {layers} T={T}")
-    units, mask = W.config3_inputs(T, device="cuda", layers=layers)
+    log(f"generating 32-layer path inputs, layers {layers} T={T}")
+    units, mask = W.llama2_path_inputs(T, device="cuda", layers=layers)
     assert sum(mask) == 16
     assert any(mask[l] for l in layers) and not all(mask[l] for l in layers), "window mixes restored/unrestored"
     plan_units, devs = [], []
@@ -63,13 +63,13 @@ def test_config3_path_window(T):
         ref = oracle_unit(u, restore=bool(mask[l]), rows=rows)
         for i, (y, yr) in enumerate(zip(pu.y, ref)):
             assert_parity(y[torch.from_numpy(rows).cuda()], yr,
-                          f"cfg3 T={T} layer {l} {u.name}[{i}] restore={mask[l]}")
+                          f"path T={T} layer {l} {u.name}[{i}] restore={mask[l]}")
 
 
 @pytest.mark.parametrize("T,r", [(64, 64), (64, 128), (4096, 64), (4096, 128)])
-def test_config4_gqa(T, r):
-    log(f"generating config 4 T={T} r={r}")
-    units = W.config4_units(T, r, device="cuda")
+def test_llama3_gqa(T, r):
+    log(f"generating GQA units T={T} r={r}")
+    units = W.llama3_gqa_units(T, r, device="cuda")
     rows = _sample_rows(T, 48, 4)
     for u in units:
         du = DevUnit(u)
@@ -77,25 +77,25 @@ def test_config4_gqa(T, r):
         torch.cuda.synchronize()
         ref = oracle_unit(u, rows=rows)
         for i, (y, yr) in enumerate(zip(ys, ref)):
-            assert_parity(y[torch.from_numpy(rows).cuda()], yr, f"cfg4 T={T} r={r} {u.name}[{i}]")
+            assert_parity(y[torch.from_numpy(rows).cuda()], yr, f"gqa T={T} r={r} {u.name}[{i}]")
 
 
 @pytest.mark.parametrize("T", [1, 16])
-def test_config1_layerwise_full(T):
+def test_llama2_qkv_layerwise_full(T):
     """The layerwise baseline (one projection per module) at the full QKV shape."""
-    unit = W.config1_unit(T, device="cuda", layerwise=True)
+    unit = W.llama2_qkv_unit(T, device="cuda", layerwise=True)
     du = DevUnit(unit, layerwise=True)
     ys = du.forward_layerwise()
     ref = oracle_unit(unit, layerwise=True)
     for i, (y, yr) in enumerate(zip(ys, ref)):
-        assert_parity(y, yr, f"cfg1 layerwise T={T} module {i}")
+        assert_parity(y, yr, f"qkv layerwise T={T} module {i}")
 
 
 def test_prefill_deterministic_and_row_independent():
     """Prefill results are bitwise repeatable, and a token's output does not depend on the other
     tokens of the batch (the first 300 tokens alone give the same rows as the full batch)."""
     g = glowq()
-    unit = W.config2_unit(700, device="cuda")
+    unit = W.llama2_gateup_unit(700, device="cuda")
     du = DevUnit(unit)
     y1 = [t.clone() for t in du.forward()]
     y2 = du.forward()

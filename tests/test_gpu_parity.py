@@ -84,10 +84,10 @@ def test_repack_rejects_bad_zero_points():
         g.QWeight.from_canonical(qw.q_packed, s, qw.z)
 
 
-# ------------------------------------------------------------------ config 0: tiny QKV group
+# ------------------------------------------------------------------ tiny QKV group (d = 256)
 @pytest.fixture(scope="module")
-def cfg0_unit():
-    c = W.config0_inputs()
+def tiny_unit():
+    c = W.tiny_qkv_inputs()
     w_hats = [G.dequant_qw(q) for q in c["qw"]]
     E = [G._f64(w16) - wh for w16, wh in zip(c["w16"], w_hats)]
     Q, lam = c["Q"].numpy(), c["lam"].numpy()
@@ -98,21 +98,21 @@ def cfg0_unit():
     return unit
 
 
-def test_config0_group(cfg0_unit):
-    du = DevUnit(cfg0_unit)
+def test_tiny_qkv_group(tiny_unit):
+    du = DevUnit(tiny_unit)
     ys = du.forward()
-    ref = oracle_unit(cfg0_unit)
+    ref = oracle_unit(tiny_unit)
     for i, (y, yr) in enumerate(zip(ys, ref)):
-        assert_parity(y, yr, f"cfg0 module {i}")
+        assert_parity(y, yr, f"tiny module {i}")
 
 
 @pytest.mark.parametrize("restore,r", [(False, 16), (True, 0)])
-def test_config0_no_correction(cfg0_unit, restore, r):
-    du = DevUnit(cfg0_unit)
+def test_tiny_qkv_no_correction(tiny_unit, restore, r):
+    du = DevUnit(tiny_unit)
     ys = du.forward(restore=restore, r=r)
-    ref = oracle_unit(cfg0_unit, restore=restore, r=r)
+    ref = oracle_unit(tiny_unit, restore=restore, r=r)
     for i, (y, yr) in enumerate(zip(ys, ref)):
-        assert_parity(y, yr, f"cfg0 restore={restore} r={r} module {i}")
+        assert_parity(y, yr, f"tiny restore={restore} r={r} module {i}")
 
 
 # ------------------------------------------------------------------ ragged shapes, both paths
@@ -166,24 +166,24 @@ def test_t_zero_is_noop():
     assert ys[0].shape == (0, 32)
 
 
-# ------------------------------------------------------------------ config 1: QKV decode
+# ------------------------------------------------------------------ LLaMA-2-7B QKV decode
 @pytest.fixture(scope="module")
-def cfg1_units():
-    return {T: W.config1_unit(T) for T in (1, 4, 16)}
+def qkv_units():
+    return {T: W.llama2_qkv_unit(T) for T in (1, 4, 16)}
 
 
 @pytest.mark.parametrize("T", [1, 4, 16])
-def test_config1_decode(cfg1_units, T):
-    unit = cfg1_units[T]
+def test_llama2_qkv_decode(qkv_units, T):
+    unit = qkv_units[T]
     du = DevUnit(unit)
     ys = du.forward()
     ref = oracle_unit(unit)
     for i, (y, yr) in enumerate(zip(ys, ref)):
-        assert_parity(y, yr, f"cfg1 T={T} module {i}")
+        assert_parity(y, yr, f"qkv T={T} module {i}")
 
 
-def test_config1_deterministic(cfg1_units):
-    du = DevUnit(cfg1_units[4])
+def test_llama2_qkv_deterministic(qkv_units):
+    du = DevUnit(qkv_units[4])
     first = [y.clone() for y in du.forward()]
     for _ in range(20):
         ys = du.forward()
@@ -191,17 +191,17 @@ def test_config1_deterministic(cfg1_units):
             assert torch.equal(a, b)
 
 
-# ------------------------------------------------------------------ config 2: gate/up prefill
-def test_config2_prefill():
-    log("generating config 2")
-    unit = W.config2_unit(2048)
+# ------------------------------------------------------------------ LLaMA-2-7B gate/up prefill
+def test_llama2_gateup_prefill():
+    log("generating gate/up T=2048")
+    unit = W.llama2_gateup_unit(2048)
     du = DevUnit(unit)
     ys = du.forward()
     torch.cuda.synchronize()
-    log("oracle config 2")
+    log("oracle gate/up T=2048")
     ref = oracle_unit(unit)
     for i, (y, yr) in enumerate(zip(ys, ref)):
-        assert_parity(y, yr, f"cfg2 module {i}")
+        assert_parity(y, yr, f"gate/up T=2048 module {i}")
     # decode and prefill kernels agree on the same tokens (first 64 through the decode path)
     yd = du.forward(x=du.x[:64].contiguous())
     for i, (a, b) in enumerate(zip(yd, ys)):

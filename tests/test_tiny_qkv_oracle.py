@@ -9,8 +9,8 @@ from oracle import solve as S
 
 
 @pytest.fixture(scope="module")
-def cfg0():
-    c = W.config0_inputs()
+def tiny():
+    c = W.tiny_qkv_inputs()
     w_hats = [G.dequant_qw(q) for q in c["qw"]]
     E = [G._f64(w16) - wh for w16, wh in zip(c["w16"], w_hats)]
     Q, lam = c["Q"].numpy(), c["lam"].numpy()
@@ -18,8 +18,8 @@ def cfg0():
     return c, w_hats, E, A, B, sv
 
 
-def test_config0_bruteforce(cfg0):
-    c, w_hats, E, A, B, _ = cfg0
+def test_tiny_qkv_bruteforce(tiny):
+    c, w_hats, E, A, B, _ = tiny
     a16 = [a.astype(np.float16) for a in A]
     b16 = B.astype(np.float16)
     ys = G.group_forward(c["x"], w_hats, b16, a16, restore=True)
@@ -29,10 +29,10 @@ def test_config0_bruteforce(cfg0):
         assert np.max(np.abs(y - yb)) <= 1e-13 * np.max(np.abs(yb))
 
 
-def test_config0_correction_reduces_error(cfg0):
+def test_tiny_qkv_correction_reduces_error(tiny):
     """With covariance-aligned factors the corrected output is closer to the fp16 model's
     output than the quantised product alone."""
-    c, w_hats, E, A, B, sv = cfg0
+    c, w_hats, E, A, B, sv = tiny
     x = G._f64(c["x"])
     ys = G.group_forward(c["x"], w_hats, B, A, restore=True)
     y0 = G.group_forward(c["x"], w_hats, B, A, restore=False)

@@ -10,8 +10,9 @@ It holds none of the correction method's arithmetic: no shared projection, no
 correction epilogue and no factor solve (the whitened SVD that yields exact factors
 lives in the oracle).  The base quantiser here is the W4A16 "INT4, g128" weight format
 that the correction is applied on top of (GlowQ paper note, "Experimental setup";
-GlowQ arXiv page, Table 1 header "INT4, g128"); its rounding rules are the workload
-recipe and are listed in the design doc.
+GlowQ arXiv page, Table 1 header "INT4, g128"); its rounding rules (half-to-even, zero
+point from the fp16 scale, q clipped to 0..15, z not clamped) are this recipe's reading of
+that format.
 
 All functions take a ``device`` so that large workloads can be drawn directly on the
 GPU (random streams then differ from the CPU ones; both sides of a parity test always
@@ -251,7 +252,7 @@ ALPHA_QKV = 1.19
 ALPHA_MLP = 0.77
 
 
-def config0_inputs(device="cpu"):
+def tiny_qkv_inputs(device="cpu"):
     """Tiny QKV group, d = 256, 3 x 256 outputs, T = 8, r = 16.  Returns the fp16
     weights before quantisation, the quantised weights, X and the covariance (Q, lam)
     so that exact whitened factors can be solved by the caller."""
@@ -266,13 +267,13 @@ def config0_inputs(device="cpu"):
     return dict(x=x, w16=w16, qw=qw, Q=Q, lam=lam, r=16, d=d, T=T)
 
 
-def config1_unit(T: int, device="cpu", layerwise=False) -> Unit:
+def llama2_qkv_unit(T: int, device="cpu", layerwise=False) -> Unit:
     keys = (0, 1, 0, 0)
     x = make_x(T, 4096, ALPHA_QKV, keys, device)
     return make_unit("qkv", "group", x, [4096, 4096, 4096], 64, keys, device, layerwise=layerwise)
 
 
-def config2_unit(T: int = 2048, device="cpu", layerwise=False) -> Unit:
+def llama2_gateup_unit(T: int = 2048, device="cpu", layerwise=False) -> Unit:
     keys = (0, 2, 0, 0)
     x = make_x(T, 4096, ALPHA_MLP, keys, device)
     return make_unit("gateup", "group", x, [11008, 11008], 64, keys, device, layerwise=layerwise)
@@ -281,7 +282,7 @@ def config2_unit(T: int = 2048, device="cpu", layerwise=False) -> Unit:
 LLAMA2_7B = dict(d=4096, inter=11008, n_layers=32)
 
 
-def config3_inputs(T: int, device="cpu", layers: Optional[Sequence[int]] = None, r: int = 64,
+def llama2_path_inputs(T: int, device="cpu", layers: Optional[Sequence[int]] = None, r: int = 64,
                    layerwise=False):
     """32-layer LLaMA-2-7B linear path.  One activation per input kind, shared by all
     layers (the layers are not chained).  Returns (units per layer, mask per layer)."""
@@ -304,7 +305,7 @@ def config3_inputs(T: int, device="cpu", layers: Optional[Sequence[int]] = None,
     return out, mask
 
 
-def config4_units(T: int, r: int, device="cpu", layerwise=False, which=("qkv", "gateup", "down")):
+def llama3_gqa_units(T: int, r: int, device="cpu", layerwise=False, which=("qkv", "gateup", "down")):
     """LLaMA-3.1-8B GQA shapes: QKV 4096 -> 4096 + 1024 + 1024, gate/up 4096 -> 2 x 14336,
     solo down 14336 -> 4096."""
     units = []
