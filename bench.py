@@ -282,7 +282,7 @@ def main():
                          "device copy (a reference kernel of known traffic for hardware counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
+        print("bench.py: the library runs on one GPU (no multi-GPU path is built); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
