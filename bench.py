@@ -269,6 +269,45 @@ def extra_prefill_gateup(g, reps=20):
     return out
 
 
+def achievable_peaks(reps=5):
+    """The achievable peaks on this GPU, measured by the probe library: a streaming read of a
+    4 GiB buffer (16 times the last-level cache) and a matrix-core-only fp16 loop."""
+    import torch
+    from rank_error_compensation_amd import probe
+    stream = torch.cuda.current_stream()
+    n = 4 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(4096 * 256 * 16, dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hbm = 0.0
+    for blocks in (512, 1024, 2048, 4096):  # best launch shape
+        probe.read(src, sink, blocks)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            probe.read(src, sink, blocks)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        hbm = max(hbm, n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src
+    mblocks, iters = 512, 20000
+    msink = torch.empty(mblocks * 256 * 16, dtype=torch.uint8, device="cuda")
+    probe.mfma_f16(iters // 10, msink, mblocks)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    fl = 0.0
+    for _ in range(reps):
+        fl += probe.mfma_f16(iters, msink, mblocks)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mfma = fl / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    torch.cuda.empty_cache()
+    return {"hbm_read_GB_per_s": round(hbm, 1), "mfma_f16_TFLOP_per_s": round(mfma, 1),
+            "how": "probe library: 4 GiB nontemporal streaming read (best of 512..4096 workgroups of 256 "
+                   "threads, 8 x 16 B in flight each); v_mfma_f32_16x16x32_f16 loop on registers (512 x 4 "
+                   "waves, 8 independent chains each, sustained over 5 launches)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +356,11 @@ def main():
     value = T * args.steps / elapsed
     log(f"[bench] decode path: {ms * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us), {value:.1f} tokens/s")
 
+    # achievable peaks on this GPU (after the timed region, so that the matrix-core loop's heat
+    # does not touch the headline)
+    peaks = achievable_peaks()
+    log(f"[bench] achievable peaks: {peaks}")
+
     # ---- dominant kernel: the fused decode kernel, one launch per unit (every launch of the step)
     launch_us = elapsed / args.steps / len(descr) * 1e6
     achieved = sum(nbytes) / (elapsed / args.steps) / 1e9
@@ -332,6 +376,8 @@ def main():
         e["GB_per_s"] = round(e["bytes"] / (e["us"] * 1e-6) / 1e9, 1)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "peak_measured": peaks["hbm_read_GB_per_s"],
+                "frac_measured": round(achieved / peaks["hbm_read_GB_per_s"], 4),
                 "kernel": "glowq::decode_kernel (fused projection + INT4 product + correction)",
                 "launches_per_step": len(descr),
                 "alg_bytes_per_launch_mean": int(sum(nbytes) / len(nbytes)),
@@ -394,6 +440,9 @@ def main():
         extra["decode_qkv_T1"] = extra_decode_qkv(g)
         log(f"[bench] QKV decode T=1: {extra['decode_qkv_T1']}")
         extra["prefill_gateup_T2048"] = extra_prefill_gateup(g)
+        for k in ("group", "layerwise"):
+            e = extra["prefill_gateup_T2048"][k]
+            e["frac_mfma_measured_peak"] = round(e["alg_TFLOP_per_s"] / peaks["mfma_f16_TFLOP_per_s"], 4)
         log(f"[bench] gate/up prefill T=2048: {extra['prefill_gateup_T2048']}")
 
     cpu = None
@@ -427,7 +476,7 @@ def main():
         "config": {"workload": "llama2-7b-32-layer-linear-path decode T=1 r=64 restore=16/32 layers",
                    "T": 1, "r": 64, "layers": 32, "d": 4096, "inter": 11008,
                    "units_per_step": len(descr), "weights": "INT4-g128 fp16 scale/zero"},
-        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+        "roofline": roofline, "cpu_baseline": cpu, "achievable_peaks": peaks, "extra": extra,
     }
     print(json.dumps(line), flush=True)
 

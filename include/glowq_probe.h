@@ -1,0 +1,37 @@
+/*
+ * glowq_probe.h -- measurement probes shipped as a separate library (libglowq_probe.so) next to
+ * libglowq.so.  They are not part of the forward path: the benchmark uses them to measure, on
+ * the GPU it runs on, the achievable peaks its kernels are compared against (an HBM streaming
+ * read and a matrix-core-only loop), next to the vendor peaks.
+ *
+ * Both launch asynchronously on `stream` and return 0, or -1 for an invalid argument (checked on
+ * the host before any HIP call), or -6 for a launch failure.  All pointers are device pointers
+ * owned by the caller, 16-byte aligned.
+ */
+#ifndef GLOWQ_PROBE_H
+#define GLOWQ_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` (a multiple of 16) at src_dev with `blocks` workgroups of 256 threads; sink_dev
+ * receives blocks * 256 16-byte words (the xor of what each thread read). */
+int glowq_probe_read(const void* src_dev, size_t bytes, void* sink_dev, int32_t blocks, hipStream_t stream);
+
+/* `blocks` workgroups of 4 wavefronts, each wavefront running `iters` rounds of 8 independent
+ * v_mfma_f32_16x16x32_f16 on register operands; sink_dev receives blocks * 256 fp32 x4. */
+int glowq_probe_mfma_f16(int64_t iters, void* sink_dev, int32_t blocks, hipStream_t stream);
+
+/* Dense fp16 floating-point operations one glowq_probe_mfma_f16 call performs. */
+double glowq_probe_mfma_f16_flops(int64_t iters, int32_t blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLOWQ_PROBE_H */

@@ -1,0 +1,84 @@
+// Measurement probes (libglowq_probe.so): the achievable peaks that the forward kernels are
+// compared against, measured on the same GPU in the same process.
+//
+//   * a streaming read: 16-byte nontemporal loads over a buffer much larger than the last-level
+//     cache, eight per thread in flight, grid-stride, folded into a per-thread xor (the only
+//     store) -- the HBM read rate a kernel with a perfect access pattern reaches;
+//   * a matrix-core loop: v_mfma_f32_16x16x32_f16 on register operands, eight independent
+//     accumulators per wave, no memory traffic in the loop -- the dense fp16 rate the matrix
+//     cores sustain (including any clock reduction under that load).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "glowq_probe.h"
+
+namespace {
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void read_kernel(const u4* __restrict__ p, uint64_t n16, u4* __restrict__ sink) {
+    const uint64_t tid = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    const uint64_t stride = (uint64_t)gridDim.x * 256;
+    u4 acc = {0u, 0u, 0u, 0u};
+    for (uint64_t i = tid; i < n16; i += 8 * stride) {
+        u4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint64_t j = i + (uint64_t)u * stride;
+            v[u] = j < n16 ? __builtin_nontemporal_load(p + j) : u4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u];
+    }
+    sink[tid] = acc;
+}
+
+__global__ __launch_bounds__(256) void mfma_kernel(int64_t iters, f4* __restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    // small exact operands (no overflow over any number of iterations of a fixed sum)
+    h8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (_Float16)((float)((lane + e) & 3) * 0.25f);
+        b[e] = (_Float16)((float)((lane * 3 + e) & 3) * 0.125f);
+    }
+    f4 acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[k], 0, 0, 0);
+    }
+    f4 s = acc[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) s += acc[k];
+    sink[(uint64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int glowq_probe_read(const void* src_dev, size_t bytes, void* sink_dev, int32_t blocks, hipStream_t stream) {
+    if (src_dev == nullptr || sink_dev == nullptr || blocks < 1 || bytes % 16 != 0) return -1;
+    if ((reinterpret_cast<uintptr_t>(src_dev) & 15) != 0 || (reinterpret_cast<uintptr_t>(sink_dev) & 15) != 0)
+        return -1;
+    hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const u4*>(src_dev), (uint64_t)(bytes / 16), static_cast<u4*>(sink_dev));
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int glowq_probe_mfma_f16(int64_t iters, void* sink_dev, int32_t blocks, hipStream_t stream) {
+    if (sink_dev == nullptr || blocks < 1 || iters < 0) return -1;
+    if ((reinterpret_cast<uintptr_t>(sink_dev) & 15) != 0) return -1;
+    hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, iters, static_cast<f4*>(sink_dev));
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+double glowq_probe_mfma_f16_flops(int64_t iters, int32_t blocks) {
+    return (double)blocks * 4.0 * (double)iters * 8.0 * 16.0 * 16.0 * 32.0 * 2.0;
+}
+
+}  // extern "C"

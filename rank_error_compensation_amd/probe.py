@@ -1,0 +1,52 @@
+"""ctypes binding of libglowq_probe.so (include/glowq_probe.h): the achievable-peak probes used
+by the benchmark.  Argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libglowq_probe.so")
+_vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+EXPORTS = {
+    "glowq_probe_read": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
+    "glowq_probe_mfma_f16": (ctypes.c_int, [_i64, _vp, _i32, _vp]),
+    "glowq_probe_mfma_f16_flops": (ctypes.c_double, [_i64, _i32]),
+}
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP libraries first "
+                               "(python -m rank_error_compensation_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def read(src: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
+    rc = lib().glowq_probe_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), blocks,
+                                _stream())
+    if rc != 0:
+        raise RuntimeError(f"glowq_probe_read failed ({rc})")
+
+
+def mfma_f16(iters: int, sink: torch.Tensor, blocks: int) -> float:
+    """Launch the matrix-core loop; returns the dense fp16 flops it performs."""
+    rc = lib().glowq_probe_mfma_f16(iters, sink.data_ptr(), blocks, _stream())
+    if rc != 0:
+        raise RuntimeError(f"glowq_probe_mfma_f16 failed ({rc})")
+    return lib().glowq_probe_mfma_f16_flops(iters, blocks)

@@ -152,3 +152,22 @@ def test_path_validates_every_unit_first():
                        ctypes.cast(ac, P(ctypes.c_void_p)), 8, 1, ctypes.cast(yc, P(ctypes.c_void_p)))
     assert L.glowq_path_forward((g.UnitC * 1)(bad_kind), 1, FAKE, 1 << 20, None) == g.ERR_INVALID_ARG
     assert L.glowq_path_forward(None, 3, FAKE, 1 << 20, None) == g.ERR_INVALID_ARG
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """The measurement probes (libglowq_probe.so, include/glowq_probe.h): every declared function
+    is exported, and invalid arguments are rejected before any HIP call."""
+    from rank_error_compensation_amd import probe
+    src = open(os.path.join(ROOT, "include", "glowq_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(glowq_[a-z_0-9]+)\s*\(", src)))
+    L = probe.lib()
+    assert set(names) == set(probe.EXPORTS), set(names) ^ set(probe.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.glowq_probe_read(None, 1024, FAKE, 4, None) == -1
+    assert L.glowq_probe_read(FAKE, 1000, FAKE, 4, None) == -1      # not a multiple of 16
+    assert L.glowq_probe_read(FAKE, 1024, FAKE, 0, None) == -1
+    assert L.glowq_probe_mfma_f16(10, None, 4, None) == -1
+    assert L.glowq_probe_mfma_f16(-1, FAKE, 4, None) == -1
+    assert L.glowq_probe_mfma_f16_flops(3, 2) == 2 * 4 * 3 * 8 * 16 * 16 * 32 * 2
