@@ -290,8 +290,8 @@ def achievable_peaks(reps=5):
         torch.cuda.synchronize()
         hbm = max(hbm, n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     del src
-    mblocks, iters = 512, 20000
-    msink = torch.empty(mblocks * 256 * 16, dtype=torch.uint8, device="cuda")
+    mblocks, iters = 512, 10000
+    msink = torch.empty(mblocks * 256 * 64, dtype=torch.uint8, device="cuda")
     probe.mfma_f16(iters // 10, msink, mblocks)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -304,8 +304,8 @@ def achievable_peaks(reps=5):
     torch.cuda.empty_cache()
     return {"hbm_read_GB_per_s": round(hbm, 1), "mfma_f16_TFLOP_per_s": round(mfma, 1),
             "how": "probe library: 4 GiB nontemporal streaming read (best of 512..4096 workgroups of 256 "
-                   "threads, 8 x 16 B in flight each); v_mfma_f32_16x16x32_f16 loop on registers (512 x 4 "
-                   "waves, 8 independent chains each, sustained over 5 launches)"}
+                   "threads, 8 x 16 B in flight each); v_mfma_f32_32x32x16_f16 loop on registers (512 x 4 "
+                   "waves, 4 independent chains each, sustained over 5 launches)"}
 
 
 def main():

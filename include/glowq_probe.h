@@ -23,8 +23,9 @@ extern "C" {
  * receives blocks * 256 16-byte words (the xor of what each thread read). */
 int glowq_probe_read(const void* src_dev, size_t bytes, void* sink_dev, int32_t blocks, hipStream_t stream);
 
-/* `blocks` workgroups of 4 wavefronts, each wavefront running `iters` rounds of 8 independent
- * v_mfma_f32_16x16x32_f16 on register operands; sink_dev receives blocks * 256 fp32 x4. */
+/* `blocks` workgroups of 4 wavefronts, each wavefront running `iters` rounds of 4 independent
+ * v_mfma_f32_32x32x16_f16 on register operands; sink_dev receives blocks * 256 x 16 fp32 (each
+ * lane's 16 outputs summed over the 4 chains). */
 int glowq_probe_mfma_f16(int64_t iters, void* sink_dev, int32_t blocks, hipStream_t stream);
 
 /* Dense fp16 floating-point operations one glowq_probe_mfma_f16 call performs. */

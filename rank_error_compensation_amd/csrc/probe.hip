@@ -4,9 +4,10 @@
 //   * a streaming read: 16-byte nontemporal loads over a buffer much larger than the last-level
 //     cache, eight per thread in flight, grid-stride, folded into a per-thread xor (the only
 //     store) -- the HBM read rate a kernel with a perfect access pattern reaches;
-//   * a matrix-core loop: v_mfma_f32_16x16x32_f16 on register operands, eight independent
+//   * a matrix-core loop: v_mfma_f32_32x32x16_f16 on register operands, four independent
 //     accumulators per wave, no memory traffic in the loop -- the dense fp16 rate the matrix
-//     cores sustain (including any clock reduction under that load).
+//     cores sustain (including any clock reduction under that load).  The 32x32x16 form is used
+//     because it is the fastest fp16 matrix step here: 16x16x32 sustains about half its rate.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,6 +18,7 @@ namespace {
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16x __attribute__((ext_vector_type(16)));
 
 __global__ __launch_bounds__(256) void read_kernel(const u4* __restrict__ p, uint64_t n16, u4* __restrict__ sink) {
     const uint64_t tid = (uint64_t)blockIdx.x * 256 + threadIdx.x;
@@ -44,17 +46,23 @@ __global__ __launch_bounds__(256) void mfma_kernel(int64_t iters, f4* __restrict
         a[e] = (_Float16)((float)((lane + e) & 3) * 0.25f);
         b[e] = (_Float16)((float)((lane * 3 + e) & 3) * 0.125f);
     }
-    f4 acc[8];
+    f16x acc[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[k][i] = 0.f;
     for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[k], 0, 0, 0);
+        for (int k = 0; k < 4; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[k], 0, 0, 0);
     }
-    f4 s = acc[0];
+    // lane l: the 16 outputs it holds, summed over the chains, as four f4
 #pragma unroll
-    for (int k = 1; k < 8; ++k) s += acc[k];
-    sink[(uint64_t)blockIdx.x * 256 + threadIdx.x] = s;
+    for (int q = 0; q < 4; ++q) {
+        f4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v += f4{acc[k][4 * q], acc[k][4 * q + 1], acc[k][4 * q + 2], acc[k][4 * q + 3]};
+        sink[((uint64_t)blockIdx.x * 256 + threadIdx.x) * 4 + q] = v;
+    }
 }
 
 }  // namespace
@@ -78,7 +86,7 @@ int glowq_probe_mfma_f16(int64_t iters, void* sink_dev, int32_t blocks, hipStrea
 }
 
 double glowq_probe_mfma_f16_flops(int64_t iters, int32_t blocks) {
-    return (double)blocks * 4.0 * (double)iters * 8.0 * 16.0 * 16.0 * 32.0 * 2.0;
+    return (double)blocks * 4.0 * (double)iters * 4.0 * 32.0 * 32.0 * 16.0 * 2.0;
 }
 
 }  // extern "C"

@@ -170,4 +170,4 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert L.glowq_probe_read(FAKE, 1024, FAKE, 0, None) == -1
     assert L.glowq_probe_mfma_f16(10, None, 4, None) == -1
     assert L.glowq_probe_mfma_f16(-1, FAKE, 4, None) == -1
-    assert L.glowq_probe_mfma_f16_flops(3, 2) == 2 * 4 * 3 * 8 * 16 * 16 * 32 * 2
+    assert L.glowq_probe_mfma_f16_flops(3, 2) == 2 * 4 * 3 * 4 * 32 * 32 * 16 * 2

@@ -16,28 +16,28 @@ def _gpu():
 
 
 def test_mfma_probe_result():
-    """Each wavefront's 8 chains accumulate iters copies of the 16x16x32 product A B^T of its
-    fixed operands (lane l holds A[l % 16][8 (l / 16) + e] and B[l % 16][8 (l / 16) + e]); the
-    sum over chains, in the output layout (lane l: rows 4 (l / 16) + i, column l % 16), must be
-    8 iters (A B^T) exactly (all values are small dyadic rationals)."""
+    """Each wavefront's 4 chains accumulate iters copies of the 32x32x16 product A B^T of its
+    fixed operands (lane l holds A[l % 32][8 (l / 32) + e] and B[l % 32][8 (l / 32) + e]); the
+    sum over chains, in the output layout (lane l: column l % 32, element i: row
+    8 (i / 4) + 4 (l / 32) + i % 4), must be 4 iters (A B^T) exactly (small dyadic rationals)."""
     from rank_error_compensation_amd import probe
     iters, blocks = 3, 2
-    sink = torch.zeros(blocks * 256 * 16, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(blocks * 256 * 64, dtype=torch.uint8, device="cuda")
     fl = probe.mfma_f16(iters, sink, blocks)
     torch.cuda.synchronize()
-    assert fl == blocks * 4 * iters * 8 * 16 * 16 * 32 * 2
-    out = sink.view(torch.float32).cpu().numpy().reshape(blocks * 4, 64, 4)
-    A = np.zeros((16, 32))
-    B = np.zeros((16, 32))
+    assert fl == blocks * 4 * iters * 4 * 32 * 32 * 16 * 2
+    out = sink.view(torch.float32).cpu().numpy().reshape(blocks * 4, 64, 16)
+    A = np.zeros((32, 16))
+    B = np.zeros((32, 16))
     for l in range(64):
         for e in range(8):
-            A[l % 16, 8 * (l // 16) + e] = ((l + e) & 3) * 0.25
-            B[l % 16, 8 * (l // 16) + e] = ((l * 3 + e) & 3) * 0.125
-    D = 8 * iters * (A @ B.T)
-    want = np.zeros((64, 4))
+            A[l % 32, 8 * (l // 32) + e] = ((l + e) & 3) * 0.25
+            B[l % 32, 8 * (l // 32) + e] = ((l * 3 + e) & 3) * 0.125
+    D = 4 * iters * (A @ B.T)
+    want = np.zeros((64, 16))
     for l in range(64):
-        for i in range(4):
-            want[l, i] = D[4 * (l // 16) + i, l % 16]
+        for i in range(16):
+            want[l, i] = D[8 * (i // 4) + 4 * (l // 32) + i % 4, l % 32]
     for w in range(blocks * 4):
         np.testing.assert_array_equal(out[w], want)
 
