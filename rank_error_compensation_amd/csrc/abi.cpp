@@ -136,9 +136,15 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
         p.n_proj = c.n_proj;
         for (int i = 0; i < c.n_proj; ++i) p.b[i] = static_cast<const _Float16*>(c.b[i]);
         p.R = R;
+        // 32-token blocks (16 when that leaves the chip idle even at the largest split, or when
+        // r_pad > 128), then as many K ranges as make about kProjWant workgroups
         const int64_t G = c.d / kGroup;
-        p.ks = (int32_t)(G < kProjMaxSplit ? G : kProjMaxSplit);
-        p.k_per = (int32_t)(ceil_div(G, p.ks) * kGroup);
+        p.tok_tiles = (rp <= 128 && ceil_div(c.T, 32) * c.n_proj * kProjMaxSplit >= kProjWant) ? 2 : 1;
+        const int64_t blocks = ceil_div(c.T, 16 * p.tok_tiles) * c.n_proj;
+        int64_t ks = ceil_div(kProjWant, blocks);
+        ks = ks > kProjMaxSplit ? kProjMaxSplit : ks;
+        ks = ks > G ? G : ks;
+        p.k_per = (int32_t)(ceil_div(G, ks) * kGroup);
         p.ks = (int32_t)ceil_div(c.d, p.k_per);
         p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(R) + prefill_r_bytes(c.T, c.r, c.n_proj));
         if (launch_proj_prefill(p, stream) != hipSuccess) return GLOWQ_ERR_HIP;

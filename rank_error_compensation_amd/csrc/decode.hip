@@ -180,9 +180,9 @@ __device__ void produce(const ForwardArgs& a, int p) {
             }
             __syncthreads();
             const uint32_t tag = ptag;
-            if (scrub && tag == 1u) {
-                // first call after the zero fill or after the epoch wrapped: clear every pair of
-                // the decode area outside this call's range (no one reads them in this call)
+            if (scrub && (tag == 1u || tag == 0xFFFFFFFFu)) {
+                // first and last tag of a wrap: clear every pair of the decode area outside this
+                // call's range (no one reads them in this call)
                 const size_t from = (size_t)kRReplicas * a.n_proj * T * r;
                 for (size_t k = from + (size_t)p * NTH + threadIdx.x; k < kDecodeAreaPairs;
                      k += (size_t)a.n_prod * NTH)

@@ -38,9 +38,10 @@ constexpr size_t kWsHeader = 2048;  // workspace bytes reserved for synchronisat
 // stores; a pair is current when its tag equals epoch + 1, where epoch is the header word read by
 // every workgroup at start.  The last arrival of a call (per-XCD arrival counters, then a counter
 // over the XCDs) advances the epoch, so no memset is ever needed and stale pairs never match:
-// tags run 1 .. 2^32 - 1 (the epoch skips 2^32 - 1), and a call with tag 1 (the first after the
-// zero fill or after a wrap) clears every pair outside its own range, so that a pair written
-// 2^32 - 1 calls earlier cannot be mistaken for a current one.
+// tags run 1 .. 2^32 - 1 (the epoch skips 2^32 - 1), and the calls with tags 1 and 2^32 - 1
+// clear every pair outside their own range.  A pair that still held tag t when the tag comes
+// round again would have outlived a whole wrap, so also the last of those two calls before it:
+// that call either overwrote the pair with its own tag or cleared it.
 constexpr int kXcds = 8;
 constexpr int kSyncEpoch = 0;     // epoch of the call in flight
 constexpr int kSyncDone = 16;     // done[x] at word kSyncDone + 16 x: consumers of XCD x finished
@@ -162,6 +163,7 @@ struct ProjArgs {
     const _Float16* x;   // [T][d]
     int32_t T, d, r, r_pad, n_proj;
     int32_t ks, k_per;   // K split: ks ranges of k_per inputs (a multiple of 128)
+    int32_t tok_tiles;   // 16-token tiles per workgroup: 1, or 2 when r_pad <= 128
     float* part;         // fp32 partials [ks][n_proj][T][r_pad]
     const _Float16* b[kMaxModules];  // [r][d] per projection
     void* R;             // output
@@ -187,8 +189,10 @@ hipError_t launch_proj_prefill(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 
-// Largest K split of the prefill projection.
+// Prefill projection launch: largest K split, and the workgroup count the split aims at (one per
+// CU; 512 workgroups, also with 16 splits, measured slower).
 constexpr int kProjMaxSplit = 8;
+constexpr int64_t kProjWant = 256;
 
 // Prefill tile shapes compiled, largest first: (TT, RR) token-tile x row-tile counts per wave.
 constexpr int kPrefillShapes[4][2] = {{8, 4}, {8, 2}, {4, 4}, {4, 2}};

@@ -13,6 +13,10 @@ from gpu_util import DevUnit, assert_parity, glowq, log, oracle_unit
 from oracle import glowq_ref as G
 from oracle import solve as S
 
+# workspace header: synchronisation words of the decode hand-off (int32 word 0: the epoch; every
+# other word is back to zero after each call)
+WS_HEADER = 2048
+
 pytestmark = pytest.mark.gpu
 
 
@@ -127,6 +131,9 @@ RAGGED = [
     (130, 256, (100, 36), 40),
     (300, 640, (272, 16, 48), 64),
     (257, 128, (520,), 256),
+    # enough 32-token blocks that the prefill projection needs no K split (written directly)
+    (8200, 128, (40, 24), 32),
+    (8224, 256, (24,), 64),
 ]
 
 
@@ -229,21 +236,44 @@ def test_decode_workspace_state_after_calls():
             calls += 1
         g.group_forward(du.x, du.w, du.b, du.a, 24, False, workspace=ws)  # restore off: no hand-off
         torch.cuda.synchronize()
-        hdr = ws[:2048].view(torch.int32).cpu()
+        hdr = ws[:WS_HEADER].view(torch.int32).cpu()
         assert int(hdr[0]) == calls, (int(hdr[0]), calls)          # epoch
         assert int(hdr[1:].abs().sum()) == 0, hdr[1:].nonzero()     # counters and error flag
 
 
+def test_prefill_split_projection():
+    """Prefill calls whose projection R = X B^T is split over K (fp32 partials summed in a fixed
+    order) match the oracle call after call, group and layerwise, with token blocks ragged at T,
+    and leave the workspace header untouched."""
+    g = glowq()
+    keys = (12,)
+    ws = g.make_workspace(300, 40, 3)
+    for T, d, lw in ((100, 512, False), (300, 640, True), (65, 1024, False), (300, 640, False)):
+        x = W.make_x(T, d, 0.77, keys + (T, d))
+        unit = W.make_unit("g", "group", x, [72, 40, 24], 40, keys + (T, d), layerwise=True)
+        du = DevUnit(unit, layerwise=True)
+        ref = oracle_unit(unit, layerwise=lw)
+        for _ in range(2):
+            if lw:
+                ys = g.layerwise_forward(du.x, du.w, du.b_lw, du.a, 40, True, workspace=ws)
+            else:
+                ys = g.group_forward(du.x, du.w, du.b, du.a, 40, True, workspace=ws)
+            torch.cuda.synchronize()
+            for i, (y, yr) in enumerate(zip(ys, ref)):
+                assert_parity(y, yr, f"T={T} d={d} layerwise={lw} module {i}")
+            assert int(ws[:WS_HEADER].view(torch.int32).abs().sum()) == 0
+
+
 def test_epoch_wrap_clears_stale_pairs():
-    """The epoch skips 2^32 - 1 (tags are never 0), and the first call after a wrap (tag 1)
-    clears every pair outside its own range: a pair planted there with the tag a later, larger
+    """The epoch skips 2^32 - 1 (tags are never 0), and the calls with the last and the first tag
+    of a wrap (2^32 - 1 and 1) clear every pair outside their range: a pair planted there with the tag a later, larger
     call will use is gone before that call runs, and every result matches the oracle."""
     g = glowq()
     keys = (11,)
     r, n_out = 16, [48, 32]
     ws = g.make_workspace(4, r, 1)
-    pairs = ws[2048:].view(torch.int64)  # the decode area: (fp32 value, u32 tag) pairs
-    hdr = ws[:2048].view(torch.int32)
+    pairs = ws[WS_HEADER:].view(torch.int64)  # the decode area: (fp32 value, u32 tag) pairs
+    hdr = ws[:WS_HEADER].view(torch.int32)
     hdr[0] = -2  # epoch 2^32 - 2: the next call uses tag 2^32 - 1
     # pair index 8 * 1 * 1 * r (first slot past a T=1 call's range) is inside a T=4 call's range;
     # plant a pair carrying tag 2 (what the T=4 call below will wait for) and a huge value
@@ -255,9 +285,11 @@ def test_epoch_wrap_clears_stale_pairs():
         d = devs[T]
         return g.group_forward(d.x, d.w, d.b, d.a, r, True, workspace=ws)
 
-    run(1)  # tag 2^32 - 1
+    run(1)  # tag 2^32 - 1: the last tag of a wrap also clears the area outside its range
     torch.cuda.synchronize()
     assert int(hdr[0]) == 0, int(hdr[0])  # 2^32 - 1 skipped
+    assert int(pairs[planted]) == 0
+    pairs[planted] = (1 << 32) | 0x7F000000  # a pair left with tag 1, to be cleared by the tag-1 call
     ys = run(1)  # tag 1: clears the area outside its range
     torch.cuda.synchronize()
     assert int(hdr[0]) == 1
