@@ -147,6 +147,7 @@ struct ForwardArgs {
     int32_t m_tiles;     // token tiles (prefill)
     int32_t tile_tt;     // prefill tile shape: 16-token tiles per wave
     int32_t tile_rr;     // prefill tile shape: 16-row tiles per wave (4 waves side by side)
+    int32_t tile_ks;     // prefill small grids: wave groups splitting the input groups (1, 2 or 4)
     void* R;             // projections: decode (fp32, tag) pairs [n_proj][T][r]; prefill fp16 [n_proj][T][r_pad]
     int32_t* sync;       // workspace header (decode)
     int32_t n_proj;      // projections (1 shared, m layerwise)
@@ -194,7 +195,7 @@ hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 constexpr int kProjMaxSplit = 8;
 constexpr int64_t kProjWant = 256;
 
-// Prefill tile shapes compiled, largest first: (TT, RR) token-tile x row-tile counts per wave.
-constexpr int kPrefillShapes[4][2] = {{8, 4}, {8, 2}, {4, 4}, {4, 2}};
+// Fewest tiles (128 tokens x 256 rows) for which the prefill launch uses the wide kernel.
+constexpr int64_t kWideMinTiles = 256;
 
 }  // namespace glowq

@@ -28,19 +28,25 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
-template <int TT, int RR>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(const ForwardArgs args) {
+// Small grids: KS groups of four wavefronts per workgroup (256 KS threads) share one output tile
+// and split the input groups between them (group g goes to wave group g % KS), each with its own
+// double-buffered activation tile in LDS; at the end the wave groups' sums are added through LDS
+// in wave-group order (deterministic) and wave group 0 applies the correction and stores.  With
+// KS = 4 a launch of one workgroup per CU keeps four wavefronts on every SIMD.
+template <int TT, int RR, int KS>
+__global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(const ForwardArgs args) {
     constexpr int BM = 16 * TT;
     constexpr int LS = 136;              // LDS row stride in halves (128 + 8 padding)
     constexpr int NCH = BM * 16 / 256;   // 16-byte X chunks per thread per group
-    __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * LS];
+    __shared__ __attribute__((aligned(16))) _Float16 xs[KS][2][BM * LS];
 
     const int L = xcd_remap(blockIdx.x, args.n_tiles);
     const int mb = L % args.m_tiles, nbl = L / args.m_tiles;
     const ModuleArgs M = args.mod[module_of(args, nbl)];
     const int nb = nbl - M.tile_begin;
     const int m0 = mb * BM;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x & 255, lane = tid & 63;
+    const int kg = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8);  // wave group
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = args.T, d = args.d, G = args.G;
     const NibConsts nc = nib_consts();
@@ -72,18 +78,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const ForwardArgs args)
     }
     const u4 zero4 = {0u, 0u, 0u, 0u};
 
+    // this wave group's groups: kg, kg + KS, ... (G >= 1, so every wave group of KS = 1 has one;
+    // with KS = 2 and G = 1 wave group 1 has none and only contributes zeros)
+    const int n_it = (G + KS - 1) / KS;
     u4 st[NCH];
     u4 qv[RR];
     uint32_t zs[RR];
+    const bool act0 = kg < G;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) st[c] = x_ok[c] ? *reinterpret_cast<const u4*>(xsrc[c]) : zero4;
+    for (int c = 0; c < NCH; ++c)
+        st[c] = (act0 && x_ok[c]) ? *reinterpret_cast<const u4*>(xsrc[c] + (size_t)kg * kGroup) : zero4;
 #pragma unroll
     for (int rr = 0; rr < RR; ++rr) {
-        qv[rr] = w_ok[rr] ? *reinterpret_cast<const u4*>(qp[rr]) : zero4;
-        zs[rr] = w_ok[rr] ? *reinterpret_cast<const uint32_t*>(zp[rr]) : 0u;
+        qv[rr] = (act0 && w_ok[rr]) ? *reinterpret_cast<const u4*>(qp[rr] + (size_t)kg * qstride) : zero4;
+        zs[rr] = (act0 && w_ok[rr]) ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)kg * szstride) : 0u;
     }
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) *reinterpret_cast<u4*>(&xs[0][xdst[c]]) = st[c];
+    for (int c = 0; c < NCH; ++c) *reinterpret_cast<u4*>(&xs[kg][0][xdst[c]]) = st[c];
     __syncthreads();
 
     f4 acc[TT][RR];
@@ -92,45 +103,48 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const ForwardArgs args)
 #pragma unroll
         for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = f4{0.f, 0.f, 0.f, 0.f};
 
-    for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        const bool more = g + 1 < G;
+    for (int it = 0; it < n_it; ++it) {
+        const int g = it * KS + kg;
+        const int buf = it & 1;
+        const bool act = g < G, more = g + KS < G;
         u4 qn[RR];
         uint32_t zn[RR];
         if (more) {
 #pragma unroll
             for (int c = 0; c < NCH; ++c)
-                st[c] = x_ok[c] ? *reinterpret_cast<const u4*>(xsrc[c] + (size_t)(g + 1) * kGroup) : zero4;
+                st[c] = x_ok[c] ? *reinterpret_cast<const u4*>(xsrc[c] + (size_t)(g + KS) * kGroup) : zero4;
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr) {
-                qn[rr] = w_ok[rr] ? *reinterpret_cast<const u4*>(qp[rr] + (size_t)(g + 1) * qstride) : zero4;
-                zn[rr] = w_ok[rr] ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)(g + 1) * szstride) : 0u;
+                qn[rr] = w_ok[rr] ? *reinterpret_cast<const u4*>(qp[rr] + (size_t)(g + KS) * qstride) : zero4;
+                zn[rr] = w_ok[rr] ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)(g + KS) * szstride) : 0u;
             }
         }
-        h2 c1024[RR], c64[RR];
-        h8 s8[RR];
+        if (act) {
+            h2 c1024[RR], c64[RR];
+            h8 s8[RR];
 #pragma unroll
-        for (int rr = 0; rr < RR; ++rr) {
-            zero_consts(zs[rr], c1024[rr], c64[rr]);
-            const _Float16 s = as_h2(zs[rr])[1];
-            s8[rr] = h8{s, s, s, s, s, s, s, s};
-        }
-        const _Float16* xb = &xs[buf][(lane & 15) * LS + kofs];
+            for (int rr = 0; rr < RR; ++rr) {
+                zero_consts(zs[rr], c1024[rr], c64[rr]);
+                const _Float16 sc = as_h2(zs[rr])[1];
+                s8[rr] = h8{sc, sc, sc, sc, sc, sc, sc, sc};
+            }
+            const _Float16* xb = &xs[kg][buf][(lane & 15) * LS + kofs];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            h8 a[RR];
+            for (int j = 0; j < 4; ++j) {
+                h8 a[RR];
 #pragma unroll
-            for (int rr = 0; rr < RR; ++rr) a[rr] = nib8_minus_z(qv[rr][j], c1024[rr], c64[rr], nc) * s8[rr];
+                for (int rr = 0; rr < RR; ++rr) a[rr] = nib8_minus_z(qv[rr][j], c1024[rr], c64[rr], nc) * s8[rr];
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                const h8 b = *reinterpret_cast<const h8*>(xb + tt * 16 * LS + 32 * j);
+                for (int tt = 0; tt < TT; ++tt) {
+                    const h8 b = *reinterpret_cast<const h8*>(xb + tt * 16 * LS + 32 * j);
 #pragma unroll
-                for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = mfma16(a[rr], b, acc[tt][rr]);
+                    for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = mfma16(a[rr], b, acc[tt][rr]);
+                }
             }
         }
         if (more) {
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) *reinterpret_cast<u4*>(&xs[buf ^ 1][xdst[c]]) = st[c];
+            for (int c = 0; c < NCH; ++c) *reinterpret_cast<u4*>(&xs[kg][buf ^ 1][xdst[c]]) = st[c];
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr) {
                 qv[rr] = qn[rr];
@@ -138,6 +152,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const ForwardArgs args)
             }
         }
         __syncthreads();
+    }
+
+    if (KS > 1) {
+        // wave groups 1 .. KS-1 hand their sums to wave group 0 through LDS (the activation
+        // buffers are free after the loop's last barrier)
+        f4* red = reinterpret_cast<f4*>(&xs[0][0][0]);
+        static_assert(sizeof(xs) >= (KS - 1) * TT * RR * 256 * sizeof(f4), "reduction space");
+        if (kg > 0) {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) red[(((kg - 1) * TT + tt) * RR + rr) * 256 + tid] = acc[tt][rr];
+        }
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll
+        for (int k = 1; k < KS; ++k)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) acc[tt][rr] += red[(((k - 1) * TT + tt) * RR + rr) * 256 + tid];
     }
 
     // correction: r_pad / 32 more K steps, A-operand A_i rows, B-operand R tokens
@@ -378,12 +413,13 @@ hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(prefill_wide_kernel, grid, block, 2 * 8 * 4 * 64 * sizeof(u4), stream, a);
         return hipGetLastError();
     }
-    if (a.tile_tt == 4 && a.tile_rr == 4)
-        hipLaunchKernelGGL((prefill_kernel<4, 4>), grid, block, 0, stream, a);
-    else if (a.tile_tt == 8 && a.tile_rr == 2)
-        hipLaunchKernelGGL((prefill_kernel<8, 2>), grid, block, 0, stream, a);
-    else if (a.tile_tt == 4 && a.tile_rr == 2)
-        hipLaunchKernelGGL((prefill_kernel<4, 2>), grid, block, 0, stream, a);
+    if (a.tile_tt != 4 || a.tile_rr != 2) return hipErrorInvalidValue;
+    if (a.tile_ks == 4)
+        hipLaunchKernelGGL((prefill_kernel<4, 2, 4>), grid, dim3(1024), 0, stream, a);
+    else if (a.tile_ks == 2)
+        hipLaunchKernelGGL((prefill_kernel<4, 2, 2>), grid, dim3(512), 0, stream, a);
+    else if (a.tile_ks == 1)
+        hipLaunchKernelGGL((prefill_kernel<4, 2, 1>), grid, block, 0, stream, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -134,6 +134,10 @@ RAGGED = [
     # enough 32-token blocks that the prefill projection needs no K split (written directly)
     (8200, 128, (40, 24), 32),
     (8224, 256, (24,), 64),
+    # prefill grids below the wide tile's threshold with 512 and 640 small tiles (two wave
+    # groups, one wave group per workgroup); the smaller cases above take four
+    (1024, 256, (4096,), 32),
+    (1000, 256, (2560, 2560), 16),
 ]
 
 
