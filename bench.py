@@ -269,6 +269,50 @@ def extra_prefill_gateup(g, reps=20):
     return out
 
 
+def extra_restore_selection(g, reps=3, k=16):
+    """GlowQ-S selection over 32 LLaMA-2-7B-shaped layers (q, k, v, o, gate, up, down): the
+    normalised error ratio of all 224 modules (fp16 W and its INT4-g128 form, both resident in
+    HBM) and the top-k choice of the layers, timed as one pass."""
+    import torch
+    import workload as W
+    d, inter, L = 4096, 11008, 32
+    shapes = [(d, d)] * 4 + [(inter, d)] * 2 + [(d, inter)]
+    mods = []
+    for l in range(L):
+        for i, (O, kin) in enumerate(shapes):
+            keys = (0, 5, l, i)
+            w = W.make_w(O, kin, keys, W.outlier_columns(kin, keys), "cuda")
+            mods.append((w, g.QWeight.from_workload(W.rtn_quantize(w))))
+    torch.cuda.synchronize()
+    sums = torch.empty(L * len(shapes), 2, dtype=torch.float64, device="cuda")
+    ws = torch.empty(int(g.lib().glowq_ner_workspace_bytes(inter)), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run():
+        for j, (w, qw) in enumerate(mods):
+            g.ner_sums(w, qw, out=sums[j], workspace=ws)
+        return g.restore_topk(sums.view(L, len(shapes), 2), k)
+
+    run()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        _, mask = run()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    t = statistics.median(ts)
+    nb = sum(O * kin * 2 + O * kin // 2 + O * (kin // 128) * 4 for O, kin in shapes) * L
+    out = {"workload": f"llama2-7b-shaped 32 layers x 7 modules: g_ner of every module + top-{k} layers",
+           "ms": round(t * 1e3, 3), "alg_bytes": nb, "GB_per_s": round(nb / t / 1e9, 1),
+           "frac_hbm_peak": round(nb / t / 1e9 / HBM_PEAK_GBS, 4), "restored": int(mask.sum())}
+    del mods, sums, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def achievable_peaks(reps=5):
     """The achievable peaks on this GPU, measured by the probe library: a streaming read of a
     4 GiB buffer (16 times the last-level cache) and a matrix-core-only fp16 loop."""
@@ -444,6 +488,10 @@ def main():
             e = extra["prefill_gateup_T2048"][k]
             e["frac_mfma_measured_peak"] = round(e["alg_TFLOP_per_s"] / peaks["mfma_f16_TFLOP_per_s"], 4)
         log(f"[bench] gate/up prefill T=2048: {extra['prefill_gateup_T2048']}")
+        extra["restore_selection_32L"] = extra_restore_selection(g)
+        e = extra["restore_selection_32L"]
+        e["frac_hbm_measured_peak"] = round(e["GB_per_s"] / peaks["hbm_read_GB_per_s"], 4)
+        log(f"[bench] restore selection: {e}")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -165,6 +165,41 @@ typedef struct glowq_unit {
 int glowq_path_forward(const glowq_unit* units, int32_t n_units, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- GlowQ-S restore selection
+ * Importance scores and the budgeted top-k choice of the units to restore (GlowQ paper note,
+ * key design 4: units are ranked by a score -- the normalised error ratio
+ * g_ner(u) = ||E_u||_F^2 / ||W_u||_F^2 with E = W - W_hat is one of the two -- and only the
+ * top k are activated, layer order deciding when the signal is weak; the arXiv page, Figure 12,
+ * sorts restorable groups by this ratio among other metrics).  A unit is any set of modules
+ * (a group, a solo module, a whole decoder layer); its ratio is the sum of its modules' squared
+ * errors over the sum of their squared weights.
+ */
+
+/* Workspace bytes of glowq_ner_sums for a module with n_out rows (0 if n_out is invalid). */
+size_t glowq_ner_workspace_bytes(int64_t n_out);
+
+/* Squared error and squared weight of one module:
+ *   w_dev    : the fp16 weight W [n_out][k_in] the module was quantised from
+ *   wq       : its quantised form in the device layout (glowq_repack)
+ *   sums_dev : fp64 [2] output, sums_dev[0] = ||W - W_hat||_F^2, sums_dev[1] = ||W||_F^2
+ * W_hat = (q - z) s is rebuilt exactly; the difference and its square are exact in fp64 and the
+ * sums are taken in a fixed order (bitwise repeatable).  workspace: device memory of at least
+ * glowq_ner_workspace_bytes(n_out) bytes, 256-byte aligned, overwritten.  Asynchronous. */
+int glowq_ner_sums(const void* w_dev, const glowq_qweight* wq, void* workspace, size_t workspace_bytes,
+                   double* sums_dev, hipStream_t stream);
+
+/* Scores and restore mask of n_units units (1 <= n_units <= 4096), each made of n_per_unit
+ * modules (1 .. 1024):
+ *   sums_dev   : fp64 [n_units][n_per_unit][2], the glowq_ner_sums pairs of every module
+ *   k          : how many units to restore, 0 <= k <= n_units
+ *   scores_dev : fp64 [n_units] output, sum of the errors over sum of the weights (0 if the
+ *                latter is 0), summed in module order
+ *   mask_dev   : int32 [n_units] output, 1 for the k highest scores, equal scores going to
+ *                the lower unit index, else 0
+ * Asynchronous. */
+int glowq_restore_topk(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k,
+                       double* scores_dev, int32_t* mask_dev, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

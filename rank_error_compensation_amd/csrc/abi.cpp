@@ -295,6 +295,37 @@ int glowq_dequant(const glowq_qweight* w, void* out_dev, int32_t out_dtype, hipS
     return e == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
 }
 
+size_t glowq_ner_workspace_bytes(int64_t n_out) {
+    if (n_out < 1 || n_out > kMaxRows) return 0;
+    return round256((size_t)ceil_div(n_out, 16) * 16u);
+}
+
+int glowq_ner_sums(const void* w_dev, const glowq_qweight* wq, void* workspace, size_t workspace_bytes,
+                   double* sums_dev, hipStream_t stream) {
+    if (!w_dev || !wq || !wq->q || !wq->sz || !sums_dev || !workspace) return GLOWQ_ERR_INVALID_ARG;
+    if (wq->n_out < 1 || wq->k_in < kGroup || wq->k_in % kGroup != 0) return GLOWQ_ERR_SHAPE;
+    if (wq->n_out > kMaxRows || wq->k_in > kMaxD) return GLOWQ_ERR_UNSUPPORTED;
+    if (!aligned(w_dev, 16) || !aligned(wq->q, 16) || !aligned(wq->sz, 16) || !aligned(sums_dev, 16))
+        return GLOWQ_ERR_ALIGN;
+    if (!aligned(workspace, 256)) return GLOWQ_ERR_ALIGN;
+    if (workspace_bytes < glowq_ner_workspace_bytes(wq->n_out)) return GLOWQ_ERR_WORKSPACE;
+    const hipError_t e = launch_ner(static_cast<const _Float16*>(w_dev), static_cast<const uint8_t*>(wq->q),
+                                    static_cast<const uint8_t*>(wq->sz), wq->n_out, wq->k_in,
+                                    static_cast<double*>(workspace), sums_dev, stream);
+    return e == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
+}
+
+int glowq_restore_topk(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k,
+                       double* scores_dev, int32_t* mask_dev, hipStream_t stream) {
+    if (!sums_dev || !scores_dev || !mask_dev) return GLOWQ_ERR_INVALID_ARG;
+    if (n_units < 1 || n_units > kMaxScoreUnits || n_per_unit < 1 || n_per_unit > 1024 || k < 0 ||
+        k > n_units)
+        return GLOWQ_ERR_SHAPE;
+    if (!aligned(sums_dev, 16) || !aligned(scores_dev, 16) || !aligned(mask_dev, 16)) return GLOWQ_ERR_ALIGN;
+    const hipError_t e = launch_topk(sums_dev, n_units, n_per_unit, k, scores_dev, mask_dev, stream);
+    return e == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
+}
+
 int glowq_group_forward(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
                         const void* b_shared, const void* const* a, int32_t r, int32_t restore,
                         void* workspace, size_t workspace_bytes, void* const* y, hipStream_t stream) {

@@ -188,6 +188,13 @@ hipError_t launch_dequant(const uint8_t* q, const uint8_t* sz, int64_t n_out, in
                           int dtype, hipStream_t stream);
 hipError_t launch_proj_prefill(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
+hipError_t launch_ner(const _Float16* w, const uint8_t* q, const uint8_t* sz, int64_t n_out, int64_t k_in,
+                      double* part, double* sums, hipStream_t stream);
+hipError_t launch_topk(const double* sums, int32_t n_units, int32_t n_per, int32_t k, double* scores,
+                       int32_t* mask, hipStream_t stream);
+
+// Most units one restore selection ranks (their scores sit in LDS).
+constexpr int kMaxScoreUnits = 4096;
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 
 // Prefill projection launch: largest K split, and the workgroup count the split aims at (one per

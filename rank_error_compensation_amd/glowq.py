@@ -64,6 +64,9 @@ EXPORTS = {
                                                ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _i32,
                                                _vp, _sz, ctypes.POINTER(_vp), _vp]),
     "glowq_path_forward": (ctypes.c_int, [ctypes.POINTER(UnitC), _i32, _vp, _sz, _vp]),
+    "glowq_ner_workspace_bytes": (_sz, [_i64]),
+    "glowq_ner_sums": (ctypes.c_int, [_vp, ctypes.POINTER(QWeightC), _vp, _sz, _vp, _vp]),
+    "glowq_restore_topk": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -151,6 +154,34 @@ def dequant(w: QWeight, dtype=torch.float32, stream=None) -> torch.Tensor:
     wc = w.c()
     check(lib().glowq_dequant(ctypes.byref(wc), _ptr(out), code, _stream(stream)), "glowq_dequant")
     return out
+
+
+# --------------------------------------------------------------------------- restore selection
+def ner_sums(w: torch.Tensor, qw: QWeight, out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp64 [2]: ||W - W_hat||_F^2 and ||W||_F^2 of one module (glowq_ner_sums); `out` may be a
+    16-byte aligned fp64 view of two elements."""
+    w = w.contiguous()
+    if out is None:
+        out = torch.empty(2, dtype=torch.float64, device=w.device)
+    if workspace is None:
+        workspace = torch.empty(int(lib().glowq_ner_workspace_bytes(qw.n_out)), dtype=torch.uint8,
+                                device=w.device)
+    wc = qw.c()
+    check(lib().glowq_ner_sums(_ptr(w), ctypes.byref(wc), _ptr(workspace), workspace.numel(), _ptr(out),
+                               _stream(stream)), "glowq_ner_sums")
+    return out
+
+
+def restore_topk(sums: torch.Tensor, k: int, stream=None):
+    """sums fp64 [n_units][n_per_unit][2] -> (scores fp64 [n_units], mask int32 [n_units])."""
+    sums = sums.contiguous()
+    n_units, n_per = int(sums.shape[0]), int(sums.shape[1])
+    scores = torch.empty(n_units, dtype=torch.float64, device=sums.device)
+    mask = torch.empty(n_units, dtype=torch.int32, device=sums.device)
+    check(lib().glowq_restore_topk(_ptr(sums), n_units, n_per, k, _ptr(scores), _ptr(mask),
+                                   _stream(stream)), "glowq_restore_topk")
+    return scores, mask
 
 
 # --------------------------------------------------------------------------- forward

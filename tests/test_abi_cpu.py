@@ -134,6 +134,29 @@ def test_other_entry_points_validate():
     assert L.glowq_repack(FAKE, FAKE, FAKE, 16, 128, FAKE + 4, FAKE, FAKE, None) == g.ERR_ALIGN
 
 
+def test_restore_selection_validates():
+    """glowq_ner_sums / glowq_restore_topk reject bad arguments before any HIP call."""
+    L = g.lib()
+    wc = _w()
+    assert L.glowq_ner_workspace_bytes(0) == 0
+    assert L.glowq_ner_workspace_bytes(17) == 256 and L.glowq_ner_workspace_bytes(4096) == 4096
+    need = L.glowq_ner_workspace_bytes(wc.n_out)
+    assert L.glowq_ner_sums(None, ctypes.byref(wc), FAKE, need, FAKE, None) == g.ERR_INVALID_ARG
+    assert L.glowq_ner_sums(FAKE, None, FAKE, need, FAKE, None) == g.ERR_INVALID_ARG
+    assert L.glowq_ner_sums(FAKE, ctypes.byref(wc), FAKE, need, None, None) == g.ERR_INVALID_ARG
+    assert L.glowq_ner_sums(FAKE, ctypes.byref(_w(k_in=200)), FAKE, 1 << 20, FAKE, None) == g.ERR_SHAPE
+    assert L.glowq_ner_sums(FAKE + 8, ctypes.byref(wc), FAKE, need, FAKE, None) == g.ERR_ALIGN
+    assert L.glowq_ner_sums(FAKE, ctypes.byref(wc), FAKE + 16, need, FAKE, None) == g.ERR_ALIGN
+    assert L.glowq_ner_sums(FAKE, ctypes.byref(wc), FAKE, need - 1, FAKE, None) == g.ERR_WORKSPACE
+    assert L.glowq_restore_topk(None, 4, 1, 2, FAKE, FAKE, None) == g.ERR_INVALID_ARG
+    assert L.glowq_restore_topk(FAKE, 0, 1, 0, FAKE, FAKE, None) == g.ERR_SHAPE
+    assert L.glowq_restore_topk(FAKE, 4097, 1, 2, FAKE, FAKE, None) == g.ERR_SHAPE
+    assert L.glowq_restore_topk(FAKE, 4, 0, 2, FAKE, FAKE, None) == g.ERR_SHAPE
+    assert L.glowq_restore_topk(FAKE, 4, 1, 5, FAKE, FAKE, None) == g.ERR_SHAPE
+    assert L.glowq_restore_topk(FAKE, 4, 1, -1, FAKE, FAKE, None) == g.ERR_SHAPE
+    assert L.glowq_restore_topk(FAKE, 4, 1, 2, FAKE, FAKE + 4, None) == g.ERR_ALIGN
+
+
 def test_path_validates_every_unit_first():
     L = g.lib()
     wq = (g.QWeightC * 1)(_w())
