@@ -272,7 +272,7 @@ def extra_prefill_gateup(g, reps=20):
 def extra_restore_selection(g, reps=3, k=16):
     """GlowQ-S selection over 32 LLaMA-2-7B-shaped layers (q, k, v, o, gate, up, down): the
     normalised error ratio of all 224 modules (fp16 W and its INT4-g128 form, both resident in
-    HBM) and the top-k choice of the layers, timed as one pass."""
+    HBM; one batch call) and the top-k choice of the layers, timed as one pass."""
     import torch
     import workload as W
     d, inter, L = 4096, 11008, 32
@@ -285,12 +285,11 @@ def extra_restore_selection(g, reps=3, k=16):
             mods.append((w, g.QWeight.from_workload(W.rtn_quantize(w))))
     torch.cuda.synchronize()
     sums = torch.empty(L * len(shapes), 2, dtype=torch.float64, device="cuda")
-    ws = torch.empty(int(g.lib().glowq_ner_workspace_bytes(inter)), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(g.ner_workspace_bytes_batch([qw.n_out for _, qw in mods]), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def run():
-        for j, (w, qw) in enumerate(mods):
-            g.ner_sums(w, qw, out=sums[j], workspace=ws)
+        g.ner_sums_batch(mods, out=sums, workspace=ws)
         return g.restore_topk(sums.view(L, len(shapes), 2), k)
 
     run()

@@ -188,6 +188,12 @@ size_t glowq_ner_workspace_bytes(int64_t n_out);
 int glowq_ner_sums(const void* w_dev, const glowq_qweight* wq, void* workspace, size_t workspace_bytes,
                    double* sums_dev, hipStream_t stream);
 
+/* The same for n >= 1 modules at once (a few launches for the whole set): w_devs and wqs are
+ * host arrays of n entries, sums_dev fp64 [n][2] receives module i's pair at sums_dev[2 i],
+ * and workspace_bytes >= the sum over the modules of glowq_ner_workspace_bytes(n_out). */
+int glowq_ner_sums_batch(int32_t n, const void* const* w_devs, const glowq_qweight* wqs, void* workspace,
+                         size_t workspace_bytes, double* sums_dev, hipStream_t stream);
+
 /* Scores and restore mask of n_units units (1 <= n_units <= 4096), each made of n_per_unit
  * modules (1 .. 1024):
  *   sums_dev   : fp64 [n_units][n_per_unit][2], the glowq_ner_sums pairs of every module

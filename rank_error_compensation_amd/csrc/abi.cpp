@@ -300,19 +300,51 @@ size_t glowq_ner_workspace_bytes(int64_t n_out) {
     return round256((size_t)ceil_div(n_out, 16) * 16u);
 }
 
+int glowq_ner_sums_batch(int32_t n, const void* const* w_devs, const glowq_qweight* wqs, void* workspace,
+                         size_t workspace_bytes, double* sums_dev, hipStream_t stream) {
+    if (n < 1 || !w_devs || !wqs || !sums_dev || !workspace) return GLOWQ_ERR_INVALID_ARG;
+    size_t need = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const glowq_qweight& w = wqs[i];
+        if (!w_devs[i] || !w.q || !w.sz) return GLOWQ_ERR_INVALID_ARG;
+        if (w.n_out < 1 || w.k_in < kGroup || w.k_in % kGroup != 0) return GLOWQ_ERR_SHAPE;
+        if (w.n_out > kMaxRows || w.k_in > kMaxD) return GLOWQ_ERR_UNSUPPORTED;
+        if (!aligned(w_devs[i], 16) || !aligned(w.q, 16) || !aligned(w.sz, 16)) return GLOWQ_ERR_ALIGN;
+        need += glowq_ner_workspace_bytes(w.n_out);
+    }
+    if (!aligned(sums_dev, 16) || !aligned(workspace, 256)) return GLOWQ_ERR_ALIGN;
+    if (workspace_bytes < need) return GLOWQ_ERR_WORKSPACE;
+    // launches of up to kNerBatch modules; module i's tile partials at its own offset
+    double* part = static_cast<double*>(workspace);
+    for (int32_t c0 = 0; c0 < n; c0 += kNerBatch) {
+        NerBatch a;
+        std::memset(&a, 0, sizeof(a));
+        a.n_mod = n - c0 < kNerBatch ? n - c0 : kNerBatch;
+        int32_t tiles = 0;
+        for (int k = 0; k < a.n_mod; ++k) {
+            const glowq_qweight& w = wqs[c0 + k];
+            a.tile_begin[k] = tiles;
+            a.n_out[k] = (int32_t)w.n_out;
+            a.k_in[k] = (int32_t)w.k_in;
+            a.w[k] = static_cast<const _Float16*>(w_devs[c0 + k]);
+            a.q[k] = static_cast<const uint8_t*>(w.q);
+            a.sz[k] = static_cast<const uint8_t*>(w.sz);
+            tiles += (int32_t)ceil_div(w.n_out, 16);
+        }
+        a.tile_begin[a.n_mod] = tiles;
+        a.part = part;
+        a.sums = sums_dev + 2 * (size_t)c0;
+        if (launch_ner(a, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+        part += 2 * (size_t)tiles;
+    }
+    return GLOWQ_OK;
+}
+
 int glowq_ner_sums(const void* w_dev, const glowq_qweight* wq, void* workspace, size_t workspace_bytes,
                    double* sums_dev, hipStream_t stream) {
-    if (!w_dev || !wq || !wq->q || !wq->sz || !sums_dev || !workspace) return GLOWQ_ERR_INVALID_ARG;
-    if (wq->n_out < 1 || wq->k_in < kGroup || wq->k_in % kGroup != 0) return GLOWQ_ERR_SHAPE;
-    if (wq->n_out > kMaxRows || wq->k_in > kMaxD) return GLOWQ_ERR_UNSUPPORTED;
-    if (!aligned(w_dev, 16) || !aligned(wq->q, 16) || !aligned(wq->sz, 16) || !aligned(sums_dev, 16))
-        return GLOWQ_ERR_ALIGN;
-    if (!aligned(workspace, 256)) return GLOWQ_ERR_ALIGN;
-    if (workspace_bytes < glowq_ner_workspace_bytes(wq->n_out)) return GLOWQ_ERR_WORKSPACE;
-    const hipError_t e = launch_ner(static_cast<const _Float16*>(w_dev), static_cast<const uint8_t*>(wq->q),
-                                    static_cast<const uint8_t*>(wq->sz), wq->n_out, wq->k_in,
-                                    static_cast<double*>(workspace), sums_dev, stream);
-    return e == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
+    if (!w_dev || !wq) return GLOWQ_ERR_INVALID_ARG;
+    const void* w_devs[1] = {w_dev};
+    return glowq_ner_sums_batch(1, w_devs, wq, workspace, workspace_bytes, sums_dev, stream);
 }
 
 int glowq_restore_topk(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k,

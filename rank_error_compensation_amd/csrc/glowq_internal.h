@@ -188,8 +188,19 @@ hipError_t launch_dequant(const uint8_t* q, const uint8_t* sz, int64_t n_out, in
                           int dtype, hipStream_t stream);
 hipError_t launch_proj_prefill(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
-hipError_t launch_ner(const _Float16* w, const uint8_t* q, const uint8_t* sz, int64_t n_out, int64_t k_in,
-                      double* part, double* sums, hipStream_t stream);
+// Modules of one restore-score launch (their descriptors travel in the kernel arguments).
+constexpr int kNerBatch = 32;
+struct NerBatch {
+    int32_t n_mod;
+    int32_t tile_begin[kNerBatch + 1];  // prefix of the modules' 16-row tiles
+    int32_t n_out[kNerBatch], k_in[kNerBatch];
+    const _Float16* w[kNerBatch];       // fp16 [n_out][k_in]
+    const uint8_t* q[kNerBatch];        // device layout
+    const uint8_t* sz[kNerBatch];
+    double* part;                       // [tiles][2]
+    double* sums;                       // [n_mod][2]
+};
+hipError_t launch_ner(const NerBatch& a, hipStream_t stream);
 hipError_t launch_topk(const double* sums, int32_t n_units, int32_t n_per, int32_t k, double* scores,
                        int32_t* mask, hipStream_t stream);
 

@@ -3,14 +3,15 @@
 // ratio g_ner(u) = ||E_u||_F^2 / ||W_u||_F^2 with E = W - W_hat; the arXiv page, Figure 12, sorts
 // restorable groups by this ratio among other metrics).
 //
-//   * ner_partial_kernel: one workgroup per 16-row tile of a module; the four waves take the
+//   * ner_partial_kernel: one launch for a batch of up to kNerBatch modules, one workgroup per
+//     16-row tile of each module (module found from a prefix table); the four waves take the
 //     input groups g = w, w + 4, ... (four groups of loads in flight per wave), read the fp16
 //     weight W and the packed INT4 weight in its device layout, rebuild W_hat = (q - z) s exactly
 //     (the same in-register unpacking as the forward kernels, then one exact fp32 product) and
 //     accumulate (W - W_hat)^2 and W^2 in fp64 -- the difference of an fp16 and a 22-bit value is
 //     exact in fp64, and so is its square (at most 2 x 25 significant bits); the lanes and waves
 //     are summed in a fixed order.
-//   * ner_finish_kernel: one workgroup adds the per-tile partial sums in a fixed order.
+//   * ner_finish_kernel: one workgroup per module adds its per-tile partial sums in a fixed order.
 //   * topk_kernel: one workgroup forms each unit's score sum_m err / sum_m w over its modules
 //     (0 when sum_m w is 0) and restores the k best units, equal scores going to the lower unit
 //     index (the order in which the pages fall back to layer order).
@@ -19,62 +20,66 @@
 
 namespace glowq {
 
-struct NerArgs {
-    const _Float16* w;   // [n_out][k_in]
-    const uint8_t* q;    // device layout
-    const uint8_t* sz;
-    int32_t n_out, k_in, G, NT;
-    double* part;        // [NT][2]
-    double* sums;        // [2]
-};
-
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;
 }
 
-__global__ __launch_bounds__(256) void ner_partial_kernel(const NerArgs a) {
+// Module of work tile `tile` in a batch (uniform across the workgroup).
+__device__ __forceinline__ int ner_module_of(const NerBatch& a, int tile) {
+    int i = 0;
+#pragma unroll
+    for (int k = 1; k < kNerBatch; ++k) i += (k < a.n_mod && tile >= a.tile_begin[k]) ? 1 : 0;
+    return __builtin_amdgcn_readfirstlane(i);
+}
+
+__global__ __launch_bounds__(256) void ner_partial_kernel(const NerBatch a) {
     constexpr int U = 4;  // groups of loads in flight per wave
     __shared__ double red[4][2];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int rt = blockIdx.x;
+    const int tile = blockIdx.x;
+    const int mi = ner_module_of(a, tile);
+    const int rt = tile - a.tile_begin[mi];
+    const int n_out = a.n_out[mi], k_in = a.k_in[mi], G = k_in / kGroup, NT = (n_out + 15) / 16;
+    const uint8_t* q = a.q[mi];
+    const uint8_t* sz = a.sz[mi];
     const int row = rt * 16 + (lane & 15);
-    const bool ok = row < a.n_out;
+    const bool ok = row < n_out;
     const NibConsts nc = nib_consts();
-    const _Float16* wr = a.w + (size_t)(ok ? row : 0) * a.k_in + 8 * (lane >> 4);
+    const _Float16* wr = a.w[mi] + (size_t)(ok ? row : 0) * k_in + 8 * (lane >> 4);
     const u4 zero4 = {0u, 0u, 0u, 0u};
     const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     double e2 = 0.0, w2 = 0.0;
-    for (int g0 = wave; g0 < a.G; g0 += 4 * U) {
+    for (int g0 = wave; g0 < G; g0 += 4 * U) {
         u4 qv[U];
         uint32_t zs[U];
         h8 wv[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int g = g0 + 4 * u;
-            const bool live = g < a.G;
-            const size_t blk = (size_t)(live ? g : 0) * a.NT + rt;
-            qv[u] = live ? *reinterpret_cast<const u4*>(a.q + blk * 1024 + lane * 16) : zero4;
-            zs[u] = live ? *reinterpret_cast<const uint32_t*>(a.sz + blk * 64 + (lane & 15) * 4) : 0u;
+            const bool live = g < G;
+            const size_t blk = (size_t)(live ? g : 0) * NT + rt;
+            qv[u] = live ? *reinterpret_cast<const u4*>(q + blk * 1024 + lane * 16) : zero4;
+            zs[u] = live ? *reinterpret_cast<const uint32_t*>(sz + blk * 64 + (lane & 15) * 4) : 0u;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 wv[u][j] = (live && ok) ? load_h8(wr + (size_t)g * kGroup + 32 * j) : zero8;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (!(g0 + 4 * u < a.G) || !ok) continue;
+            if (!(g0 + 4 * u < G) || !ok) continue;
             h2 c1024, c64;
             zero_consts(zs[u], c1024, c64);
-            const float s = (float)as_h2(zs[u])[1];
+            const float sc = (float)as_h2(zs[u])[1];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const h8 qz = nib8_minus_z(qv[u][j], c1024, c64, nc);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const double wd = (double)(float)wv[u][j][e];
-                    const double de = wd - (double)((float)qz[e] * s);
+                    const double de = wd - (double)((float)qz[e] * sc);
                     e2 = fma(de, de, e2);
                     w2 = fma(wd, wd, w2);
                 }
@@ -89,15 +94,17 @@ __global__ __launch_bounds__(256) void ner_partial_kernel(const NerArgs a) {
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        a.part[2 * rt] = ((red[0][0] + red[1][0]) + red[2][0]) + red[3][0];
-        a.part[2 * rt + 1] = ((red[0][1] + red[1][1]) + red[2][1]) + red[3][1];
+        a.part[2 * tile] = ((red[0][0] + red[1][0]) + red[2][0]) + red[3][0];
+        a.part[2 * tile + 1] = ((red[0][1] + red[1][1]) + red[2][1]) + red[3][1];
     }
 }
 
-__global__ __launch_bounds__(256) void ner_finish_kernel(const NerArgs a) {
+// Workgroup m: the partial sums of module m's tiles, in a fixed order.
+__global__ __launch_bounds__(256) void ner_finish_kernel(const NerBatch a) {
     __shared__ double red[2][256];
+    const int m = blockIdx.x;
     double e2 = 0.0, w2 = 0.0;
-    for (int i = threadIdx.x; i < a.NT; i += 256) {
+    for (int i = a.tile_begin[m] + threadIdx.x; i < a.tile_begin[m + 1]; i += 256) {
         e2 += a.part[2 * i];
         w2 += a.part[2 * i + 1];
     }
@@ -112,8 +119,8 @@ __global__ __launch_bounds__(256) void ner_finish_kernel(const NerArgs a) {
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        a.sums[0] = red[0][0];
-        a.sums[1] = red[1][0];
+        a.sums[2 * m] = red[0][0];
+        a.sums[2 * m + 1] = red[1][0];
     }
 }
 
@@ -145,22 +152,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs a) {
     }
 }
 
-hipError_t launch_ner(const _Float16* w, const uint8_t* q, const uint8_t* sz, int64_t n_out, int64_t k_in,
-                      double* part, double* sums, hipStream_t stream) {
-    NerArgs a;
-    a.w = w;
-    a.q = q;
-    a.sz = sz;
-    a.n_out = (int32_t)n_out;
-    a.k_in = (int32_t)k_in;
-    a.G = (int32_t)(k_in / kGroup);
-    a.NT = (int32_t)ceil_div(n_out, 16);
-    a.part = part;
-    a.sums = sums;
-    hipLaunchKernelGGL(ner_partial_kernel, dim3((unsigned)a.NT), dim3(256), 0, stream, a);
+hipError_t launch_ner(const NerBatch& a, hipStream_t stream) {
+    hipLaunchKernelGGL(ner_partial_kernel, dim3((unsigned)a.tile_begin[a.n_mod]), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ner_finish_kernel, dim3(1), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(ner_finish_kernel, dim3((unsigned)a.n_mod), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

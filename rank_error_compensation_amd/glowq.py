@@ -66,6 +66,8 @@ EXPORTS = {
     "glowq_path_forward": (ctypes.c_int, [ctypes.POINTER(UnitC), _i32, _vp, _sz, _vp]),
     "glowq_ner_workspace_bytes": (_sz, [_i64]),
     "glowq_ner_sums": (ctypes.c_int, [_vp, ctypes.POINTER(QWeightC), _vp, _sz, _vp, _vp]),
+    "glowq_ner_sums_batch": (ctypes.c_int, [_i32, ctypes.POINTER(_vp), ctypes.POINTER(QWeightC), _vp, _sz,
+                                            _vp, _vp]),
     "glowq_restore_topk": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
 }
 
@@ -170,6 +172,27 @@ def ner_sums(w: torch.Tensor, qw: QWeight, out: Optional[torch.Tensor] = None,
     wc = qw.c()
     check(lib().glowq_ner_sums(_ptr(w), ctypes.byref(wc), _ptr(workspace), workspace.numel(), _ptr(out),
                                _stream(stream)), "glowq_ner_sums")
+    return out
+
+
+def ner_workspace_bytes_batch(n_outs: Sequence[int]) -> int:
+    return int(sum(lib().glowq_ner_workspace_bytes(n) for n in n_outs))
+
+
+def ner_sums_batch(ws_and_qws: Sequence, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp64 [n][2] pairs of glowq_ner_sums for (fp16 W, QWeight) pairs, in one batch call."""
+    items = [(w.contiguous(), qw) for w, qw in ws_and_qws]
+    dev = items[0][0].device
+    if out is None:
+        out = torch.empty(len(items), 2, dtype=torch.float64, device=dev)
+    if workspace is None:
+        workspace = torch.empty(ner_workspace_bytes_batch([qw.n_out for _, qw in items]), dtype=torch.uint8,
+                                device=dev)
+    wp = _arr(_vp, [w.data_ptr() for w, _ in items])
+    wc = _arr(QWeightC, [qw.c() for _, qw in items])
+    check(lib().glowq_ner_sums_batch(len(items), wp, wc, _ptr(workspace), workspace.numel(), _ptr(out),
+                                     _stream(stream)), "glowq_ner_sums_batch")
     return out
 
 

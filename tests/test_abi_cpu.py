@@ -148,6 +148,14 @@ def test_restore_selection_validates():
     assert L.glowq_ner_sums(FAKE + 8, ctypes.byref(wc), FAKE, need, FAKE, None) == g.ERR_ALIGN
     assert L.glowq_ner_sums(FAKE, ctypes.byref(wc), FAKE + 16, need, FAKE, None) == g.ERR_ALIGN
     assert L.glowq_ner_sums(FAKE, ctypes.byref(wc), FAKE, need - 1, FAKE, None) == g.ERR_WORKSPACE
+    wp = (ctypes.c_void_p * 2)(FAKE, 0)
+    wqs = (g.QWeightC * 2)(_w(), _w())
+    assert L.glowq_ner_sums_batch(0, wp, wqs, FAKE, 1 << 20, FAKE, None) == g.ERR_INVALID_ARG
+    assert L.glowq_ner_sums_batch(2, wp, wqs, FAKE, 1 << 20, FAKE, None) == g.ERR_INVALID_ARG
+    wp2 = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    assert L.glowq_ner_sums_batch(2, wp2, wqs, FAKE, 2 * need - 1, FAKE, None) == g.ERR_WORKSPACE
+    wqs_bad = (g.QWeightC * 2)(_w(), _w(n_out=0))
+    assert L.glowq_ner_sums_batch(2, wp2, wqs_bad, FAKE, 1 << 20, FAKE, None) == g.ERR_SHAPE
     assert L.glowq_restore_topk(None, 4, 1, 2, FAKE, FAKE, None) == g.ERR_INVALID_ARG
     assert L.glowq_restore_topk(FAKE, 0, 1, 0, FAKE, FAKE, None) == g.ERR_SHAPE
     assert L.glowq_restore_topk(FAKE, 4097, 1, 2, FAKE, FAKE, None) == g.ERR_SHAPE

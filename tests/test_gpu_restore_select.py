@@ -65,6 +65,26 @@ def test_ner_ratio_llama_gate_shape():
     assert abs(got - want) <= REL * abs(want), (got, want)
 
 
+def test_batch_equals_single_calls():
+    """40 modules of mixed shapes in one batch call (two launches of up to 32 modules) give the
+    same pairs, bit for bit, as one call per module, and match the oracle."""
+    g = glowq()
+    shapes = [(16 + 8 * (i % 5), 128 * (1 + i % 3)) for i in range(40)]
+    items = []
+    for i, (O, d) in enumerate(shapes):
+        w, qw = make_module(O, d, (24, i))
+        items.append((w, qw, w.cuda(), g.QWeight.from_workload(qw)))
+    batch = g.ner_sums_batch([(wd, dq) for _, _, wd, dq in items])
+    single = torch.stack([g.ner_sums(wd, dq) for _, _, wd, dq in items])
+    torch.cuda.synchronize()
+    assert torch.equal(batch, single)
+    for i, (w, qw, _, _) in enumerate(items):
+        E, W64 = oracle_err_w(w, qw)
+        want = S.g_ner(E, W64)
+        got = float(batch[i, 0]) / float(batch[i, 1])
+        assert abs(got - want) <= REL * abs(want), (i, got, want)
+
+
 def check_masks(scores_gpu, mask_gpu, scores_ref, k):
     sg = [float(v) for v in scores_gpu.cpu()]
     mg = [bool(v) for v in mask_gpu.cpu()]
