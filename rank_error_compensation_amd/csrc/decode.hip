@@ -26,7 +26,10 @@
 // order; after a group is consumed its slot is refilled with the group U ahead.  Nibbles become exact fp16
 // (q - z) values in registers; four v_mfma_f32_16x16x32_f16 accumulate the group's partial sums
 // against the tokens (padded to 16 per tile); the per-(row, group) scale is applied once per group
-// in fp32.  The four waves' partial sums, each carrying its share of the correction terms, are
+// in fp32.  The correction A_i R is r_pad / 32 more matrix-core steps shared out over the waves
+// (R rounded once to fp16 for them, as in the prefill path; each wave's first A operand is loaded
+// with the weight ring, 9 % faster per restored launch than loading A and adding in fp32 after the
+// main loop).  The four waves' partial sums, each carrying its share of the correction terms, are
 // reduced in LDS in a fixed order (deterministic) and rounded once to fp16.
 #include "glowq_internal.h"
 
@@ -349,6 +352,15 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
     // prologue: fill the ring (indices past the wave's last group reload that group)
 #pragma unroll
     for (int u = 0; u < U; ++u) issue(u, min(u, max(n_my - 1, 0)));
+    // with the ring: the A operand of this wave's first correction step (rank columns
+    // 32 wave .. 32 wave + 31), so that its latency is hidden by the weight stream
+    h8 apre[RT];
+#pragma unroll
+    for (int rr = 0; rr < RT; ++rr) {
+        const int row = (rt0 + rr) * 16 + (lane & 15);
+        const int col = 32 * wave + 8 * (lane >> 4);
+        apre[rr] = (correct && row < M.n_out && col < r) ? load_h8(M.a + (size_t)row * r + col) : zero8;
+    }
     if (XLDS) {
 #pragma unroll
         for (int c = 0; c < XC; ++c) {
@@ -388,71 +400,45 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
         top_prev = arrive_xcd(args, arrived);
     }
 
-    // correction epilogue: this wave adds R[t][8c..8c+8) . A[row][8c..8c+8) for chunks c = wave mod KW.
-    // The first A chunks are loaded before R is needed; with one token tile R is copied once into
-    // LDS (coherent 8-byte pair reads of this workgroup's copy, which also wait for the producers)
-    // and read from there; otherwise each element is read as a pair.
+    // correction epilogue on the matrix cores: acc += A_i[rows][32 kb .. +32) R[tokens][32 kb .. +32)^T
+    // for the K steps kb = wave, wave + KW, ... (A operand: 16 rows x 32 rank columns straight
+    // from A_i; B operand: R rounded once to fp16, as in the prefill path).  With one token tile R
+    // is copied once into LDS (coherent 8-byte pair reads of this workgroup's copy, which also
+    // wait for the producers) and read from there; otherwise each element is read as a pair.
     if (correct) {
-        const int nc8 = r / 8;
         const u64* Rp = reinterpret_cast<const u64*>(args.R) +
                         (size_t)(blockIdx.x & (kRReplicas - 1)) * args.n_proj * T * r + (size_t)M.proj * T * r;
-        constexpr int PF = RT == 1 ? 2 : 1;  // A chunks prefetched per wave
-        h8 apf[PF][RT][4];
-#pragma unroll
-        for (int k = 0; k < PF; ++k) {
-            const int c = wave + KW * k;
-#pragma unroll
-            for (int rr = 0; rr < RT; ++rr)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = (rt0 + rr) * 16 + 4 * (lane >> 4) + i;
-                    apf[k][rr][i] = (c < nc8 && row < M.n_out) ? load_h8(M.a + (size_t)row * r + 8 * c) : zero8;
-                }
-        }
         float* rl = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(xs) + args.r_lds_off);
         if (NTT == 1) {
             for (int k = threadIdx.x; k < T * r; k += NTH) rl[k] = load_pair(args, Rp + k, tag);
             __syncthreads();
         }
-        for (int c = wave, k = 0; c < nc8; c += KW, ++k) {
-            h8 a8[RT][4];
+        for (int kb = wave; kb * 32 < r; kb += KW) {
+            const int col = 32 * kb + 8 * (lane >> 4);  // r % 8 == 0: col < r covers col .. col + 7
+            h8 aop[RT];
 #pragma unroll
-            for (int rr = 0; rr < RT; ++rr)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (k < PF) {
-#pragma unroll
-                        for (int kk = 0; kk < PF; ++kk)
-                            if (kk == k) a8[rr][i] = apf[kk][rr][i];
-                    } else {
-                        const int row = (rt0 + rr) * 16 + 4 * (lane >> 4) + i;
-                        a8[rr][i] = row < M.n_out ? load_h8(M.a + (size_t)row * r + 8 * c) : zero8;
-                    }
-                }
+            for (int rr = 0; rr < RT; ++rr) {
+                const int row = (rt0 + rr) * 16 + (lane & 15);
+                aop[rr] = kb == wave ? apre[rr]
+                                     : ((row < M.n_out && col < r) ? load_h8(M.a + (size_t)row * r + col) : zero8);
+            }
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
                 const int t = 16 * tt + (lane & 15);
-                if (t < T) {
-                    float rv[8];
+                h8 bop = zero8;
+                if (t < T && col < r) {
                     if (NTT == 1) {
-                        const f4* rp = reinterpret_cast<const f4*>(rl + (size_t)t * r + 8 * c);
+                        const f4* rp = reinterpret_cast<const f4*>(rl + (size_t)t * r + col);
                         const f4 r0 = rp[0], r1 = rp[1];
-                        rv[0] = r0[0]; rv[1] = r0[1]; rv[2] = r0[2]; rv[3] = r0[3];
-                        rv[4] = r1[0]; rv[5] = r1[1]; rv[6] = r1[2]; rv[7] = r1[3];
+                        bop = h8{(_Float16)r0[0], (_Float16)r0[1], (_Float16)r0[2], (_Float16)r0[3],
+                                 (_Float16)r1[0], (_Float16)r1[1], (_Float16)r1[2], (_Float16)r1[3]};
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) rv[e] = load_pair(args, Rp + (size_t)t * r + 8 * c + e, tag);
+                        for (int e = 0; e < 8; ++e) bop[e] = (_Float16)load_pair(args, Rp + (size_t)t * r + col + e, tag);
                     }
-#pragma unroll
-                    for (int rr = 0; rr < RT; ++rr)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            float s = acc[rr][tt][i];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) s = fmaf((float)a8[rr][i][e], rv[e], s);
-                            acc[rr][tt][i] = s;
-                        }
                 }
+#pragma unroll
+                for (int rr = 0; rr < RT; ++rr) acc[rr][tt] = mfma16(aop[rr], bop, acc[rr][tt]);
             }
         }
     }
