@@ -20,6 +20,8 @@ be pinned end to end (an exactly rank-r error is reproduced to rounding):
     factor); a randomized SVD with oversampling p and q power iterations extracts the
     dominant subspace; balanced factors A = U_r S_r^{1/2}, B = S_r^{1/2} V_r^T are lifted
     back to the original variables (pseudo-inverse square root when Sigma_x is singular).
+  * Sigma_x is the uncentred second moment of the calibration inputs, X^T X / N (the
+    identity of key design 2 needs E[x x^T]).
   * key design 4: restore scores g_ec(u) = sum_{j<=r} sigma_j(M_u)^2 / ||M_u||_F^2 and
     g_ner(u) = ||E_u||_F^2 / ||W_u||_F^2; the top-k units are restored, layer order
     breaking ties (the pages fall back to layer order when the signal is weak).
@@ -29,6 +31,15 @@ from __future__ import annotations
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
+
+
+def second_moment(X) -> np.ndarray:
+    """Input second moment Sigma_x = E[x x^T] over calibration tokens: X is [N][d] (one token
+    per row), Sigma_x = X^T X / N in fp64.  key design 2 (GlowQ paper note): the usage-weighted
+    risk E||M x||^2 = ||M Sigma_x^{1/2}||_F^2 holds for this uncentred moment; Figure 2 of the
+    arXiv page streams calibration samples and takes the empirical input covariance."""
+    X = np.asarray(X, dtype=np.float64)
+    return (X.T @ X) / X.shape[0]
 
 
 def stack_errors(E_list: Sequence[np.ndarray]) -> np.ndarray:

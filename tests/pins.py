@@ -342,6 +342,31 @@ def check_usage_weighted_risk(sol):
     assert abs(mc - lhs) <= 4 * se
 
 
+def check_second_moment(sol):
+    """Sigma_x = X^T X / N: brute force with correctly rounded sums on a tiny input; the
+    usage-weighted risk identity on the sample itself (mean of ||M x_t||^2 over the tokens equals
+    tr(M Sigma_x M^T)); a closed form (tokens that are scaled basis vectors give a diagonal);
+    symmetry and invariance to the token order."""
+    rng = np.random.default_rng(61)
+    X = rng.standard_normal((7, 5))
+    S = sol.second_moment(X)
+    for i in range(5):
+        for j in range(5):
+            want = math.fsum(X[t, i] * X[t, j] for t in range(7)) / 7
+            assert abs(S[i, j] - want) <= 1e-15 * (1 + abs(want)), (i, j)
+    X = rng.standard_normal((300, 16))
+    M = rng.standard_normal((6, 16))
+    S = sol.second_moment(X)
+    risk = math.fsum(float(np.sum((M @ X[t]) ** 2)) for t in range(300)) / 300
+    assert abs(risk - float(np.trace(M @ S @ M.T))) <= 1e-12 * risk
+    assert np.array_equal(S, S.T) or np.max(np.abs(S - S.T)) <= 1e-15 * np.max(np.abs(S))
+    perm = rng.permutation(300)
+    assert np.max(np.abs(sol.second_moment(X[perm]) - S)) <= 1e-13 * np.max(np.abs(S))
+    E = np.zeros((6, 3))
+    E[0, 0], E[1, 1], E[2, 1], E[3, 2], E[4, 2], E[5, 2] = 2.0, 1.0, -3.0, 1.0, 1.0, 2.0
+    assert np.array_equal(sol.second_moment(E), np.diag([4.0 / 6, 10.0 / 6, 6.0 / 6]))
+
+
 def check_qr_core(sol):
     """sigma(R_e Sigma^{1/2}) = sigma(E_cat Sigma^{1/2}) (left-orthogonal invariance)."""
     rng = np.random.default_rng(61)
@@ -420,4 +445,4 @@ ALL_REF_CHECKS = [check_dequant_exhaustive, check_dequant_golden, check_restore_
                   check_associativity_small_int, check_bruteforce, check_row_independence,
                   check_path_mask]
 ALL_SOL_CHECKS = [check_eckart_young, check_isotropic, check_usage_weighted_risk, check_qr_core,
-                  check_cholesky_vs_symmetric, check_randomized_svd, check_scores]
+                  check_cholesky_vs_symmetric, check_randomized_svd, check_scores, check_second_moment]

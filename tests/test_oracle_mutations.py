@@ -123,6 +123,23 @@ def topk_lowest(scores, k):
     return [u in chosen for u in range(len(scores))]
 
 
+def moment_centred(X):
+    X = np.asarray(X, dtype=np.float64)
+    Xc = X - X.mean(axis=0)
+    return (Xc.T @ Xc) / X.shape[0]
+
+
+def moment_unbiased(X):
+    X = np.asarray(X, dtype=np.float64)
+    return (X.T @ X) / (X.shape[0] - 1)
+
+
+def moment_token_gram(X):
+    X = np.asarray(X, dtype=np.float64)
+    G = X @ X.T / X.shape[1]
+    return G[:X.shape[1], :X.shape[1]] if G.shape[0] >= X.shape[1] else np.pad(G, (0, X.shape[1] - G.shape[0]))
+
+
 REF_MUTANTS = {
     "dequant_plus_z": dict(dequant=dequant_plus_z),
     "dequant_group64": dict(dequant=dequant_group64),
@@ -141,6 +158,9 @@ SOL_MUTANTS = {
     "unbalanced_full_s": dict(whitened_factors=whitened_full_s),
     "no_whitening": dict(whitened_factors=whitened_unwhitened),
     "topk_lowest": dict(topk_restore=topk_lowest),
+    "moment_centred": dict(second_moment=moment_centred),
+    "moment_unbiased": dict(second_moment=moment_unbiased),
+    "moment_token_gram": dict(second_moment=moment_token_gram),
 }
 
 
