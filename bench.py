@@ -312,6 +312,40 @@ def extra_restore_selection(g, reps=3, k=16):
     return out
 
 
+def extra_second_moment(g, reps=5):
+    """Offline factor solve, first step: Sigma_x = X^T X / N over 64 calibration sequences of 2048
+    tokens at d = 4096 (the LLaMA-2-7B attention input), activations resident in HBM."""
+    import torch
+    import workload as W
+    d, seqs, L = 4096, 64, 2048
+    basis = W.haar_basis(d, 42, 0)
+    x = torch.cat([W.make_x(L, d, 1.19, (42, q), device="cuda", basis=basis) for q in range(seqs)])
+    N = int(x.shape[0])
+    out = torch.empty(d, d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(int(g.lib().glowq_second_moment_workspace_bytes(N, d)), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    g.second_moment(x, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.second_moment(x, out=out, workspace=ws)
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    t = statistics.median(ts)
+    nb = d // 128
+    alg = N * d * (d + 1)                       # N d (d + 1) / 2 distinct products, 2 flops each
+    executed = 2 * N * 128 * 128 * (nb * (nb + 1) // 2)
+    del x, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"Sigma_x = X^T X / N, N = {seqs} x {L} calibration tokens, d = {d}",
+            "ms": round(t * 1e3, 3), "alg_TFLOP_per_s": round(alg / t / 1e12, 1),
+            "executed_TFLOP_per_s": round(executed / t / 1e12, 1),
+            "frac_mfma_f16_peak": round(executed / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+
+
 def achievable_peaks(reps=5):
     """The achievable peaks on this GPU, measured by the probe library: a streaming read of a
     4 GiB buffer (16 times the last-level cache) and a matrix-core-only fp16 loop."""
@@ -491,6 +525,10 @@ def main():
         e = extra["restore_selection_32L"]
         e["frac_hbm_measured_peak"] = round(e["GB_per_s"] / peaks["hbm_read_GB_per_s"], 4)
         log(f"[bench] restore selection: {e}")
+        extra["second_moment_calib"] = extra_second_moment(g)
+        e = extra["second_moment_calib"]
+        e["frac_mfma_measured_peak"] = round(e["executed_TFLOP_per_s"] / peaks["mfma_f16_TFLOP_per_s"], 4)
+        log(f"[bench] second moment: {e}")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -206,6 +206,27 @@ int glowq_ner_sums_batch(int32_t n, const void* const* w_devs, const glowq_qweig
 int glowq_restore_topk(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k,
                        double* scores_dev, int32_t* mask_dev, hipStream_t stream);
 
+/* ---------------------------------------------------------------- offline factor solve
+ * Input second moment of the calibration activations, the statistic the covariance-aligned fit
+ * is built on (GlowQ paper note, key design 2: the usage-weighted risk E||M x||^2 equals
+ * ||M Sigma_x^{1/2}||_F^2 with Sigma_x = E[x x^T]; the arXiv page, Figure 2, takes the empirical
+ * input covariance of the calibration samples).
+ */
+
+/* Workspace bytes of glowq_second_moment (0 if N or d is invalid). */
+size_t glowq_second_moment_workspace_bytes(int64_t N, int64_t d);
+
+/* Sigma_x = X^T X / N:
+ *   x_dev     : fp16 [N][d], one calibration token per row (N >= 1; d % 128 == 0, d <= 16384,
+ *               N d <= 2^31)
+ *   sigma_dev : fp32 [d][d] output, symmetric (both triangles written)
+ * Products of fp16 values are exact in fp32 and accumulated in fp32 on the matrix cores per
+ * token range, the ranges added in a fixed order (bitwise repeatable), then scaled by 1 / N.
+ * workspace: at least glowq_second_moment_workspace_bytes(N, d) bytes, 256-byte aligned,
+ * overwritten.  Asynchronous. */
+int glowq_second_moment(const void* x_dev, int64_t N, int64_t d, float* sigma_dev, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

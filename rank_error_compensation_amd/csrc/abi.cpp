@@ -18,6 +18,8 @@ namespace {
 constexpr int64_t kMaxT = 1 << 20;
 constexpr int64_t kMaxD = 1 << 20;
 constexpr int64_t kMaxRows = 1 << 24;
+constexpr int64_t kMaxMomentD = 16384;              // features of a second-moment call
+constexpr int64_t kMaxMomentElems = (int64_t)1 << 31;  // N d (int32 offsets stay in range)
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -345,6 +347,63 @@ int glowq_ner_sums(const void* w_dev, const glowq_qweight* wq, void* workspace, 
     if (!w_dev || !wq) return GLOWQ_ERR_INVALID_ARG;
     const void* w_devs[1] = {w_dev};
     return glowq_ner_sums_batch(1, w_devs, wq, workspace, workspace_bytes, sums_dev, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Token ranges of the second-moment launch: the count in 1..16 whose workgroup total comes
+// closest to whole rounds of 1024 resident workgroups (4 per CU), at least 1024 workgroups when
+// the ranges allow (each range at least 32 tokens).
+void moment_plan(int64_t N, int64_t d, int32_t& n_tiles, int32_t& S, int32_t& kc) {
+    const int64_t nb = d / kGroup;
+    n_tiles = (int32_t)(nb * (nb + 1) / 2);
+    const int64_t steps = ceil_div(N, 32);
+    double best = 1e30;
+    int32_t best_s = 1;
+    for (int32_t s = 1; s <= 16 && s <= steps; ++s) {
+        const double units = (double)n_tiles * s;
+        const double rounds = (double)ceil_div((int64_t)units, 1024);
+        const double waste = rounds / (units / 1024.0) + (units < 1024 ? 1.0 : 0.0);
+        if (waste < best - 1e-9) {
+            best = waste;
+            best_s = s;
+        }
+    }
+    S = best_s;
+    kc = (int32_t)(ceil_div(steps, S) * 32);
+    S = (int32_t)ceil_div(N, kc);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t glowq_second_moment_workspace_bytes(int64_t N, int64_t d) {
+    if (N < 1 || d < kGroup || d % kGroup != 0 || d > kMaxMomentD || N * d > kMaxMomentElems) return 0;
+    int32_t n_tiles, S, kc;
+    moment_plan(N, d, n_tiles, S, kc);
+    return round256((size_t)S * n_tiles * 16384u * 4u);
+}
+
+int glowq_second_moment(const void* x_dev, int64_t N, int64_t d, float* sigma_dev, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    if (!x_dev || !sigma_dev || !workspace) return GLOWQ_ERR_INVALID_ARG;
+    if (N < 1 || d < kGroup || d % kGroup != 0) return GLOWQ_ERR_SHAPE;
+    if (d > kMaxMomentD || N * d > kMaxMomentElems) return GLOWQ_ERR_UNSUPPORTED;
+    if (!aligned(x_dev, 16) || !aligned(sigma_dev, 16) || !aligned(workspace, 256)) return GLOWQ_ERR_ALIGN;
+    if (workspace_bytes < glowq_second_moment_workspace_bytes(N, d)) return GLOWQ_ERR_WORKSPACE;
+    MomentArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = static_cast<const _Float16*>(x_dev);
+    a.N = (int32_t)N;
+    a.d = (int32_t)d;
+    moment_plan(N, d, a.n_tiles, a.S, a.kc);
+    a.inv_n = (float)(1.0 / (double)N);
+    a.part = static_cast<float*>(workspace);
+    a.sigma = sigma_dev;
+    return launch_moment(a, stream) == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
 }
 
 int glowq_restore_topk(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k,

@@ -69,6 +69,8 @@ EXPORTS = {
     "glowq_ner_sums_batch": (ctypes.c_int, [_i32, ctypes.POINTER(_vp), ctypes.POINTER(QWeightC), _vp, _sz,
                                             _vp, _vp]),
     "glowq_restore_topk": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "glowq_second_moment_workspace_bytes": (_sz, [_i64, _i64]),
+    "glowq_second_moment": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -205,6 +207,22 @@ def restore_topk(sums: torch.Tensor, k: int, stream=None):
     check(lib().glowq_restore_topk(_ptr(sums), n_units, n_per, k, _ptr(scores), _ptr(mask),
                                    _stream(stream)), "glowq_restore_topk")
     return scores, mask
+
+
+# --------------------------------------------------------------------------- offline factor solve
+def second_moment(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp32 [d][d] Sigma_x = X^T X / N of fp16 calibration activations x [N][d]."""
+    x = x.contiguous()
+    N, d = int(x.shape[0]), int(x.shape[1])
+    if out is None:
+        out = torch.empty(d, d, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(int(lib().glowq_second_moment_workspace_bytes(N, d)), dtype=torch.uint8,
+                                device=x.device)
+    check(lib().glowq_second_moment(_ptr(x), N, d, _ptr(out), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)), "glowq_second_moment")
+    return out
 
 
 # --------------------------------------------------------------------------- forward

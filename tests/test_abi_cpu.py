@@ -165,6 +165,21 @@ def test_restore_selection_validates():
     assert L.glowq_restore_topk(FAKE, 4, 1, 2, FAKE, FAKE + 4, None) == g.ERR_ALIGN
 
 
+def test_second_moment_validates():
+    L = g.lib()
+    assert L.glowq_second_moment_workspace_bytes(0, 128) == 0
+    assert L.glowq_second_moment_workspace_bytes(4, 100) == 0
+    assert L.glowq_second_moment_workspace_bytes(4, 16512) == 0
+    need = L.glowq_second_moment_workspace_bytes(1000, 256)
+    assert need > 0 and need % 256 == 0
+    assert L.glowq_second_moment(None, 1000, 256, FAKE, FAKE, need, None) == g.ERR_INVALID_ARG
+    assert L.glowq_second_moment(FAKE, 1000, 200, FAKE, FAKE, need, None) == g.ERR_SHAPE
+    assert L.glowq_second_moment(FAKE, 0, 256, FAKE, FAKE, need, None) == g.ERR_SHAPE
+    assert L.glowq_second_moment(FAKE, 1000, 256, FAKE + 8, FAKE, need, None) == g.ERR_ALIGN
+    assert L.glowq_second_moment(FAKE, 1000, 256, FAKE, FAKE, need - 1, None) == g.ERR_WORKSPACE
+    assert L.glowq_second_moment(FAKE, 1 << 20, 4096, FAKE, FAKE, 1 << 40, None) == g.ERR_UNSUPPORTED
+
+
 def test_path_validates_every_unit_first():
     L = g.lib()
     wq = (g.QWeightC * 1)(_w())
