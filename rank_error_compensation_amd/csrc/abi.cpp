@@ -10,6 +10,7 @@
 
 #include "glowq.h"
 #include "glowq_internal.h"
+#include "glowq_offline.h"
 
 using namespace glowq;
 

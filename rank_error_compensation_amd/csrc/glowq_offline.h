@@ -1,0 +1,44 @@
+// Offline steps around the inference path (restore selection, factor solve): kernel argument
+// blocks and launchers shared by score.hip / moment.hip and the C ABI.
+#ifndef GLOWQ_OFFLINE_H
+#define GLOWQ_OFFLINE_H
+
+#include "glowq_internal.h"
+
+namespace glowq {
+
+// Modules of one restore-score launch (their descriptors travel in the kernel arguments).
+constexpr int kNerBatch = 32;
+struct NerBatch {
+    int32_t n_mod;
+    int32_t tile_begin[kNerBatch + 1];  // prefix of the modules' 16-row tiles
+    int32_t n_out[kNerBatch], k_in[kNerBatch];
+    const _Float16* w[kNerBatch];       // fp16 [n_out][k_in]
+    const uint8_t* q[kNerBatch];        // device layout
+    const uint8_t* sz[kNerBatch];
+    double* part;                       // [tiles][2]
+    double* sums;                       // [n_mod][2]
+};
+hipError_t launch_ner(const NerBatch& a, hipStream_t stream);
+hipError_t launch_topk(const double* sums, int32_t n_units, int32_t n_per, int32_t k, double* scores,
+                       int32_t* mask, hipStream_t stream);
+
+// Input second moment (offline factor solve): lower-triangle 128 x 128 tiles x token ranges.
+struct MomentArgs {
+    const _Float16* x;   // [N][d] calibration activations
+    int32_t N, d;
+    int32_t n_tiles;     // (d / 128) (d / 128 + 1) / 2
+    int32_t S, kc;       // token ranges and tokens per range (a multiple of 32)
+    float inv_n;
+    float* part;         // [S][n_tiles][128][128] fp32 partial sums
+    float* sigma;        // [d][d]
+};
+hipError_t launch_moment(const MomentArgs& a, hipStream_t stream);
+typedef _Float16 h4x __attribute__((ext_vector_type(4)));
+
+// Most units one restore selection ranks (their scores sit in LDS).
+constexpr int kMaxScoreUnits = 4096;
+
+}  // namespace glowq
+
+#endif  // GLOWQ_OFFLINE_H

@@ -17,7 +17,7 @@
 // moment_reduce_kernel: adds the partials of the token ranges in range order (deterministic),
 // scales by 1 / N and writes Sigma and its mirror image (only i >= j inside diagonal tiles, so that
 // every element has one writer).
-#include "glowq_internal.h"
+#include "glowq_offline.h"
 
 namespace glowq {
 

@@ -16,7 +16,7 @@
 //     (0 when sum_m w is 0) and restores the k best units, equal scores going to the lower unit
 //     index (the order in which the pages fall back to layer order).
 // Everything HBM-bound: per weight element 2 bytes of W, half a byte of q, 4/128 of (z, s).
-#include "glowq_internal.h"
+#include "glowq_offline.h"
 
 namespace glowq {
 
