@@ -355,8 +355,8 @@ int glowq_ner_sums(const void* w_dev, const glowq_qweight* wq, void* workspace, 
 namespace {
 
 // Token ranges of the second-moment launch: the count in 1..16 whose workgroup total comes
-// closest to whole rounds of 1024 resident workgroups (4 per CU), at least 1024 workgroups when
-// the ranges allow (each range at least 32 tokens).
+// closest to whole rounds of the resident workgroups, at least one round when the ranges allow
+// (each range at least 32 tokens).
 void moment_plan(int64_t N, int64_t d, int32_t& n_tiles, int32_t& S, int32_t& kc) {
     const int64_t nb = d / kGroup;
     n_tiles = (int32_t)(nb * (nb + 1) / 2);
@@ -365,8 +365,8 @@ void moment_plan(int64_t N, int64_t d, int32_t& n_tiles, int32_t& S, int32_t& kc
     int32_t best_s = 1;
     for (int32_t s = 1; s <= 16 && s <= steps; ++s) {
         const double units = (double)n_tiles * s;
-        const double rounds = (double)ceil_div((int64_t)units, 1024);
-        const double waste = rounds / (units / 1024.0) + (units < 1024 ? 1.0 : 0.0);
+        const double rounds = (double)ceil_div((int64_t)units, kMomentResident);
+        const double waste = rounds / (units / kMomentResident) + (units < kMomentResident ? 1.0 : 0.0);
         if (waste < best - 1e-9) {
             best = waste;
             best_s = s;

@@ -7,8 +7,9 @@
 // step of 32 tokens the two 32 x 128 activation slices (the tile's row and column features) are
 // copied HBM -> LDS by the load unit (global_load_lds, 16 bytes per lane, token-major as they lie
 // in memory; 16-byte chunk c of token row r sits at position c ^ 4 (r % 4), so that the four rows a
-// transposing read touches fall on different banks), double-buffered.  The matrix-core operands
-// need the tokens (the contraction index) along each lane, i.e. the slices transposed: every
+// transposing read touches fall on different banks), in a ring of three steps (two in flight).
+// The matrix-core operands need the tokens (the contraction index) along each lane, i.e. the
+// slices transposed: every
 // operand is two ds_read_b64_tr_b16, which hand lane 4a + b of each 16-lane group element b of the
 // 8-byte chunks addressed by lanes a, a + 4, a + 8, a + 12 -- with lane q addressing token
 // t + q / 4, features f + 4 (q % 4), lane i receives feature f + i of tokens t .. t + 3.  Each wave
@@ -55,7 +56,8 @@ __device__ __forceinline__ h8 tr_operand(const _Float16* slice, int row0, int fc
 }
 
 __global__ __launch_bounds__(256) void moment_kernel(const MomentArgs a) {
-    __shared__ __attribute__((aligned(16))) _Float16 xs[2][2][32 * 128];  // [buffer][row / column slice]
+    constexpr int R = kMomentStages;  // ring of 32-token steps in LDS
+    __shared__ __attribute__((aligned(16))) _Float16 xs[R][2][32 * 128];  // [stage][row / column slice]
     const int u = blockIdx.x;
     const int tile = u % a.n_tiles, s = u / a.n_tiles;
     int bi, bj;
@@ -94,12 +96,24 @@ __global__ __launch_bounds__(256) void moment_kernel(const MomentArgs a) {
 #pragma unroll
             for (int k = 0; k < 16; ++k) acc[x][y][k] = 0.f;
 
-    if (steps > 0) copy(0, 0);
+    // R - 1 steps in flight: at step st this wave waits only for its own copy of step st (the
+    // copies of the later steps, 4 instructions each, may stay outstanding), then the barrier
+    // makes every wave's copy visible; the copy of step st + R - 1 goes to the stage step st - 1
+    // used, which every wave has finished reading by then.
+#pragma unroll
+    for (int p = 0; p < R - 1; ++p)
+        if (p < steps) copy(p, p);
     for (int st = 0; st < steps; ++st) {
-        const int buf = st & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const int buf = st % R;
+        const int later = min(R - 2, steps - 1 - st);
+        if (later >= 2)
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if (later == 1)
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (st + 1 < steps) copy(st + 1, buf ^ 1);
+        if (st + R - 1 < steps) copy(st + R - 1, (st + R - 1) % R);
         const int valid = t_end - (t_begin + 32 * st);  // tokens of this step (>= 32 except the last)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
