@@ -335,9 +335,9 @@ def extra_second_moment(g, reps=5):
         e1.synchronize()
         ts.append(e0.elapsed_time(e1) * 1e-3)
     t = statistics.median(ts)
-    nb = d // 128
+    nb = -(-d // 256)                           # 256 x 256 lower-triangle tiles
     alg = N * d * (d + 1)                       # N d (d + 1) / 2 distinct products, 2 flops each
-    executed = 2 * N * 128 * 128 * (nb * (nb + 1) // 2)
+    executed = 2 * N * 256 * 256 * (nb * (nb + 1) // 2)
     del x, out, ws
     torch.cuda.empty_cache()
     return {"workload": f"Sigma_x = X^T X / N, N = {seqs} x {L} calibration tokens, d = {d}",

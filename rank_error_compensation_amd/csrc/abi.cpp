@@ -358,7 +358,7 @@ namespace {
 // closest to whole rounds of the resident workgroups, at least one round when the ranges allow
 // (each range at least 32 tokens).
 void moment_plan(int64_t N, int64_t d, int32_t& n_tiles, int32_t& S, int32_t& kc) {
-    const int64_t nb = d / kGroup;
+    const int64_t nb = ceil_div(d, kMomentTile);  // the last block may be half empty (d % 256 == 128)
     n_tiles = (int32_t)(nb * (nb + 1) / 2);
     const int64_t steps = ceil_div(N, 32);
     double best = 1e30;
@@ -385,7 +385,7 @@ size_t glowq_second_moment_workspace_bytes(int64_t N, int64_t d) {
     if (N < 1 || d < kGroup || d % kGroup != 0 || d > kMaxMomentD || N * d > kMaxMomentElems) return 0;
     int32_t n_tiles, S, kc;
     moment_plan(N, d, n_tiles, S, kc);
-    return round256((size_t)S * n_tiles * 16384u * 4u);
+    return round256((size_t)S * n_tiles * kMomentTile * kMomentTile * 4u);
 }
 
 int glowq_second_moment(const void* x_dev, int64_t N, int64_t d, float* sigma_dev, void* workspace,

@@ -23,21 +23,22 @@ hipError_t launch_ner(const NerBatch& a, hipStream_t stream);
 hipError_t launch_topk(const double* sums, int32_t n_units, int32_t n_per, int32_t k, double* scores,
                        int32_t* mask, hipStream_t stream);
 
-// Input second moment (offline factor solve): lower-triangle 128 x 128 tiles x token ranges.
+// Input second moment (offline factor solve): lower-triangle tiles x token ranges.
 struct MomentArgs {
     const _Float16* x;   // [N][d] calibration activations
     int32_t N, d;
-    int32_t n_tiles;     // (d / 128) (d / 128 + 1) / 2
+    int32_t n_tiles;     // (d / kMomentTile) (d / kMomentTile + 1) / 2
     int32_t S, kc;       // token ranges and tokens per range (a multiple of 32)
     float inv_n;
-    float* part;         // [S][n_tiles][128][128] fp32 partial sums
+    float* part;         // [S][n_tiles][kMomentTile][kMomentTile] fp32 partial sums
     float* sigma;        // [d][d]
 };
 hipError_t launch_moment(const MomentArgs& a, hipStream_t stream);
-// 32-token steps of the second-moment kernel's LDS ring (3 x 16 KiB: three workgroups per CU; measured
-// 3.42 ms at the calibration shape vs 3.51 ms with 2 stages and 4.13 ms with 4).
-constexpr int kMomentStages = 3;
-constexpr int kMomentResident = 768;  // workgroups resident at once (256 CUs x 3)
+// Second-moment kernel: 256 x 256 tiles (four waves of 128 x 128, 4 x 4 matrix-core blocks each),
+// a ring of four 32-token LDS steps (4 x 32 KiB, one workgroup per CU).
+constexpr int kMomentTile = 256;
+constexpr int kMomentStages = 4;
+constexpr int kMomentResident = 256;  // workgroups resident at once (one per CU)
 typedef _Float16 h4x __attribute__((ext_vector_type(4)));
 
 // Most units one restore selection ranks (their scores sit in LDS).
