@@ -227,6 +227,30 @@ size_t glowq_second_moment_workspace_bytes(int64_t N, int64_t d);
 int glowq_second_moment(const void* x_dev, int64_t N, int64_t d, float* sigma_dev, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes of glowq_solve_factors (0 if the sizes are invalid). */
+size_t glowq_solve_workspace_bytes(int64_t m, int64_t d, int32_t k, int32_t r);
+
+/* Shared factors of one input-sharing group (GlowQ paper note, key designs 1-3): the group's
+ * quantisation errors stacked row-wise, E_cat (m x d), whitened by the input second moment,
+ * then a randomized SVD with the caller's test matrix and q power iterations, balanced factors
+ * and the lift back to the original variables:
+ *   e_dev     : fp64 [m][d] stacked errors W_i - W_hat_i of the group's modules
+ *   sigma_dev : fp64 [d][d] Sigma_x, symmetric positive definite
+ *   omega_dev : fp64 [d][k] test matrix (k = r + p oversampled columns, r <= k <= min(96, d))
+ *   r, q      : rank, power iterations (0 <= q <= 16)
+ *   a_dev     : fp64 [m][r] output A = U_r S_r^{1/2} (rows of module i at its offset in E_cat)
+ *   b_dev     : fp64 [r][d] output B = S_r^{1/2} V_r^T L^{-1}
+ *   s_dev     : fp64 [r] output, the r largest singular values of the whitened error
+ * Whitening uses the Cholesky factor L of Sigma_x (Sigma_x = L L^T); the product A B is the same
+ * for every square root of Sigma_x.  The range finder runs on E_cat L directly (the same bases
+ * as on the QR-reduced core R_e L, up to the left factor Q_e that A carries).  All arithmetic in
+ * fp64.  This is an offline step: it SYNCHRONISES `stream` and returns GLOWQ_ERR_RANGE if
+ * Sigma_x is not positive definite.  workspace: at least glowq_solve_workspace_bytes(m, d, k, r)
+ * bytes, 256-byte aligned, overwritten. */
+int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double* sigma_dev,
+                        const double* omega_dev, int32_t r, int32_t k, int32_t q, double* a_dev, double* b_dev,
+                        double* s_dev, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -407,6 +407,70 @@ int glowq_second_moment(const void* x_dev, int64_t N, int64_t d, float* sigma_de
     return launch_moment(a, stream) == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
 }
 
+size_t glowq_solve_workspace_bytes(int64_t m, int64_t d, int32_t k, int32_t r) {
+    if (m < 1 || d < 1 || r < 1 || k < r || k > kSolveMaxK || k > d || m > kMaxRows || d > kMaxMomentD) return 0;
+    const size_t n = (size_t)d * d + (size_t)m * d + (size_t)m * k + (size_t)d * k + 2u * (size_t)k * k + (size_t)k +
+                     (size_t)k * d + (size_t)r * d + 2u;
+    return round256(n * sizeof(double));
+}
+
+int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double* sigma_dev,
+                        const double* omega_dev, int32_t r, int32_t k, int32_t q, double* a_dev, double* b_dev,
+                        double* s_dev, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!e_dev || !sigma_dev || !omega_dev || !a_dev || !b_dev || !s_dev || !workspace) return GLOWQ_ERR_INVALID_ARG;
+    if (m < 1 || d < 1 || r < 1 || k < r || q < 0 || q > 16) return GLOWQ_ERR_SHAPE;
+    if (k > kSolveMaxK || k > d || m > kMaxRows || d > kMaxMomentD) return GLOWQ_ERR_UNSUPPORTED;
+    const void* ptrs[] = {e_dev, sigma_dev, omega_dev, a_dev, b_dev, s_dev};
+    for (const void* p : ptrs)
+        if (!aligned(p, 16)) return GLOWQ_ERR_ALIGN;
+    if (!aligned(workspace, 256)) return GLOWQ_ERR_ALIGN;
+    if (workspace_bytes < glowq_solve_workspace_bytes(m, d, k, r)) return GLOWQ_ERR_WORKSPACE;
+    const int M = (int)m, D = (int)d;
+    double* L = static_cast<double*>(workspace);
+    double* Et = L + (size_t)d * d;
+    double* Y = Et + (size_t)m * d;
+    double* Z = Y + (size_t)m * k;
+    double* G = Z + (size_t)d * k;
+    double* V = G + (size_t)k * k;
+    double* w = V + (size_t)k * k;
+    double* Bs = w + k;
+    double* Bw = Bs + (size_t)k * d;
+    int* flag = reinterpret_cast<int*>(Bw + (size_t)r * d);
+    auto gemm = [&](int Mm, int Nn, int Kk, const double* A, int lda, int ta, const double* B, int ldb, int tb,
+                    double* C, int ldc) {
+        GemmArgs g{};
+        g.M = Mm, g.N = Nn, g.K = Kk, g.A = A, g.lda = lda, g.ta = ta, g.B = B, g.ldb = ldb, g.tb = tb;
+        g.C = C, g.ldc = ldc, g.alpha = 1.0, g.beta = 0.0;
+        return launch_gemm(g, stream) == hipSuccess;
+    };
+    bool ok = hipMemcpyAsync(L, sigma_dev, (size_t)d * d * sizeof(double), hipMemcpyDeviceToDevice, stream) ==
+              hipSuccess;
+    ok = ok && launch_cholesky(L, D, flag, stream) == hipSuccess;           // Sigma_x = L L^T
+    ok = ok && gemm(M, D, D, e_dev, D, 0, L, D, 0, Et, D);                 // E~ = E_cat L
+    ok = ok && gemm(M, k, D, Et, D, 0, omega_dev, k, 0, Y, k);              // Y = E~ Omega
+    ok = ok && launch_orth(Y, k, M, k, stream) == hipSuccess;
+    for (int it = 0; it < q && ok; ++it) {
+        ok = ok && gemm(D, k, M, Et, D, 1, Y, k, 0, Z, k);                  // Z = orth(E~^T Q)
+        ok = ok && launch_orth(Z, k, D, k, stream) == hipSuccess;
+        ok = ok && gemm(M, k, D, Et, D, 0, Z, k, 0, Y, k);                  // Q = orth(E~ Z)
+        ok = ok && launch_orth(Y, k, M, k, stream) == hipSuccess;
+    }
+    ok = ok && gemm(k, D, M, Y, k, 1, Et, D, 0, Bs, D);                     // B_small = Q^T E~
+    ok = ok && gemm(k, k, D, Bs, D, 0, Bs, D, 1, G, k);                     // B_small B_small^T = U S^2 U^T
+    ok = ok && launch_jacobi(G, k, w, V, stream) == hipSuccess;
+    ok = ok && launch_sqrt(w, s_dev, r, stream) == hipSuccess;
+    ok = ok && gemm(M, r, k, Y, k, 0, V, k, 0, a_dev, r);                   // A = Q U_r S_r^{1/2}
+    ok = ok && launch_colscale(a_dev, r, M, r, w, 0, 0, stream) == hipSuccess;
+    ok = ok && gemm(r, D, k, V, k, 1, Bs, D, 0, Bw, D);                     // B_w = S_r^{-1/2} U_r^T B_small
+    ok = ok && launch_colscale(Bw, D, r, D, w, 1, 1, stream) == hipSuccess;
+    ok = ok && launch_lift(L, D, Bw, b_dev, r, stream) == hipSuccess;      // B = B_w L^{-1}
+    if (!ok) return GLOWQ_ERR_HIP;
+    int h = 0;
+    if (hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    return h ? GLOWQ_ERR_RANGE : GLOWQ_OK;
+}
+
 int glowq_restore_topk(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k,
                        double* scores_dev, int32_t* mask_dev, hipStream_t stream) {
     if (!sums_dev || !scores_dev || !mask_dev) return GLOWQ_ERR_INVALID_ARG;

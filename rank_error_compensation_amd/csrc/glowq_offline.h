@@ -44,6 +44,27 @@ typedef _Float16 h4x __attribute__((ext_vector_type(4)));
 // Most units one restore selection ranks (their scores sit in LDS).
 constexpr int kMaxScoreUnits = 4096;
 
+// Offline factor solve (fp64).
+constexpr int kSolveMaxK = 96;  // r + p columns of the range finder (LDS of the small steps)
+struct GemmArgs {                // C = alpha op(A) op(B) + beta C, row-major
+    int32_t M, N, K;
+    const double* A;
+    int32_t lda, ta;              // ta: op(A) = A^T (A stored K x M)
+    const double* B;
+    int32_t ldb, tb;              // tb: op(B) = B^T (B stored N x K)
+    double* C;
+    int32_t ldc;
+    double alpha, beta;
+};
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream);
+hipError_t launch_orth(double* X, int ld, int n, int k, hipStream_t stream);
+hipError_t launch_jacobi(const double* G, int k, double* w, double* V, hipStream_t stream);
+hipError_t launch_colscale(double* X, int ld, int n, int r, const double* w, int mode, int by_row,
+                           hipStream_t stream);
+hipError_t launch_sqrt(const double* w, double* s, int r, hipStream_t stream);
+hipError_t launch_lift(const double* L, int d, const double* Bw, double* B, int r, hipStream_t stream);
+
 }  // namespace glowq
 
 #endif  // GLOWQ_OFFLINE_H

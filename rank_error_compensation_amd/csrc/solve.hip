@@ -1,0 +1,386 @@
+// Offline factor solve of one input-sharing group on the GPU, in fp64 (GlowQ paper note, key designs
+// 1-3: stack the group's quantisation errors, whiten them by the input covariance, extract the
+// dominant right subspace with a randomized SVD (p oversampling columns, q power iterations, Halko,
+// Martinsson and Tropp), return balanced factors A = U_r S_r^{1/2}, B = S_r^{1/2} V_r^T lifted back
+// to the original variables).
+//
+// Whitening uses the Cholesky factor L of Sigma_x (Sigma_x = L L^T) as the square root and L^{-1} as
+// the lift: the lifted product A B does not depend on which square root is used.  The range finder
+// runs on the whitened stacked error E~ = E_cat L itself rather than on the QR-reduced core
+// M = R_e L: with E~ = Q_e M and the same test matrix, every step (the ranges, their orthonormal
+// bases, the small projected matrix and its SVD) is the same up to the left factor Q_e, which the
+// final A = Q U_b S^{1/2} carries directly -- so A and B are those of the QR-reduced solve, without
+// the extra thin QR (the whitened error, m x d fp64, fits in HBM).
+//
+// Kernels (all fp64):
+//   gemm_kernel        C = alpha op(A) op(B) + beta C, 64 x 64 tiles, 16-deep K steps through LDS
+//   chol_diag_kernel   one workgroup factors a 64 x 64 diagonal block in LDS (right-looking)
+//   chol_panel_kernel  rows below the block: x L_kk^T = a by forward substitution, a row per thread
+//   orth_kernel        one workgroup orthonormalises the k columns of an n x k matrix (classical
+//                      Gram-Schmidt applied twice per column; a column with no norm left becomes 0)
+//   jacobi_kernel      one workgroup: eigenvalues / eigenvectors of a symmetric k x k matrix in LDS
+//                      (cyclic Jacobi sweeps until the off-diagonal mass is negligible), sorted
+//                      descending
+//   lift_kernel        one workgroup per row b of B: solves b L = b_w by back substitution
+#include "glowq_offline.h"
+
+namespace glowq {
+
+// --------------------------------------------------------------------------- GEMM
+__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
+    __shared__ double As[16][65];
+    __shared__ double Bs[16][65];
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    double acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+    for (int k0 = 0; k0 < g.K; k0 += 16) {
+        // tile loads: 64 x 16 of op(A) and 16 x 64 of op(B), 4 elements per thread each
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // consecutive threads walk the contiguous index of each operand as stored
+            const int idx = threadIdx.x + 256 * e;  // 0 .. 1023
+            {
+                const int ii = g.ta ? (idx & 63) : (idx >> 4), kk = g.ta ? (idx >> 6) : (idx & 15);
+                const int i = i0 + ii, k = k0 + kk;
+                double va = 0.0;
+                if (i < g.M && k < g.K) va = g.ta ? g.A[(size_t)k * g.lda + i] : g.A[(size_t)i * g.lda + k];
+                As[kk][ii] = va;
+            }
+            {
+                const int jj = g.tb ? (idx >> 4) : (idx & 63), kk = g.tb ? (idx & 15) : (idx >> 6);
+                const int j = j0 + jj, k = k0 + kk;
+                double vb = 0.0;
+                if (j < g.N && k < g.K) vb = g.tb ? g.B[(size_t)j * g.ldb + k] : g.B[(size_t)k * g.ldb + j];
+                Bs[kk][jj] = vb;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            double a[4], b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = As[kk][ty + 16 * e];
+                b[e] = Bs[kk][tx + 16 * e];
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            const int i = i0 + ty + 16 * x, j = j0 + tx + 16 * y;
+            if (i < g.M && j < g.N) {
+                double* c = g.C + (size_t)i * g.ldc + j;
+                *c = g.alpha * acc[x][y] + (g.beta != 0.0 ? g.beta * *c : 0.0);
+            }
+        }
+}
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
+    if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    const dim3 grid((unsigned)ceil_div(g.N, 64), (unsigned)ceil_div(g.M, 64));
+    hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, stream, g);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------- Cholesky
+// Factor the nb x nb diagonal block at (n0, n0) of the lower triangle of S (row stride ld) in
+// place; a non-positive pivot sets *flag.
+__global__ __launch_bounds__(256) void chol_diag_kernel(double* S, int ld, int n0, int nb, int* flag) {
+    __shared__ double a[64][65];
+    if (n0 == 0 && threadIdx.x == 0) *flag = 0;  // the first block clears the flag before any pivot
+    for (int idx = threadIdx.x; idx < nb * nb; idx += 256) {
+        const int i = idx / nb, j = idx % nb;
+        a[i][j] = S[(size_t)(n0 + i) * ld + n0 + j];
+    }
+    __syncthreads();
+    for (int j = 0; j < nb; ++j) {
+        __shared__ double piv;
+        if (threadIdx.x == 0) {
+            const double v = a[j][j];
+            if (!(v > 0.0)) atomicOr(flag, 1);
+            piv = v > 0.0 ? sqrt(v) : 1.0;
+            a[j][j] = piv;
+        }
+        __syncthreads();
+        for (int i = j + 1 + threadIdx.x; i < nb; i += 256) a[i][j] /= piv;
+        __syncthreads();
+        // trailing update of the block's lower triangle
+        for (int idx = threadIdx.x; idx < (nb - j - 1) * (nb - j - 1); idx += 256) {
+            const int i = j + 1 + idx / (nb - j - 1), c = j + 1 + idx % (nb - j - 1);
+            if (c <= i) a[i][c] -= a[i][j] * a[c][j];
+        }
+        __syncthreads();
+    }
+    for (int idx = threadIdx.x; idx < nb * nb; idx += 256) {
+        const int i = idx / nb, j = idx % nb;
+        S[(size_t)(n0 + i) * ld + n0 + j] = j <= i ? a[i][j] : 0.0;
+    }
+}
+
+// Rows n0 + nb .. n - 1: L[i][n0 .. n0 + nb) = S[i][n0 .. n0 + nb) L_kk^{-T}.
+__global__ __launch_bounds__(64) void chol_panel_kernel(double* S, int ld, int n, int n0, int nb) {
+    __shared__ double lkk[64][65];
+    __shared__ double x[64][65];  // [thread][column]
+    for (int idx = threadIdx.x; idx < nb * nb; idx += 64) {
+        const int i = idx / nb, j = idx % nb;
+        lkk[i][j] = S[(size_t)(n0 + i) * ld + n0 + j];
+    }
+    __syncthreads();
+    const int row = n0 + nb + blockIdx.x * 64 + threadIdx.x;
+    if (row >= n) return;
+    double* srow = S + (size_t)row * ld + n0;
+    for (int j = 0; j < nb; ++j) {
+        double s = srow[j];
+        for (int l = 0; l < j; ++l) s -= x[threadIdx.x][l] * lkk[j][l];
+        const double v = s / lkk[j][j];
+        x[threadIdx.x][j] = v;
+        srow[j] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void zero_upper_kernel(double* S, int ld, int n) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)n * n) return;
+    const int i = (int)(idx / n), j = (int)(idx % n);
+    if (j > i) S[(size_t)i * ld + j] = 0.0;
+}
+
+// --------------------------------------------------------------------------- small dense steps
+__device__ __forceinline__ double block_sum(double v, double* red) {
+    // 1024 threads: wave sums, then the 16 wave results in order
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    double s = 0.0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += red[w];
+    return s;
+}
+
+// Orthonormalise the k columns of X (n x k, row stride ld) in place: column j loses its components
+// along columns 0 .. j-1 twice (classical Gram-Schmidt, repeated), then is normalised; a column whose
+// norm falls below tol times its norm before the projections is set to 0 (rank deficiency).
+__global__ __launch_bounds__(1024) void orth_kernel(double* X, int ld, int n, int k) {
+    __shared__ double red[16];
+    __shared__ double coef[kSolveMaxK];
+    for (int j = 0; j < k; ++j) {
+        double nn = 0.0;
+        for (int t = threadIdx.x; t < n; t += blockDim.x) nn += X[(size_t)t * ld + j] * X[(size_t)t * ld + j];
+        const double norm0 = sqrt(block_sum(nn, red));
+        for (int pass = 0; pass < 2; ++pass) {
+            for (int i = 0; i < j; ++i) {
+                double d = 0.0;
+                for (int t = threadIdx.x; t < n; t += blockDim.x) d += X[(size_t)t * ld + i] * X[(size_t)t * ld + j];
+                d = block_sum(d, red);
+                if (threadIdx.x == 0) coef[i] = d;
+            }
+            __syncthreads();
+            for (int t = threadIdx.x; t < n; t += blockDim.x) {
+                double v = X[(size_t)t * ld + j];
+                for (int i = 0; i < j; ++i) v -= coef[i] * X[(size_t)t * ld + i];
+                X[(size_t)t * ld + j] = v;
+            }
+            __syncthreads();
+        }
+        nn = 0.0;
+        for (int t = threadIdx.x; t < n; t += blockDim.x) nn += X[(size_t)t * ld + j] * X[(size_t)t * ld + j];
+        const double norm = sqrt(block_sum(nn, red));
+        const double scale = (norm > 1e-13 * norm0 && norm > 0.0) ? 1.0 / norm : 0.0;
+        for (int t = threadIdx.x; t < n; t += blockDim.x) X[(size_t)t * ld + j] *= scale;
+        __syncthreads();
+    }
+}
+
+// Symmetric k x k G (row-major) -> eigenvalues w (descending) and eigenvectors as the columns of
+// V (k x k, row-major).  Cyclic Jacobi: each rotation zeroes one off-diagonal pair; sweeps repeat
+// until the off-diagonal Frobenius mass is below 1e-30 of the total (or 40 sweeps).
+__global__ __launch_bounds__(256) void jacobi_kernel(const double* G, int k, double* w, double* V) {
+    __shared__ double a[kSolveMaxK][kSolveMaxK + 1];
+    __shared__ double v[kSolveMaxK][kSolveMaxK + 1];
+    __shared__ double cs[2];
+    __shared__ double red[4];
+    __shared__ int order[kSolveMaxK];
+    for (int idx = threadIdx.x; idx < k * k; idx += 256) {
+        const int i = idx / k, j = idx % k;
+        a[i][j] = G[idx];
+        v[i][j] = i == j ? 1.0 : 0.0;
+    }
+    __syncthreads();
+    for (int sweep = 0; sweep < 40; ++sweep) {
+        double off = 0.0, tot = 0.0;
+        for (int idx = threadIdx.x; idx < k * k; idx += 256) {
+            const int i = idx / k, j = idx % k;
+            const double x = a[i][j] * a[i][j];
+            tot += x;
+            if (i != j) off += x;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            off += __shfl_xor(off, o, 64);
+            tot += __shfl_xor(tot, o, 64);
+        }
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = off;
+        __syncthreads();
+        const double off_all = red[0] + red[1] + red[2] + red[3];
+        __syncthreads();
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tot;
+        __syncthreads();
+        const double tot_all = red[0] + red[1] + red[2] + red[3];
+        __syncthreads();
+        if (!(off_all > 1e-30 * tot_all)) break;
+        for (int p = 0; p < k - 1; ++p) {
+            for (int q = p + 1; q < k; ++q) {
+                if (threadIdx.x == 0) {
+                    const double apq = a[p][q];
+                    double c = 1.0, s = 0.0;
+                    if (apq != 0.0) {
+                        const double tau = (a[q][q] - a[p][p]) / (2.0 * apq);
+                        const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+                        c = 1.0 / sqrt(1.0 + t * t);
+                        s = t * c;
+                    }
+                    cs[0] = c;
+                    cs[1] = s;
+                }
+                __syncthreads();
+                const double c = cs[0], s = cs[1];
+                if (s != 0.0) {
+                    // A <- J^T A J with J the rotation in the (p, q) plane; V <- V J
+                    for (int i = threadIdx.x; i < k; i += 256) {
+                        const double aip = a[i][p], aiq = a[i][q];
+                        a[i][p] = c * aip - s * aiq;
+                        a[i][q] = s * aip + c * aiq;
+                        const double vip = v[i][p], viq = v[i][q];
+                        v[i][p] = c * vip - s * viq;
+                        v[i][q] = s * vip + c * viq;
+                    }
+                    __syncthreads();
+                    for (int j = threadIdx.x; j < k; j += 256) {
+                        const double apj = a[p][j], aqj = a[q][j];
+                        a[p][j] = c * apj - s * aqj;
+                        a[q][j] = s * apj + c * aqj;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+    // sort descending (selection by rank, ties to the lower index)
+    for (int i = threadIdx.x; i < k; i += 256) {
+        int rank = 0;
+        for (int j = 0; j < k; ++j) rank += (a[j][j] > a[i][i] || (a[j][j] == a[i][i] && j < i)) ? 1 : 0;
+        order[rank] = i;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < k * k; idx += 256) {
+        const int i = idx / k, c = idx % k;
+        V[idx] = v[i][order[c]];
+    }
+    for (int c = threadIdx.x; c < k; c += 256) w[c] = a[order[c]][order[c]];
+}
+
+// Scale by the eigenvalues w of the Gram (w = S^2): element (i, c) of X (n x r) times f(w[c])
+// (by_row = 0) or f(w[i]) (by_row = 1), f = S^{1/2} (mode 0) or 1 / S^{1/2} (mode 1); a
+// non-positive w gives 0.
+__global__ __launch_bounds__(256) void colscale_kernel(double* X, int ld, int n, int r, const double* w, int mode,
+                                                       int by_row) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)n * r) return;
+    const int i = (int)(idx / r), c = (int)(idx % r);
+    const double s2 = w[by_row ? i : c];
+    double f = 0.0;
+    if (s2 > 0.0) {
+        const double sh = sqrt(sqrt(s2));
+        f = mode == 0 ? sh : 1.0 / sh;
+    }
+    X[(size_t)i * ld + c] *= f;
+}
+
+__global__ __launch_bounds__(256) void sqrt_kernel(const double* w, double* s, int r) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c < r) s[c] = w[c] > 0.0 ? sqrt(w[c]) : 0.0;
+}
+
+// Workgroup b: row b of B solves B[b] L = Bw[b] (L lower triangular, d x d) by back substitution:
+// B[b][j] = (Bw[b][j] - sum_{l > j} B[b][l] L[l][j]) / L[j][j], j = d - 1 .. 0.
+__global__ __launch_bounds__(256) void lift_kernel(const double* L, int d, const double* Bw, double* B) {
+    __shared__ double red[4];
+    const int b = blockIdx.x;
+    const double* bw = Bw + (size_t)b * d;
+    double* bo = B + (size_t)b * d;
+    for (int j = d - 1; j >= 0; --j) {
+        double s = 0.0;
+        for (int l = j + 1 + threadIdx.x; l < d; l += 256) s += bo[l] * L[(size_t)l * d + j];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+        __syncthreads();
+        if (threadIdx.x == 0) bo[j] = (bw[j] - (((red[0] + red[1]) + red[2]) + red[3])) / L[(size_t)j * d + j];
+        __syncthreads();
+    }
+}
+
+// --------------------------------------------------------------------------- launchers
+hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream) {
+    for (int n0 = 0; n0 < d; n0 += 64) {
+        const int nb = min(64, d - n0);
+        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, stream, S, d, n0, nb, flag);
+        const int rest = d - n0 - nb;
+        if (rest > 0) {
+            hipLaunchKernelGGL(chol_panel_kernel, dim3((unsigned)ceil_div(rest, 64)), dim3(64), 0, stream, S, d, d,
+                               n0, nb);
+            GemmArgs g{};  // S22 -= L21 L21^T (the whole trailing square; only its lower half is used)
+            g.M = rest, g.N = rest, g.K = nb;
+            g.A = S + (size_t)(n0 + nb) * d + n0, g.lda = d, g.ta = 0;
+            g.B = S + (size_t)(n0 + nb) * d + n0, g.ldb = d, g.tb = 1;
+            g.C = S + (size_t)(n0 + nb) * d + n0 + nb, g.ldc = d;
+            g.alpha = -1.0, g.beta = 1.0;
+            const hipError_t e = launch_gemm(g, stream);
+            if (e != hipSuccess) return e;
+        }
+    }
+    hipLaunchKernelGGL(zero_upper_kernel, dim3((unsigned)ceil_div((int64_t)d * d, 256)), dim3(256), 0, stream, S, d, d);
+    return hipGetLastError();
+}
+
+hipError_t launch_orth(double* X, int ld, int n, int k, hipStream_t stream) {
+    hipLaunchKernelGGL(orth_kernel, dim3(1), dim3(1024), 0, stream, X, ld, n, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_jacobi(const double* G, int k, double* w, double* V, hipStream_t stream) {
+    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(256), 0, stream, G, k, w, V);
+    return hipGetLastError();
+}
+
+hipError_t launch_colscale(double* X, int ld, int n, int r, const double* w, int mode, int by_row,
+                           hipStream_t stream) {
+    hipLaunchKernelGGL(colscale_kernel, dim3((unsigned)ceil_div((int64_t)n * r, 256)), dim3(256), 0, stream, X, ld, n,
+                       r, w, mode, by_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_sqrt(const double* w, double* s, int r, hipStream_t stream) {
+    hipLaunchKernelGGL(sqrt_kernel, dim3((unsigned)ceil_div(r, 256)), dim3(256), 0, stream, w, s, r);
+    return hipGetLastError();
+}
+
+hipError_t launch_lift(const double* L, int d, const double* Bw, double* B, int r, hipStream_t stream) {
+    hipLaunchKernelGGL(lift_kernel, dim3((unsigned)r), dim3(256), 0, stream, L, d, Bw, B);
+    return hipGetLastError();
+}
+
+}  // namespace glowq

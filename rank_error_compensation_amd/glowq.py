@@ -71,6 +71,9 @@ EXPORTS = {
     "glowq_restore_topk": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "glowq_second_moment_workspace_bytes": (_sz, [_i64, _i64]),
     "glowq_second_moment": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "glowq_solve_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
+    "glowq_solve_factors": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
+                                           _vp]),
 }
 
 _lib = None
@@ -223,6 +226,23 @@ def second_moment(x: torch.Tensor, out: Optional[torch.Tensor] = None,
     check(lib().glowq_second_moment(_ptr(x), N, d, _ptr(out), _ptr(workspace), workspace.numel(),
                                     _stream(stream)), "glowq_second_moment")
     return out
+
+
+def solve_factors(e: torch.Tensor, sigma: torch.Tensor, omega: torch.Tensor, r: int, q: int = 0,
+                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """fp64 stacked errors e [m][d], Sigma_x [d][d], test matrix omega [d][k] -> (A [m][r],
+    B [r][d], S [r]) (glowq_solve_factors; synchronises the stream)."""
+    e, sigma, omega = e.contiguous(), sigma.contiguous(), omega.contiguous()
+    m, d = int(e.shape[0]), int(e.shape[1])
+    k = int(omega.shape[1])
+    A = torch.empty(m, r, dtype=torch.float64, device=e.device)
+    B = torch.empty(r, d, dtype=torch.float64, device=e.device)
+    S = torch.empty(r, dtype=torch.float64, device=e.device)
+    if workspace is None:
+        workspace = torch.empty(int(lib().glowq_solve_workspace_bytes(m, d, k, r)), dtype=torch.uint8, device=e.device)
+    check(lib().glowq_solve_factors(_ptr(e), m, d, _ptr(sigma), _ptr(omega), r, k, q, _ptr(A), _ptr(B), _ptr(S),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)), "glowq_solve_factors")
+    return A, B, S
 
 
 # --------------------------------------------------------------------------- forward

@@ -180,6 +180,24 @@ def test_second_moment_validates():
     assert L.glowq_second_moment(FAKE, 1 << 20, 4096, FAKE, FAKE, 1 << 40, None) == g.ERR_UNSUPPORTED
 
 
+def test_solve_validates():
+    L = g.lib()
+    assert L.glowq_solve_workspace_bytes(0, 128, 16, 8) == 0
+    assert L.glowq_solve_workspace_bytes(96, 128, 8, 16) == 0     # k < r
+    assert L.glowq_solve_workspace_bytes(96, 128, 97, 8) == 0     # k > 96
+    need = L.glowq_solve_workspace_bytes(96, 128, 16, 8)
+    assert need > 0 and need % 256 == 0
+    args = lambda **kw: [kw.get(n, v) for n, v in (("e", FAKE), ("m", 96), ("d", 128), ("s", FAKE), ("o", FAKE),
+                                                       ("r", 8), ("k", 16), ("q", 1), ("a", FAKE), ("b", FAKE),
+                                                       ("sv", FAKE), ("ws", FAKE), ("n", need), ("st", None))]
+    assert L.glowq_solve_factors(*args(e=None)) == g.ERR_INVALID_ARG
+    assert L.glowq_solve_factors(*args(k=4)) == g.ERR_SHAPE
+    assert L.glowq_solve_factors(*args(q=-1)) == g.ERR_SHAPE
+    assert L.glowq_solve_factors(*args(k=100)) == g.ERR_UNSUPPORTED
+    assert L.glowq_solve_factors(*args(a=FAKE + 8)) == g.ERR_ALIGN
+    assert L.glowq_solve_factors(*args(n=need - 1)) == g.ERR_WORKSPACE
+
+
 def test_path_validates_every_unit_first():
     L = g.lib()
     wq = (g.QWeightC * 1)(_w())
