@@ -410,7 +410,7 @@ int glowq_second_moment(const void* x_dev, int64_t N, int64_t d, float* sigma_de
 size_t glowq_solve_workspace_bytes(int64_t m, int64_t d, int32_t k, int32_t r) {
     if (m < 1 || d < 1 || r < 1 || k < r || k > kSolveMaxK || k > d || m > kMaxRows || d > kMaxMomentD) return 0;
     const size_t n = (size_t)d * d + (size_t)m * d + (size_t)m * k + (size_t)d * k + 2u * (size_t)k * k + (size_t)k +
-                     (size_t)k * d + (size_t)r * d + 2u;
+                     (size_t)k * d + (size_t)r * d + (size_t)(m > d ? m : d) * k + (size_t)k * k + 2u;
     return round256(n * sizeof(double));
 }
 
@@ -435,7 +435,9 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
     double* w = V + (size_t)k * k;
     double* Bs = w + k;
     double* Bw = Bs + (size_t)k * d;
-    int* flag = reinterpret_cast<int*>(Bw + (size_t)r * d);
+    double* T = Bw + (size_t)r * d;                 // orthonormalisation scratch
+    double* Ri = T + (size_t)(m > d ? m : d) * k;
+    int* flag = reinterpret_cast<int*>(Ri + (size_t)k * k);
     auto gemm = [&](int Mm, int Nn, int Kk, const double* A, int lda, int ta, const double* B, int ldb, int tb,
                     double* C, int ldc) {
         GemmArgs g{};
@@ -448,12 +450,12 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
     ok = ok && launch_cholesky(L, D, flag, stream) == hipSuccess;           // Sigma_x = L L^T
     ok = ok && gemm(M, D, D, e_dev, D, 0, L, D, 0, Et, D);                 // E~ = E_cat L
     ok = ok && gemm(M, k, D, Et, D, 0, omega_dev, k, 0, Y, k);              // Y = E~ Omega
-    ok = ok && launch_orth(Y, k, M, k, stream) == hipSuccess;
+    ok = ok && launch_orth(Y, M, k, T, G, Ri, stream) == hipSuccess;
     for (int it = 0; it < q && ok; ++it) {
         ok = ok && gemm(D, k, M, Et, D, 1, Y, k, 0, Z, k);                  // Z = orth(E~^T Q)
-        ok = ok && launch_orth(Z, k, D, k, stream) == hipSuccess;
+        ok = ok && launch_orth(Z, D, k, T, G, Ri, stream) == hipSuccess;
         ok = ok && gemm(M, k, D, Et, D, 0, Z, k, 0, Y, k);                  // Q = orth(E~ Z)
-        ok = ok && launch_orth(Y, k, M, k, stream) == hipSuccess;
+        ok = ok && launch_orth(Y, M, k, T, G, Ri, stream) == hipSuccess;
     }
     ok = ok && gemm(k, D, M, Y, k, 1, Et, D, 0, Bs, D);                     // B_small = Q^T E~
     ok = ok && gemm(k, k, D, Bs, D, 0, Bs, D, 1, G, k);                     // B_small B_small^T = U S^2 U^T

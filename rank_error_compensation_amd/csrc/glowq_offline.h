@@ -58,7 +58,7 @@ struct GemmArgs {                // C = alpha op(A) op(B) + beta C, row-major
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream);
-hipError_t launch_orth(double* X, int ld, int n, int k, hipStream_t stream);
+hipError_t launch_orth(double* X, int n, int k, double* T, double* G, double* Rinv, hipStream_t stream);
 hipError_t launch_jacobi(const double* G, int k, double* w, double* V, hipStream_t stream);
 hipError_t launch_colscale(double* X, int ld, int n, int r, const double* w, int mode, int by_row,
                            hipStream_t stream);

@@ -16,8 +16,9 @@
 //   gemm_kernel        C = alpha op(A) op(B) + beta C, 64 x 64 tiles, 16-deep K steps through LDS
 //   chol_diag_kernel   one workgroup factors a 64 x 64 diagonal block in LDS (right-looking)
 //   chol_panel_kernel  rows below the block: x L_kk^T = a by forward substitution, a row per thread
-//   orth_kernel        one workgroup orthonormalises the k columns of an n x k matrix (classical
-//                      Gram-Schmidt applied twice per column; a column with no norm left becomes 0)
+//   chol_inv_small_kernel  orthonormal bases by Cholesky-QR, twice: G = X^T X, one workgroup
+//                      factors G = R^T R (dropping columns already in the span) and inverts R,
+//                      X <- X R^{-1}
 //   jacobi_kernel      one workgroup: eigenvalues / eigenvectors of a symmetric k x k matrix in LDS
 //                      (cyclic Jacobi sweeps until the off-diagonal mass is negligible), sorted
 //                      descending
@@ -170,38 +171,66 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
     return s;
 }
 
-// Orthonormalise the k columns of X (n x k, row stride ld) in place: column j loses its components
-// along columns 0 .. j-1 twice (classical Gram-Schmidt, repeated), then is normalised; a column whose
-// norm falls below tol times its norm before the projections is set to 0 (rank deficiency).
-__global__ __launch_bounds__(1024) void orth_kernel(double* X, int ld, int n, int k) {
-    __shared__ double red[16];
-    __shared__ double coef[kSolveMaxK];
+// Cholesky factor with dropped columns and its inverse, for an orthonormal basis of the columns of
+// X from their Gram G = X^T X (k x k): G = R^T R (R upper triangular); a column whose remaining
+// pivot falls to 1e-24 of its diagonal entry (or is 0) lies in the span of the earlier ones and
+// is dropped (row and column of R zero, Rinv column zero), so X Rinv has orthonormal columns
+// where X has new directions and zero columns elsewhere.  One workgroup, R and Rinv in LDS.
+__global__ __launch_bounds__(256) void chol_inv_small_kernel(const double* G, int k, double* Rinv_out) {
+    __shared__ double R[kSolveMaxK][kSolveMaxK + 1];
+    __shared__ double Ri[kSolveMaxK][kSolveMaxK + 1];
+    __shared__ int live[kSolveMaxK];
+    __shared__ double piv;
+    for (int idx = threadIdx.x; idx < k * k; idx += 256) {
+        const int i = idx / k, j = idx % k;
+        R[i][j] = G[idx];
+        Ri[i][j] = 0.0;
+    }
+    __syncthreads();
+    // right-looking: row j of R from the updated trailing block
     for (int j = 0; j < k; ++j) {
-        double nn = 0.0;
-        for (int t = threadIdx.x; t < n; t += blockDim.x) nn += X[(size_t)t * ld + j] * X[(size_t)t * ld + j];
-        const double norm0 = sqrt(block_sum(nn, red));
-        for (int pass = 0; pass < 2; ++pass) {
-            for (int i = 0; i < j; ++i) {
-                double d = 0.0;
-                for (int t = threadIdx.x; t < n; t += blockDim.x) d += X[(size_t)t * ld + i] * X[(size_t)t * ld + j];
-                d = block_sum(d, red);
-                if (threadIdx.x == 0) coef[i] = d;
-            }
-            __syncthreads();
-            for (int t = threadIdx.x; t < n; t += blockDim.x) {
-                double v = X[(size_t)t * ld + j];
-                for (int i = 0; i < j; ++i) v -= coef[i] * X[(size_t)t * ld + i];
-                X[(size_t)t * ld + j] = v;
-            }
-            __syncthreads();
+        if (threadIdx.x == 0) {
+            const double v = R[j][j];
+            const double g0 = G[(size_t)j * k + j];
+            const bool ok = v > 1e-24 * g0 && v > 0.0;
+            live[j] = ok ? 1 : 0;
+            piv = ok ? sqrt(v) : 0.0;
         }
-        nn = 0.0;
-        for (int t = threadIdx.x; t < n; t += blockDim.x) nn += X[(size_t)t * ld + j] * X[(size_t)t * ld + j];
-        const double norm = sqrt(block_sum(nn, red));
-        const double scale = (norm > 1e-13 * norm0 && norm > 0.0) ? 1.0 / norm : 0.0;
-        for (int t = threadIdx.x; t < n; t += blockDim.x) X[(size_t)t * ld + j] *= scale;
+        __syncthreads();
+        const double p = piv;
+        for (int c = j + threadIdx.x; c < k; c += 256) R[j][c] = p > 0.0 ? R[j][c] / p : 0.0;
+        for (int i = 0; i < j; ++i) {
+            if (threadIdx.x == 0) R[j][i] = 0.0;
+        }
+        __syncthreads();
+        // trailing update R[a][c] -= R[j][a] R[j][c] for j < a <= c
+        for (int idx = threadIdx.x; idx < (k - j - 1) * (k - j - 1); idx += 256) {
+            const int a2 = j + 1 + idx / (k - j - 1), c = j + 1 + idx % (k - j - 1);
+            if (c >= a2) R[a2][c] -= R[j][a2] * R[j][c];
+        }
+        __syncthreads();
+        // keep the trailing block symmetric for the pivot reads (mirror the updated upper part)
+        for (int idx = threadIdx.x; idx < (k - j - 1) * (k - j - 1); idx += 256) {
+            const int a2 = j + 1 + idx / (k - j - 1), c = j + 1 + idx % (k - j - 1);
+            if (c < a2) R[a2][c] = R[c][a2];
+        }
         __syncthreads();
     }
+    // Rinv = R^{-1} on the live columns: column c solves R x = e_c by back substitution
+    for (int c = threadIdx.x; c < k; c += 256) {
+        if (!live[c]) continue;
+        for (int i = c; i >= 0; --i) {
+            if (!live[i]) {
+                Ri[i][c] = 0.0;
+                continue;
+            }
+            double s = i == c ? 1.0 : 0.0;
+            for (int l = i + 1; l <= c; ++l) s -= R[i][l] * Ri[l][c];
+            Ri[i][c] = s / R[i][i];
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < k * k; idx += 256) Rinv_out[idx] = Ri[idx / k][idx % k];
 }
 
 // Symmetric k x k G (row-major) -> eigenvalues w (descending) and eigenvectors as the columns of
@@ -356,9 +385,28 @@ hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_orth(double* X, int ld, int n, int k, hipStream_t stream) {
-    hipLaunchKernelGGL(orth_kernel, dim3(1), dim3(1024), 0, stream, X, ld, n, k);
-    return hipGetLastError();
+// Orthonormal basis of the columns of X (n x k, contiguous rows) in place, by two Cholesky-QR
+// passes (the second restores orthogonality lost to the conditioning of the first): G = X^T X,
+// Rinv from chol_inv_small_kernel, X <- X Rinv.  T (n x k) and G, Rinv (k x k) are scratch.
+hipError_t launch_orth(double* X, int n, int k, double* T, double* G, double* Rinv, hipStream_t stream) {
+    for (int pass = 0; pass < 2; ++pass) {
+        double* src = pass == 0 ? X : T;
+        double* dst = pass == 0 ? T : X;
+        GemmArgs g{};
+        g.M = k, g.N = k, g.K = n, g.A = src, g.lda = k, g.ta = 1, g.B = src, g.ldb = k, g.tb = 0;
+        g.C = G, g.ldc = k, g.alpha = 1.0, g.beta = 0.0;
+        hipError_t e = launch_gemm(g, stream);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(chol_inv_small_kernel, dim3(1), dim3(256), 0, stream, G, k, Rinv);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        GemmArgs h{};
+        h.M = n, h.N = k, h.K = k, h.A = src, h.lda = k, h.ta = 0, h.B = Rinv, h.ldb = k, h.tb = 0;
+        h.C = dst, h.ldc = k, h.alpha = 1.0, h.beta = 0.0;
+        e = launch_gemm(h, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_jacobi(const double* G, int k, double* w, double* V, hipStream_t stream) {
