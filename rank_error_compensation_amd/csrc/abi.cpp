@@ -241,7 +241,7 @@ const char* glowq_status_string(int status) {
         case GLOWQ_ERR_UNSUPPORTED: return "GLOWQ_ERR_UNSUPPORTED: configuration not supported";
         case GLOWQ_ERR_WORKSPACE: return "GLOWQ_ERR_WORKSPACE: workspace missing or too small";
         case GLOWQ_ERR_HIP: return "GLOWQ_ERR_HIP: HIP runtime or launch failure";
-        case GLOWQ_ERR_RANGE: return "GLOWQ_ERR_RANGE: zero point or scale out of range";
+        case GLOWQ_ERR_RANGE: return "GLOWQ_ERR_RANGE: value out of range (zero point, scale, or a matrix that is not positive definite)";
         default: return "GLOWQ_ERR_UNKNOWN";
     }
 }
@@ -448,7 +448,12 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
     bool ok = hipMemcpyAsync(L, sigma_dev, (size_t)d * d * sizeof(double), hipMemcpyDeviceToDevice, stream) ==
               hipSuccess;
     ok = ok && launch_cholesky(L, D, flag, stream) == hipSuccess;           // Sigma_x = L L^T
-    ok = ok && gemm(M, D, D, e_dev, D, 0, L, D, 0, Et, D);                 // E~ = E_cat L
+    {
+        GemmArgs g{};                                                       // E~ = E_cat L (L lower)
+        g.M = M, g.N = D, g.K = D, g.A = e_dev, g.lda = D, g.B = L, g.ldb = D, g.C = Et, g.ldc = D;
+        g.alpha = 1.0, g.beta = 0.0, g.b_lower = 1;
+        ok = ok && launch_gemm(g, stream) == hipSuccess;
+    }
     ok = ok && gemm(M, k, D, Et, D, 0, omega_dev, k, 0, Y, k);              // Y = E~ Omega
     ok = ok && launch_orth(Y, M, k, T, G, Ri, stream) == hipSuccess;
     for (int it = 0; it < q && ok; ++it) {

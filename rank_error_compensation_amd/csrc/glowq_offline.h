@@ -55,6 +55,8 @@ struct GemmArgs {                // C = alpha op(A) op(B) + beta C, row-major
     double* C;
     int32_t ldc;
     double alpha, beta;
+    int32_t b_lower;              // B lower triangular: K of column j starts at j
+    int32_t c_lower;              // only C's lower triangle is needed
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream);

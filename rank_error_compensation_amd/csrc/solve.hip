@@ -13,7 +13,7 @@
 // the extra thin QR (the whitened error, m x d fp64, fits in HBM).
 //
 // Kernels (all fp64):
-//   gemm_kernel        C = alpha op(A) op(B) + beta C, 64 x 64 tiles, 16-deep K steps through LDS
+//   gemm_kernel        C = alpha op(A) op(B) + beta C on the fp64 matrix cores, 128 x 128 tiles
 //   chol_diag_kernel   one workgroup factors a 64 x 64 diagonal block in LDS (right-looking)
 //   chol_panel_kernel  rows below the block: x L_kk^T = a by forward substitution, a row per thread
 //   chol_inv_small_kernel  orthonormal bases by Cholesky-QR, twice: G = X^T X, one workgroup
@@ -28,68 +28,100 @@
 namespace glowq {
 
 // --------------------------------------------------------------------------- GEMM
+// 128 x 128 tile per workgroup, four waves of 64 x 64, each 4 x 4 v_mfma_f64_16x16x4_f64 tiles
+// (A operand lane l: row l % 16, k l / 16; B operand lane l: k l / 16, column l % 16; result element
+// e of lane l: row l / 16 + 4 e, column l % 16 -- measured with an in-bounds probe).  K in steps of 16 through LDS, the next step's global
+// loads held in registers while the current one is multiplied.  b_lower: B is lower triangular, so
+// the K loop of a tile starts at its first column; c_lower: only tiles touching the lower triangle
+// of C are computed.
+typedef double d4 __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
-    __shared__ double As[16][65];
-    __shared__ double Bs[16][65];
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-    double acc[4][4];
+    __shared__ double As[16][128 + 2];
+    __shared__ double Bs[16][128 + 2];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int wi = wave >> 1, wj = wave & 1;
+    const int i0 = blockIdx.y * 128, j0 = blockIdx.x * 128;
+    if (g.c_lower && j0 > i0 + 127) return;
+    const int kbeg = g.b_lower ? (j0 / 16) * 16 : 0;
+    d4 acc[4][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-    for (int k0 = 0; k0 < g.K; k0 += 16) {
-        // tile loads: 64 x 16 of op(A) and 16 x 64 of op(B), 4 elements per thread each
+        for (int y = 0; y < 4; ++y) acc[x][y] = d4{0.0, 0.0, 0.0, 0.0};
+
+    double ra[8], rb[8];
+    auto load = [&](int k0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // consecutive threads walk the contiguous index of each operand as stored
-            const int idx = threadIdx.x + 256 * e;  // 0 .. 1023
+        for (int e = 0; e < 8; ++e) {
+            const int idx = threadIdx.x + 256 * e;  // 0 .. 2047; consecutive threads walk the
+                                                    // contiguous index of each operand as stored
             {
-                const int ii = g.ta ? (idx & 63) : (idx >> 4), kk = g.ta ? (idx >> 6) : (idx & 15);
+                const int ii = g.ta ? (idx & 127) : (idx >> 4), kk = g.ta ? (idx >> 7) : (idx & 15);
                 const int i = i0 + ii, k = k0 + kk;
-                double va = 0.0;
-                if (i < g.M && k < g.K) va = g.ta ? g.A[(size_t)k * g.lda + i] : g.A[(size_t)i * g.lda + k];
-                As[kk][ii] = va;
+                ra[e] = (i < g.M && k < g.K) ? (g.ta ? g.A[(size_t)k * g.lda + i] : g.A[(size_t)i * g.lda + k]) : 0.0;
             }
             {
-                const int jj = g.tb ? (idx >> 4) : (idx & 63), kk = g.tb ? (idx & 15) : (idx >> 6);
+                const int jj = g.tb ? (idx >> 4) : (idx & 127), kk = g.tb ? (idx & 15) : (idx >> 7);
                 const int j = j0 + jj, k = k0 + kk;
-                double vb = 0.0;
-                if (j < g.N && k < g.K) vb = g.tb ? g.B[(size_t)j * g.ldb + k] : g.B[(size_t)k * g.ldb + j];
-                Bs[kk][jj] = vb;
+                rb[e] = (j < g.N && k < g.K) ? (g.tb ? g.B[(size_t)j * g.ldb + k] : g.B[(size_t)k * g.ldb + j]) : 0.0;
             }
         }
-        __syncthreads();
+    };
+    auto store = [&]() {
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
+        for (int e = 0; e < 8; ++e) {
+            const int idx = threadIdx.x + 256 * e;
+            {
+                const int ii = g.ta ? (idx & 127) : (idx >> 4), kk = g.ta ? (idx >> 7) : (idx & 15);
+                As[kk][ii] = ra[e];
+            }
+            {
+                const int jj = g.tb ? (idx >> 4) : (idx & 127), kk = g.tb ? (idx & 15) : (idx >> 7);
+                Bs[kk][jj] = rb[e];
+            }
+        }
+    };
+    if (kbeg < g.K) load(kbeg);
+    for (int k0 = kbeg; k0 < g.K; k0 += 16) {
+        store();
+        __syncthreads();
+        if (k0 + 16 < g.K) load(k0 + 16);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kr = 4 * ks + (lane >> 4);
             double a[4], b[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                a[e] = As[kk][ty + 16 * e];
-                b[e] = Bs[kk][tx + 16 * e];
+            for (int x = 0; x < 4; ++x) {
+                a[x] = As[kr][64 * wi + 16 * x + (lane & 15)];
+                b[x] = Bs[kr][64 * wj + 16 * x + (lane & 15)];
             }
 #pragma unroll
             for (int x = 0; x < 4; ++x)
 #pragma unroll
-                for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+                for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
         }
         __syncthreads();
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const int i = i0 + ty + 16 * x, j = j0 + tx + 16 * y;
-            if (i < g.M && j < g.N) {
-                double* c = g.C + (size_t)i * g.ldc + j;
-                *c = g.alpha * acc[x][y] + (g.beta != 0.0 ? g.beta * *c : 0.0);
+        for (int y = 0; y < 4; ++y)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = i0 + 64 * wi + 16 * x + (lane >> 4) + 4 * e;
+                const int j = j0 + 64 * wj + 16 * y + (lane & 15);
+                if (i < g.M && j < g.N) {
+                    double* c = g.C + (size_t)i * g.ldc + j;
+                    *c = g.alpha * acc[x][y][e] + (g.beta != 0.0 ? g.beta * *c : 0.0);
+                }
             }
-        }
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    const dim3 grid((unsigned)ceil_div(g.N, 64), (unsigned)ceil_div(g.M, 64));
+    const dim3 grid((unsigned)ceil_div(g.N, 128), (unsigned)ceil_div(g.M, 128));
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, stream, g);
     return hipGetLastError();
 }
@@ -371,12 +403,12 @@ hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream) {
         if (rest > 0) {
             hipLaunchKernelGGL(chol_panel_kernel, dim3((unsigned)ceil_div(rest, 64)), dim3(64), 0, stream, S, d, d,
                                n0, nb);
-            GemmArgs g{};  // S22 -= L21 L21^T (the whole trailing square; only its lower half is used)
+            GemmArgs g{};  // S22 -= L21 L21^T (tiles touching the lower triangle; only it is used)
             g.M = rest, g.N = rest, g.K = nb;
             g.A = S + (size_t)(n0 + nb) * d + n0, g.lda = d, g.ta = 0;
             g.B = S + (size_t)(n0 + nb) * d + n0, g.ldb = d, g.tb = 1;
             g.C = S + (size_t)(n0 + nb) * d + n0 + nb, g.ldc = d;
-            g.alpha = -1.0, g.beta = 1.0;
+            g.alpha = -1.0, g.beta = 1.0, g.c_lower = 1;
             const hipError_t e = launch_gemm(g, stream);
             if (e != hipSuccess) return e;
         }
