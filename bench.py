@@ -312,6 +312,46 @@ def extra_restore_selection(g, reps=3, k=16):
     return out
 
 
+def extra_factor_solve(g, sigma32, reps=3, r=64, p=8, q=2):
+    """Offline factor solve of the LLaMA-2-7B QKV group (m = 3 x 4096 stacked error rows, d = 4096):
+    the quantisation errors of three generated fp16 weights, whitened by the calibration second
+    moment measured in extra_second_moment, randomized SVD with k = r + p and q power iterations."""
+    import torch
+    import workload as W
+    d = 4096
+    errs = []
+    for i in range(3):
+        keys = (0, 6, 0, i)
+        w = W.make_w(d, d, keys, W.outlier_columns(d, keys), "cuda")
+        qw = W.rtn_quantize(w)
+        w_hat = (qw.q.double() - qw.z.double().repeat_interleave(128, dim=1)) * qw.s.double().repeat_interleave(128, dim=1)
+        errs.append(w.double() - w_hat)
+    E = torch.cat(errs).contiguous()
+    m = int(E.shape[0])
+    k = r + p
+    sigma = sigma32.double().contiguous()
+    omega = torch.randn(d, k, generator=torch.Generator(device="cuda").manual_seed(0), device="cuda",
+                        dtype=torch.float64)
+    ws = torch.empty(int(g.lib().glowq_solve_workspace_bytes(m, d, k, r)), dtype=torch.uint8, device="cuda")
+    g.solve_factors(E, sigma, omega, r, q, workspace=ws)
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        A, B, S = g.solve_factors(E, sigma, omega, r, q, workspace=ws)  # synchronises
+        ts.append(time.perf_counter() - t0)
+    t = statistics.median(ts)
+    flops = (d ** 3 / 3 + m * d * d + 2 * m * d * k * (2 + 2 * q) + 2 * m * k * k * 2 * (1 + 2 * q)
+             + 2 * k * k * d + 2 * m * k * r + 2 * r * d * k + r * d * d)
+    out = {"workload": f"QKV group m = {m}, d = {d}, r = {r}, p = {p}, q = {q} (errors of generated LLaMA-2-7B-shaped "
+                       "weights, Sigma_x from the calibration second moment)",
+           "ms": round(t * 1e3, 2), "fp64_TFLOP_per_s": round(flops / t / 1e12, 2),
+           "frac_fp64_peak": round(flops / t / 1e12 / 78.6, 4),
+           "top_singular_value": float(S[0]), "r_th_singular_value": float(S[-1])}
+    del E, sigma, omega, ws, A, B
+    torch.cuda.empty_cache()
+    return out
+
+
 def extra_second_moment(g, reps=5):
     """Offline factor solve, first step: Sigma_x = X^T X / N over 64 calibration sequences of 2048
     tokens at d = 4096 (the LLaMA-2-7B attention input), activations resident in HBM."""
@@ -335,12 +375,13 @@ def extra_second_moment(g, reps=5):
         e1.synchronize()
         ts.append(e0.elapsed_time(e1) * 1e-3)
     t = statistics.median(ts)
+    sigma = out.clone()
     nb = -(-d // 256)                           # 256 x 256 lower-triangle tiles
     alg = N * d * (d + 1)                       # N d (d + 1) / 2 distinct products, 2 flops each
     executed = 2 * N * 256 * 256 * (nb * (nb + 1) // 2)
     del x, out, ws
     torch.cuda.empty_cache()
-    return {"workload": f"Sigma_x = X^T X / N, N = {seqs} x {L} calibration tokens, d = {d}",
+    return sigma, {"workload": f"Sigma_x = X^T X / N, N = {seqs} x {L} calibration tokens, d = {d}",
             "ms": round(t * 1e3, 3), "alg_TFLOP_per_s": round(alg / t / 1e12, 1),
             "executed_TFLOP_per_s": round(executed / t / 1e12, 1),
             "frac_mfma_f16_peak": round(executed / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
@@ -525,10 +566,13 @@ def main():
         e = extra["restore_selection_32L"]
         e["frac_hbm_measured_peak"] = round(e["GB_per_s"] / peaks["hbm_read_GB_per_s"], 4)
         log(f"[bench] restore selection: {e}")
-        extra["second_moment_calib"] = extra_second_moment(g)
+        sigma, extra["second_moment_calib"] = extra_second_moment(g)
         e = extra["second_moment_calib"]
         e["frac_mfma_measured_peak"] = round(e["executed_TFLOP_per_s"] / peaks["mfma_f16_TFLOP_per_s"], 4)
         log(f"[bench] second moment: {e}")
+        extra["factor_solve_qkv"] = extra_factor_solve(g, sigma)
+        del sigma
+        log(f"[bench] factor solve: {extra['factor_solve_qkv']}")
 
     cpu = None
     if not args.no_cpu_baseline:

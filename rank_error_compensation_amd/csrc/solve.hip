@@ -20,8 +20,8 @@
 //                      factors G = R^T R (dropping columns already in the span) and inverts R,
 //                      X <- X R^{-1}
 //   jacobi_kernel      one workgroup: eigenvalues / eigenvectors of a symmetric k x k matrix in LDS
-//                      (cyclic Jacobi sweeps until the off-diagonal mass is negligible), sorted
-//                      descending
+//                      (parallel cyclic Jacobi: disjoint rotations of a round-robin round applied
+//                      together), sorted descending
 //   lift_kernel        one workgroup per row b of B: solves b L = b_w by back substitution
 #include "glowq_offline.h"
 
@@ -266,19 +266,26 @@ __global__ __launch_bounds__(256) void chol_inv_small_kernel(const double* G, in
 }
 
 // Symmetric k x k G (row-major) -> eigenvalues w (descending) and eigenvectors as the columns of
-// V (k x k, row-major).  Cyclic Jacobi: each rotation zeroes one off-diagonal pair; sweeps repeat
-// until the off-diagonal Frobenius mass is below 1e-30 of the total (or 40 sweeps).
+// V (k x k, row-major).  Parallel cyclic Jacobi: each sweep is n - 1 rounds of a round-robin
+// tournament over the n = k (rounded up to even) indices; a round's n / 2 pairs are disjoint, so
+// their rotations (each zeroing one off-diagonal pair) are computed from the same matrix and
+// applied together.  Sweeps repeat until the off-diagonal Frobenius mass is below 1e-30 of the
+// total (or 40 sweeps).
 __global__ __launch_bounds__(256) void jacobi_kernel(const double* G, int k, double* w, double* V) {
     __shared__ double a[kSolveMaxK][kSolveMaxK + 1];
     __shared__ double v[kSolveMaxK][kSolveMaxK + 1];
-    __shared__ double cs[2];
+    __shared__ double cs[kSolveMaxK / 2][2];
+    __shared__ int pr[kSolveMaxK / 2][2];
+    __shared__ int pos[kSolveMaxK];
     __shared__ double red[4];
     __shared__ int order[kSolveMaxK];
+    const int n = k + (k & 1);  // index k (when k is odd) is a dummy: its pairs are skipped
     for (int idx = threadIdx.x; idx < k * k; idx += 256) {
         const int i = idx / k, j = idx % k;
         a[i][j] = G[idx];
         v[i][j] = i == j ? 1.0 : 0.0;
     }
+    for (int i = threadIdx.x; i < n; i += 256) pos[i] = i;
     __syncthreads();
     for (int sweep = 0; sweep < 40; ++sweep) {
         double off = 0.0, tot = 0.0;
@@ -302,41 +309,63 @@ __global__ __launch_bounds__(256) void jacobi_kernel(const double* G, int k, dou
         const double tot_all = red[0] + red[1] + red[2] + red[3];
         __syncthreads();
         if (!(off_all > 1e-30 * tot_all)) break;
-        for (int p = 0; p < k - 1; ++p) {
-            for (int q = p + 1; q < k; ++q) {
-                if (threadIdx.x == 0) {
+        for (int round = 0; round < n - 1; ++round) {
+            // pairs of this round and their rotations, all from the current matrix
+            for (int t = threadIdx.x; t < n / 2; t += 256) {
+                int p = pos[t], q = pos[n - 1 - t];
+                if (p > q) {
+                    const int x = p;
+                    p = q;
+                    q = x;
+                }
+                double c = 1.0, sn = 0.0;
+                if (q < k) {
                     const double apq = a[p][q];
-                    double c = 1.0, s = 0.0;
                     if (apq != 0.0) {
                         const double tau = (a[q][q] - a[p][p]) / (2.0 * apq);
-                        const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
-                        c = 1.0 / sqrt(1.0 + t * t);
-                        s = t * c;
-                    }
-                    cs[0] = c;
-                    cs[1] = s;
-                }
-                __syncthreads();
-                const double c = cs[0], s = cs[1];
-                if (s != 0.0) {
-                    // A <- J^T A J with J the rotation in the (p, q) plane; V <- V J
-                    for (int i = threadIdx.x; i < k; i += 256) {
-                        const double aip = a[i][p], aiq = a[i][q];
-                        a[i][p] = c * aip - s * aiq;
-                        a[i][q] = s * aip + c * aiq;
-                        const double vip = v[i][p], viq = v[i][q];
-                        v[i][p] = c * vip - s * viq;
-                        v[i][q] = s * vip + c * viq;
-                    }
-                    __syncthreads();
-                    for (int j = threadIdx.x; j < k; j += 256) {
-                        const double apj = a[p][j], aqj = a[q][j];
-                        a[p][j] = c * apj - s * aqj;
-                        a[q][j] = s * apj + c * aqj;
+                        const double tt = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+                        c = 1.0 / sqrt(1.0 + tt * tt);
+                        sn = tt * c;
                     }
                 }
-                __syncthreads();
+                pr[t][0] = p;
+                pr[t][1] = q;
+                cs[t][0] = c;
+                cs[t][1] = sn;
             }
+            __syncthreads();
+            // columns: A <- A J and V <- V J (pair t touches columns p, q only)
+            for (int idx = threadIdx.x; idx < (n / 2) * k; idx += 256) {
+                const int t = idx / k, i = idx % k;
+                const int p = pr[t][0], q = pr[t][1];
+                const double c = cs[t][0], sn = cs[t][1];
+                if (q >= k || sn == 0.0) continue;
+                const double aip = a[i][p], aiq = a[i][q];
+                a[i][p] = c * aip - sn * aiq;
+                a[i][q] = sn * aip + c * aiq;
+                const double vip = v[i][p], viq = v[i][q];
+                v[i][p] = c * vip - sn * viq;
+                v[i][q] = sn * vip + c * viq;
+            }
+            __syncthreads();
+            // rows: A <- J^T A (pair t touches rows p, q only)
+            for (int idx = threadIdx.x; idx < (n / 2) * k; idx += 256) {
+                const int t = idx / k, j = idx % k;
+                const int p = pr[t][0], q = pr[t][1];
+                const double c = cs[t][0], sn = cs[t][1];
+                if (q >= k || sn == 0.0) continue;
+                const double apj = a[p][j], aqj = a[q][j];
+                a[p][j] = c * apj - sn * aqj;
+                a[q][j] = sn * apj + c * aqj;
+            }
+            __syncthreads();
+            // next round: positions 1 .. n-1 rotate by one
+            if (threadIdx.x == 0) {
+                const int last = pos[n - 1];
+                for (int i = n - 1; i > 1; --i) pos[i] = pos[i - 1];
+                pos[1] = last;
+            }
+            __syncthreads();
         }
     }
     // sort descending (selection by rank, ties to the lower index)
