@@ -407,10 +407,16 @@ int glowq_second_moment(const void* x_dev, int64_t N, int64_t d, float* sigma_de
     return launch_moment(a, stream) == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
 }
 
+// split-K partial products of the solve's skinny GEMMs (a tall operand against k columns)
+static size_t solve_part_doubles(int64_t m, int64_t d, int32_t k) {
+    return (size_t)kSolveSplitMax * (size_t)(m > d ? m : d) * (size_t)k;
+}
+
 size_t glowq_solve_workspace_bytes(int64_t m, int64_t d, int32_t k, int32_t r) {
     if (m < 1 || d < 1 || r < 1 || k < r || k > kSolveMaxK || k > d || m > kMaxRows || d > kMaxMomentD) return 0;
     const size_t n = (size_t)d * d + (size_t)m * d + (size_t)m * k + (size_t)d * k + 2u * (size_t)k * k + (size_t)k +
-                     (size_t)k * d + (size_t)r * d + (size_t)(m > d ? m : d) * k + (size_t)k * k + 2u;
+                     (size_t)k * d + (size_t)r * d + (size_t)(m > d ? m : d) * k + (size_t)k * k + 2u +
+                     solve_part_doubles(m, d, k);
     return round256(n * sizeof(double));
 }
 
@@ -437,12 +443,14 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
     double* Bw = Bs + (size_t)k * d;
     double* T = Bw + (size_t)r * d;                 // orthonormalisation scratch
     double* Ri = T + (size_t)(m > d ? m : d) * k;
-    int* flag = reinterpret_cast<int*>(Ri + (size_t)k * k);
+    double* part = Ri + (size_t)k * k;             // split-K partial products
+    const int64_t part_cap = (int64_t)solve_part_doubles(m, d, k);
+    int* flag = reinterpret_cast<int*>(part + part_cap);
     auto gemm = [&](int Mm, int Nn, int Kk, const double* A, int lda, int ta, const double* B, int ldb, int tb,
                     double* C, int ldc) {
         GemmArgs g{};
         g.M = Mm, g.N = Nn, g.K = Kk, g.A = A, g.lda = lda, g.ta = ta, g.B = B, g.ldb = ldb, g.tb = tb;
-        g.C = C, g.ldc = ldc, g.alpha = 1.0, g.beta = 0.0;
+        g.C = C, g.ldc = ldc, g.alpha = 1.0, g.beta = 0.0, g.part = part, g.part_cap = part_cap;
         return launch_gemm(g, stream) == hipSuccess;
     };
     bool ok = hipMemcpyAsync(L, sigma_dev, (size_t)d * d * sizeof(double), hipMemcpyDeviceToDevice, stream) ==
@@ -455,12 +463,12 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
         ok = ok && launch_gemm(g, stream) == hipSuccess;
     }
     ok = ok && gemm(M, k, D, Et, D, 0, omega_dev, k, 0, Y, k);              // Y = E~ Omega
-    ok = ok && launch_orth(Y, M, k, T, G, Ri, stream) == hipSuccess;
+    ok = ok && launch_orth(Y, M, k, T, G, Ri, part, part_cap, stream) == hipSuccess;
     for (int it = 0; it < q && ok; ++it) {
         ok = ok && gemm(D, k, M, Et, D, 1, Y, k, 0, Z, k);                  // Z = orth(E~^T Q)
-        ok = ok && launch_orth(Z, D, k, T, G, Ri, stream) == hipSuccess;
+        ok = ok && launch_orth(Z, D, k, T, G, Ri, part, part_cap, stream) == hipSuccess;
         ok = ok && gemm(M, k, D, Et, D, 0, Z, k, 0, Y, k);                  // Q = orth(E~ Z)
-        ok = ok && launch_orth(Y, M, k, T, G, Ri, stream) == hipSuccess;
+        ok = ok && launch_orth(Y, M, k, T, G, Ri, part, part_cap, stream) == hipSuccess;
     }
     ok = ok && gemm(k, D, M, Y, k, 1, Et, D, 0, Bs, D);                     // B_small = Q^T E~
     ok = ok && gemm(k, k, D, Bs, D, 0, Bs, D, 1, G, k);                     // B_small B_small^T = U S^2 U^T

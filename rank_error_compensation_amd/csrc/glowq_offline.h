@@ -57,15 +57,25 @@ struct GemmArgs {                // C = alpha op(A) op(B) + beta C, row-major
     double alpha, beta;
     int32_t b_lower;              // B lower triangular: K of column j starts at j
     int32_t c_lower;              // only C's lower triangle is needed
+    double* part;                 // optional scratch for split-K partial products (or nullptr)
+    int64_t part_cap;             // its capacity in doubles
+    int32_t splits, kc;           // set by launch_gemm: K ranges of kc, one per grid z
 };
+// split-K: a launch with fewer tiles than kGemmWant splits K (ranges of at least kGemmMinK) over
+// the grid's z dimension when a partial buffer is given, and a second kernel adds the partial
+// products in range order (deterministic)
+constexpr int kGemmWant = 512;
+constexpr int kGemmMinK = 128;
+constexpr int kSolveSplitMax = 16;  // partial-product buffer of the solve: 16 max(m, d) k doubles
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
 hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream);
-hipError_t launch_orth(double* X, int n, int k, double* T, double* G, double* Rinv, hipStream_t stream);
+hipError_t launch_orth(double* X, int n, int k, double* T, double* G, double* Rinv, double* part, int64_t part_cap,
+                       hipStream_t stream);
 hipError_t launch_jacobi(const double* G, int k, double* w, double* V, hipStream_t stream);
 hipError_t launch_colscale(double* X, int ld, int n, int r, const double* w, int mode, int by_row,
                            hipStream_t stream);
 hipError_t launch_sqrt(const double* w, double* s, int r, hipStream_t stream);
-hipError_t launch_lift(const double* L, int d, const double* Bw, double* B, int r, hipStream_t stream);
+hipError_t launch_lift(const double* L, int d, double* Bw, double* B, int r, hipStream_t stream);
 
 }  // namespace glowq
 

@@ -22,7 +22,8 @@
 //   jacobi_kernel      one workgroup: eigenvalues / eigenvectors of a symmetric k x k matrix in LDS
 //                      (parallel cyclic Jacobi: disjoint rotations of a round-robin round applied
 //                      together), sorted descending
-//   lift_kernel        one workgroup per row b of B: solves b L = b_w by back substitution
+//   lift_diag_kernel   B L = B_w by column blocks from the last: each block's triangular solve in
+//                      registers, then a GEMM takes its share out of the earlier columns
 #include "glowq_offline.h"
 
 namespace glowq {
@@ -44,7 +45,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
     const int wi = wave >> 1, wj = wave & 1;
     const int i0 = blockIdx.y * 128, j0 = blockIdx.x * 128;
     if (g.c_lower && j0 > i0 + 127) return;
-    const int kbeg = g.b_lower ? (j0 / 16) * 16 : 0;
+    // K range: all of K, or range z of a split launch (never combined with b_lower / c_lower)
+    const bool split = g.splits > 1;
+    const int kbeg = split ? (int)blockIdx.z * g.kc : (g.b_lower ? (j0 / 16) * 16 : 0);
+    const int kend = split ? min(g.K, kbeg + g.kc) : g.K;
     d4 acc[4][4];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
@@ -60,12 +64,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
             {
                 const int ii = g.ta ? (idx & 127) : (idx >> 4), kk = g.ta ? (idx >> 7) : (idx & 15);
                 const int i = i0 + ii, k = k0 + kk;
-                ra[e] = (i < g.M && k < g.K) ? (g.ta ? g.A[(size_t)k * g.lda + i] : g.A[(size_t)i * g.lda + k]) : 0.0;
+                ra[e] = (i < g.M && k < kend) ? (g.ta ? g.A[(size_t)k * g.lda + i] : g.A[(size_t)i * g.lda + k]) : 0.0;
             }
             {
                 const int jj = g.tb ? (idx >> 4) : (idx & 127), kk = g.tb ? (idx & 15) : (idx >> 7);
                 const int j = j0 + jj, k = k0 + kk;
-                rb[e] = (j < g.N && k < g.K) ? (g.tb ? g.B[(size_t)j * g.ldb + k] : g.B[(size_t)k * g.ldb + j]) : 0.0;
+                rb[e] = (j < g.N && k < kend) ? (g.tb ? g.B[(size_t)j * g.ldb + k] : g.B[(size_t)k * g.ldb + j]) : 0.0;
             }
         }
     };
@@ -83,11 +87,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
             }
         }
     };
-    if (kbeg < g.K) load(kbeg);
-    for (int k0 = kbeg; k0 < g.K; k0 += 16) {
+    if (kbeg < kend) load(kbeg);
+    for (int k0 = kbeg; k0 < kend; k0 += 16) {
         store();
         __syncthreads();
-        if (k0 + 16 < g.K) load(k0 + 16);
+        if (k0 + 16 < kend) load(k0 + 16);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int kr = 4 * ks + (lane >> 4);
@@ -113,16 +117,50 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
                 const int i = i0 + 64 * wi + 16 * x + (lane >> 4) + 4 * e;
                 const int j = j0 + 64 * wj + 16 * y + (lane & 15);
                 if (i < g.M && j < g.N) {
-                    double* c = g.C + (size_t)i * g.ldc + j;
-                    *c = g.alpha * acc[x][y][e] + (g.beta != 0.0 ? g.beta * *c : 0.0);
+                    if (split) {
+                        g.part[((size_t)blockIdx.z * g.M + i) * g.N + j] = acc[x][y][e];
+                    } else {
+                        double* c = g.C + (size_t)i * g.ldc + j;
+                        *c = g.alpha * acc[x][y][e] + (g.beta != 0.0 ? g.beta * *c : 0.0);
+                    }
                 }
             }
 }
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
-    if (g.M <= 0 || g.N <= 0) return hipSuccess;
-    const dim3 grid((unsigned)ceil_div(g.N, 128), (unsigned)ceil_div(g.M, 128));
+// C = alpha (sum of the split partial products, in range order) + beta C
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const GemmArgs g) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t mn = (size_t)g.M * g.N;
+    if (idx >= mn) return;
+    double s = 0.0;
+    for (int z = 0; z < g.splits; ++z) s += g.part[(size_t)z * mn + idx];
+    const int i = (int)(idx / g.N), j = (int)(idx % g.N);
+    double* c = g.C + (size_t)i * g.ldc + j;
+    *c = g.alpha * s + (g.beta != 0.0 ? g.beta * *c : 0.0);
+}
+
+hipError_t launch_gemm(const GemmArgs& g0, hipStream_t stream) {
+    if (g0.M <= 0 || g0.N <= 0) return hipSuccess;
+    GemmArgs g = g0;
+    const int64_t tiles = ceil_div(g.N, 128) * ceil_div(g.M, 128);
+    const int64_t mn = (int64_t)g.M * g.N;
+    int64_t s = 1;
+    if (g.part != nullptr && !g.b_lower && !g.c_lower && tiles < kGemmWant) {
+        s = ceil_div(kGemmWant, tiles);
+        s = std::min<int64_t>(s, g.K / kGemmMinK);
+        s = std::min<int64_t>(s, g.part_cap / mn);
+        s = std::max<int64_t>(s, 1);
+    }
+    // K ranges of a multiple of 16 (the kernel's step), and no empty range
+    const int64_t kc = g.K > 0 ? ceil_div(ceil_div(g.K, s), 16) * 16 : 16;
+    s = g.K > 0 ? ceil_div(g.K, kc) : 1;
+    g.splits = (int32_t)s;
+    g.kc = (int32_t)kc;
+    const dim3 grid((unsigned)ceil_div(g.N, 128), (unsigned)ceil_div(g.M, 128), (unsigned)s);
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, stream, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || s == 1) return e;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)ceil_div(mn, 256)), dim3(256), 0, stream, g);
     return hipGetLastError();
 }
 
@@ -161,25 +199,35 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* S, int ld, int n
     }
 }
 
-// Rows n0 + nb .. n - 1: L[i][n0 .. n0 + nb) = S[i][n0 .. n0 + nb) L_kk^{-T}.
-__global__ __launch_bounds__(64) void chol_panel_kernel(double* S, int ld, int n, int n0, int nb) {
-    __shared__ double lkk[64][65];
-    __shared__ double x[64][65];  // [thread][column]
-    for (int idx = threadIdx.x; idx < nb * nb; idx += 64) {
-        const int i = idx / nb, j = idx % nb;
-        lkk[i][j] = S[(size_t)(n0 + i) * ld + n0 + j];
+// Rows n0 + nb .. n - 1: L[i][n0 .. n0 + nb) = S[i][n0 .. n0 + nb) L_kk^{-T}, i.e. x L_kk^T = s
+// for each such row s: x_l = s_l / L_ll (times the reciprocal), then s_j -= x_l L_jl for j > l.  A row per thread, kept
+// in registers; L_kk is held transposed in LDS (lt[l][j] = L_jl, so that each step reads a
+// contiguous run), every element a broadcast read.
+__global__ __launch_bounds__(128) void chol_panel_kernel(double* S, int ld, int n, int n0) {
+    constexpr int nb = 64;  // only a full block has rows below it
+    __shared__ double lt[64][64];
+    __shared__ double rd[64];  // 1 / L_ll
+    for (int idx = threadIdx.x; idx < 64 * 64; idx += 128) {
+        const int i = idx >> 6, j = idx & 63;  // L element (i, j) -> lt[j][i]
+        lt[j][i] = j <= i ? S[(size_t)(n0 + i) * ld + n0 + j] : 0.0;
     }
     __syncthreads();
-    const int row = n0 + nb + blockIdx.x * 64 + threadIdx.x;
+    if (threadIdx.x < 64) rd[threadIdx.x] = 1.0 / lt[threadIdx.x][threadIdx.x];
+    __syncthreads();
+    const int row = n0 + nb + blockIdx.x * 128 + threadIdx.x;
     if (row >= n) return;
     double* srow = S + (size_t)row * ld + n0;
-    for (int j = 0; j < nb; ++j) {
-        double s = srow[j];
-        for (int l = 0; l < j; ++l) s -= x[threadIdx.x][l] * lkk[j][l];
-        const double v = s / lkk[j][j];
-        x[threadIdx.x][j] = v;
-        srow[j] = v;
+    double x[64];
+#pragma unroll
+    for (int j = 0; j < 64; ++j) x[j] = srow[j];
+#pragma unroll
+    for (int l = 0; l < 64; ++l) {
+        x[l] *= rd[l];
+#pragma unroll
+        for (int j = l + 1; j < 64; ++j) x[j] -= x[l] * lt[l][j];
     }
+#pragma unroll
+    for (int j = 0; j < 64; ++j) srow[j] = x[j];
 }
 
 __global__ __launch_bounds__(256) void zero_upper_kernel(double* S, int ld, int n) {
@@ -404,23 +452,37 @@ __global__ __launch_bounds__(256) void sqrt_kernel(const double* w, double* s, i
     if (c < r) s[c] = w[c] > 0.0 ? sqrt(w[c]) : 0.0;
 }
 
-// Workgroup b: row b of B solves B[b] L = Bw[b] (L lower triangular, d x d) by back substitution:
-// B[b][j] = (Bw[b][j] - sum_{l > j} B[b][l] L[l][j]) / L[j][j], j = d - 1 .. 0.
-__global__ __launch_bounds__(256) void lift_kernel(const double* L, int d, const double* Bw, double* B) {
-    __shared__ double red[4];
-    const int b = blockIdx.x;
-    const double* bw = Bw + (size_t)b * d;
-    double* bo = B + (size_t)b * d;
-    for (int j = d - 1; j >= 0; --j) {
-        double s = 0.0;
-        for (int l = j + 1 + threadIdx.x; l < d; l += 256) s += bo[l] * L[(size_t)l * d + j];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
-        __syncthreads();
-        if (threadIdx.x == 0) bo[j] = (bw[j] - (((red[0] + red[1]) + red[2]) + red[3])) / L[(size_t)j * d + j];
-        __syncthreads();
+// One column block of the lift B L = Bw (L lower triangular, d x d): thread t < r solves
+// x L_JJ = b for row t, where L_JJ is the diagonal block at (c0, c0) (padded to 64 x 64 with the
+// identity) and b is row t of Bw on the block's columns, already stripped of the contributions of
+// the later blocks.  From the last column: x_j = b_j / L_jj, then b_i -= x_j L_ji for i < j; the
+// row stays in registers and every L element is a broadcast LDS read.
+__global__ __launch_bounds__(128) void lift_diag_kernel(const double* L, int d, int c0, const double* Bw, double* B,
+                                                        int r) {
+    __shared__ double l[64][64];
+    const int nb = min(64, d - c0);
+    for (int idx = threadIdx.x; idx < 64 * 64; idx += 128) {
+        const int i = idx >> 6, j = idx & 63;
+        l[i][j] = (i < nb && j < nb) ? (j <= i ? L[(size_t)(c0 + i) * d + c0 + j] : 0.0) : (i == j ? 1.0 : 0.0);
     }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t >= r) return;
+    double x[64];
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+        const double v = Bw[(size_t)t * d + c0 + min(j, nb - 1)];  // unconditional load
+        x[j] = j < nb ? v : 0.0;
+    }
+#pragma unroll
+    for (int j = 63; j >= 0; --j) {
+        x[j] /= l[j][j];
+#pragma unroll
+        for (int i = 0; i < j; ++i) x[i] -= x[j] * l[j][i];
+    }
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+        if (j < nb) B[(size_t)t * d + c0 + j] = x[j];
 }
 
 // --------------------------------------------------------------------------- launchers
@@ -430,8 +492,8 @@ hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream) {
         hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, stream, S, d, n0, nb, flag);
         const int rest = d - n0 - nb;
         if (rest > 0) {
-            hipLaunchKernelGGL(chol_panel_kernel, dim3((unsigned)ceil_div(rest, 64)), dim3(64), 0, stream, S, d, d,
-                               n0, nb);
+            hipLaunchKernelGGL(chol_panel_kernel, dim3((unsigned)ceil_div(rest, 128)), dim3(128), 0, stream, S, d, d,
+                               n0);  // rest > 0: the block is a full 64 wide
             GemmArgs g{};  // S22 -= L21 L21^T (tiles touching the lower triangle; only it is used)
             g.M = rest, g.N = rest, g.K = nb;
             g.A = S + (size_t)(n0 + nb) * d + n0, g.lda = d, g.ta = 0;
@@ -449,13 +511,14 @@ hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream) {
 // Orthonormal basis of the columns of X (n x k, contiguous rows) in place, by two Cholesky-QR
 // passes (the second restores orthogonality lost to the conditioning of the first): G = X^T X,
 // Rinv from chol_inv_small_kernel, X <- X Rinv.  T (n x k) and G, Rinv (k x k) are scratch.
-hipError_t launch_orth(double* X, int n, int k, double* T, double* G, double* Rinv, hipStream_t stream) {
+hipError_t launch_orth(double* X, int n, int k, double* T, double* G, double* Rinv, double* part, int64_t part_cap,
+                       hipStream_t stream) {
     for (int pass = 0; pass < 2; ++pass) {
         double* src = pass == 0 ? X : T;
         double* dst = pass == 0 ? T : X;
         GemmArgs g{};
         g.M = k, g.N = k, g.K = n, g.A = src, g.lda = k, g.ta = 1, g.B = src, g.ldb = k, g.tb = 0;
-        g.C = G, g.ldc = k, g.alpha = 1.0, g.beta = 0.0;
+        g.C = G, g.ldc = k, g.alpha = 1.0, g.beta = 0.0, g.part = part, g.part_cap = part_cap;
         hipError_t e = launch_gemm(g, stream);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(chol_inv_small_kernel, dim3(1), dim3(256), 0, stream, G, k, Rinv);
@@ -487,9 +550,26 @@ hipError_t launch_sqrt(const double* w, double* s, int r, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_lift(const double* L, int d, const double* Bw, double* B, int r, hipStream_t stream) {
-    hipLaunchKernelGGL(lift_kernel, dim3((unsigned)r), dim3(256), 0, stream, L, d, Bw, B);
-    return hipGetLastError();
+// B = Bw L^{-1}, i.e. B L = Bw, by column blocks of 64 from the last: the block's columns of B
+// from its diagonal block (lift_diag_kernel), then the columns before it drop the block's share,
+// Bw[:, 0:c0] -= B[:, J] L[J, 0:c0] (a GEMM on the matrix cores).  Bw is overwritten.
+hipError_t launch_lift(const double* L, int d, double* Bw, double* B, int r, hipStream_t stream) {
+    if (r > 128) return hipErrorInvalidValue;
+    for (int c0 = (int)((d - 1) / 64) * 64; c0 >= 0; c0 -= 64) {
+        const int nb = min(64, d - c0);
+        hipLaunchKernelGGL(lift_diag_kernel, dim3(1), dim3(128), 0, stream, L, d, c0, Bw, B, r);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (c0 == 0) break;
+        GemmArgs g{};
+        g.M = r, g.N = c0, g.K = nb;
+        g.A = B + c0, g.lda = d, g.ta = 0;
+        g.B = L + (size_t)c0 * d, g.ldb = d, g.tb = 0;
+        g.C = Bw, g.ldc = d, g.alpha = -1.0, g.beta = 1.0;
+        e = launch_gemm(g, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace glowq

@@ -64,7 +64,9 @@ def test_exact_rank_error_is_reproduced(m, d, r0, r, p, q):
     assert rel(A @ B, P_ref) <= 1e-9
 
 
-@pytest.mark.parametrize("m,d,r,p,q", [(200, 256, 16, 8, 2), (96, 128, 8, 24, 1), (160, 192, 32, 32, 3)])
+# the last shape has GEMMs with K split over up to 16 ranges and ten column blocks in the lift
+@pytest.mark.parametrize("m,d,r,p,q", [(200, 256, 16, 8, 2), (96, 128, 8, 24, 1), (160, 192, 32, 32, 3),
+                                       (2048, 640, 16, 8, 1)])
 def test_matches_oracle_with_gap(m, d, r, p, q):
     g = glowq()
     rng = np.random.default_rng(7 * m + d)
