@@ -43,7 +43,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int wi = wave >> 1, wj = wave & 1;
-    const int i0 = blockIdx.y * 128, j0 = blockIdx.x * 128;
+    // tile of this workgroup: consecutive workgroup ids go to different XCDs, so the linear id is
+    // remapped to give each XCD a contiguous range of tiles (row-major over the tile grid): the
+    // workgroups resident on one XCD share A's row panel in its L2
+    int ty, tx;
+    {
+        const int n = (int)(gridDim.x * gridDim.y), b = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+        const int xcd = b & 7, local = b >> 3, per = n >> 3, rem = n & 7;
+        const int L = xcd * per + (xcd < rem ? xcd : rem) + local;
+        ty = L / (int)gridDim.x;
+        tx = L - ty * (int)gridDim.x;
+    }
+    const int i0 = ty * 128, j0 = tx * 128;
     if (g.c_lower && j0 > i0 + 127) return;
     // K range: all of K, or range z of a split launch (never combined with b_lower / c_lower)
     const bool split = g.splits > 1;
