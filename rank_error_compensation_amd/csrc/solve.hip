@@ -14,7 +14,8 @@
 //
 // Kernels (all fp64):
 //   gemm_kernel        C = alpha op(A) op(B) + beta C on the fp64 matrix cores, 128 x 128 tiles
-//   chol_diag_kernel   one workgroup factors a 64 x 64 diagonal block in LDS (right-looking)
+//   chol_diag_kernel   one workgroup factors a 64 x 64 diagonal block in LDS (right-looking, one
+//                      barrier per column)
 //   chol_panel_kernel  rows below the block: x L_kk^T = a by forward substitution, a row per thread
 //   chol_inv_small_kernel  orthonormal bases by Cholesky-QR, twice: G = X^T X, one workgroup
 //                      factors G = R^T R (dropping columns already in the span) and inverts R,
@@ -186,24 +187,28 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* S, int ld, int n
         a[i][j] = S[(size_t)(n0 + i) * ld + n0 + j];
     }
     __syncthreads();
+    // thread t updates column c = t % 64 on rows t / 64 + 4 q.  Step j (one barrier): with the
+    // pivot v = a[j][j], the trailing lower triangle loses a[i][j] a[c][j] / v (j < c <= i), which
+    // only reads column j; then column j itself is finished (L_jj = sqrt v, L_ij = a[i][j] / L_jj)
+    // while the next step reads only columns past j.
+    const int c = threadIdx.x & 63, i0 = threadIdx.x >> 6;
     for (int j = 0; j < nb; ++j) {
-        __shared__ double piv;
+        const double v = a[j][j];
+        const bool ok = v > 0.0;
+        const double inv = ok ? 1.0 / v : 1.0;
+        if (c > j && c < nb) {
+            const double acj = a[c][j] * inv;
+            for (int i = c + ((i0 - c) & 3); i < nb; i += 4) a[i][c] -= a[i][j] * acj;  // rows i >= c
+        }
+        __syncthreads();
+        const double piv = ok ? sqrt(v) : 1.0;
         if (threadIdx.x == 0) {
-            const double v = a[j][j];
-            if (!(v > 0.0)) atomicOr(flag, 1);
-            piv = v > 0.0 ? sqrt(v) : 1.0;
+            if (!ok) atomicOr(flag, 1);
             a[j][j] = piv;
         }
-        __syncthreads();
-        for (int i = j + 1 + threadIdx.x; i < nb; i += 256) a[i][j] /= piv;
-        __syncthreads();
-        // trailing update of the block's lower triangle
-        for (int idx = threadIdx.x; idx < (nb - j - 1) * (nb - j - 1); idx += 256) {
-            const int i = j + 1 + idx / (nb - j - 1), c = j + 1 + idx % (nb - j - 1);
-            if (c <= i) a[i][c] -= a[i][j] * a[c][j];
-        }
-        __syncthreads();
+        for (int i = j + 1 + (int)threadIdx.x; i < nb; i += 256) a[i][j] /= piv;
     }
+    __syncthreads();
     for (int idx = threadIdx.x; idx < nb * nb; idx += 256) {
         const int i = idx / nb, j = idx % nb;
         S[(size_t)(n0 + i) * ld + n0 + j] = j <= i ? a[i][j] : 0.0;
@@ -271,57 +276,53 @@ __global__ __launch_bounds__(256) void chol_inv_small_kernel(const double* G, in
     __shared__ double R[kSolveMaxK][kSolveMaxK + 1];
     __shared__ double Ri[kSolveMaxK][kSolveMaxK + 1];
     __shared__ int live[kSolveMaxK];
-    __shared__ double piv;
     for (int idx = threadIdx.x; idx < k * k; idx += 256) {
         const int i = idx / k, j = idx % k;
         R[i][j] = G[idx];
-        Ri[i][j] = 0.0;
+        Ri[i][j] = i == j ? 1.0 : 0.0;
     }
     __syncthreads();
-    // right-looking: row j of R from the updated trailing block
+    // thread t works on column c = t % 128 (c < k), rows t / 128 + 2 q.
+    const int c = threadIdx.x & 127, a0 = threadIdx.x >> 7;
+    // Right-looking, one barrier per step: with the pivot v = R[j][j] of a live column j, the
+    // trailing upper triangle loses R[j][a] R[j][c] / v (j < a <= c), which only reads row j; then
+    // row j itself is finished (R_jj = sqrt v, R_jc = R[j][c] / R_jj; a dropped column's row is
+    // zero) while the next step reads only rows past j.
     for (int j = 0; j < k; ++j) {
-        if (threadIdx.x == 0) {
-            const double v = R[j][j];
-            const double g0 = G[(size_t)j * k + j];
-            const bool ok = v > 1e-24 * g0 && v > 0.0;
-            live[j] = ok ? 1 : 0;
-            piv = ok ? sqrt(v) : 0.0;
+        const double v = R[j][j];
+        const bool ok = v > 1e-24 * G[(size_t)j * k + j] && v > 0.0;
+        if (ok && c > j && c < k) {
+            const double rjc = R[j][c] / v;
+            for (int a = j + 1 + ((j + 1 - a0) & 1); a <= c; a += 2) R[a][c] -= R[j][a] * rjc;  // j < a <= c
         }
         __syncthreads();
-        const double p = piv;
-        for (int c = j + threadIdx.x; c < k; c += 256) R[j][c] = p > 0.0 ? R[j][c] / p : 0.0;
-        for (int i = 0; i < j; ++i) {
-            if (threadIdx.x == 0) R[j][i] = 0.0;
+        if (threadIdx.x == 0) live[j] = ok ? 1 : 0;
+        const double p = ok ? sqrt(v) : 0.0;
+        for (int cc = (int)threadIdx.x; cc < k; cc += 256) {
+            if (cc < j) R[j][cc] = 0.0;
+            else if (cc > j) R[j][cc] = ok ? R[j][cc] / p : 0.0;
         }
-        __syncthreads();
-        // trailing update R[a][c] -= R[j][a] R[j][c] for j < a <= c
-        for (int idx = threadIdx.x; idx < (k - j - 1) * (k - j - 1); idx += 256) {
-            const int a2 = j + 1 + idx / (k - j - 1), c = j + 1 + idx % (k - j - 1);
-            if (c >= a2) R[a2][c] -= R[j][a2] * R[j][c];
-        }
-        __syncthreads();
-        // keep the trailing block symmetric for the pivot reads (mirror the updated upper part)
-        for (int idx = threadIdx.x; idx < (k - j - 1) * (k - j - 1); idx += 256) {
-            const int a2 = j + 1 + idx / (k - j - 1), c = j + 1 + idx % (k - j - 1);
-            if (c < a2) R[a2][c] = R[c][a2];
-        }
-        __syncthreads();
-    }
-    // Rinv = R^{-1} on the live columns: column c solves R x = e_c by back substitution
-    for (int c = threadIdx.x; c < k; c += 256) {
-        if (!live[c]) continue;
-        for (int i = c; i >= 0; --i) {
-            if (!live[i]) {
-                Ri[i][c] = 0.0;
-                continue;
-            }
-            double s = i == c ? 1.0 : 0.0;
-            for (int l = i + 1; l <= c; ++l) s -= R[i][l] * Ri[l][c];
-            Ri[i][c] = s / R[i][i];
-        }
+        if (threadIdx.x == 0) R[j][j] = p;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < k * k; idx += 256) Rinv_out[idx] = Ri[idx / k][idx % k];
+    // Rinv = R^{-1} on the live columns by back substitution for all columns at once: for i from
+    // the last row, row i of Rinv is divided by R_ii (zero for a dropped i), then every row l < i
+    // loses R[l][i] times it.  Dropped columns of Rinv are zero.
+    for (int i = k - 1; i >= 0; --i) {
+        const bool li = live[i] != 0;
+        const double rii = R[i][i];
+        if (a0 == 0 && c < k) Ri[i][c] = li ? Ri[i][c] / rii : 0.0;
+        __syncthreads();
+        if (li && c < k) {
+            const double x = Ri[i][c];
+            for (int l = a0; l < i; l += 2) Ri[l][c] -= R[l][i] * x;
+        }
+        __syncthreads();
+    }
+    for (int idx = threadIdx.x; idx < k * k; idx += 256) {
+        const int i = idx / k, cc = idx % k;
+        Rinv_out[idx] = live[cc] ? Ri[i][cc] : 0.0;
+    }
 }
 
 // Symmetric k x k G (row-major) -> eigenvalues w (descending) and eigenvectors as the columns of
