@@ -239,7 +239,8 @@ size_t glowq_solve_workspace_bytes(int64_t m, int64_t d, int32_t k, int32_t r);
  *   omega_dev : fp64 [d][k] test matrix (k = r + p oversampled columns, r <= k <= min(96, d))
  *   r, q      : rank, power iterations (0 <= q <= 16)
  *   a_dev     : fp64 [m][r] output A = U_r S_r^{1/2} (rows of module i at its offset in E_cat)
- *   b_dev     : fp64 [r][d] output B = S_r^{1/2} V_r^T L^{-1}
+ *   b_dev     : fp64 [r][d] output B = S_r^{1/2} V_r^T L^{-1} (formed as S_r^{-1/2} U_r^T Q^T E_cat,
+ *               the same matrix, without a triangular solve)
  *   s_dev     : fp64 [r] output, the r largest singular values of the whitened error
  * Whitening uses the Cholesky factor L of Sigma_x (Sigma_x = L L^T); the product A B is the same
  * for every square root of Sigma_x.  The range finder runs on E_cat L directly (the same bases

@@ -415,7 +415,7 @@ static size_t solve_part_doubles(int64_t m, int64_t d, int32_t k) {
 size_t glowq_solve_workspace_bytes(int64_t m, int64_t d, int32_t k, int32_t r) {
     if (m < 1 || d < 1 || r < 1 || k < r || k > kSolveMaxK || k > d || m > kMaxRows || d > kMaxMomentD) return 0;
     const size_t n = (size_t)d * d + (size_t)m * d + (size_t)m * k + (size_t)d * k + 2u * (size_t)k * k + (size_t)k +
-                     (size_t)k * d + (size_t)r * d + (size_t)(m > d ? m : d) * k + (size_t)k * k + 2u +
+                     (size_t)k * d + (size_t)(m > d ? m : d) * k + (size_t)k * k + 2u +
                      solve_part_doubles(m, d, k);
     return round256(n * sizeof(double));
 }
@@ -440,8 +440,7 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
     double* V = G + (size_t)k * k;
     double* w = V + (size_t)k * k;
     double* Bs = w + k;
-    double* Bw = Bs + (size_t)k * d;
-    double* T = Bw + (size_t)r * d;                 // orthonormalisation scratch
+    double* T = Bs + (size_t)k * d;                 // orthonormalisation scratch
     double* Ri = T + (size_t)(m > d ? m : d) * k;
     double* part = Ri + (size_t)k * k;             // split-K partial products
     const int64_t part_cap = (int64_t)solve_part_doubles(m, d, k);
@@ -476,9 +475,11 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
     ok = ok && launch_sqrt(w, s_dev, r, stream) == hipSuccess;
     ok = ok && gemm(M, r, k, Y, k, 0, V, k, 0, a_dev, r);                   // A = Q U_r S_r^{1/2}
     ok = ok && launch_colscale(a_dev, r, M, r, w, 0, 0, stream) == hipSuccess;
-    ok = ok && gemm(r, D, k, V, k, 1, Bs, D, 0, Bw, D);                     // B_w = S_r^{-1/2} U_r^T B_small
-    ok = ok && launch_colscale(Bw, D, r, D, w, 1, 1, stream) == hipSuccess;
-    ok = ok && launch_lift(L, D, Bw, b_dev, r, stream) == hipSuccess;      // B = B_w L^{-1}
+    // B = S_r^{1/2} V_r^T L^{-1} = S_r^{-1/2} U_r^T Q^T E~ L^{-1} = S_r^{-1/2} U_r^T (Q^T E_cat), since
+    // E~ = E_cat L: the lift needs no triangular solve
+    ok = ok && gemm(k, D, M, Y, k, 1, e_dev, D, 0, Bs, D);                  // P = Q^T E_cat (B_small's buffer)
+    ok = ok && gemm(r, D, k, V, k, 1, Bs, D, 0, b_dev, D);                  // U_r^T P
+    ok = ok && launch_colscale(b_dev, D, r, D, w, 1, 1, stream) == hipSuccess;  // rows times S_r^{-1/2}
     if (!ok) return GLOWQ_ERR_HIP;
     int h = 0;
     if (hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess) return GLOWQ_ERR_HIP;

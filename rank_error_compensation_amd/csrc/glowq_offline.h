@@ -75,7 +75,6 @@ hipError_t launch_jacobi(const double* G, int k, double* w, double* V, hipStream
 hipError_t launch_colscale(double* X, int ld, int n, int r, const double* w, int mode, int by_row,
                            hipStream_t stream);
 hipError_t launch_sqrt(const double* w, double* s, int r, hipStream_t stream);
-hipError_t launch_lift(const double* L, int d, double* Bw, double* B, int r, hipStream_t stream);
 
 }  // namespace glowq
 

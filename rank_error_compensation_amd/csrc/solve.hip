@@ -4,8 +4,10 @@
 // Martinsson and Tropp), return balanced factors A = U_r S_r^{1/2}, B = S_r^{1/2} V_r^T lifted back
 // to the original variables).
 //
-// Whitening uses the Cholesky factor L of Sigma_x (Sigma_x = L L^T) as the square root and L^{-1} as
-// the lift: the lifted product A B does not depend on which square root is used.  The range finder
+// Whitening uses the Cholesky factor L of Sigma_x (Sigma_x = L L^T) as the square root: the lifted
+// product A B does not depend on which square root is used.  The lift B = S_r^{1/2} V_r^T L^{-1}
+// needs no triangular solve: with V_r^T = S_r^{-1} U_r^T Q^T E~ and E~ = E_cat L it is
+// S_r^{-1/2} U_r^T (Q^T E_cat), two more products on the matrix cores.  The range finder
 // runs on the whitened stacked error E~ = E_cat L itself rather than on the QR-reduced core
 // M = R_e L: with E~ = Q_e M and the same test matrix, every step (the ranges, their orthonormal
 // bases, the small projected matrix and its SVD) is the same up to the left factor Q_e, which the
@@ -23,8 +25,6 @@
 //   jacobi_kernel      one workgroup: eigenvalues / eigenvectors of a symmetric k x k matrix in LDS
 //                      (parallel cyclic Jacobi: disjoint rotations of a round-robin round applied
 //                      together), sorted descending
-//   lift_diag_kernel   B L = B_w by column blocks from the last: each block's triangular solve in
-//                      registers, then a GEMM takes its share out of the earlier columns
 #include "glowq_offline.h"
 
 namespace glowq {
@@ -464,39 +464,6 @@ __global__ __launch_bounds__(256) void sqrt_kernel(const double* w, double* s, i
     if (c < r) s[c] = w[c] > 0.0 ? sqrt(w[c]) : 0.0;
 }
 
-// One column block of the lift B L = Bw (L lower triangular, d x d): thread t < r solves
-// x L_JJ = b for row t, where L_JJ is the diagonal block at (c0, c0) (padded to 64 x 64 with the
-// identity) and b is row t of Bw on the block's columns, already stripped of the contributions of
-// the later blocks.  From the last column: x_j = b_j / L_jj, then b_i -= x_j L_ji for i < j; the
-// row stays in registers and every L element is a broadcast LDS read.
-__global__ __launch_bounds__(128) void lift_diag_kernel(const double* L, int d, int c0, const double* Bw, double* B,
-                                                        int r) {
-    __shared__ double l[64][64];
-    const int nb = min(64, d - c0);
-    for (int idx = threadIdx.x; idx < 64 * 64; idx += 128) {
-        const int i = idx >> 6, j = idx & 63;
-        l[i][j] = (i < nb && j < nb) ? (j <= i ? L[(size_t)(c0 + i) * d + c0 + j] : 0.0) : (i == j ? 1.0 : 0.0);
-    }
-    __syncthreads();
-    const int t = threadIdx.x;
-    if (t >= r) return;
-    double x[64];
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-        const double v = Bw[(size_t)t * d + c0 + min(j, nb - 1)];  // unconditional load
-        x[j] = j < nb ? v : 0.0;
-    }
-#pragma unroll
-    for (int j = 63; j >= 0; --j) {
-        x[j] /= l[j][j];
-#pragma unroll
-        for (int i = 0; i < j; ++i) x[i] -= x[j] * l[j][i];
-    }
-#pragma unroll
-    for (int j = 0; j < 64; ++j)
-        if (j < nb) B[(size_t)t * d + c0 + j] = x[j];
-}
-
 // --------------------------------------------------------------------------- launchers
 hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream) {
     for (int n0 = 0; n0 < d; n0 += 64) {
@@ -560,28 +527,6 @@ hipError_t launch_colscale(double* X, int ld, int n, int r, const double* w, int
 hipError_t launch_sqrt(const double* w, double* s, int r, hipStream_t stream) {
     hipLaunchKernelGGL(sqrt_kernel, dim3((unsigned)ceil_div(r, 256)), dim3(256), 0, stream, w, s, r);
     return hipGetLastError();
-}
-
-// B = Bw L^{-1}, i.e. B L = Bw, by column blocks of 64 from the last: the block's columns of B
-// from its diagonal block (lift_diag_kernel), then the columns before it drop the block's share,
-// Bw[:, 0:c0] -= B[:, J] L[J, 0:c0] (a GEMM on the matrix cores).  Bw is overwritten.
-hipError_t launch_lift(const double* L, int d, double* Bw, double* B, int r, hipStream_t stream) {
-    if (r > 128) return hipErrorInvalidValue;
-    for (int c0 = (int)((d - 1) / 64) * 64; c0 >= 0; c0 -= 64) {
-        const int nb = min(64, d - c0);
-        hipLaunchKernelGGL(lift_diag_kernel, dim3(1), dim3(128), 0, stream, L, d, c0, Bw, B, r);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        if (c0 == 0) break;
-        GemmArgs g{};
-        g.M = r, g.N = c0, g.K = nb;
-        g.A = B + c0, g.lda = d, g.ta = 0;
-        g.B = L + (size_t)c0 * d, g.ldb = d, g.tb = 0;
-        g.C = Bw, g.ldc = d, g.alpha = -1.0, g.beta = 1.0;
-        e = launch_gemm(g, stream);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
 }
 
 }  // namespace glowq
