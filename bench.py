@@ -340,8 +340,11 @@ def extra_factor_solve(g, sigma32, reps=3, r=64, p=8, q=2):
         A, B, S = g.solve_factors(E, sigma, omega, r, q, workspace=ws)  # synchronises
         ts.append(time.perf_counter() - t0)
     t = statistics.median(ts)
-    flops = (d ** 3 / 3 + m * d * d + 2 * m * d * k * (2 + 2 * q) + 2 * m * k * k * 2 * (1 + 2 * q)
-             + 2 * k * k * d + 2 * m * k * r + 2 * r * d * k + r * d * d)
+    # algorithmic flops: Cholesky d^3/3; products with the triangle L (d^2 k each: L Omega, L^T P
+    # and L Z per power iteration, the final L^T P); with E_cat (2 m d k each: 2 + 2q of them);
+    # Cholesky-QR bases (two passes of Gram + X R^-1, 8 n k^2 per basis); the small Gram, A and B
+    flops = (d ** 3 / 3 + d * d * k * (2 + 2 * q) + 2 * m * d * k * (2 + 2 * q) + 8 * k * k * (m * (1 + q) + d * q)
+             + 2 * k * k * d + 2 * m * k * r + 2 * r * d * k)
     out = {"workload": f"QKV group m = {m}, d = {d}, r = {r}, p = {p}, q = {q} (errors of generated LLaMA-2-7B-shaped "
                        "weights, Sigma_x from the calibration second moment)",
            "ms": round(t * 1e3, 2), "fp64_TFLOP_per_s": round(flops / t / 1e12, 2),

@@ -244,7 +244,8 @@ size_t glowq_solve_workspace_bytes(int64_t m, int64_t d, int32_t k, int32_t r);
  *   s_dev     : fp64 [r] output, the r largest singular values of the whitened error
  * Whitening uses the Cholesky factor L of Sigma_x (Sigma_x = L L^T); the product A B is the same
  * for every square root of Sigma_x.  The range finder runs on E_cat L directly (the same bases
- * as on the QR-reduced core R_e L, up to the left factor Q_e that A carries).  All arithmetic in
+ * as on the QR-reduced core R_e L, up to the left factor Q_e that A carries), without forming
+ * it: its products are taken as products with E_cat and with L.  All arithmetic in
  * fp64.  This is an offline step: it SYNCHRONISES `stream` and returns GLOWQ_ERR_RANGE if
  * Sigma_x is not positive definite.  workspace: at least glowq_solve_workspace_bytes(m, d, k, r)
  * bytes, 256-byte aligned, overwritten. */

@@ -414,9 +414,8 @@ static size_t solve_part_doubles(int64_t m, int64_t d, int32_t k) {
 
 size_t glowq_solve_workspace_bytes(int64_t m, int64_t d, int32_t k, int32_t r) {
     if (m < 1 || d < 1 || r < 1 || k < r || k > kSolveMaxK || k > d || m > kMaxRows || d > kMaxMomentD) return 0;
-    const size_t n = (size_t)d * d + (size_t)m * d + (size_t)m * k + (size_t)d * k + 2u * (size_t)k * k + (size_t)k +
-                     (size_t)k * d + (size_t)(m > d ? m : d) * k + (size_t)k * k + 2u +
-                     solve_part_doubles(m, d, k);
+    const size_t n = (size_t)d * d + (size_t)m * k + 3u * (size_t)d * k + 2u * (size_t)k * k + (size_t)k +
+                     (size_t)(m > d ? m : d) * k + (size_t)k * k + 2u + solve_part_doubles(m, d, k);
     return round256(n * sizeof(double));
 }
 
@@ -433,14 +432,14 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
     if (workspace_bytes < glowq_solve_workspace_bytes(m, d, k, r)) return GLOWQ_ERR_WORKSPACE;
     const int M = (int)m, D = (int)d;
     double* L = static_cast<double*>(workspace);
-    double* Et = L + (size_t)d * d;
-    double* Y = Et + (size_t)m * d;
-    double* Z = Y + (size_t)m * k;
-    double* G = Z + (size_t)d * k;
+    double* Y = L + (size_t)d * d;                  // range basis Q (m x k)
+    double* Z = Y + (size_t)m * k;                  // co-range basis (d x k)
+    double* W = Z + (size_t)d * k;                  // L times a d x k block
+    double* P = W + (size_t)d * k;                  // E_cat^T Q (d x k)
+    double* G = P + (size_t)d * k;
     double* V = G + (size_t)k * k;
     double* w = V + (size_t)k * k;
-    double* Bs = w + k;
-    double* T = Bs + (size_t)k * d;                 // orthonormalisation scratch
+    double* T = w + k;                              // orthonormalisation scratch, then B_small^T
     double* Ri = T + (size_t)(m > d ? m : d) * k;
     double* part = Ri + (size_t)k * k;             // split-K partial products
     const int64_t part_cap = (int64_t)solve_part_doubles(m, d, k);
@@ -452,33 +451,32 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
         g.C = C, g.ldc = ldc, g.alpha = 1.0, g.beta = 0.0, g.part = part, g.part_cap = part_cap;
         return launch_gemm(g, stream) == hipSuccess;
     };
+    // The whitened error E~ = E_cat L is never formed: every product with it is taken as a product
+    // with E_cat and one with L (a d x k block), E~ X = E_cat (L X), E~^T Y = L^T (E_cat^T Y).
     bool ok = hipMemcpyAsync(L, sigma_dev, (size_t)d * d * sizeof(double), hipMemcpyDeviceToDevice, stream) ==
               hipSuccess;
     ok = ok && launch_cholesky(L, D, flag, stream) == hipSuccess;           // Sigma_x = L L^T
-    {
-        GemmArgs g{};                                                       // E~ = E_cat L (L lower)
-        g.M = M, g.N = D, g.K = D, g.A = e_dev, g.lda = D, g.B = L, g.ldb = D, g.C = Et, g.ldc = D;
-        g.alpha = 1.0, g.beta = 0.0, g.b_lower = 1;
-        ok = ok && launch_gemm(g, stream) == hipSuccess;
-    }
-    ok = ok && gemm(M, k, D, Et, D, 0, omega_dev, k, 0, Y, k);              // Y = E~ Omega
+    ok = ok && gemm(D, k, D, L, D, 0, omega_dev, k, 0, W, k);               // L Omega
+    ok = ok && gemm(M, k, D, e_dev, D, 0, W, k, 0, Y, k);                   // Y = E~ Omega
     ok = ok && launch_orth(Y, M, k, T, G, Ri, part, part_cap, stream) == hipSuccess;
     for (int it = 0; it < q && ok; ++it) {
-        ok = ok && gemm(D, k, M, Et, D, 1, Y, k, 0, Z, k);                  // Z = orth(E~^T Q)
+        ok = ok && gemm(D, k, M, e_dev, D, 1, Y, k, 0, P, k);               // E_cat^T Q
+        ok = ok && gemm(D, k, D, L, D, 1, P, k, 0, Z, k);                   // Z = orth(E~^T Q)
         ok = ok && launch_orth(Z, D, k, T, G, Ri, part, part_cap, stream) == hipSuccess;
-        ok = ok && gemm(M, k, D, Et, D, 0, Z, k, 0, Y, k);                  // Q = orth(E~ Z)
+        ok = ok && gemm(D, k, D, L, D, 0, Z, k, 0, W, k);                   // L Z
+        ok = ok && gemm(M, k, D, e_dev, D, 0, W, k, 0, Y, k);               // Q = orth(E~ Z)
         ok = ok && launch_orth(Y, M, k, T, G, Ri, part, part_cap, stream) == hipSuccess;
     }
-    ok = ok && gemm(k, D, M, Y, k, 1, Et, D, 0, Bs, D);                     // B_small = Q^T E~
-    ok = ok && gemm(k, k, D, Bs, D, 0, Bs, D, 1, G, k);                     // B_small B_small^T = U S^2 U^T
+    ok = ok && gemm(D, k, M, e_dev, D, 1, Y, k, 0, P, k);                   // P = E_cat^T Q
+    ok = ok && gemm(D, k, D, L, D, 1, P, k, 0, T, k);                       // B_small^T = (Q^T E~)^T = L^T P
+    ok = ok && gemm(k, k, D, T, k, 1, T, k, 0, G, k);                       // B_small B_small^T = U S^2 U^T
     ok = ok && launch_jacobi(G, k, w, V, stream) == hipSuccess;
     ok = ok && launch_sqrt(w, s_dev, r, stream) == hipSuccess;
     ok = ok && gemm(M, r, k, Y, k, 0, V, k, 0, a_dev, r);                   // A = Q U_r S_r^{1/2}
     ok = ok && launch_colscale(a_dev, r, M, r, w, 0, 0, stream) == hipSuccess;
     // B = S_r^{1/2} V_r^T L^{-1} = S_r^{-1/2} U_r^T Q^T E~ L^{-1} = S_r^{-1/2} U_r^T (Q^T E_cat), since
     // E~ = E_cat L: the lift needs no triangular solve
-    ok = ok && gemm(k, D, M, Y, k, 1, e_dev, D, 0, Bs, D);                  // P = Q^T E_cat (B_small's buffer)
-    ok = ok && gemm(r, D, k, V, k, 1, Bs, D, 0, b_dev, D);                  // U_r^T P
+    ok = ok && gemm(r, D, k, V, k, 1, P, k, 1, b_dev, D);                   // U_r^T P^T
     ok = ok && launch_colscale(b_dev, D, r, D, w, 1, 1, stream) == hipSuccess;  // rows times S_r^{-1/2}
     if (!ok) return GLOWQ_ERR_HIP;
     int h = 0;

@@ -55,7 +55,6 @@ struct GemmArgs {                // C = alpha op(A) op(B) + beta C, row-major
     double* C;
     int32_t ldc;
     double alpha, beta;
-    int32_t b_lower;              // B lower triangular: K of column j starts at j
     int32_t c_lower;              // only C's lower triangle is needed
     double* part;                 // optional scratch for split-K partial products (or nullptr)
     int64_t part_cap;             // its capacity in doubles

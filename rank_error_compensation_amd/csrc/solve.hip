@@ -12,7 +12,8 @@
 // M = R_e L: with E~ = Q_e M and the same test matrix, every step (the ranges, their orthonormal
 // bases, the small projected matrix and its SVD) is the same up to the left factor Q_e, which the
 // final A = Q U_b S^{1/2} carries directly -- so A and B are those of the QR-reduced solve, without
-// the extra thin QR (the whitened error, m x d fp64, fits in HBM).
+// the extra thin QR.  E~ itself is never formed: E~ X = E_cat (L X) and E~^T Y = L^T (E_cat^T Y),
+// so every product with it is one with E_cat and one with the triangle L against k columns.
 //
 // Kernels (all fp64):
 //   gemm_kernel        C = alpha op(A) op(B) + beta C on the fp64 matrix cores, 128 x 128 tiles
@@ -33,9 +34,8 @@ namespace glowq {
 // 128 x 128 tile per workgroup, four waves of 64 x 64, each 4 x 4 v_mfma_f64_16x16x4_f64 tiles
 // (A operand lane l: row l % 16, k l / 16; B operand lane l: k l / 16, column l % 16; result element
 // e of lane l: row l / 16 + 4 e, column l % 16 -- measured with an in-bounds probe).  K in steps of 16 through LDS, the next step's global
-// loads held in registers while the current one is multiplied.  b_lower: B is lower triangular, so
-// the K loop of a tile starts at its first column; c_lower: only tiles touching the lower triangle
-// of C are computed.
+// loads held in registers while the current one is multiplied.  c_lower: only tiles touching the
+// lower triangle of C are computed.
 typedef double d4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
@@ -57,9 +57,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs g) {
     }
     const int i0 = ty * 128, j0 = tx * 128;
     if (g.c_lower && j0 > i0 + 127) return;
-    // K range: all of K, or range z of a split launch (never combined with b_lower / c_lower)
+    // K range: all of K, or range z of a split launch (never combined with c_lower)
     const bool split = g.splits > 1;
-    const int kbeg = split ? (int)blockIdx.z * g.kc : (g.b_lower ? (j0 / 16) * 16 : 0);
+    const int kbeg = split ? (int)blockIdx.z * g.kc : 0;
     const int kend = split ? min(g.K, kbeg + g.kc) : g.K;
     d4 acc[4][4];
 #pragma unroll
@@ -157,7 +157,7 @@ hipError_t launch_gemm(const GemmArgs& g0, hipStream_t stream) {
     const int64_t tiles = ceil_div(g.N, 128) * ceil_div(g.M, 128);
     const int64_t mn = (int64_t)g.M * g.N;
     int64_t s = 1;
-    if (g.part != nullptr && !g.b_lower && !g.c_lower && tiles < kGemmWant) {
+    if (g.part != nullptr && !g.c_lower && tiles < kGemmWant) {
         s = ceil_div(kGemmWant, tiles);
         s = std::min<int64_t>(s, g.K / kGemmMinK);
         s = std::min<int64_t>(s, g.part_cap / mn);
