@@ -177,20 +177,23 @@ hipError_t launch_gemm(const GemmArgs& g0, hipStream_t stream) {
 }
 
 // --------------------------------------------------------------------------- Cholesky
+constexpr int kSmallThreads = 1024;  // one-workgroup factorisations: threads per workgroup
+
 // Factor the nb x nb diagonal block at (n0, n0) of the lower triangle of S (row stride ld) in
 // place; a non-positive pivot sets *flag.
-__global__ __launch_bounds__(256) void chol_diag_kernel(double* S, int ld, int n0, int nb, int* flag) {
+__global__ __launch_bounds__(kSmallThreads) void chol_diag_kernel(double* S, int ld, int n0, int nb, int* flag) {
     __shared__ double a[64][65];
     if (n0 == 0 && threadIdx.x == 0) *flag = 0;  // the first block clears the flag before any pivot
-    for (int idx = threadIdx.x; idx < nb * nb; idx += 256) {
+    for (int idx = threadIdx.x; idx < nb * nb; idx += kSmallThreads) {
         const int i = idx / nb, j = idx % nb;
         a[i][j] = S[(size_t)(n0 + i) * ld + n0 + j];
     }
     __syncthreads();
-    // thread t updates column c = t % 64 on rows t / 64 + 4 q.  Step j (one barrier): with the
+    // thread t updates column c = t % 64 on rows t / 64 + RS q.  Step j (one barrier): with the
     // pivot v = a[j][j], the trailing lower triangle loses a[i][j] a[c][j] / v (j < c <= i), which
     // only reads column j; then column j itself is finished (L_jj = sqrt v, L_ij = a[i][j] / L_jj)
     // while the next step reads only columns past j.
+    constexpr int RS = kSmallThreads / 64;
     const int c = threadIdx.x & 63, i0 = threadIdx.x >> 6;
     for (int j = 0; j < nb; ++j) {
         const double v = a[j][j];
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* S, int ld, int n
         const double inv = ok ? 1.0 / v : 1.0;
         if (c > j && c < nb) {
             const double acj = a[c][j] * inv;
-            for (int i = c + ((i0 - c) & 3); i < nb; i += 4) a[i][c] -= a[i][j] * acj;  // rows i >= c
+            for (int i = c + ((i0 - c) & (RS - 1)); i < nb; i += RS) a[i][c] -= a[i][j] * acj;  // rows i >= c
         }
         __syncthreads();
         const double piv = ok ? sqrt(v) : 1.0;
@@ -206,10 +209,10 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* S, int ld, int n
             if (!ok) atomicOr(flag, 1);
             a[j][j] = piv;
         }
-        for (int i = j + 1 + (int)threadIdx.x; i < nb; i += 256) a[i][j] /= piv;
+        for (int i = j + 1 + (int)threadIdx.x; i < nb; i += kSmallThreads) a[i][j] /= piv;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < nb * nb; idx += 256) {
+    for (int idx = threadIdx.x; idx < nb * nb; idx += kSmallThreads) {
         const int i = idx / nb, j = idx % nb;
         S[(size_t)(n0 + i) * ld + n0 + j] = j <= i ? a[i][j] : 0.0;
     }
@@ -272,17 +275,18 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 // pivot falls to 1e-24 of its diagonal entry (or is 0) lies in the span of the earlier ones and
 // is dropped (row and column of R zero, Rinv column zero), so X Rinv has orthonormal columns
 // where X has new directions and zero columns elsewhere.  One workgroup, R and Rinv in LDS.
-__global__ __launch_bounds__(256) void chol_inv_small_kernel(const double* G, int k, double* Rinv_out) {
+__global__ __launch_bounds__(kSmallThreads) void chol_inv_small_kernel(const double* G, int k, double* Rinv_out) {
     __shared__ double R[kSolveMaxK][kSolveMaxK + 1];
     __shared__ double Ri[kSolveMaxK][kSolveMaxK + 1];
     __shared__ int live[kSolveMaxK];
-    for (int idx = threadIdx.x; idx < k * k; idx += 256) {
+    for (int idx = threadIdx.x; idx < k * k; idx += kSmallThreads) {
         const int i = idx / k, j = idx % k;
         R[i][j] = G[idx];
         Ri[i][j] = i == j ? 1.0 : 0.0;
     }
     __syncthreads();
-    // thread t works on column c = t % 128 (c < k), rows t / 128 + 2 q.
+    // thread t works on column c = t % 128 (c < k), rows t / 128 + RS q.
+    constexpr int RS = kSmallThreads / 128;
     const int c = threadIdx.x & 127, a0 = threadIdx.x >> 7;
     // Right-looking, one barrier per step: with the pivot v = R[j][j] of a live column j, the
     // trailing upper triangle loses R[j][a] R[j][c] / v (j < a <= c), which only reads row j; then
@@ -293,12 +297,12 @@ __global__ __launch_bounds__(256) void chol_inv_small_kernel(const double* G, in
         const bool ok = v > 1e-24 * G[(size_t)j * k + j] && v > 0.0;
         if (ok && c > j && c < k) {
             const double rjc = R[j][c] / v;
-            for (int a = j + 1 + ((j + 1 - a0) & 1); a <= c; a += 2) R[a][c] -= R[j][a] * rjc;  // j < a <= c
+            for (int a = j + 1 + ((a0 - j - 1) & (RS - 1)); a <= c; a += RS) R[a][c] -= R[j][a] * rjc;  // j < a <= c
         }
         __syncthreads();
         if (threadIdx.x == 0) live[j] = ok ? 1 : 0;
         const double p = ok ? sqrt(v) : 0.0;
-        for (int cc = (int)threadIdx.x; cc < k; cc += 256) {
+        for (int cc = (int)threadIdx.x; cc < k; cc += kSmallThreads) {
             if (cc < j) R[j][cc] = 0.0;
             else if (cc > j) R[j][cc] = ok ? R[j][cc] / p : 0.0;
         }
@@ -315,15 +319,17 @@ __global__ __launch_bounds__(256) void chol_inv_small_kernel(const double* G, in
         __syncthreads();
         if (li && c < k) {
             const double x = Ri[i][c];
-            for (int l = a0; l < i; l += 2) Ri[l][c] -= R[l][i] * x;
+            for (int l = a0; l < i; l += RS) Ri[l][c] -= R[l][i] * x;
         }
         __syncthreads();
     }
-    for (int idx = threadIdx.x; idx < k * k; idx += 256) {
+    for (int idx = threadIdx.x; idx < k * k; idx += kSmallThreads) {
         const int i = idx / k, cc = idx % k;
         Rinv_out[idx] = live[cc] ? Ri[i][cc] : 0.0;
     }
 }
+
+constexpr int kJacobiThreads = 1024;
 
 // Symmetric k x k G (row-major) -> eigenvalues w (descending) and eigenvectors as the columns of
 // V (k x k, row-major).  Parallel cyclic Jacobi: each sweep is n - 1 rounds of a round-robin
@@ -331,25 +337,29 @@ __global__ __launch_bounds__(256) void chol_inv_small_kernel(const double* G, in
 // their rotations (each zeroing one off-diagonal pair) are computed from the same matrix and
 // applied together.  Sweeps repeat until the off-diagonal Frobenius mass is below 1e-30 of the
 // total (or 40 sweeps).
-__global__ __launch_bounds__(256) void jacobi_kernel(const double* G, int k, double* w, double* V) {
+__global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(const double* G, int k, double* w, double* V) {
     __shared__ double a[kSolveMaxK][kSolveMaxK + 1];
     __shared__ double v[kSolveMaxK][kSolveMaxK + 1];
     __shared__ double cs[kSolveMaxK / 2][2];
     __shared__ int pr[kSolveMaxK / 2][2];
-    __shared__ int pos[kSolveMaxK];
-    __shared__ double red[4];
+    __shared__ double red[kJacobiThreads / 64];
     __shared__ int order[kSolveMaxK];
     const int n = k + (k & 1);  // index k (when k is odd) is a dummy: its pairs are skipped
-    for (int idx = threadIdx.x; idx < k * k; idx += 256) {
+    for (int idx = threadIdx.x; idx < k * k; idx += kJacobiThreads) {
         const int i = idx / k, j = idx % k;
         a[i][j] = G[idx];
         v[i][j] = i == j ? 1.0 : 0.0;
     }
-    for (int i = threadIdx.x; i < n; i += 256) pos[i] = i;
     __syncthreads();
+    // round-robin tournament: index 0 stays, positions 1 .. n - 1 rotate by one per round, so in
+    // round rd position i holds 1 + ((i - 1 - rd) mod (n - 1)); pair t is positions t, n - 1 - t
+    auto pos = [&](int i, int rd) { return i == 0 ? 0 : 1 + ((i - 1 - rd) % (n - 1) + (n - 1)) % (n - 1); };
+    // thread t updates column (or row) e = t % 128 of the pairs t / 128 + JS i
+    constexpr int JS = kJacobiThreads / 128;
+    const int e = threadIdx.x & 127, t0 = threadIdx.x >> 7;
     for (int sweep = 0; sweep < 40; ++sweep) {
         double off = 0.0, tot = 0.0;
-        for (int idx = threadIdx.x; idx < k * k; idx += 256) {
+        for (int idx = threadIdx.x; idx < k * k; idx += kJacobiThreads) {
             const int i = idx / k, j = idx % k;
             const double x = a[i][j] * a[i][j];
             tot += x;
@@ -362,17 +372,19 @@ __global__ __launch_bounds__(256) void jacobi_kernel(const double* G, int k, dou
         }
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = off;
         __syncthreads();
-        const double off_all = red[0] + red[1] + red[2] + red[3];
+        double off_all = 0.0;
+        for (int wv = 0; wv < kJacobiThreads / 64; ++wv) off_all += red[wv];
         __syncthreads();
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tot;
         __syncthreads();
-        const double tot_all = red[0] + red[1] + red[2] + red[3];
+        double tot_all = 0.0;
+        for (int wv = 0; wv < kJacobiThreads / 64; ++wv) tot_all += red[wv];
         __syncthreads();
         if (!(off_all > 1e-30 * tot_all)) break;
         for (int round = 0; round < n - 1; ++round) {
             // pairs of this round and their rotations, all from the current matrix
-            for (int t = threadIdx.x; t < n / 2; t += 256) {
-                int p = pos[t], q = pos[n - 1 - t];
+            for (int t = threadIdx.x; t < n / 2; t += kJacobiThreads) {
+                int p = pos(t, round), q = pos(n - 1 - t, round);
                 if (p > q) {
                     const int x = p;
                     p = q;
@@ -394,52 +406,47 @@ __global__ __launch_bounds__(256) void jacobi_kernel(const double* G, int k, dou
                 cs[t][1] = sn;
             }
             __syncthreads();
-            // columns: A <- A J and V <- V J (pair t touches columns p, q only)
-            for (int idx = threadIdx.x; idx < (n / 2) * k; idx += 256) {
-                const int t = idx / k, i = idx % k;
-                const int p = pr[t][0], q = pr[t][1];
-                const double c = cs[t][0], sn = cs[t][1];
-                if (q >= k || sn == 0.0) continue;
-                const double aip = a[i][p], aiq = a[i][q];
-                a[i][p] = c * aip - sn * aiq;
-                a[i][q] = sn * aip + c * aiq;
-                const double vip = v[i][p], viq = v[i][q];
-                v[i][p] = c * vip - sn * viq;
-                v[i][q] = sn * vip + c * viq;
+            // columns: A <- A J and V <- V J (pair t touches columns p, q only); row i = e
+            if (e < k) {
+                for (int t = t0; t < n / 2; t += JS) {
+                    const int p = pr[t][0], q = pr[t][1];
+                    const double c = cs[t][0], sn = cs[t][1];
+                    if (q >= k || sn == 0.0) continue;
+                    const double aip = a[e][p], aiq = a[e][q];
+                    a[e][p] = c * aip - sn * aiq;
+                    a[e][q] = sn * aip + c * aiq;
+                    const double vip = v[e][p], viq = v[e][q];
+                    v[e][p] = c * vip - sn * viq;
+                    v[e][q] = sn * vip + c * viq;
+                }
             }
             __syncthreads();
-            // rows: A <- J^T A (pair t touches rows p, q only)
-            for (int idx = threadIdx.x; idx < (n / 2) * k; idx += 256) {
-                const int t = idx / k, j = idx % k;
-                const int p = pr[t][0], q = pr[t][1];
-                const double c = cs[t][0], sn = cs[t][1];
-                if (q >= k || sn == 0.0) continue;
-                const double apj = a[p][j], aqj = a[q][j];
-                a[p][j] = c * apj - sn * aqj;
-                a[q][j] = sn * apj + c * aqj;
-            }
-            __syncthreads();
-            // next round: positions 1 .. n-1 rotate by one
-            if (threadIdx.x == 0) {
-                const int last = pos[n - 1];
-                for (int i = n - 1; i > 1; --i) pos[i] = pos[i - 1];
-                pos[1] = last;
+            // rows: A <- J^T A (pair t touches rows p, q only); column j = e
+            if (e < k) {
+                for (int t = t0; t < n / 2; t += JS) {
+                    const int p = pr[t][0], q = pr[t][1];
+                    const double c = cs[t][0], sn = cs[t][1];
+                    if (q >= k || sn == 0.0) continue;
+                    const double apj = a[p][e], aqj = a[q][e];
+                    a[p][e] = c * apj - sn * aqj;
+                    a[q][e] = sn * apj + c * aqj;
+                }
             }
             __syncthreads();
         }
     }
     // sort descending (selection by rank, ties to the lower index)
-    for (int i = threadIdx.x; i < k; i += 256) {
+    for (int i = threadIdx.x; i < k; i += kJacobiThreads) {
         int rank = 0;
         for (int j = 0; j < k; ++j) rank += (a[j][j] > a[i][i] || (a[j][j] == a[i][i] && j < i)) ? 1 : 0;
         order[rank] = i;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < k * k; idx += 256) {
+    for (int idx = threadIdx.x; idx < k * k; idx += kJacobiThreads) {
         const int i = idx / k, c = idx % k;
         V[idx] = v[i][order[c]];
     }
-    for (int c = threadIdx.x; c < k; c += 256) w[c] = a[order[c]][order[c]];
+    for (int c = threadIdx.x; c < k; c += kJacobiThreads) w[c] = a[order[c]][order[c]];
 }
 
 // Scale by the eigenvalues w of the Gram (w = S^2): element (i, c) of X (n x r) times f(w[c])
@@ -468,7 +475,7 @@ __global__ __launch_bounds__(256) void sqrt_kernel(const double* w, double* s, i
 hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream) {
     for (int n0 = 0; n0 < d; n0 += 64) {
         const int nb = min(64, d - n0);
-        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, stream, S, d, n0, nb, flag);
+        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kSmallThreads), 0, stream, S, d, n0, nb, flag);
         const int rest = d - n0 - nb;
         if (rest > 0) {
             hipLaunchKernelGGL(chol_panel_kernel, dim3((unsigned)ceil_div(rest, 128)), dim3(128), 0, stream, S, d, d,
@@ -500,7 +507,7 @@ hipError_t launch_orth(double* X, int n, int k, double* T, double* G, double* Ri
         g.C = G, g.ldc = k, g.alpha = 1.0, g.beta = 0.0, g.part = part, g.part_cap = part_cap;
         hipError_t e = launch_gemm(g, stream);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(chol_inv_small_kernel, dim3(1), dim3(256), 0, stream, G, k, Rinv);
+        hipLaunchKernelGGL(chol_inv_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, G, k, Rinv);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         GemmArgs h{};
@@ -513,7 +520,7 @@ hipError_t launch_orth(double* X, int n, int k, double* T, double* G, double* Ri
 }
 
 hipError_t launch_jacobi(const double* G, int k, double* w, double* V, hipStream_t stream) {
-    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(256), 0, stream, G, k, w, V);
+    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kJacobiThreads), 0, stream, G, k, w, V);
     return hipGetLastError();
 }
 
