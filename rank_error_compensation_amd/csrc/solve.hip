@@ -472,24 +472,43 @@ __global__ __launch_bounds__(256) void sqrt_kernel(const double* w, double* s, i
 }
 
 // --------------------------------------------------------------------------- launchers
+// S -= L L^T over rows / columns [c0, d) with L the columns [l0, l0 + kw) of the rows [c0, d)
+// (only tiles touching the lower triangle), or, with ncols > 0, only the columns [c0, c0 + ncols)
+// of those rows.
+static hipError_t chol_update(double* S, int d, int c0, int l0, int kw, int ncols, hipStream_t stream) {
+    GemmArgs g{};
+    g.M = d - c0, g.N = ncols > 0 ? ncols : d - c0, g.K = kw;
+    g.A = S + (size_t)c0 * d + l0, g.lda = d, g.ta = 0;
+    g.B = S + (size_t)c0 * d + l0, g.ldb = d, g.tb = 1;
+    g.C = S + (size_t)c0 * d + c0, g.ldc = d;
+    g.alpha = -1.0, g.beta = 1.0, g.c_lower = 1;
+    return launch_gemm(g, stream);
+}
+
+// Blocked right-looking Cholesky with 128-column blocks, each factored as two 64-column halves:
+// the first half's diagonal block and the rows below it, the second half's columns updated by the
+// first half, the second half's diagonal block and rows below, then one trailing update with both
+// halves (K = 128: half the passes over the trailing matrix of a 64-column blocking).
 hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream) {
-    for (int n0 = 0; n0 < d; n0 += 64) {
-        const int nb = min(64, d - n0);
-        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kSmallThreads), 0, stream, S, d, n0, nb, flag);
-        const int rest = d - n0 - nb;
-        if (rest > 0) {
-            hipLaunchKernelGGL(chol_panel_kernel, dim3((unsigned)ceil_div(rest, 128)), dim3(128), 0, stream, S, d, d,
-                               n0);  // rest > 0: the block is a full 64 wide
-            GemmArgs g{};  // S22 -= L21 L21^T (tiles touching the lower triangle; only it is used)
-            g.M = rest, g.N = rest, g.K = nb;
-            g.A = S + (size_t)(n0 + nb) * d + n0, g.lda = d, g.ta = 0;
-            g.B = S + (size_t)(n0 + nb) * d + n0, g.ldb = d, g.tb = 1;
-            g.C = S + (size_t)(n0 + nb) * d + n0 + nb, g.ldc = d;
-            g.alpha = -1.0, g.beta = 1.0, g.c_lower = 1;
-            const hipError_t e = launch_gemm(g, stream);
-            if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    for (int n0 = 0; n0 < d && e == hipSuccess; n0 += 128) {
+        const int nb2 = min(128, d - n0);
+        for (int h = 0; h < nb2 && e == hipSuccess; h += 64) {
+            const int c0 = n0 + h, nb = min(64, nb2 - h);
+            if (h > 0) {
+                e = chol_update(S, d, c0, n0, 64, nb, stream);  // second half's columns, first half's L
+                if (e != hipSuccess) break;
+            }
+            hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kSmallThreads), 0, stream, S, d, c0, nb, flag);
+            const int rest = d - c0 - nb;
+            if (rest > 0)  // a full 64-wide block has rows below it
+                hipLaunchKernelGGL(chol_panel_kernel, dim3((unsigned)ceil_div(rest, 128)), dim3(128), 0, stream, S, d,
+                                   d, c0);
+            e = hipGetLastError();
         }
+        if (e == hipSuccess && n0 + nb2 < d) e = chol_update(S, d, n0 + nb2, n0, nb2, 0, stream);
     }
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(zero_upper_kernel, dim3((unsigned)ceil_div((int64_t)d * d, 256)), dim3(256), 0, stream, S, d, d);
     return hipGetLastError();
 }
