@@ -2,8 +2,8 @@
 (oracle.solve.core_factors with the Cholesky factor of Sigma_x as the square root, and
 oracle.solve.randomized_svd for the singular values), the same test matrix on both sides.
 
-Bar: both sides run the same fp64 algorithm up to the orthonormalisation method (Gram-Schmidt
-here, Householder QR in the oracle) and the left factor of the QR reduction, so the lifted
+Bar: both sides run the same fp64 algorithm up to the orthonormalisation method (two Cholesky-QR
+passes here, Householder QR in the oracle) and the left factor of the QR reduction, so the lifted
 products A B agree to 1e-8 relative Frobenius norm and the singular values to 1e-9 relative
 where the spectrum has a gap at r; an exactly rank-r0 whitened error (r0 <= r) is reproduced:
 A B = E_cat to 1e-9."""
@@ -87,3 +87,15 @@ def test_not_positive_definite_is_reported():
     with pytest.raises(g.GlowQError) as ei:
         run(g, E, Sigma, r, 4, 0, seed=1)
     assert ei.value.status == g.ERR_RANGE
+
+
+def test_deterministic():
+    """Split-K partial products are added in range order: two solves give identical bits."""
+    g = glowq()
+    m, d, r, p, q = 2048, 640, 16, 8, 1
+    rng = np.random.default_rng(5)
+    Sigma = covariance(d, 1.19, 9)
+    E = rng.standard_normal((m, r)) @ rng.standard_normal((r, d)) + 1e-3 * rng.standard_normal((m, d))
+    A1, B1, S1 = run(g, E, Sigma, r, p, q, seed=2)
+    A2, B2, S2 = run(g, E, Sigma, r, p, q, seed=2)
+    assert np.array_equal(A1, A2) and np.array_equal(B1, B2) and np.array_equal(S1, S2)
