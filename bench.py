@@ -429,6 +429,31 @@ def achievable_peaks(reps=5):
                    "waves, 4 independent chains each, sustained over 5 launches)"}
 
 
+def launch_sequence_floor(nbytes, reps=5):
+    """Time of one pass of streaming reads with the decode step's launch sequence: one launch per
+    unit reading that unit's algorithmic bytes (regions laid end to end, 3.6 GB in all, beyond the
+    last-level cache), one workgroup per 32 KiB -- what separate launches of these sizes allow."""
+    import torch
+    from rank_error_compensation_amd import probe
+    sizes = [(int(b) + 15) // 16 * 16 for b in nbytes]
+    seq = probe.ReadSequence(sizes)
+    src = torch.ones(seq.total, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(max((b + 32767) // 32768 for b in sizes) * 256 * 16, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    seq.run(src, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        seq.run(src, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del src, sink
+    torch.cuda.empty_cache()
+    return us
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -504,7 +529,14 @@ def main():
                 "alg_bytes_per_launch_mean": int(sum(nbytes) / len(nbytes)),
                 "launch_us_mean": round(launch_us, 3),
                 "per_unit_single_launch_event_us": per_kind}
-    log(f"[bench] decode kernel: {achieved:.0f} GB/s, {launch_us:.2f} us per launch over {len(descr)} launches")
+    floor_us = launch_sequence_floor(nbytes)
+    roofline["launch_sequence_floor"] = {
+        "us_per_step": round(floor_us, 1), "GB_per_s": round(sum(nbytes) / (floor_us * 1e-6) / 1e9, 1),
+        "frac": round(floor_us / (elapsed / args.steps * 1e6), 4),
+        "how": "probe library: the same 128 launches as plain streaming reads of each unit's algorithmic "
+               "bytes, one workgroup of 256 threads per 32 KiB; frac = floor / decode step time"}
+    log(f"[bench] decode kernel: {achieved:.0f} GB/s, {launch_us:.2f} us per launch over {len(descr)} launches; "
+        f"streaming floor of the same launch sequence {floor_us:.1f} us/step")
 
     # ---- layerwise baseline on the same path
     extra = {}

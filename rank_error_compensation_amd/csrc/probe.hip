@@ -7,13 +7,17 @@
 //   * a matrix-core loop: v_mfma_f32_32x32x16_f16 on register operands, four independent
 //     accumulators per wave, no memory traffic in the loop -- the dense fp16 rate the matrix
 //     cores sustain (including any clock reduction under that load).  The 32x32x16 form is used
-//     because it is the fastest fp16 matrix step here: 16x16x32 sustains about half its rate.
+//     because it is the fastest fp16 matrix step here: 16x16x32 sustains about half its rate;
+//   * a sequence of streaming reads, one launch per region with one workgroup per 32 KiB -- what
+//     back-to-back launches of given sizes allow, launch ramp and tail included.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "glowq_probe.h"
 
 namespace {
+
+constexpr int64_t kSequenceMaxBlocks = 8192;  // workgroups of one read of a sequence (256 MiB)
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -83,6 +87,24 @@ int glowq_probe_mfma_f16(int64_t iters, void* sink_dev, int32_t blocks, hipStrea
     if ((reinterpret_cast<uintptr_t>(sink_dev) & 15) != 0) return -1;
     hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, iters, static_cast<f4*>(sink_dev));
     return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int glowq_probe_read_sequence(const void* src_dev, const int64_t* bytes, int32_t n, void* sink_dev,
+                              hipStream_t stream) {
+    if (src_dev == nullptr || bytes == nullptr || sink_dev == nullptr || n < 1) return -1;
+    if ((reinterpret_cast<uintptr_t>(src_dev) & 15) != 0 || (reinterpret_cast<uintptr_t>(sink_dev) & 15) != 0)
+        return -1;
+    for (int32_t i = 0; i < n; ++i)
+        if (bytes[i] < 16 || bytes[i] % 16 != 0 || (bytes[i] + 32767) / 32768 > kSequenceMaxBlocks) return -1;
+    const char* p = static_cast<const char*>(src_dev);
+    for (int32_t i = 0; i < n; ++i) {
+        const unsigned blocks = (unsigned)((bytes[i] + 32767) / 32768);
+        hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(256), 0, stream, reinterpret_cast<const u4*>(p),
+                           (uint64_t)(bytes[i] / 16), static_cast<u4*>(sink_dev));
+        if (hipGetLastError() != hipSuccess) return -6;
+        p += bytes[i];
+    }
+    return 0;
 }
 
 double glowq_probe_mfma_f16_flops(int64_t iters, int32_t blocks) {

@@ -14,6 +14,7 @@ EXPORTS = {
     "glowq_probe_read": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "glowq_probe_mfma_f16": (ctypes.c_int, [_i64, _vp, _i32, _vp]),
     "glowq_probe_mfma_f16_flops": (ctypes.c_double, [_i64, _i32]),
+    "glowq_probe_read_sequence": (ctypes.c_int, [_vp, ctypes.POINTER(_i64), _i32, _vp, _vp]),
 }
 _lib = None
 
@@ -50,3 +51,19 @@ def mfma_f16(iters: int, sink: torch.Tensor, blocks: int) -> float:
     if rc != 0:
         raise RuntimeError(f"glowq_probe_mfma_f16 failed ({rc})")
     return lib().glowq_probe_mfma_f16_flops(iters, blocks)
+
+
+class ReadSequence:
+    """Marshalled size array for repeated glowq_probe_read_sequence calls over one buffer."""
+
+    def __init__(self, sizes):
+        self.n = len(sizes)
+        self.arr = (_i64 * self.n)(*[int(b) for b in sizes])
+        self.total = sum(int(b) for b in sizes)
+
+    def run(self, src: torch.Tensor, sink: torch.Tensor) -> None:
+        if src.numel() * src.element_size() < self.total:
+            raise ValueError("source buffer smaller than the sequence")
+        rc = lib().glowq_probe_read_sequence(src.data_ptr(), self.arr, self.n, sink.data_ptr(), _stream())
+        if rc != 0:
+            raise RuntimeError(f"glowq_probe_read_sequence failed ({rc})")

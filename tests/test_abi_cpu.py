@@ -235,3 +235,8 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert L.glowq_probe_mfma_f16(10, None, 4, None) == -1
     assert L.glowq_probe_mfma_f16(-1, FAKE, 4, None) == -1
     assert L.glowq_probe_mfma_f16_flops(3, 2) == 2 * 4 * 3 * 4 * 32 * 32 * 16 * 2
+    sizes = (ctypes.c_int64 * 3)(1024, 1000, 2048)                   # 1000: not a multiple of 16
+    assert L.glowq_probe_read_sequence(FAKE, sizes, 3, FAKE, None) == -1
+    sizes = (ctypes.c_int64 * 1)(257 << 20)                          # beyond 256 MiB per read
+    assert L.glowq_probe_read_sequence(FAKE, sizes, 1, FAKE, None) == -1
+    assert L.glowq_probe_read_sequence(FAKE, sizes, 0, FAKE, None) == -1

@@ -56,3 +56,21 @@ def test_read_probe_folds_every_word():
     got = np.bitwise_xor.reduce(sink.view(torch.int32).cpu().numpy().reshape(-1, 4), axis=0)
     want = np.bitwise_xor.reduce(words.numpy().reshape(-1, 4), axis=0)
     np.testing.assert_array_equal(got, want)
+
+
+def test_read_sequence_reads_consecutive_regions():
+    """The launch-sequence probe reads region i right after region i - 1: with two regions of one
+    size, the second launch overwrites every sink word, and the xor over the sink equals the xor
+    of the second region alone."""
+    from rank_error_compensation_amd import probe
+    n16 = 1 << 12                                    # 64 KiB per region: 2 workgroups per read
+    g = torch.Generator(device="cpu").manual_seed(11)
+    words = torch.randint(0, 2**31 - 1, (2 * n16 * 4,), generator=g, dtype=torch.int64).to(torch.int32)
+    src = words.cuda()
+    sink = torch.zeros(2 * 256 * 16, dtype=torch.uint8, device="cuda")
+    seq = probe.ReadSequence([n16 * 16, n16 * 16])
+    seq.run(src.view(torch.uint8), sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.view(torch.int32).cpu().numpy().reshape(-1, 4), axis=0)
+    want = np.bitwise_xor.reduce(words.numpy()[n16 * 4:].reshape(-1, 4), axis=0)
+    np.testing.assert_array_equal(got, want)
