@@ -205,9 +205,9 @@ def rotating_group(T, copies, g, device):
     return u, sets, a_sets, ys
 
 
-def extra_decode_qkv(g, reps=50):
+def extra_decode_qkv(g, T=1, reps=50):
     import torch
-    T, copies = 1, 20
+    copies = 20
     u, sets, a_sets, ys = rotating_group(T, copies, g, "cuda")
     ws = g.make_workspace(T, u.r)
     stream = torch.cuda.current_stream()
@@ -226,9 +226,62 @@ def extra_decode_qkv(g, reps=50):
     ts = [e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs]
     t = statistics.median(ts)
     nb = unit_bytes(T, 4096, u.n_outs, u.r, True)
-    return {"workload": "llama2-7b QKV group decode T=1 r=64 (20 rotating weight copies)",
+    return {"workload": f"llama2-7b QKV group decode T={T} r=64 (20 rotating weight copies)",
             "us_median": round(t * 1e6, 3), "tokens_per_s": round(T / t, 1),
             "alg_bytes": nb, "TB_per_s": round(nb / t / 1e12, 4), "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4)}
+
+
+def extra_llama3(g, reps=10, min_bytes=600 << 20):
+    """LLaMA-3.1-8B GQA units (QKV group 4096 -> 4096 + 1024 + 1024, gate/up group 4096 ->
+    2 x 14336, solo down 14336 -> 4096) at T = 64 and 4096, r = 64 and 128: median time of one call
+    between events; at T = 64 the call cycles over enough weight copies (>= 600 MB) that its
+    weights stream from HBM."""
+    import torch
+    import workload as W
+    stream = torch.cuda.current_stream()
+    out = {}
+    for r in (64, 128):
+        for T in (64, 4096):
+            units = W.llama3_gqa_units(T, r, device="cuda")
+            for u in units:
+                w0 = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
+                wbytes = sum(w.q.numel() * w.q.element_size() + w.sz.numel() * w.sz.element_size() for w in w0)
+                copies = max(1, -(-min_bytes // wbytes)) if T <= 64 else 1
+                sets = [w0] + [[g.QWeight(w.q.clone(), w.sz.clone(), w.n_out, w.k_in) for w in w0]
+                               for _ in range(copies - 1)]
+                ws = g.make_workspace(T, r, 1)
+                ys = [torch.empty(T, w.n_out, dtype=torch.float16, device="cuda") for w in w0]
+
+                def call(i):
+                    if u.kind == "solo":
+                        g.solo_forward(u.x, sets[i][0], u.b, u.a[0], r, True, workspace=ws, y=ys[0])
+                    else:
+                        g.group_forward(u.x, sets[i], u.b, u.a, r, True, workspace=ws, y=ys)
+
+                for i in range(copies):
+                    call(i)
+                torch.cuda.synchronize()
+                evs = []
+                for k in range(reps * copies):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    call(k % copies)
+                    e1.record(stream)
+                    evs.append((e0, e1))
+                torch.cuda.synchronize()
+                t = statistics.median(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
+                nb = unit_bytes(T, u.d, u.n_outs, r, True)
+                fl = unit_flops(T, u.d, u.n_outs, r, True)
+                e = {"us": round(t * 1e6, 2), "tokens_per_s": round(T / t, 1),
+                     "TB_per_s": round(nb / t / 1e12, 3), "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4),
+                     "TFLOP_per_s": round(fl / t / 1e12, 1), "frac_mfma_f16_peak": round(fl / t / 1e12 / 2500.0, 4)}
+                if copies > 1:
+                    e["weight_copies"] = copies
+                out[f"{u.name} T={T} r={r}"] = e
+                del sets, w0, ws, ys
+            del units
+            torch.cuda.empty_cache()
+    return out
 
 
 def extra_prefill_gateup(g, reps=20):
@@ -590,8 +643,11 @@ def main():
         log(f"[bench] prefill path T=512: {tp * 1e3:.3f} ms, {fl / tp / 1e12:.1f} TFLOP/s")
         del plan_p, units_p
         torch.cuda.empty_cache()
-        extra["decode_qkv_T1"] = extra_decode_qkv(g)
-        log(f"[bench] QKV decode T=1: {extra['decode_qkv_T1']}")
+        for Tq in (1, 4, 16):
+            extra[f"decode_qkv_T{Tq}"] = extra_decode_qkv(g, Tq)
+            log(f"[bench] QKV decode T={Tq}: {extra[f'decode_qkv_T{Tq}']}")
+        extra["llama3_gqa_units"] = extra_llama3(g)
+        log(f"[bench] LLaMA-3.1-8B GQA units: {extra['llama3_gqa_units']}")
         extra["prefill_gateup_T2048"] = extra_prefill_gateup(g)
         for k in ("group", "layerwise"):
             e = extra["prefill_gateup_T2048"][k]

@@ -166,7 +166,9 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
     if (c.correct && !prefill) {
         const int64_t total = (int64_t)c.n_proj * c.r;
         f.prod_rows = (int32_t)ceil_div(total, kMaxProducers);
-        f.n_prod = (int32_t)ceil_div(total, f.prod_rows);
+        // one producer per (row block, token tile); tiles of 1, 4 or 16 tokens as the kernel picks
+        const int64_t ptt = c.T == 1 ? 1 : (c.T <= 4 ? 4 : 16);
+        f.n_prod = (int32_t)(ceil_div(total, f.prod_rows) * ceil_div(c.T, ptt));
     }
     int tt = 0, rr = 0, ks = 1;
     if (prefill) choose_prefill_shape(c, tt, rr, ks);

@@ -102,12 +102,14 @@ __device__ __forceinline__ void finish(const ForwardArgs& a, int top_prev, uint3
     __hip_atomic_store(a.sync + kSyncEpoch, (int32_t)next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Producer workgroup: rows [p * prod_rows, (p+1) * prod_rows) of the stacked projections
-// (row jj = projection jj / r, rank index jj % r), all tokens; fp32 accumulation of exact fp16
-// products, fixed-order block reduction, each value stored as a tagged pair.
-template <int KW>
+// Producer workgroup p: rows [pr prod_rows, (pr + 1) prod_rows) of the stacked projections (row
+// jj = projection jj / r, rank index jj % r) for the TT-token tile tt of the call's tokens, with
+// p = pr n_tt + tt; fp32 accumulation of exact fp16 products, fixed-order block reduction, each
+// value stored as a tagged pair.  Per 8-input chunk a thread reads the B chunk and the tile's TT
+// token chunks (rows past T re-read the last token and are never stored) before any product, so
+// a chunk costs one memory round trip, not one per token.
+template <int KW, int TT>
 __device__ void produce(const ForwardArgs& a, int p) {
-    constexpr int C = 4;  // 8-input chunks per thread in flight
     constexpr int NTH = 64 * KW;
     __shared__ float part[KW][16];
     __shared__ uint32_t ptag;
@@ -122,87 +124,69 @@ __device__ void produce(const ForwardArgs& a, int p) {
     const int T = a.T, d = a.d, r = a.r;
     u64* R = reinterpret_cast<u64*>(a.R);
     const int total = a.n_proj * r;
-    const int j0 = p * a.prod_rows;
+    const int n_tt = (T + TT - 1) / TT;
+    const int pr = p / n_tt, t0 = (p - pr * n_tt) * TT;
+    const int nt = min(TT, T - t0);
+    const int j0 = pr * a.prod_rows;
     const int j1 = min(j0 + a.prod_rows, total);
     const int n8 = d / 8;
     for (int jj = j0; jj < j1; ++jj) {
         const int pi = jj / r, j = jj - pi * r;
         const _Float16* brow = pick_bp(a, pi) + (size_t)j * d;
-        for (int t0 = 0; t0 < T; t0 += 16) {
-            const int nt = min(16, T - t0);
-            float acc[16];
+        float acc[TT];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) acc[t] = 0.f;
-            for (int c0 = threadIdx.x; c0 < n8; c0 += NTH * C) {
-                h8 bv[C];
+        for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+        for (int c = threadIdx.x; c < n8; c += NTH) {
+            const h8 bv = load_h8(brow + 8 * c);
+            h8 xv[TT];
 #pragma unroll
-                for (int k = 0; k < C; ++k) {
-                    const int c = min(c0 + NTH * k, n8 - 1);
-                    bv[k] = load_h8(brow + 8 * c);
-                }
+            for (int t = 0; t < TT; ++t) xv[t] = load_h8(a.x + (size_t)(t0 + min(t, nt - 1)) * d + 8 * c);
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    if (t < nt) {
-                        h8 xv[C];
+            for (int t = 0; t < TT; ++t) {
+                float s = acc[t];
 #pragma unroll
-                        for (int k = 0; k < C; ++k) {
-                            const int c = min(c0 + NTH * k, n8 - 1);
-                            xv[k] = load_h8(a.x + (size_t)(t0 + t) * d + 8 * c);
-                        }
-                        float s = acc[t];
-#pragma unroll
-                        for (int k = 0; k < C; ++k) {
-                            if (c0 + NTH * k < n8) {
-#pragma unroll
-                                for (int e = 0; e < 8; ++e) s = fmaf((float)bv[k][e], (float)xv[k][e], s);
-                            }
-                        }
-                        acc[t] = s;
-                    }
-                }
+                for (int e = 0; e < 8; ++e) s = fmaf((float)bv[e], (float)xv[t][e], s);
+                acc[t] = s;
             }
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                if (t < nt) {
-                    float v = acc[t];
-#pragma unroll
-                    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-                    acc[t] = v;
-                }
-            }
-            if (lane == 0) {
-#pragma unroll
-                for (int t = 0; t < 16; ++t) part[wave][t] = acc[t];
-            }
-            if (first) {
-                if (threadIdx.x == 0) {
-                    ptag = epoch0 + 1u;
-                    arrived = arrive(a);
-                }
-                first = false;
-            }
-            __syncthreads();
-            const uint32_t tag = ptag;
-            if (scrub && (tag == 1u || tag == 0xFFFFFFFFu)) {
-                // first and last tag of a wrap: clear every pair of the decode area outside this
-                // call's range (no one reads them in this call)
-                const size_t from = (size_t)kRReplicas * a.n_proj * T * r;
-                for (size_t k = from + (size_t)p * NTH + threadIdx.x; k < kDecodeAreaPairs;
-                     k += (size_t)a.n_prod * NTH)
-                    R[k] = 0ull;
-            }
-            scrub = false;
-            if (threadIdx.x < 16 && (int)threadIdx.x < nt) {
-                const int t = threadIdx.x;
-                float v = part[0][t];
-#pragma unroll
-                for (int w = 1; w < KW; ++w) v += part[w][t];
-                const size_t off = ((size_t)pi * T + t0 + t) * r + j, copy = (size_t)a.n_proj * T * r;
-#pragma unroll
-                for (int c = 0; c < kRReplicas; ++c) store_pair(R + c * copy + off, v, tag);
-            }
-            __syncthreads();
         }
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            float v = acc[t];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+            acc[t] = v;
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) part[wave][t] = acc[t];
+        }
+        if (first) {
+            if (threadIdx.x == 0) {
+                ptag = epoch0 + 1u;
+                arrived = arrive(a);
+            }
+            first = false;
+        }
+        __syncthreads();
+        const uint32_t tag = ptag;
+        if (scrub && (tag == 1u || tag == 0xFFFFFFFFu)) {
+            // first and last tag of a wrap: clear every pair of the decode area outside this
+            // call's range (no one reads them in this call)
+            const size_t from = (size_t)kRReplicas * a.n_proj * T * r;
+            for (size_t k = from + (size_t)p * NTH + threadIdx.x; k < kDecodeAreaPairs; k += (size_t)a.n_prod * NTH)
+                R[k] = 0ull;
+        }
+        scrub = false;
+        if ((int)threadIdx.x < nt) {
+            const int t = threadIdx.x;
+            float v = part[0][t];
+#pragma unroll
+            for (int w = 1; w < KW; ++w) v += part[w][t];
+            const size_t off = ((size_t)pi * T + t0 + t) * r + j, copy = (size_t)a.n_proj * T * r;
+#pragma unroll
+            for (int c = 0; c < kRReplicas; ++c) store_pair(R + c * copy + off, v, tag);
+        }
+        __syncthreads();
     }
     if (threadIdx.x == 0) finish(a, arrive_xcd(a, arrived), epoch0);
 }
@@ -225,7 +209,13 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
     extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
 
     if ((int)blockIdx.x < args.n_prod) {
-        produce<KW>(args, blockIdx.x);
+        // token tile of a producer: one token, up to 4, or 16 (the launcher sizes n_prod to match)
+        if (args.T == 1)
+            produce<KW, 1>(args, blockIdx.x);
+        else if (args.T <= 4)
+            produce<KW, 4>(args, blockIdx.x);
+        else
+            produce<KW, 16>(args, blockIdx.x);
         return;
     }
     const int tile = blockIdx.x - args.n_prod;
