@@ -117,7 +117,9 @@ void choose_prefill_shape(const Call& c, int& tt, int& rr, int& ks) {
 
 int run(const Call& c, void* workspace, hipStream_t stream) {
     if (c.T == 0) return GLOWQ_OK;
-    const bool prefill = c.T > kDecodeMaxT;
+    int64_t row_tiles = 0;
+    for (int i = 0; i < c.m; ++i) row_tiles += ceil_div(c.w[i].n_out, 128);
+    const bool prefill = c.T > kDecodeMaxT || (c.T > kDecodeWideT && row_tiles >= kPrefillMinRowTiles);
     const int32_t rp = (int32_t)r_pad_of(c.r);
     void* R = nullptr;
     if (c.correct) {
@@ -262,8 +264,8 @@ size_t glowq_sz_bytes(int64_t n_out, int64_t k_in) {
 
 size_t glowq_workspace_bytes(int64_t T, int32_t r, int32_t n_proj) {
     if (T <= 0 || r <= 0 || n_proj <= 0) return 0;
-    if (T > kDecodeMaxT) return kWsHeader + kDecodeAreaBytes + prefill_r_bytes(T, r, n_proj) +
-                                prefill_part_bytes(T, r, n_proj);
+    if (T > kDecodeWideT) return kWsHeader + kDecodeAreaBytes + prefill_r_bytes(T, r, n_proj) +
+                                 prefill_part_bytes(T, r, n_proj);
     return kWsHeader + kDecodeAreaBytes;
 }
 

@@ -53,6 +53,11 @@ constexpr int kSpinLimit = 1 << 20;
 constexpr int kRReplicas = 8;
 // Token count above which the prefill (dequant-to-register MFMA GEMM) kernels are used.
 constexpr int kDecodeMaxT = 64;
+// Between kDecodeWideT and kDecodeMaxT tokens the activations no longer fit in LDS and the decode
+// kernel re-reads them from L2 for every 16-row tile; a call with at least kPrefillMinRowTiles
+// 128-row tiles (a wide group) then runs the prefill path instead, whose tiles share them.
+constexpr int kDecodeWideT = 16;
+constexpr int kPrefillMinRowTiles = 40;
 // The decode pairs live in a fixed area right after the header, sized for the largest decode
 // call (T <= kDecodeMaxT, r <= kMaxRank, up to kMaxModules projections, kRReplicas copies), so
 // that no other data (the prefill projection of an earlier call) ever lies where a later decode

@@ -45,14 +45,15 @@ def test_buffer_sizes():
     hdr = 2048  # synchronisation words of the decode hand-off
     r256 = lambda n: (n + 255) // 256 * 256
     # the fixed decode area ((fp32, tag) pairs for T <= 64, r <= 256, 8 projections, 8 copies),
-    # then for prefill calls the projection in fp16 (r padded to 32) and its fp32 split-K
-    # partials (up to 8 splits)
+    # then for calls that may take the prefill path (T > 16) the projection in fp16 (r padded to
+    # 32) and its fp32 split-K partials (up to 8 splits)
     area = 64 * 256 * 8 * 8 * 8
-    ws = lambda T, r, p: hdr + area + (0 if T <= 64 else
+    ws = lambda T, r, p: hdr + area + (0 if T <= 16 else
                                        r256(T * ((r + 31) // 32 * 32) * 2 * p) +
                                        r256(8 * T * ((r + 31) // 32 * 32) * 4 * p))
     assert L.glowq_workspace_bytes(1, 64, 1) == hdr + area
-    assert L.glowq_workspace_bytes(64, 256, 8) == hdr + area
+    assert L.glowq_workspace_bytes(16, 256, 8) == hdr + area
+    assert L.glowq_workspace_bytes(64, 256, 8) == ws(64, 256, 8)
     assert L.glowq_workspace_bytes(2048, 64, 1) == hdr + area + 2048 * 64 * 2 + 8 * 2048 * 64 * 4
     assert L.glowq_workspace_bytes(100, 8, 3) == ws(100, 8, 3)
 
