@@ -183,7 +183,8 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
         for (int i = 0; i < c.m; ++i) total16 += ceil_div(c.w[i].n_out, 16);
         const bool xlds = c.T <= 16 && (size_t)(c.T + 1) * (size_t)c.d * 2u <= kDecodeXLdsMax;
         f.dec_kw = (total16 <= kDecodeWide8Tiles && f.G >= kDecodeWide8Groups) ? 8 : 4;
-        dec_rt = (f.dec_kw == 4 && xlds && total16 > kDecodeRt2Tiles) ? 2 : 1;
+        const bool rt2 = xlds ? total16 > kDecodeRt2Tiles : (c.T <= 16 && total16 >= kDecodeRt2NoLdsTiles);
+        dec_rt = (f.dec_kw == 4 && rt2) ? 2 : 1;
         f.dec_rt = dec_rt;
     }
     int64_t tiles = 0;

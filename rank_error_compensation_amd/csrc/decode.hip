@@ -489,7 +489,11 @@ static hipError_t launch_decode_kw(const ForwardArgs& a, hipStream_t stream) {
                                stream, b);
         return hipGetLastError();
     }
-    if (RT != 1) return hipErrorInvalidValue;
+    if (RT != 1) {  // two row tiles share each activation operand read from L2 (one token tile)
+        if (ntt != 1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((decode_kernel<1, 0, KW, RT>), grid, block, shmem, stream, b);
+        return hipGetLastError();
+    }
     switch (ntt) {
         case 1: hipLaunchKernelGGL((decode_kernel<1, 0, KW, 1>), grid, block, shmem, stream, b); break;
         case 2: hipLaunchKernelGGL((decode_kernel<2, 0, KW, 1>), grid, block, shmem, stream, b); break;

@@ -72,6 +72,10 @@ constexpr size_t kDecodeXLdsMax = 48 * 1024;
 constexpr int kDecodeWide8Tiles = 512;
 constexpr int kDecodeWide8Groups = 64;
 constexpr int kDecodeRt2Tiles = 1024;
+// Without the activations in LDS (6 to 16 tokens at d = 4096) every workgroup reads them from L2
+// with its weights; two row tiles per workgroup then halve that traffic once a launch has this many
+// 16-row tiles (QKV decode at T = 16: 25.8 -> 18.5 us).
+constexpr int kDecodeRt2NoLdsTiles = 512;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -153,6 +153,19 @@ def test_ragged_group(T, d, n_outs, r):
         assert_parity(y, yr, f"T={T} d={d} O={n_outs[i]} r={r}")
 
 
+@pytest.mark.parametrize("T", [6, 16])
+def test_decode_two_row_tiles_without_lds(T):
+    """6-16 tokens at d = 4096 (activations read from L2, not staged in LDS) with 513 16-row tiles:
+    two row tiles per workgroup, the last module's last workgroup holding one real tile."""
+    x = W.make_x(T, 4096, 1.19, (37, T))
+    u = W.make_unit("wide", "group", x, [4096, 2064, 2048], 64, (37, T, 64))
+    du = DevUnit(u)
+    for restore in (True, False):
+        ys = du.forward(restore=restore)
+        for i, (y, yr) in enumerate(zip(ys, oracle_unit(u, restore=restore))):
+            assert_parity(y, yr, f"T={T} restore={restore} module {i}")
+
+
 @pytest.mark.parametrize("T", [1, 5, 100])
 def test_solo_and_layerwise(T):
     keys = (8, T)
