@@ -231,6 +231,35 @@ def extra_decode_qkv(g, T=1, reps=50):
             "alg_bytes": nb, "TB_per_s": round(nb / t / 1e12, 4), "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4)}
 
 
+def extra_tiny_qkv(g, reps=200):
+    """The tiny QKV group (d = 256, 3 x 256 outputs, T = 8, r = 16): a latency-bound launch.  Its
+    correction factors are drawn as scaled Gaussians of the same shapes (their values do not change
+    the launch)."""
+    import torch
+    import workload as W
+    c = W.tiny_qkv_inputs(device="cuda")
+    w = [g.QWeight.from_workload(q, device="cuda") for q in c["qw"]]
+    a, b = W.gaussian_factors([q.n_out for q in c["qw"]], c["d"], c["r"], [q.err_sq for q in c["qw"]],
+                              (0, 0, 0, 9), "cuda")
+    ws = g.make_workspace(c["T"], c["r"])
+    ys = [torch.empty(c["T"], q.n_out, dtype=torch.float16, device="cuda") for q in c["qw"]]
+    stream = torch.cuda.current_stream()
+    for _ in range(10):
+        g.group_forward(c["x"], w, b, a, c["r"], True, workspace=ws, y=ys)
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.group_forward(c["x"], w, b, a, c["r"], True, workspace=ws, y=ys)
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    t = statistics.median(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
+    return {"workload": "tiny QKV group d = 256, 3 x 256, T = 8, r = 16", "us_median": round(t * 1e6, 2),
+            "tokens_per_s": round(c["T"] / t, 1)}
+
+
 def extra_llama3(g, reps=10, min_bytes=600 << 20):
     """LLaMA-3.1-8B GQA units (QKV group 4096 -> 4096 + 1024 + 1024, gate/up group 4096 ->
     2 x 14336, solo down 14336 -> 4096) at T = 64 and 4096, r = 64 and 128: median time of one call
@@ -643,6 +672,8 @@ def main():
         log(f"[bench] prefill path T=512: {tp * 1e3:.3f} ms, {fl / tp / 1e12:.1f} TFLOP/s")
         del plan_p, units_p
         torch.cuda.empty_cache()
+        extra["tiny_qkv"] = extra_tiny_qkv(g)
+        log(f"[bench] tiny QKV: {extra['tiny_qkv']}")
         for Tq in (1, 4, 16):
             extra[f"decode_qkv_T{Tq}"] = extra_decode_qkv(g, Tq)
             log(f"[bench] QKV decode T={Tq}: {extra[f'decode_qkv_T{Tq}']}")
