@@ -105,3 +105,43 @@ def test_prefill_deterministic_and_row_independent():
     for a, b in zip(ys, y1):
         e = G.parity_errors(a.float().cpu().numpy(), b[:300].float().cpu().numpy().astype(np.float64))
         assert e["rel_fro"] <= 1e-3
+
+
+def test_path_graph_replay_matches_eager():
+    """The decode schedule (layers 0..3, T = 1, mixed restore bits) captured in a HIP graph: every
+    replay, with eager work and synchronisation between replays, reproduces the eager outputs
+    bitwise (the hand-off's epoch lives in the workspace, so replays never reuse a tag)."""
+    g = glowq()
+    layers, T = [0, 1, 2, 3], 1
+    units, mask = W.llama2_path_inputs(T, device="cuda", layers=layers)
+    plan_units = []
+    for l in layers:
+        for u in units[l]:
+            du = DevUnit(u)
+            ys = [torch.empty(T, q.n_out, dtype=torch.float16, device="cuda") for q in u.weights]
+            kind = g.UNIT_GROUP if u.kind == "group" else g.UNIT_SOLO
+            plan_units.append(g.PathUnit(kind, du.x, du.w, du.b, du.a, u.r, bool(mask[l]), ys))
+    plan = g.PathPlan(plan_units)
+    plan.run()
+    torch.cuda.synchronize()
+    ref = [y.clone() for pu in plan_units for y in pu.y]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.run()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for pu in plan_units:
+            for y in pu.y:
+                y.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [y for pu in plan_units for y in pu.y]
+        for i, (a, b) in enumerate(zip(got, ref)):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager run"
