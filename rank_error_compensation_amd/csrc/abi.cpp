@@ -36,6 +36,10 @@ inline size_t prefill_r_bytes(int64_t T, int32_t r, int32_t n_proj) {
     return round256((size_t)T * (size_t)r_pad_of(r) * 2u * (size_t)n_proj);
 }
 // fp32 split-K partials of the prefill projection, after the fp16 projection
+inline size_t narrow_part_bytes(int64_t T) {
+    return round256((size_t)kNarrowKs * (size_t)T * (size_t)kNarrowMaxRows * 4u);
+}
+
 inline size_t prefill_part_bytes(int64_t T, int32_t r, int32_t n_proj) {
     return round256((size_t)kProjMaxSplit * (size_t)T * (size_t)r_pad_of(r) * 4u * (size_t)n_proj);
 }
@@ -185,9 +189,21 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
         f.dec_kw = (total16 <= kDecodeWide8Tiles && f.G >= kDecodeWide8Groups) ? 8 : 4;
         const bool rt2 = xlds ? total16 > kDecodeRt2Tiles : (c.T <= 16 && total16 >= kDecodeRt2NoLdsTiles);
         dec_rt = (f.dec_kw == 4 && rt2) ? 2 : 1;
+        f.dec_ks = 1;
+        f.dec_gk = f.G;
+        if (c.T > kDecodeWideT && c.correct && f.G >= kNarrowMinGroups) {  // narrow, long rows: split K
+            f.dec_kw = 4;
+            dec_rt = kNarrowRt;
+            f.dec_ks = (int32_t)(f.G < kNarrowKs ? f.G : kNarrowKs);
+            f.dec_gk = (int32_t)ceil_div(f.G, f.dec_ks);
+            f.dec_ks = (int32_t)ceil_div(f.G, f.dec_gk);
+            uint8_t* base = static_cast<uint8_t*>(workspace) + kWsHeader + kDecodeAreaBytes +
+                            prefill_r_bytes(c.T, c.r, c.n_proj) + prefill_part_bytes(c.T, c.r, c.n_proj);
+            f.ypart = reinterpret_cast<float*>(base);
+        }
         f.dec_rt = dec_rt;
     }
-    int64_t tiles = 0;
+    int64_t tiles = 0, rows = 0;
     for (int i = 0; i < c.m; ++i) {
         ModuleArgs& M = f.mod[i];
         M.q = static_cast<const uint8_t*>(c.w[i].q);
@@ -199,8 +215,11 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
         M.tile_begin = (int32_t)tiles;
         f.tile_begin[i] = (int32_t)tiles;
         M.proj = c.n_proj > 1 ? i : 0;
+        M.row_begin = (int32_t)rows;
+        rows += c.w[i].n_out;
         tiles += prefill ? ceil_div(M.n_tiles16, 4 * rr) : ceil_div(M.n_tiles16, dec_rt);
     }
+    f.rows_total = (int32_t)rows;
     hipError_t e;
     if (prefill) {
         f.m_tiles = (int32_t)ceil_div(c.T, 16 * tt);
@@ -208,7 +227,8 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
         e = launch_prefill(f, stream);
     } else {
         f.m_tiles = 1;
-        f.n_tiles = (int32_t)tiles;
+        f.dec_tiles = (int32_t)tiles;
+        f.n_tiles = (int32_t)(tiles * f.dec_ks);
         e = launch_decode(f, stream);
     }
     return e == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
@@ -266,7 +286,7 @@ size_t glowq_sz_bytes(int64_t n_out, int64_t k_in) {
 size_t glowq_workspace_bytes(int64_t T, int32_t r, int32_t n_proj) {
     if (T <= 0 || r <= 0 || n_proj <= 0) return 0;
     if (T > kDecodeWideT) return kWsHeader + kDecodeAreaBytes + prefill_r_bytes(T, r, n_proj) +
-                                 prefill_part_bytes(T, r, n_proj);
+                                 prefill_part_bytes(T, r, n_proj) + (T <= kDecodeMaxT ? narrow_part_bytes(T) : 0);
     return kWsHeader + kDecodeAreaBytes;
 }
 

@@ -218,7 +218,10 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
             produce<KW, 16>(args, blockIdx.x);
         return;
     }
-    const int tile = blockIdx.x - args.n_prod;
+    // consumer workgroup: row block `tile`, K range `ks_idx` (one range unless the launch splits K)
+    const int tile_all = blockIdx.x - args.n_prod;
+    const int ks_idx = tile_all / args.dec_tiles;
+    const int tile = tile_all - ks_idx * args.dec_tiles;
     const ModuleArgs M = args.mod[module_of(args, tile)];
     const int rt0 = (tile - M.tile_begin) * RT;  // first 16-row tile of this workgroup
     const int lane = threadIdx.x & 63;
@@ -236,9 +239,13 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
     const int kofs = 8 * (lane >> 4);
     const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     const NibConsts nc = nib_consts();
-    const int n_my = G > wave ? (G - wave + KW - 1) / KW : 0;  // groups of this wave: g = wave + KW i
+    const int g0 = ks_idx * args.dec_gk, g1 = min(G, g0 + args.dec_gk);  // this workgroup's groups
+    const int n_my = g1 - g0 > wave ? (g1 - g0 - wave + KW - 1) / KW : 0;  // g = g0 + wave + KW i
     const bool hand = args.n_prod > 0;  // correcting launch: R hand-off and epoch protocol
-    const bool correct = hand && M.a != nullptr;
+    // with a K split the partial sums go to the workspace (the first K range carrying the
+    // correction) and a second launch adds them
+    const bool split = args.dec_ks > 1;
+    const bool correct = hand && M.a != nullptr && ks_idx == 0;
     const int r = args.r;
     // the epoch: one read per workgroup, the first load of thread 0 (so that waiting for it never
     // waits for weights), handed to the other waves through LDS
@@ -277,7 +284,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
     u4 zs4[U][RT];
     h8 bx[XLDS ? 1 : U][NTT][4];
     auto issue = [&](int u, int i) {
-        const int g = min(wave + KW * i, G - 1);  // always a valid group of this row tile
+        const int g = min(g0 + wave + KW * i, g1 - 1);  // always a valid group of this workgroup
         if (!XLDS) {
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt)
@@ -302,7 +309,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
         for (int tt = 0; tt < NTT; ++tt) acc[rr][tt] = f4{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int u, int i) {
-        const int g = wave + KW * i;
+        const int g = g0 + wave + KW * i;
         // activation operands first: the LDS reads complete while the weights are unpacked
         h8 bl[XLDS ? NTT : 1][4];
         if (XLDS) {
@@ -446,7 +453,12 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
         for (int w = 1; w < KW; ++w) v += red[w][rr][tt][lane];  // fixed order: deterministic
         const int t = 16 * tt + (lane & 15);
         const int row0 = (rt0 + rr) * 16 + 4 * (lane >> 4);
-        if (t < T && rt0 + rr < M.n_tiles16) {
+        if (split && t < T && rt0 + rr < M.n_tiles16) {
+            float* pp = args.ypart + ((size_t)ks_idx * T + t) * args.rows_total + M.row_begin + row0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (row0 + i < M.n_out) pp[i] = v[i];
+        } else if (t < T && rt0 + rr < M.n_tiles16) {
             _Float16 o[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = (_Float16)v[i];
@@ -464,19 +476,42 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
     if (hand && threadIdx.x == 0) finish(args, top_prev, epoch0);
 }
 
+// Narrow calls with a K split: y = the K ranges' fp32 partial sums (the first range's carrying the
+// correction) added in range order, rounded once to fp16.  One thread per (token, row): rows are
+// consecutive across a wave, so every read and write is coalesced.
+__global__ __launch_bounds__(256) void decode_reduce_kernel(const ForwardArgs a) {
+    const size_t n = (size_t)a.T * a.rows_total;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n) return;
+    const int t = (int)(idx / a.rows_total), row = (int)(idx - (size_t)t * a.rows_total);
+    // the module holding this row: field by field selection (no indexed load of the records)
+    _Float16* y = a.mod[0].y;
+    int n_out = a.mod[0].n_out, row_begin = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxModules; ++k) {
+        const bool in = k < a.n_mod && row >= a.mod[k].row_begin;
+        y = in ? a.mod[k].y : y;
+        n_out = in ? a.mod[k].n_out : n_out;
+        row_begin = in ? a.mod[k].row_begin : row_begin;
+    }
+    float v = 0.f;
+    for (int s = 0; s < a.dec_ks; ++s) v += a.ypart[((size_t)s * a.T + t) * a.rows_total + row];
+    y[(size_t)t * n_out + (row - row_begin)] = (_Float16)v;
+}
+
 template <int KW, int RT>
 static hipError_t launch_decode_kw(const ForwardArgs& a, hipStream_t stream) {
     constexpr int NTH = 64 * KW;
     const int ntt = (int)ceil_div(a.T, 16);
     const dim3 grid(a.n_prod + a.n_tiles), block(NTH);
     const size_t xbytes = (size_t)(a.T + 1) * a.d * 2;  // tokens + one zero row
-    const bool xlds = ntt == 1 && xbytes <= kDecodeXLdsMax;
+    const bool xlds = RT != kNarrowRt && ntt == 1 && xbytes <= kDecodeXLdsMax;
     const size_t xarea = xlds ? (xbytes + 15) / 16 * 16 : 0;
     const size_t rarea = (ntt == 1 && a.r > 0) ? (size_t)a.T * a.r * 4 : 0;
     ForwardArgs b = a;
     b.r_lds_off = (int32_t)xarea;
     const size_t shmem = xarea + rarea;
-    if (xlds) {
+    if constexpr (RT != kNarrowRt) if (xlds) {
         const int chunks = (int)ceil_div((int64_t)xbytes / 16, NTH);
         if (chunks <= 2)
             hipLaunchKernelGGL((decode_kernel<1, 2, KW, RT>), grid, block, shmem, stream, b);
@@ -487,6 +522,15 @@ static hipError_t launch_decode_kw(const ForwardArgs& a, hipStream_t stream) {
         else
             hipLaunchKernelGGL((decode_kernel<1, (int)(kDecodeXLdsMax / 16 / NTH), KW, RT>), grid, block, shmem,
                                stream, b);
+        return hipGetLastError();
+    }
+    if constexpr (RT == kNarrowRt) {  // K-split narrow calls: 17 .. 64 tokens
+        switch (ntt) {
+            case 2: hipLaunchKernelGGL((decode_kernel<2, 0, KW, RT>), grid, block, shmem, stream, b); break;
+            case 3: hipLaunchKernelGGL((decode_kernel<3, 0, KW, RT>), grid, block, shmem, stream, b); break;
+            case 4: hipLaunchKernelGGL((decode_kernel<4, 0, KW, RT>), grid, block, shmem, stream, b); break;
+            default: return hipErrorInvalidValue;
+        }
         return hipGetLastError();
     }
     if (RT != 1) {  // two row tiles share each activation operand read from L2 (one token tile)
@@ -505,6 +549,14 @@ static hipError_t launch_decode_kw(const ForwardArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream) {
+    if (a.dec_ks > 1) {  // narrow call with a K split: 4 waves, kNarrowRt row tiles, then the sums
+        if (a.dec_kw != 4 || a.dec_rt != kNarrowRt) return hipErrorInvalidValue;
+        hipError_t e = launch_decode_kw<4, kNarrowRt>(a, stream);
+        if (e != hipSuccess) return e;
+        const size_t n = (size_t)a.T * a.rows_total;
+        hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)ceil_div((int64_t)n, 256)), dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     if (a.dec_kw == 8) return launch_decode_kw<8, 1>(a, stream);
     return a.dec_rt == 2 ? launch_decode_kw<4, 2>(a, stream) : launch_decode_kw<4, 1>(a, stream);
 }

@@ -58,6 +58,17 @@ constexpr int kDecodeMaxT = 64;
 // 128-row tiles (a wide group) then runs the prefill path instead, whose tiles share them.
 constexpr int kDecodeWideT = 16;
 constexpr int kPrefillMinRowTiles = 40;
+// The correcting narrow calls of kDecodeWideT + 1 .. kDecodeMaxT tokens that stay on the decode
+// path (fewer than kPrefillMinRowTiles 128-row tiles, so at most kNarrowMaxRows rows) with long
+// rows (at least kNarrowMinGroups input groups) split K into kNarrowKs ranges over workgroups of
+// kNarrowRt row tiles: the activations each CU reads from L2 shrink 4x at the same workgroup
+// count; the first range carries the correction and a second launch adds the fp32 partial sums
+// in range order (down_proj 4096 <- 14336 at T = 64: 67.6 -> 42.9 us; at d = 4096 the split is
+// no faster, its ranges being two groups per wave).
+constexpr int kNarrowKs = 4;
+constexpr int kNarrowRt = 4;
+constexpr int kNarrowMinGroups = 64;
+constexpr int kNarrowMaxRows = kPrefillMinRowTiles * 128;
 // The decode pairs live in a fixed area right after the header, sized for the largest decode
 // call (T <= kDecodeMaxT, r <= kMaxRank, up to kMaxModules projections, kRReplicas copies), so
 // that no other data (the prefill projection of an earlier call) ever lies where a later decode
@@ -143,6 +154,7 @@ struct ModuleArgs {
     int32_t n_tiles16;   // ceil(n_out / 16)
     int32_t tile_begin;  // first work tile of this module in the launch's tile numbering
     int32_t proj;        // which projection R_p this module adds (0 for shared B)
+    int32_t row_begin;   // first row of this module in the launch's concatenated rows
 };
 
 struct ForwardArgs {
@@ -164,7 +176,12 @@ struct ForwardArgs {
     int32_t prod_rows;   // decode: stacked projection rows per producer
     int32_t r_lds_off;   // decode: byte offset of the R copy in dynamic LDS (set by the launcher)
     int32_t dec_kw;      // decode: waves per workgroup (4 or 8)
-    int32_t dec_rt;      // decode: 16-row tiles per workgroup (1 or 2)
+    int32_t dec_rt;      // decode: 16-row tiles per workgroup (1, 2, or 4 with a K split)
+    int32_t dec_ks;      // decode: K ranges per row block (1, or kNarrowKs for narrow calls)
+    int32_t dec_gk;      // decode: input groups per K range
+    int32_t dec_tiles;   // decode: row blocks (n_tiles = dec_tiles * dec_ks consumer workgroups)
+    int32_t rows_total;  // decode: rows of all modules
+    float* ypart;        // decode with a K split: fp32 partial sums [dec_ks][T][rows_total]
     const _Float16* b[kMaxModules];  // [r][d] right factors, one per projection
     ModuleArgs mod[kMaxModules];
 };

@@ -166,6 +166,34 @@ def test_decode_two_row_tiles_without_lds(T):
             assert_parity(y, yr, f"T={T} restore={restore} module {i}")
 
 
+@pytest.mark.parametrize("T", [17, 33, 64])
+def test_decode_narrow_k_split(T):
+    """17-64 tokens on a correcting narrow call (fewer than 40 128-row tiles) with long rows (at
+    least 64 input groups): the groups split into 4 K ranges over 4-row-tile workgroups, the first
+    range adding the correction, then a second launch sums the ranges.  A ragged module (520 rows:
+    the last workgroup holds one real 16-row tile and a half-empty one), a solo module whose 65
+    groups split 17 + 17 + 17 + 14, and a layerwise group (one projection per module); without
+    restore the call takes the unsplit decode kernel.  (The solo and layerwise cases run at one
+    token count: their factors at d >= 8192 take the oracle most of the test's time.)"""
+    x = W.make_x(T, 8192, 1.19, (41, T))
+    u = W.make_unit("nar", "group", x, [1024, 520, 256], 64, (41, T, 64))
+    du = DevUnit(u)
+    for restore in (True, False):
+        ys = du.forward(restore=restore)
+        for i, (y, yr) in enumerate(zip(ys, oracle_unit(u, restore=restore))):
+            assert_parity(y, yr, f"T={T} restore={restore} module {i}")
+    if T != 33:
+        return
+    xs = W.make_x(T, 8320, 0.77, (42, T))
+    solo = W.make_unit("ns", "solo", xs, [200], 24, (42, T))
+    assert_parity(DevUnit(solo).forward()[0], oracle_unit(solo)[0], f"solo T={T}")
+    xl = W.make_x(T, 8192, 0.77, (43, T))
+    lw = W.make_unit("nl", "group", xl, [64, 48, 16], 16, (43, T), layerwise=True)
+    for i, (y, yr) in enumerate(zip(DevUnit(lw, layerwise=True).forward_layerwise(),
+                                    oracle_unit(lw, layerwise=True))):
+        assert_parity(y, yr, f"layerwise T={T} module {i}")
+
+
 @pytest.mark.parametrize("T", [1, 5, 100])
 def test_solo_and_layerwise(T):
     keys = (8, T)
