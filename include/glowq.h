@@ -103,9 +103,10 @@ int glowq_dequant(const glowq_qweight* w, void* out_dev, int32_t out_dtype, hipS
 
 /* ---------------------------------------------------------------- forward
  * Workspace bytes for a call with T tokens, rank r and n_proj right projections (1 for a
- * group or solo call, m for the layerwise baseline).  Holds the projection R = X B^T and
- * synchronisation words.  Zero-fill it once after allocation; every call leaves it
- * reusable.  Returns 0 when no workspace is needed (r == 0 or T == 0).
+ * group or solo call, m for the layerwise baseline).  Holds the projection R = X B^T,
+ * synchronisation words and, for 17 to 64 tokens, the fp32 partial outputs of a call whose
+ * input groups are split over workgroups.  Zero-fill it once after allocation; every call
+ * leaves it reusable.  Returns 0 when no workspace is needed (r == 0 or T == 0).
  */
 size_t glowq_workspace_bytes(int64_t T, int32_t r, int32_t n_proj);
 
