@@ -254,6 +254,26 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
                         const double* omega_dev, int32_t r, int32_t k, int32_t q, double* a_dev, double* b_dev,
                         double* s_dev, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes of glowq_ec_score (0 if the sizes are invalid). */
+size_t glowq_ec_score_workspace_bytes(int64_t m, int64_t d);
+
+/* Restore score g_ec of one unit (GlowQ paper note, key design 4): the share of the whitened
+ * error's energy that its best rank r captures, sum_{j < r} s_j^2 / ||E_cat L||_F^2.
+ *   e_dev     : fp64 [m][d] stacked errors of the unit's modules
+ *   sigma_dev : fp64 [d][d] Sigma_x (symmetric; only the lower triangle is read)
+ *   s_dev     : fp64 [r] singular values of the whitened error (as glowq_solve_factors returns
+ *               them), may be NULL when r == 0; 0 <= r <= min(m, d)
+ *   out_dev   : fp64 [3] output: ||E_cat L||_F^2 = trace(E_cat Sigma_x E_cat^T) (the same for
+ *               every square root L of Sigma_x), sum_{j < r} s_j^2, and their ratio (0 when the
+ *               energy is 0)
+ * The energy is formed as sum_ij Sigma_ij (E_cat^T E_cat)_ij from the fp64 GEMM's lower triangle,
+ * summed in a fixed order (bitwise repeatable).  With singular values from the randomized solve
+ * the captured energy is that of its rank-r approximation, at most the exact best rank r.
+ * workspace: at least glowq_ec_score_workspace_bytes(m, d) bytes, 256-byte aligned,
+ * overwritten.  Asynchronous on `stream`. */
+int glowq_ec_score(const double* e_dev, int64_t m, int64_t d, const double* sigma_dev, const double* s_dev,
+                   int32_t r, double* out_dev, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

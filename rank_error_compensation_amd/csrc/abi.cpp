@@ -510,6 +510,31 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
     return h ? GLOWQ_ERR_RANGE : GLOWQ_OK;
 }
 
+size_t glowq_ec_score_workspace_bytes(int64_t m, int64_t d) {
+    if (m < 1 || d < 1 || m > kMaxRows || d > kMaxMomentD) return 0;
+    return round256(((size_t)d * d + (size_t)d) * sizeof(double));
+}
+
+int glowq_ec_score(const double* e_dev, int64_t m, int64_t d, const double* sigma_dev, const double* s_dev,
+                   int32_t r, double* out_dev, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!e_dev || !sigma_dev || !out_dev || !workspace || (r > 0 && !s_dev)) return GLOWQ_ERR_INVALID_ARG;
+    if (m < 1 || d < 1 || r < 0 || r > m || r > d) return GLOWQ_ERR_SHAPE;
+    if (m > kMaxRows || d > kMaxMomentD) return GLOWQ_ERR_UNSUPPORTED;
+    if (!aligned(e_dev, 16) || !aligned(sigma_dev, 16) || !aligned(out_dev, 16) || (s_dev && !aligned(s_dev, 16)) ||
+        !aligned(workspace, 256))
+        return GLOWQ_ERR_ALIGN;
+    if (workspace_bytes < glowq_ec_score_workspace_bytes(m, d)) return GLOWQ_ERR_WORKSPACE;
+    double* C = static_cast<double*>(workspace);
+    double* part = C + (size_t)d * d;
+    GemmArgs g{};  // C = E_cat^T E_cat, lower triangle
+    g.M = (int32_t)d, g.N = (int32_t)d, g.K = (int32_t)m;
+    g.A = e_dev, g.lda = (int32_t)d, g.ta = 1;
+    g.B = e_dev, g.ldb = (int32_t)d, g.tb = 0;
+    g.C = C, g.ldc = (int32_t)d, g.alpha = 1.0, g.beta = 0.0, g.c_lower = 1;
+    if (launch_gemm(g, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    return launch_ec(C, sigma_dev, (int)d, s_dev, r, part, out_dev, stream) == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
+}
+
 int glowq_restore_topk(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k,
                        double* scores_dev, int32_t* mask_dev, hipStream_t stream) {
     if (!sums_dev || !scores_dev || !mask_dev) return GLOWQ_ERR_INVALID_ARG;

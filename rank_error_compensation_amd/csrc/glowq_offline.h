@@ -22,6 +22,10 @@ struct NerBatch {
 hipError_t launch_ner(const NerBatch& a, hipStream_t stream);
 hipError_t launch_topk(const double* sums, int32_t n_units, int32_t n_per, int32_t k, double* scores,
                        int32_t* mask, hipStream_t stream);
+// g_ec terms from C = E_cat^T E_cat (lower triangle, d x d): out = (energy, captured, ratio);
+// part holds d doubles
+hipError_t launch_ec(const double* C, const double* sigma, int d, const double* sv, int r, double* part,
+                     double* out, hipStream_t stream);
 
 // Input second moment (offline factor solve): lower-triangle tiles x token ranges.
 struct MomentArgs {

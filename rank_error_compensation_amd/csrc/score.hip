@@ -152,6 +152,62 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs a) {
     }
 }
 
+// The other score, g_ec(u): the share of a unit's whitened error energy that its best rank r
+// captures, sum_{j <= r} sigma_j^2 / ||E_cat L||_F^2 (GlowQ paper note, key design 4; the
+// singular values are those of the whitened error, e.g. from the factor solve).  With
+// C = E_cat^T E_cat (lower triangle, from the fp64 GEMM) the energy is
+// ||E_cat L||_F^2 = trace(E_cat Sigma_x E_cat^T) = sum_ij Sigma_ij C_ij, whichever square root L
+// of Sigma_x whitens.
+//   * ec_rows_kernel: workgroup i adds Sigma_ij C_ij over j < i, doubles it (the mirror terms)
+//     and adds the diagonal term, lanes and waves in a fixed order.
+//   * ec_finish_kernel: one workgroup adds the rows in a fixed order, then the r squared singular
+//     values in order, and forms the ratio (0 for a zero error).
+__global__ __launch_bounds__(256) void ec_rows_kernel(const double* C, const double* sigma, int d, double* part) {
+    __shared__ double red[256];
+    const int i = blockIdx.x;
+    const double* c = C + (size_t)i * d;
+    const double* sg = sigma + (size_t)i * d;
+    double v = 0.0;
+    for (int j = threadIdx.x; j < i; j += 256) v = fma(sg[j], c[j], v);
+    red[threadIdx.x] = v;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[i] = 2.0 * red[0] + sg[i] * c[i];
+}
+
+__global__ __launch_bounds__(256) void ec_finish_kernel(const double* part, int d, const double* sv, int r,
+                                                        double* out) {
+    __shared__ double red[256];
+    double v = 0.0;
+    for (int i = threadIdx.x; i < d; i += 256) v += part[i];
+    red[threadIdx.x] = v;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double energy = red[0];
+        double cap = 0.0;
+        for (int j = 0; j < r; ++j) cap = fma(sv[j], sv[j], cap);
+        out[0] = energy;
+        out[1] = cap;
+        out[2] = energy > 0.0 ? cap / energy : 0.0;
+    }
+}
+
+hipError_t launch_ec(const double* C, const double* sigma, int d, const double* sv, int r, double* part,
+                     double* out, hipStream_t stream) {
+    hipLaunchKernelGGL(ec_rows_kernel, dim3((unsigned)d), dim3(256), 0, stream, C, sigma, d, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ec_finish_kernel, dim3(1), dim3(256), 0, stream, part, d, sv, r, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_ner(const NerBatch& a, hipStream_t stream) {
     hipLaunchKernelGGL(ner_partial_kernel, dim3((unsigned)a.tile_begin[a.n_mod]), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();

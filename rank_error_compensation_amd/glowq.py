@@ -74,6 +74,8 @@ EXPORTS = {
     "glowq_solve_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "glowq_solve_factors": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
                                            _vp]),
+    "glowq_ec_score_workspace_bytes": (_sz, [_i64, _i64]),
+    "glowq_ec_score": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -243,6 +245,21 @@ def solve_factors(e: torch.Tensor, sigma: torch.Tensor, omega: torch.Tensor, r: 
     check(lib().glowq_solve_factors(_ptr(e), m, d, _ptr(sigma), _ptr(omega), r, k, q, _ptr(A), _ptr(B), _ptr(S),
                                     _ptr(workspace), workspace.numel(), _stream(stream)), "glowq_solve_factors")
     return A, B, S
+
+
+def ec_score(e: torch.Tensor, sigma: torch.Tensor, s: Optional[torch.Tensor], r: int,
+             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp64 [3]: ||E_cat L||_F^2, sum of the first r squared singular values s, and g_ec, their
+    ratio (glowq_ec_score)."""
+    e, sigma = e.contiguous(), sigma.contiguous()
+    m, d = int(e.shape[0]), int(e.shape[1])
+    out = torch.empty(3, dtype=torch.float64, device=e.device)
+    if workspace is None:
+        workspace = torch.empty(int(lib().glowq_ec_score_workspace_bytes(m, d)), dtype=torch.uint8, device=e.device)
+    s = s.contiguous() if s is not None else None
+    check(lib().glowq_ec_score(_ptr(e), m, d, _ptr(sigma), _ptr(s), r, _ptr(out), _ptr(workspace), workspace.numel(),
+                               _stream(stream)), "glowq_ec_score")
+    return out
 
 
 # --------------------------------------------------------------------------- forward

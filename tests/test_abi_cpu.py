@@ -201,6 +201,26 @@ def test_solve_validates():
     assert L.glowq_solve_factors(*args(n=need - 1)) == g.ERR_WORKSPACE
 
 
+def test_ec_score_validates():
+    L = g.lib()
+    assert L.glowq_ec_score_workspace_bytes(0, 128) == 0
+    assert L.glowq_ec_score_workspace_bytes(96, 0) == 0
+    need = L.glowq_ec_score_workspace_bytes(96, 128)
+    assert need == (128 * 128 + 128) * 8  # E^T E (d x d) and one partial sum per row
+    args = lambda **kw: [kw.get(n, v) for n, v in (("e", FAKE), ("m", 96), ("d", 128), ("s", FAKE), ("sv", FAKE),
+                                                       ("r", 8), ("o", FAKE), ("ws", FAKE), ("n", need),
+                                                       ("st", None))]
+    assert L.glowq_ec_score(*args(e=None)) == g.ERR_INVALID_ARG
+    assert L.glowq_ec_score(*args(sv=None)) == g.ERR_INVALID_ARG
+    assert L.glowq_ec_score(*args(r=-1)) == g.ERR_SHAPE
+    assert L.glowq_ec_score(*args(r=97)) == g.ERR_SHAPE        # r > m
+    assert L.glowq_ec_score(*args(m=0)) == g.ERR_SHAPE
+    assert L.glowq_ec_score(*args(d=1 << 20, n=1 << 40)) == g.ERR_UNSUPPORTED
+    assert L.glowq_ec_score(*args(o=FAKE + 8)) == g.ERR_ALIGN
+    assert L.glowq_ec_score(*args(ws=FAKE + 16)) == g.ERR_ALIGN
+    assert L.glowq_ec_score(*args(n=need - 1)) == g.ERR_WORKSPACE
+
+
 def test_path_validates_every_unit_first():
     L = g.lib()
     wq = (g.QWeightC * 1)(_w())
