@@ -432,7 +432,20 @@ def extra_factor_solve(g, sigma32, reps=3, r=64, p=8, q=2):
            "ms": round(t * 1e3, 2), "fp64_TFLOP_per_s": round(flops / t / 1e12, 2),
            "frac_fp64_peak": round(flops / t / 1e12 / 78.6, 4),
            "top_singular_value": float(S[0]), "r_th_singular_value": float(S[-1])}
-    del E, sigma, omega, ws, A, B
+    # the unit's restore score g_ec from the same errors and the solve's singular values
+    ews = torch.empty(int(g.lib().glowq_ec_score_workspace_bytes(m, d)), dtype=torch.uint8, device="cuda")
+    g.ec_score(E, sigma, S, r, workspace=ews)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        sc = g.ec_score(E, sigma, S, r, workspace=ews)
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    t = statistics.median(ts)
+    out["g_ec"] = {"ms": round(t * 1e3, 2), "fp64_TFLOP_per_s": round(m * d * d / t / 1e12, 2),
+                   "frac_fp64_peak": round(m * d * d / t / 1e12 / 78.6, 4), "score": float(sc[2])}
+    del E, sigma, omega, ws, A, B, ews
     torch.cuda.empty_cache()
     return out
 
