@@ -13,8 +13,8 @@
 // counter.  Producers have the lowest workgroup ids and never wait, so they are dispatched before
 // any consumer and always finish; every wait is bounded and raises a flag in the workspace header
 // if it expires.
-// Epoch: every workgroup reads it as its first load and then "arrives" (per-XCD counters, then one
-// counter over the XCDs); the last arrival of the launch resets the counters and advances the
+// Epoch: every workgroup reads it as its first load and then "arrives" (64 slot counters, then one
+// counter over the slots); the last arrival of the launch resets the counters and advances the
 // epoch, so stale pairs never match and no memset is ever needed.  Consumers arrive right after
 // their first loads are issued and producers when their first sums are ready, so the counting
 // overlaps the weight stream instead of lengthening the launch's tail.
@@ -43,10 +43,9 @@ __device__ __forceinline__ const _Float16* pick_bp(const ForwardArgs& a, int i) 
     return b;
 }
 
-// Number of workgroup ids b in [lo, hi) with b % 8 == x.
-__device__ __forceinline__ int count_mod8(int lo, int hi, int x) {
-    const int first = lo + (((x - (lo & 7)) % 8) + 8) % 8;
-    return first < hi ? (hi - 1 - first) / 8 + 1 : 0;
+// Number of workgroup ids b in [0, n) with b % kArriveSlots == s.
+__device__ __forceinline__ int count_slot(int n, int s) {
+    return s < n ? (n - 1 - s) / kArriveSlots + 1 : 0;
 }
 
 typedef unsigned long long u64;
@@ -77,26 +76,26 @@ __device__ __forceinline__ float load_pair(const ForwardArgs& a, const u64* p, u
 
 // Hand-off arrival of this workgroup (thread 0), made after its epoch read has completed.
 __device__ __forceinline__ int arrive(const ForwardArgs& a) {
-    return __hip_atomic_fetch_add(a.sync + kSyncDone + 16 * (blockIdx.x & 7), 1, __ATOMIC_RELAXED,
+    return __hip_atomic_fetch_add(a.sync + kSyncDone + 16 * (blockIdx.x % kArriveSlots), 1, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// With the result of arrive(): the last arrival of its XCD resets that XCD's counter and counts
-// the XCD; returns the previous XCD count, or -1 for every other workgroup.
-__device__ __forceinline__ int arrive_xcd(const ForwardArgs& a, int prev) {
-    const int x = blockIdx.x & 7;
-    if (prev != count_mod8(0, a.n_prod + a.n_tiles, x) - 1) return -1;
-    __hip_atomic_store(a.sync + kSyncDone + 16 * x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// With the result of arrive(): the last arrival of its slot resets the slot's counter and counts
+// the slot; returns the previous slot count, or -1 for every other workgroup.
+__device__ __forceinline__ int arrive_slot(const ForwardArgs& a, int prev) {
+    const int sl = blockIdx.x % kArriveSlots;
+    if (prev != count_slot(a.n_prod + a.n_tiles, sl) - 1) return -1;
+    __hip_atomic_store(a.sync + kSyncDone + 16 * sl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return __hip_atomic_fetch_add(a.sync + kSyncTop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// With the result of arrive_xcd(): the launch's very last arrival resets the top counter and
+// With the result of arrive_slot(): the launch's very last arrival resets the top counter and
 // advances the epoch (read as `epoch` by this thread), skipping 2^32 - 1 so that the tag epoch + 1
 // is never 0.  Every workgroup read the epoch before arriving, so no one in this launch sees the
 // new value.
 __device__ __forceinline__ void finish(const ForwardArgs& a, int top_prev, uint32_t epoch) {
     const int grid = a.n_prod + a.n_tiles;
-    if (top_prev != (grid < kXcds ? grid : kXcds) - 1) return;
+    if (top_prev != (grid < kArriveSlots ? grid : kArriveSlots) - 1) return;
     const uint32_t next = epoch + 1u == 0xFFFFFFFFu ? 0u : epoch + 1u;
     __hip_atomic_store(a.sync + kSyncTop, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(a.sync + kSyncEpoch, (int32_t)next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -188,7 +187,7 @@ __device__ void produce(const ForwardArgs& a, int p) {
         }
         __syncthreads();
     }
-    if (threadIdx.x == 0) finish(a, arrive_xcd(a, arrived), epoch0);
+    if (threadIdx.x == 0) finish(a, arrive_slot(a, arrived), epoch0);
 }
 
 // NTT: 16-token tiles.  RT: 16-row tiles per workgroup, multiplied side by side against the same
@@ -386,15 +385,15 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
                 issue(u, min(i0 + U + u, n_my - 1));
             }
         }
-        // the arrival's count has returned by now: the XCD's last arrival counts the XCD before
+        // the arrival's count has returned by now: the slot's last arrival counts the slot before
         // the drain rather than at the tail
-        if (hand && threadIdx.x == 0) top_prev = arrive_xcd(args, arrived);
+        if (hand && threadIdx.x == 0) top_prev = arrive_slot(args, arrived);
         // drain
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (i0 + u < n_my) compute(u, i0 + u);
     } else if (hand && threadIdx.x == 0) {
-        top_prev = arrive_xcd(args, arrived);
+        top_prev = arrive_slot(args, arrived);
     }
 
     // correction epilogue on the matrix cores: acc += A_i[rows][32 kb .. +32) R[tokens][32 kb .. +32)^T

@@ -42,7 +42,7 @@ def test_buffer_sizes():
     assert L.glowq_q_bytes(16, 100) == 0 and L.glowq_q_bytes(0, 128) == 0
     assert L.glowq_workspace_bytes(0, 64, 1) == 0
     assert L.glowq_workspace_bytes(4, 0, 1) == 0
-    hdr = 2048  # synchronisation words of the decode hand-off
+    hdr = 8192  # synchronisation words of the decode hand-off
     r256 = lambda n: (n + 255) // 256 * 256
     # the fixed decode area ((fp32, tag) pairs for T <= 64, r <= 256, 8 projections, 8 copies),
     # then for calls that may take the prefill path (T > 16) the projection in fp16 (r padded to

@@ -15,7 +15,7 @@ from oracle import solve as S
 
 # workspace header: synchronisation words of the decode hand-off (int32 word 0: the epoch; every
 # other word is back to zero after each call)
-WS_HEADER = 2048
+WS_HEADER = 8192
 
 pytestmark = pytest.mark.gpu
 
