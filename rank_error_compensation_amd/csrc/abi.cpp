@@ -96,9 +96,10 @@ int validate(const Call& c, void* workspace, size_t ws_bytes) {
     return GLOWQ_OK;
 }
 
-// Below this many 64 x 128 tiles the prefill launch takes 64 x 64 tiles: twice the workgroups,
-// each wave one 16-row tile, always 4 wave groups (the tile count stays under 256).  LLaMA-3.1-8B
-// QKV group at T = 64 (48 tiles of 64 x 128): 35.8 -> 29.7 us per call.
+// Below this many 64 x 128 tiles the prefill launch takes 64 x 64 tiles (twice the workgroups,
+// each wave one 16-row tile, always 4 wave groups), and below this many of those 32 x 64 tiles
+// (the tile count stays under 256 either way).  LLaMA-3.1-8B QKV group at T = 64 (48 tiles of
+// 64 x 128): 35.8 us per call, 29.6 us with 64 x 64 tiles, 24.3 us with 32 x 64.
 constexpr int64_t kPrefillHalfRowTiles = 128;
 
 // Prefill tiles of the call for a tile of 16 tt tokens x 64 rr rows.
@@ -124,6 +125,10 @@ void choose_prefill_shape(const Call& c, int& tt, int& rr, int& ks) {
     if (n < kPrefillHalfRowTiles) {  // too few workgroups to stream the weights: 64 x 64 tiles
         rr = 1;
         n = prefill_tiles(c, 4, 1);
+        if (n < kPrefillHalfRowTiles) {  // and still too few: 32 x 64 tiles
+            tt = 2;
+            n = prefill_tiles(c, 2, 1);
+        }
     }
     ks = n <= 256 ? 4 : (n <= 512 ? 2 : 1);
 }

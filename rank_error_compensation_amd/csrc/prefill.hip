@@ -413,9 +413,12 @@ hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(prefill_wide_kernel, grid, block, 2 * 8 * 4 * 64 * sizeof(u4), stream, a);
         return hipGetLastError();
     }
-    if (a.tile_tt == 4 && a.tile_rr == 1) {  // small grids: 64 x 64 tiles, 4 wave groups
-        if (a.tile_ks != 4) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((prefill_kernel<4, 1, 4>), grid, dim3(1024), 0, stream, a);
+    if (a.tile_rr == 1) {  // small grids: 64 or 32 tokens x 64 rows, 4 wave groups
+        if (a.tile_ks != 4 || (a.tile_tt != 4 && a.tile_tt != 2)) return hipErrorInvalidValue;
+        if (a.tile_tt == 4)
+            hipLaunchKernelGGL((prefill_kernel<4, 1, 4>), grid, dim3(1024), 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_kernel<2, 1, 4>), grid, dim3(1024), 0, stream, a);
         return hipGetLastError();
     }
     if (a.tile_tt != 4 || a.tile_rr != 2) return hipErrorInvalidValue;

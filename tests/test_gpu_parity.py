@@ -196,10 +196,10 @@ def test_decode_narrow_k_split(T):
 
 @pytest.mark.parametrize("T", [70, 130])
 def test_prefill_small_grid_half_row_tiles(T):
-    """Prefill calls with fewer than 128 tiles of 64 tokens x 128 rows take 64 x 64 tiles (one
-    16-row tile per wave, 4 wave groups splitting the 5 input groups 2 + 1 + 1 + 1): ragged tokens,
-    a 130-row module whose last wave holds a 2-row tile and waves past its end, with and without
-    restore."""
+    """Prefill calls with fewer than 128 tiles of 64 tokens x 128 rows take 64 x 64 tiles, and
+    with fewer than 128 of those 32 x 64 tiles (one 16-row tile per wave, 4 wave groups splitting
+    the 5 input groups 2 + 1 + 1 + 1), as here: ragged tokens, a 130-row module whose last wave
+    holds a 2-row tile and waves past its end, with and without restore."""
     x = W.make_x(T, 640, 1.19, (47, T))
     u = W.make_unit("hr", "group", x, [256, 130, 64], 32, (47, T, 32))
     du = DevUnit(u)
