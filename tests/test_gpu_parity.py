@@ -209,6 +209,19 @@ def test_prefill_small_grid_half_row_tiles(T):
             assert_parity(y, yr, f"T={T} restore={restore} module {i}")
 
 
+def test_prefill_small_grid_64x64_tiles():
+    """A wide group at T = 64 (72 row tiles of 128) with 72 tiles of 64 x 128 and 144 of 64 x 64:
+    the 64 x 64 tiles (4 wave groups), with and without restore."""
+    T = 64
+    x = W.make_x(T, 256, 1.19, (48, T))
+    u = W.make_unit("hr64", "group", x, [4096, 4096, 1024], 32, (48, T, 32))
+    du = DevUnit(u)
+    for restore in (True, False):
+        ys = du.forward(restore=restore)
+        for i, (y, yr) in enumerate(zip(ys, oracle_unit(u, restore=restore))):
+            assert_parity(y, yr, f"restore={restore} module {i}")
+
+
 @pytest.mark.parametrize("T", [1, 5, 100])
 def test_solo_and_layerwise(T):
     keys = (8, T)
