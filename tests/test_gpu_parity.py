@@ -222,6 +222,19 @@ def test_prefill_small_grid_64x64_tiles():
             assert_parity(y, yr, f"restore={restore} module {i}")
 
 
+@pytest.mark.parametrize("T", [40, 64])
+def test_prefill_small_t_wide_group(T):
+    """A wide group at 17-64 tokens with at least 128 tiles of 64 x 128 (two 8200-row modules,
+    the last tile of each ragged): 32-token x 128-row tiles, with and without restore."""
+    x = W.make_x(T, 256, 1.19, (49, T))
+    u = W.make_unit("wg", "group", x, [8200, 8200], 32, (49, T, 32))
+    du = DevUnit(u)
+    for restore in (True, False):
+        ys = du.forward(restore=restore)
+        for i, (y, yr) in enumerate(zip(ys, oracle_unit(u, restore=restore))):
+            assert_parity(y, yr, f"T={T} restore={restore} module {i}")
+
+
 @pytest.mark.parametrize("T", [1, 5, 100])
 def test_solo_and_layerwise(T):
     keys = (8, T)
