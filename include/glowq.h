@@ -50,7 +50,10 @@ extern "C" {
 #define GLOWQ_ERR_WORKSPACE (-5)   /* workspace missing or smaller than required          */
 #define GLOWQ_ERR_HIP (-6)         /* a HIP runtime call or kernel launch failed           */
 #define GLOWQ_ERR_RANGE (-7)       /* repack: a zero point is not an integer in [-1024,1024]
-                                      or a scale is not finite                           */
+                                      or a scale is not finite; solve: Sigma_x not PSD   */
+#define GLOWQ_ERR_HANDOFF (-8)     /* glowq_workspace_status: a bounded wait for the shared
+                                      projection expired in a call since the last check;
+                                      that call's corrected outputs are invalid            */
 
 #define GLOWQ_MAX_MODULES 8
 #define GLOWQ_MAX_RANK 256
@@ -103,15 +106,34 @@ int glowq_dequant(const glowq_qweight* w, void* out_dev, int32_t out_dtype, hipS
 
 /* ---------------------------------------------------------------- forward
  * Workspace bytes for a call with T tokens, rank r and n_proj right projections (1 for a
- * group or solo call, m for the layerwise baseline).  Holds the projection R = X B^T,
+ * group or solo call, m for the layerwise baseline).  Holds the projection R = X B^T (the
+ * cache of key design 4 in the GlowQ paper note: formed once, consumed by every module),
  * synchronisation words and, for 17 to 64 tokens, the fp32 partial outputs of a call whose
- * input groups are split over workgroups.  Zero-fill it once after allocation; every call
- * leaves it reusable.  Returns 0 when no workspace is needed (r == 0 or T == 0).
+ * input groups are split over workgroups.  It must be zero-filled once after allocation
+ * (glowq_workspace_init); every call leaves it reusable.  Returns 0 when no workspace is
+ * needed (r == 0 or T == 0).
  */
 size_t glowq_workspace_bytes(int64_t T, int32_t r, int32_t n_proj);
 
-/* Input-sharing group of m modules (1 <= m <= 8), w[0] the anchor.
- *   x        : fp16 [T][d], the group's shared input (T >= 0; T == 0 is a no-op)
+/* Zero-fill a freshly allocated workspace (device, 256-byte aligned, workspace_bytes >= 8192)
+ * with a fill kernel on `stream` (no memset node, so a captured graph may hold it).  A
+ * workspace that is not zero when first used can hold stale synchronisation counters and
+ * projection tags: the hand-off would then wait for the wrong call and report
+ * GLOWQ_ERR_HANDOFF.  Asynchronous. */
+int glowq_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Hand-off status of a workspace: SYNCHRONISES `stream`, reads the error word that a
+ * correcting decode call raises when one of its bounded waits for the shared projection
+ * expires (its corrected outputs are then wrong), clears the word and returns GLOWQ_OK
+ * (no expiry since the last check or init) or GLOWQ_ERR_HANDOFF.  Allocates nothing; not
+ * for use under graph capture. */
+int glowq_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Input-sharing group of m modules (1 <= m <= 8), w[0] the anchor (GlowQ paper note, key
+ * design 4: the anchor of an input-sharing group computes the projection of the shared right
+ * factor once and every consumer reuses it; the flowchart's last node: each module's output is
+ * its quantised product plus A_i times that projection).
+ *   x        : fp16 [T][d], the group's shared input (T >= 0; T == 0 is a no-op; T d <= 2^30)
  *   w        : host array of m module descriptors, every w[i].k_in == d
  *   b_shared : fp16 [r][d] shared right factor
  *   a        : host array of m device pointers, a[i] fp16 [w[i].n_out][r]
@@ -126,7 +148,8 @@ int glowq_group_forward(const void* x, int64_t T, int64_t d, int32_t m, const gl
                         void* workspace, size_t workspace_bytes, void* const* y,
                         hipStream_t stream);
 
-/* Solo module (o_proj, down_proj): y = X W_hat^T + (X b^T) a^T with its private b fp16
+/* Solo module (o_proj, down_proj; GlowQ paper note, key design 4: modules that share their
+ * input with no other correct on the fly, nothing cached): y = X W_hat^T + (X b^T) a^T with its private b fp16
  * [r][d], a fp16 [n_out][r] and y fp16 [T][n_out]; nothing is kept after the call.  Same
  * rules as glowq_group_forward. */
 int glowq_solo_forward(const void* x, int64_t T, int64_t d, const glowq_qweight* w, const void* b,

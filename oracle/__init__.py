@@ -9,7 +9,8 @@ no code with the HIP library (``rank_error_compensation_amd``), which never impo
   solve     : the offline factor solve and restore scores, used to build exact factors
               for the tiny workload and to pin the inference oracle end to end
 
-Every function is pinned by ``tests/test_oracle_pins.py`` against closed forms, exact
-arithmetic, brute force or special cases; none is marked "parity unpinned".
+Every function is pinned by ``tests/test_oracle_pins.py`` (checks in ``tests/pins.py``)
+against closed forms, exact arithmetic, brute force, special cases or hand-worked values
+(the comparator ``parity_errors`` included); none is marked "parity unpinned".
 """
 from . import glowq_ref, solve  # noqa: F401

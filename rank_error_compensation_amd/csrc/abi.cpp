@@ -21,6 +21,10 @@ constexpr int64_t kMaxD = 1 << 20;
 constexpr int64_t kMaxRows = 1 << 24;
 constexpr int64_t kMaxMomentD = 16384;              // features of a second-moment call
 constexpr int64_t kMaxMomentElems = (int64_t)1 << 31;  // N d (int32 offsets stay in range)
+// Forward calls: the kernels form activation byte offsets T d 2 in 32 bits and number their work
+// tiles in int32; calls past these bounds are rejected before any HIP call.
+constexpr int64_t kMaxActElems = (int64_t)1 << 30;     // T d
+constexpr int64_t kMaxTiles = ((int64_t)1 << 31) - 1;  // 16-token tiles x 16-row tiles
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -66,8 +70,10 @@ int validate(const Call& c, void* workspace, size_t ws_bytes) {
     if (c.T > kMaxT || c.d > kMaxD) return GLOWQ_ERR_UNSUPPORTED;
     if (c.r < 0) return GLOWQ_ERR_SHAPE;
     if (c.r > GLOWQ_MAX_RANK || c.r % 8 != 0) return GLOWQ_ERR_UNSUPPORTED;
+    if (c.T * c.d > kMaxActElems) return GLOWQ_ERR_UNSUPPORTED;
     if (c.w == nullptr || c.y == nullptr) return GLOWQ_ERR_INVALID_ARG;
     if (c.T > 0 && c.x == nullptr) return GLOWQ_ERR_INVALID_ARG;
+    int64_t tiles16 = 0;
     for (int i = 0; i < c.m; ++i) {
         const glowq_qweight& w = c.w[i];
         if (w.q == nullptr || w.sz == nullptr) return GLOWQ_ERR_INVALID_ARG;
@@ -75,7 +81,10 @@ int validate(const Call& c, void* workspace, size_t ws_bytes) {
         if (w.n_out < 1 || w.k_in != c.d) return GLOWQ_ERR_SHAPE;
         if (w.n_out > kMaxRows) return GLOWQ_ERR_UNSUPPORTED;
         if (!aligned(w.q, 16) || !aligned(w.sz, 16) || !aligned(c.y[i], 16)) return GLOWQ_ERR_ALIGN;
+        tiles16 += ceil_div(w.n_out, 16);
     }
+    // every launch has at most (16-token tiles) x (16-row tiles) work tiles
+    if (ceil_div(c.T, 16) * tiles16 > kMaxTiles) return GLOWQ_ERR_UNSUPPORTED;
     if (c.x != nullptr && !aligned(c.x, 16)) return GLOWQ_ERR_ALIGN;
     if (c.correct) {
         if (c.a == nullptr || c.b == nullptr) return GLOWQ_ERR_INVALID_ARG;
@@ -280,12 +289,34 @@ const char* glowq_status_string(int status) {
         case GLOWQ_ERR_UNSUPPORTED: return "GLOWQ_ERR_UNSUPPORTED: configuration not supported";
         case GLOWQ_ERR_WORKSPACE: return "GLOWQ_ERR_WORKSPACE: workspace missing or too small";
         case GLOWQ_ERR_HIP: return "GLOWQ_ERR_HIP: HIP runtime or launch failure";
-        case GLOWQ_ERR_RANGE: return "GLOWQ_ERR_RANGE: value out of range (zero point, scale, or a matrix that is not positive definite)";
+        case GLOWQ_ERR_RANGE: return "GLOWQ_ERR_RANGE: value out of range (zero point, scale, or a matrix that is not positive semidefinite)";
+        case GLOWQ_ERR_HANDOFF: return "GLOWQ_ERR_HANDOFF: a bounded wait for the projection expired; outputs since the last check are invalid";
         default: return "GLOWQ_ERR_UNKNOWN";
     }
 }
 
-int glowq_version(void) { return 100; }
+int glowq_version(void) { return 200; }
+
+int glowq_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (workspace == nullptr) return GLOWQ_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return GLOWQ_ERR_ALIGN;
+    if (workspace_bytes < kWsHeader) return GLOWQ_ERR_WORKSPACE;
+    return launch_fill_zero(workspace, workspace_bytes, stream) == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
+}
+
+int glowq_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (workspace == nullptr) return GLOWQ_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256)) return GLOWQ_ERR_ALIGN;
+    if (workspace_bytes < kWsHeader) return GLOWQ_ERR_WORKSPACE;
+    int32_t* word = static_cast<int32_t*>(workspace) + kSyncError;
+    int32_t h = 0;
+    if (hipMemcpyAsync(&h, word, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    if (h == 0) return GLOWQ_OK;
+    if (launch_flag_clear(word, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    return GLOWQ_ERR_HANDOFF;
+}
 
 size_t glowq_q_bytes(int64_t n_out, int64_t k_in) {
     if (n_out < 1 || k_in < kGroup || k_in % kGroup != 0 || n_out > kMaxRows || k_in > kMaxD) return 0;

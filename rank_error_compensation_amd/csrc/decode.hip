@@ -162,6 +162,10 @@ __device__ void produce(const ForwardArgs& a, int p) {
         if (first) {
             if (threadIdx.x == 0) {
                 ptag = epoch0 + 1u;
+                // the epoch read must be complete before this workgroup's arrival can count: a
+                // relaxed load and a relaxed atomic to another address are not ordered, so wait
+                // for the load here (the compiler may not move memory operations across this)
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 arrived = arrive(a);
             }
             first = false;
@@ -367,8 +371,8 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
     // the workgroup arrives once thread 0 holds the epoch (every wave reads it after the barrier)
     int arrived = 0, top_prev = -1;
     if (hand) {
-        if (threadIdx.x == 0) tag_lds = epoch0 + 1u;
-        __syncthreads();
+        if (threadIdx.x == 0) tag_lds = epoch0 + 1u;  // needs the epoch load's value
+        __syncthreads();  // a fence: the arrival below is not moved above the epoch's use
         if (threadIdx.x == 0) arrived = arrive(args);
     } else if (XLDS) {
         __syncthreads();

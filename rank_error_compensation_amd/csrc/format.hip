@@ -61,6 +61,15 @@ __global__ __launch_bounds__(256) void repack_sz_kernel(const _Float16* __restri
 
 __global__ void flag_clear_kernel(int32_t* flag) { *flag = 0; }
 
+// Zero-fill of n bytes: 16-byte stores in a grid-stride loop, the last n % 16 bytes by thread 0.
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint8_t* __restrict__ p, size_t n) {
+    const size_t n16 = n / 16;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+        reinterpret_cast<u4*>(p)[i] = u4{0u, 0u, 0u, 0u};
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        for (size_t i = n16 * 16; i < n; ++i) p[i] = 0;
+}
+
 // One thread per device-layout word: eight consecutive inputs of one row.
 template <int DTYPE>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ qd,
@@ -98,6 +107,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
 
 hipError_t launch_flag_clear(int32_t* flag, hipStream_t stream) {
     hipLaunchKernelGGL(flag_clear_kernel, dim3(1), dim3(1), 0, stream, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
+    const size_t n16 = bytes / 16;
+    const size_t want = (n16 + 255) / 256;
+    const unsigned grid = (unsigned)(want < 1 ? 1 : (want > 2048 ? 2048 : want));
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, static_cast<uint8_t*>(p), bytes);
     return hipGetLastError();
 }
 

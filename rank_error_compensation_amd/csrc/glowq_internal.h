@@ -215,6 +215,7 @@ hipError_t launch_repack(const uint32_t* qc, const _Float16* s, const _Float16* 
                          int64_t k_in, uint8_t* q_dev, uint8_t* sz_dev, int32_t* flag,
                          hipStream_t stream);
 hipError_t launch_flag_clear(int32_t* flag, hipStream_t stream);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* sz, int64_t n_out, int64_t k_in, void* out,
                           int dtype, hipStream_t stream);
 hipError_t launch_proj_prefill(const ProjArgs& p, hipStream_t stream);

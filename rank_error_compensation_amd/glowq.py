@@ -24,6 +24,7 @@ ERR_UNSUPPORTED = -4
 ERR_WORKSPACE = -5
 ERR_HIP = -6
 ERR_RANGE = -7
+ERR_HANDOFF = -8
 
 DTYPE_F32 = 0
 DTYPE_F16 = 1
@@ -55,6 +56,8 @@ EXPORTS = {
     "glowq_repack": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "glowq_dequant": (ctypes.c_int, [ctypes.POINTER(QWeightC), _vp, _i32, _vp]),
     "glowq_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "glowq_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
+    "glowq_workspace_status": (ctypes.c_int, [_vp, _sz, _vp]),
     "glowq_group_forward": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(QWeightC), _vp,
                                            ctypes.POINTER(_vp), _i32, _i32, _vp, _sz,
                                            ctypes.POINTER(_vp), _vp]),
@@ -267,11 +270,26 @@ def workspace_bytes(T: int, r: int, n_proj: int = 1) -> int:
     return int(lib().glowq_workspace_bytes(T, r, n_proj))
 
 
-def make_workspace(T: int, r: int, n_proj: int = 1, device=None) -> Optional[torch.Tensor]:
-    n = workspace_bytes(T, r, n_proj)
+def init_workspace(ws: torch.Tensor, stream=None) -> torch.Tensor:
+    """Zero-fill a workspace with the library's fill kernel (glowq_workspace_init)."""
+    check(lib().glowq_workspace_init(_ptr(ws), ws.numel(), _stream(stream)), "glowq_workspace_init")
+    return ws
+
+
+def workspace_status(ws: torch.Tensor, stream=None) -> int:
+    """glowq_workspace_status: synchronises, returns OK or ERR_HANDOFF and clears the word."""
+    st = int(lib().glowq_workspace_status(_ptr(ws), ws.numel(), _stream(stream)))
+    if st not in (OK, ERR_HANDOFF):
+        check(st, "glowq_workspace_status")
+    return st
+
+
+def make_workspace(T: int, r: int, n_proj: int = 1, device=None, min_bytes: int = 0) -> Optional[torch.Tensor]:
+    n = max(workspace_bytes(T, r, n_proj), min_bytes)
     if n == 0:
         return None
-    return torch.zeros(n, dtype=torch.uint8, device=device or torch.device("cuda"))
+    ws = torch.empty(n, dtype=torch.uint8, device=device or torch.device("cuda"))
+    return init_workspace(ws)
 
 
 def _arr(kind, items):
@@ -370,7 +388,7 @@ class PathPlan:
         self.arr = arr
         need = max([workspace_bytes(u.x.shape[0], u.r, 1) for u in self.units if u.restore] + [0])
         dev = self.units[0].x.device if self.units else torch.device("cuda")
-        self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        self.workspace = make_workspace(1, 8, 1, dev, min_bytes=need)
 
     def run(self, stream=None) -> None:
         check(lib().glowq_path_forward(self.arr, len(self.units), _ptr(self.workspace),

@@ -42,13 +42,28 @@ class DevUnit:
         restore = self.unit.restore if restore is None else restore
         r = self.r if r is None else r
         x = self.x if x is None else x
+        ws = g.make_workspace(x.shape[0], r, 1, x.device) if (restore and r > 0) else None
         if self.unit.kind == "solo":
-            return [g.solo_forward(x, self.w[0], self.b, self.a[0], r, restore)]
-        return g.group_forward(x, self.w, self.b, self.a, r, restore)
+            ys = [g.solo_forward(x, self.w[0], self.b, self.a[0], r, restore, workspace=ws)]
+        else:
+            ys = g.group_forward(x, self.w, self.b, self.a, r, restore, workspace=ws)
+        assert_handoff_ok(ws)
+        return ys
 
     def forward_layerwise(self, restore=True):
         g = glowq()
-        return g.layerwise_forward(self.x, self.w, self.b_lw, self.a, self.r, restore)
+        ws = g.make_workspace(self.x.shape[0], self.r, len(self.w), self.x.device) if (restore and self.r > 0) else None
+        ys = g.layerwise_forward(self.x, self.w, self.b_lw, self.a, self.r, restore, workspace=ws)
+        assert_handoff_ok(ws)
+        return ys
+
+
+def assert_handoff_ok(ws):
+    """No bounded wait of the projection hand-off expired in the calls on `ws` since the last
+    check (glowq_workspace_status, which synchronises and clears the word)."""
+    if ws is not None:
+        g = glowq()
+        assert g.workspace_status(ws) == g.OK, "a hand-off wait expired"
 
 
 def oracle_unit(unit, restore=None, layerwise=False, rows=None, r=None):

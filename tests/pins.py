@@ -441,8 +441,39 @@ def check_scores(sol):
         assert sol.topk_restore(scores, k) == want, k
 
 
+# ------------------------------------------------------------------ the parity comparator
+def check_parity_errors(ref):
+    """The comparator behind every GPU parity assertion, against values worked by hand: the
+    relative Frobenius error ||y - y_ref||_F / ||y_ref||_F and the largest elementwise error
+    over max|y_ref| (the two bounds of the parity bar), with a negative difference, several
+    rows, and a zero reference, where the bound becomes an equality."""
+    def near(a, b):
+        assert abs(a - b) <= 1e-15 * max(1.0, abs(b)), (a, b)
+
+    e = ref.parity_errors(np.array([[3.0, 4.5]]), np.array([[3.0, 4.0]]))
+    near(e["rel_fro"], 0.1)            # |0.5| / 5
+    near(e["max_abs_rel"], 0.125)      # 0.5 / 4
+    e = ref.parity_errors(np.array([[-2.5, 1.0], [0.0, 0.0]]), np.array([[-2.0, 1.0], [0.0, 0.0]]))
+    near(e["rel_fro"], 0.5 / math.sqrt(5.0))
+    near(e["max_abs_rel"], 0.25)       # |-0.5| / |-2|
+    y_ref = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]])
+    y = y_ref + np.array([[0.0, 0.1], [-0.3, 0.0], [0.0, 0.0]])
+    e = ref.parity_errors(y, y_ref)
+    near(e["rel_fro"], math.sqrt((0.1 ** 2 + 0.3 ** 2) / 91.0))
+    near(e["max_abs_rel"], 0.3 / 6.0)
+    z = np.zeros((2, 3))
+    e = ref.parity_errors(z, z)
+    assert e["rel_fro"] == 0.0 and e["max_abs_rel"] == 0.0, e
+    zt = z.copy()
+    zt[1, 2] = 1e-30
+    e = ref.parity_errors(zt, z)
+    assert math.isinf(e["rel_fro"]) and math.isinf(e["max_abs_rel"]), e
+    e = ref.parity_errors(y_ref, y_ref)
+    assert e["rel_fro"] == 0.0 and e["max_abs_rel"] == 0.0, e
+
+
 ALL_REF_CHECKS = [check_dequant_exhaustive, check_dequant_golden, check_restore_off,
                   check_associativity_small_int, check_bruteforce, check_row_independence,
-                  check_path_mask]
+                  check_path_mask, check_parity_errors]
 ALL_SOL_CHECKS = [check_eckart_young, check_isotropic, check_usage_weighted_risk, check_qr_core,
                   check_cholesky_vs_symmetric, check_randomized_svd, check_scores, check_second_moment]

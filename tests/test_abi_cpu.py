@@ -28,8 +28,8 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings_and_version():
     L = g.lib()
-    assert L.glowq_version() == 100
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    assert L.glowq_version() == 200
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert L.glowq_status_string(code).startswith(b"GLOWQ_")
     assert L.glowq_status_string(12345) == b"GLOWQ_ERR_UNKNOWN"
 
@@ -102,9 +102,31 @@ def call_group(x=FAKE, T=4, d=256, m=1, w=None, b=FAKE, a=None, r=8, restore=1, 
     (dict(ws=None), g.ERR_WORKSPACE),
     (dict(ws_bytes=100), g.ERR_WORKSPACE),
     (dict(ws=FAKE + 16), g.ERR_ALIGN),
+    # activation offsets T d 2 are 32-bit in the kernels: T d above 2^30 is refused
+    (dict(T=1 << 19, d=4096), g.ERR_UNSUPPORTED),
+    (dict(T=262144, d=8192), g.ERR_UNSUPPORTED),
+    (dict(T=(1 << 30) // 4096 + 1, d=4096), g.ERR_UNSUPPORTED),
+    # int32 work-tile numbering: (T / 16) x (rows / 16) tiles above 2^31 - 1 are refused
+    (dict(T=1 << 16, d=128, m=8, w=[_w(n_out=1 << 24, k_in=128)] * 8), g.ERR_UNSUPPORTED),
 ])
 def test_group_validation_rejects_before_any_hip_call(kw, code):
     assert call_group(**kw) == code
+
+
+def test_activation_block_bound_rejects_before_any_hip_call():
+    # restore off, no workspace: T d one row above 2^30 is still refused before any launch
+    L = g.lib()
+    wc = (g.QWeightC * 1)(_w(n_out=16, k_in=4096))
+    assert L.glowq_group_forward(FAKE, (1 << 30) // 4096 + 1, 4096, 1, wc, None, None, 0, 0, None, 0,
+                                 (ctypes.c_void_p * 1)(FAKE), None) == g.ERR_UNSUPPORTED
+
+
+def test_workspace_init_and_status_validate():
+    L = g.lib()
+    for fn in (L.glowq_workspace_init, L.glowq_workspace_status):
+        assert fn(None, 1 << 20, None) == g.ERR_INVALID_ARG
+        assert fn(FAKE + 16, 1 << 20, None) == g.ERR_ALIGN
+        assert fn(FAKE, 8191, None) == g.ERR_WORKSPACE
 
 
 def test_restore_off_needs_no_factors_and_t0_is_noop():

@@ -140,6 +140,36 @@ def moment_token_gram(X):
     return G[:X.shape[1], :X.shape[1]] if G.shape[0] >= X.shape[1] else np.pad(G, (0, X.shape[1] - G.shape[0]))
 
 
+def parity_by_test_norm(y_test, y_ref):
+    yt, yr = G._f64(y_test), G._f64(y_ref)
+    d = np.abs(yt - yr)
+    return dict(rel_fro=float(np.linalg.norm(d) / np.linalg.norm(yt)), max_abs_rel=float(d.max() / np.abs(yt).max()))
+
+
+def parity_mean_not_max(y_test, y_ref):
+    yt, yr = G._f64(y_test), G._f64(y_ref)
+    d = np.abs(yt - yr)
+    nref, mref = np.linalg.norm(yr), np.abs(yr).max()
+    return dict(rel_fro=float(np.linalg.norm(d) / nref) if nref > 0 else 0.0,
+                max_abs_rel=float(d.mean() / mref) if mref > 0 else 0.0)
+
+
+def parity_no_abs(y_test, y_ref):
+    yt, yr = G._f64(y_test), G._f64(y_ref)
+    d = yt - yr
+    nref, mref = np.linalg.norm(yr), yr.max()
+    return dict(rel_fro=float(np.linalg.norm(d) / nref) if nref > 0 else 0.0,
+                max_abs_rel=float(d.max() / mref) if mref > 0 else 0.0)
+
+
+def parity_zero_ref_passes(y_test, y_ref):
+    yt, yr = G._f64(y_test), G._f64(y_ref)
+    d = np.abs(yt - yr)
+    nref, mref = np.linalg.norm(yr), np.abs(yr).max()
+    return dict(rel_fro=float(np.linalg.norm(d) / nref) if nref > 0 else 0.0,
+                max_abs_rel=float(d.max() / mref) if mref > 0 else 0.0)
+
+
 REF_MUTANTS = {
     "dequant_plus_z": dict(dequant=dequant_plus_z),
     "dequant_group64": dict(dequant=dequant_group64),
@@ -151,6 +181,10 @@ REF_MUTANTS = {
     "group_ignores_restore": dict(group_forward=group_ignores_restore),
     "group_transposed_b": dict(group_forward=group_transposed_b),
     "path_inverted_mask": dict(path_forward=path_inverted_mask),
+    "parity_by_test_norm": dict(parity_errors=parity_by_test_norm),
+    "parity_mean_not_max": dict(parity_errors=parity_mean_not_max),
+    "parity_no_abs": dict(parity_errors=parity_no_abs),
+    "parity_zero_ref_passes": dict(parity_errors=parity_zero_ref_passes),
 }
 
 SOL_MUTANTS = {
