@@ -259,7 +259,7 @@ size_t glowq_solve_workspace_bytes(int64_t m, int64_t d, int32_t k, int32_t r);
  * then a randomized SVD with the caller's test matrix and q power iterations, balanced factors
  * and the lift back to the original variables:
  *   e_dev     : fp64 [m][d] stacked errors W_i - W_hat_i of the group's modules
- *   sigma_dev : fp64 [d][d] Sigma_x, symmetric positive definite
+ *   sigma_dev : fp64 [d][d] Sigma_x, symmetric positive semidefinite
  *   omega_dev : fp64 [d][k] test matrix (k = r + p oversampled columns, r <= k <= min(96, d))
  *   r, q      : rank, power iterations (0 <= q <= 16)
  *   a_dev     : fp64 [m][r] output A = U_r S_r^{1/2} (rows of module i at its offset in E_cat)
@@ -267,11 +267,15 @@ size_t glowq_solve_workspace_bytes(int64_t m, int64_t d, int32_t k, int32_t r);
  *               the same matrix, without a triangular solve)
  *   s_dev     : fp64 [r] output, the r largest singular values of the whitened error
  * Whitening uses the Cholesky factor L of Sigma_x (Sigma_x = L L^T); the product A B is the same
- * for every square root of Sigma_x.  The range finder runs on E_cat L directly (the same bases
+ * for every square root of Sigma_x.  A singular Sigma_x (key design 3 of the paper note lifts with
+ * the pseudo-inverse then): pivots at or below 1e-10 of their column's diagonal entry are zero,
+ * their columns of L are dropped, and B = S_r^{1/2} V_r^T L^+ -- the rows of B are projected onto
+ * the range of Sigma_x (the minimum-norm lift); at most 96 such null directions
+ * (GLOWQ_ERR_UNSUPPORTED beyond).  The range finder runs on E_cat L directly (the same bases
  * as on the QR-reduced core R_e L, up to the left factor Q_e that A carries), without forming
  * it: its products are taken as products with E_cat and with L.  All arithmetic in
  * fp64.  This is an offline step: it SYNCHRONISES `stream` and returns GLOWQ_ERR_RANGE if
- * Sigma_x is not positive definite.  workspace: at least glowq_solve_workspace_bytes(m, d, k, r)
+ * Sigma_x is not positive semidefinite (a pivot below -1e-10 of its diagonal entry).  workspace: at least glowq_solve_workspace_bytes(m, d, k, r)
  * bytes, 256-byte aligned, overwritten. */
 int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double* sigma_dev,
                         const double* omega_dev, int32_t r, int32_t k, int32_t q, double* a_dev, double* b_dev,

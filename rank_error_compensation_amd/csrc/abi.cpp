@@ -7,6 +7,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "glowq.h"
 #include "glowq_internal.h"
@@ -482,10 +483,18 @@ static size_t solve_part_doubles(int64_t m, int64_t d, int32_t k) {
     return (size_t)kSolveSplitMax * (size_t)(m > d ? m : d) * (size_t)k;
 }
 
+// pseudo-inverse lift: the original diagonal of Sigma_x, the dropped-pivot marks and their list,
+// the null-space basis and its orthonormalisation scratch, B times that basis
+static size_t solve_null_doubles(int64_t d) {
+    return (size_t)d + ((size_t)d + 1u) / 2u + (size_t)kSolveMaxNull / 2u + 2u * (size_t)d * kSolveMaxNull +
+           3u * (size_t)kSolveMaxNull * kSolveMaxNull;
+}
+
 size_t glowq_solve_workspace_bytes(int64_t m, int64_t d, int32_t k, int32_t r) {
     if (m < 1 || d < 1 || r < 1 || k < r || k > kSolveMaxK || k > d || m > kMaxRows || d > kMaxMomentD) return 0;
     const size_t n = (size_t)d * d + (size_t)m * k + 3u * (size_t)d * k + 2u * (size_t)k * k + (size_t)k +
-                     (size_t)(m > d ? m : d) * k + (size_t)k * k + 2u + solve_part_doubles(m, d, k);
+                     (size_t)(m > d ? m : d) * k + (size_t)k * k + 2u + solve_part_doubles(m, d, k) +
+                     solve_null_doubles(d);
     return round256(n * sizeof(double));
 }
 
@@ -514,6 +523,14 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
     double* part = Ri + (size_t)k * k;             // split-K partial products
     const int64_t part_cap = (int64_t)solve_part_doubles(m, d, k);
     int* flag = reinterpret_cast<int*>(part + part_cap);
+    double* dg = part + part_cap + 2;                                       // diag(Sigma_x)
+    int* drop = reinterpret_cast<int*>(dg + d);                             // dropped pivots [d]
+    int* list = drop + 2 * (((size_t)d + 1u) / 2u);                         // their indices
+    double* Nb = reinterpret_cast<double*>(list + kSolveMaxNull);           // null basis [d][n0]
+    double* Nt = Nb + (size_t)d * kSolveMaxNull;                            // orth scratch [d][n0]
+    double* Ng = Nt + (size_t)d * kSolveMaxNull;                            // [n0][n0]
+    double* Nr = Ng + (size_t)kSolveMaxNull * kSolveMaxNull;                // [n0][n0]
+    double* BN = Nr + (size_t)kSolveMaxNull * kSolveMaxNull;                // B N [r][n0]
     auto gemm = [&](int Mm, int Nn, int Kk, const double* A, int lda, int ta, const double* B, int ldb, int tb,
                     double* C, int ldc) {
         GemmArgs g{};
@@ -525,7 +542,24 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
     // with E_cat and one with L (a d x k block), E~ X = E_cat (L X), E~^T Y = L^T (E_cat^T Y).
     bool ok = hipMemcpyAsync(L, sigma_dev, (size_t)d * d * sizeof(double), hipMemcpyDeviceToDevice, stream) ==
               hipSuccess;
-    ok = ok && launch_cholesky(L, D, flag, stream) == hipSuccess;           // Sigma_x = L L^T
+    ok = ok && launch_cholesky(L, D, flag, dg, drop, stream) == hipSuccess;  // Sigma_x = L L^T
+    if (!ok) return GLOWQ_ERR_HIP;
+    // not positive semidefinite: stop; numerically zero pivots: their columns of L are zero and the
+    // lift below projects B onto the range of Sigma_x (pseudo-inverse)
+    int h = 0;
+    std::vector<int> dropped((size_t)d);
+    if (hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipMemcpyAsync(dropped.data(), drop, (size_t)d * sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return GLOWQ_ERR_HIP;
+    if (h) return GLOWQ_ERR_RANGE;
+    std::vector<int> nulls;
+    for (int i = 0; i < D; ++i)
+        if (dropped[(size_t)i]) nulls.push_back(i);
+    const int n0 = (int)nulls.size();
+    if (n0 > kSolveMaxNull) return GLOWQ_ERR_UNSUPPORTED;
+    if (n0 > 0 && hipMemcpyAsync(list, nulls.data(), (size_t)n0 * sizeof(int), hipMemcpyHostToDevice, stream) != hipSuccess)
+        return GLOWQ_ERR_HIP;
     ok = ok && gemm(D, k, D, L, D, 0, omega_dev, k, 0, W, k);               // L Omega
     ok = ok && gemm(M, k, D, e_dev, D, 0, W, k, 0, Y, k);                   // Y = E~ Omega
     ok = ok && launch_orth(Y, M, k, T, G, Ri, part, part_cap, stream) == hipSuccess;
@@ -548,11 +582,25 @@ int glowq_solve_factors(const double* e_dev, int64_t m, int64_t d, const double*
     // E~ = E_cat L: the lift needs no triangular solve
     ok = ok && gemm(r, D, k, V, k, 1, P, k, 1, b_dev, D);                   // U_r^T P^T
     ok = ok && launch_colscale(b_dev, D, r, D, w, 1, 1, stream) == hipSuccess;  // rows times S_r^{-1/2}
+    if (ok && n0 > 0) {
+        // pseudo-inverse lift: B = S_r^{1/2} V_r^T L^+ = S_r^{-1/2} U_r^T Q^T E_cat (L L^+), and L L^+ is
+        // the orthogonal projector onto range(Sigma_x) = I - N N^T for an orthonormal basis N of the
+        // null space: B <- B - (B N) N^T
+        ok = launch_null_vectors(L, D, drop, list, n0, Nb, stream) == hipSuccess;
+        ok = ok && launch_orth(Nb, D, n0, Nt, Ng, Nr, part, part_cap, stream) == hipSuccess;
+        if (ok) {
+            GemmArgs g1{};  // B N
+            g1.M = r, g1.N = n0, g1.K = D, g1.A = b_dev, g1.lda = D, g1.ta = 0, g1.B = Nb, g1.ldb = n0, g1.tb = 0;
+            g1.C = BN, g1.ldc = n0, g1.alpha = 1.0, g1.beta = 0.0;
+            ok = launch_gemm(g1, stream) == hipSuccess;
+            GemmArgs g2{};  // B - (B N) N^T
+            g2.M = r, g2.N = D, g2.K = n0, g2.A = BN, g2.lda = n0, g2.ta = 0, g2.B = Nb, g2.ldb = n0, g2.tb = 1;
+            g2.C = b_dev, g2.ldc = D, g2.alpha = -1.0, g2.beta = 1.0;
+            ok = ok && launch_gemm(g2, stream) == hipSuccess;
+        }
+    }
     if (!ok) return GLOWQ_ERR_HIP;
-    int h = 0;
-    if (hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess) return GLOWQ_ERR_HIP;
-    if (hipStreamSynchronize(stream) != hipSuccess) return GLOWQ_ERR_HIP;
-    return h ? GLOWQ_ERR_RANGE : GLOWQ_OK;
+    return hipStreamSynchronize(stream) == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
 }
 
 size_t glowq_ec_score_workspace_bytes(int64_t m, int64_t d) {

@@ -50,6 +50,10 @@ constexpr int kMaxScoreUnits = 4096;
 
 // Offline factor solve (fp64).
 constexpr int kSolveMaxK = 96;  // r + p columns of the range finder (LDS of the small steps)
+constexpr int kMaxSolveD = 16384;  // features of a factor solve
+// Most null directions of Sigma_x the solve projects out of B (the pseudo-inverse lift), the
+// columns of one orthonormalisation.
+constexpr int kSolveMaxNull = kSolveMaxK;
 struct GemmArgs {                // C = alpha op(A) op(B) + beta C, row-major
     int32_t M, N, K;
     const double* A;
@@ -71,7 +75,9 @@ constexpr int kGemmWant = 512;
 constexpr int kGemmMinK = 128;
 constexpr int kSolveSplitMax = 16;  // partial-product buffer of the solve: 16 max(m, d) k doubles
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream);
-hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream);
+hipError_t launch_cholesky(double* S, int d, int* flag, double* dg, int* drop, hipStream_t stream);
+hipError_t launch_null_vectors(const double* L, int d, const int* drop, const int* list, int n0, double* N,
+                               hipStream_t stream);
 hipError_t launch_orth(double* X, int n, int k, double* T, double* G, double* Rinv, double* part, int64_t part_cap,
                        hipStream_t stream);
 hipError_t launch_jacobi(const double* G, int k, double* w, double* V, hipStream_t stream);

@@ -179,9 +179,24 @@ hipError_t launch_gemm(const GemmArgs& g0, hipStream_t stream) {
 // --------------------------------------------------------------------------- Cholesky
 constexpr int kSmallThreads = 1024;  // one-workgroup factorisations: threads per workgroup
 
+// Semidefinite Cholesky: a pivot at or below kPsdTol times the original diagonal entry dg[j] of
+// its column is numerically zero.  For a positive semidefinite matrix the rest of such a column is
+// then zero as well (|S_ij|^2 <= S_ii S_jj): the column of L is set to zero and the index marked
+// dropped, so that L L^T = S still holds and L's nonzero columns span the range of S.  A pivot
+// below -kPsdTol dg[j] (or a negative diagonal entry) means S is not positive semidefinite and
+// sets *flag.
+constexpr double kPsdTol = 1e-10;
+
+__global__ __launch_bounds__(256) void diag_kernel(const double* S, int d, double* dg) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < d) dg[i] = S[(size_t)i * d + i];
+}
+
 // Factor the nb x nb diagonal block at (n0, n0) of the lower triangle of S (row stride ld) in
-// place; a non-positive pivot sets *flag.
-__global__ __launch_bounds__(kSmallThreads) void chol_diag_kernel(double* S, int ld, int n0, int nb, int* flag) {
+// place, dropping numerically zero pivots (drop[n0 + j] = 1, column zero); a negative one sets
+// *flag.
+__global__ __launch_bounds__(kSmallThreads) void chol_diag_kernel(double* S, int ld, int n0, int nb, int* flag,
+                                                                  const double* dg, int* drop) {
     __shared__ double a[64][65];
     if (n0 == 0 && threadIdx.x == 0) *flag = 0;  // the first block clears the flag before any pivot
     for (int idx = threadIdx.x; idx < nb * nb; idx += kSmallThreads) {
@@ -197,19 +212,21 @@ __global__ __launch_bounds__(kSmallThreads) void chol_diag_kernel(double* S, int
     const int c = threadIdx.x & 63, i0 = threadIdx.x >> 6;
     for (int j = 0; j < nb; ++j) {
         const double v = a[j][j];
-        const bool ok = v > 0.0;
-        const double inv = ok ? 1.0 / v : 1.0;
-        if (c > j && c < nb) {
-            const double acj = a[c][j] * inv;
+        const double dj = dg[n0 + j];
+        const bool ok = v > kPsdTol * dj;                      // a live column
+        const bool bad = dj < 0.0 || v < -kPsdTol * dj;        // not positive semidefinite
+        if (ok && c > j && c < nb) {
+            const double acj = a[c][j] / v;
             for (int i = c + ((i0 - c) & (RS - 1)); i < nb; i += RS) a[i][c] -= a[i][j] * acj;  // rows i >= c
         }
         __syncthreads();
-        const double piv = ok ? sqrt(v) : 1.0;
+        const double piv = ok ? sqrt(v) : 0.0;
         if (threadIdx.x == 0) {
-            if (!ok) atomicOr(flag, 1);
+            if (bad) atomicOr(flag, 1);
             a[j][j] = piv;
+            drop[n0 + j] = ok ? 0 : 1;
         }
-        for (int i = j + 1 + (int)threadIdx.x; i < nb; i += kSmallThreads) a[i][j] /= piv;
+        for (int i = j + 1 + (int)threadIdx.x; i < nb; i += kSmallThreads) a[i][j] = ok ? a[i][j] / piv : 0.0;
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < nb * nb; idx += kSmallThreads) {
@@ -231,7 +248,8 @@ __global__ __launch_bounds__(128) void chol_panel_kernel(double* S, int ld, int 
         lt[j][i] = j <= i ? S[(size_t)(n0 + i) * ld + n0 + j] : 0.0;
     }
     __syncthreads();
-    if (threadIdx.x < 64) rd[threadIdx.x] = 1.0 / lt[threadIdx.x][threadIdx.x];
+    // a dropped column (zero pivot) gives a zero column of L below it
+    if (threadIdx.x < 64) rd[threadIdx.x] = lt[threadIdx.x][threadIdx.x] > 0.0 ? 1.0 / lt[threadIdx.x][threadIdx.x] : 0.0;
     __syncthreads();
     const int row = n0 + nb + blockIdx.x * 128 + threadIdx.x;
     if (row >= n) return;
@@ -254,6 +272,50 @@ __global__ __launch_bounds__(256) void zero_upper_kernel(double* S, int ld, int 
     if (idx >= (size_t)n * n) return;
     const int i = (int)(idx / n), j = (int)(idx % n);
     if (j > i) S[(size_t)i * ld + j] = 0.0;
+}
+
+// Null space of a semidefinite Cholesky factor: for each dropped index j = list[b] the vector v with
+// L^T v = 0, v_j = 1 and v_i = 0 for i > j, by back substitution on the upper triangle L^T:
+// v_i = -(sum_{i < l <= j} L_li v_l) / L_ii for a live i, 0 for a dropped i.  Column-oriented: once
+// v_l is known, every i < l gains L_li v_l (row l of L, contiguous), and the owner of index l - 1
+// finishes v_{l-1}; one barrier per step.  The vectors are linearly independent (each ends at its
+// own j) and span the null space of L^T, i.e. of S = L L^T.  Output column b of N [d][n0].
+constexpr int kNullThreads = 1024;
+constexpr int kNullPer = kMaxSolveD / kNullThreads;  // indices per thread
+
+__global__ __launch_bounds__(kNullThreads) void null_vec_kernel(const double* L, int d, const int* drop,
+                                                               const int* list, int n0, double* N) {
+    __shared__ double vsh[2];
+    const int b = blockIdx.x, j = list[b];
+    const int t = threadIdx.x;
+    double acc[kNullPer];
+#pragma unroll
+    for (int q = 0; q < kNullPer; ++q) acc[q] = 0.0;
+    for (int i = t; i < d; i += kNullThreads)
+        if (i >= j) N[(size_t)i * n0 + b] = i == j ? 1.0 : 0.0;
+    double v = 1.0;
+    for (int l = j; l >= 1; --l) {
+        if (v != 0.0) {
+            const double* row = L + (size_t)l * d;
+#pragma unroll
+            for (int q = 0; q < kNullPer; ++q) {
+                const int i = t + kNullThreads * q;
+                if (i < l) acc[q] += row[i] * v;
+            }
+        }
+        const int o = l - 1;
+        if (t == o % kNullThreads) {
+            double a = 0.0;
+#pragma unroll
+            for (int q = 0; q < kNullPer; ++q)
+                if (q == o / kNullThreads) a = acc[q];
+            const double vn = drop[o] ? 0.0 : -a / L[(size_t)o * d + o];
+            vsh[l & 1] = vn;
+            N[(size_t)o * n0 + b] = vn;
+        }
+        __syncthreads();
+        v = vsh[l & 1];
+    }
 }
 
 // --------------------------------------------------------------------------- small dense steps
@@ -489,8 +551,9 @@ static hipError_t chol_update(double* S, int d, int c0, int l0, int kw, int ncol
 // the first half's diagonal block and the rows below it, the second half's columns updated by the
 // first half, the second half's diagonal block and rows below, then one trailing update with both
 // halves (K = 128: half the passes over the trailing matrix of a 64-column blocking).
-hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream) {
-    hipError_t e = hipSuccess;
+hipError_t launch_cholesky(double* S, int d, int* flag, double* dg, int* drop, hipStream_t stream) {
+    hipLaunchKernelGGL(diag_kernel, dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, stream, S, d, dg);
+    hipError_t e = hipGetLastError();
     for (int n0 = 0; n0 < d && e == hipSuccess; n0 += 128) {
         const int nb2 = min(128, d - n0);
         for (int h = 0; h < nb2 && e == hipSuccess; h += 64) {
@@ -499,7 +562,8 @@ hipError_t launch_cholesky(double* S, int d, int* flag, hipStream_t stream) {
                 e = chol_update(S, d, c0, n0, 64, nb, stream);  // second half's columns, first half's L
                 if (e != hipSuccess) break;
             }
-            hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kSmallThreads), 0, stream, S, d, c0, nb, flag);
+            hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(kSmallThreads), 0, stream, S, d, c0, nb, flag, dg,
+                               drop);
             const int rest = d - c0 - nb;
             if (rest > 0)  // a full 64-wide block has rows below it
                 hipLaunchKernelGGL(chol_panel_kernel, dim3((unsigned)ceil_div(rest, 128)), dim3(128), 0, stream, S, d,
@@ -536,6 +600,13 @@ hipError_t launch_orth(double* X, int n, int k, double* T, double* G, double* Ri
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_null_vectors(const double* L, int d, const int* drop, const int* list, int n0, double* N,
+                               hipStream_t stream) {
+    if (d > kMaxSolveD) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(null_vec_kernel, dim3((unsigned)n0), dim3(kNullThreads), 0, stream, L, d, drop, list, n0, N);
+    return hipGetLastError();
 }
 
 hipError_t launch_jacobi(const double* G, int k, double* w, double* V, hipStream_t stream) {

@@ -278,6 +278,31 @@ def check_exact_rank(ref, sol, singular=False):
     assert np.linalg.norm(AB1 - AB2) <= 1e-10 * np.linalg.norm(AB1)
 
 
+def check_pinv_lift(sol):
+    """Singular Sigma_x with an error that also has a part outside its range (the case the
+    pseudo-inverse lift of key design 3 exists for): the Moore-Penrose inverse of the symmetric
+    root agrees with numpy's SVD-based pinv; B's rows lie in range(Sigma_x) (the minimum-norm
+    lift); the factors equal those of the error projected onto that range (whitening cannot see
+    the rest); and the whitened residual is the Eckart-Young optimum."""
+    rng = np.random.default_rng(41)
+    d, n_zero, r, m = 96, 12, 5, 60
+    Q, lam = _cov(d, 1.19, 17, n_zero=n_zero)
+    S_half = sol.sqrt_psd(Q, lam)
+    S_lift = sol.pinv_sqrt_psd(Q, lam)
+    assert np.linalg.norm(S_lift - np.linalg.pinv(S_half)) <= 1e-9 * np.linalg.norm(S_lift)
+    E = rng.standard_normal((m, d))
+    A_list, B, s = sol.whitened_factors([E], S_half, S_lift, r)
+    N = Q[:, d - n_zero:]                      # orthonormal basis of the null space
+    assert np.linalg.norm(B @ N) <= 1e-12 * np.linalg.norm(B)
+    P = np.eye(d) - N @ N.T
+    A2, B2, s2 = sol.whitened_factors([E @ P], S_half, S_lift, r)
+    AB, AB2 = np.vstack(A_list) @ B, np.vstack(A2) @ B2
+    assert np.linalg.norm(AB - AB2) <= 1e-10 * np.linalg.norm(AB)
+    assert np.max(np.abs(s - s2)) <= 1e-12 * s[0]
+    resid = np.linalg.norm((E - AB) @ S_half) ** 2
+    assert abs(resid - float(np.sum(s[r:] ** 2))) <= 1e-10 * float(np.sum(s ** 2))
+
+
 def check_eckart_young(sol):
     """Whitened residual of the shared factors equals sum_{j>r} sigma_j^2 of the whitened
     error (closed form), and no other rank-r pair tried does better."""
@@ -476,4 +501,5 @@ ALL_REF_CHECKS = [check_dequant_exhaustive, check_dequant_golden, check_restore_
                   check_associativity_small_int, check_bruteforce, check_row_independence,
                   check_path_mask, check_parity_errors]
 ALL_SOL_CHECKS = [check_eckart_young, check_isotropic, check_usage_weighted_risk, check_qr_core,
-                  check_cholesky_vs_symmetric, check_randomized_svd, check_scores, check_second_moment]
+                  check_cholesky_vs_symmetric, check_randomized_svd, check_scores, check_second_moment,
+                  check_pinv_lift]

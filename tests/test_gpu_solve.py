@@ -79,6 +79,54 @@ def test_matches_oracle_with_gap(m, d, r, p, q):
     assert np.max(np.abs(Sv - s_ref)) <= 1e-9 * s_ref[0]
 
 
+@pytest.mark.parametrize("d,n_zero,m,r,p,q", [(384, 20, 200, 16, 16, 2), (256, 3, 96, 8, 8, 1), (160, 96, 64, 4, 4, 1)])
+def test_singular_sigma_pseudo_inverse_lift(d, n_zero, m, r, p, q):
+    """Singular Sigma_x (n_zero zero eigenvalues, null directions spread over several Cholesky blocks)
+    and an error with a part in its null space, which whitening cannot see: the solve succeeds,
+    B's rows lie in range(Sigma_x) (pseudo-inverse lift), and A B equals the oracle's
+    S_r^{1/2} V_r^T Sigma_x^{+1/2} product -- here the error's part inside the range, whose
+    whitened form has rank r0 <= r (so the randomized solve is exact)."""
+    g = glowq()
+    rng = np.random.default_rng(d + n_zero)
+    Q, R = np.linalg.qr(rng.standard_normal((d, d)))
+    Q = Q * np.sign(np.diag(R))
+    lam = np.arange(1, d + 1, dtype=np.float64) ** (-1.19)
+    lam *= d / lam.sum()
+    lam[d - n_zero:] = 0.0
+    Sigma = (Q * lam) @ Q.T
+    Sigma = 0.5 * (Sigma + Sigma.T)
+    Nq = Q[:, d - n_zero:]
+    P = np.eye(d) - Nq @ Nq.T
+    r0 = r - 2
+    U0, _ = np.linalg.qr(rng.standard_normal((m, r0)))
+    V0, _ = np.linalg.qr(P @ rng.standard_normal((d, r0)))
+    E_in = (U0 * np.linspace(2.0, 0.5, r0)) @ V0.T          # rows in range(Sigma_x)
+    E = E_in + rng.standard_normal((m, n_zero)) @ Nq.T       # plus a null-space part
+    A, B, Sv = run(g, E, Sigma, r, p, q, seed=5)
+    # rows of B with nonzero singular values lie in range(Sigma_x); the last r - r0 rows belong to
+    # numerically zero singular values (S^{-1/2} amplifies rounding there, and A's columns are ~0)
+    assert np.linalg.norm(B[:r0] @ Nq) <= 1e-9 * np.linalg.norm(B[:r0])
+    assert np.linalg.norm(A @ B @ Nq) <= 1e-9 * np.linalg.norm(A @ B)
+    A_list, B_ref, s_ref = S.whitened_factors([E], S.sqrt_psd(Q, lam), S.pinv_sqrt_psd(Q, lam), r)
+    P_ref = np.vstack(A_list) @ B_ref
+    assert rel(P_ref, E_in) <= 1e-9                          # the oracle's product: E's range part
+    assert rel(A @ B, P_ref) <= 1e-9
+    assert np.max(np.abs(Sv[:r0] - s_ref[:r0])) <= 1e-9 * s_ref[0]
+
+
+def test_too_many_null_directions_is_unsupported():
+    g = glowq()
+    d, m, r = 256, 32, 4
+    rng = np.random.default_rng(3)
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    lam = np.ones(d)
+    lam[:100] = 0.0
+    Sigma = (Q * lam) @ Q.T
+    with pytest.raises(g.GlowQError) as ei:
+        run(g, rng.standard_normal((m, d)), 0.5 * (Sigma + Sigma.T), r, 4, 0, seed=1)
+    assert ei.value.status == g.ERR_UNSUPPORTED
+
+
 def test_not_positive_definite_is_reported():
     g = glowq()
     d, m, r = 64, 32, 4

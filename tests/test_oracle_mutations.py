@@ -117,6 +117,14 @@ def whitened_unwhitened(E_list, S_half, S_half_lift, r):
     return SOL.split_rows(A, n_outs), B, S
 
 
+def pinv_identity_on_null(Q, lam, rtol=1e-12):
+    # a generalised inverse of the root that is not the Moore-Penrose one (1 on the null space)
+    lam = np.asarray(lam, dtype=np.float64)
+    cut = rtol * float(lam.max())
+    inv = np.where(lam > cut, 1.0 / np.sqrt(np.where(lam > cut, lam, 1.0)), 1.0)
+    return (Q * inv) @ Q.T
+
+
 def topk_lowest(scores, k):
     order = sorted(range(len(scores)), key=lambda u: (float(scores[u]), u))
     chosen = set(order[:k])
@@ -192,6 +200,7 @@ SOL_MUTANTS = {
     "unbalanced_full_s": dict(whitened_factors=whitened_full_s),
     "no_whitening": dict(whitened_factors=whitened_unwhitened),
     "topk_lowest": dict(topk_restore=topk_lowest),
+    "pinv_identity_on_null": dict(pinv_sqrt_psd=pinv_identity_on_null),
     "moment_centred": dict(second_moment=moment_centred),
     "moment_unbiased": dict(second_moment=moment_unbiased),
     "moment_token_gram": dict(second_moment=moment_token_gram),
