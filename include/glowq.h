@@ -156,6 +156,24 @@ int glowq_solo_forward(const void* x, int64_t T, int64_t d, const glowq_qweight*
                        const void* a, int32_t r, int32_t restore, void* workspace,
                        size_t workspace_bytes, void* y, hipStream_t stream);
 
+/* Allocation-free variant of glowq_group_forward, for callers that cannot allocate (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels,
+ * with the library's own scratch in place of the caller's workspace.  The scratch is a
+ * file-scope device array of glowq_static_scratch_bytes() bytes (16 MiB), one per GPU, held
+ * until the process ends; the first correcting call on a device looks up its address and
+ * zero-fills it with a kernel on `stream`.  No call allocates (no hipMalloc / hipFree).
+ * Calls whose workspace need, glowq_workspace_bytes(T, r, 1), exceeds the scratch return
+ * GLOWQ_ERR_WORKSPACE before any HIP call (every decode call, T <= 64, fits; prefill calls fit
+ * up to about T = 2048 at r = 64).  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents: calls that overlap in time on one GPU (two streams, or two
+ * threads) race and give wrong results; order them on one stream or synchronise between them.
+ * Hand-off expiries are flagged in the scratch and are not reported by this entry point.
+ * Arguments and results as glowq_group_forward. */
+size_t glowq_static_scratch_bytes(void);
+int glowq_group_forward_static(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
+                               const void* b_shared, const void* const* a, int32_t r, int32_t restore,
+                               void* const* y, hipStream_t stream);
+
 /* Layerwise baseline (the comparison of the paper's latency table): every module i has
  * its own right factor b[i] fp16 [r][d] and its own projection X b[i]^T, computed in the
  * same kernels.  workspace_bytes >= glowq_workspace_bytes(T, r, m). */

@@ -7,6 +7,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "glowq.h"
@@ -659,6 +660,63 @@ int glowq_solo_forward(const void* x, int64_t T, int64_t d, const glowq_qweight*
     const int v = validate(c, workspace, workspace_bytes);
     if (v != GLOWQ_OK) return v;
     return run(c, workspace, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free variant
+// Scratch of glowq_group_forward_static: a file-scope device array of kStaticScratchBytes, one copy
+// per GPU, held until the process ends.  Host code never passes the array's name to a kernel (on
+// the host it only stands for the symbol): its device address is taken once per device with
+// hipGetSymbolAddress and that pointer is used everywhere.
+namespace {
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+// Device address of the current device's scratch; the first call on a device looks it up and
+// zero-fills the array with a kernel on `stream` (stream-ordered before this call's kernels).
+int static_scratch(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GLOWQ_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GLOWQ_ERR_HIP;
+        if (launch_fill_zero(p, kStaticScratchBytes, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GLOWQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t glowq_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+int glowq_group_forward_static(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
+                               const void* b_shared, const void* const* a, int32_t r, int32_t restore,
+                               void* const* y, hipStream_t stream) {
+    const void* bp[1] = {b_shared};
+    const Call c = make_group(x, T, d, m, w, bp, 1, a, r, restore, y);
+    // the scratch stands in for the workspace: validate against its size with a stand-in
+    // address (aligned, never dereferenced), then substitute the device pointer
+    void* const stand_in = reinterpret_cast<void*>((uintptr_t)256);
+    const int v = validate(c, stand_in, kStaticScratchBytes);
+    if (v != GLOWQ_OK) return v;
+    if (T == 0) return GLOWQ_OK;
+    void* ws = nullptr;
+    if (c.correct) {
+        const int s = static_scratch(stream, &ws);
+        if (s != GLOWQ_OK) return s;
+    }
+    return run(c, ws, stream);
 }
 
 int glowq_layerwise_forward(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,

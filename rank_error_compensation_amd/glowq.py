@@ -61,6 +61,9 @@ EXPORTS = {
     "glowq_group_forward": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(QWeightC), _vp,
                                            ctypes.POINTER(_vp), _i32, _i32, _vp, _sz,
                                            ctypes.POINTER(_vp), _vp]),
+    "glowq_static_scratch_bytes": (_sz, []),
+    "glowq_group_forward_static": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(QWeightC), _vp,
+                                                  ctypes.POINTER(_vp), _i32, _i32, ctypes.POINTER(_vp), _vp]),
     "glowq_solo_forward": (ctypes.c_int, [_vp, _i64, _i64, ctypes.POINTER(QWeightC), _vp, _vp, _i32,
                                           _i32, _vp, _sz, _vp, _vp]),
     "glowq_layerwise_forward": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(QWeightC),
@@ -317,6 +320,21 @@ def group_forward(x: torch.Tensor, weights: Sequence[QWeight], b: Optional[torch
     check(lib().glowq_group_forward(_ptr(x), x.shape[0], x.shape[1], m, wc, _ptr(b), ac, r,
                                     int(bool(restore)), _ptr(workspace), ws_n, yc, _stream(stream)),
           "glowq_group_forward")
+    return y
+
+
+def group_forward_static(x: torch.Tensor, weights: Sequence[QWeight], b: Optional[torch.Tensor],
+                         a: Sequence[torch.Tensor], r: int, restore: bool = True,
+                         y: Optional[List[torch.Tensor]] = None, stream=None) -> List[torch.Tensor]:
+    """glowq_group_forward_static: no workspace argument; the library's per-device scratch."""
+    m = len(weights)
+    y = _outs(x, weights, y)
+    wc = _arr(QWeightC, [w.c() for w in weights])
+    ac = _arr(_vp, [t.data_ptr() for t in a]) if a else None
+    yc = _arr(_vp, [t.data_ptr() for t in y])
+    check(lib().glowq_group_forward_static(_ptr(x), x.shape[0], x.shape[1], m, wc, _ptr(b), ac, r,
+                                           int(bool(restore)), yc, _stream(stream)),
+          "glowq_group_forward_static")
     return y
 
 
