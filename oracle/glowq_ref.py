@@ -124,6 +124,94 @@ def path_forward(layers: Dict[int, list], mask: Sequence[bool]) -> Dict[int, Lis
     return out
 
 
+# --------------------------------------------------------------------------- W4A8
+# The arXiv page (Tables 14 and 15) and the paper note's results bullets run the method with 8-bit
+# activations as well ("W4A8"): the quantised weight product then takes 8-bit activations while
+# the correction branch stays high precision.  The pages give no activation quantiser; this oracle
+# takes the plainest one: per token (row of X), symmetric, round-to-nearest-even to the integers
+# -127..127, the scale a / 127 with a = max_k |x[t, k]|.  Every step of it is fp32 (the fp16
+# inputs are exact in fp32; the division and the rounding are IEEE operations), so that the
+# integer codes are decided in one fixed precision; a zero row gets scale 0 and codes 0.
+def quantize_x_int8(x):
+    """Per-token symmetric int8 codes of fp16 activations: (codes int64 [T][d] in -127..127,
+    scales fp32 [T]); x ~ scale[t] * codes[t]."""
+    xf = _np(x).astype(np.float32)
+    amax = np.abs(xf).max(axis=1) if xf.size else np.zeros(xf.shape[0], np.float32)
+    scale = (amax.astype(np.float32) / np.float32(127.0)).astype(np.float32)
+    codes = np.zeros(xf.shape, dtype=np.int64)
+    nz = scale > 0
+    if np.any(nz):
+        ratio = (xf[nz] / scale[nz, None]).astype(np.float32)
+        codes[nz] = np.clip(np.rint(ratio), -127, 127).astype(np.int64)
+    return codes, scale
+
+
+def group_forward_w4a8(x, w_hats: Sequence[np.ndarray], b, a_list, restore: bool = True
+                       ) -> List[np.ndarray]:
+    """W4A8 group forward: y_i = scale_t * (codes_t . W_hat_i^T) + [restore and r > 0]
+    (X B^T) A_i^T, with (codes, scale) = quantize_x_int8(X), the quantised product in fp64
+    (exact products of integers and exact weights), and the shared projection R = X B^T formed
+    once from the fp16 activations (the high-precision branch)."""
+    codes, scale = quantize_x_int8(x)
+    xq = codes.astype(np.float64)
+    sc = scale.astype(np.float64)[:, None]
+    outs = [sc * (xq @ wh.T) for wh in w_hats]
+    r = 0 if b is None else _np(b).shape[0]
+    if restore and r > 0:
+        R = shared_projection(x, b)
+        outs = [y + R @ _f64(a).T for y, a in zip(outs, a_list)]
+    return outs
+
+
+def bruteforce_group_w4a8(x, q_packed_list, s_list, z_list, n_outs, k_in, b, a_list,
+                          restore: bool = True) -> List[np.ndarray]:
+    """W4A8 element by element: per token the code of every input from its own fp32 division
+    and rounding, the quantised sum over groups of s * sum (q - z) * code (nibbles read from the
+    packed words), times the token's scale, plus the correction; correctly rounded sums (fsum).
+    Tiny shapes only."""
+    xs = _np(x).astype(np.float32)
+    T = xs.shape[0]
+    r = 0 if b is None else _np(b).shape[0]
+    R = None
+    if restore and r > 0:
+        bb = _f64(b)
+        R = [[math.fsum(float(xs[t, k]) * float(bb[j, k]) for k in range(k_in)) for j in range(r)]
+             for t in range(T)]
+    codes, scales = [], []
+    for t in range(T):
+        amax = np.float32(0.0)
+        for k in range(k_in):
+            amax = max(amax, np.float32(abs(xs[t, k])))
+        sc = np.float32(amax / np.float32(127.0))
+        row = []
+        for k in range(k_in):
+            if sc == 0:
+                row.append(0)
+            else:
+                v = float(np.rint(np.float32(xs[t, k] / sc)))
+                row.append(int(min(127.0, max(-127.0, v))))
+        codes.append(row)
+        scales.append(float(sc))
+    outs = []
+    for qp, s, z, O, a in zip(q_packed_list, s_list, z_list, n_outs, a_list):
+        words = _np(qp).astype(np.int64) & 0xFFFFFFFF
+        s64, z64 = _f64(s), _f64(z)
+        aa = None if R is None else _f64(a)
+        y = np.zeros((T, O))
+        for t in range(T):
+            for o in range(O):
+                terms = []
+                for k in range(k_in):
+                    q = (int(words[o, k // 8]) >> (4 * (k % 8))) & 0xF
+                    g = k // GROUP
+                    terms.append(scales[t] * float(s64[o, g]) * (q - float(z64[o, g])) * codes[t][k])
+                if R is not None:
+                    terms.extend(R[t][j] * float(aa[o, j]) for j in range(r))
+                y[t, o] = math.fsum(terms)
+        outs.append(y)
+    return outs
+
+
 # --------------------------------------------------------------------------- brute force
 def bruteforce_group(x, q_packed_list, s_list, z_list, n_outs, k_in, b, a_list,
                      restore: bool = True) -> List[np.ndarray]:

@@ -466,6 +466,74 @@ def check_scores(sol):
         assert sol.topk_restore(scores, k) == want, k
 
 
+# ------------------------------------------------------------------ W4A8 (8-bit activations)
+def check_w4a8_quantizer_hand(ref):
+    """Hand-worked per-token codes in exact fp32 cases: a row whose max is 127 (scale 1, ties to
+    even: -63.5 -> -64, 62.5 -> 62, 1.5 -> 2, -0.5 -> 0), a zero row (scale 0, codes 0) and a row
+    whose max is 254 (scale 2: 63.5 -> 64, -31.5 -> -32, 0.5 -> 0, 3 -> 2)."""
+    x = np.array([[127, -63.5, 62.5, 0.25, -0.5, 1.5, -127, 3],
+                  [0, 0, 0, 0, 0, 0, 0, 0],
+                  [254, 127, -63, 1, 6, -254, 0.5, 5]], dtype=np.float16)
+    codes, scale = ref.quantize_x_int8(x)
+    assert [float(v) for v in scale] == [1.0, 0.0, 2.0], scale
+    assert codes[0].tolist() == [127, -64, 62, 0, 0, 2, -127, 3], codes[0]
+    assert codes[1].tolist() == [0] * 8
+    assert codes[2].tolist() == [127, 64, -32, 0, 3, -127, 0, 2], codes[2]
+
+
+def check_w4a8_quantizer_invariants(ref):
+    """Round to nearest: |x - scale * code| <= scale / 2 (up to the fp32 rounding of the ratio);
+    codes in -127..127; every nonzero row's largest |x| maps to +-127."""
+    rng = np.random.default_rng(61)
+    x = (rng.standard_normal((9, 384)) * np.exp(rng.uniform(-6, 6, (9, 1)))).astype(np.float16)
+    codes, scale = ref.quantize_x_int8(x)
+    xf = x.astype(np.float64)
+    assert codes.min() >= -127 and codes.max() <= 127
+    err = np.abs(xf - scale.astype(np.float64)[:, None] * codes)
+    assert np.all(err <= scale.astype(np.float64)[:, None] * (0.5 + 1e-6))
+    amax_idx = np.abs(xf).argmax(axis=1)
+    assert np.all(np.abs(codes[np.arange(9), amax_idx]) == 127)
+
+
+def _w4a8_problem(seed, T=3, d=256, n_outs=(24, 16), r=4):
+    p = tiny_problem(seed, T=T, d=d, n_outs=n_outs, r=r)
+    rng = np.random.default_rng(seed + 100)
+    p.x = (rng.standard_normal((T, d)) * 3).astype(np.float16)
+    return p
+
+
+def check_w4a8_bruteforce(ref):
+    """The numpy W4A8 forward against element-by-element fsum loops (each code from its own fp32
+    division and rounding; products exact in fp64), restore on and off."""
+    p = _w4a8_problem(71)
+    wh = _w_hats(ref, p)
+    for restore in (True, False):
+        ys = ref.group_forward_w4a8(p.x, wh, p.b, p.a, restore=restore)
+        bf = ref.bruteforce_group_w4a8(p.x, p.words, p.s, p.z, p.n_outs, p.d, p.b, p.a, restore=restore)
+        for y, yb in zip(ys, bf):
+            assert np.linalg.norm(y - yb) <= 1e-13 * np.linalg.norm(yb), restore
+
+
+def check_w4a8_lossless_and_scale(ref):
+    """Integer activations whose row maximum is 127 quantise losslessly (scale 1, codes = X): the
+    W4A8 forward then equals the pinned W4A16 forward exactly.  Doubling X (exact in fp16) keeps
+    the codes, doubles the scales and so exactly doubles the quantised product."""
+    p = _w4a8_problem(73)
+    rng = np.random.default_rng(5)
+    xi = rng.integers(-127, 128, size=(3, p.d)).astype(np.float64)
+    xi[:, 7] = 127.0
+    x16 = xi.astype(np.float16)
+    wh = _w_hats(ref, p)
+    y8 = ref.group_forward_w4a8(x16, wh, p.b, p.a, restore=True)
+    y16 = ref.group_forward(x16, wh, p.b, p.a, restore=True)
+    for a, b in zip(y8, y16):
+        assert np.array_equal(a, b)
+    base = ref.group_forward_w4a8(p.x, wh, None, p.a, restore=False)
+    dbl = ref.group_forward_w4a8((p.x.astype(np.float32) * 2).astype(np.float16), wh, None, p.a, restore=False)
+    for a, b in zip(base, dbl):
+        assert np.array_equal(2.0 * a, b)
+
+
 # ------------------------------------------------------------------ the parity comparator
 def check_parity_errors(ref):
     """The comparator behind every GPU parity assertion, against values worked by hand: the
@@ -499,7 +567,8 @@ def check_parity_errors(ref):
 
 ALL_REF_CHECKS = [check_dequant_exhaustive, check_dequant_golden, check_restore_off,
                   check_associativity_small_int, check_bruteforce, check_row_independence,
-                  check_path_mask, check_parity_errors]
+                  check_path_mask, check_parity_errors, check_w4a8_quantizer_hand,
+                  check_w4a8_quantizer_invariants, check_w4a8_bruteforce, check_w4a8_lossless_and_scale]
 ALL_SOL_CHECKS = [check_eckart_young, check_isotropic, check_usage_weighted_risk, check_qr_core,
                   check_cholesky_vs_symmetric, check_randomized_svd, check_scores, check_second_moment,
                   check_pinv_lift]

@@ -178,6 +178,52 @@ def parity_zero_ref_passes(y_test, y_ref):
                 max_abs_rel=float(d.max() / mref) if mref > 0 else 0.0)
 
 
+def _quant_with(x, rnd=np.rint, per_tensor=False, div=127.0, lo=-127):
+    xf = G._np(x).astype(np.float32)
+    amax = np.abs(xf).max() * np.ones(xf.shape[0], np.float32) if per_tensor else np.abs(xf).max(axis=1)
+    scale = (amax.astype(np.float32) / np.float32(div)).astype(np.float32)
+    codes = np.zeros(xf.shape, dtype=np.int64)
+    nz = scale > 0
+    codes[nz] = np.clip(rnd((xf[nz] / scale[nz, None]).astype(np.float32)), lo, -lo).astype(np.int64)
+    return codes, scale
+
+
+def quant_half_away(x):
+    return _quant_with(x, rnd=lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5))
+
+
+def quant_per_tensor(x):
+    return _quant_with(x, per_tensor=True)
+
+
+def quant_div128(x):
+    return _quant_with(x, div=128.0)
+
+
+def quant_unsigned_range(x):
+    # an 8-bit range taken as 255 steps (the unsigned width) on a symmetric code
+    return _quant_with(x, div=255.0, lo=-255)
+
+
+def w4a8_no_scale(x, w_hats, b, a_list, restore=True):
+    codes, _ = G.quantize_x_int8(x)
+    outs = [codes.astype(np.float64) @ wh.T for wh in w_hats]
+    if restore and b is not None and G._np(b).shape[0] > 0:
+        R = G._f64(x) @ G._f64(b).T
+        outs = [y + R @ G._f64(a).T for y, a in zip(outs, a_list)]
+    return outs
+
+
+def w4a8_corr_on_codes(x, w_hats, b, a_list, restore=True):
+    codes, scale = G.quantize_x_int8(x)
+    xh = scale.astype(np.float64)[:, None] * codes
+    outs = [xh @ wh.T for wh in w_hats]
+    if restore and b is not None and G._np(b).shape[0] > 0:
+        R = xh @ G._f64(b).T  # correction from the dequantised activations
+        outs = [y + R @ G._f64(a).T for y, a in zip(outs, a_list)]
+    return outs
+
+
 REF_MUTANTS = {
     "dequant_plus_z": dict(dequant=dequant_plus_z),
     "dequant_group64": dict(dequant=dequant_group64),
@@ -193,6 +239,12 @@ REF_MUTANTS = {
     "parity_mean_not_max": dict(parity_errors=parity_mean_not_max),
     "parity_no_abs": dict(parity_errors=parity_no_abs),
     "parity_zero_ref_passes": dict(parity_errors=parity_zero_ref_passes),
+    "quant_half_away": dict(quantize_x_int8=quant_half_away),
+    "quant_per_tensor": dict(quantize_x_int8=quant_per_tensor),
+    "quant_div128": dict(quantize_x_int8=quant_div128),
+    "quant_unsigned_range": dict(quantize_x_int8=quant_unsigned_range),
+    "w4a8_no_scale": dict(group_forward_w4a8=w4a8_no_scale),
+    "w4a8_corr_on_codes": dict(group_forward_w4a8=w4a8_corr_on_codes),
 }
 
 SOL_MUTANTS = {
