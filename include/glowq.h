@@ -182,6 +182,26 @@ int glowq_layerwise_forward(const void* x, int64_t T, int64_t d, int32_t m, cons
                             void* workspace, size_t workspace_bytes, void* const* y,
                             hipStream_t stream);
 
+/* ---------------------------------------------------------------- W4A8
+ * The same group forward with 8-bit activations for the quantised product (the W4A8 rows of the
+ * GlowQ arXiv page, Tables 14 and 15: INT4-g128 weights, 8-bit activations, the correction
+ * applied as in W4A16).  Per token t (a row of X): scale_t = max_k |x[t, k]| / 127 (fp32),
+ * code[t, k] = round-half-even(x[t, k] / scale_t) clamped to -127..127 (fp32 division), all
+ * codes 0 for a zero row.  Result:
+ *   y_i = fp16_RNE(scale_t * (code X W_hat_i^T) + (X b_shared^T) a[i]^T)
+ * with the quantised product summed exactly per 128-input group on the int8 matrix cores
+ * (nibble products minus z times the group's code sum), scaled in fp32; the projection is formed
+ * once per call from the fp16 activations (the high-precision branch).  d <= 16384.
+ * Workspace (always needed when T > 0), glowq_w4a8_workspace_bytes(T, d, r or 0) bytes,
+ * 256-byte aligned, overwritten: the codes int8 [T][d] (within each 128-input group, position
+ * 16 (4 m + g) + 8 h + b holds input 64 m + 32 h + 8 g + {0,4,1,5,2,6,3,7}[b]), then the code
+ * sums int32 [T][d / 128], the scales fp32 [T] (each part starting at a multiple of 256 bytes),
+ * then for a correcting call the projection.  Other rules as glowq_group_forward. */
+size_t glowq_w4a8_workspace_bytes(int64_t T, int64_t d, int32_t r);
+int glowq_group_forward_w4a8(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
+                             const void* b_shared, const void* const* a, int32_t r, int32_t restore,
+                             void* workspace, size_t workspace_bytes, void* const* y, hipStream_t stream);
+
 /* ---------------------------------------------------------------- decoder-layer schedule
  * A sequence of units run in order on one stream: per decoder layer the QKV group, the
  * o_proj solo, the gate/up group and the down_proj solo, each with the restore bit of the

@@ -63,6 +63,7 @@ struct Call {
     int32_t r;
     bool correct;
     void* const* y;
+    bool w4a8;  // 8-bit activations (glowq_group_forward_w4a8)
 };
 
 int validate(const Call& c, void* workspace, size_t ws_bytes) {
@@ -88,6 +89,7 @@ int validate(const Call& c, void* workspace, size_t ws_bytes) {
     // every launch has at most (16-token tiles) x (16-row tiles) work tiles
     if (ceil_div(c.T, 16) * tiles16 > kMaxTiles) return GLOWQ_ERR_UNSUPPORTED;
     if (c.x != nullptr && !aligned(c.x, 16)) return GLOWQ_ERR_ALIGN;
+    if (c.w4a8 && c.d > kW4a8MaxD) return GLOWQ_ERR_UNSUPPORTED;
     if (c.correct) {
         if (c.a == nullptr || c.b == nullptr) return GLOWQ_ERR_INVALID_ARG;
         for (int i = 0; i < c.m; ++i)
@@ -98,8 +100,12 @@ int validate(const Call& c, void* workspace, size_t ws_bytes) {
             if (!aligned(c.a[i], 16)) return GLOWQ_ERR_ALIGN;
         for (int p = 0; p < c.n_proj; ++p)
             if (!aligned(c.b[p], 16)) return GLOWQ_ERR_ALIGN;
-        if (c.T > 0) {
-            const size_t need = glowq_workspace_bytes(c.T, c.r, c.n_proj);
+    }
+    if (c.T > 0) {
+        // W4A8 calls always need their workspace (the activation codes); the others only to correct
+        const size_t need = c.w4a8 ? glowq_w4a8_workspace_bytes(c.T, c.d, c.correct ? c.r : 0)
+                                   : (c.correct ? glowq_workspace_bytes(c.T, c.r, c.n_proj) : 0);
+        if (need > 0) {
             if (workspace == nullptr || ws_bytes < need) return GLOWQ_ERR_WORKSPACE;
             if (!aligned(workspace, 256)) return GLOWQ_ERR_ALIGN;
         }
@@ -144,6 +150,33 @@ void choose_prefill_shape(const Call& c, int& tt, int& rr, int& ks) {
     ks = n <= 256 ? 4 : (n <= 512 ? 2 : 1);
 }
 
+// The projection R = X B_p^T into fp16 [n_proj][T][r_pad] at R (followed by its fp32 split-K
+// partials): 32-token blocks (16 when that leaves the chip idle even at the largest split, or when
+// r_pad > 128), then as many K ranges as make about kProjWant workgroups.
+hipError_t launch_projection(const Call& c, void* R, hipStream_t stream) {
+    const int32_t rp = (int32_t)r_pad_of(c.r);
+    ProjArgs p;
+    std::memset(&p, 0, sizeof(p));
+    p.x = static_cast<const _Float16*>(c.x);
+    p.T = (int32_t)c.T;
+    p.d = (int32_t)c.d;
+    p.r = c.r;
+    p.r_pad = rp;
+    p.n_proj = c.n_proj;
+    for (int i = 0; i < c.n_proj; ++i) p.b[i] = static_cast<const _Float16*>(c.b[i]);
+    p.R = R;
+    const int64_t G = c.d / kGroup;
+    p.tok_tiles = (rp <= 128 && ceil_div(c.T, 32) * c.n_proj * kProjMaxSplit >= kProjWant) ? 2 : 1;
+    const int64_t blocks = ceil_div(c.T, 16 * p.tok_tiles) * c.n_proj;
+    int64_t ks = ceil_div(kProjWant, blocks);
+    ks = ks > kProjMaxSplit ? kProjMaxSplit : ks;
+    ks = ks > G ? G : ks;
+    p.k_per = (int32_t)(ceil_div(G, ks) * kGroup);
+    p.ks = (int32_t)ceil_div(c.d, p.k_per);
+    p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(R) + prefill_r_bytes(c.T, c.r, c.n_proj));
+    return launch_proj_prefill(p, stream);
+}
+
 int run(const Call& c, void* workspace, hipStream_t stream) {
     if (c.T == 0) return GLOWQ_OK;
     int64_t row_tiles = 0;
@@ -157,28 +190,7 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
     }
 
     if (c.correct && prefill) {
-        ProjArgs p;
-        std::memset(&p, 0, sizeof(p));
-        p.x = static_cast<const _Float16*>(c.x);
-        p.T = (int32_t)c.T;
-        p.d = (int32_t)c.d;
-        p.r = c.r;
-        p.r_pad = rp;
-        p.n_proj = c.n_proj;
-        for (int i = 0; i < c.n_proj; ++i) p.b[i] = static_cast<const _Float16*>(c.b[i]);
-        p.R = R;
-        // 32-token blocks (16 when that leaves the chip idle even at the largest split, or when
-        // r_pad > 128), then as many K ranges as make about kProjWant workgroups
-        const int64_t G = c.d / kGroup;
-        p.tok_tiles = (rp <= 128 && ceil_div(c.T, 32) * c.n_proj * kProjMaxSplit >= kProjWant) ? 2 : 1;
-        const int64_t blocks = ceil_div(c.T, 16 * p.tok_tiles) * c.n_proj;
-        int64_t ks = ceil_div(kProjWant, blocks);
-        ks = ks > kProjMaxSplit ? kProjMaxSplit : ks;
-        ks = ks > G ? G : ks;
-        p.k_per = (int32_t)(ceil_div(G, ks) * kGroup);
-        p.ks = (int32_t)ceil_div(c.d, p.k_per);
-        p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(R) + prefill_r_bytes(c.T, c.r, c.n_proj));
-        if (launch_proj_prefill(p, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+        if (launch_projection(c, R, stream) != hipSuccess) return GLOWQ_ERR_HIP;
     }
 
     ForwardArgs f;
@@ -275,7 +287,77 @@ Call make_group(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qwei
     c.r = r;
     c.correct = restore != 0 && r > 0;
     c.y = y;
+    c.w4a8 = false;
     return c;
+}
+
+// W4A8 tile: 16, 32 or 64 tokens (decode-sized calls take one token tile) x 128 rows, 64 rows when
+// that leaves fewer than 128 tiles; wave groups splitting the input groups as in the prefill
+// kernel, so that about four wavefronts share every SIMD on small grids.
+void choose_w4a8_shape(const Call& c, int& tt, int& rr, int& ks) {
+    tt = c.T <= 16 ? 1 : (c.T <= 32 ? 2 : 4);
+    rr = 2;
+    int64_t n = prefill_tiles(c, tt, rr);
+    if (n < kPrefillHalfRowTiles) {
+        rr = 1;
+        n = prefill_tiles(c, tt, rr);
+    }
+    ks = n <= 256 ? 4 : (n <= 512 ? 2 : 1);
+    if (tt == 4 && rr == 2 && ks == 4) ks = 2;  // 1024 threads would cap this tile at 128 VGPRs (spills)
+}
+
+// W4A8 workspace: codes [T][d] int8 | code sums [T][G] int32 | scales [T] fp32 | for correcting
+// calls the fp16 projection [T][r_pad] and its split-K partials.
+int run_w4a8(const Call& c, void* workspace, hipStream_t stream) {
+    if (c.T == 0) return GLOWQ_OK;
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    int8_t* xq = reinterpret_cast<int8_t*>(base);
+    base += round256((size_t)c.T * c.d);
+    int32_t* xsum = reinterpret_cast<int32_t*>(base);
+    base += round256((size_t)c.T * (c.d / kGroup) * 4u);
+    float* xscale = reinterpret_cast<float*>(base);
+    base += round256((size_t)c.T * 4u);
+    void* R = c.correct ? base : nullptr;
+    if (launch_quant_x(static_cast<const _Float16*>(c.x), (int)c.T, (int)c.d, xq, xsum, xscale, stream) != hipSuccess)
+        return GLOWQ_ERR_HIP;
+    if (c.correct && launch_projection(c, R, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    ForwardArgs f;
+    std::memset(&f, 0, sizeof(f));
+    f.x = static_cast<const _Float16*>(c.x);
+    f.T = (int32_t)c.T;
+    f.d = (int32_t)c.d;
+    f.G = (int32_t)(c.d / kGroup);
+    f.r = c.correct ? c.r : 0;
+    f.r_pad = c.correct ? (int32_t)r_pad_of(c.r) : 0;
+    f.n_mod = c.m;
+    f.R = R;
+    f.n_proj = 1;
+    f.b[0] = c.correct ? static_cast<const _Float16*>(c.b[0]) : nullptr;
+    f.xq = xq;
+    f.xsum = xsum;
+    f.xscale = xscale;
+    int tt = 1, rr = 1, ks = 1;
+    choose_w4a8_shape(c, tt, rr, ks);
+    f.tile_tt = tt;
+    f.tile_rr = rr;
+    f.tile_ks = ks;
+    int64_t tiles = 0;
+    for (int i = 0; i < c.m; ++i) {
+        ModuleArgs& M = f.mod[i];
+        M.q = static_cast<const uint8_t*>(c.w[i].q);
+        M.sz = static_cast<const uint8_t*>(c.w[i].sz);
+        M.a = c.correct ? static_cast<const _Float16*>(c.a[i]) : nullptr;
+        M.y = static_cast<_Float16*>(c.y[i]);
+        M.n_out = (int32_t)c.w[i].n_out;
+        M.n_tiles16 = (int32_t)ceil_div(c.w[i].n_out, 16);
+        M.tile_begin = (int32_t)tiles;
+        f.tile_begin[i] = (int32_t)tiles;
+        M.proj = 0;
+        tiles += ceil_div(M.n_tiles16, 4 * rr);
+    }
+    f.m_tiles = (int32_t)ceil_div(c.T, 16 * tt);
+    f.n_tiles = (int32_t)(tiles * f.m_tiles);
+    return launch_w4a8(f, stream) == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
 }
 
 }  // namespace
@@ -328,6 +410,24 @@ size_t glowq_q_bytes(int64_t n_out, int64_t k_in) {
 size_t glowq_sz_bytes(int64_t n_out, int64_t k_in) {
     if (n_out < 1 || k_in < kGroup || k_in % kGroup != 0 || n_out > kMaxRows || k_in > kMaxD) return 0;
     return (size_t)ceil_div(n_out, 16) * (size_t)(k_in / kGroup) * 64u;
+}
+
+size_t glowq_w4a8_workspace_bytes(int64_t T, int64_t d, int32_t r) {
+    if (T <= 0 || d < kGroup || d % kGroup != 0 || d > kW4a8MaxD || r < 0 || r > GLOWQ_MAX_RANK) return 0;
+    size_t n = round256((size_t)T * d) + round256((size_t)T * (d / kGroup) * 4u) + round256((size_t)T * 4u);
+    if (r > 0) n += prefill_r_bytes(T, r, 1) + prefill_part_bytes(T, r, 1);
+    return n;
+}
+
+int glowq_group_forward_w4a8(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
+                             const void* b_shared, const void* const* a, int32_t r, int32_t restore,
+                             void* workspace, size_t workspace_bytes, void* const* y, hipStream_t stream) {
+    const void* bp[1] = {b_shared};
+    Call c = make_group(x, T, d, m, w, bp, 1, a, r, restore, y);
+    c.w4a8 = true;
+    const int v = validate(c, workspace, workspace_bytes);
+    if (v != GLOWQ_OK) return v;
+    return run_w4a8(c, workspace, stream);
 }
 
 size_t glowq_workspace_bytes(int64_t T, int32_t r, int32_t n_proj) {

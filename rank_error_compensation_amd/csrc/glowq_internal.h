@@ -187,6 +187,9 @@ struct ForwardArgs {
     int32_t dec_tiles;   // decode: row blocks (n_tiles = dec_tiles * dec_ks consumer workgroups)
     int32_t rows_total;  // decode: rows of all modules
     float* ypart;        // decode with a K split: fp32 partial sums [dec_ks][T][rows_total]
+    const int8_t* xq;     // W4A8: token codes [T][d] in the matrix-core operand order
+    const int32_t* xsum;  // W4A8: per (token, group) code sums [T][G]
+    const float* xscale;  // W4A8: per-token scales [T]
     const _Float16* b[kMaxModules];  // [r][d] right factors, one per projection
     ModuleArgs mod[kMaxModules];
 };
@@ -221,6 +224,11 @@ hipError_t launch_dequant(const uint8_t* q, const uint8_t* sz, int64_t n_out, in
 hipError_t launch_proj_prefill(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
+hipError_t launch_quant_x(const _Float16* x, int T, int d, int8_t* xq, int32_t* xsum, float* xscale,
+                          hipStream_t stream);
+hipError_t launch_w4a8(const ForwardArgs& a, hipStream_t stream);
+// W4A8: features of a call (the quantise kernel holds a token's row in registers)
+constexpr int64_t kW4a8MaxD = 16384;
 
 // Prefill projection launch: largest K split, and the workgroup count the split aims at (one per
 // CU; 512 workgroups, also with 16 splits, measured slower).
