@@ -212,6 +212,48 @@ def bruteforce_group_w4a8(x, q_packed_list, s_list, z_list, n_outs, k_in, b, a_l
     return outs
 
 
+# --------------------------------------------------------------------------- mixture of experts
+# The arXiv page's Figures 7-9 (Qwen1.5-MoE-A2.7B) show the covariance-aligned shared basis for
+# the MLP gate/up projections both aggregated over all experts (Fig. 8) and for one expert alone
+# (Fig. 9).  An MoE layer routes every token to a few experts; each expert's gate and up form an
+# input-sharing group over the tokens routed to it, and its down projection is a solo module on
+# its own hidden rows.  Routed rows are listed grouped by expert: rows offsets[e] ..
+# offsets[e + 1] - 1 belong to expert e, and row j reads token row_token[j] of X (or row j of X
+# when row_token is None, as for the down projection whose input is already in routed order).
+# Sharing: "expert" -- each expert e forms R_e = X_e B_e^T from its own rows with its own B_e
+# (Fig. 9); "all" -- one B for every expert, R = X B^T per token, consumed by every expert that
+# token is routed to (Fig. 8).
+def moe_forward(x, row_token, offsets, w_hats, b, a, restore: bool = True, share: str = "expert"
+                ) -> List[np.ndarray]:
+    """Outputs y_i [n_rows][O_i] in routed-row order for m modules per expert.
+
+    w_hats[e][i] is expert e's dequantised module i, a[e][i] its left factor; b[e] is expert e's
+    right factor (share == "expert") or b is the one right factor of all experts (share == "all")."""
+    x64 = _f64(x)
+    offs = [int(v) for v in _np(offsets)]
+    n_rows = offs[-1]
+    rows_x = x64[np.asarray(_np(row_token), dtype=np.int64)] if row_token is not None else x64[:n_rows]
+    m = len(w_hats[0])
+    outs = [np.zeros((n_rows, w_hats[0][i].shape[0])) for i in range(m)]
+    R_all = None
+    if restore and share == "all" and b is not None and _np(b).shape[0] > 0:
+        R_all = shared_projection(rows_x, b)  # per routed row: the row's token times B^T
+    for e in range(len(w_hats)):
+        lo, hi = offs[e], offs[e + 1]
+        if hi <= lo:
+            continue
+        xe = rows_x[lo:hi]
+        if share == "all":
+            ys = group_forward(xe, w_hats[e], None, a[e], restore=False)
+            if R_all is not None:
+                ys = [y + R_all[lo:hi] @ _f64(ai).T for y, ai in zip(ys, a[e])]
+        else:
+            ys = group_forward(xe, w_hats[e], b[e] if restore else None, a[e], restore=restore)
+        for i in range(m):
+            outs[i][lo:hi] = ys[i]
+    return outs
+
+
 # --------------------------------------------------------------------------- brute force
 def bruteforce_group(x, q_packed_list, s_list, z_list, n_outs, k_in, b, a_list,
                      restore: bool = True) -> List[np.ndarray]:

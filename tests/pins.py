@@ -534,6 +534,79 @@ def check_w4a8_lossless_and_scale(ref):
         assert np.array_equal(2.0 * a, b)
 
 
+# ------------------------------------------------------------------ mixture of experts
+def _moe_problem(seed, n_exp=5, T=7, d=256, n_outs=(24, 16), r=4, top=2):
+    rng = np.random.default_rng(seed)
+    G = d // 128
+    experts = []
+    for e in range(n_exp):
+        mods = []
+        for O in n_outs:
+            q = rng.integers(0, 16, size=(O, d))
+            s = rng.uniform(0.002, 0.05, size=(O, G)).astype(np.float16)
+            z = rng.integers(0, 16, size=(O, G)).astype(np.float16)
+            mods.append((pack_words(q), s, z, O))
+        experts.append(mods)
+    x = rng.standard_normal((T, d)).astype(np.float16)
+    b = [(rng.standard_normal((r, d)) / math.sqrt(d)).astype(np.float16) for _ in range(n_exp)]
+    a = [[(rng.standard_normal((O, r)) * 0.05).astype(np.float16) for O in n_outs] for _ in range(n_exp)]
+    # top-`top` routing of every token to distinct experts; expert 1 receives no token
+    pairs = []
+    for t in range(T):
+        choice = rng.permutation([e for e in range(n_exp) if e != 1])[:top]
+        pairs += [(int(e), t) for e in choice]
+    pairs.sort()
+    row_token = np.array([t for _, t in pairs], dtype=np.int32)
+    counts = np.bincount([e for e, _ in pairs], minlength=n_exp)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return SimpleNamespace(experts=experts, x=x, b=b, a=a, row_token=row_token, offsets=offsets, d=d,
+                           n_exp=n_exp, n_outs=list(n_outs), r=r)
+
+
+def _moe_w_hats(ref, p):
+    return [[ref.dequant(w, s, z, O, p.d) for (w, s, z, O) in mods] for mods in p.experts]
+
+
+def check_moe_rows(ref):
+    """Every routed row equals the single-token group forward of its token through its expert's
+    modules (rows are independent, so this is computed one row at a time, by a route that shares
+    no blocking with the per-expert batches); an expert without rows changes nothing; with every
+    expert holding the same B, one B for all experts gives the same outputs; permuting the rows
+    inside an expert's range permutes the outputs."""
+    p = _moe_problem(81)
+    wh = _moe_w_hats(ref, p)
+    ys = ref.moe_forward(p.x, p.row_token, p.offsets, wh, p.b, p.a, restore=True, share="expert")
+    owner = np.repeat(np.arange(p.n_exp), np.diff(p.offsets))
+    for j in range(len(p.row_token)):
+        e, t = int(owner[j]), int(p.row_token[j])
+        one = ref.group_forward(p.x[t:t + 1], wh[e], p.b[e], p.a[e], restore=True)
+        for i in range(len(p.n_outs)):
+            assert np.allclose(ys[i][j], one[i][0], rtol=1e-13, atol=1e-13 * np.abs(one[i]).max())
+    assert p.offsets[1] == p.offsets[2]  # expert 1 has no rows
+    # one B for all experts == every expert with that same B
+    b0 = p.b[0]
+    y_all = ref.moe_forward(p.x, p.row_token, p.offsets, wh, b0, p.a, restore=True, share="all")
+    y_same = ref.moe_forward(p.x, p.row_token, p.offsets, wh, [b0] * p.n_exp, p.a, restore=True, share="expert")
+    for u, v in zip(y_all, y_same):
+        assert np.allclose(u, v, rtol=1e-13, atol=1e-13 * np.abs(v).max())
+    # restore off: the quantised products alone, in both sharing modes
+    y0 = ref.moe_forward(p.x, p.row_token, p.offsets, wh, p.b, p.a, restore=False, share="expert")
+    y0a = ref.moe_forward(p.x, p.row_token, p.offsets, wh, b0, p.a, restore=False, share="all")
+    for j in range(len(p.row_token)):
+        e, t = int(owner[j]), int(p.row_token[j])
+        for i in range(len(p.n_outs)):
+            want = p.x[t].astype(np.float64) @ wh[e][i].T
+            assert np.array_equal(y0[i][j], y0a[i][j])
+            assert np.allclose(y0[i][j], want, rtol=1e-13, atol=1e-13 * np.abs(want).max())
+    # a permutation of expert 3's rows permutes its outputs
+    lo, hi = int(p.offsets[3]), int(p.offsets[4])
+    perm = np.arange(len(p.row_token))
+    perm[lo:hi] = perm[lo:hi][::-1]
+    yp = ref.moe_forward(p.x, p.row_token[perm], p.offsets, wh, p.b, p.a, restore=True, share="expert")
+    for u, v in zip(ys, yp):
+        assert np.allclose(u[perm], v, rtol=1e-13, atol=1e-13 * np.abs(u).max())
+
+
 # ------------------------------------------------------------------ the parity comparator
 def check_parity_errors(ref):
     """The comparator behind every GPU parity assertion, against values worked by hand: the
@@ -568,7 +641,8 @@ def check_parity_errors(ref):
 ALL_REF_CHECKS = [check_dequant_exhaustive, check_dequant_golden, check_restore_off,
                   check_associativity_small_int, check_bruteforce, check_row_independence,
                   check_path_mask, check_parity_errors, check_w4a8_quantizer_hand,
-                  check_w4a8_quantizer_invariants, check_w4a8_bruteforce, check_w4a8_lossless_and_scale]
+                  check_w4a8_quantizer_invariants, check_w4a8_bruteforce, check_w4a8_lossless_and_scale,
+                  check_moe_rows]
 ALL_SOL_CHECKS = [check_eckart_young, check_isotropic, check_usage_weighted_risk, check_qr_core,
                   check_cholesky_vs_symmetric, check_randomized_svd, check_scores, check_second_moment,
                   check_pinv_lift]

@@ -224,6 +224,26 @@ def w4a8_corr_on_codes(x, w_hats, b, a_list, restore=True):
     return outs
 
 
+def moe_next_expert_b(x, row_token, offsets, w_hats, b, a, restore=True, share="expert"):
+    n = len(w_hats)
+    if share == "expert" and b is not None:
+        b = [b[(e + 1) % n] for e in range(n)]  # expert e corrects with its neighbour's B
+    return G.moe_forward(x, row_token, offsets, w_hats, b, a, restore, share)
+
+
+def moe_no_gather(x, row_token, offsets, w_hats, b, a, restore=True, share="expert"):
+    xx = G._f64(x)
+    n_rows = int(G._np(offsets)[-1])
+    idx = np.arange(n_rows) % xx.shape[0]
+    return G.moe_forward(xx[idx], None, offsets, w_hats, b, a, restore, share)
+
+
+def moe_offsets_shifted(x, row_token, offsets, w_hats, b, a, restore=True, share="expert"):
+    o = np.array(G._np(offsets), dtype=np.int64).copy()
+    o[1:-1] = np.minimum(o[1:-1] + 1, o[-1])  # every boundary one row late
+    return G.moe_forward(x, row_token, o, w_hats, b, a, restore, share)
+
+
 REF_MUTANTS = {
     "dequant_plus_z": dict(dequant=dequant_plus_z),
     "dequant_group64": dict(dequant=dequant_group64),
@@ -245,6 +265,9 @@ REF_MUTANTS = {
     "quant_unsigned_range": dict(quantize_x_int8=quant_unsigned_range),
     "w4a8_no_scale": dict(group_forward_w4a8=w4a8_no_scale),
     "w4a8_corr_on_codes": dict(group_forward_w4a8=w4a8_corr_on_codes),
+    "moe_next_expert_b": dict(moe_forward=moe_next_expert_b),
+    "moe_no_gather": dict(moe_forward=moe_no_gather),
+    "moe_offsets_shifted": dict(moe_forward=moe_offsets_shifted),
 }
 
 SOL_MUTANTS = {
