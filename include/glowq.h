@@ -54,6 +54,8 @@ extern "C" {
 #define GLOWQ_ERR_HANDOFF (-8)     /* glowq_workspace_status: a bounded wait for the shared
                                       projection expired in a call since the last check;
                                       that call's corrected outputs are invalid            */
+#define GLOWQ_ERR_ROUTING (-9)     /* glowq_workspace_status: a mixture-of-experts call met
+                                      routing data out of range (clamped; outputs invalid)  */
 
 #define GLOWQ_MAX_MODULES 8
 #define GLOWQ_MAX_RANK 256
@@ -122,11 +124,11 @@ size_t glowq_workspace_bytes(int64_t T, int32_t r, int32_t n_proj);
  * GLOWQ_ERR_HANDOFF.  Asynchronous. */
 int glowq_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Hand-off status of a workspace: SYNCHRONISES `stream`, reads the error word that a
- * correcting decode call raises when one of its bounded waits for the shared projection
- * expires (its corrected outputs are then wrong), clears the word and returns GLOWQ_OK
- * (no expiry since the last check or init) or GLOWQ_ERR_HANDOFF.  Allocates nothing; not
- * for use under graph capture. */
+/* Status of a workspace: SYNCHRONISES `stream`, reads the error word that a correcting decode
+ * call raises when one of its bounded waits for the shared projection expires (its corrected
+ * outputs are then wrong) and that glowq_moe_forward raises on routing data out of range, clears
+ * the word and returns GLOWQ_OK (nothing raised since the last check or init),
+ * GLOWQ_ERR_HANDOFF or GLOWQ_ERR_ROUTING.  Allocates nothing; not for use under graph capture. */
 int glowq_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Input-sharing group of m modules (1 <= m <= 8), w[0] the anchor (GlowQ paper note, key
@@ -201,6 +203,55 @@ size_t glowq_w4a8_workspace_bytes(int64_t T, int64_t d, int32_t r);
 int glowq_group_forward_w4a8(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
                              const void* b_shared, const void* const* a, int32_t r, int32_t restore,
                              void* workspace, size_t workspace_bytes, void* const* y, hipStream_t stream);
+
+/* ---------------------------------------------------------------- mixture of experts
+ * The path on an MoE layer (the GlowQ arXiv page, Figures 7-9, Qwen1.5-MoE-A2.7B: the shared
+ * covariance-aligned basis of the MLP gate/up projections holds for one expert and across all
+ * experts).  Tokens are routed to experts; every routed row is one token sent to one expert, and
+ * the rows are listed grouped by expert: rows offsets[e] .. offsets[e + 1] - 1 belong to expert e
+ * (offsets non-decreasing, offsets[0] = 0, offsets[n_exp] = n_rows).  Each expert's m modules form
+ * an input-sharing group over its rows (m = 2: gate, the anchor, and up; m = 1: a solo module such
+ * as down_proj).  With share == GLOWQ_MOE_SHARE_EXPERT each expert forms its projection
+ * R_e = X_e B_e^T once from its own rows and its own B_e; with GLOWQ_MOE_SHARE_ALL one B serves
+ * every expert and R = X B^T is formed once per token, then consumed by every expert the token is
+ * routed to.  Result, for routed row j of expert e reading token t:
+ *   y_i[j] = fp16_RNE(X[t] W_hat_{e,i}^T + R[.] A_{e,i}^T)
+ * One launch covers every expert (its work is enumerated on the device from the offsets, so the
+ * host does not need the per-expert counts).  Routing data out of range (offsets, token indices)
+ * is clamped -- never read out of bounds -- and reported by glowq_workspace_status.
+ */
+#define GLOWQ_MOE_SHARE_EXPERT 0
+#define GLOWQ_MOE_SHARE_ALL 1
+#define GLOWQ_MOE_MAX_EXPERTS 256
+#define GLOWQ_MOE_MAX_MODULES 4
+
+typedef struct glowq_moe_module {
+    const void* q;   /* device layout of all experts' modules: expert e at byte e * glowq_q_bytes(n_out, k_in) */
+    const void* sz;  /* expert e at byte e * glowq_sz_bytes(n_out, k_in)                          */
+    const void* a;   /* fp16 [n_exp][n_out][r] left factors (may be NULL when not correcting)     */
+    void* y;         /* fp16 [n_rows][n_out] output, in routed-row order                           */
+    int64_t n_out;   /* rows of one expert's module                                               */
+    int64_t k_in;    /* == d                                                                      */
+} glowq_moe_module;
+
+/* Workspace of glowq_moe_forward: 8192 bytes of status words, then (correcting calls) the fp16
+ * projection [rows][r_pad] (rows = n_rows per expert, or T shared by all) and, shared by all, its
+ * split-K partials.  Zero-fill it once (glowq_workspace_init). */
+size_t glowq_moe_workspace_bytes(int64_t n_rows, int64_t T, int32_t r, int32_t share);
+
+/*   x            : fp16 [T][d]; with row_token_dev NULL row j reads x[j] (then T == n_rows)
+ *   n_exp, m     : experts (1 .. 256), modules per expert (1 .. 4)
+ *   mods         : host array of m module descriptors (stacked over experts)
+ *   b            : fp16 [n_exp][r][d] (SHARE_EXPERT) or [r][d] (SHARE_ALL); NULL when not correcting
+ *   r, restore   : rank (0 .. 256, r % 8 == 0) and the GlowQ-S bit of this call
+ *   row_token_dev: device int32 [n_rows], token of each routed row, or NULL
+ *   offsets_dev  : device int32 [n_exp + 1]
+ *   n_rows       : routed rows (0 is a no-op)
+ * Asynchronous on `stream`. */
+int glowq_moe_forward(const void* x, int64_t T, int64_t d, int32_t n_exp, int32_t m, const glowq_moe_module* mods,
+                      const void* b, int32_t share, int32_t r, int32_t restore, const int32_t* row_token_dev,
+                      const int32_t* offsets_dev, int64_t n_rows, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /* ---------------------------------------------------------------- decoder-layer schedule
  * A sequence of units run in order on one stream: per decoder layer the QKV group, the

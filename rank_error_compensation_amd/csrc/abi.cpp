@@ -399,7 +399,108 @@ int glowq_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t 
     if (h == 0) return GLOWQ_OK;
     if (launch_flag_clear(word, stream) != hipSuccess) return GLOWQ_ERR_HIP;
     if (hipStreamSynchronize(stream) != hipSuccess) return GLOWQ_ERR_HIP;
-    return GLOWQ_ERR_HANDOFF;
+    return (h & 1) ? GLOWQ_ERR_HANDOFF : GLOWQ_ERR_ROUTING;
+}
+
+size_t glowq_moe_workspace_bytes(int64_t n_rows, int64_t T, int32_t r, int32_t share) {
+    if (n_rows < 0 || T < 0 || r < 0 || r > GLOWQ_MAX_RANK || n_rows > kMaxT * 8 || T > kMaxT) return 0;
+    if (share != GLOWQ_MOE_SHARE_EXPERT && share != GLOWQ_MOE_SHARE_ALL) return 0;
+    size_t n = kWsHeader;
+    if (r > 0 && n_rows > 0) {
+        if (share == GLOWQ_MOE_SHARE_ALL) n += prefill_r_bytes(T, r, 1) + prefill_part_bytes(T, r, 1);
+        else n += prefill_r_bytes(n_rows, r, 1);
+    }
+    return n;
+}
+
+int glowq_moe_forward(const void* x, int64_t T, int64_t d, int32_t n_exp, int32_t m, const glowq_moe_module* mods,
+                      const void* b, int32_t share, int32_t r, int32_t restore, const int32_t* row_token_dev,
+                      const int32_t* offsets_dev, int64_t n_rows, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    if (n_exp < 1 || n_exp > GLOWQ_MOE_MAX_EXPERTS || m < 1 || m > GLOWQ_MOE_MAX_MODULES) return GLOWQ_ERR_UNSUPPORTED;
+    if (share != GLOWQ_MOE_SHARE_EXPERT && share != GLOWQ_MOE_SHARE_ALL) return GLOWQ_ERR_INVALID_ARG;
+    if (n_rows < 0 || T < 0 || d < kGroup || d % kGroup != 0) return GLOWQ_ERR_SHAPE;
+    if (r < 0) return GLOWQ_ERR_SHAPE;
+    if (r > GLOWQ_MAX_RANK || r % 8 != 0) return GLOWQ_ERR_UNSUPPORTED;
+    if (n_rows > kMaxT * 8 || T > kMaxT || d > kMaxD || T * d > kMaxActElems) return GLOWQ_ERR_UNSUPPORTED;
+    if (mods == nullptr) return GLOWQ_ERR_INVALID_ARG;
+    if (n_rows == 0) return GLOWQ_OK;
+    if (x == nullptr || offsets_dev == nullptr) return GLOWQ_ERR_INVALID_ARG;
+    if (row_token_dev == nullptr && T != n_rows) return GLOWQ_ERR_SHAPE;
+    if (T < 1) return GLOWQ_ERR_SHAPE;
+    const bool correct = restore != 0 && r > 0;
+    int64_t rb = 0;
+    for (int i = 0; i < m; ++i) {
+        const glowq_moe_module& M = mods[i];
+        if (M.q == nullptr || M.sz == nullptr || M.y == nullptr) return GLOWQ_ERR_INVALID_ARG;
+        if (M.n_out < 1 || M.k_in != d) return GLOWQ_ERR_SHAPE;
+        if (M.n_out > kMaxRows) return GLOWQ_ERR_UNSUPPORTED;
+        if (!aligned(M.q, 16) || !aligned(M.sz, 16) || !aligned(M.y, 16)) return GLOWQ_ERR_ALIGN;
+        if (correct && (M.a == nullptr)) return GLOWQ_ERR_INVALID_ARG;
+        if (correct && !aligned(M.a, 16)) return GLOWQ_ERR_ALIGN;
+        rb += ceil_div(ceil_div(M.n_out, 16), 4 * 2);
+    }
+    if (correct && b == nullptr) return GLOWQ_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(offsets_dev, 4) || (row_token_dev && !aligned(row_token_dev, 4)) ||
+        (correct && !aligned(b, 16)))
+        return GLOWQ_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < glowq_moe_workspace_bytes(n_rows, T, correct ? r : 0, share))
+        return GLOWQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return GLOWQ_ERR_ALIGN;
+    // items of the grouped launch: at most n_rb (n_rows / BM + n_exp)
+    const int64_t avg = ceil_div(n_rows, n_exp);
+    const int tt = avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
+    if (rb * (ceil_div(n_rows, 16 * tt) + n_exp) > kMaxTiles) return GLOWQ_ERR_UNSUPPORTED;
+
+    MoeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = static_cast<const _Float16*>(x);
+    a.T = (int32_t)T;
+    a.d = (int32_t)d;
+    a.G = (int32_t)(d / kGroup);
+    a.row_token = row_token_dev;
+    a.offsets = offsets_dev;
+    a.n_exp = n_exp;
+    a.n_rows = (int32_t)n_rows;
+    a.m = m;
+    int32_t rbs = 0;
+    for (int i = 0; i < m; ++i) {
+        const glowq_moe_module& M = mods[i];
+        a.q[i] = static_cast<const uint8_t*>(M.q);
+        a.sz[i] = static_cast<const uint8_t*>(M.sz);
+        a.qbytes[i] = (int64_t)glowq_q_bytes(M.n_out, M.k_in);
+        a.szbytes[i] = (int64_t)glowq_sz_bytes(M.n_out, M.k_in);
+        a.a[i] = correct ? static_cast<const _Float16*>(M.a) : nullptr;
+        a.y[i] = static_cast<_Float16*>(M.y);
+        a.n_out[i] = (int32_t)M.n_out;
+        a.n_tiles16[i] = (int32_t)ceil_div(M.n_out, 16);
+        a.rb_begin[i] = rbs;
+        rbs += (int32_t)ceil_div(a.n_tiles16[i], 8);
+    }
+    a.rb_begin[m] = rbs;
+    a.n_rb = rbs;
+    a.r = correct ? r : 0;
+    a.r_pad = correct ? (int32_t)r_pad_of(r) : 0;
+    a.tile_tt = tt;
+    a.err = static_cast<int32_t*>(workspace) + kSyncError;
+    uint8_t* R = static_cast<uint8_t*>(workspace) + kWsHeader;
+    if (correct) {
+        a.R = reinterpret_cast<const _Float16*>(R);
+        if (share == GLOWQ_MOE_SHARE_ALL) {
+            a.r_by_token = 1;
+            const void* bp[1] = {b};
+            Call c = make_group(x, T, d, 1, nullptr, bp, 1, nullptr, r, 1, nullptr);
+            if (launch_projection(c, R, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+        } else {
+            a.r_by_token = 0;
+            a.b = static_cast<const _Float16*>(b);
+            a.Rout = reinterpret_cast<_Float16*>(R);
+            if (launch_moe_proj(a, ceil_div(n_rows, 16) + n_exp, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+        }
+    }
+    if (launch_moe_gemm(a, (int64_t)rbs * (ceil_div(n_rows, 16 * tt) + n_exp), stream) != hipSuccess)
+        return GLOWQ_ERR_HIP;
+    return GLOWQ_OK;
 }
 
 size_t glowq_q_bytes(int64_t n_out, int64_t k_in) {

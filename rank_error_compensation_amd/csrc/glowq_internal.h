@@ -204,6 +204,35 @@ struct ProjArgs {
     void* R;             // output
 };
 
+// Mixture of experts: stacked expert modules and device-side routing (one launch for all experts).
+constexpr int kMoeMaxExperts = 256;
+constexpr int kMoeMaxMod = 4;
+constexpr int64_t kMoeMaxGrid = 2048;  // persistent workgroups of a grouped launch
+struct MoeArgs {
+    const _Float16* x;          // [T][d]; row j reads x[row_token[j]] (or x[j] without row_token)
+    int32_t T, d, G;
+    const int32_t* row_token;   // [n_rows] or nullptr
+    const int32_t* offsets;     // [n_exp + 1]
+    int32_t n_exp, n_rows, m;
+    const uint8_t* q[kMoeMaxMod];
+    const uint8_t* sz[kMoeMaxMod];
+    int64_t qbytes[kMoeMaxMod], szbytes[kMoeMaxMod];  // one expert's module, bytes
+    const _Float16* a[kMoeMaxMod];  // [n_exp][n_out][r]
+    _Float16* y[kMoeMaxMod];        // [n_rows][n_out]
+    int32_t n_out[kMoeMaxMod], n_tiles16[kMoeMaxMod];
+    int32_t rb_begin[kMoeMaxMod + 1];  // prefix of the modules' row blocks (64 RR rows)
+    int32_t n_rb;
+    int32_t r, r_pad;
+    const _Float16* R;          // fp16 projection rows [.][r_pad]
+    int32_t r_by_token;         // 1: R row = the row's token (one B for all experts); 0: R row = j
+    int32_t tile_tt;            // 16 TT routed rows per block
+    int32_t* err;               // workspace error word (bit 1: routing data out of range)
+    const _Float16* b;          // per-expert right factors [n_exp][r][d] (projection launch)
+    _Float16* Rout;             // projection output [n_rows][r_pad]
+};
+hipError_t launch_moe_proj(const MoeArgs& a, int64_t max_items, hipStream_t stream);
+hipError_t launch_moe_gemm(const MoeArgs& a, int64_t max_items, hipStream_t stream);
+
 // Module owning work tile `tile` (uniform across the workgroup): one contiguous scalar load of the
 // tile_begin table, so the module's own arguments are fetched with a single dependent load.
 __device__ __forceinline__ int module_of(const ForwardArgs& a, int tile) {

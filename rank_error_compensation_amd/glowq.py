@@ -25,6 +25,9 @@ ERR_WORKSPACE = -5
 ERR_HIP = -6
 ERR_RANGE = -7
 ERR_HANDOFF = -8
+ERR_ROUTING = -9
+MOE_SHARE_EXPERT = 0
+MOE_SHARE_ALL = 1
 
 DTYPE_F32 = 0
 DTYPE_F16 = 1
@@ -40,6 +43,10 @@ _sz = ctypes.c_size_t
 
 class QWeightC(ctypes.Structure):
     _fields_ = [("q", _vp), ("sz", _vp), ("n_out", _i64), ("k_in", _i64)]
+
+
+class MoeModuleC(ctypes.Structure):
+    _fields_ = [("q", _vp), ("sz", _vp), ("a", _vp), ("y", _vp), ("n_out", _i64), ("k_in", _i64)]
 
 
 class UnitC(ctypes.Structure):
@@ -67,6 +74,9 @@ EXPORTS = {
     "glowq_w4a8_workspace_bytes": (_sz, [_i64, _i64, _i32]),
     "glowq_group_forward_w4a8": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(QWeightC), _vp,
                                                 ctypes.POINTER(_vp), _i32, _i32, _vp, _sz, ctypes.POINTER(_vp), _vp]),
+    "glowq_moe_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
+    "glowq_moe_forward": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, ctypes.POINTER(MoeModuleC), _vp, _i32, _i32,
+                                         _i32, _vp, _vp, _i64, _vp, _sz, _vp]),
     "glowq_solo_forward": (ctypes.c_int, [_vp, _i64, _i64, ctypes.POINTER(QWeightC), _vp, _vp, _i32,
                                           _i32, _vp, _sz, _vp, _vp]),
     "glowq_layerwise_forward": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(QWeightC),
@@ -285,7 +295,7 @@ def init_workspace(ws: torch.Tensor, stream=None) -> torch.Tensor:
 def workspace_status(ws: torch.Tensor, stream=None) -> int:
     """glowq_workspace_status: synchronises, returns OK or ERR_HANDOFF and clears the word."""
     st = int(lib().glowq_workspace_status(_ptr(ws), ws.numel(), _stream(stream)))
-    if st not in (OK, ERR_HANDOFF):
+    if st not in (OK, ERR_HANDOFF, ERR_ROUTING):
         check(st, "glowq_workspace_status")
     return st
 
@@ -363,6 +373,48 @@ def group_forward_w4a8(x: torch.Tensor, weights: Sequence[QWeight], b: Optional[
     check(lib().glowq_group_forward_w4a8(_ptr(x), x.shape[0], x.shape[1], m, wc, _ptr(b), ac, r,
                                          int(bool(restore)), _ptr(workspace), ws_n, yc, _stream(stream)),
           "glowq_group_forward_w4a8")
+    return y
+
+
+# --------------------------------------------------------------------------- mixture of experts
+@dataclass
+class MoeModule:
+    """One module (gate, up or down) of every expert, stacked: expert e's device layout at
+    e * q_bytes / e * sz_bytes, its left factor a[e] fp16 [n_out][r]."""
+    q: torch.Tensor
+    sz: torch.Tensor
+    a: Optional[torch.Tensor]   # fp16 [n_exp][n_out][r]
+    n_out: int
+    k_in: int
+
+    @staticmethod
+    def stack(weights: Sequence[QWeight], a: Optional[Sequence[torch.Tensor]]) -> "MoeModule":
+        q = torch.cat([w.q for w in weights]).contiguous()
+        sz = torch.cat([w.sz for w in weights]).contiguous()
+        a_st = torch.stack(list(a)).contiguous() if a is not None else None
+        return MoeModule(q, sz, a_st, weights[0].n_out, weights[0].k_in)
+
+
+def moe_workspace_bytes(n_rows: int, T: int, r: int, share: int) -> int:
+    return int(lib().glowq_moe_workspace_bytes(n_rows, T, r, share))
+
+
+def moe_forward(x: torch.Tensor, n_exp: int, modules: Sequence[MoeModule], b: Optional[torch.Tensor], share: int,
+                r: int, restore: bool, row_token: Optional[torch.Tensor], offsets: torch.Tensor, n_rows: int,
+                workspace: Optional[torch.Tensor] = None, y: Optional[List[torch.Tensor]] = None,
+                stream=None) -> List[torch.Tensor]:
+    """glowq_moe_forward: outputs y_i fp16 [n_rows][n_out_i] in routed-row order."""
+    if y is None:
+        y = [torch.empty(n_rows, mm.n_out, dtype=torch.float16, device=x.device) for mm in modules]
+    if workspace is None:
+        workspace = make_workspace(1, 8, 1, x.device,
+                                   min_bytes=moe_workspace_bytes(n_rows, x.shape[0], r if restore else 0, share))
+    mc = _arr(MoeModuleC, [MoeModuleC(mm.q.data_ptr(), mm.sz.data_ptr(),
+                                      None if mm.a is None else mm.a.data_ptr(), yy.data_ptr(), mm.n_out, mm.k_in)
+                           for mm, yy in zip(modules, y)])
+    check(lib().glowq_moe_forward(_ptr(x), x.shape[0], x.shape[1], n_exp, len(modules), mc, _ptr(b), share, r,
+                                  int(bool(restore)), _ptr(row_token), _ptr(offsets), n_rows, _ptr(workspace),
+                                  workspace.numel(), _stream(stream)), "glowq_moe_forward")
     return y
 
 

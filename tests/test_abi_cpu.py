@@ -285,3 +285,31 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     sizes = (ctypes.c_int64 * 1)(257 << 20)                          # beyond 256 MiB per read
     assert L.glowq_probe_read_sequence(FAKE, sizes, 1, FAKE, None) == -1
     assert L.glowq_probe_read_sequence(FAKE, sizes, 0, FAKE, None) == -1
+
+
+def test_moe_validation_rejects_before_any_hip_call():
+    L = g.lib()
+    mod = (g.MoeModuleC * 2)(g.MoeModuleC(FAKE, FAKE, FAKE, FAKE, 64, 256), g.MoeModuleC(FAKE, FAKE, FAKE, FAKE, 64, 256))
+
+    def call(x=FAKE, T=8, d=256, n_exp=4, m=2, mods=mod, b=FAKE, share=0, r=16, restore=1, tok=FAKE, off=FAKE,
+             n_rows=16, ws=FAKE, ws_bytes=1 << 24):
+        return L.glowq_moe_forward(x, T, d, n_exp, m, mods, b, share, r, restore, tok, off, n_rows, ws, ws_bytes, None)
+
+    assert call(n_exp=0) == g.ERR_UNSUPPORTED
+    assert call(n_exp=257) == g.ERR_UNSUPPORTED
+    assert call(m=5) == g.ERR_UNSUPPORTED
+    assert call(share=2) == g.ERR_INVALID_ARG
+    assert call(d=100) == g.ERR_SHAPE
+    assert call(r=12) == g.ERR_UNSUPPORTED
+    assert call(n_rows=0) == g.OK                      # no routed rows: nothing to do
+    assert call(off=None) == g.ERR_INVALID_ARG
+    assert call(tok=None, T=8, n_rows=16) == g.ERR_SHAPE  # rows read x[j]: T must equal n_rows
+    assert call(b=None) == g.ERR_INVALID_ARG
+    assert call(ws_bytes=100) == g.ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == g.ERR_ALIGN
+    assert call(x=FAKE + 2) == g.ERR_ALIGN
+    bad = (g.MoeModuleC * 2)(g.MoeModuleC(FAKE, FAKE, FAKE, FAKE, 64, 384), g.MoeModuleC(FAKE, FAKE, FAKE, FAKE, 64, 256))
+    assert call(mods=bad) == g.ERR_SHAPE
+    assert L.glowq_moe_workspace_bytes(16, 8, 16, 0) == 8192 + 16 * 32 * 2 + 0 * 256 + (256 - 16 * 32 * 2 % 256) % 256
+    assert L.glowq_moe_workspace_bytes(16, 8, 0, 0) == 8192
+    assert L.glowq_moe_workspace_bytes(16, 8, 16, 3) == 0

@@ -31,7 +31,7 @@ import torch
 GROUP = 128  # inputs per quantisation group (INT4 "g128")
 
 # stable integer codes for seed keys
-KIND = {"x": 1, "w": 2, "outlier": 3, "a": 4, "b": 5, "basis": 6, "mask": 7, "z": 8}
+KIND = {"x": 1, "w": 2, "outlier": 3, "a": 4, "b": 5, "basis": 6, "mask": 7, "z": 8, "route": 9}
 
 
 def seed_of(*keys: int) -> int:
@@ -197,6 +197,23 @@ def restore_mask(n_units: int, n_restore: int, keys: Sequence[int]) -> List[bool
     order = sorted(range(n_units), key=lambda u: (-float(score[u]), u))
     chosen = set(order[:n_restore])
     return [u in chosen for u in range(n_units)]
+
+
+def moe_routing(T: int, n_exp: int, top_k: int, keys: Sequence[int], skip: Sequence[int] = ()):
+    """Top-k routing of T tokens to n_exp experts from seeded uniform scores (experts in `skip`
+    receive no token), listed grouped by expert and, within an expert, by token:
+    (row_token int32 [T top_k], offsets int32 [n_exp + 1])."""
+    g = generator("cpu", *keys, KIND["route"])
+    score = torch.rand(T, n_exp, generator=g, dtype=torch.float64)
+    if len(skip):
+        score[:, list(skip)] = -1.0
+    top = torch.topk(score, top_k, dim=1).indices  # distinct experts per token
+    pairs = sorted((int(top[t, k]), t) for t in range(T) for k in range(top_k))
+    row_token = torch.tensor([t for _, t in pairs], dtype=torch.int32)
+    counts = torch.bincount(torch.tensor([e for e, _ in pairs], dtype=torch.int64), minlength=n_exp)
+    offsets = torch.zeros(n_exp + 1, dtype=torch.int32)
+    offsets[1:] = torch.cumsum(counts, 0).to(torch.int32)
+    return row_token, offsets
 
 
 # ----------------------------------------------------------------------------------
