@@ -93,6 +93,22 @@ def time_steps(fn, steps, warmup):
     return time.perf_counter() - t0
 
 
+def graphed(fn):
+    """fn's launches captured once in a HIP graph (torch's graph API on a side stream)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        fn()
+    torch.cuda.synchronize()
+    return gr
+
+
 def call_unit(u, g, ws, layerwise=False):
     if layerwise and u.kind == g.UNIT_GROUP:
         return g.layerwise_forward(u.x, u.weights, u.b_layerwise, u.a, u.r, u.restore, workspace=ws, y=u.y)
@@ -348,6 +364,224 @@ def extra_prefill_gateup(g, reps=20):
                      "frac_mfma_f16_peak": round(unit_flops(T, 4096, u.n_outs, u.r, True) / t / 1e12 / 2500.0, 4),
                      "flops_executed": fl}
     out["workload"] = "llama2-7b gate/up group prefill T=2048 r=64 (one call: projection + grouped GEMM)"
+    return out
+
+
+def paired_ci(fn_a, fn_b, trials=30, calls=10):
+    """Interleaved paired timing of two call sequences on the launch stream: each trial times
+    `calls` back-to-back calls of A and of B between HIP events, the order of the two alternating
+    from trial to trial (clock and power drift cancel in the pairs).  Returns the per-call medians
+    and the mean relative difference (B - A) / A per trial with its 95 % confidence interval
+    (Student t over the trials); `significant` when the interval excludes zero."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        fn_a()
+        fn_b()
+    torch.cuda.synchronize()
+    ta, tb = [], []
+    for k in range(trials):
+        order = ((fn_a, ta), (fn_b, tb)) if k % 2 == 0 else ((fn_b, tb), (fn_a, ta))
+        for fn, acc in order:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(calls):
+                fn()
+            e1.record(stream)
+            e1.synchronize()
+            acc.append(e0.elapsed_time(e1) * 1e3 / calls)
+    rel = [(b - a) / a for a, b in zip(ta, tb)]
+    n = len(rel)
+    mean = sum(rel) / n
+    sd = statistics.stdev(rel) if n > 1 else 0.0
+    try:
+        from scipy.stats import t as student_t
+        q = float(student_t.ppf(0.975, n - 1))
+    except Exception:
+        q = 2.045
+    half = q * sd / n ** 0.5
+    return {"a_us_median": round(statistics.median(ta), 3), "b_us_median": round(statistics.median(tb), 3),
+            "rel_diff_mean": round(mean, 5), "ci95": [round(mean - half, 5), round(mean + half, 5)],
+            "significant": bool(mean - half > 0 or mean + half < 0), "trials": n, "calls_per_trial": calls}
+
+
+def extra_group_vs_layerwise(g):
+    """Group (one shared B, one projection) against layerwise (a B_i and a projection per module)
+    on the same kernels at the same rank, paired interleaved trials with a 95 % CI of the relative
+    difference (layerwise - group) / group: LLaMA-2-7B QKV decode T = 1 (rotating weight copies),
+    gate/up prefill T = 2048, LLaMA-3.1-8B QKV at T = 64 (rotating copies) and gate/up at T = 4096."""
+    import torch
+    import workload as W
+    out = {}
+    # QKV decode, rotating copies so that the weights stream from HBM
+    copies = 20
+    u = W.llama2_qkv_unit(1, device="cuda", layerwise=True)
+    base = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
+    sets = [base] + [[g.QWeight(w.q.clone(), w.sz.clone(), w.n_out, w.k_in) for w in base] for _ in range(copies - 1)]
+    ws = g.make_workspace(1, u.r, 3)
+    ys = [torch.empty(1, w.n_out, dtype=torch.float16, device="cuda") for w in base]
+    it = {"a": 0, "b": 0}
+
+    def grp():
+        it["a"] = (it["a"] + 1) % copies
+        g.group_forward(u.x, sets[it["a"]], u.b, u.a, u.r, True, workspace=ws, y=ys)
+
+    def lw():
+        it["b"] = (it["b"] + 1) % copies
+        g.layerwise_forward(u.x, sets[it["b"]], u.b_layerwise, u.a, u.r, True, workspace=ws, y=ys)
+
+    out["qkv_decode_T1"] = paired_ci(grp, lw, trials=40, calls=20)
+    del sets, base
+    # gate/up prefill T = 2048
+    u = W.llama2_gateup_unit(2048, device="cuda", layerwise=True)
+    w = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
+    ws = g.make_workspace(2048, u.r, 2)
+    ys = [torch.empty(2048, q.n_out, dtype=torch.float16, device="cuda") for q in w]
+    out["gateup_prefill_T2048"] = paired_ci(
+        lambda: g.group_forward(u.x, w, u.b, u.a, u.r, True, workspace=ws, y=ys),
+        lambda: g.layerwise_forward(u.x, w, u.b_layerwise, u.a, u.r, True, workspace=ws, y=ys), trials=30, calls=3)
+    del w, ws, ys
+    torch.cuda.empty_cache()
+    # LLaMA-3.1-8B QKV (T = 64, rotating copies) and gate/up (T = 4096)
+    for T, name in ((64, "qkv"), (4096, "gateup")):
+        units = W.llama3_gqa_units(T, 64, device="cuda", layerwise=True, which=(name,))
+        u = units[0]
+        w0 = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
+        ncp = 40 if T == 64 else 1
+        sets = [w0] + [[g.QWeight(x.q.clone(), x.sz.clone(), x.n_out, x.k_in) for x in w0] for _ in range(ncp - 1)]
+        ws = g.make_workspace(T, 64, len(w0))
+        ys = [torch.empty(T, q.n_out, dtype=torch.float16, device="cuda") for q in w0]
+        it = {"a": 0, "b": 0}
+
+        def grp2():
+            it["a"] = (it["a"] + 1) % ncp
+            g.group_forward(u.x, sets[it["a"]], u.b, u.a, 64, True, workspace=ws, y=ys)
+
+        def lw2():
+            it["b"] = (it["b"] + 1) % ncp
+            g.layerwise_forward(u.x, sets[it["b"]], u.b_layerwise, u.a, 64, True, workspace=ws, y=ys)
+
+        out[f"llama3_{name}_T{T}"] = paired_ci(grp2, lw2, trials=30, calls=10 if T == 64 else 2)
+        del sets, w0, ws, ys, units
+        torch.cuda.empty_cache()
+    out["how"] = ("a = group, b = layerwise; rel_diff = (layerwise - group) / group per trial; positive = group faster; "
+                  "95 % Student-t interval over the trials")
+    return out
+
+
+def extra_w4a8(g, reps=20):
+    """W4A8 (per-token int8 activations on the int8 matrix cores, fp16 correction): LLaMA-2-7B
+    gate/up at T = 2048 (integer matrix-core ops against the 5.0 POP/s int8 peak) and QKV at
+    T = 1 (HBM), with the W4A16 call of the same unit for comparison."""
+    import torch
+    import workload as W
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, T, mk in (("gateup_T2048", 2048, W.llama2_gateup_unit), ("qkv_T1", 1, W.llama2_qkv_unit)):
+        u = mk(T, device="cuda")
+        w = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
+        ws8 = torch.empty(g.w4a8_workspace_bytes(T, 4096, u.r), dtype=torch.uint8, device="cuda")
+        ws16 = g.make_workspace(T, u.r, 1)
+        ys = [torch.empty(T, q.n_out, dtype=torch.float16, device="cuda") for q in w]
+        res = {}
+        for tag, fn in (("w4a8", lambda: g.group_forward_w4a8(u.x, w, u.b, u.a, u.r, True, workspace=ws8, y=ys)),
+                        ("w4a16", lambda: g.group_forward(u.x, w, u.b, u.a, u.r, True, workspace=ws16, y=ys))):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+            t = statistics.median(ts)
+            fl = unit_flops(T, 4096, u.n_outs, u.r, True)
+            nb = unit_bytes(T, 4096, u.n_outs, u.r, True)
+            e = {"us": round(t * 1e6, 2), "tokens_per_s": round(T / t, 1)}
+            if T > 64:
+                peak = 5000.0 if tag == "w4a8" else MFMA_F16_PEAK_TFLOPS
+                e.update({"alg_TOP_per_s": round(fl / t / 1e12, 1), "peak_TOP_per_s": peak,
+                          "frac_peak": round(fl / t / 1e12 / peak, 4)})
+            else:
+                e.update({"TB_per_s": round(nb / t / 1e12, 3), "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4)})
+            res[tag] = e
+        out[name] = res
+        del w, ws8, ws16, ys
+        torch.cuda.empty_cache()
+    out["workload"] = "llama2-7b gate/up T=2048 and QKV T=1, r=64; W4A8 = int8 activation codes per token"
+    return out
+
+
+def extra_moe(g, reps=10):
+    """Qwen1.5-MoE-A2.7B MLP: 60 experts, gate/up group 2048 -> 2 x 1408 and down 1408 -> 2048 per
+    expert, top-4 routing, r = 64, one launch for all experts (plus the projection when
+    correcting): per-expert shared basis and one basis for all experts, T = 1, 64 and 2048 tokens.
+    Bytes are the active experts' algorithmic bytes, flops the routed rows'."""
+    import torch
+    import workload as W
+    stream = torch.cuda.current_stream()
+    E, d, inter, r = 60, 2048, 1408, 64
+    zx = lambda k: torch.zeros(1, k, dtype=torch.float16, device="cuda")
+    gu = [W.make_unit(f"e{e}", "group", zx(d), [inter, inter], r, (0, 8, e), device="cuda") for e in range(E)]
+    mods = [g.MoeModule.stack([g.QWeight.from_workload(u.weights[i]) for u in gu], [u.a[i] for u in gu])
+            for i in range(2)]
+    b_exp = torch.stack([u.b for u in gu]).contiguous()
+    b_all = gu[0].b
+    dn = [W.make_unit(f"d{e}", "solo", zx(inter), [d], r, (0, 9, e), device="cuda") for e in range(E)]
+    dmods = [g.MoeModule.stack([g.QWeight.from_workload(u.weights[0]) for u in dn], [u.a[0] for u in dn])]
+    db = torch.stack([u.b for u in dn]).contiguous()
+    del gu, dn
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return statistics.median(ts)
+
+    out = {}
+    for T in (1, 64, 2048):
+        x = W.make_x(T, d, 0.77, (0, 10, T), device="cuda")
+        rt, off = W.moe_routing(T, E, 4, (0, 10, T))
+        rt, off = rt.cuda(), off.cuda()
+        n = T * 4
+        active = int((torch.diff(off) > 0).sum())
+        ys = [torch.empty(n, inter, dtype=torch.float16, device="cuda") for _ in range(2)]
+        res = {"routed_rows": n, "active_experts": active}
+        for share, tag in ((0, "gateup_per_expert"), (1, "gateup_all_experts")):
+            ws = g.make_workspace(1, 8, 1, min_bytes=g.moe_workspace_bytes(n, T, r, share))
+            b = b_exp if share == 0 else b_all
+            t = timed(lambda: g.moe_forward(x, E, mods, b, share, r, True, rt, off, n, workspace=ws, y=ys))
+            nb = active * unit_bytes(0, d, [inter, inter], r, True, 1 if share == 0 else 0) + (
+                r * d * 2 if share == 1 else 0) + T * d * 2 + n * 2 * inter * 2
+            fl = 2 * n * d * 2 * inter + (2 * n if share == 0 else 2 * T) * d * r + 2 * n * r * 2 * inter
+            res[tag] = {"us": round(t * 1e6, 2), "tokens_per_s": round(T / t, 1),
+                        "TB_per_s": round(nb / t / 1e12, 3), "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4),
+                        "TFLOP_per_s": round(fl / t / 1e12, 1), "frac_mfma_f16_peak": round(fl / t / 1e12 / 2500.0, 4)}
+        h = W.make_x(n, inter, 0.77, (0, 11, T), device="cuda")
+        yd = [torch.empty(n, d, dtype=torch.float16, device="cuda")]
+        ws = g.make_workspace(1, 8, 1, min_bytes=g.moe_workspace_bytes(n, n, r, 0))
+        t = timed(lambda: g.moe_forward(h, E, dmods, db, 0, r, True, None, off, n, workspace=ws, y=yd))
+        nb = active * unit_bytes(0, inter, [d], r, True) + n * inter * 2 + n * d * 2
+        fl = 2 * n * inter * d + 2 * n * inter * r + 2 * n * r * d
+        res["down_per_expert"] = {"us": round(t * 1e6, 2), "TB_per_s": round(nb / t / 1e12, 3),
+                                  "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4), "TFLOP_per_s": round(fl / t / 1e12, 1),
+                                  "frac_mfma_f16_peak": round(fl / t / 1e12 / 2500.0, 4)}
+        out[f"T{T}"] = res
+        del x, h, ys, yd, ws
+    out["workload"] = "Qwen1.5-MoE-A2.7B MLP, 60 experts, gate/up 2 x 1408 over d = 2048, down 1408 -> 2048, top-4, r=64"
+    del mods, dmods, b_exp, db
+    torch.cuda.empty_cache()
     return out
 
 
@@ -648,16 +882,15 @@ def main():
             for u in units_lw:
                 call_unit(u, g, ws_lw, layerwise=False)
 
-        # alternate the two schedules step by step (same clock and power state for both)
-        t_lw = t_gr = 0.0
-        for _ in range(args.warmup):
-            run_lw()
-            run_grp()
-        for _ in range(args.steps):
-            t_lw += time_steps(run_lw, 1, 0)
-            t_gr += time_steps(run_grp, 1, 0)
-        t_lw /= args.steps
-        t_gr /= args.steps
+        # alternate the two schedules step by step (same clock and power state for both); the
+        # per-step pairs give a 95 % interval of the relative difference
+        # each schedule is captured in a HIP graph (128 launches issued from Python per step would
+        # leave the GPU waiting for the host) and the replays are timed in pairs
+        gr_grp, gr_lw = graphed(run_grp), graphed(run_lw)
+        path_ci = paired_ci(gr_grp.replay, gr_lw.replay, trials=max(20, args.steps), calls=1)
+        del gr_grp, gr_lw
+        t_gr = path_ci["a_us_median"] * 1e-6
+        t_lw = path_ci["b_us_median"] * 1e-6
         d_lw = d_gr = 0.0
         for _ in range(2):
             d_lw += sum(per_launch_events(units_lw, descr_lw, g, max(1, args.event_reps // 2), layerwise=True))
@@ -667,7 +900,7 @@ def main():
         extra["layerwise_vs_group_T1_path"] = {
             "group_us_per_step_percall": round(t_gr * 1e6, 1), "layerwise_us_per_step_percall": round(t_lw * 1e6, 1),
             "group_kernel_sum_us": round(d_gr * 1e6, 1), "layerwise_kernel_sum_us": round(d_lw * 1e6, 1),
-            "kernel_speedup": round(d_lw / d_gr, 4)}
+            "kernel_speedup": round(d_lw / d_gr, 4), "paired_steps_ci": path_ci}
         del units_lw
         torch.cuda.empty_cache()
         log(f"[bench] layerwise {d_lw * 1e6:.1f} us vs group {d_gr * 1e6:.1f} us (kernel sums)")
@@ -697,6 +930,12 @@ def main():
             e = extra["prefill_gateup_T2048"][k]
             e["frac_mfma_measured_peak"] = round(e["alg_TFLOP_per_s"] / peaks["mfma_f16_TFLOP_per_s"], 4)
         log(f"[bench] gate/up prefill T=2048: {extra['prefill_gateup_T2048']}")
+        extra["group_vs_layerwise"] = extra_group_vs_layerwise(g)
+        log(f"[bench] group vs layerwise: {extra['group_vs_layerwise']}")
+        extra["w4a8"] = extra_w4a8(g)
+        log(f"[bench] W4A8: {extra['w4a8']}")
+        extra["moe_qwen15"] = extra_moe(g)
+        log(f"[bench] MoE: {extra['moe_qwen15']}")
         extra["restore_selection_32L"] = extra_restore_selection(g)
         e = extra["restore_selection_32L"]
         e["frac_hbm_measured_peak"] = round(e["GB_per_s"] / peaks["hbm_read_GB_per_s"], 4)
