@@ -146,7 +146,7 @@ def source_digest():
     """sha256 over the decode kernel's sources: counter readings are only valid for this code."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("decode.hip", "glowq_internal.h"):
+    for f in ("decode.hip", "handoff.h", "glowq_internal.h"):
         with open(os.path.join(ROOT, "rank_error_compensation_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

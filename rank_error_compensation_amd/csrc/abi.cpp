@@ -183,13 +183,19 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
     for (int i = 0; i < c.m; ++i) row_tiles += ceil_div(c.w[i].n_out, 128);
     const bool prefill = c.T > kDecodeMaxT || (c.T > kDecodeWideT && row_tiles >= kPrefillMinRowTiles);
     const int32_t rp = (int32_t)r_pad_of(c.r);
+    int tt = 0, rr = 0, ks = 1;
+    if (prefill) choose_prefill_shape(c, tt, rr, ks);
+    // 17 .. 64 tokens on the small prefill tiles: the projection is formed inside the launch by
+    // producer workgroups and handed over as tagged pairs (one launch instead of three)
+    const bool fuse = c.correct && prefill && c.T <= kDecodeMaxT && !(tt == 8 && rr == 4);
+    if (fuse && tt == 4 && rr == 2 && ks == 4) ks = 2;  // the fused 64 x 128 tile: two wave groups
     void* R = nullptr;
     if (c.correct) {
         uint8_t* base = static_cast<uint8_t*>(workspace) + kWsHeader;
-        R = prefill ? base + kDecodeAreaBytes : base;
+        R = (prefill && !fuse) ? base + kDecodeAreaBytes : base;
     }
 
-    if (c.correct && prefill) {
+    if (c.correct && prefill && !fuse) {
         if (launch_projection(c, R, stream) != hipSuccess) return GLOWQ_ERR_HIP;
     }
 
@@ -213,8 +219,7 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
         const int64_t ptt = c.T == 1 ? 1 : (c.T <= 4 ? 4 : 16);
         f.n_prod = (int32_t)(ceil_div(total, f.prod_rows) * ceil_div(c.T, ptt));
     }
-    int tt = 0, rr = 0, ks = 1;
-    if (prefill) choose_prefill_shape(c, tt, rr, ks);
+    if (fuse) f.n_prod = (int32_t)(ceil_div(c.T, 16) * c.n_proj * (rp / 16));  // 16 x 16 tiles of R
     f.tile_tt = tt;
     f.tile_rr = rr;
     f.tile_ks = ks;

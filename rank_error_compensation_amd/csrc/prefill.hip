@@ -16,7 +16,7 @@
 //
 // Workgroups are numbered XCD-aware: consecutive logical tiles (same weight block, successive
 // token blocks) land on the same XCD and share its L2.
-#include "glowq_internal.h"
+#include "handoff.h"
 
 namespace glowq {
 
@@ -28,19 +28,104 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
+// Producer of a fused launch (17 .. 64 tokens): workgroup p < n_prod forms one 16-token x 16-rank
+// tile of the stacked projections R_p = X B_p^T over all of d with its first four waves (32-input
+// steps interleaved over the waves, four steps of loads in flight, sums added through LDS in wave
+// order), and writes it as tagged pairs in every per-XCD copy, as the decode producers do; waves
+// past the fourth only take part in the barriers.  Tokens past T and ranks past r are never stored.
+__device__ void produce_tile(const ForwardArgs& a, int p) {
+    __shared__ f4 red[3][64];
+    __shared__ uint32_t ptag;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t epoch0 = 0;
+    if (tid == 0) epoch0 = load_epoch(a);
+    const int T = a.T, d = a.d, r = a.r, rp = a.r_pad;
+    const int n_rt = a.n_proj * (rp / 16);  // rank tiles over the stacked projections
+    const int tt = p / n_rt, jt = p - tt * n_rt;
+    const int pi = (jt * 16) / rp, j0 = (jt * 16) - pi * rp;
+    const int t0 = 16 * tt;
+    const int t = t0 + (lane & 15), j = j0 + (lane & 15);
+    const bool t_ok = t < T, j_ok = j < r;
+    const int kofs = 8 * (lane >> 4);
+    const _Float16* xr = a.x + (size_t)(t_ok ? t : 0) * d + kofs;
+    const _Float16* br = pick_bp(a, pi) + (size_t)(j_ok ? j : 0) * d + kofs;
+    const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (wave < 4) {
+        const int n = d / 128;  // 32-input steps of this wave: 128 i + 32 wave
+        for (int c = 0; c < n; c += 4) {
+            h8 xa[4], bb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int kk = 32 * wave + 128 * min(c + u, n - 1);
+                xa[u] = t_ok ? load_h8(xr + kk) : zero8;
+                bb[u] = j_ok ? load_h8(br + kk) : zero8;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (c + u < n) acc = mfma16(xa[u], bb[u], acc);
+        }
+        if (wave > 0) red[wave - 1][lane] = acc;
+    }
+    if (tid == 0) {
+        ptag = epoch0 + 1u;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the epoch read completes before the arrival
+    }
+    __syncthreads();
+    int arrived = 0;
+    if (tid == 0) arrived = arrive(a);
+    const uint32_t tag = ptag;
+    u64* R = reinterpret_cast<u64*>(a.R);
+    if (tag == 1u || tag == 0xFFFFFFFFu) {
+        // first and last tag of a wrap: clear every pair of the decode area outside this call's range
+        const size_t from = (size_t)kRReplicas * a.n_proj * T * r;
+        for (size_t k = from + (size_t)p * blockDim.x + tid; k < kDecodeAreaPairs; k += (size_t)a.n_prod * blockDim.x)
+            R[k] = 0ull;
+    }
+    if (wave == 0) {
+        f4 v = acc;
+#pragma unroll
+        for (int w = 0; w < 3; ++w) v += red[w][lane];
+        const int jj = j0 + (lane & 15);
+        const size_t copy = (size_t)a.n_proj * T * r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ti = t0 + 4 * (lane >> 4) + i;  // output rows: tokens
+            if (ti < T && jj < r) {
+                const size_t off = ((size_t)pi * T + ti) * r + jj;
+#pragma unroll
+                for (int c = 0; c < kRReplicas; ++c) store_pair(R + c * copy + off, v[i], tag);
+            }
+        }
+    }
+    if (tid == 0) finish(a, arrive_slot(a, arrived), epoch0);
+}
+
 // Small grids: KS groups of four wavefronts per workgroup (256 KS threads) share one output tile
 // and split the input groups between them (group g goes to wave group g % KS), each with its own
 // double-buffered activation tile in LDS; at the end the wave groups' sums are added through LDS
 // in wave-group order (deterministic) and wave group 0 applies the correction and stores.  With
 // KS = 4 a launch of one workgroup per CU keeps four wavefronts on every SIMD.
-template <int TT, int RR, int KS>
+// FUSE (17 .. 64 tokens, correcting calls): the first n_prod workgroups are producers of the
+// projection (produce_tile) and the tiles read R as tagged pairs at their correction step, so the
+// whole call is one launch.
+template <int TT, int RR, int KS, bool FUSE>
 __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(const ForwardArgs args) {
     constexpr int BM = 16 * TT;
     constexpr int LS = 136;              // LDS row stride in halves (128 + 8 padding)
     constexpr int NCH = BM * 16 / 256;   // 16-byte X chunks per thread per group
     __shared__ __attribute__((aligned(16))) _Float16 xs[KS][2][BM * LS];
+    // hand-off state of thread 0 kept in LDS, not registers (the 1024-thread tiles have none spare)
+    __shared__ uint32_t tag_lds;
+    __shared__ int arrived_lds;
 
-    const int L = xcd_remap(blockIdx.x, args.n_tiles);
+    if (FUSE && (int)blockIdx.x < args.n_prod) {
+        produce_tile(args, blockIdx.x);
+        return;
+    }
+    if (FUSE && threadIdx.x == 0) tag_lds = load_epoch(args) + 1u;
+    const int L = xcd_remap(blockIdx.x - (FUSE ? args.n_prod : 0), args.n_tiles);
     const int mb = L % args.m_tiles, nbl = L / args.m_tiles;
     const ModuleArgs M = args.mod[module_of(args, nbl)];
     const int nb = nbl - M.tile_begin;
@@ -95,7 +180,9 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
     }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) *reinterpret_cast<u4*>(&xs[kg][0][xdst[c]]) = st[c];
-    __syncthreads();
+    __syncthreads();  // tag_lds written (the epoch read complete) before the arrival
+    if (FUSE && threadIdx.x == 0) arrived_lds = arrive(args);
+    const uint32_t tag = FUSE ? tag_lds : 0u;
 
     f4 acc[TT][RR];
 #pragma unroll
@@ -154,11 +241,29 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
         __syncthreads();
     }
 
+    // fused launch: the tile's projection rows, waited for as tagged pairs by all threads at once
+    // and kept in LDS as fp16 (after the wave groups' reduction area; the activation buffers are
+    // free after the loop's last barrier)
+    constexpr int kRedBytes = (KS - 1) * TT * RR * 256 * 16;
+    _Float16* rl = reinterpret_cast<_Float16*>(reinterpret_cast<uint8_t*>(&xs[0][0][0]) + kRedBytes);
+    if (FUSE && args.r > 0 && M.a != nullptr) {
+        static_assert(sizeof(xs) >= kRedBytes + BM * kMaxRank * 2, "projection rows fit");
+        const int r = args.r, rp = args.r_pad;
+        const u64* Rp = reinterpret_cast<const u64*>(args.R) +
+                        (size_t)(blockIdx.x & (kRReplicas - 1)) * args.n_proj * T * r + (size_t)M.proj * T * r;
+        for (int k = threadIdx.x; k < BM * rp; k += 256 * KS) {
+            const int tl = k / rp, col = k - tl * rp, t = m0 + tl;
+            const float v = (t < T && col < r) ? load_pair(args, Rp + (size_t)t * r + col, tag) : 0.f;
+            rl[k] = (_Float16)v;
+        }
+        __syncthreads();
+    }
+
     if (KS > 1) {
         // wave groups 1 .. KS-1 hand their sums to wave group 0 through LDS (the activation
         // buffers are free after the loop's last barrier)
         f4* red = reinterpret_cast<f4*>(&xs[0][0][0]);
-        static_assert(sizeof(xs) >= (KS - 1) * TT * RR * 256 * sizeof(f4), "reduction space");
+        static_assert(sizeof(xs) >= kRedBytes, "reduction space");
         if (kg > 0) {
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
@@ -175,7 +280,9 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
                 for (int rr = 0; rr < RR; ++rr) acc[tt][rr] += red[(((k - 1) * TT + tt) * RR + rr) * 256 + tid];
     }
 
-    // correction: r_pad / 32 more K steps, A-operand A_i rows, B-operand R tokens
+    // correction: r_pad / 32 more K steps, A-operand A_i rows, B-operand R tokens (fp16 from the
+    // projection launch, or the producers' fp32 pairs of this launch rounded to fp16)
+    if (FUSE && threadIdx.x == 0) arrived_lds = arrive_slot(args, arrived_lds);  // now the slot result
     if (args.r > 0 && M.a != nullptr) {
         const int r = args.r, rp = args.r_pad;
         const _Float16* R = reinterpret_cast<const _Float16*>(args.R) + (size_t)M.proj * T * rp;
@@ -191,7 +298,11 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
                 const int t = m0 + 16 * tt + (lane & 15);
-                const h8 b = t < T ? load_h8(R + (size_t)t * rp + col) : zero8;
+                h8 b = zero8;
+                if (FUSE)
+                    b = *reinterpret_cast<const h8*>(rl + (16 * tt + (lane & 15)) * rp + col);  // zero past T
+                else
+                    b = t < T ? load_h8(R + (size_t)t * rp + col) : zero8;
 #pragma unroll
                 for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = mfma16(a[rr], b, acc[tt][rr]);
             }
@@ -218,6 +329,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
             }
         }
     }
+    if (FUSE && threadIdx.x == 0) finish(args, arrived_lds, tag_lds - 1u);
 }
 
 // Wide tile for large grids: BM = 128 tokens x BN = 256 rows, wave w owning 4 row tiles of 16
@@ -407,30 +519,40 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
     }
 }
 
-hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
-    const dim3 grid(a.n_tiles), block(256);
-    if (a.tile_tt == 8 && a.tile_rr == 4) {
-        hipLaunchKernelGGL(prefill_wide_kernel, grid, block, 2 * 8 * 4 * 64 * sizeof(u4), stream, a);
-        return hipGetLastError();
-    }
+template <bool FUSE>
+static hipError_t launch_prefill_small(const ForwardArgs& a, hipStream_t stream) {
+    const dim3 grid(a.n_tiles + (FUSE ? a.n_prod : 0));
     if (a.tile_rr == 1) {  // small grids: 64 or 32 tokens x 64 rows, 4 wave groups
         if (a.tile_ks != 4 || (a.tile_tt != 4 && a.tile_tt != 2)) return hipErrorInvalidValue;
         if (a.tile_tt == 4)
-            hipLaunchKernelGGL((prefill_kernel<4, 1, 4>), grid, dim3(1024), 0, stream, a);
+            hipLaunchKernelGGL((prefill_kernel<4, 1, 4, FUSE>), grid, dim3(1024), 0, stream, a);
         else
-            hipLaunchKernelGGL((prefill_kernel<2, 1, 4>), grid, dim3(1024), 0, stream, a);
+            hipLaunchKernelGGL((prefill_kernel<2, 1, 4, FUSE>), grid, dim3(1024), 0, stream, a);
         return hipGetLastError();
     }
     if (a.tile_tt != 4 || a.tile_rr != 2) return hipErrorInvalidValue;
-    if (a.tile_ks == 4)
-        hipLaunchKernelGGL((prefill_kernel<4, 2, 4>), grid, dim3(1024), 0, stream, a);
+    if (a.tile_ks == 4) {
+        // the fused form of this tile would need more than the 128 registers of a 1024-thread
+        // workgroup; the launcher gives fused calls two wave groups instead
+        if constexpr (FUSE) return hipErrorInvalidValue;
+        else hipLaunchKernelGGL((prefill_kernel<4, 2, 4, FUSE>), grid, dim3(1024), 0, stream, a);
+    }
     else if (a.tile_ks == 2)
-        hipLaunchKernelGGL((prefill_kernel<4, 2, 2>), grid, dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((prefill_kernel<4, 2, 2, FUSE>), grid, dim3(512), 0, stream, a);
     else if (a.tile_ks == 1)
-        hipLaunchKernelGGL((prefill_kernel<4, 2, 1>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((prefill_kernel<4, 2, 1, FUSE>), grid, dim3(256), 0, stream, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
+    if (a.tile_tt == 8 && a.tile_rr == 4) {
+        if (a.n_prod > 0) return hipErrorInvalidValue;  // the wide tile takes R from a projection launch
+        hipLaunchKernelGGL(prefill_wide_kernel, dim3(a.n_tiles), dim3(256), 2 * 8 * 4 * 64 * sizeof(u4), stream, a);
+        return hipGetLastError();
+    }
+    return a.n_prod > 0 ? launch_prefill_small<true>(a, stream) : launch_prefill_small<false>(a, stream);
 }
 
 }  // namespace glowq
