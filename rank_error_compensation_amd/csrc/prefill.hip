@@ -29,15 +29,18 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 }
 
 // Producer of a fused launch (17 .. 64 tokens): workgroup p < n_prod forms one 16-token x 16-rank
-// tile of the stacked projections R_p = X B_p^T over all of d with its first four waves (32-input
-// steps interleaved over the waves, four steps of loads in flight, sums added through LDS in wave
-// order), and writes it as tagged pairs in every per-XCD copy, as the decode producers do; waves
-// past the fourth only take part in the barriers.  Tokens past T and ranks past r are never stored.
+// tile of the stacked projections R_p = X B_p^T over all of d with all its waves (32-input steps
+// interleaved over the waves, eight steps of loads in flight per wave, sums added through LDS in
+// wave order), and writes it as tagged pairs in every per-XCD copy, as the decode producers do.
+// Tokens past T and ranks past r are never stored.
+constexpr int kProdMaxWaves = 16;
+
 __device__ void produce_tile(const ForwardArgs& a, int p) {
-    __shared__ f4 red[3][64];
+    __shared__ f4 red[kProdMaxWaves - 1][64];
     __shared__ uint32_t ptag;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = (int)(blockDim.x >> 6);
     uint32_t epoch0 = 0;
     if (tid == 0) epoch0 = load_epoch(a);
     const int T = a.T, d = a.d, r = a.r, rp = a.r_pad;
@@ -52,22 +55,22 @@ __device__ void produce_tile(const ForwardArgs& a, int p) {
     const _Float16* br = pick_bp(a, pi) + (size_t)(j_ok ? j : 0) * d + kofs;
     const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     f4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (wave < 4) {
-        const int n = d / 128;  // 32-input steps of this wave: 128 i + 32 wave
-        for (int c = 0; c < n; c += 4) {
-            h8 xa[4], bb[4];
+    constexpr int S = 8;
+    const int n = d / 32;  // 32-input steps; wave w takes w, w + nw, ...
+    for (int c = wave; c < n; c += S * nw) {
+        h8 xa[S], bb[S];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int kk = 32 * wave + 128 * min(c + u, n - 1);
-                xa[u] = t_ok ? load_h8(xr + kk) : zero8;
-                bb[u] = j_ok ? load_h8(br + kk) : zero8;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (c + u < n) acc = mfma16(xa[u], bb[u], acc);
+        for (int u = 0; u < S; ++u) {
+            const int st = c + u * nw;
+            const int kk = 32 * (st < n ? st : c);  // steps past the end reload the first (unused)
+            xa[u] = t_ok ? load_h8(xr + kk) : zero8;
+            bb[u] = j_ok ? load_h8(br + kk) : zero8;
         }
-        if (wave > 0) red[wave - 1][lane] = acc;
+#pragma unroll
+        for (int u = 0; u < S; ++u)
+            if (c + u * nw < n) acc = mfma16(xa[u], bb[u], acc);
     }
+    if (wave > 0) red[wave - 1][lane] = acc;
     if (tid == 0) {
         ptag = epoch0 + 1u;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the epoch read completes before the arrival
@@ -85,8 +88,7 @@ __device__ void produce_tile(const ForwardArgs& a, int p) {
     }
     if (wave == 0) {
         f4 v = acc;
-#pragma unroll
-        for (int w = 0; w < 3; ++w) v += red[w][lane];
+        for (int w = 1; w < nw; ++w) v += red[w - 1][lane];  // fixed order: deterministic
         const int jj = j0 + (lane & 15);
         const size_t copy = (size_t)a.n_proj * T * r;
 #pragma unroll
