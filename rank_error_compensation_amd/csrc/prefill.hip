@@ -351,8 +351,19 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
     constexpr int TT = 8, RR = 4, BM = 128;
     extern __shared__ __attribute__((aligned(16))) u4 xw[];  // [2][TT * 4][64]
 
-    const int L = xcd_remap(blockIdx.x, args.n_tiles);
-    const int mb = L % args.m_tiles, nbl = L / args.m_tiles;
+    int mb, nbl;
+    if ((args.m_tiles & 7) == 0) {
+        // XCD x (workgroups b with b % 8 == x) owns the token blocks [x m / 8, (x + 1) m / 8) for
+        // every row block: its slice of the activations stays in its L2 while the weights stream
+        // through (the row blocks in order, each used by the XCD's token blocks one after another)
+        const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3, mp = args.m_tiles >> 3;
+        nbl = local / mp;
+        mb = xcd * mp + (local - nbl * mp);
+    } else {
+        const int L = xcd_remap(blockIdx.x, args.n_tiles);
+        mb = L % args.m_tiles;
+        nbl = L / args.m_tiles;
+    }
     const ModuleArgs M = args.mod[module_of(args, nbl)];
     const int nb = nbl - M.tile_begin;
     const int m0 = mb * BM;
