@@ -225,7 +225,7 @@ struct MoeArgs {
     int32_t r, r_pad;
     const _Float16* R;          // fp16 projection rows [.][r_pad]
     int32_t r_by_token;         // 1: R row = the row's token (one B for all experts); 0: R row = j
-    int32_t tile_tt;            // 16 TT routed rows per block
+    int32_t tile_tt;            // 16 TT routed rows per block (0: decode items of 16 rows x 16 routed rows)
     int32_t* err;               // workspace error word (bit 1: routing data out of range)
     const _Float16* b;          // per-expert right factors [n_exp][r][d] (projection launch)
     _Float16* Rout;             // projection output [n_rows][r_pad]

@@ -361,6 +361,134 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(const MoeArgs a) {
     }
 }
 
+// Decode-sized calls (at most 16 routed rows per expert on average): items (expert e, one 16-row
+// tile of one module, block of 16 of e's routed rows).  The four waves split the input groups
+// (group g to wave g % 4), each keeping a ring of four groups of weight loads in flight; the routed
+// rows' activations are read from L2 with each group (they are few); weights are turned into exact
+// fp16 (q - z) and each group's sums scaled in fp32; every wave adds its share of the correction
+// steps (rank columns 32 kb, kb = wave, wave + 4, ...), and the four partial tiles are added in LDS
+// in wave order before the one fp16 rounding.
+__global__ __launch_bounds__(256) void moe_decode_kernel(const MoeArgs a) {
+    __shared__ MoeShared s;
+    __shared__ f4 red[4][64];
+    moe_routing(a, 16, s);
+    constexpr int U = 4;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int d = a.d, G = a.G;
+    const NibConsts nc = nib_consts();
+    const int kofs = 8 * (lane >> 4);
+    const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int total = s.total * a.n_rb;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        int e = 0;
+        {
+            int lo = 0, hi = a.n_exp - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s.pre[mid] * a.n_rb <= item) lo = mid;
+                else hi = mid - 1;
+            }
+            e = lo;
+        }
+        const int nbe = s.pre[e + 1] - s.pre[e];
+        const int local = item - s.pre[e] * a.n_rb;
+        const int rb = local / nbe, tb = local - rb * nbe;
+        int mi = 0;
+#pragma unroll
+        for (int k = 1; k < kMoeMaxMod; ++k) mi += (k < a.m && rb >= a.rb_begin[k]) ? 1 : 0;
+        mi = __builtin_amdgcn_readfirstlane(mi);
+        const int n_out = a.n_out[mi], nt16 = a.n_tiles16[mi];
+        const int rt = rb - a.rb_begin[mi];  // this item's 16-row tile
+        const uint8_t* qb = a.q[mi] + (size_t)e * a.qbytes[mi] + (size_t)rt * 1024 + lane * 16;
+        const uint8_t* zb = a.sz[mi] + (size_t)e * a.szbytes[mi] + (size_t)rt * 64;
+        const size_t qstride = (size_t)nt16 * 1024, szstride = (size_t)nt16 * 64;
+        const _Float16* Ma = a.a[mi] != nullptr ? a.a[mi] + (size_t)e * n_out * a.r : nullptr;
+        const int j0 = s.off[e] + tb * 16, j1 = s.end[e];
+        const int jl = j0 + (lane & 15);
+        const bool row_ok = jl < j1;
+        const int tok = moe_token(a, row_ok ? jl : j0);
+        const _Float16* xr = a.x + (size_t)tok * d + kofs;
+        const int n_my = G > wave ? (G - wave + 3) / 4 : 0;  // groups g = wave + 4 i
+
+        u4 qv[U];
+        uint32_t zso[U];
+        u4 zs4[U];
+        auto issue = [&](int u, int i) {
+            const int g = wave + 4 * min(i, max(n_my - 1, 0));
+            qv[u] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(qb + (size_t)g * qstride));
+            zso[u] = *reinterpret_cast<const uint32_t*>(zb + (size_t)g * szstride + (lane & 15) * 4);
+            zs4[u] = *reinterpret_cast<const u4*>(zb + (size_t)g * szstride + (lane >> 4) * 16);
+        };
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](int u, int i) {
+            // the routed rows' activations of this group come from L2 here: prefetching them with the
+            // weights (16 more registers per slot) measured slower at every size
+            const int g = wave + 4 * i;
+            h8 bx[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bx[j] = row_ok ? load_h8(xr + (size_t)g * kGroup + 32 * j) : zero8;
+            h2 c1024, c64;
+            zero_consts(zso[u], c1024, c64);
+            f4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part = mfma16(nib8_minus_z(qv[u][j], c1024, c64, nc), bx[j], part);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] += (float)as_h2(zs4[u][k])[1] * part[k];
+        };
+        if (n_my > 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) issue(u, u);
+            int i0 = 0;
+            for (; i0 + U < n_my; i0 += U) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    compute(u, i0 + u);
+                    issue(u, i0 + U + u);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (i0 + u < n_my) compute(u, i0 + u);
+        }
+        // this wave's share of the correction: A rows of the tile x R rows of the routed block
+        if (a.r > 0 && Ma != nullptr) {
+            const int r = a.r, rp = a.r_pad;
+            for (int kb = wave; kb * 32 < r; kb += 4) {
+                const int col = 32 * kb + kofs;
+                const int row = rt * 16 + (lane & 15);
+                const h8 av = (row < n_out && col < r) ? load_h8(Ma + (size_t)row * r + col) : zero8;
+                h8 bv = zero8;
+                if (row_ok && col < r) {
+                    const int ri = a.r_by_token ? tok : jl;
+                    bv = load_h8(a.R + (size_t)ri * rp + col);
+                }
+                acc = mfma16(av, bv, acc);
+            }
+        }
+        red[wave][lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+            f4 v = red[0][lane];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) v += red[w][lane];  // fixed order: deterministic
+            const int row0 = rt * 16 + 4 * (lane >> 4);
+            if (row_ok) {
+                _Float16* yrow = a.y[mi] + (size_t)jl * n_out;
+                if ((n_out & 3) == 0 && row0 + 3 < n_out) {
+                    const h2 lo = {(_Float16)v[0], (_Float16)v[1]}, hi = {(_Float16)v[2], (_Float16)v[3]};
+                    *reinterpret_cast<u2*>(yrow + row0) = u2{as_u32(lo), as_u32(hi)};
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (row0 + i < n_out) yrow[row0 + i] = (_Float16)v[i];
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
 template <int NJ>
 static void launch_moe_proj_nj(const MoeArgs& a, unsigned grid, hipStream_t stream) {
     hipLaunchKernelGGL((moe_proj_kernel<NJ>), dim3(grid), dim3(256), 0, stream, a);
@@ -384,7 +512,8 @@ hipError_t launch_moe_proj(const MoeArgs& a, int64_t max_items, hipStream_t stre
 
 hipError_t launch_moe_gemm(const MoeArgs& a, int64_t max_items, hipStream_t stream) {
     const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(max_items, kMoeMaxGrid)));
-    if (a.tile_tt == 1) hipLaunchKernelGGL((moe_gemm_kernel<1, 2>), grid, dim3(256), 0, stream, a);
+    if (a.tile_tt == 0) hipLaunchKernelGGL(moe_decode_kernel, grid, dim3(256), 0, stream, a);
+    else if (a.tile_tt == 1) hipLaunchKernelGGL((moe_gemm_kernel<1, 2>), grid, dim3(256), 0, stream, a);
     else if (a.tile_tt == 2) hipLaunchKernelGGL((moe_gemm_kernel<2, 2>), grid, dim3(256), 0, stream, a);
     else if (a.tile_tt == 4) hipLaunchKernelGGL((moe_gemm_kernel<4, 2>), grid, dim3(256), 0, stream, a);
     else return hipErrorInvalidValue;
