@@ -751,11 +751,26 @@ def achievable_peaks(reps=5):
     e1.record(stream)
     torch.cuda.synchronize()
     mfma = fl / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    # the 16x16x32 instruction the GEMM kernels use, with 4 and 16 independent accumulators per wave
+    shape_rates = {}
+    ssink = torch.empty(1024 * 256 * 16, dtype=torch.uint8, device="cuda")
+    for chains in (4, 16):
+        probe.mfma_shape(1, chains, 100, ssink, 1024)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fl = 0.0
+        for _ in range(reps):
+            fl += probe.mfma_shape(1, chains, 8000, ssink, 1024)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        shape_rates[f"mfma_16x16x32_f16_{chains}_chains_TFLOP_per_s"] = round(fl / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
     torch.cuda.empty_cache()
-    return {"hbm_read_GB_per_s": round(hbm, 1), "mfma_f16_TFLOP_per_s": round(mfma, 1),
+    return {"hbm_read_GB_per_s": round(hbm, 1), "mfma_f16_TFLOP_per_s": round(mfma, 1), **shape_rates,
             "how": "probe library: 4 GiB nontemporal streaming read (best of 512..4096 workgroups of 256 "
                    "threads, 8 x 16 B in flight each); v_mfma_f32_32x32x16_f16 loop on registers (512 x 4 "
-                   "waves, 4 independent chains each, sustained over 5 launches)"}
+                   "waves, 4 independent chains each, sustained over 5 launches); v_mfma_f32_16x16x32_f16 loop with 4 "
+                   "and 16 accumulators per wave (1024 x 4 waves): the 16x16x32 instruction needs about 16 "
+                   "independent accumulators per wave to reach the full rate"}
 
 
 def launch_sequence_floor(nbytes, reps=5):

@@ -40,6 +40,13 @@ int glowq_probe_read_sequence(const void* src_dev, const int64_t* bytes, int32_t
 /* Dense fp16 floating-point operations one glowq_probe_mfma_f16 call performs. */
 double glowq_probe_mfma_f16_flops(int64_t iters, int32_t blocks);
 
+/* Matrix-core issue rate of one fp16 instruction shape: shape 0 = v_mfma_f32_32x32x16_f16,
+ * 1 = v_mfma_f32_16x16x32_f16; chains = 4, 8 or 16 independent accumulators per wave, iters
+ * iterations, blocks workgroups of 4 waves; sink_dev takes blocks * 256 * 16 bytes.  Asynchronous. */
+int glowq_probe_mfma_shape(int32_t shape, int32_t chains, int64_t iters, void* sink_dev, int32_t blocks,
+                           hipStream_t stream);
+double glowq_probe_mfma_shape_flops(int32_t shape, int32_t chains, int64_t iters, int32_t blocks);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,9 +69,76 @@ __global__ __launch_bounds__(256) void mfma_kernel(int64_t iters, f4* __restrict
     }
 }
 
+// Matrix-core rate of one fp16 instruction shape with C independent accumulation chains per wave:
+// SHAPE 0 = v_mfma_f32_32x32x16_f16 (16 outputs per lane), 1 = v_mfma_f32_16x16x32_f16 (4 outputs
+// per lane).  Enough chains hide each instruction's latency, so the loop measures issue rate.
+typedef float f4x __attribute__((ext_vector_type(4)));
+
+template <int SHAPE, int C>
+__global__ __launch_bounds__(256) void mfma_shape_kernel(int64_t iters, f4* __restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    h8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (_Float16)((float)((lane + e) & 3) * 0.25f);
+        b[e] = (_Float16)((float)((lane * 3 + e) & 3) * 0.125f);
+    }
+    f4 out = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (SHAPE == 0) {
+        f16x acc[C];
+#pragma unroll
+        for (int k = 0; k < C; ++k)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[k][i] = 0.f;
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int k = 0; k < C; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[k], 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < C; ++k)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) out[i & 3] += acc[k][i];
+    } else {
+        f4x acc[C];
+#pragma unroll
+        for (int k = 0; k < C; ++k) acc[k] = f4x{0.f, 0.f, 0.f, 0.f};
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int k = 0; k < C; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[k], 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < C; ++k) out += acc[k];
+    }
+    sink[(uint64_t)blockIdx.x * 256 + threadIdx.x] = out;
+}
+
 }  // namespace
 
 extern "C" {
+
+int glowq_probe_mfma_shape(int32_t shape, int32_t chains, int64_t iters, void* sink_dev, int32_t blocks,
+                           hipStream_t stream) {
+    if (sink_dev == nullptr || blocks < 1 || iters < 0 || (shape != 0 && shape != 1)) return -1;
+    if (chains != 4 && chains != 8 && chains != 16) return -1;
+    if ((reinterpret_cast<uintptr_t>(sink_dev) & 15) != 0) return -1;
+    const dim3 grid((unsigned)blocks), block(256);
+    f4* sk = static_cast<f4*>(sink_dev);
+    if (shape == 0) {
+        if (chains == 4) hipLaunchKernelGGL((mfma_shape_kernel<0, 4>), grid, block, 0, stream, iters, sk);
+        else if (chains == 8) hipLaunchKernelGGL((mfma_shape_kernel<0, 8>), grid, block, 0, stream, iters, sk);
+        else hipLaunchKernelGGL((mfma_shape_kernel<0, 16>), grid, block, 0, stream, iters, sk);
+    } else {
+        if (chains == 4) hipLaunchKernelGGL((mfma_shape_kernel<1, 4>), grid, block, 0, stream, iters, sk);
+        else if (chains == 8) hipLaunchKernelGGL((mfma_shape_kernel<1, 8>), grid, block, 0, stream, iters, sk);
+        else hipLaunchKernelGGL((mfma_shape_kernel<1, 16>), grid, block, 0, stream, iters, sk);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+double glowq_probe_mfma_shape_flops(int32_t shape, int32_t chains, int64_t iters, int32_t blocks) {
+    // 32 x 32 x 16 = 16384 multiply-adds per instruction, 16 x 16 x 32 = 8192
+    return (double)blocks * 4.0 * (double)iters * (double)chains * 32.0 * 32.0 * 16.0 * 2.0 / (shape == 0 ? 1.0 : 2.0);
+}
 
 int glowq_probe_read(const void* src_dev, size_t bytes, void* sink_dev, int32_t blocks, hipStream_t stream) {
     if (src_dev == nullptr || sink_dev == nullptr || blocks < 1 || bytes % 16 != 0) return -1;

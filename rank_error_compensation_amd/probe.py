@@ -14,6 +14,8 @@ EXPORTS = {
     "glowq_probe_read": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "glowq_probe_mfma_f16": (ctypes.c_int, [_i64, _vp, _i32, _vp]),
     "glowq_probe_mfma_f16_flops": (ctypes.c_double, [_i64, _i32]),
+    "glowq_probe_mfma_shape": (ctypes.c_int, [_i32, _i32, _i64, _vp, _i32, _vp]),
+    "glowq_probe_mfma_shape_flops": (ctypes.c_double, [_i32, _i32, _i64, _i32]),
     "glowq_probe_read_sequence": (ctypes.c_int, [_vp, ctypes.POINTER(_i64), _i32, _vp, _vp]),
 }
 _lib = None
@@ -43,6 +45,14 @@ def read(src: torch.Tensor, sink: torch.Tensor, blocks: int) -> None:
                                 _stream())
     if rc != 0:
         raise RuntimeError(f"glowq_probe_read failed ({rc})")
+
+
+def mfma_shape(shape: int, chains: int, iters: int, sink: torch.Tensor, blocks: int) -> float:
+    """One launch of the shape probe; returns its fp16 flops."""
+    rc = lib().glowq_probe_mfma_shape(shape, chains, iters, sink.data_ptr(), blocks, _stream())
+    if rc != 0:
+        raise RuntimeError(f"glowq_probe_mfma_shape failed ({rc})")
+    return lib().glowq_probe_mfma_shape_flops(shape, chains, iters, blocks)
 
 
 def mfma_f16(iters: int, sink: torch.Tensor, blocks: int) -> float:

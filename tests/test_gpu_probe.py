@@ -74,3 +74,45 @@ def test_read_sequence_reads_consecutive_regions():
     got = np.bitwise_xor.reduce(sink.view(torch.int32).cpu().numpy().reshape(-1, 4), axis=0)
     want = np.bitwise_xor.reduce(words.numpy()[n16 * 4:].reshape(-1, 4), axis=0)
     np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("chains", [4, 8, 16])
+def test_mfma_shape_probe_results(chains):
+    """The shape probe's two instructions compute what the kernels assume of them: for
+    v_mfma_f32_16x16x32_f16 lane l holds A[l % 16][8 (l / 16) + e] and B[l % 16][8 (l / 16) + e] and
+    returns D = A B^T at rows 4 (l / 16) + q, column l % 16; for 32x32x16 the layout of the test
+    above (whose four outputs per quad are summed here).  Chains x iters copies, exact."""
+    from rank_error_compensation_amd import probe
+    iters, blocks = 3, 2
+    for shape in (0, 1):
+        sink = torch.zeros(blocks * 256 * 16, dtype=torch.uint8, device="cuda")
+        fl = probe.mfma_shape(shape, chains, iters, sink, blocks)
+        torch.cuda.synchronize()
+        out = sink.view(torch.float32).cpu().numpy().reshape(blocks * 4, 64, 4)
+        want = np.zeros((64, 4))
+        if shape == 1:
+            assert fl == blocks * 4 * iters * chains * 16 * 16 * 32 * 2
+            A = np.zeros((16, 32))
+            B = np.zeros((16, 32))
+            for l in range(64):
+                for e in range(8):
+                    A[l % 16, 8 * (l // 16) + e] = ((l + e) & 3) * 0.25
+                    B[l % 16, 8 * (l // 16) + e] = ((l * 3 + e) & 3) * 0.125
+            D = chains * iters * (A @ B.T)
+            for l in range(64):
+                for q in range(4):
+                    want[l, q] = D[4 * (l // 16) + q, l % 16]
+        else:
+            assert fl == blocks * 4 * iters * chains * 32 * 32 * 16 * 2
+            A = np.zeros((32, 16))
+            B = np.zeros((32, 16))
+            for l in range(64):
+                for e in range(8):
+                    A[l % 32, 8 * (l // 32) + e] = ((l + e) & 3) * 0.25
+                    B[l % 32, 8 * (l // 32) + e] = ((l * 3 + e) & 3) * 0.125
+            D = chains * iters * (A @ B.T)
+            for l in range(64):
+                for i in range(16):
+                    want[l, i & 3] += D[8 * (i // 4) + 4 * (l // 32) + i % 4, l % 32]
+        for w in range(blocks * 4):
+            np.testing.assert_array_equal(out[w], want)
