@@ -28,6 +28,7 @@ be pinned end to end (an exactly rank-r error is reproduced to rounding):
 """
 from __future__ import annotations
 
+import math
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -150,3 +151,22 @@ def topk_restore(scores: Sequence[float], k: int) -> List[bool]:
     order = sorted(range(len(scores)), key=lambda u: (-float(scores[u]), u))
     chosen = set(order[:k])
     return [u in chosen for u in range(len(scores))]
+
+
+def topk_restore_tol(scores: Sequence[float], k: int, rel_tol: float) -> List[bool]:
+    """GlowQ-S selection with the layer-order fallback of key design 4 when the signal is weak:
+    a unit's distance from the best score is measured in steps of rel_tol times the best score,
+    key(u) = floor((max - score(u)) / (rel_tol * max)) in fp64; units with the same key count as
+    equal, and among them the lower index (layer order) goes first.  When every score lies within
+    one step of the best the choice is the first k units; rel_tol = 0 is the exact ranking
+    (topk_restore)."""
+    s = [float(v) for v in scores]
+    mx = max(s) if s else 0.0
+    if rel_tol > 0.0 and mx > 0.0:
+        step = rel_tol * mx
+        keys = [math.floor((mx - v) / step) for v in s]
+        order = sorted(range(len(s)), key=lambda u: (keys[u], u))
+    else:
+        order = sorted(range(len(s)), key=lambda u: (-s[u], u))
+    chosen = set(order[:k])
+    return [u in chosen for u in range(len(s))]

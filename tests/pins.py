@@ -638,6 +638,28 @@ def check_parity_errors(ref):
     assert e["rel_fro"] == 0.0 and e["max_abs_rel"] == 0.0, e
 
 
+def check_restore_tol(sol):
+    """Layer-order fallback: a hand-worked case (scores within 1 % of the best count as equal, the
+    lower index first), every score within one step -> the first k units, rel_tol = 0 and any
+    tolerance on well-separated scores equal the exact ranking (exhaustive search pins that one),
+    an all-zero score vector -> the first k."""
+    sc = [0.5, 0.503, 0.501, 0.2, 0.5029]
+    assert sol.topk_restore_tol(sc, 2, 0.01) == [True, True, False, False, False]
+    assert sol.topk_restore_tol(sc, 4, 0.01) == [True, True, True, False, True]
+    assert sol.topk_restore_tol(sc, 2, 0.0) == [False, True, False, False, True]
+    near = [1.0 + 1e-5 * u for u in range(12)]  # the best is the last unit, all within one step
+    assert sol.topk_restore_tol(near, 5, 1e-3) == [u < 5 for u in range(12)]
+    rng = np.random.default_rng(17)
+    for _ in range(20):
+        v = list(rng.uniform(0, 1, 9))
+        for k in range(10):
+            assert sol.topk_restore_tol(v, k, 0.0) == sol.topk_restore(v, k)
+    spaced = [0.1 * (u % 7) + 0.05 for u in range(7)]  # distinct scores 0.1 apart, max 0.65
+    for k in range(8):
+        assert sol.topk_restore_tol(spaced, k, 0.05) == sol.topk_restore(spaced, k)
+    assert sol.topk_restore_tol([0.0] * 6, 3, 0.01) == [True, True, True, False, False, False]
+
+
 ALL_REF_CHECKS = [check_dequant_exhaustive, check_dequant_golden, check_restore_off,
                   check_associativity_small_int, check_bruteforce, check_row_independence,
                   check_path_mask, check_parity_errors, check_w4a8_quantizer_hand,
@@ -645,4 +667,4 @@ ALL_REF_CHECKS = [check_dequant_exhaustive, check_dequant_golden, check_restore_
                   check_moe_rows]
 ALL_SOL_CHECKS = [check_eckart_young, check_isotropic, check_usage_weighted_risk, check_qr_core,
                   check_cholesky_vs_symmetric, check_randomized_svd, check_scores, check_second_moment,
-                  check_pinv_lift]
+                  check_pinv_lift, check_restore_tol]

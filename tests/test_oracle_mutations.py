@@ -1,6 +1,8 @@
 """Plant plausible mistakes in copies of the oracle (on the CPU) and confirm that at least
 one pin check fails for each: the pins are strong enough to catch a dropped term, a wrong
 sign or index, a transposed operand or a wrong nibble order."""
+import math
+
 import numpy as np
 import pytest
 
@@ -123,6 +125,27 @@ def pinv_identity_on_null(Q, lam, rtol=1e-12):
     cut = rtol * float(lam.max())
     inv = np.where(lam > cut, 1.0 / np.sqrt(np.where(lam > cut, lam, 1.0)), 1.0)
     return (Q * inv) @ Q.T
+
+
+def topk_tol_relative_to_score(scores, k, rel_tol):
+    # steps measured from zero rather than from the best score
+    if rel_tol <= 0:
+        return SOL.topk_restore(scores, k)
+    mx = max(float(v) for v in scores)
+    keys = [-math.floor(float(v) / (rel_tol * mx)) if mx > 0 else 0 for v in scores]
+    order = sorted(range(len(scores)), key=lambda u: (keys[u], u))
+    return [u in set(order[:k]) for u in range(len(scores))]
+
+
+def topk_tol_upper_index(scores, k, rel_tol):
+    # ties within a step go to the higher index
+    mx = max(float(v) for v in scores) if len(scores) else 0.0
+    if rel_tol <= 0 or mx <= 0:
+        order = sorted(range(len(scores)), key=lambda u: (-float(scores[u]), -u))
+    else:
+        keys = [math.floor((mx - float(v)) / (rel_tol * mx)) for v in scores]
+        order = sorted(range(len(scores)), key=lambda u: (keys[u], -u))
+    return [u in set(order[:k]) for u in range(len(scores))]
 
 
 def topk_lowest(scores, k):
@@ -275,6 +298,8 @@ SOL_MUTANTS = {
     "unbalanced_full_s": dict(whitened_factors=whitened_full_s),
     "no_whitening": dict(whitened_factors=whitened_unwhitened),
     "topk_lowest": dict(topk_restore=topk_lowest),
+    "topk_tol_relative_to_score": dict(topk_restore_tol=topk_tol_relative_to_score),
+    "topk_tol_upper_index": dict(topk_restore_tol=topk_tol_upper_index),
     "pinv_identity_on_null": dict(pinv_sqrt_psd=pinv_identity_on_null),
     "moment_centred": dict(second_moment=moment_centred),
     "moment_unbiased": dict(second_moment=moment_unbiased),
