@@ -319,6 +319,15 @@ int glowq_ner_sums_batch(int32_t n, const void* const* w_devs, const glowq_qweig
 int glowq_restore_topk(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k,
                        double* scores_dev, int32_t* mask_dev, hipStream_t stream);
 
+/* The same choice with the layer-order fallback for a weak signal (key design 4: when the scores
+ * do not separate the units, restore in layer order).  rel_tol in [0, 1]: a unit's distance from
+ * the best score max is counted in steps of rel_tol * max, key = floor((max - score) /
+ * (rel_tol * max)) in fp64; the k units with the smallest keys are restored, equal keys going to
+ * the lower unit index -- so when every score lies within one step of the best, the first k units
+ * are restored.  rel_tol == 0 is glowq_restore_topk.  Asynchronous. */
+int glowq_restore_select(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k, double rel_tol,
+                         double* scores_dev, int32_t* mask_dev, hipStream_t stream);
+
 /* ---------------------------------------------------------------- offline factor solve
  * Input second moment of the calibration activations, the statistic the covariance-aligned fit
  * is built on (GlowQ paper note, key design 2: the usage-weighted risk E||M x||^2 equals

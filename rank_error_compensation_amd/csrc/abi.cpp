@@ -841,15 +841,21 @@ int glowq_ec_score(const double* e_dev, int64_t m, int64_t d, const double* sigm
     return launch_ec(C, sigma_dev, (int)d, s_dev, r, part, out_dev, stream) == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
 }
 
-int glowq_restore_topk(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k,
-                       double* scores_dev, int32_t* mask_dev, hipStream_t stream) {
+int glowq_restore_select(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k, double rel_tol,
+                         double* scores_dev, int32_t* mask_dev, hipStream_t stream) {
     if (!sums_dev || !scores_dev || !mask_dev) return GLOWQ_ERR_INVALID_ARG;
+    if (!(rel_tol >= 0.0 && rel_tol <= 1.0)) return GLOWQ_ERR_INVALID_ARG;  // also rejects NaN
     if (n_units < 1 || n_units > kMaxScoreUnits || n_per_unit < 1 || n_per_unit > 1024 || k < 0 ||
         k > n_units)
         return GLOWQ_ERR_SHAPE;
     if (!aligned(sums_dev, 16) || !aligned(scores_dev, 16) || !aligned(mask_dev, 16)) return GLOWQ_ERR_ALIGN;
-    const hipError_t e = launch_topk(sums_dev, n_units, n_per_unit, k, scores_dev, mask_dev, stream);
+    const hipError_t e = launch_topk(sums_dev, n_units, n_per_unit, k, rel_tol, scores_dev, mask_dev, stream);
     return e == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
+}
+
+int glowq_restore_topk(const double* sums_dev, int32_t n_units, int32_t n_per_unit, int32_t k,
+                       double* scores_dev, int32_t* mask_dev, hipStream_t stream) {
+    return glowq_restore_select(sums_dev, n_units, n_per_unit, k, 0.0, scores_dev, mask_dev, stream);
 }
 
 int glowq_group_forward(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,

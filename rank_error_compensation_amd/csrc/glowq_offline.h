@@ -20,7 +20,7 @@ struct NerBatch {
     double* sums;                       // [n_mod][2]
 };
 hipError_t launch_ner(const NerBatch& a, hipStream_t stream);
-hipError_t launch_topk(const double* sums, int32_t n_units, int32_t n_per, int32_t k, double* scores,
+hipError_t launch_topk(const double* sums, int32_t n_units, int32_t n_per, int32_t k, double rel_tol, double* scores,
                        int32_t* mask, hipStream_t stream);
 // g_ec terms from C = E_cat^T E_cat (lower triangle, d x d): out = (energy, captured, ratio);
 // part holds d doubles

@@ -127,12 +127,17 @@ __global__ __launch_bounds__(256) void ner_finish_kernel(const NerBatch a) {
 struct TopkArgs {
     const double* sums;  // [n_units][n_per][2]
     int32_t n_units, n_per, k;
+    double rel_tol;      // 0: exact ranking; > 0: steps of rel_tol times the best score
     double* scores;      // [n_units]
     int32_t* mask;       // [n_units]
 };
 
+// With rel_tol > 0 a unit's key is floor((max - score) / (rel_tol max)), fp64, and units with equal
+// keys go in layer order (the fallback of key design 4 when the signal is weak: all scores within
+// one step of the best restore the first k units).
 __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs a) {
     __shared__ double sc[kMaxScoreUnits];
+    __shared__ double red[256];
     for (int u = threadIdx.x; u < a.n_units; u += 256) {
         double e2 = 0.0, w2 = 0.0;
         for (int m = 0; m < a.n_per; ++m) {
@@ -144,6 +149,25 @@ __global__ __launch_bounds__(256) void topk_kernel(const TopkArgs a) {
         a.scores[u] = s;
     }
     __syncthreads();
+    if (a.rel_tol > 0.0) {
+        double m = 0.0;
+        for (int u = threadIdx.x; u < a.n_units; u += 256) m = fmax(m, sc[u]);
+        red[threadIdx.x] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double mx = red[0];
+            for (int t = 1; t < 256; ++t) mx = fmax(mx, red[t]);
+            red[0] = mx;
+        }
+        __syncthreads();
+        const double mx = red[0];
+        __syncthreads();
+        if (mx > 0.0) {
+            const double step = a.rel_tol * mx;
+            for (int u = threadIdx.x; u < a.n_units; u += 256) sc[u] = -floor((mx - sc[u]) / step);  // higher is better
+            __syncthreads();
+        }
+    }
     for (int u = threadIdx.x; u < a.n_units; u += 256) {
         const double su = sc[u];
         int rank = 0;
@@ -216,13 +240,14 @@ hipError_t launch_ner(const NerBatch& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const double* sums, int32_t n_units, int32_t n_per, int32_t k, double* scores,
+hipError_t launch_topk(const double* sums, int32_t n_units, int32_t n_per, int32_t k, double rel_tol, double* scores,
                        int32_t* mask, hipStream_t stream) {
     TopkArgs a;
     a.sums = sums;
     a.n_units = n_units;
     a.n_per = n_per;
     a.k = k;
+    a.rel_tol = rel_tol;
     a.scores = scores;
     a.mask = mask;
     hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(256), 0, stream, a);

@@ -88,6 +88,7 @@ EXPORTS = {
     "glowq_ner_sums_batch": (ctypes.c_int, [_i32, ctypes.POINTER(_vp), ctypes.POINTER(QWeightC), _vp, _sz,
                                             _vp, _vp]),
     "glowq_restore_topk": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "glowq_restore_select": (ctypes.c_int, [_vp, _i32, _i32, _i32, ctypes.c_double, _vp, _vp, _vp]),
     "glowq_second_moment_workspace_bytes": (_sz, [_i64, _i64]),
     "glowq_second_moment": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "glowq_solve_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
@@ -220,6 +221,18 @@ def ner_sums_batch(ws_and_qws: Sequence, out: Optional[torch.Tensor] = None,
     check(lib().glowq_ner_sums_batch(len(items), wp, wc, _ptr(workspace), workspace.numel(), _ptr(out),
                                      _stream(stream)), "glowq_ner_sums_batch")
     return out
+
+
+def restore_select(sums: torch.Tensor, k: int, rel_tol: float, stream=None):
+    """glowq_restore_select: (scores fp64 [n_units], mask int32 [n_units]) with the layer-order
+    fallback for scores within rel_tol steps of the best."""
+    sums = sums.contiguous()
+    n_units, n_per = int(sums.shape[0]), int(sums.shape[1])
+    scores = torch.empty(n_units, dtype=torch.float64, device=sums.device)
+    mask = torch.empty(n_units, dtype=torch.int32, device=sums.device)
+    check(lib().glowq_restore_select(_ptr(sums), n_units, n_per, k, float(rel_tol), _ptr(scores), _ptr(mask),
+                                     _stream(stream)), "glowq_restore_select")
+    return scores, mask
 
 
 def restore_topk(sums: torch.Tensor, k: int, stream=None):

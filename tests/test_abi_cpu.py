@@ -160,7 +160,7 @@ def test_other_entry_points_validate():
 
 
 def test_restore_selection_validates():
-    """glowq_ner_sums / glowq_restore_topk reject bad arguments before any HIP call."""
+    """glowq_ner_sums / glowq_restore_topk / glowq_restore_select reject bad arguments before any HIP call."""
     L = g.lib()
     wc = _w()
     assert L.glowq_ner_workspace_bytes(0) == 0
@@ -188,6 +188,10 @@ def test_restore_selection_validates():
     assert L.glowq_restore_topk(FAKE, 4, 1, 5, FAKE, FAKE, None) == g.ERR_SHAPE
     assert L.glowq_restore_topk(FAKE, 4, 1, -1, FAKE, FAKE, None) == g.ERR_SHAPE
     assert L.glowq_restore_topk(FAKE, 4, 1, 2, FAKE, FAKE + 4, None) == g.ERR_ALIGN
+    for bad in (-1e-3, 1.5, float("nan"), float("inf")):
+        assert L.glowq_restore_select(FAKE, 4, 1, 2, bad, FAKE, FAKE, None) == g.ERR_INVALID_ARG
+    assert L.glowq_restore_select(FAKE, 4, 1, 5, 0.01, FAKE, FAKE, None) == g.ERR_SHAPE
+    assert L.glowq_restore_select(None, 4, 1, 2, 0.01, FAKE, FAKE, None) == g.ERR_INVALID_ARG
 
 
 def test_second_moment_validates():

@@ -137,3 +137,30 @@ def test_topk_ties_zero_weight_and_extremes():
     torch.cuda.synchronize()
     assert scores.cpu().tolist() == [2.0 / 8.0, 2.0 / 4.0]
     assert mask.cpu().tolist() == [0, 1]
+
+
+@pytest.mark.parametrize("rel_tol", [0.0, 1e-3, 0.01, 0.2])
+def test_select_with_layer_order_fallback(rel_tol):
+    """glowq_restore_select against oracle.solve.topk_restore_tol on the GPU's own scores (the
+    keys floor((max - s) / (rel_tol max)) are fp64 on both sides, bit-identical): near-equal
+    scores fall back to layer order; separated ones keep the exact ranking."""
+    g = glowq()
+    rng = np.random.default_rng(29)
+    base = [(1.0 + 1e-4 * rng.standard_normal(), 100.0) for _ in range(20)]          # weak signal
+    sep = [(float(v), 1.0) for v in rng.uniform(0.1, 1.0, 12)]                       # strong signal
+    mixed = base[:6] + [(50.0, 100.0), (0.2, 100.0)] + base[6:10]
+    for pairs in (base, sep, mixed):
+        st = torch.tensor(pairs, dtype=torch.float64, device="cuda").reshape(len(pairs), 1, 2)
+        for k in (0, 1, 5, len(pairs) // 2, len(pairs)):
+            scores, mask = g.restore_select(st, k, rel_tol)
+            torch.cuda.synchronize()
+            sg = [float(v) for v in scores.cpu()]
+            assert [bool(v) for v in mask.cpu()] == S.topk_restore_tol(sg, k, rel_tol), (rel_tol, k)
+            if rel_tol == 0.0:
+                _, m0 = g.restore_topk(st, k)
+                assert torch.equal(mask, m0)
+    # weak signal with a tolerance above its spread: the first k layers exactly
+    st = torch.tensor(base, dtype=torch.float64, device="cuda").reshape(len(base), 1, 2)
+    _, mask = g.restore_select(st, 7, 0.01)
+    torch.cuda.synchronize()
+    assert [bool(v) for v in mask.cpu()] == [u < 7 for u in range(len(base))]
