@@ -77,7 +77,56 @@ def dequant(q_packed, s, z, n_out: int, k_in: int) -> np.ndarray:
 
 def dequant_qw(qw) -> np.ndarray:
     """Dequantise a workload QuantWeight-like object (q_packed, s, z, n_out, k_in)."""
+    if getattr(qw, "fmt", "int4") != "int4":
+        return dequant_mx(qw.codes, qw.scales, qw.fmt, qw.n_out, qw.k_in)
     return dequant(qw.q_packed, qw.s, qw.z, qw.n_out, qw.k_in)
+
+
+# --------------------------------------------------------------------------- MX weights
+# GlowQ on microscaling weight formats (GlowQ arXiv page, Table 13: MXFP4 and MXFP6 rows,
+# quantised alone and with the correction).  The formats themselves are those of the OCP
+# Microscaling (MX) Formats specification v1.0: blocks of 32 consecutive elements along a row
+# share one E8M0 scale 2^(S - 127) (S = 255 encodes NaN); an element is a sign bit, ebits
+# exponent bits and mbits mantissa bits with the given bias, no infinities or NaNs; exponent
+# field 0 is subnormal.  The pages do not say which 6-bit element MXFP6 means: both the E2M3
+# and the E3M2 element are covered.
+MX_BLOCK = 32
+MX_ELEM = {"mxfp4": (2, 1, 1), "mxfp6_e2m3": (2, 3, 1), "mxfp6_e3m2": (3, 2, 3)}  # ebits, mbits, bias
+
+
+def mx_element_value(code: int, fmt: str) -> float:
+    """Value of one element code: (-1)^sign 2^(E - bias) (1 + M / 2^mbits) for E > 0,
+    (-1)^sign 2^(1 - bias) (M / 2^mbits) for E = 0."""
+    ebits, mbits, bias = MX_ELEM[fmt]
+    nbits = 1 + ebits + mbits
+    assert 0 <= code < (1 << nbits)
+    sign = -1.0 if (code >> (nbits - 1)) & 1 else 1.0
+    e = (code >> mbits) & ((1 << ebits) - 1)
+    m = code & ((1 << mbits) - 1)
+    if e == 0:
+        mag = math.ldexp(m / (1 << mbits), 1 - bias)
+    else:
+        mag = math.ldexp(1.0 + m / (1 << mbits), e - bias)
+    return sign * mag
+
+
+def e8m0_value(s: int) -> float:
+    """The shared scale of an MX block: 2^(s - 127); s = 255 is NaN."""
+    return math.nan if s == 255 else math.ldexp(1.0, int(s) - 127)
+
+
+def dequant_mx(codes, scales, fmt: str, n_out: int, k_in: int) -> np.ndarray:
+    """W_hat[o, k] = element(codes[o, k]) * 2^(scales[o, k // 32] - 127) in fp64 (exact).
+
+    codes: uint8 [n_out][k_in], one element code per byte in its low bits;
+    scales: uint8 [n_out][k_in / 32], E8M0."""
+    c = _np(codes).astype(np.int64)
+    s = _np(scales).astype(np.int64)
+    assert c.shape == (n_out, k_in) and s.shape == (n_out, k_in // MX_BLOCK), (c.shape, s.shape)
+    ebits, mbits, _ = MX_ELEM[fmt]
+    table = np.array([mx_element_value(v, fmt) for v in range(1 << (1 + ebits + mbits))])
+    scale = np.array([e8m0_value(v) for v in range(256)])
+    return table[c] * scale[s][:, np.arange(k_in) // MX_BLOCK]
 
 
 # --------------------------------------------------------------------------- forward

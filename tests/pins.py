@@ -660,11 +660,87 @@ def check_restore_tol(sol):
     assert sol.topk_restore_tol([0.0] * 6, 3, 0.01) == [True, True, True, False, False, False]
 
 
+# ------------------------------------------------------------------ MX weight formats
+MX_BITS = {"mxfp4": (2, 1), "mxfp6_e2m3": (2, 3), "mxfp6_e3m2": (3, 2)}
+
+
+def _mx_golden():
+    full, props = {}, {}
+    with open(os.path.join(GOLDEN, "mx_elements.txt")) as f:
+        for line in f:
+            tok = line.split()
+            if not tok or tok[0].startswith("#"):
+                continue
+            if tok[0] == "all":
+                full[tok[1]] = [float(v) for v in tok[2:]]
+            elif tok[0] == "props":
+                props[tok[1]] = {kv.split("=")[0]: float(kv.split("=")[1]) for kv in tok[2:]}
+    return full, props
+
+
+def check_mx_elements(ref):
+    """Every element code of the three MX element formats against the specification's printed
+    values (tests/golden/mx_elements.txt): FP4's full table; for the FP6 formats the largest and
+    smallest normal and subnormal magnitudes; magnitudes strictly increase with the code, the
+    sign bit negates (code 100..0 is -0), and the exponent field 0 codes are the subnormals."""
+    full, props = _mx_golden()
+    for fmt, (eb, mb) in MX_BITS.items():
+        n = 1 + eb + mb
+        mags = [ref.mx_element_value(c, fmt) for c in range(1 << (n - 1))]
+        if fmt in full:
+            assert mags == full[fmt], (fmt, mags)
+        assert all(a < b for a, b in zip(mags, mags[1:])), fmt
+        sub = [m for c, m in enumerate(mags) if c >> mb == 0 and c > 0]
+        nor = [m for c, m in enumerate(mags) if c >> mb > 0]
+        pr = props[fmt]
+        assert max(nor) == pr["max_normal"] and min(nor) == pr["min_normal"], fmt
+        assert max(sub) == pr["max_subnormal"] and min(sub) == pr["min_subnormal"], fmt
+        for c in range(1 << (n - 1)):
+            neg = ref.mx_element_value(c | (1 << (n - 1)), fmt)
+            assert neg == -mags[c] and math.copysign(1.0, neg) == -1.0, (fmt, c)
+
+
+def check_mx_scales(ref):
+    """E8M0 scales against torch's float8_e8m0fnu conversion (all 256 bytes; 255 is NaN)."""
+    import torch
+    want = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64)
+    for s in range(256):
+        got = ref.e8m0_value(s)
+        if s == 255:
+            assert math.isnan(got) and math.isnan(float(want[s]))
+        else:
+            assert got == float(want[s]), (s, got, float(want[s]))
+
+
+def check_mx_dequant_hand(ref):
+    """dequant_mx on 3 rows x 96 inputs (three blocks per row, each (row, block) its own
+    scale): element k of row o is the printed FP4 magnitude of its code, negated when the code's
+    sign bit is set, times 2^(S[o][k // 32] - 127)."""
+    full, _ = _mx_golden()
+    table = full["mxfp4"]
+    O, K = 3, 96
+    codes = np.array([[(5 * k + 3 * o) % 16 for k in range(K)] for o in range(O)], dtype=np.uint8)
+    scales = np.array([[127, 130, 119], [126, 140, 104], [127, 127, 128]], dtype=np.uint8)
+    W = ref.dequant_mx(codes, scales, "mxfp4", O, K)
+    assert W.shape == (O, K)
+    for o in range(O):
+        for k in range(K):
+            c = int(codes[o, k])
+            v = table[c & 7] * (-1.0 if c & 8 else 1.0)
+            assert W[o, k] == v * 2.0 ** (int(scales[o, k // 32]) - 127), (o, k)
+    # every format's dequantised codes at scale 2^0 are the element values, in code order
+    for fmt, (eb, mb) in MX_BITS.items():
+        n = 1 << (1 + eb + mb)
+        c = np.array([[v % n for v in range(128)]], dtype=np.uint8)
+        Wf = ref.dequant_mx(c, np.full((1, 4), 127, dtype=np.uint8), fmt, 1, 128)
+        assert [float(v) for v in Wf[0]] == [ref.mx_element_value(v % n, fmt) for v in range(128)], fmt
+
+
 ALL_REF_CHECKS = [check_dequant_exhaustive, check_dequant_golden, check_restore_off,
                   check_associativity_small_int, check_bruteforce, check_row_independence,
                   check_path_mask, check_parity_errors, check_w4a8_quantizer_hand,
                   check_w4a8_quantizer_invariants, check_w4a8_bruteforce, check_w4a8_lossless_and_scale,
-                  check_moe_rows]
+                  check_moe_rows, check_mx_elements, check_mx_scales, check_mx_dequant_hand]
 ALL_SOL_CHECKS = [check_eckart_young, check_isotropic, check_usage_weighted_risk, check_qr_core,
                   check_cholesky_vs_symmetric, check_randomized_svd, check_scores, check_second_moment,
                   check_pinv_lift, check_restore_tol]

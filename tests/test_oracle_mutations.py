@@ -267,6 +267,49 @@ def moe_offsets_shifted(x, row_token, offsets, w_hats, b, a, restore=True, share
     return G.moe_forward(x, row_token, o, w_hats, b, a, restore, share)
 
 
+def _mx_value_with(bias_over=None, implicit_sub=False, swap=False):
+    def f(code, fmt):
+        eb, mb, bias = G.MX_ELEM[fmt]
+        if bias_over is not None:
+            bias = bias_over
+        n = 1 + eb + mb
+        sign = -1.0 if (code >> (n - 1)) & 1 else 1.0
+        if swap:
+            m, e = (code >> eb) & ((1 << mb) - 1), code & ((1 << eb) - 1)
+        else:
+            e, m = (code >> mb) & ((1 << eb) - 1), code & ((1 << mb) - 1)
+        if e == 0 and not implicit_sub:
+            mag = math.ldexp(m / (1 << mb), 1 - bias)
+        else:
+            mag = math.ldexp(1.0 + m / (1 << mb), max(e, 1) - bias)
+        return sign * mag
+    return f
+
+
+def mx_dequant_block_mod(codes, scales, fmt, n_out, k_in):
+    W = G.dequant_mx(codes, scales, fmt, n_out, k_in)
+    s = G._np(scales).astype(np.int64)
+    nb = k_in // 32
+    good = 2.0 ** (s[:, np.arange(k_in) // 32] - 127)
+    bad = 2.0 ** (s[:, np.arange(k_in) % nb] - 127)
+    return W / good * bad
+
+
+def mx_dequant_block16(codes, scales, fmt, n_out, k_in):
+    W = G.dequant_mx(codes, scales, fmt, n_out, k_in)
+    s = G._np(scales).astype(np.int64)
+    idx = np.minimum(np.arange(k_in) // 16, k_in // 32 - 1)
+    return W / 2.0 ** (s[:, np.arange(k_in) // 32] - 127) * 2.0 ** (s[:, idx] - 127)
+
+
+def e8m0_bias128(s):
+    return math.nan if s == 255 else math.ldexp(1.0, int(s) - 128)
+
+
+def e8m0_no_nan(s):
+    return math.ldexp(1.0, int(s) - 127)
+
+
 REF_MUTANTS = {
     "dequant_plus_z": dict(dequant=dequant_plus_z),
     "dequant_group64": dict(dequant=dequant_group64),
@@ -291,6 +334,13 @@ REF_MUTANTS = {
     "moe_next_expert_b": dict(moe_forward=moe_next_expert_b),
     "moe_no_gather": dict(moe_forward=moe_no_gather),
     "moe_offsets_shifted": dict(moe_forward=moe_offsets_shifted),
+    "mx_bias_one_for_all": dict(mx_element_value=_mx_value_with(bias_over=1)),
+    "mx_subnormal_implicit_one": dict(mx_element_value=_mx_value_with(implicit_sub=True)),
+    "mx_fields_swapped": dict(mx_element_value=_mx_value_with(swap=True)),
+    "mx_dequant_block_mod": dict(dequant_mx=mx_dequant_block_mod),
+    "mx_dequant_block16": dict(dequant_mx=mx_dequant_block16),
+    "e8m0_bias128": dict(e8m0_value=e8m0_bias128),
+    "e8m0_no_nan": dict(e8m0_value=e8m0_no_nan),
 }
 
 SOL_MUTANTS = {

@@ -91,3 +91,43 @@ def test_outlier_columns_shared_within_group():
     # the outlier columns carry ~10x larger quantisation scales in every module
     for qw in unit.weights:
         assert qw.s.shape == (16, 2)
+
+
+def test_mx_quantizer_nearest_element_and_ranges():
+    """Microscaling quantisation: every code is the element nearest to w / 2^X (the oracle's
+    element table, brute force), the block exponent puts the block maximum in the element's top
+    binade (inside the exact-fp16 range), codes fit their width, an all-zero block gets the
+    range's low end and zero codes, and err_sq is ||W - dequant||^2."""
+    cols = W.outlier_columns(256, (8,))
+    w = W.make_w(24, 256, (8,), cols)
+    w[3, :32] = 0
+    for fmt, (eb, mb, bias) in W.MX_FORMATS.items():
+        q = W.mx_quantize(w, fmt)
+        lo, hi = W.MX_EXP_RANGE[fmt]
+        n = 1 << (1 + eb + mb)
+        vals = np.array([glowq_ref.mx_element_value(c, fmt) for c in range(n)])
+        codes, X = q.codes.numpy().astype(np.int64), q.scales.numpy().astype(np.int64) - 127
+        assert codes.max() < n and X.min() >= lo and X.max() <= hi
+        assert X[3, 0] == lo and np.all(codes[3, :32] % (n // 2) == 0)
+        wb = w.double().numpy()
+        u = wb / np.ldexp(1.0, X)[:, np.arange(256) // 32]
+        dist = np.abs(vals[None, None, :] - u[:, :, None])
+        assert np.all(np.abs(vals[codes] - u) == dist.min(axis=2))
+        emax = (1 << eb) - 1 - bias
+        amax = np.abs(wb).reshape(24, 8, 32).max(axis=2)
+        nz = amax > 0
+        assert np.all(np.floor(np.log2(amax[nz])) - emax == X[nz])
+        wh = glowq_ref.dequant_mx(q.codes, q.scales, fmt, 24, 256)
+        assert abs(((wb - wh) ** 2).sum() - q.err_sq) <= 1e-12 * q.err_sq
+
+
+def test_mx_quantizer_ties_to_even():
+    """A value halfway between two FP4 elements rounds to the one with the even mantissa
+    (1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2.0, 5.0 -> 4.0) and values past the largest element
+    saturate to 6."""
+    row = torch.zeros(1, 32, dtype=torch.float16)
+    row[0, :6] = torch.tensor([1.25, 1.75, 2.5, 5.0, -5.0, 7.5])
+    q = W.mx_quantize(row, "mxfp4")
+    assert int(q.scales[0, 0]) == 127  # max 7.5 -> floor(log2 7.5) - 2 = 0
+    got = [glowq_ref.mx_element_value(int(c), "mxfp4") for c in q.codes[0, :6]]
+    assert got == [1.0, 2.0, 2.0, 4.0, -4.0, 6.0]

@@ -3,7 +3,8 @@
 This module draws every random input that both the fp64 oracle (``oracle/``) and the
 HIP library consume: activations X with a power-law covariance spectrum, fp16 weights
 with outlier input columns, the round-to-nearest INT4-g128 base quantisation of those
-weights (packed in the library's canonical nibble format), seeded Gaussian low-rank
+weights (packed in the library's canonical nibble format) or their microscaling (MXFP4 /
+MXFP6) quantisation, seeded Gaussian low-rank
 factors rescaled to the size of the quantisation error, and the GlowQ-S restore mask.
 
 It holds none of the correction method's arithmetic: no shared projection, no
@@ -150,6 +151,72 @@ def rtn_quantize(w: torch.Tensor) -> QuantWeight:
                        q_packed=pack_canonical(q8), err_sq=err_sq, w_sq=w_sq)
 
 
+MX_BLOCK = 32
+# element formats (exponent bits, mantissa bits, bias) of the OCP MX v1.0 specification
+MX_FORMATS = {"mxfp4": (2, 1, 1), "mxfp6_e2m3": (2, 3, 1), "mxfp6_e3m2": (3, 2, 3)}
+# block exponents X for which every element times 2^X is an exact fp16 (the device layout's
+# range): the finest element step times 2^X must reach 2^-24, the largest element must stay
+# below 65520
+MX_EXP_RANGE = {"mxfp4": (-23, 13), "mxfp6_e2m3": (-21, 13), "mxfp6_e3m2": (-20, 11)}
+
+
+@dataclass
+class MxWeight:
+    fmt: str
+    codes: torch.Tensor    # uint8 [O][d], one element code per byte (low 4 or 6 bits)
+    scales: torch.Tensor   # uint8 [O][d/32], E8M0 biased block exponents
+    err_sq: float          # ||W - W_hat||_F^2 (fp64)
+    w_sq: float            # ||W||_F^2 (fp64)
+
+    @property
+    def n_out(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def k_in(self) -> int:
+        return int(self.codes.shape[1])
+
+
+def mx_quantize(w: torch.Tensor, fmt: str) -> MxWeight:
+    """Microscaling quantisation of the generated weights (the conversion of the OCP MX v1.0
+    specification): per block of 32 inputs the shared exponent is floor(log2 max|w|) minus the
+    element's largest exponent, kept inside MX_EXP_RANGE (an all-zero block takes the range's
+    low end); each w / 2^X is rounded to the nearest element, ties to the even mantissa,
+    saturating at the largest element."""
+    eb, mb, bias = MX_FORMATS[fmt]
+    lo, hi = MX_EXP_RANGE[fmt]
+    emax = (1 << eb) - 1 - bias
+    emin = 1 - bias
+    top = math.ldexp(2.0 - 2.0 ** -mb, emax)
+    O, d = w.shape
+    assert d % MX_BLOCK == 0
+    wb = w.detach().to("cpu", torch.float64).numpy().reshape(O, d // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(wb).max(axis=2)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - emax, lo)
+    X = np.clip(X, lo, hi)
+    u = np.abs(wb) / np.ldexp(1.0, X.astype(np.int64))[:, :, None]
+    with np.errstate(divide="ignore"):
+        k = np.floor(np.log2(np.where(u > 0, u, 1.0)))
+    k = np.clip(k, emin, emax)  # below the normal range the step is the subnormal one
+    step = np.ldexp(1.0, (k - mb).astype(np.int64))
+    mag = np.minimum(np.rint(u / step) * step, top)
+    # encode: subnormal when below 2^emin, else exponent field and mantissa of the magnitude
+    sub = mag < math.ldexp(1.0, emin)
+    with np.errstate(divide="ignore"):
+        kk = np.floor(np.log2(np.where(sub, 1.0, mag)))
+    e_field = np.where(sub, 0, kk + bias)
+    m_field = np.where(sub, mag / math.ldexp(1.0, emin - mb), (mag / np.ldexp(1.0, kk.astype(np.int64)) - 1.0) * (1 << mb))
+    assert np.all(m_field == np.round(m_field)) and np.all(m_field < (1 << mb))
+    sign = (wb < 0) & (mag > 0)
+    codes = (sign.astype(np.int64) << (eb + mb)) | (e_field.astype(np.int64) << mb) | m_field.astype(np.int64)
+    w_hat = np.where(sign, -mag, mag) * np.ldexp(1.0, X.astype(np.int64))[:, :, None]
+    err_sq = float(((wb - w_hat) ** 2).sum())
+    w_sq = float((wb ** 2).sum())
+    return MxWeight(fmt=fmt, codes=torch.from_numpy(codes.reshape(O, d).astype(np.uint8)),
+                    scales=torch.from_numpy((X + 127).astype(np.uint8)), err_sq=err_sq, w_sq=w_sq)
+
+
 def pack_canonical(q: torch.Tensor) -> torch.Tensor:
     """uint8 [O][d] (0..15) -> int32 [O][d/8]; nibble j (bits 4j..4j+3) of word w holds
     q[o][8w + j] (low nibble first).  The int32 holds the uint32 bit pattern."""
@@ -249,13 +316,14 @@ class Unit:
 
 def make_unit(name: str, kind: str, x: torch.Tensor, n_outs: Sequence[int], r: int,
               keys: Sequence[int], device="cpu", restore: bool = True,
-              layerwise: bool = False, w_override: Optional[List[torch.Tensor]] = None) -> Unit:
+              layerwise: bool = False, w_override: Optional[List[torch.Tensor]] = None,
+              fmt: str = "int4") -> Unit:
     d = x.shape[1]
     cols = outlier_columns(d, keys)  # shared by the modules of one group (an input property)
     weights = []
     for i, O in enumerate(n_outs):
         w = w_override[i] if w_override is not None else make_w(O, d, list(keys) + [i], cols, device)
-        weights.append(rtn_quantize(w))
+        weights.append(rtn_quantize(w) if fmt == "int4" else mx_quantize(w, fmt))
     a, b = gaussian_factors(n_outs, d, r, [q.err_sq for q in weights], keys, device)
     b_lw = None
     if layerwise:
