@@ -214,7 +214,7 @@ def rotating_group(T, copies, g, device):
     import workload as W
     u = W.llama2_qkv_unit(T, device=device)
     base = [g.QWeight.from_workload(q, device=device) for q in u.weights]
-    sets = [base] + [[g.QWeight(w.q.clone(), w.sz.clone(), w.n_out, w.k_in) for w in base]
+    sets = [base] + [[g.QWeight(w.q.clone(), w.sz.clone(), w.n_out, w.k_in, w.fmt) for w in base]
                      for _ in range(copies - 1)]
     a_sets = [u.a] + [[a.clone() for a in u.a] for _ in range(copies - 1)]
     ys = [torch.empty(T, w.n_out, dtype=torch.float16, device=device) for w in base]
@@ -292,7 +292,7 @@ def extra_llama3(g, reps=10, min_bytes=600 << 20):
                 w0 = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
                 wbytes = sum(w.q.numel() * w.q.element_size() + w.sz.numel() * w.sz.element_size() for w in w0)
                 copies = max(1, -(-min_bytes // wbytes)) if T <= 64 else 1
-                sets = [w0] + [[g.QWeight(w.q.clone(), w.sz.clone(), w.n_out, w.k_in) for w in w0]
+                sets = [w0] + [[g.QWeight(w.q.clone(), w.sz.clone(), w.n_out, w.k_in, w.fmt) for w in w0]
                                for _ in range(copies - 1)]
                 ws = g.make_workspace(T, r, 1)
                 ys = [torch.empty(T, w.n_out, dtype=torch.float16, device="cuda") for w in w0]
@@ -417,7 +417,7 @@ def extra_group_vs_layerwise(g):
     copies = 20
     u = W.llama2_qkv_unit(1, device="cuda", layerwise=True)
     base = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
-    sets = [base] + [[g.QWeight(w.q.clone(), w.sz.clone(), w.n_out, w.k_in) for w in base] for _ in range(copies - 1)]
+    sets = [base] + [[g.QWeight(w.q.clone(), w.sz.clone(), w.n_out, w.k_in, w.fmt) for w in base] for _ in range(copies - 1)]
     ws = g.make_workspace(1, u.r, 3)
     ys = [torch.empty(1, w.n_out, dtype=torch.float16, device="cuda") for w in base]
     it = {"a": 0, "b": 0}
@@ -448,7 +448,7 @@ def extra_group_vs_layerwise(g):
         u = units[0]
         w0 = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
         ncp = 40 if T == 64 else 1
-        sets = [w0] + [[g.QWeight(x.q.clone(), x.sz.clone(), x.n_out, x.k_in) for x in w0] for _ in range(ncp - 1)]
+        sets = [w0] + [[g.QWeight(x.q.clone(), x.sz.clone(), x.n_out, x.k_in, x.fmt) for x in w0] for _ in range(ncp - 1)]
         ws = g.make_workspace(T, 64, len(w0))
         ys = [torch.empty(T, q.n_out, dtype=torch.float16, device="cuda") for q in w0]
         it = {"a": 0, "b": 0}

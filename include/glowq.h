@@ -80,11 +80,49 @@ int glowq_version(void);
  * multiple of 16 with zero weights.
  */
 typedef struct glowq_qweight {
-    const void* q;  /* device layout words, glowq_q_bytes(n_out, k_in) bytes           */
-    const void* sz; /* device layout zero/scale pairs, glowq_sz_bytes(n_out, k_in) bytes */
+    const void* q;  /* device layout words, glowq_q_bytes(n_out, k_in) bytes
+                       (MX formats: glowq_mx_q_bytes(format, n_out, k_in))               */
+    const void* sz; /* device layout zero/scale pairs (MX: block scales),
+                       glowq_sz_bytes(n_out, k_in) bytes for every format                */
     int64_t n_out;  /* output rows O_i >= 1                                            */
     int64_t k_in;   /* input columns d, a positive multiple of 128                      */
+    int32_t format; /* GLOWQ_FMT_*; 0 (a zero-initialised struct) is INT4-g128          */
+    int32_t reserved; /* must be 0                                                     */
 } glowq_qweight;
+
+/* ---------------------------------------------------------------- MX weight formats
+ * Microscaling weights, the MXFP4 / MXFP6 datatypes GlowQ is applied on (GlowQ arXiv page,
+ * Table 13).  Encodings of the OCP Microscaling (MX) v1.0 specification: blocks of 32
+ * consecutive inputs of a row share one E8M0 scale 2^(S - 127); an element is sign,
+ * exponent and mantissa bits (FP4 E2M1, FP6 E2M3, FP6 E3M2; exponent field 0 subnormal).
+ * The pages do not say which FP6 element they use; both are accepted.
+ *   codes  : uint8 [n_out][k_in], one element code per byte in its low 4 (FP4) or 6 bits;
+ *   scales : uint8 [n_out][k_in / 32], E8M0 biased exponents S.
+ * The forward kernels dequantise to fp16 in registers (the gfx950 scaled conversion
+ * instructions), which is exact when every element times 2^(S - 127) is an fp16 value:
+ * S - 127 in [-23, 13] (MXFP4), [-21, 13] (E2M3), [-20, 11] (E3M2).  glowq_repack_mx rejects
+ * other scales (including the NaN scale 255) with GLOWQ_ERR_RANGE.  Every forward entry
+ * point accepts these formats except glowq_group_forward_w4a8 and glowq_moe_forward (INT4
+ * only: GLOWQ_ERR_UNSUPPORTED); all modules of one call share one format.  glowq_ner_sums
+ * takes INT4 weights only.
+ */
+#define GLOWQ_FMT_INT4_G128 0
+#define GLOWQ_FMT_MXFP4 1
+#define GLOWQ_FMT_MXFP6_E2M3 2
+#define GLOWQ_FMT_MXFP6_E3M2 3
+
+/* Bytes of the device-layout codes of one MX module (0 if the shape or format is invalid):
+ * 1024 (MXFP4) or 1536 (MXFP6) bytes per 16 rows x 128 inputs; the scales take
+ * glowq_sz_bytes(n_out, k_in) (64 bytes per 16 rows x 128 inputs). */
+size_t glowq_mx_q_bytes(int32_t format, int64_t n_out, int64_t k_in);
+
+/* Convert one MX module from codes_dev / scales_dev (the layout above) into the device layout
+ * (q_dev: glowq_mx_q_bytes, sz_dev: glowq_sz_bytes).  flag_dev is a caller-provided device
+ * int32 that reports a code wider than the element or a scale outside the exact range.  An
+ * offline load step: it SYNCHRONISES `stream` and returns GLOWQ_ERR_RANGE on such data (the
+ * layout is written regardless).  Shape rules: n_out >= 1, k_in % 128 == 0. */
+int glowq_repack_mx(int32_t format, const void* codes_dev, const void* scales_dev, int64_t n_out,
+                    int64_t k_in, void* q_dev, void* sz_dev, int32_t* flag_dev, hipStream_t stream);
 
 /* Bytes of the device-layout buffers of one module (0 if the shape is invalid). */
 size_t glowq_q_bytes(int64_t n_out, int64_t k_in);
@@ -102,8 +140,9 @@ int glowq_repack(const void* q_canon_dev, const void* scales_dev, const void* ze
 
 /* Export the dequantised weight (q - z) * s of one module to out_dev [n_out][k_in] as fp32
  * (exact: the product of a 5-bit integer difference and an fp16 scale fits in 24 bits) or
- * fp16 (the exact value rounded once to nearest-even).  It runs the same in-register
- * dequantisation routine as the forward kernels.  Asynchronous on `stream`. */
+ * fp16 (the exact value rounded once to nearest-even).  MX modules export
+ * element * 2^(S - 127), exact in both.  It runs the same in-register dequantisation
+ * routines as the forward kernels.  Asynchronous on `stream`. */
 int glowq_dequant(const glowq_qweight* w, void* out_dev, int32_t out_dtype, hipStream_t stream);
 
 /* ---------------------------------------------------------------- forward

@@ -80,6 +80,9 @@ int validate(const Call& c, void* workspace, size_t ws_bytes) {
     for (int i = 0; i < c.m; ++i) {
         const glowq_qweight& w = c.w[i];
         if (w.q == nullptr || w.sz == nullptr) return GLOWQ_ERR_INVALID_ARG;
+        if (w.format < GLOWQ_FMT_INT4_G128 || w.format > GLOWQ_FMT_MXFP6_E3M2 || w.reserved != 0)
+            return GLOWQ_ERR_INVALID_ARG;
+        if (w.format != c.w[0].format) return GLOWQ_ERR_UNSUPPORTED;  // one format per call
         if (c.T > 0 && c.y[i] == nullptr) return GLOWQ_ERR_INVALID_ARG;
         if (w.n_out < 1 || w.k_in != c.d) return GLOWQ_ERR_SHAPE;
         if (w.n_out > kMaxRows) return GLOWQ_ERR_UNSUPPORTED;
@@ -89,7 +92,7 @@ int validate(const Call& c, void* workspace, size_t ws_bytes) {
     // every launch has at most (16-token tiles) x (16-row tiles) work tiles
     if (ceil_div(c.T, 16) * tiles16 > kMaxTiles) return GLOWQ_ERR_UNSUPPORTED;
     if (c.x != nullptr && !aligned(c.x, 16)) return GLOWQ_ERR_ALIGN;
-    if (c.w4a8 && c.d > kW4a8MaxD) return GLOWQ_ERR_UNSUPPORTED;
+    if (c.w4a8 && (c.d > kW4a8MaxD || c.w[0].format != GLOWQ_FMT_INT4_G128)) return GLOWQ_ERR_UNSUPPORTED;
     if (c.correct) {
         if (c.a == nullptr || c.b == nullptr) return GLOWQ_ERR_INVALID_ARG;
         for (int i = 0; i < c.m; ++i)
@@ -134,7 +137,9 @@ int64_t prefill_tiles(const Call& c, int tt, int rr) {
 // tiles, 46 us on average with 4 wave groups vs 70 us with one.)
 void choose_prefill_shape(const Call& c, int& tt, int& rr, int& ks) {
     if (prefill_tiles(c, 8, 4) >= kWideMinTiles) {
-        tt = 8, rr = 4, ks = 1;
+        // MXFP6 takes the wide tile with 64 tokens (the kernel's registers)
+        tt = c.w[0].format == GLOWQ_FMT_MXFP6_E2M3 || c.w[0].format == GLOWQ_FMT_MXFP6_E3M2 ? 4 : 8;
+        rr = 4, ks = 1;
         return;
     }
     tt = 4, rr = 2;
@@ -187,7 +192,7 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
     if (prefill) choose_prefill_shape(c, tt, rr, ks);
     // 17 .. 64 tokens on the small prefill tiles: the projection is formed inside the launch by
     // producer workgroups and handed over as tagged pairs (one launch instead of three)
-    const bool fuse = c.correct && prefill && c.T <= kDecodeMaxT && !(tt == 8 && rr == 4);
+    const bool fuse = c.correct && prefill && c.T <= kDecodeMaxT && rr != 4;  // rr == 4: the wide tile
     if (fuse && tt == 4 && rr == 2 && ks == 4) ks = 2;  // the fused 64 x 128 tile: two wave groups
     void* R = nullptr;
     if (c.correct) {
@@ -205,6 +210,7 @@ int run(const Call& c, void* workspace, hipStream_t stream) {
     f.T = (int32_t)c.T;
     f.d = (int32_t)c.d;
     f.G = (int32_t)(c.d / kGroup);
+    f.fmt = c.w[0].format;
     f.r = c.correct ? c.r : 0;
     f.r_pad = c.correct ? rp : 0;
     f.n_mod = c.m;
@@ -384,7 +390,7 @@ const char* glowq_status_string(int status) {
     }
 }
 
-int glowq_version(void) { return 200; }
+int glowq_version(void) { return 300; }
 
 int glowq_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (workspace == nullptr) return GLOWQ_ERR_INVALID_ARG;
@@ -524,6 +530,34 @@ size_t glowq_sz_bytes(int64_t n_out, int64_t k_in) {
     return (size_t)ceil_div(n_out, 16) * (size_t)(k_in / kGroup) * 64u;
 }
 
+size_t glowq_mx_q_bytes(int32_t format, int64_t n_out, int64_t k_in) {
+    if (format != GLOWQ_FMT_MXFP4 && format != GLOWQ_FMT_MXFP6_E2M3 && format != GLOWQ_FMT_MXFP6_E3M2) return 0;
+    const size_t q4 = glowq_q_bytes(n_out, k_in);
+    return format == GLOWQ_FMT_MXFP4 ? q4 : q4 / 2u * 3u;
+}
+
+int glowq_repack_mx(int32_t format, const void* codes_dev, const void* scales_dev, int64_t n_out, int64_t k_in,
+                    void* q_dev, void* sz_dev, int32_t* flag_dev, hipStream_t stream) {
+    if (format != GLOWQ_FMT_MXFP4 && format != GLOWQ_FMT_MXFP6_E2M3 && format != GLOWQ_FMT_MXFP6_E3M2)
+        return GLOWQ_ERR_INVALID_ARG;
+    if (!codes_dev || !scales_dev || !q_dev || !sz_dev || !flag_dev) return GLOWQ_ERR_INVALID_ARG;
+    if (n_out < 1 || k_in < kGroup || k_in % kGroup != 0) return GLOWQ_ERR_SHAPE;
+    if (n_out > kMaxRows || k_in > kMaxD) return GLOWQ_ERR_UNSUPPORTED;
+    if (!aligned(codes_dev, 16) || !aligned(scales_dev, 4) || !aligned(q_dev, 16) || !aligned(sz_dev, 16) ||
+        !aligned(flag_dev, 4))
+        return GLOWQ_ERR_ALIGN;
+    if (launch_flag_clear(flag_dev, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    if (launch_repack_mx(format, static_cast<const uint8_t*>(codes_dev), static_cast<const uint8_t*>(scales_dev),
+                         n_out, k_in, static_cast<uint8_t*>(q_dev), static_cast<uint8_t*>(sz_dev), flag_dev,
+                         stream) != hipSuccess)
+        return GLOWQ_ERR_HIP;
+    int32_t flag = 0;
+    if (hipMemcpyAsync(&flag, flag_dev, sizeof(flag), hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return GLOWQ_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return GLOWQ_ERR_HIP;
+    return flag ? GLOWQ_ERR_RANGE : GLOWQ_OK;
+}
+
 size_t glowq_w4a8_workspace_bytes(int64_t T, int64_t d, int32_t r) {
     if (T <= 0 || d < kGroup || d % kGroup != 0 || d > kW4a8MaxD || r < 0 || r > GLOWQ_MAX_RANK) return 0;
     size_t n = round256((size_t)T * d) + round256((size_t)T * (d / kGroup) * 4u) + round256((size_t)T * 4u);
@@ -573,10 +607,12 @@ int glowq_repack(const void* q_canon_dev, const void* scales_dev, const void* ze
 int glowq_dequant(const glowq_qweight* w, void* out_dev, int32_t out_dtype, hipStream_t stream) {
     if (!w || !out_dev || !w->q || !w->sz) return GLOWQ_ERR_INVALID_ARG;
     if (out_dtype != GLOWQ_DTYPE_F32 && out_dtype != GLOWQ_DTYPE_F16) return GLOWQ_ERR_INVALID_ARG;
+    if (w->format < GLOWQ_FMT_INT4_G128 || w->format > GLOWQ_FMT_MXFP6_E3M2 || w->reserved != 0)
+        return GLOWQ_ERR_INVALID_ARG;
     if (w->n_out < 1 || w->k_in < kGroup || w->k_in % kGroup != 0) return GLOWQ_ERR_SHAPE;
     if (w->n_out > kMaxRows || w->k_in > kMaxD) return GLOWQ_ERR_UNSUPPORTED;
     if (!aligned(w->q, 16) || !aligned(w->sz, 16) || !aligned(out_dev, 16)) return GLOWQ_ERR_ALIGN;
-    const hipError_t e = launch_dequant(static_cast<const uint8_t*>(w->q), static_cast<const uint8_t*>(w->sz),
+    const hipError_t e = launch_dequant(w->format, static_cast<const uint8_t*>(w->q), static_cast<const uint8_t*>(w->sz),
                                         w->n_out, w->k_in, out_dev, out_dtype == GLOWQ_DTYPE_F32 ? 0 : 1,
                                         stream);
     return e == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
@@ -594,6 +630,7 @@ int glowq_ner_sums_batch(int32_t n, const void* const* w_devs, const glowq_qweig
     for (int32_t i = 0; i < n; ++i) {
         const glowq_qweight& w = wqs[i];
         if (!w_devs[i] || !w.q || !w.sz) return GLOWQ_ERR_INVALID_ARG;
+        if (w.format != GLOWQ_FMT_INT4_G128) return GLOWQ_ERR_UNSUPPORTED;  // INT4 weights only
         if (w.n_out < 1 || w.k_in < kGroup || w.k_in % kGroup != 0) return GLOWQ_ERR_SHAPE;
         if (w.n_out > kMaxRows || w.k_in > kMaxD) return GLOWQ_ERR_UNSUPPORTED;
         if (!aligned(w_devs[i], 16) || !aligned(w.q, 16) || !aligned(w.sz, 16)) return GLOWQ_ERR_ALIGN;

@@ -136,9 +136,11 @@ __device__ void produce(const ForwardArgs& a, int p) {
 // does not wait for the weights; lanes of padding tokens read an all-zero LDS row, so the B operand
 // needs no masking.  XC == 0: each group's B operand is loaded from global memory together with
 // the group's weights.
-template <int NTT, int XC, int KW, int RT>
+template <int F, int NTT, int XC, int KW, int RT>
 __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0 && KW == 4) ? (RT == 2 ? 3 : 4) : 1))) void decode_kernel(const ForwardArgs args) {
     constexpr bool XLDS = XC > 0;
+    constexpr bool MX = Fmt<F>::mx, SIX = Fmt<F>::six;
+    constexpr int QB = Fmt<F>::qblock;
     constexpr int NTH = 64 * KW;
     constexpr int U = NTT == 1 ? 4 / RT : 1;  // ring of groups per wave
     static_assert(U >= 1, "ring");
@@ -169,10 +171,12 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
 #pragma unroll
     for (int rr = 0; rr < RT; ++rr) {
         const int rt = min(rt0 + rr, M.n_tiles16 - 1);  // a tile past the module end rereads the last
-        qbase[rr] = M.q + (size_t)rt * 1024 + lane * 16;
+        qbase[rr] = M.q + (size_t)rt * QB + lane * 16;
         szbase[rr] = M.sz + (size_t)rt * 64;
     }
-    const size_t qstride = (size_t)M.n_tiles16 * 1024, szstride = (size_t)M.n_tiles16 * 64;  // per group
+    const size_t qstride = (size_t)M.n_tiles16 * QB, szstride = (size_t)M.n_tiles16 * 64;  // per group
+    // MXFP6: the second plane of a lane's codes (8 bytes at 1024 + 8 lane of the block)
+    const int q6ofs = 1024 + 8 * lane - 16 * lane;
     const int kofs = 8 * (lane >> 4);
     const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     const NibConsts nc = nib_consts();
@@ -217,8 +221,9 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
     }
 
     u4 qv[U][RT];
-    uint32_t zso[U][RT];
-    u4 zs4[U][RT];
+    u2 qv6[SIX ? U : 1][RT];
+    uint32_t zso[U][RT];  // INT4: the row's (z, s) pair; MX: the row's four block scales
+    u4 zs4[MX ? 1 : U][RT];
     h8 bx[XLDS ? 1 : U][NTT][4];
     auto issue = [&](int u, int i) {
         const int g = min(g0 + wave + KW * i, g1 - 1);  // always a valid group of this workgroup
@@ -234,8 +239,12 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
 #pragma unroll
         for (int rr = 0; rr < RT; ++rr) {
             qv[u][rr] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(qbase[rr] + (size_t)g * qstride));
+            if constexpr (SIX)
+                qv6[SIX ? u : 0][rr] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u2*>(qbase[rr] + (size_t)g * qstride + q6ofs));
             zso[u][rr] = *reinterpret_cast<const uint32_t*>(szbase[rr] + (size_t)g * szstride + (lane & 15) * 4);
-            zs4[u][rr] = *reinterpret_cast<const u4*>(szbase[rr] + (size_t)g * szstride + (lane >> 4) * 16);
+            if constexpr (!MX)
+                zs4[MX ? 0 : u][rr] = *reinterpret_cast<const u4*>(szbase[rr] + (size_t)g * szstride + (lane >> 4) * 16);
         }
     };
 
@@ -258,6 +267,30 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
             __builtin_amdgcn_sched_barrier(0);
         }
         h8 aop[RT][4];
+        if constexpr (MX) {
+            // MX: the operands carry their block scales (exact fp16), so the matrix cores
+            // accumulate straight into the running sums
+#pragma unroll
+            for (int rr = 0; rr < RT; ++rr) {
+                if constexpr (SIX) {
+                    const h32 e = mx6_h32<F>(qv[u][rr], qv6[SIX ? u : 0][rr]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) aop[rr][j] = mx6_slice(e, j, mx_scale(zso[u][rr], j));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) aop[rr][j] = mx4_h8(qv[u][rr][j], mx_scale(zso[u][rr], j));
+                }
+            }
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const h8 b = XLDS ? bl[XLDS ? tt : 0][j] : bx[XLDS ? 0 : u][tt][j];
+#pragma unroll
+                    for (int rr = 0; rr < RT; ++rr) acc[rr][tt] = mfma16(aop[rr][j], b, acc[rr][tt]);
+                }
+            return;
+        }
 #pragma unroll
         for (int rr = 0; rr < RT; ++rr) {
             h2 c1024, c64;
@@ -279,7 +312,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
 #pragma unroll
             for (int rr = 0; rr < RT; ++rr)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) acc[rr][tt][k] += (float)as_h2(zs4[u][rr][k])[1] * part[rr][k];
+                for (int k = 0; k < 4; ++k) acc[rr][tt][k] += (float)as_h2(zs4[MX ? 0 : u][rr][k])[1] * part[rr][k];
         }
     };
 
@@ -436,7 +469,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const ForwardArgs a)
     y[(size_t)t * n_out + (row - row_begin)] = (_Float16)v;
 }
 
-template <int KW, int RT>
+template <int F, int KW, int RT>
 static hipError_t launch_decode_kw(const ForwardArgs& a, hipStream_t stream) {
     constexpr int NTH = 64 * KW;
     const int ntt = (int)ceil_div(a.T, 16);
@@ -451,51 +484,62 @@ static hipError_t launch_decode_kw(const ForwardArgs& a, hipStream_t stream) {
     if constexpr (RT != kNarrowRt) if (xlds) {
         const int chunks = (int)ceil_div((int64_t)xbytes / 16, NTH);
         if (chunks <= 2)
-            hipLaunchKernelGGL((decode_kernel<1, 2, KW, RT>), grid, block, shmem, stream, b);
+            hipLaunchKernelGGL((decode_kernel<F, 1, 2, KW, RT>), grid, block, shmem, stream, b);
         else if (chunks <= 4)
-            hipLaunchKernelGGL((decode_kernel<1, 4, KW, RT>), grid, block, shmem, stream, b);
+            hipLaunchKernelGGL((decode_kernel<F, 1, 4, KW, RT>), grid, block, shmem, stream, b);
         else if (chunks <= 8)
-            hipLaunchKernelGGL((decode_kernel<1, 8, KW, RT>), grid, block, shmem, stream, b);
+            hipLaunchKernelGGL((decode_kernel<F, 1, 8, KW, RT>), grid, block, shmem, stream, b);
         else
-            hipLaunchKernelGGL((decode_kernel<1, (int)(kDecodeXLdsMax / 16 / NTH), KW, RT>), grid, block, shmem,
+            hipLaunchKernelGGL((decode_kernel<F, 1, (int)(kDecodeXLdsMax / 16 / NTH), KW, RT>), grid, block, shmem,
                                stream, b);
         return hipGetLastError();
     }
     if constexpr (RT == kNarrowRt) {  // K-split narrow calls: 17 .. 64 tokens
         switch (ntt) {
-            case 2: hipLaunchKernelGGL((decode_kernel<2, 0, KW, RT>), grid, block, shmem, stream, b); break;
-            case 3: hipLaunchKernelGGL((decode_kernel<3, 0, KW, RT>), grid, block, shmem, stream, b); break;
-            case 4: hipLaunchKernelGGL((decode_kernel<4, 0, KW, RT>), grid, block, shmem, stream, b); break;
+            case 2: hipLaunchKernelGGL((decode_kernel<F, 2, 0, KW, RT>), grid, block, shmem, stream, b); break;
+            case 3: hipLaunchKernelGGL((decode_kernel<F, 3, 0, KW, RT>), grid, block, shmem, stream, b); break;
+            case 4: hipLaunchKernelGGL((decode_kernel<F, 4, 0, KW, RT>), grid, block, shmem, stream, b); break;
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
     }
     if (RT != 1) {  // two row tiles share each activation operand read from L2 (one token tile)
         if (ntt != 1) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((decode_kernel<1, 0, KW, RT>), grid, block, shmem, stream, b);
+        hipLaunchKernelGGL((decode_kernel<F, 1, 0, KW, RT>), grid, block, shmem, stream, b);
         return hipGetLastError();
     }
     switch (ntt) {
-        case 1: hipLaunchKernelGGL((decode_kernel<1, 0, KW, 1>), grid, block, shmem, stream, b); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<2, 0, KW, 1>), grid, block, shmem, stream, b); break;
-        case 3: hipLaunchKernelGGL((decode_kernel<3, 0, KW, 1>), grid, block, shmem, stream, b); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<4, 0, KW, 1>), grid, block, shmem, stream, b); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<F, 1, 0, KW, 1>), grid, block, shmem, stream, b); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<F, 2, 0, KW, 1>), grid, block, shmem, stream, b); break;
+        case 3: hipLaunchKernelGGL((decode_kernel<F, 3, 0, KW, 1>), grid, block, shmem, stream, b); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<F, 4, 0, KW, 1>), grid, block, shmem, stream, b); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream) {
+template <int F>
+static hipError_t launch_decode_fmt(const ForwardArgs& a, hipStream_t stream) {
     if (a.dec_ks > 1) {  // narrow call with a K split: 4 waves, kNarrowRt row tiles, then the sums
         if (a.dec_kw != 4 || a.dec_rt != kNarrowRt) return hipErrorInvalidValue;
-        hipError_t e = launch_decode_kw<4, kNarrowRt>(a, stream);
+        hipError_t e = launch_decode_kw<F, 4, kNarrowRt>(a, stream);
         if (e != hipSuccess) return e;
         const size_t n = (size_t)a.T * a.rows_total;
         hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)ceil_div((int64_t)n, 256)), dim3(256), 0, stream, a);
         return hipGetLastError();
     }
-    if (a.dec_kw == 8) return launch_decode_kw<8, 1>(a, stream);
-    return a.dec_rt == 2 ? launch_decode_kw<4, 2>(a, stream) : launch_decode_kw<4, 1>(a, stream);
+    if (a.dec_kw == 8) return launch_decode_kw<F, 8, 1>(a, stream);
+    return a.dec_rt == 2 ? launch_decode_kw<F, 4, 2>(a, stream) : launch_decode_kw<F, 4, 1>(a, stream);
+}
+
+hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream) {
+    switch (a.fmt) {
+        case kFmtInt4: return launch_decode_fmt<kFmtInt4>(a, stream);
+        case kFmtMxfp4: return launch_decode_fmt<kFmtMxfp4>(a, stream);
+        case kFmtMxfp6E2M3: return launch_decode_fmt<kFmtMxfp6E2M3>(a, stream);
+        case kFmtMxfp6E3M2: return launch_decode_fmt<kFmtMxfp6E3M2>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace glowq

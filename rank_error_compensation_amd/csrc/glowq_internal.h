@@ -141,6 +141,74 @@ __device__ __forceinline__ void zero_consts(uint32_t zs, h2& zc1024, h2& zc64) {
     zc64 = h2{b, b};
 }
 
+// --------------------------------------------------------------------- MX weight formats
+// Device layout of an MX module (elements of the OCP Microscaling v1.0 formats, one E8M0 scale per
+// 32 inputs of a row), in the INT4 geometry:
+//   q  : G x NT blocks of Fmt<F>::qblock bytes, block (rt, g) at (g NT + rt) qblock.  Lane l owns
+//        the 32 codes of row 16 rt + l % 16 for the inputs k = 128 g + 32 j + 8 (l / 16) + e
+//        (slice j = 0..3, e = 0..7; code n = 8 j + e), i.e. the matrix-core operand order above.
+//        MXFP4: the 16 bytes at 16 l, code n in bits 4n..4n+3 (the scaled fp4 conversion turns
+//        byte b of a word into the fp16 pair (2b, 2b + 1), low nibble first).  MXFP6: 24 bytes in
+//        two naturally aligned planes, 16 at 16 l and 8 at 1024 + 8 l, code n in bits 6n..6n+5 of
+//        their 192-bit concatenation (the order of the 32-value fp6 conversion).
+//   sz : 64-byte blocks as for INT4; row i's word at 4 i holds in byte j the E8M0 scale S of the
+//        inputs 128 g + 32 j .. + 31.  Rows >= n_out have codes 0 and scale bytes 127.
+// The repack admits only scales for which every element times 2^(S - 127) is an fp16 value, so
+// the dequantised operands are exact.
+enum : int { kFmtInt4 = 0, kFmtMxfp4 = 1, kFmtMxfp6E2M3 = 2, kFmtMxfp6E3M2 = 3 };
+template <int F>
+struct Fmt {
+    static constexpr bool mx = F != kFmtInt4;
+    static constexpr bool six = F == kFmtMxfp6E2M3 || F == kFmtMxfp6E3M2;
+    static constexpr int qblock = six ? 1536 : 1024;
+};
+typedef _Float16 h32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u6 __attribute__((ext_vector_type(6)));
+
+// The fp32 power of two 2^(S - 127) of scale byte j of a row's scale word (S in 1..254).
+__device__ __forceinline__ float mx_scale(uint32_t sw, int j) {
+    return __builtin_bit_cast(float, ((sw >> (8 * j)) & 0xFFu) << 23);
+}
+
+// Eight FP4 codes (one word, code e in bits 4e..4e+3) -> fp16 element * scale.
+__device__ __forceinline__ h8 mx4_h8(uint32_t w, float s) {
+    const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 0);
+    const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 1);
+    const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 2);
+    const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 3);
+    return h8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// A lane's 32 FP6 codes -> their fp16 element values (unscaled, exact).
+template <int F>
+__device__ __forceinline__ h32 mx6_h32(u4 lo, u2 hi) {
+    const u6 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1]};
+    if constexpr (F == kFmtMxfp6E3M2)
+        return __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(w, 1.0f);
+    else
+        return __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(w, 1.0f);
+}
+
+// The same conversion, never merged with an identical one: kernels that hold many row tiles take
+// one slice per conversion instead of keeping all 32 values live across their slice loop (the
+// empty asm makes the input a fresh value; it emits no instruction).
+template <int F>
+__device__ __forceinline__ h32 mx6_h32_fresh(u4 lo, u2 hi) {
+    uint32_t w0 = lo[0];
+    asm volatile("" : "+v"(w0));
+    return mx6_h32<F>(u4{w0, lo[1], lo[2], lo[3]}, hi);
+}
+
+// Slice j (codes 8 j .. 8 j + 7) of a lane's FP6 values times the block's scale, in fp16 (the
+// product is exact in the admitted scale range).
+__device__ __forceinline__ h8 mx6_slice(const h32& v, int j, float s) {
+    const _Float16 sh = (_Float16)s;
+    const h8 s8 = {sh, sh, sh, sh, sh, sh, sh, sh};
+    const h8 e = {v[8 * j], v[8 * j + 1], v[8 * j + 2], v[8 * j + 3],
+                  v[8 * j + 4], v[8 * j + 5], v[8 * j + 6], v[8 * j + 7]};
+    return e * s8;
+}
+
 __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -165,6 +233,7 @@ struct ModuleArgs {
 struct ForwardArgs {
     const _Float16* x;   // [T][d]
     int32_t T, d, G;     // G = d / 128
+    int32_t fmt;         // weight format of every module (kFmt*)
     int32_t r;           // rank (0 = no correction)
     int32_t r_pad;       // r rounded up to 32 (prefill R row stride)
     int32_t n_mod;
@@ -248,8 +317,10 @@ hipError_t launch_repack(const uint32_t* qc, const _Float16* s, const _Float16* 
                          hipStream_t stream);
 hipError_t launch_flag_clear(int32_t* flag, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
-hipError_t launch_dequant(const uint8_t* q, const uint8_t* sz, int64_t n_out, int64_t k_in, void* out,
+hipError_t launch_dequant(int fmt, const uint8_t* q, const uint8_t* sz, int64_t n_out, int64_t k_in, void* out,
                           int dtype, hipStream_t stream);
+hipError_t launch_repack_mx(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t n_out, int64_t k_in,
+                            uint8_t* q_dev, uint8_t* sz_dev, int32_t* flag, hipStream_t stream);
 hipError_t launch_proj_prefill(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);

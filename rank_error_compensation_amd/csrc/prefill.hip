@@ -112,8 +112,10 @@ __device__ void produce_tile(const ForwardArgs& a, int p) {
 // FUSE (17 .. 64 tokens, correcting calls): the first n_prod workgroups are producers of the
 // projection (produce_tile) and the tiles read R as tagged pairs at their correction step, so the
 // whole call is one launch.
-template <int TT, int RR, int KS, bool FUSE>
+template <int F, int TT, int RR, int KS, bool FUSE>
 __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(const ForwardArgs args) {
+    constexpr bool MX = Fmt<F>::mx, SIX = Fmt<F>::six;
+    constexpr int QB = Fmt<F>::qblock;
     constexpr int BM = 16 * TT;
     constexpr int LS = 136;              // LDS row stride in halves (128 + 8 padding)
     constexpr int NCH = BM * 16 / 256;   // 16-byte X chunks per thread per group
@@ -139,7 +141,8 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
     const NibConsts nc = nib_consts();
     const int kofs = 8 * (lane >> 4);
     const int rt0 = nb * 4 * RR + wave * RR;
-    const size_t qstride = (size_t)M.n_tiles16 * 1024, szstride = (size_t)M.n_tiles16 * 64;  // per group
+    const size_t qstride = (size_t)M.n_tiles16 * QB, szstride = (size_t)M.n_tiles16 * 64;  // per group
+    const int q6ofs = 1024 + 8 * lane - 16 * lane;  // MXFP6: second plane of the lane's codes
 
     const uint8_t* qp[RR];
     const uint8_t* zp[RR];
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
     for (int rr = 0; rr < RR; ++rr) {
         const int rt = rt0 + rr;
         w_ok[rr] = rt < M.n_tiles16;
-        qp[rr] = M.q + (size_t)(w_ok[rr] ? rt : 0) * 1024 + lane * 16;
+        qp[rr] = M.q + (size_t)(w_ok[rr] ? rt : 0) * QB + lane * 16;
         zp[rr] = M.sz + (size_t)(w_ok[rr] ? rt : 0) * 64 + (lane & 15) * 4;
     }
     const _Float16* xsrc[NCH];
@@ -170,14 +173,18 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
     const int n_it = (G + KS - 1) / KS;
     u4 st[NCH];
     u4 qv[RR];
-    uint32_t zs[RR];
+    u2 q6[SIX ? RR : 1];
+    uint32_t zs[RR];  // INT4: (z, s) of the row; MX: the row's four block scales
     const bool act0 = kg < G;
+    const u2 zero2 = {0u, 0u};
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
         st[c] = (act0 && x_ok[c]) ? *reinterpret_cast<const u4*>(xsrc[c] + (size_t)kg * kGroup) : zero4;
 #pragma unroll
     for (int rr = 0; rr < RR; ++rr) {
         qv[rr] = (act0 && w_ok[rr]) ? *reinterpret_cast<const u4*>(qp[rr] + (size_t)kg * qstride) : zero4;
+        if constexpr (SIX)
+            q6[SIX ? rr : 0] = (act0 && w_ok[rr]) ? *reinterpret_cast<const u2*>(qp[rr] + (size_t)kg * qstride + q6ofs) : zero2;
         zs[rr] = (act0 && w_ok[rr]) ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)kg * szstride) : 0u;
     }
 #pragma unroll
@@ -197,6 +204,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
         const int buf = it & 1;
         const bool act = g < G, more = g + KS < G;
         u4 qn[RR];
+        u2 q6n[SIX ? RR : 1];
         uint32_t zn[RR];
         if (more) {
 #pragma unroll
@@ -205,10 +213,43 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr) {
                 qn[rr] = w_ok[rr] ? *reinterpret_cast<const u4*>(qp[rr] + (size_t)(g + KS) * qstride) : zero4;
+                if constexpr (SIX)
+                    q6n[SIX ? rr : 0] =
+                        w_ok[rr] ? *reinterpret_cast<const u2*>(qp[rr] + (size_t)(g + KS) * qstride + q6ofs) : zero2;
                 zn[rr] = w_ok[rr] ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)(g + KS) * szstride) : 0u;
             }
         }
-        if (act) {
+        if (act && MX) {
+            // MX operands carry their block scales (exact fp16)
+            const _Float16* xb = &xs[kg][buf][(lane & 15) * LS + kofs];
+            // MXFP6: one 32-value conversion per row tile, or per (row tile, slice) when the
+            // 1024-thread tile of two row tiles could not hold both conversions' values
+            constexpr bool kFresh = RR * KS >= 8;
+            h32 e6[SIX && !kFresh ? RR : 1];
+            if constexpr (SIX && !kFresh) {
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) e6[rr] = mx6_h32<F>(qv[rr], q6[rr]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h8 a[RR];
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) {
+                    if constexpr (SIX && kFresh)
+                        a[rr] = mx6_slice(mx6_h32_fresh<F>(qv[rr], q6[rr]), j, mx_scale(zs[rr], j));
+                    else if constexpr (SIX)
+                        a[rr] = mx6_slice(e6[rr], j, mx_scale(zs[rr], j));
+                    else
+                        a[rr] = mx4_h8(qv[rr][j], mx_scale(zs[rr], j));
+                }
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt) {
+                    const h8 b = *reinterpret_cast<const h8*>(xb + tt * 16 * LS + 32 * j);
+#pragma unroll
+                    for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = mfma16(a[rr], b, acc[tt][rr]);
+                }
+            }
+        } else if (act) {
             h2 c1024[RR], c64[RR];
             h8 s8[RR];
 #pragma unroll
@@ -237,6 +278,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr) {
                 qv[rr] = qn[rr];
+                if constexpr (SIX) q6[SIX ? rr : 0] = q6n[SIX ? rr : 0];
                 zs[rr] = zn[rr];
             }
         }
@@ -334,9 +376,9 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
     if (FUSE && threadIdx.x == 0) finish(args, arrived_lds, tag_lds - 1u);
 }
 
-// Wide tile for large grids: BM = 128 tokens x BN = 256 rows, wave w owning 4 row tiles of 16
-// rows and all 8 token tiles, so every activation operand read from LDS feeds 4 matrix-core
-// steps and every dequantised weight operand 8.  The activation tile of a 128-input group is
+// Wide tile for large grids: BM = 128 tokens (64 for MXFP6) x BN = 256 rows, wave w owning 4 row
+// tiles of 16 rows and all TT token tiles, so every activation operand read from LDS feeds 4
+// matrix-core steps and every dequantised weight operand TT.  The activation tile of a 128-input group is
 // copied HBM/L2 -> LDS by the load unit itself (16-byte global_load_lds, no registers), whole
 // 256-byte rows per four lanes; in LDS row r keeps its 16-byte chunk c at position c ^ (r % 16),
 // so that the operand reads (16 rows, one chunk each) hit 16 different bank groups.  Two LDS
@@ -347,9 +389,13 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
 // tile; neither is stored.
 typedef __attribute__((address_space(3))) void lds_void;
 
+template <int F, int TT>
 __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs args) {
-    constexpr int TT = 8, RR = 4, BM = 128;
+    constexpr int RR = 4, BM = 16 * TT;
+    constexpr bool MX = Fmt<F>::mx, SIX = Fmt<F>::six;
+    constexpr int QB = Fmt<F>::qblock;
     extern __shared__ __attribute__((aligned(16))) u4 xw[];  // [2][TT * 4][64]
+    static_assert(TT == 8 || TT == 4, "128 or 64 tokens per tile");
 
     int mb, nbl;
     if ((args.m_tiles & 7) == 0) {
@@ -380,29 +426,32 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
     uint32_t rtc[RR];
 #pragma unroll
     for (int rr = 0; rr < RR; ++rr) rtc[rr] = (uint32_t)min(rt0 + rr, NT - 1);
-    const uint32_t qlane = lane * 16, zlane = (lane & 15) * 4;
+    const uint32_t qlane = lane * 16, zlane = (lane & 15) * 4, q6lane = 1024 + 8 * lane;
     auto qaddr = [&](int g, int rr) {
-        return reinterpret_cast<const u4*>(M.q + ((size_t)g * NT + rtc[rr]) * 1024 + qlane);
+        return reinterpret_cast<const u4*>(M.q + ((size_t)g * NT + rtc[rr]) * QB + qlane);
+    };
+    auto q6addr = [&](int g, int rr) {  // MXFP6: second plane of the lane's codes
+        return reinterpret_cast<const u2*>(M.q + ((size_t)g * NT + rtc[rr]) * QB + q6lane);
     };
     auto zaddr = [&](int g, int rr) {
         return reinterpret_cast<const uint32_t*>(M.sz + ((size_t)g * NT + rtc[rr]) * 64 + zlane);
     };
-    // activation copy: instruction i of wave w fills tile rows 32 w + 4 i .. + 3 (256 bytes each,
-    // whole cache lines); lane l lands at LDS slot 16 l, i.e. row 32 w + 4 i + l / 16, 16-byte
+    // activation copy: instruction i of wave w fills tile rows 4 TT w + 4 i .. + 3 (256 bytes each,
+    // whole cache lines); lane l lands at LDS slot 16 l, i.e. row 4 TT w + 4 i + l / 16, 16-byte
     // position l % 16, which holds input chunk (l % 16) ^ (row % 16) of that row (XOR swizzle)
-    uint32_t xoff[8];
+    uint32_t xoff[TT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 32 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < TT; ++i) {
+        const int row = 4 * TT * wave + 4 * i + (lane >> 4);
         const int t = min(m0 + row, T - 1);
         xoff[i] = (uint32_t)(t * d + 8 * ((lane & 15) ^ (row & 15))) * 2u;
     }
     const char* xbase = reinterpret_cast<const char*>(args.x);
     auto copy_x = [&](int g, int buf) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < TT; ++i)
             __builtin_amdgcn_global_load_lds((const void*)(xbase + (size_t)g * kGroup * 2 + xoff[i]),
-                                             (lds_void*)(xw + ((size_t)buf * BM + 32 * wave + 4 * i) * 16), 16, 0, 0);
+                                             (lds_void*)(xw + ((size_t)buf * BM + 4 * TT * wave + 4 * i) * 16), 16, 0, 0);
     };
     // operand read of slice j: lane l takes row 16 tt + l % 16, chunk 4 j + l / 16, swizzled
     uint32_t bofs[4];
@@ -410,11 +459,13 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
     for (int j = 0; j < 4; ++j) bofs[j] = (uint32_t)((lane & 15) * 16 + ((4 * j + (lane >> 4)) ^ (lane & 15)));
 
     u4 qv[RR];
-    uint32_t zs[RR];
+    u2 q6[SIX ? RR : 1];
+    uint32_t zs[RR];  // INT4: (z, s) of the row; MX: the row's four block scales
     copy_x(0, 0);
 #pragma unroll
     for (int rr = 0; rr < RR; ++rr) {
         qv[rr] = *qaddr(0, rr);
+        if constexpr (SIX) q6[SIX ? rr : 0] = *q6addr(0, rr);
         zs[rr] = *zaddr(0, rr);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -430,23 +481,36 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
         const int buf = g & 1;
         const bool more = g + 1 < G;
         u4 qn[RR];
+        u2 q6n[SIX ? RR : 1];
         uint32_t zn[RR];
         if (more) {
             copy_x(g + 1, buf ^ 1);
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr) {
                 qn[rr] = *qaddr(g + 1, rr);
+                if constexpr (SIX) q6n[SIX ? rr : 0] = *q6addr(g + 1, rr);
                 zn[rr] = *zaddr(g + 1, rr);
             }
         }
         h2 c1024[RR], c64[RR];
         h8 s8[RR];
+        if constexpr (!MX) {
 #pragma unroll
-        for (int rr = 0; rr < RR; ++rr) {
-            zero_consts(zs[rr], c1024[rr], c64[rr]);
-            const _Float16 s = as_h2(zs[rr])[1];
-            s8[rr] = h8{s, s, s, s, s, s, s, s};
+            for (int rr = 0; rr < RR; ++rr) {
+                zero_consts(zs[rr], c1024[rr], c64[rr]);
+                const _Float16 s = as_h2(zs[rr])[1];
+                s8[rr] = h8{s, s, s, s, s, s, s, s};
+            }
         }
+        // operand j of row tile rr: INT4 (q - z) s; MX element times its block scale (exact)
+        auto unpack = [&](int j, int rr) -> h8 {
+            if constexpr (SIX)  // one conversion per slice: 4 row tiles x 32 values would not fit
+                return mx6_slice(mx6_h32_fresh<F>(qv[rr], q6[SIX ? rr : 0]), j, mx_scale(zs[rr], j));
+            else if constexpr (MX)
+                return mx4_h8(qv[rr][j], mx_scale(zs[rr], j));
+            else
+                return nib8_minus_z(qv[rr][j], c1024[rr], c64[rr], nc) * s8[rr];
+        };
         const u4* xb = xw + (size_t)buf * BM * 16;
         {
             // 32 steps (slice j, token tile tt): the activation operand of step st is read two
@@ -459,14 +523,15 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
             bq[1] = bread(1);
             h8 aj[4][RR];
 #pragma unroll
-            for (int rr = 0; rr < RR; ++rr) aj[0][rr] = nib8_minus_z(qv[rr][0], c1024[rr], c64[rr], nc) * s8[rr];
+            for (int rr = 0; rr < RR; ++rr) aj[0][rr] = unpack(0, rr);
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
                 const int j = st / TT, tt = st % TT;
                 if (st + 2 < NS) bq[(st + 2) % 3] = bread(st + 2);
-                if (j < 3 && (tt & 1) == 0) {
-                    const int rr = tt >> 1;
-                    aj[j + 1][rr] = nib8_minus_z(qv[rr][j + 1], c1024[rr], c64[rr], nc) * s8[rr];
+                constexpr int kEvery = TT / RR;  // steps per row tile's unpacking (2, or 1 at 64 tokens)
+                if (j < 3 && tt % kEvery == 0) {
+                    const int rr = tt / kEvery;
+                    aj[j + 1][rr] = unpack(j + 1, rr);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -479,6 +544,7 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr) {
                 qv[rr] = qn[rr];
+                if constexpr (SIX) q6[SIX ? rr : 0] = q6n[SIX ? rr : 0];
                 zs[rr] = zn[rr];
             }
         }
@@ -532,15 +598,15 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
     }
 }
 
-template <bool FUSE>
+template <int F, bool FUSE>
 static hipError_t launch_prefill_small(const ForwardArgs& a, hipStream_t stream) {
     const dim3 grid(a.n_tiles + (FUSE ? a.n_prod : 0));
     if (a.tile_rr == 1) {  // small grids: 64 or 32 tokens x 64 rows, 4 wave groups
         if (a.tile_ks != 4 || (a.tile_tt != 4 && a.tile_tt != 2)) return hipErrorInvalidValue;
         if (a.tile_tt == 4)
-            hipLaunchKernelGGL((prefill_kernel<4, 1, 4, FUSE>), grid, dim3(1024), 0, stream, a);
+            hipLaunchKernelGGL((prefill_kernel<F, 4, 1, 4, FUSE>), grid, dim3(1024), 0, stream, a);
         else
-            hipLaunchKernelGGL((prefill_kernel<2, 1, 4, FUSE>), grid, dim3(1024), 0, stream, a);
+            hipLaunchKernelGGL((prefill_kernel<F, 2, 1, 4, FUSE>), grid, dim3(1024), 0, stream, a);
         return hipGetLastError();
     }
     if (a.tile_tt != 4 || a.tile_rr != 2) return hipErrorInvalidValue;
@@ -548,24 +614,38 @@ static hipError_t launch_prefill_small(const ForwardArgs& a, hipStream_t stream)
         // the fused form of this tile would need more than the 128 registers of a 1024-thread
         // workgroup; the launcher gives fused calls two wave groups instead
         if constexpr (FUSE) return hipErrorInvalidValue;
-        else hipLaunchKernelGGL((prefill_kernel<4, 2, 4, FUSE>), grid, dim3(1024), 0, stream, a);
+        else hipLaunchKernelGGL((prefill_kernel<F, 4, 2, 4, FUSE>), grid, dim3(1024), 0, stream, a);
     }
     else if (a.tile_ks == 2)
-        hipLaunchKernelGGL((prefill_kernel<4, 2, 2, FUSE>), grid, dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((prefill_kernel<F, 4, 2, 2, FUSE>), grid, dim3(512), 0, stream, a);
     else if (a.tile_ks == 1)
-        hipLaunchKernelGGL((prefill_kernel<4, 2, 1, FUSE>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((prefill_kernel<F, 4, 2, 1, FUSE>), grid, dim3(256), 0, stream, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
-    if (a.tile_tt == 8 && a.tile_rr == 4) {
-        if (a.n_prod > 0) return hipErrorInvalidValue;  // the wide tile takes R from a projection launch
-        hipLaunchKernelGGL(prefill_wide_kernel, dim3(a.n_tiles), dim3(256), 2 * 8 * 4 * 64 * sizeof(u4), stream, a);
+template <int F>
+static hipError_t launch_prefill_fmt(const ForwardArgs& a, hipStream_t stream) {
+    if (a.tile_rr == 4) {
+        // the wide tile takes R from a projection launch; MXFP6 runs it with 64 tokens (its 32-value
+        // conversions would not fit beside 128 tokens' sums)
+        if (a.n_prod > 0 || a.tile_tt != (Fmt<F>::six ? 4 : 8)) return hipErrorInvalidValue;
+        constexpr int TT = Fmt<F>::six ? 4 : 8;
+        hipLaunchKernelGGL((prefill_wide_kernel<F, TT>), dim3(a.n_tiles), dim3(256), 2 * TT * 4 * 64 * sizeof(u4), stream, a);
         return hipGetLastError();
     }
-    return a.n_prod > 0 ? launch_prefill_small<true>(a, stream) : launch_prefill_small<false>(a, stream);
+    return a.n_prod > 0 ? launch_prefill_small<F, true>(a, stream) : launch_prefill_small<F, false>(a, stream);
+}
+
+hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
+    switch (a.fmt) {
+        case kFmtInt4: return launch_prefill_fmt<kFmtInt4>(a, stream);
+        case kFmtMxfp4: return launch_prefill_fmt<kFmtMxfp4>(a, stream);
+        case kFmtMxfp6E2M3: return launch_prefill_fmt<kFmtMxfp6E2M3>(a, stream);
+        case kFmtMxfp6E3M2: return launch_prefill_fmt<kFmtMxfp6E3M2>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace glowq

@@ -28,6 +28,11 @@ ERR_HANDOFF = -8
 ERR_ROUTING = -9
 MOE_SHARE_EXPERT = 0
 MOE_SHARE_ALL = 1
+FMT_INT4_G128 = 0
+FMT_MXFP4 = 1
+FMT_MXFP6_E2M3 = 2
+FMT_MXFP6_E3M2 = 3
+FORMATS = {"int4": FMT_INT4_G128, "mxfp4": FMT_MXFP4, "mxfp6_e2m3": FMT_MXFP6_E2M3, "mxfp6_e3m2": FMT_MXFP6_E3M2}
 
 DTYPE_F32 = 0
 DTYPE_F16 = 1
@@ -42,7 +47,7 @@ _sz = ctypes.c_size_t
 
 
 class QWeightC(ctypes.Structure):
-    _fields_ = [("q", _vp), ("sz", _vp), ("n_out", _i64), ("k_in", _i64)]
+    _fields_ = [("q", _vp), ("sz", _vp), ("n_out", _i64), ("k_in", _i64), ("format", _i32), ("reserved", _i32)]
 
 
 class MoeModuleC(ctypes.Structure):
@@ -61,6 +66,8 @@ EXPORTS = {
     "glowq_q_bytes": (_sz, [_i64, _i64]),
     "glowq_sz_bytes": (_sz, [_i64, _i64]),
     "glowq_repack": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "glowq_mx_q_bytes": (_sz, [_i32, _i64, _i64]),
+    "glowq_repack_mx": (ctypes.c_int, [_i32, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "glowq_dequant": (ctypes.c_int, [ctypes.POINTER(QWeightC), _vp, _i32, _vp]),
     "glowq_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "glowq_workspace_init": (ctypes.c_int, [_vp, _sz, _vp]),
@@ -141,14 +148,35 @@ def _stream(stream=None):
 # --------------------------------------------------------------------------- weights
 @dataclass
 class QWeight:
-    """One INT4-g128 module in the library's device layout."""
-    q: torch.Tensor     # uint8, glowq_q_bytes
+    """One module (INT4-g128 or MX) in the library's device layout."""
+    q: torch.Tensor     # uint8, glowq_q_bytes (MX: glowq_mx_q_bytes)
     sz: torch.Tensor    # uint8, glowq_sz_bytes
     n_out: int
     k_in: int
+    fmt: int = FMT_INT4_G128
 
     def c(self) -> QWeightC:
-        return QWeightC(self.q.data_ptr(), self.sz.data_ptr(), self.n_out, self.k_in)
+        return QWeightC(self.q.data_ptr(), self.sz.data_ptr(), self.n_out, self.k_in, self.fmt, 0)
+
+    @staticmethod
+    def from_mx(fmt, codes: torch.Tensor, scales: torch.Tensor, device=None, stream=None) -> "QWeight":
+        """Repack MX codes (uint8 [n_out][k_in], one code per byte) and E8M0 scales (uint8
+        [n_out][k_in/32]) into the device layout (glowq_repack_mx; synchronises the stream)."""
+        device = device or torch.device("cuda")
+        f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+        n_out, k_in = codes.shape
+        c = codes.to(device=device, dtype=torch.uint8).contiguous()
+        s = scales.to(device=device, dtype=torch.uint8).contiguous()
+        L = lib()
+        qb, zb = L.glowq_mx_q_bytes(f, n_out, k_in), L.glowq_sz_bytes(n_out, k_in)
+        if qb == 0 or zb == 0:
+            raise GlowQError(ERR_SHAPE, "glowq_mx_q_bytes")
+        q_dev = torch.empty(qb, dtype=torch.uint8, device=device)
+        sz_dev = torch.empty(zb, dtype=torch.uint8, device=device)
+        flag = torch.empty(1, dtype=torch.int32, device=device)
+        check(L.glowq_repack_mx(f, _ptr(c), _ptr(s), n_out, k_in, _ptr(q_dev), _ptr(sz_dev), _ptr(flag),
+                                _stream(stream)), "glowq_repack_mx")
+        return QWeight(q_dev, sz_dev, int(n_out), int(k_in), f)
 
     @staticmethod
     def from_canonical(q_packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
@@ -174,6 +202,8 @@ class QWeight:
 
     @staticmethod
     def from_workload(qw, device=None, stream=None) -> "QWeight":
+        if getattr(qw, "fmt", "int4") != "int4":
+            return QWeight.from_mx(qw.fmt, qw.codes, qw.scales, device, stream)
         return QWeight.from_canonical(qw.q_packed, qw.s, qw.z, device, stream)
 
 

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
 
 def test_status_strings_and_version():
     L = g.lib()
-    assert L.glowq_version() == 200
+    assert L.glowq_version() == 300
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert L.glowq_status_string(code).startswith(b"GLOWQ_")
     assert L.glowq_status_string(12345) == b"GLOWQ_ERR_UNKNOWN"
@@ -63,8 +63,8 @@ def test_buffer_sizes():
 FAKE = 0x10000  # 64 KiB-aligned fake device address: never dereferenced, validation fails first
 
 
-def _w(n_out=32, k_in=256, q=FAKE, sz=FAKE):
-    return g.QWeightC(q, sz, n_out, k_in)
+def _w(n_out=32, k_in=256, q=FAKE, sz=FAKE, fmt=0, reserved=0):
+    return g.QWeightC(q, sz, n_out, k_in, fmt, reserved)
 
 
 def call_group(x=FAKE, T=4, d=256, m=1, w=None, b=FAKE, a=None, r=8, restore=1, ws=FAKE,
@@ -317,3 +317,45 @@ def test_moe_validation_rejects_before_any_hip_call():
     assert L.glowq_moe_workspace_bytes(16, 8, 16, 0) == 8192 + 16 * 32 * 2 + 0 * 256 + (256 - 16 * 32 * 2 % 256) % 256
     assert L.glowq_moe_workspace_bytes(16, 8, 0, 0) == 8192
     assert L.glowq_moe_workspace_bytes(16, 8, 16, 3) == 0
+
+
+def test_mx_sizes_and_repack_validation():
+    """MX device-layout sizes (1024 / 1536 bytes per 16 rows x 128 inputs, scales in the INT4
+    geometry) and glowq_repack_mx's checks before any HIP call."""
+    L = g.lib()
+    assert L.glowq_mx_q_bytes(g.FMT_MXFP4, 32, 256) == L.glowq_q_bytes(32, 256) == 2 * 2 * 1024
+    assert L.glowq_mx_q_bytes(g.FMT_MXFP6_E2M3, 17, 384) == 2 * 3 * 1536
+    assert L.glowq_mx_q_bytes(g.FMT_MXFP6_E3M2, 16, 128) == 1536
+    assert L.glowq_mx_q_bytes(g.FMT_INT4_G128, 16, 128) == 0 and L.glowq_mx_q_bytes(7, 16, 128) == 0
+    assert L.glowq_mx_q_bytes(g.FMT_MXFP4, 16, 100) == 0 and L.glowq_mx_q_bytes(g.FMT_MXFP4, 0, 128) == 0
+    R = L.glowq_repack_mx
+    assert R(g.FMT_INT4_G128, FAKE, FAKE, 16, 128, FAKE, FAKE, FAKE, None) == g.ERR_INVALID_ARG
+    assert R(4, FAKE, FAKE, 16, 128, FAKE, FAKE, FAKE, None) == g.ERR_INVALID_ARG
+    assert R(g.FMT_MXFP4, None, FAKE, 16, 128, FAKE, FAKE, FAKE, None) == g.ERR_INVALID_ARG
+    assert R(g.FMT_MXFP4, FAKE, FAKE, 16, 128, FAKE, FAKE, None, None) == g.ERR_INVALID_ARG
+    assert R(g.FMT_MXFP4, FAKE, FAKE, 16, 96, FAKE, FAKE, FAKE, None) == g.ERR_SHAPE
+    assert R(g.FMT_MXFP4, FAKE, FAKE, 0, 128, FAKE, FAKE, FAKE, None) == g.ERR_SHAPE
+    assert R(g.FMT_MXFP6_E2M3, FAKE + 8, FAKE, 16, 128, FAKE, FAKE, FAKE, None) == g.ERR_ALIGN
+    assert R(g.FMT_MXFP6_E2M3, FAKE, FAKE + 2, 16, 128, FAKE, FAKE, FAKE, None) == g.ERR_ALIGN
+    assert R(g.FMT_MXFP6_E3M2, FAKE, FAKE, 16, 128, FAKE + 4, FAKE, FAKE, None) == g.ERR_ALIGN
+
+
+def test_forward_format_validation():
+    """Forward calls: an unknown format or a nonzero reserved word is INVALID_ARG, modules of
+    different formats in one call UNSUPPORTED; W4A8 takes INT4 only; the dequant export and the
+    restore scores validate the format too."""
+    L = g.lib()
+    assert call_group(w=[_w(fmt=4)]) == g.ERR_INVALID_ARG
+    assert call_group(w=[_w(fmt=-1)]) == g.ERR_INVALID_ARG
+    assert call_group(w=[_w(fmt=1, reserved=3)]) == g.ERR_INVALID_ARG
+    mixed = (g.QWeightC * 2)(_w(fmt=1), _w(fmt=2))
+    ys = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    as_ = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    assert L.glowq_group_forward(FAKE, 4, 256, 2, mixed, FAKE, as_, 8, 1, FAKE, 1 << 20, ys, None) == g.ERR_UNSUPPORTED
+    w8 = (g.QWeightC * 1)(_w(fmt=g.FMT_MXFP4))
+    a1 = (ctypes.c_void_p * 1)(FAKE)
+    y1 = (ctypes.c_void_p * 1)(FAKE)
+    assert L.glowq_group_forward_w4a8(FAKE, 4, 256, 1, w8, FAKE, a1, 8, 1, FAKE, 1 << 24, y1, None) == g.ERR_UNSUPPORTED
+    assert L.glowq_dequant(ctypes.byref(_w(fmt=9)), FAKE, 0, None) == g.ERR_INVALID_ARG
+    need = L.glowq_ner_workspace_bytes(32)
+    assert L.glowq_ner_sums(FAKE, ctypes.byref(_w(fmt=g.FMT_MXFP4)), FAKE, need, FAKE, None) == g.ERR_UNSUPPORTED
