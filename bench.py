@@ -515,6 +515,76 @@ def extra_w4a8(g, reps=20):
     return out
 
 
+def mx_weight_bytes(fmt, n_outs, d):
+    """Bytes of the quantised weights: INT4 codes + (z, s) pairs per 128 inputs, or MX codes
+    (4 or 6 bits) + one scale byte per 32 inputs."""
+    so = sum(n_outs)
+    bits = {"int4": 4, "mxfp4": 4, "mxfp6_e2m3": 6, "mxfp6_e3m2": 6}[fmt]
+    scale = so * (d // 128) * 4 if fmt == "int4" else so * (d // 32)
+    return so * d * bits // 8 + scale
+
+
+def extra_mx(g, reps=20, copies=20):
+    """Microscaling weights (arXiv page, Table 13 datatypes) beside INT4-g128 on the same units:
+    LLaMA-2-7B QKV decode at T = 1 (20 rotating weight copies, HBM-bound: algorithmic bytes with
+    the format's own weight bytes) and gate/up prefill at T = 2048 (matrix-core bound)."""
+    import torch
+    import workload as W
+    stream = torch.cuda.current_stream()
+    out = {}
+    for fmt in ("int4", "mxfp4", "mxfp6_e2m3"):
+        res = {}
+        u = W.llama2_qkv_unit(1, device="cuda", fmt=fmt)
+        base = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
+        sets = [base] + [[g.QWeight(w.q.clone(), w.sz.clone(), w.n_out, w.k_in, w.fmt) for w in base]
+                         for _ in range(copies - 1)]
+        ws = g.make_workspace(1, u.r)
+        ys = [torch.empty(1, w.n_out, dtype=torch.float16, device="cuda") for w in base]
+        for i in range(copies):
+            g.group_forward(u.x, sets[i], u.b, u.a, u.r, True, workspace=ws, y=ys)
+        torch.cuda.synchronize()
+        evs = []
+        for k in range(reps * copies):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.group_forward(u.x, sets[k % copies], u.b, u.a, u.r, True, workspace=ws, y=ys)
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        t = statistics.median([e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs])
+        nb = unit_bytes(1, 4096, u.n_outs, u.r, True) - mx_weight_bytes("int4", u.n_outs, 4096) + \
+            mx_weight_bytes(fmt, u.n_outs, 4096)
+        res["qkv_T1"] = {"us_median": round(t * 1e6, 3), "alg_bytes": nb, "TB_per_s": round(nb / t / 1e12, 4),
+                         "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4)}
+        del sets, base, ws, ys, u
+        u = W.llama2_gateup_unit(2048, device="cuda", fmt=fmt)
+        w = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
+        ws = g.make_workspace(2048, u.r, 1)
+        ys = [torch.empty(2048, q.n_out, dtype=torch.float16, device="cuda") for q in w]
+        fn = graphed(lambda: g.group_forward(u.x, w, u.b, u.a, u.r, True, workspace=ws, y=ys)).replay
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        t = statistics.median(ts)
+        fl = unit_flops(2048, 4096, u.n_outs, u.r, True)
+        res["gateup_T2048"] = {"us_median": round(t * 1e6, 2), "TFLOP_per_s": round(fl / t / 1e12, 1),
+                               "frac_mfma_f16_peak": round(fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+        out[fmt] = res
+        del w, ws, ys, u
+        torch.cuda.empty_cache()
+    out["workload"] = ("llama2-7b QKV T=1 (rotating copies) and gate/up T=2048, r=64, per weight format; "
+                       "MX = OCP microscaling, 32-input blocks, E8M0 scales")
+    return out
+
+
 def extra_moe(g, reps=10):
     """Qwen1.5-MoE-A2.7B MLP: 60 experts, gate/up group 2048 -> 2 x 1408 and down 1408 -> 2048 per
     expert, top-4 routing, r = 64, one launch for all experts (plus the projection when
@@ -951,6 +1021,8 @@ def main():
         log(f"[bench] W4A8: {extra['w4a8']}")
         extra["moe_qwen15"] = extra_moe(g)
         log(f"[bench] MoE: {extra['moe_qwen15']}")
+        extra["mx_formats"] = extra_mx(g)
+        log(f"[bench] MX formats: {extra['mx_formats']}")
         extra["restore_selection_32L"] = extra_restore_selection(g)
         e = extra["restore_selection_32L"]
         e["frac_hbm_measured_peak"] = round(e["GB_per_s"] / peaks["hbm_read_GB_per_s"], 4)

@@ -503,9 +503,15 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
             }
         }
         // operand j of row tile rr: INT4 (q - z) s; MX element times its block scale (exact)
+        // MXFP6 (64-token tile): each row tile's 32 values converted once per group
+        h32 e6[SIX ? RR : 1];
+        if constexpr (SIX) {
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) e6[rr] = mx6_h32<F>(qv[rr], q6[rr]);
+        }
         auto unpack = [&](int j, int rr) -> h8 {
-            if constexpr (SIX)  // one conversion per slice: 4 row tiles x 32 values would not fit
-                return mx6_slice(mx6_h32_fresh<F>(qv[rr], q6[SIX ? rr : 0]), j, mx_scale(zs[rr], j));
+            if constexpr (SIX)
+                return mx6_slice(e6[SIX ? rr : 0], j, mx_scale(zs[rr], j));
             else if constexpr (MX)
                 return mx4_h8(qv[rr][j], mx_scale(zs[rr], j));
             else

@@ -182,7 +182,8 @@ def mx_quantize(w: torch.Tensor, fmt: str) -> MxWeight:
     specification): per block of 32 inputs the shared exponent is floor(log2 max|w|) minus the
     element's largest exponent, kept inside MX_EXP_RANGE (an all-zero block takes the range's
     low end); each w / 2^X is rounded to the nearest element, ties to the even mantissa,
-    saturating at the largest element."""
+    saturating at the largest element.  Runs in fp64 on w's device; codes and scales are
+    returned on the CPU."""
     eb, mb, bias = MX_FORMATS[fmt]
     lo, hi = MX_EXP_RANGE[fmt]
     emax = (1 << eb) - 1 - bias
@@ -190,31 +191,28 @@ def mx_quantize(w: torch.Tensor, fmt: str) -> MxWeight:
     top = math.ldexp(2.0 - 2.0 ** -mb, emax)
     O, d = w.shape
     assert d % MX_BLOCK == 0
-    wb = w.detach().to("cpu", torch.float64).numpy().reshape(O, d // MX_BLOCK, MX_BLOCK)
-    amax = np.abs(wb).max(axis=2)
-    with np.errstate(divide="ignore"):
-        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - emax, lo)
-    X = np.clip(X, lo, hi)
-    u = np.abs(wb) / np.ldexp(1.0, X.astype(np.int64))[:, :, None]
-    with np.errstate(divide="ignore"):
-        k = np.floor(np.log2(np.where(u > 0, u, 1.0)))
-    k = np.clip(k, emin, emax)  # below the normal range the step is the subnormal one
-    step = np.ldexp(1.0, (k - mb).astype(np.int64))
-    mag = np.minimum(np.rint(u / step) * step, top)
+    wb = w.detach().to(torch.float64).reshape(O, d // MX_BLOCK, MX_BLOCK)
+    two = torch.tensor(2.0, dtype=torch.float64, device=wb.device)
+    amax = wb.abs().amax(dim=2)
+    X = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, 1.0))) - emax,
+                    torch.full_like(amax, float(lo))).clamp(lo, hi)
+    u = wb.abs() / torch.pow(two, X).unsqueeze(2)
+    k = torch.floor(torch.log2(torch.where(u > 0, u, 1.0))).clamp(emin, emax)  # subnormal step below
+    step = torch.pow(two, k - mb)
+    mag = torch.minimum(torch.round(u / step) * step, torch.tensor(top, dtype=torch.float64, device=wb.device))
     # encode: subnormal when below 2^emin, else exponent field and mantissa of the magnitude
     sub = mag < math.ldexp(1.0, emin)
-    with np.errstate(divide="ignore"):
-        kk = np.floor(np.log2(np.where(sub, 1.0, mag)))
-    e_field = np.where(sub, 0, kk + bias)
-    m_field = np.where(sub, mag / math.ldexp(1.0, emin - mb), (mag / np.ldexp(1.0, kk.astype(np.int64)) - 1.0) * (1 << mb))
-    assert np.all(m_field == np.round(m_field)) and np.all(m_field < (1 << mb))
+    kk = torch.floor(torch.log2(torch.where(sub, 1.0, mag)))
+    e_field = torch.where(sub, torch.zeros_like(kk), kk + bias)
+    m_field = torch.where(sub, mag / math.ldexp(1.0, emin - mb), (mag / torch.pow(two, kk) - 1.0) * (1 << mb))
+    assert bool(torch.all(m_field == torch.round(m_field))) and bool(torch.all(m_field < (1 << mb)))
     sign = (wb < 0) & (mag > 0)
-    codes = (sign.astype(np.int64) << (eb + mb)) | (e_field.astype(np.int64) << mb) | m_field.astype(np.int64)
-    w_hat = np.where(sign, -mag, mag) * np.ldexp(1.0, X.astype(np.int64))[:, :, None]
+    codes = (sign.to(torch.int64) << (eb + mb)) | (e_field.to(torch.int64) << mb) | m_field.to(torch.int64)
+    w_hat = torch.where(sign, -mag, mag) * torch.pow(two, X).unsqueeze(2)
     err_sq = float(((wb - w_hat) ** 2).sum())
     w_sq = float((wb ** 2).sum())
-    return MxWeight(fmt=fmt, codes=torch.from_numpy(codes.reshape(O, d).astype(np.uint8)),
-                    scales=torch.from_numpy((X + 127).astype(np.uint8)), err_sq=err_sq, w_sq=w_sq)
+    return MxWeight(fmt=fmt, codes=codes.reshape(O, d).to(torch.uint8).cpu().contiguous(),
+                    scales=(X + 127).to(torch.uint8).cpu().contiguous(), err_sq=err_sq, w_sq=w_sq)
 
 
 def pack_canonical(q: torch.Tensor) -> torch.Tensor:
@@ -352,16 +350,16 @@ def tiny_qkv_inputs(device="cpu"):
     return dict(x=x, w16=w16, qw=qw, Q=Q, lam=lam, r=16, d=d, T=T)
 
 
-def llama2_qkv_unit(T: int, device="cpu", layerwise=False) -> Unit:
+def llama2_qkv_unit(T: int, device="cpu", layerwise=False, fmt: str = "int4") -> Unit:
     keys = (0, 1, 0, 0)
     x = make_x(T, 4096, ALPHA_QKV, keys, device)
-    return make_unit("qkv", "group", x, [4096, 4096, 4096], 64, keys, device, layerwise=layerwise)
+    return make_unit("qkv", "group", x, [4096, 4096, 4096], 64, keys, device, layerwise=layerwise, fmt=fmt)
 
 
-def llama2_gateup_unit(T: int = 2048, device="cpu", layerwise=False) -> Unit:
+def llama2_gateup_unit(T: int = 2048, device="cpu", layerwise=False, fmt: str = "int4") -> Unit:
     keys = (0, 2, 0, 0)
     x = make_x(T, 4096, ALPHA_MLP, keys, device)
-    return make_unit("gateup", "group", x, [11008, 11008], 64, keys, device, layerwise=layerwise)
+    return make_unit("gateup", "group", x, [11008, 11008], 64, keys, device, layerwise=layerwise, fmt=fmt)
 
 
 LLAMA2_7B = dict(d=4096, inter=11008, n_layers=32)
