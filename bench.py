@@ -4,8 +4,10 @@
 A step is one pass of the whole path over one batch: the 32-layer LLaMA-2-7B-shaped decoder's
 linear units (per layer the QKV group, the o_proj solo, the gate/up group and the down_proj solo)
 at decode T = 1, rank 64, with the restore mask switching the correction on in 16 of the 32
-layers, run through one glowq_path_forward call.  Inputs and weights are seeded synthetic data
-generated on the GPU and resident in HBM before the timed region.
+layers (chosen beforehand by the library's GlowQ-S selection: g_ner of every layer and the
+budgeted top-k with the layer-order fallback), run through one glowq_path_forward call.  Inputs
+and weights are seeded synthetic data generated on the GPU and resident in HBM before the timed
+region.
 
 The JSON line also carries the dominant kernel's roofline (the fused decode kernel, measured with
 HIP events on the launch stream), the fp64 CPU oracle timed on a bounded sample, and extra
@@ -54,16 +56,41 @@ def unit_flops(T, d, n_outs, r, restore, n_proj=1):
 
 
 # ------------------------------------------------------------------ workload on the GPU
-def build_path(T, device, keep_layers=(), layerwise=False):
+# GlowQ-S fallback: layers whose g_ner lies within this fraction of the best score (in steps of it)
+# count as equal and are taken in layer order
+RESTORE_REL_TOL = 0.01
+
+
+def select_path_mask(g, device, k=16, rel_tol=RESTORE_REL_TOL):
+    """The path's restore set chosen by the library on the GPU (GlowQ-S): g_ner of every layer's
+    seven modules (their fp16 weights regenerated, and the INT4-g128 form the path runs), then the
+    budgeted top-k of the layers with the layer-order fallback for scores within rel_tol steps."""
+    import torch
+    import workload as W
+    L = W.LLAMA2_7B["n_layers"]
+    sums = torch.empty(L, 7, 2, dtype=torch.float64, device=device)
+    ws = None
+    for l in range(L):
+        mods = [(w, g.QWeight.from_workload(W.rtn_quantize(w), device=device)) for w in W.llama2_path_weights(l, device)]
+        if ws is None:
+            ws = torch.empty(g.ner_workspace_bytes_batch([qw.n_out for _, qw in mods]), dtype=torch.uint8,
+                             device=device)
+        g.ner_sums_batch(mods, out=sums[l], workspace=ws)
+        del mods
+    scores, mask = g.restore_select(sums, k, rel_tol)
+    torch.cuda.synchronize()
+    return [bool(v) for v in mask.cpu()], [float(v) for v in scores.cpu()]
+
+
+def build_path(T, device, keep_layers=(), layerwise=False, mask=None):
     import torch
     import workload as W
     from rank_error_compensation_amd import glowq as g
 
     units, descr, keep = [], [], {}
-    mask = None
     t0 = time.time()
     for l in range(W.LLAMA2_7B["n_layers"]):
-        layer_units, mask = W.llama2_path_inputs(T, device=device, layers=[l], layerwise=layerwise)
+        layer_units, mask = W.llama2_path_inputs(T, device=device, layers=[l], layerwise=layerwise, mask=mask)
         for u in layer_units[l]:
             qws = [g.QWeight.from_workload(q, device=device) for q in u.weights]
             ys = [torch.empty(T, q.n_out, dtype=torch.float16, device=device) for q in u.weights]
@@ -891,9 +918,14 @@ def main():
     torch.cuda.set_device(0)
     dev = "cuda"
 
-    # ---- headline: 32-layer path, decode T = 1
+    # ---- headline: 32-layer path, decode T = 1, the restore set selected by the library
     T = 1
-    units, descr, mask, keep = build_path(T, dev, keep_layers=())
+    t0 = time.time()
+    sel_mask, sel_scores = select_path_mask(g, dev)
+    log(f"[bench] restore set (g_ner, top-16, layer order within {RESTORE_REL_TOL} of the best): "
+        f"layers {[l for l in range(32) if sel_mask[l]]}, scores {min(sel_scores):.6g} .. {max(sel_scores):.6g}, "
+        f"{time.time() - t0:.1f}s")
+    units, descr, mask, keep = build_path(T, dev, keep_layers=(), mask=sel_mask)
     first_off = next(l for l in range(32) if not mask[l])
     first_on = next(l for l in range(32) if mask[l])
     plan = g.PathPlan(units)
@@ -956,7 +988,7 @@ def main():
     extra = {}
     if not args.no_extras:
         del plan
-        units_lw, descr_lw, _, _ = build_path(T, dev, layerwise=True)
+        units_lw, descr_lw, _, _ = build_path(T, dev, layerwise=True, mask=sel_mask)
         ws_lw = g.make_workspace(T, 64, 3)
 
         def run_lw():
@@ -991,7 +1023,7 @@ def main():
         log(f"[bench] layerwise {d_lw * 1e6:.1f} us vs group {d_gr * 1e6:.1f} us (kernel sums)")
 
         # prefill pass
-        units_p, descr_p, _, _ = build_path(512, dev)
+        units_p, descr_p, _, _ = build_path(512, dev, mask=sel_mask)
         plan_p = g.PathPlan(units_p)
         ksteps = max(3, args.steps // 10)
         ep = time_steps(plan_p.run, ksteps, 2)
@@ -1038,7 +1070,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import glowq_ref  # noqa: F401  (oracle only in the CPU-baseline leg)
-        _, _, mask2, keep = build_path_keep(T, dev, [first_on, first_off])
+        _, _, mask2, keep = build_path_keep(T, dev, [first_on, first_off], sel_mask)
         cpu = cpu_baseline(keep, mask2)
         log(f"[bench] cpu oracle: {cpu}")
 
@@ -1065,18 +1097,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama2-7b-32-layer-linear-path decode T=1 r=64 restore=16/32 layers",
                    "T": 1, "r": 64, "layers": 32, "d": 4096, "inter": 11008,
-                   "units_per_step": len(descr), "weights": "INT4-g128 fp16 scale/zero"},
+                   "units_per_step": len(descr), "weights": "INT4-g128 fp16 scale/zero",
+                   "restore_set": {"how": f"g_ner on the GPU, top-16 layers, layer order within {RESTORE_REL_TOL} "
+                                          "of the best score", "layers": [l for l in range(32) if sel_mask[l]]}},
         "roofline": roofline, "cpu_baseline": cpu, "achievable_peaks": peaks, "extra": extra,
     }
     print(json.dumps(line), flush=True)
 
 
-def build_path_keep(T, device, layers):
+def build_path_keep(T, device, layers, mask):
     """Only the requested layers of the path (for the CPU oracle sample)."""
     import workload as W
-    keep, mask = {}, None
+    keep = {}
     for l in layers:
-        lu, mask = W.llama2_path_inputs(T, device=device, layers=[l])
+        lu, mask = W.llama2_path_inputs(T, device=device, layers=[l], mask=mask)
         keep[l] = lu[l]
     return None, None, mask, keep
 

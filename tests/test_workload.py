@@ -131,3 +131,15 @@ def test_mx_quantizer_ties_to_even():
     assert int(q.scales[0, 0]) == 127  # max 7.5 -> floor(log2 7.5) - 2 = 0
     got = [glowq_ref.mx_element_value(int(c), "mxfp4") for c in q.codes[0, :6]]
     assert got == [1.0, 2.0, 2.0, 4.0, -4.0, 6.0]
+
+
+def test_module_weights_follow_unit_keys():
+    """make_unit draws module i's weight from keys + (i,) with the unit's outlier columns (the
+    convention llama2_path_weights relies on to regenerate the path's fp16 weights)."""
+    keys = (0, 3, 7, 2)
+    unit = W.make_unit("t", "group", W.make_x(1, 256, 0.77, (1,)), [32, 16], 8, keys)
+    cols = W.outlier_columns(256, keys)
+    for i, O in enumerate([32, 16]):
+        q = W.rtn_quantize(W.make_w(O, 256, list(keys) + [i], cols))
+        assert torch.equal(q.q, unit.weights[i].q) and torch.equal(q.s, unit.weights[i].s)
+    assert [u[3] for u in W.LLAMA2_PATH_UNITS] == [[4096] * 3, [4096], [11008] * 2, [4096]]

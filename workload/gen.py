@@ -365,26 +365,41 @@ def llama2_gateup_unit(T: int = 2048, device="cpu", layerwise=False, fmt: str = 
 LLAMA2_7B = dict(d=4096, inter=11008, n_layers=32)
 
 
+# The modules of layer l of the 32-layer path: (unit index, unit name, kind, n_outs, d_in); module i
+# of unit u draws its fp16 weight from the keys (0, 3, l, u, i) with the unit's outlier columns.
+LLAMA2_PATH_UNITS = [(0, "qkv", "group", [4096] * 3, 4096), (1, "o_proj", "solo", [4096], 4096),
+                     (2, "gateup", "group", [11008] * 2, 4096), (3, "down_proj", "solo", [4096], 11008)]
+
+
+def llama2_path_weights(l: int, device="cpu") -> List[torch.Tensor]:
+    """The fp16 weights of layer l's seven modules in unit order (q, k, v, o, gate, up, down), as
+    llama2_path_inputs draws them (for restore scores that need W itself)."""
+    out = []
+    for u, _, _, n_outs, d_in in LLAMA2_PATH_UNITS:
+        keys = (0, 3, l, u)
+        cols = outlier_columns(d_in, keys)
+        out += [make_w(O, d_in, list(keys) + [i], cols, device) for i, O in enumerate(n_outs)]
+    return out
+
+
 def llama2_path_inputs(T: int, device="cpu", layers: Optional[Sequence[int]] = None, r: int = 64,
-                   layerwise=False):
+                       layerwise=False, mask: Optional[Sequence[bool]] = None):
     """32-layer LLaMA-2-7B linear path.  One activation per input kind, shared by all
-    layers (the layers are not chained).  Returns (units per layer, mask per layer)."""
+    layers (the layers are not chained).  Returns (units per layer, mask per layer).  Without a
+    given mask the restore set is the seeded one of restore_mask (16 of 32 layers)."""
     d, inter, L = LLAMA2_7B["d"], LLAMA2_7B["inter"], LLAMA2_7B["n_layers"]
     x_attn = make_x(T, d, ALPHA_QKV, (0, 3, 100, 0), device)
     x_o = make_x(T, d, ALPHA_QKV, (0, 3, 101, 0), device)
     x_mlp = make_x(T, d, ALPHA_MLP, (0, 3, 102, 0), device)
     x_down = make_x(T, inter, ALPHA_MLP, (0, 3, 103, 0), device)
-    mask = restore_mask(L, 16, (0, 3, 0, 0))
+    mask = restore_mask(L, 16, (0, 3, 0, 0)) if mask is None else [bool(v) for v in mask]
+    xs = {0: x_attn, 1: x_o, 2: x_mlp, 3: x_down}
     layers = range(L) if layers is None else layers
     out = {}
     for l in layers:
         rs = mask[l]
-        out[l] = [
-            make_unit("qkv", "group", x_attn, [d, d, d], r, (0, 3, l, 0), device, rs, layerwise),
-            make_unit("o_proj", "solo", x_o, [d], r, (0, 3, l, 1), device, rs, layerwise),
-            make_unit("gateup", "group", x_mlp, [inter, inter], r, (0, 3, l, 2), device, rs, layerwise),
-            make_unit("down_proj", "solo", x_down, [d], r, (0, 3, l, 3), device, rs, layerwise),
-        ]
+        out[l] = [make_unit(name, kind, xs[u], n_outs, r, (0, 3, l, u), device, rs, layerwise)
+                  for u, name, kind, n_outs, _ in LLAMA2_PATH_UNITS]
     return out, mask
 
 
