@@ -403,3 +403,22 @@ def test_workspace_reuse_across_calls_and_paths():
         ref = oracle_unit(unit)
         for j, (y, yr) in enumerate(zip(ys, ref)):
             assert_parity(y, yr, f"reuse call {i} T={T} module {j}")
+
+
+@pytest.mark.parametrize("T,d,n_outs,r", [
+    (1, 256, (16, 33, 8, 40, 24, 17, 64, 48), 16),          # decode, the most modules a call takes
+    (12, 384, (130, 96, 33, 8, 64, 200, 17, 90), 24),       # decode, activations in LDS
+    (40, 256, (700, 650, 720, 690, 700, 710, 640, 660), 32),  # fused 17-64-token tiles
+    (300, 128, (100, 36, 48, 16, 80, 20, 64, 8), 40),       # prefill
+])
+def test_eight_modules_group_and_layerwise(T, d, n_outs, r):
+    """GLOWQ_MAX_MODULES = 8 modules in one call: the group form (one shared projection) and the
+    layerwise form (eight projections, eight right factors) against the oracle."""
+    keys = (17, T, d, r)
+    x = W.make_x(T, d, 0.77, keys)
+    unit = W.make_unit("g8", "group", x, list(n_outs), r, keys, layerwise=True)
+    du = DevUnit(unit, layerwise=True)
+    for i, (y, yr) in enumerate(zip(du.forward(), oracle_unit(unit))):
+        assert_parity(y, yr, f"8 modules T={T} module {i}")
+    for i, (y, yr) in enumerate(zip(du.forward_layerwise(), oracle_unit(unit, layerwise=True))):
+        assert_parity(y, yr, f"8 modules layerwise T={T} module {i}")

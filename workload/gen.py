@@ -177,6 +177,13 @@ class MxWeight:
         return int(self.codes.shape[1])
 
 
+def floor_log2(v: torch.Tensor) -> torch.Tensor:
+    """floor(log2 v) of positive fp64 values, exactly (from the binary exponent; a device log2 may
+    land just below an integer at powers of two); 0 where v == 0."""
+    _, e = torch.frexp(v)
+    return torch.where(v > 0, (e - 1).to(v.dtype), torch.zeros_like(v))
+
+
 def mx_quantize(w: torch.Tensor, fmt: str) -> MxWeight:
     """Microscaling quantisation of the generated weights (the conversion of the OCP MX v1.0
     specification): per block of 32 inputs the shared exponent is floor(log2 max|w|) minus the
@@ -194,15 +201,14 @@ def mx_quantize(w: torch.Tensor, fmt: str) -> MxWeight:
     wb = w.detach().to(torch.float64).reshape(O, d // MX_BLOCK, MX_BLOCK)
     two = torch.tensor(2.0, dtype=torch.float64, device=wb.device)
     amax = wb.abs().amax(dim=2)
-    X = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, 1.0))) - emax,
-                    torch.full_like(amax, float(lo))).clamp(lo, hi)
+    X = torch.where(amax > 0, floor_log2(amax) - emax, torch.full_like(amax, float(lo))).clamp(lo, hi)
     u = wb.abs() / torch.pow(two, X).unsqueeze(2)
-    k = torch.floor(torch.log2(torch.where(u > 0, u, 1.0))).clamp(emin, emax)  # subnormal step below
+    k = floor_log2(u).clamp(emin, emax)  # below the normal range the step is the subnormal one
     step = torch.pow(two, k - mb)
     mag = torch.minimum(torch.round(u / step) * step, torch.tensor(top, dtype=torch.float64, device=wb.device))
     # encode: subnormal when below 2^emin, else exponent field and mantissa of the magnitude
     sub = mag < math.ldexp(1.0, emin)
-    kk = torch.floor(torch.log2(torch.where(sub, 1.0, mag)))
+    kk = floor_log2(torch.where(sub, 1.0, mag))
     e_field = torch.where(sub, torch.zeros_like(kk), kk + bias)
     m_field = torch.where(sub, mag / math.ldexp(1.0, emin - mb), (mag / torch.pow(two, kk) - 1.0) * (1 << mb))
     assert bool(torch.all(m_field == torch.round(m_field))) and bool(torch.all(m_field < (1 << mb)))
