@@ -184,6 +184,12 @@ def floor_log2(v: torch.Tensor) -> torch.Tensor:
     return torch.where(v > 0, (e - 1).to(v.dtype), torch.zeros_like(v))
 
 
+def pow2(e: torch.Tensor) -> torch.Tensor:
+    """2^e in fp64 for integer-valued e in the normal range, exactly (built from the exponent bits;
+    a device pow is not always exact)."""
+    return ((e.to(torch.int64) + 1023) << 52).view(torch.float64)
+
+
 def mx_quantize(w: torch.Tensor, fmt: str) -> MxWeight:
     """Microscaling quantisation of the generated weights (the conversion of the OCP MX v1.0
     specification): per block of 32 inputs the shared exponent is floor(log2 max|w|) minus the
@@ -199,22 +205,21 @@ def mx_quantize(w: torch.Tensor, fmt: str) -> MxWeight:
     O, d = w.shape
     assert d % MX_BLOCK == 0
     wb = w.detach().to(torch.float64).reshape(O, d // MX_BLOCK, MX_BLOCK)
-    two = torch.tensor(2.0, dtype=torch.float64, device=wb.device)
     amax = wb.abs().amax(dim=2)
     X = torch.where(amax > 0, floor_log2(amax) - emax, torch.full_like(amax, float(lo))).clamp(lo, hi)
-    u = wb.abs() / torch.pow(two, X).unsqueeze(2)
+    u = wb.abs() / pow2(X).unsqueeze(2)
     k = floor_log2(u).clamp(emin, emax)  # below the normal range the step is the subnormal one
-    step = torch.pow(two, k - mb)
+    step = pow2(k - mb)
     mag = torch.minimum(torch.round(u / step) * step, torch.tensor(top, dtype=torch.float64, device=wb.device))
     # encode: subnormal when below 2^emin, else exponent field and mantissa of the magnitude
     sub = mag < math.ldexp(1.0, emin)
     kk = floor_log2(torch.where(sub, 1.0, mag))
     e_field = torch.where(sub, torch.zeros_like(kk), kk + bias)
-    m_field = torch.where(sub, mag / math.ldexp(1.0, emin - mb), (mag / torch.pow(two, kk) - 1.0) * (1 << mb))
+    m_field = torch.where(sub, mag / math.ldexp(1.0, emin - mb), (mag / pow2(kk) - 1.0) * (1 << mb))
     assert bool(torch.all(m_field == torch.round(m_field))) and bool(torch.all(m_field < (1 << mb)))
     sign = (wb < 0) & (mag > 0)
     codes = (sign.to(torch.int64) << (eb + mb)) | (e_field.to(torch.int64) << mb) | m_field.to(torch.int64)
-    w_hat = torch.where(sign, -mag, mag) * torch.pow(two, X).unsqueeze(2)
+    w_hat = torch.where(sign, -mag, mag) * pow2(X).unsqueeze(2)
     err_sq = float(((wb - w_hat) ** 2).sum())
     w_sq = float((wb ** 2).sum())
     return MxWeight(fmt=fmt, codes=codes.reshape(O, d).to(torch.uint8).cpu().contiguous(),
