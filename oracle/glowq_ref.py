@@ -261,6 +261,77 @@ def bruteforce_group_w4a8(x, q_packed_list, s_list, z_list, n_outs, k_in, b, a_l
     return outs
 
 
+# --------------------------------------------------------------------------- MX weights x MXFP8 activations
+# The 8-bit-activation form of the method (arXiv page, Tables 14 and 15: W4A8) on microscaling
+# weights (Table 13), with the activations in the same family: MXFP8, i.e. FP8 E4M3 elements
+# sharing one E8M0 scale per 32 consecutive inputs of a token (OCP Microscaling v1.0).  The
+# conversion is the specification's: the block's shared exponent is floor(log2 max|x|) minus the
+# element's largest exponent (8 for E4M3, whose largest value is 1.75 * 2^8 = 448), and each
+# x / 2^X becomes the nearest E4M3 value, ties to the even mantissa, saturating at 448 (a block of
+# zeros gets the smallest scale, 2^-127, and zero codes).  The correction branch stays high
+# precision, as for W4A8: R = X B^T from the fp16 activations.
+E4M3_MAX = 448.0
+
+
+def fp8_e4m3_value(code: int) -> float:
+    """Value of an E4M3 code: bias 7, exponent field 0 subnormal (2^-6 * m/8); exponent field 15
+    with mantissa 7 is NaN (no infinities)."""
+    assert 0 <= code < 256
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return math.nan
+    if e == 0:
+        return sign * math.ldexp(m / 8.0, -6)
+    return sign * math.ldexp(1.0 + m / 8.0, e - 7)
+
+
+def quantize_x_mxfp8(x):
+    """MXFP8 codes of fp16 activations: (codes uint8 [T][d], E4M3; scales uint8 [T][d/32], E8M0).
+    Every step is exact: x is fp16, x / 2^X a power-of-two scaling, and the element is chosen by
+    distance to each finite E4M3 magnitude."""
+    xf = _f64(x)
+    T, d = xf.shape
+    assert d % MX_BLOCK == 0
+    blocks = xf.reshape(T, d // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=2) if T else np.zeros((0, d // MX_BLOCK))
+    X = np.full(amax.shape, -127, dtype=np.int64)
+    for idx in zip(*np.nonzero(amax)):
+        X[idx] = math.frexp(float(amax[idx]))[1] - 1 - 8  # floor(log2 amax) - 8
+    u = np.abs(blocks) / np.ldexp(1.0, X)[:, :, None]
+    mags = np.array([fp8_e4m3_value(c) for c in range(0x7F)])  # finite non-negative values, code order
+    dist = np.abs(u[..., None] - mags)
+    best = dist.min(axis=-1, keepdims=True)
+    tie = dist == best
+    # nearest value; of two equally near ones, the even code (even mantissa)
+    cand = np.where(tie, np.arange(0x7F), 1 << 20)
+    even = np.where(tie & (np.arange(0x7F) % 2 == 0), np.arange(0x7F), 1 << 20)
+    code = np.where(tie.sum(axis=-1) > 1, even.min(axis=-1), cand.min(axis=-1))
+    code = np.where((blocks < 0) & (code > 0), code | 0x80, code)
+    return code.reshape(T, d).astype(np.uint8), (X + 127).astype(np.uint8)
+
+
+def dequant_mxfp8(codes, scales) -> np.ndarray:
+    """fp64 values of MXFP8 activations: E4M3 element times 2^(S - 127)."""
+    c = _np(codes).astype(np.int64)
+    s = _np(scales).astype(np.int64)
+    table = np.array([fp8_e4m3_value(v) for v in range(256)])
+    return table[c] * np.ldexp(1.0, s - 127)[:, np.arange(c.shape[1]) // MX_BLOCK]
+
+
+def group_forward_mx8(x, w_hats: Sequence[np.ndarray], b, a_list, restore: bool = True) -> List[np.ndarray]:
+    """MX weights x MXFP8 activations: y_i = X_q W_hat_i^T + [restore and r > 0] (X B^T) A_i^T with
+    X_q = dequant_mxfp8(quantize_x_mxfp8(X)) (fp64, exact products of the element values) and the
+    shared projection from the fp16 activations."""
+    xq = dequant_mxfp8(*quantize_x_mxfp8(x))
+    outs = [xq @ wh.T for wh in w_hats]
+    r = 0 if b is None else _np(b).shape[0]
+    if restore and r > 0:
+        R = shared_projection(x, b)
+        outs = [y + R @ _f64(a).T for y, a in zip(outs, a_list)]
+    return outs
+
+
 # --------------------------------------------------------------------------- mixture of experts
 # The arXiv page's Figures 7-9 (Qwen1.5-MoE-A2.7B) show the covariance-aligned shared basis for
 # the MLP gate/up projections both aggregated over all experts (Fig. 8) and for one expert alone

@@ -736,11 +736,82 @@ def check_mx_dequant_hand(ref):
         assert [float(v) for v in Wf[0]] == [ref.mx_element_value(v % n, fmt) for v in range(128)], fmt
 
 
+# ------------------------------------------------------------------ MXFP8 activations
+def check_fp8_e4m3_codes(ref):
+    """Every E4M3 code against torch's float8_e4m3fn conversion (0x7F and 0xFF are NaN)."""
+    import torch
+    want = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    for c in range(256):
+        got, w = ref.fp8_e4m3_value(c), float(want[c])
+        assert (math.isnan(got) and math.isnan(w)) or got == w, (c, got, w)
+
+
+def check_mx8_quantizer_hand(ref):
+    """A block whose largest magnitude is 1.9: shared exponent floor(log2 1.9) - 8 = -8 (scale byte
+    119); 1.0 -> 256 (code 0x78), 0.5 -> 128 (0x70), 1.0625 -> 272, halfway between 256 and 288,
+    -> 256 (even mantissa), 1.9 -> 486.4 -> saturated to 448 (0x7E), -0.25 -> -64 (0xE8); a block
+    of zeros: scale byte 0, codes 0."""
+    x = np.zeros((2, 64), dtype=np.float16)
+    x[0, :5] = [1.0, 0.5, 1.0625, 1.9, -0.25]
+    codes, scales = ref.quantize_x_mxfp8(x)
+    assert scales.tolist() == [[119, 0], [0, 0]], scales
+    assert codes[0, :5].tolist() == [0x78, 0x70, 0x78, 0x7E, 0xE8], codes[0, :5]
+    assert not codes[0, 5:].any() and not codes[1].any()
+    xq = ref.dequant_mxfp8(codes, scales)
+    assert xq[0, :5].tolist() == [1.0, 0.5, 1.0, 1.75, -0.25]
+
+
+def check_mx8_quantizer_vs_torch(ref):
+    """Random fp16 activations (several magnitudes): each block's scale is 2^(floor(log2 max|x|) - 8)
+    (from torch.frexp) and each element is torch's round-to-nearest-even float8_e4m3fn cast of
+    x / scale wherever that cast is finite, 448 with x's sign where it overflows."""
+    import torch
+    g = torch.Generator().manual_seed(5)
+    x = (torch.randn(24, 256, generator=g) * torch.logspace(-3, 3, 24).unsqueeze(1)).to(torch.float16)
+    x[3, 32:64] = 0
+    codes, scales = ref.quantize_x_mxfp8(x)
+    xb = x.double().reshape(24, 8, 32)
+    amax = xb.abs().amax(dim=2)
+    _, e = torch.frexp(amax)
+    want_s = torch.where(amax > 0, e - 1 - 8 + 127, torch.zeros_like(e))
+    assert np.array_equal(scales.astype(np.int64), want_s.numpy()), "block scales"
+    sc = torch.ldexp(torch.ones_like(amax), want_s - 127).repeat_interleave(32, dim=1)
+    t = (x.double() / sc).to(torch.float8_e4m3fn).to(torch.float64)
+    xq = torch.from_numpy(ref.dequant_mxfp8(codes, scales)) / sc
+    fin = torch.isfinite(t)
+    assert torch.equal(xq[fin], t[fin])
+    assert torch.equal(xq[~fin], 448.0 * torch.sign(x.double()[~fin]))
+
+
+def check_mx8_bruteforce(ref):
+    """group_forward_mx8 on a tiny problem against explicit loops (math.fsum): every activation
+    dequantised element by element from its code and block scale, the correction from the fp16
+    activations."""
+    rng = np.random.default_rng(9)
+    T, d, r, n_outs = 3, 64, 4, (5, 3)
+    x = (rng.standard_normal((T, d)) * 2).astype(np.float16)
+    w_hats = [rng.integers(-7, 8, (O, d)).astype(np.float64) / 8 for O in n_outs]
+    b = (rng.standard_normal((r, d)) / 8).astype(np.float16)
+    a_list = [(rng.standard_normal((O, r)) / 4).astype(np.float16) for O in n_outs]
+    ys = ref.group_forward_mx8(x, w_hats, b, a_list, True)
+    codes, scales = ref.quantize_x_mxfp8(x)
+    for i, O in enumerate(n_outs):
+        for t in range(T):
+            for o in range(O):
+                base = math.fsum(ref.fp8_e4m3_value(int(codes[t, k])) * 2.0 ** (int(scales[t, k // 32]) - 127)
+                                 * w_hats[i][o, k] for k in range(d))
+                rr = [math.fsum(float(x[t, k]) * float(b[j, k]) for k in range(d)) for j in range(r)]
+                corr = math.fsum(rr[j] * float(a_list[i][o, j]) for j in range(r))
+                want = base + corr
+                assert abs(ys[i][t, o] - want) <= 1e-12 * (1 + abs(want)), (i, t, o)
+
+
 ALL_REF_CHECKS = [check_dequant_exhaustive, check_dequant_golden, check_restore_off,
                   check_associativity_small_int, check_bruteforce, check_row_independence,
                   check_path_mask, check_parity_errors, check_w4a8_quantizer_hand,
                   check_w4a8_quantizer_invariants, check_w4a8_bruteforce, check_w4a8_lossless_and_scale,
-                  check_moe_rows, check_mx_elements, check_mx_scales, check_mx_dequant_hand]
+                  check_moe_rows, check_mx_elements, check_mx_scales, check_mx_dequant_hand,
+                  check_fp8_e4m3_codes, check_mx8_quantizer_hand, check_mx8_quantizer_vs_torch, check_mx8_bruteforce]
 ALL_SOL_CHECKS = [check_eckart_young, check_isotropic, check_usage_weighted_risk, check_qr_core,
                   check_cholesky_vs_symmetric, check_randomized_svd, check_scores, check_second_moment,
                   check_pinv_lift, check_restore_tol]

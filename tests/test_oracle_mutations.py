@@ -310,6 +310,46 @@ def e8m0_no_nan(s):
     return math.ldexp(1.0, int(s) - 127)
 
 
+def _mx8_with(emax=8, ties_away=False, nan_overflow=False, block=32, no_sign=False):
+    def q(x):
+        xf = G._f64(x)
+        T, d = xf.shape
+        blocks = xf.reshape(T, d // block, block)
+        amax = np.abs(blocks).max(axis=2)
+        X = np.full(amax.shape, -127, dtype=np.int64)
+        for idx in zip(*np.nonzero(amax)):
+            X[idx] = math.frexp(float(amax[idx]))[1] - 1 - emax
+        u = np.abs(blocks) / np.ldexp(1.0, X)[:, :, None]
+        mags = np.array([G.fp8_e4m3_value(c) for c in range(0x7F)])
+        dist = np.abs(u[..., None] - mags)
+        best = dist.min(axis=-1, keepdims=True)
+        tie = dist == best
+        pick = np.where(tie, np.arange(0x7F), -1).max(axis=-1) if ties_away else None
+        if pick is None:
+            cand = np.where(tie, np.arange(0x7F), 1 << 20)
+            even = np.where(tie & (np.arange(0x7F) % 2 == 0), np.arange(0x7F), 1 << 20)
+            pick = np.where(tie.sum(axis=-1) > 1, even.min(axis=-1), cand.min(axis=-1))
+        if nan_overflow:
+            pick = np.where(u > 464, 0x7F, pick)
+        if not no_sign:
+            pick = np.where((blocks < 0) & (pick > 0), pick | 0x80, pick)
+        codes = pick.reshape(T, d).astype(np.uint8)
+        sc = (X + 127).astype(np.uint8)
+        if block != 32:
+            sc = sc[:, ::32 // block]
+        return codes, sc
+    return q
+
+
+def mx8_corr_on_quantised(x, w_hats, b, a_list, restore=True):
+    xq = G.dequant_mxfp8(*G.quantize_x_mxfp8(x))
+    outs = [xq @ wh.T for wh in w_hats]
+    if restore and b is not None:
+        R = xq @ G._f64(b).T
+        outs = [y + R @ G._f64(a).T for y, a in zip(outs, a_list)]
+    return outs
+
+
 REF_MUTANTS = {
     "dequant_plus_z": dict(dequant=dequant_plus_z),
     "dequant_group64": dict(dequant=dequant_group64),
@@ -341,6 +381,12 @@ REF_MUTANTS = {
     "mx_dequant_block16": dict(dequant_mx=mx_dequant_block16),
     "e8m0_bias128": dict(e8m0_value=e8m0_bias128),
     "e8m0_no_nan": dict(e8m0_value=e8m0_no_nan),
+    "mx8_emax_7": dict(quantize_x_mxfp8=_mx8_with(emax=7)),
+    "mx8_ties_away": dict(quantize_x_mxfp8=_mx8_with(ties_away=True)),
+    "mx8_nan_on_overflow": dict(quantize_x_mxfp8=_mx8_with(nan_overflow=True)),
+    "mx8_block16": dict(quantize_x_mxfp8=_mx8_with(block=16)),
+    "mx8_no_sign": dict(quantize_x_mxfp8=_mx8_with(no_sign=True)),
+    "mx8_corr_on_quantised": dict(group_forward_mx8=mx8_corr_on_quantised),
 }
 
 SOL_MUTANTS = {
