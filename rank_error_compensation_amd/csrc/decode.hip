@@ -177,7 +177,8 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
     const size_t qstride = (size_t)M.n_tiles16 * QB, szstride = (size_t)M.n_tiles16 * 64;  // per group
     // MXFP6: the second plane of a lane's codes (8 bytes at 1024 + 8 lane of the block)
     const int q6ofs = 1024 + 8 * lane - 16 * lane;
-    const int kofs = 8 * (lane >> 4);
+    const int kofs = Fmt<F>::xofs(lane >> 4);  // the lane's activation operand within a group
+    constexpr int XS = Fmt<F>::xstep;          // and its step per matrix-core slice
     const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     const NibConsts nc = nib_consts();
     const int g0 = ks_idx * args.dec_gk, g1 = min(G, g0 + args.dec_gk);  // this workgroup's groups
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
             for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const h8 v = load_h8(xrow[tt] + (size_t)g * kGroup + 32 * j);
+                    const h8 v = load_h8(xrow[tt] + (size_t)g * kGroup + XS * j);
                     bx[XLDS ? 0 : u][tt][j] = tok_ok[tt] ? v : zero8;
                 }
         }
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
             for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    bl[XLDS ? tt : 0][j] = *reinterpret_cast<const h8*>(xrow[tt] + (size_t)g * kGroup + 32 * j);
+                    bl[XLDS ? tt : 0][j] = *reinterpret_cast<const h8*>(xrow[tt] + (size_t)g * kGroup + XS * j);
             __builtin_amdgcn_sched_barrier(0);
         }
         h8 aop[RT][4];
@@ -272,13 +273,14 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu((XC > 0
             // accumulate straight into the running sums
 #pragma unroll
             for (int rr = 0; rr < RT; ++rr) {
+                const float sc = mx_scale(zso[u][rr], lane >> 4);  // the lane's MX block
                 if constexpr (SIX) {
-                    const h32 e = mx6_h32<F>(qv[u][rr], qv6[SIX ? u : 0][rr]);
+                    const h32 e = mx6_h32<F>(qv[u][rr], qv6[SIX ? u : 0][rr], sc);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) aop[rr][j] = mx6_slice(e, j, mx_scale(zso[u][rr], j));
+                    for (int j = 0; j < 4; ++j) aop[rr][j] = mx6_slice(e, j);
                 } else {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) aop[rr][j] = mx4_h8(qv[u][rr][j], mx_scale(zso[u][rr], j));
+                    for (int j = 0; j < 4; ++j) aop[rr][j] = mx4_h8(qv[u][rr][j], sc);
                 }
             }
 #pragma unroll

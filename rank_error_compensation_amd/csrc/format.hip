@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
 }
 
 // MX codes: one thread per lane record (row tile, group, lane l) of the device layout: the 32
-// codes of row 16 rt + l % 16 at inputs 128 g + 32 j + 8 (l / 16) + e, code n = 8 j + e packed at
+// codes of row 16 rt + l % 16 at inputs 128 g + 32 (l / 16) + n (one MX block), code n packed at
 // bit NB n (NB = 4 or 6); codes wider than NB bits set bit 0 of the flag.
 template <int NB>
 __global__ __launch_bounds__(256) void repack_mx_q_kernel(const uint8_t* __restrict__ codes, int64_t n_out,
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void repack_mx_q_kernel(const uint8_t* __restr
     for (int j = 0; j < 4; ++j) {
         u2 c8 = {0u, 0u};
         if (row < n_out)
-            c8 = *reinterpret_cast<const u2*>(codes + row * k_in + g * kGroup + 32 * j + 8 * (l >> 4));
+            c8 = *reinterpret_cast<const u2*>(codes + row * k_in + g * kGroup + 32 * (l >> 4) + 8 * j);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t c = (c8[e >> 2] >> (8 * (e & 3))) & 0xFFu;
@@ -184,19 +184,19 @@ __global__ __launch_bounds__(256) void dequant_mx_kernel(const uint8_t* __restri
     if (row >= n_out) return;
     const uint8_t* base = qd + blk * Fmt<F>::qblock;
     const u4 q = *reinterpret_cast<const u4*>(base + 16 * l);
-    const uint32_t sw = szd[blk * 16 + (l & 15)];
+    const float sc = mx_scale(szd[blk * 16 + (l & 15)], l >> 4);  // the lane's block
     h8 v[4];
     if constexpr (Fmt<F>::six) {
-        const h32 e = mx6_h32<F>(q, *reinterpret_cast<const u2*>(base + 1024 + 8 * l));
+        const h32 e = mx6_h32<F>(q, *reinterpret_cast<const u2*>(base + 1024 + 8 * l), sc);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = mx6_slice(e, j, mx_scale(sw, j));
+        for (int j = 0; j < 4; ++j) v[j] = mx6_slice(e, j);
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = mx4_h8(q[j], mx_scale(sw, j));
+        for (int j = 0; j < 4; ++j) v[j] = mx4_h8(q[j], sc);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int64_t k0 = g * kGroup + 32 * j + 8 * (l >> 4);
+        const int64_t k0 = g * kGroup + 32 * (l >> 4) + 8 * j;
         if (DTYPE == 0) {
             float* o = reinterpret_cast<float*>(out) + row * k_in + k0;
             reinterpret_cast<f4*>(o)[0] = f4{(float)v[j][0], (float)v[j][1], (float)v[j][2], (float)v[j][3]};

@@ -143,16 +143,20 @@ __device__ __forceinline__ void zero_consts(uint32_t zs, h2& zc1024, h2& zc64) {
 
 // --------------------------------------------------------------------- MX weight formats
 // Device layout of an MX module (elements of the OCP Microscaling v1.0 formats, one E8M0 scale per
-// 32 inputs of a row), in the INT4 geometry:
+// 32 inputs of a row), in the INT4 block geometry but with one MX block per lane:
 //   q  : G x NT blocks of Fmt<F>::qblock bytes, block (rt, g) at (g NT + rt) qblock.  Lane l owns
-//        the 32 codes of row 16 rt + l % 16 for the inputs k = 128 g + 32 j + 8 (l / 16) + e
-//        (slice j = 0..3, e = 0..7; code n = 8 j + e), i.e. the matrix-core operand order above.
-//        MXFP4: the 16 bytes at 16 l, code n in bits 4n..4n+3 (the scaled fp4 conversion turns
-//        byte b of a word into the fp16 pair (2b, 2b + 1), low nibble first).  MXFP6: 24 bytes in
-//        two naturally aligned planes, 16 at 16 l and 8 at 1024 + 8 l, code n in bits 6n..6n+5 of
-//        their 192-bit concatenation (the order of the 32-value fp6 conversion).
-//   sz : 64-byte blocks as for INT4; row i's word at 4 i holds in byte j the E8M0 scale S of the
-//        inputs 128 g + 32 j .. + 31.  Rows >= n_out have codes 0 and scale bytes 127.
+//        the 32 codes of row 16 rt + l % 16 for the inputs 128 g + 32 (l / 16) + n, n = 0..31 -- the
+//        whole MX block l / 16 of that row, so a lane needs one scale.  MXFP4: the 16 bytes at 16 l,
+//        code n in bits 4n..4n+3 (the scaled fp4 conversion turns byte b of a word into the fp16
+//        pair (2b, 2b + 1), low nibble first; the block-scaled matrix cores read the same 16 bytes as
+//        their FP4 operand).  MXFP6: 24 bytes in two naturally aligned planes, 16 at 16 l and 8 at
+//        1024 + 8 l, code n in bits 6n..6n+5 of their 192-bit concatenation (the order of the
+//        32-value fp6 conversion).
+//        For the fp16 matrix cores (16x16x32 steps) word j of a lane, codes 8j .. 8j + 7, is the
+//        A operand of step j, so the activation operand of lane (t, q) at step j is the 8 inputs
+//        128 g + 32 q + 8 j .. + 7 of token t ("block order", instead of INT4's 128 g + 32 j + 8 q).
+//   sz : 64-byte blocks as for INT4; row i's word at 4 i holds in byte q the E8M0 scale S of the
+//        inputs 128 g + 32 q .. + 31.  Rows >= n_out have codes 0 and scale bytes 127.
 // The repack admits only scales for which every element times 2^(S - 127) is an fp16 value, so
 // the dequantised operands are exact.
 enum : int { kFmtInt4 = 0, kFmtMxfp4 = 1, kFmtMxfp6E2M3 = 2, kFmtMxfp6E3M2 = 3 };
@@ -161,13 +165,16 @@ struct Fmt {
     static constexpr bool mx = F != kFmtInt4;
     static constexpr bool six = F == kFmtMxfp6E2M3 || F == kFmtMxfp6E3M2;
     static constexpr int qblock = six ? 1536 : 1024;
+    // activation operand of matrix-core step j for lane group q (offsets in inputs within a group)
+    static __device__ __forceinline__ int xofs(int q) { return mx ? 32 * q : 8 * q; }
+    static constexpr int xstep = mx ? 8 : 32;
 };
 typedef _Float16 h32 __attribute__((ext_vector_type(32)));
 typedef uint32_t u6 __attribute__((ext_vector_type(6)));
 
-// The fp32 power of two 2^(S - 127) of scale byte j of a row's scale word (S in 1..254).
-__device__ __forceinline__ float mx_scale(uint32_t sw, int j) {
-    return __builtin_bit_cast(float, ((sw >> (8 * j)) & 0xFFu) << 23);
+// The fp32 power of two 2^(S - 127) of scale byte q of a row's scale word (S in 1..254).
+__device__ __forceinline__ float mx_scale(uint32_t sw, int q) {
+    return __builtin_bit_cast(float, ((sw >> (8 * q)) & 0xFFu) << 23);
 }
 
 // Eight FP4 codes (one word, code e in bits 4e..4e+3) -> fp16 element * scale.
@@ -179,34 +186,30 @@ __device__ __forceinline__ h8 mx4_h8(uint32_t w, float s) {
     return h8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// A lane's 32 FP6 codes -> their fp16 element values (unscaled, exact).
+// A lane's 32 FP6 codes (one MX block) -> fp16 element * scale (exact in the admitted range).
 template <int F>
-__device__ __forceinline__ h32 mx6_h32(u4 lo, u2 hi) {
+__device__ __forceinline__ h32 mx6_h32(u4 lo, u2 hi, float s) {
     const u6 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1]};
     if constexpr (F == kFmtMxfp6E3M2)
-        return __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(w, 1.0f);
+        return __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(w, s);
     else
-        return __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(w, 1.0f);
+        return __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(w, s);
 }
 
 // The same conversion, never merged with an identical one: kernels that hold many row tiles take
 // one slice per conversion instead of keeping all 32 values live across their slice loop (the
 // empty asm makes the input a fresh value; it emits no instruction).
 template <int F>
-__device__ __forceinline__ h32 mx6_h32_fresh(u4 lo, u2 hi) {
+__device__ __forceinline__ h32 mx6_h32_fresh(u4 lo, u2 hi, float s) {
     uint32_t w0 = lo[0];
     asm volatile("" : "+v"(w0));
-    return mx6_h32<F>(u4{w0, lo[1], lo[2], lo[3]}, hi);
+    return mx6_h32<F>(u4{w0, lo[1], lo[2], lo[3]}, hi, s);
 }
 
-// Slice j (codes 8 j .. 8 j + 7) of a lane's FP6 values times the block's scale, in fp16 (the
-// product is exact in the admitted scale range).
-__device__ __forceinline__ h8 mx6_slice(const h32& v, int j, float s) {
-    const _Float16 sh = (_Float16)s;
-    const h8 s8 = {sh, sh, sh, sh, sh, sh, sh, sh};
-    const h8 e = {v[8 * j], v[8 * j + 1], v[8 * j + 2], v[8 * j + 3],
-                  v[8 * j + 4], v[8 * j + 5], v[8 * j + 6], v[8 * j + 7]};
-    return e * s8;
+// Slice j (codes 8 j .. 8 j + 7) of a lane's 32 converted values.
+__device__ __forceinline__ h8 mx6_slice(const h32& v, int j) {
+    return h8{v[8 * j], v[8 * j + 1], v[8 * j + 2], v[8 * j + 3], v[8 * j + 4], v[8 * j + 5], v[8 * j + 6],
+              v[8 * j + 7]};
 }
 
 __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {

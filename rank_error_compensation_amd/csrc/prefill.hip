@@ -220,31 +220,50 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void prefill_kernel(co
             }
         }
         if (act && MX) {
-            // MX operands carry their block scales (exact fp16)
-            const _Float16* xb = &xs[kg][buf][(lane & 15) * LS + kofs];
+            // MX operands carry their block scales (exact fp16); a lane holds one MX block, so its
+            // activation operands are the block's inputs in order (block order)
+            const _Float16* xb = &xs[kg][buf][(lane & 15) * LS + Fmt<F>::xofs(lane >> 4)];
+            float sc[RR];
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) sc[rr] = mx_scale(zs[rr], lane >> 4);
             // MXFP6: one 32-value conversion per row tile, or per (row tile, slice) when the
             // 1024-thread tile of two row tiles could not hold both conversions' values
             constexpr bool kFresh = RR * KS >= 8;
+            if constexpr (SIX && kFresh) {
+                // row tile by row tile: one conversion live at a time (the activation operands are
+                // read once per row tile)
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) {
+                    const h32 e = mx6_h32_fresh<F>(qv[rr], q6[rr], sc[rr]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const h8 a = mx6_slice(e, j);
+#pragma unroll
+                        for (int tt = 0; tt < TT; ++tt) {
+                            const h8 b = *reinterpret_cast<const h8*>(xb + tt * 16 * LS + Fmt<F>::xstep * j);
+                            acc[tt][rr] = mfma16(a, b, acc[tt][rr]);
+                        }
+                    }
+                }
+            }
             h32 e6[SIX && !kFresh ? RR : 1];
             if constexpr (SIX && !kFresh) {
 #pragma unroll
-                for (int rr = 0; rr < RR; ++rr) e6[rr] = mx6_h32<F>(qv[rr], q6[rr]);
+                for (int rr = 0; rr < RR; ++rr) e6[rr] = mx6_h32<F>(qv[rr], q6[rr], sc[rr]);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 4 && !(SIX && kFresh); ++j) {
                 h8 a[RR];
 #pragma unroll
                 for (int rr = 0; rr < RR; ++rr) {
-                    if constexpr (SIX && kFresh)
-                        a[rr] = mx6_slice(mx6_h32_fresh<F>(qv[rr], q6[rr]), j, mx_scale(zs[rr], j));
-                    else if constexpr (SIX)
-                        a[rr] = mx6_slice(e6[rr], j, mx_scale(zs[rr], j));
+                    if constexpr (SIX)
+                        a[rr] = mx6_slice(e6[SIX && !kFresh ? rr : 0], j);
                     else
-                        a[rr] = mx4_h8(qv[rr][j], mx_scale(zs[rr], j));
+                        a[rr] = mx4_h8(qv[rr][j], sc[rr]);
                 }
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt) {
-                    const h8 b = *reinterpret_cast<const h8*>(xb + tt * 16 * LS + 32 * j);
+                    const h8 b = *reinterpret_cast<const h8*>(xb + tt * 16 * LS + Fmt<F>::xstep * j);
 #pragma unroll
                     for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = mfma16(a[rr], b, acc[tt][rr]);
                 }
@@ -453,10 +472,14 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
             __builtin_amdgcn_global_load_lds((const void*)(xbase + (size_t)g * kGroup * 2 + xoff[i]),
                                              (lds_void*)(xw + ((size_t)buf * BM + 4 * TT * wave + 4 * i) * 16), 16, 0, 0);
     };
-    // operand read of slice j: lane l takes row 16 tt + l % 16, chunk 4 j + l / 16, swizzled
+    // operand read of slice j: lane l takes row 16 tt + l % 16, chunk 4 j + l / 16 (MX: 4 (l / 16) + j),
+    // swizzled
     uint32_t bofs[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bofs[j] = (uint32_t)((lane & 15) * 16 + ((4 * j + (lane >> 4)) ^ (lane & 15)));
+    for (int j = 0; j < 4; ++j) {
+        const int chunk = MX ? 4 * (lane >> 4) + j : 4 * j + (lane >> 4);  // MX: block order
+        bofs[j] = (uint32_t)((lane & 15) * 16 + (chunk ^ (lane & 15)));
+    }
 
     u4 qv[RR];
     u2 q6[SIX ? RR : 1];
@@ -503,17 +526,18 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
             }
         }
         // operand j of row tile rr: INT4 (q - z) s; MX element times its block scale (exact)
-        // MXFP6 (64-token tile): each row tile's 32 values converted once per group
+        // MXFP6 (64-token tile): each row tile's 32 values converted once per group, with the
+        // lane's block scale
         h32 e6[SIX ? RR : 1];
         if constexpr (SIX) {
 #pragma unroll
-            for (int rr = 0; rr < RR; ++rr) e6[rr] = mx6_h32<F>(qv[rr], q6[rr]);
+            for (int rr = 0; rr < RR; ++rr) e6[rr] = mx6_h32<F>(qv[rr], q6[rr], mx_scale(zs[rr], lane >> 4));
         }
         auto unpack = [&](int j, int rr) -> h8 {
             if constexpr (SIX)
-                return mx6_slice(e6[SIX ? rr : 0], j, mx_scale(zs[rr], j));
+                return mx6_slice(e6[SIX ? rr : 0], j);
             else if constexpr (MX)
-                return mx4_h8(qv[rr][j], mx_scale(zs[rr], j));
+                return mx4_h8(qv[rr][j], mx_scale(zs[rr], lane >> 4));
             else
                 return nib8_minus_z(qv[rr][j], c1024[rr], c64[rr], nc) * s8[rr];
         };
