@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libglowq.so")
 PROBE_LIB = os.path.join(PKG, "libglowq_probe.so")
 
-SOURCES = ["format.hip", "proj.hip", "decode.hip", "prefill.hip", "w4a8.hip", "moe.hip", "score.hip", "moment.hip", "solve.hip",
+SOURCES = ["format.hip", "proj.hip", "decode.hip", "prefill.hip", "w4a8.hip", "mx8.hip", "moe.hip", "score.hip", "moment.hip", "solve.hip",
            "abi.cpp"]
 PROBE_SOURCES = ["probe.hip"]  # measurement probes, a library of their own
 ARCH = "gfx950"

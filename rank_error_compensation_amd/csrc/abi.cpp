@@ -64,6 +64,7 @@ struct Call {
     bool correct;
     void* const* y;
     bool w4a8;  // 8-bit activations (glowq_group_forward_w4a8)
+    bool mx8;   // MXFP4 weights x MXFP8 activations (glowq_group_forward_mx8)
 };
 
 int validate(const Call& c, void* workspace, size_t ws_bytes) {
@@ -93,6 +94,7 @@ int validate(const Call& c, void* workspace, size_t ws_bytes) {
     if (ceil_div(c.T, 16) * tiles16 > kMaxTiles) return GLOWQ_ERR_UNSUPPORTED;
     if (c.x != nullptr && !aligned(c.x, 16)) return GLOWQ_ERR_ALIGN;
     if (c.w4a8 && (c.d > kW4a8MaxD || c.w[0].format != GLOWQ_FMT_INT4_G128)) return GLOWQ_ERR_UNSUPPORTED;
+    if (c.mx8 && c.w[0].format != GLOWQ_FMT_MXFP4) return GLOWQ_ERR_UNSUPPORTED;
     if (c.correct) {
         if (c.a == nullptr || c.b == nullptr) return GLOWQ_ERR_INVALID_ARG;
         for (int i = 0; i < c.m; ++i)
@@ -106,8 +108,9 @@ int validate(const Call& c, void* workspace, size_t ws_bytes) {
     }
     if (c.T > 0) {
         // W4A8 calls always need their workspace (the activation codes); the others only to correct
-        const size_t need = c.w4a8 ? glowq_w4a8_workspace_bytes(c.T, c.d, c.correct ? c.r : 0)
-                                   : (c.correct ? glowq_workspace_bytes(c.T, c.r, c.n_proj) : 0);
+        const size_t need = c.w4a8  ? glowq_w4a8_workspace_bytes(c.T, c.d, c.correct ? c.r : 0)
+                            : c.mx8 ? glowq_mx8_workspace_bytes(c.T, c.d, c.correct ? c.r : 0)
+                                    : (c.correct ? glowq_workspace_bytes(c.T, c.r, c.n_proj) : 0);
         if (need > 0) {
             if (workspace == nullptr || ws_bytes < need) return GLOWQ_ERR_WORKSPACE;
             if (!aligned(workspace, 256)) return GLOWQ_ERR_ALIGN;
@@ -299,6 +302,7 @@ Call make_group(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qwei
     c.correct = restore != 0 && r > 0;
     c.y = y;
     c.w4a8 = false;
+    c.mx8 = false;
     return c;
 }
 
@@ -319,18 +323,35 @@ void choose_w4a8_shape(const Call& c, int& tt, int& rr, int& ks) {
 
 // W4A8 workspace: codes [T][d] int8 | code sums [T][G] int32 | scales [T] fp32 | for correcting
 // calls the fp16 projection [T][r_pad] and its split-K partials.
+// W4A8 and MXFP8 forms: quantise the activations into the workspace, form the projection from the
+// fp16 activations, then one GEMM launch over the prefill-style tiles.
+// W4A8 workspace: codes [T][d] int8 | code sums [T][G] int32 | scales [T] fp32 | projection;
+// MXFP8 workspace: codes [T][d] (operand order) | block scales [T][d / 32] | projection.
 int run_w4a8(const Call& c, void* workspace, hipStream_t stream) {
     if (c.T == 0) return GLOWQ_OK;
     uint8_t* base = static_cast<uint8_t*>(workspace);
-    int8_t* xq = reinterpret_cast<int8_t*>(base);
-    base += round256((size_t)c.T * c.d);
-    int32_t* xsum = reinterpret_cast<int32_t*>(base);
-    base += round256((size_t)c.T * (c.d / kGroup) * 4u);
-    float* xscale = reinterpret_cast<float*>(base);
-    base += round256((size_t)c.T * 4u);
+    int8_t* xq = nullptr;
+    int32_t* xsum = nullptr;
+    float* xscale = nullptr;
+    uint8_t *x8 = nullptr, *x8s = nullptr;
+    if (c.mx8) {
+        x8 = base;
+        base += round256((size_t)c.T * c.d);
+        x8s = base;
+        base += round256((size_t)c.T * (c.d / 32));
+    } else {
+        xq = reinterpret_cast<int8_t*>(base);
+        base += round256((size_t)c.T * c.d);
+        xsum = reinterpret_cast<int32_t*>(base);
+        base += round256((size_t)c.T * (c.d / kGroup) * 4u);
+        xscale = reinterpret_cast<float*>(base);
+        base += round256((size_t)c.T * 4u);
+    }
     void* R = c.correct ? base : nullptr;
-    if (launch_quant_x(static_cast<const _Float16*>(c.x), (int)c.T, (int)c.d, xq, xsum, xscale, stream) != hipSuccess)
-        return GLOWQ_ERR_HIP;
+    const hipError_t eq = c.mx8 ? launch_quant_mx8(static_cast<const _Float16*>(c.x), (int)c.T, (int)c.d, x8, x8s, stream)
+                                : launch_quant_x(static_cast<const _Float16*>(c.x), (int)c.T, (int)c.d, xq, xsum, xscale,
+                                                 stream);
+    if (eq != hipSuccess) return GLOWQ_ERR_HIP;
     if (c.correct && launch_projection(c, R, stream) != hipSuccess) return GLOWQ_ERR_HIP;
     ForwardArgs f;
     std::memset(&f, 0, sizeof(f));
@@ -347,6 +368,9 @@ int run_w4a8(const Call& c, void* workspace, hipStream_t stream) {
     f.xq = xq;
     f.xsum = xsum;
     f.xscale = xscale;
+    f.x8 = x8;
+    f.x8scale = x8s;
+    f.fmt = c.w[0].format;
     int tt = 1, rr = 1, ks = 1;
     choose_w4a8_shape(c, tt, rr, ks);
     f.tile_tt = tt;
@@ -368,7 +392,7 @@ int run_w4a8(const Call& c, void* workspace, hipStream_t stream) {
     }
     f.m_tiles = (int32_t)ceil_div(c.T, 16 * tt);
     f.n_tiles = (int32_t)(tiles * f.m_tiles);
-    return launch_w4a8(f, stream) == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
+    return (c.mx8 ? launch_mx8(f, stream) : launch_w4a8(f, stream)) == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
 }
 
 }  // namespace
@@ -563,6 +587,24 @@ size_t glowq_w4a8_workspace_bytes(int64_t T, int64_t d, int32_t r) {
     size_t n = round256((size_t)T * d) + round256((size_t)T * (d / kGroup) * 4u) + round256((size_t)T * 4u);
     if (r > 0) n += prefill_r_bytes(T, r, 1) + prefill_part_bytes(T, r, 1);
     return n;
+}
+
+size_t glowq_mx8_workspace_bytes(int64_t T, int64_t d, int32_t r) {
+    if (T <= 0 || d < kGroup || d % kGroup != 0 || d > kMaxD || r < 0 || r > GLOWQ_MAX_RANK) return 0;
+    size_t n = round256((size_t)T * d) + round256((size_t)T * (d / 32));
+    if (r > 0) n += prefill_r_bytes(T, r, 1) + prefill_part_bytes(T, r, 1);
+    return n;
+}
+
+int glowq_group_forward_mx8(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
+                            const void* b_shared, const void* const* a, int32_t r, int32_t restore,
+                            void* workspace, size_t workspace_bytes, void* const* y, hipStream_t stream) {
+    const void* bp[1] = {b_shared};
+    Call c = make_group(x, T, d, m, w, bp, 1, a, r, restore, y);
+    c.mx8 = true;
+    const int v = validate(c, workspace, workspace_bytes);
+    if (v != GLOWQ_OK) return v;
+    return run_w4a8(c, workspace, stream);
 }
 
 int glowq_group_forward_w4a8(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,

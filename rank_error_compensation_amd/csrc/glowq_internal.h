@@ -262,6 +262,8 @@ struct ForwardArgs {
     const int8_t* xq;     // W4A8: token codes [T][d] in the matrix-core operand order
     const int32_t* xsum;  // W4A8: per (token, group) code sums [T][G]
     const float* xscale;  // W4A8: per-token scales [T]
+    const uint8_t* x8;       // MXFP8 activations: E4M3 codes [T][d] in the block-scaled operand order
+    const uint8_t* x8scale;  // MXFP8 activations: E8M0 block scales [T][d / 32]
     const _Float16* b[kMaxModules];  // [r][d] right factors, one per projection
     ModuleArgs mod[kMaxModules];
 };
@@ -327,6 +329,8 @@ hipError_t launch_repack_mx(int fmt, const uint8_t* codes, const uint8_t* scales
 hipError_t launch_proj_prefill(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
+hipError_t launch_quant_mx8(const _Float16* x, int T, int d, uint8_t* xq, uint8_t* xs, hipStream_t stream);
+hipError_t launch_mx8(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_quant_x(const _Float16* x, int T, int d, int8_t* xq, int32_t* xsum, float* xscale,
                           hipStream_t stream);
 hipError_t launch_w4a8(const ForwardArgs& a, hipStream_t stream);

@@ -1,0 +1,338 @@
+// MXFP4 weights against MXFP8 activations on the gfx950 block-scaled matrix cores
+// (v_mfma_scale_f32_16x16x128_f8f6f4): the 8-bit-activation form of the method (GlowQ arXiv page,
+// Tables 14 and 15) with weights and activations both in the microscaling family of Table 13.
+//
+//   x8[t, k], S[t, b] = MXFP8 quantisation of X (OCP MX v1.0): per token and 32-input block b the
+//                       shared exponent floor(log2 max|x|) - 8, each element the nearest E4M3 value
+//                       (ties to even, saturating at 448)
+//   y_i[t, o]        = sum_b 2^(S_w[o, b] + S[t, b] - 254) sum_{k in b} w4[o, k] x8[t, k]
+//                      + R[t] . A_i[o],   R = X B^T from the fp16 X, formed once per call
+// The matrix cores apply both block scales themselves: one 16x16x128 step covers a 128-input group
+// of 16 rows and 16 tokens, four scale groups of 32 products each.
+//
+// Operand pairing of the step (measured with in-bounds probes on the device): lane l of the FP4
+// operand holds row l % 16 and the 32 products of scale group l / 16 (the weight layout's one MX
+// block per lane; its scale is the lane's E8M0 byte); the FP8 operand's lane l holds column (token)
+// l % 16 and 32 bytes, byte p of lane group h pairing with FP4 element n = 16 (h % 2) + p % 16 of
+// scale group g = 2 (p / 16) + h / 2, whose activation scale the lane l % 16 + 16 g supplies.  So the
+// activation codes of a 128-input group are stored in that order: input 32 g + n of the group at
+// byte 32 (2 (g % 2) + n / 16) + 16 (g / 2) + n % 16, and a lane reads its 32 operand bytes at 32 h.
+#include "glowq_internal.h"
+
+namespace glowq {
+
+typedef int32_t i8v __attribute__((ext_vector_type(8)));
+
+// E4M3 code of u (exact fp32 input, |u| < 512): nearest value, ties to the even mantissa, saturating
+// at 448; subnormals below 2^-6 in steps of 2^-9.  Computed with exact operations only.
+__device__ __forceinline__ uint32_t e4m3_code(float u) {
+    const float a = fminf(fabsf(u), 448.0f);
+    uint32_t code;
+    if (a < 0.015625f) {
+        code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0 .. 8; 8 is the smallest normal, code 0x08
+    } else {
+        const int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;  // floor(log2 a)
+        const float mant = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) - ((uint32_t)e << 23));
+        uint32_t q = (uint32_t)__builtin_rintf((mant - 1.0f) * 8.0f);  // 0 .. 8
+        int ee = e;
+        if (q == 8) q = 0, ++ee;
+        code = ((uint32_t)(ee + 7) << 3) | q;
+    }
+    return (u < 0.0f && code != 0) ? (code | 0x80u) : code;
+}
+
+// One workgroup per token; each thread quantises whole 32-input blocks (block i of the row for
+// i = tid, tid + 256, ...): the block's largest magnitude, its scale byte, the codes stored in the
+// operand order above (two 16-byte stores per block).
+constexpr int kMx8QuantThreads = 256;
+
+__global__ __launch_bounds__(kMx8QuantThreads) void quant_mx8_kernel(const _Float16* __restrict__ x, int d,
+                                                                   uint8_t* __restrict__ xq,
+                                                                   uint8_t* __restrict__ xs) {
+    const int t = blockIdx.x;
+    const int nb = d / 32;
+    const _Float16* row = x + (size_t)t * d;
+    for (int b = threadIdx.x; b < nb; b += kMx8QuantThreads) {
+        h8 v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = load_h8(row + 32 * b + 8 * c);
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[c][e]));
+        int X = -127;  // a block of zeros: the smallest scale, zero codes
+        if (amax > 0.f) X = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFFu) - 127 - 8;
+        // 2^-X as an fp32 power of two (X in -32 .. 7 for fp16 inputs)
+        const float inv = __builtin_bit_cast(float, (uint32_t)(127 - (amax > 0.f ? X : 0)) << 23);
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = 4 * i + j;
+                word |= e4m3_code((float)v[n >> 3][n & 7] * inv) << (8 * j);
+            }
+            w[i] = word;
+        }
+        const int G = b >> 2, g = b & 3;
+        uint8_t* base = xq + (size_t)t * d + (size_t)G * kGroup + 16 * (g >> 1);
+        *reinterpret_cast<u4*>(base + 32 * (2 * (g & 1))) = u4{w[0], w[1], w[2], w[3]};      // n = 0 .. 15
+        *reinterpret_cast<u4*>(base + 32 * (2 * (g & 1) + 1)) = u4{w[4], w[5], w[6], w[7]};  // n = 16 .. 31
+        xs[(size_t)t * nb + b] = (uint8_t)(X + 127);
+    }
+}
+
+// GEMM tile: 16 TT tokens x 64 RR rows, four waves side by side in N (wave w owns RR row tiles of
+// 16 rows, all tokens), KS groups of four waves splitting the input groups (added through LDS in
+// wave-group order, deterministic).  Per group: the token codes (BM x 128 bytes) staged in LDS,
+// double-buffered, with each token tile's activation scales; weights (16 bytes per lane: the FP4
+// operand as stored) and their scale words straight from HBM, one group ahead in registers; one
+// block-scaled matrix-core step per (row tile, token tile).  After the K loop r_pad / 32 fp16
+// matrix-core steps add R A_i^T, one rounding to fp16.
+template <int TT, int RR, int KS>
+__global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const ForwardArgs args) {
+    constexpr int BM = 16 * TT;
+    constexpr int LSB = 144;             // LDS row stride in bytes (128 + 16 padding)
+    constexpr int NCH = BM * 8 / 256;    // 16-byte code chunks per thread per group (BM rows x 8)
+    constexpr int NCHP = NCH > 0 ? NCH : 1;
+    constexpr int kTileBytes = KS * 2 * BM * LSB;
+    constexpr int kRedBytes = (KS - 1) * TT * RR * 256 * 16;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kTileBytes > kRedBytes ? kTileBytes : kRedBytes];
+    uint8_t (*xsm)[2][BM * LSB] = reinterpret_cast<uint8_t (*)[2][BM * LSB]>(smem);
+
+    const int mb = blockIdx.x % args.m_tiles, nbl = blockIdx.x / args.m_tiles;
+    const ModuleArgs M = args.mod[module_of(args, nbl)];
+    const int nb = nbl - M.tile_begin;
+    const int m0 = mb * BM;
+    const int tid = threadIdx.x & 255, lane = tid & 63;
+    const int kg = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = args.T, d = args.d, G = args.G;
+    const int rt0 = nb * 4 * RR + wave * RR;
+    const size_t qstride = (size_t)M.n_tiles16 * 1024, szstride = (size_t)M.n_tiles16 * 64;
+    const int sgrp = lane >> 4;  // the lane's scale group in a 128-input group
+
+    const uint8_t* qp[RR];
+    const uint8_t* zp[RR];
+    bool w_ok[RR];
+#pragma unroll
+    for (int rr = 0; rr < RR; ++rr) {
+        const int rt = rt0 + rr;
+        w_ok[rr] = rt < M.n_tiles16;
+        qp[rr] = M.q + (size_t)(w_ok[rr] ? rt : 0) * 1024 + lane * 16;
+        zp[rr] = M.sz + (size_t)(w_ok[rr] ? rt : 0) * 64 + (lane & 15) * 4;
+    }
+    // code staging: BM rows x 8 chunks of 16 bytes per group; thread tid copies chunks tid + 256 c
+    const uint8_t* xsrc[NCHP];
+    bool x_ok[NCHP];
+    int xdst[NCHP];
+#pragma unroll
+    for (int c = 0; c < NCHP; ++c) {
+        const int idx = c * 256 + tid;
+        const int row = idx >> 3, col = (idx & 7) * 16;
+        const int t = m0 + row;
+        x_ok[c] = idx < BM * 8 && t < T;
+        xsrc[c] = args.x8 + (size_t)(x_ok[c] ? t : 0) * d + col;
+        xdst[c] = (idx < BM * 8 ? row : 0) * LSB + col;
+    }
+    // this lane's tokens (one per token tile) and their activation-scale rows
+    int tok[TT];
+    bool t_ok[TT];
+    const uint8_t* srow[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        tok[tt] = m0 + 16 * tt + (lane & 15);
+        t_ok[tt] = tok[tt] < T;
+        srow[tt] = args.x8scale + (size_t)(t_ok[tt] ? tok[tt] : 0) * (d / 32) + sgrp;
+    }
+    const u4 zero4 = {0u, 0u, 0u, 0u};
+    const int n_it = (G + KS - 1) / KS;
+    const bool act0 = kg < G;
+    const bool copier = BM * 8 >= 256 || tid < BM * 8;  // TT = 1: 128 of 256 threads copy
+
+    u4 st[NCHP];
+    u4 qv[RR];
+    uint32_t zw[RR];
+    uint32_t sb[TT];
+#pragma unroll
+    for (int c = 0; c < NCHP; ++c)
+        st[c] = (act0 && x_ok[c]) ? *reinterpret_cast<const u4*>(xsrc[c] + (size_t)kg * kGroup) : zero4;
+#pragma unroll
+    for (int rr = 0; rr < RR; ++rr) {
+        qv[rr] = (act0 && w_ok[rr]) ? *reinterpret_cast<const u4*>(qp[rr] + (size_t)kg * qstride) : zero4;
+        zw[rr] = (act0 && w_ok[rr]) ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)kg * szstride) : 0u;
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) sb[tt] = act0 ? srow[tt][4 * kg] : 0u;
+    if (copier) {
+#pragma unroll
+        for (int c = 0; c < NCHP; ++c)
+            if (c * 256 + tid < BM * 8) *reinterpret_cast<u4*>(&xsm[kg][0][xdst[c]]) = st[c];
+    }
+    __syncthreads();
+
+    f4 acc[TT][RR];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = f4{0.f, 0.f, 0.f, 0.f};
+
+    for (int it = 0; it < n_it; ++it) {
+        const int g = it * KS + kg;
+        const int buf = it & 1;
+        const bool act = g < G, more = g + KS < G;
+        u4 qn[RR];
+        uint32_t zn[RR], sbn[TT];
+        if (more) {
+#pragma unroll
+            for (int c = 0; c < NCHP; ++c)
+                st[c] = x_ok[c] ? *reinterpret_cast<const u4*>(xsrc[c] + (size_t)(g + KS) * kGroup) : zero4;
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) {
+                qn[rr] = w_ok[rr] ? *reinterpret_cast<const u4*>(qp[rr] + (size_t)(g + KS) * qstride) : zero4;
+                zn[rr] = w_ok[rr] ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)(g + KS) * szstride) : 0u;
+            }
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) sbn[tt] = srow[tt][4 * (g + KS)];
+        }
+        if (act) {
+            const uint8_t* xb = &xsm[kg][buf][(lane & 15) * LSB + 32 * sgrp];
+            i8v a[RR];
+            int32_t sa[RR];
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) {
+                a[rr] = i8v{(int32_t)qv[rr][0], (int32_t)qv[rr][1], (int32_t)qv[rr][2], (int32_t)qv[rr][3], 0, 0, 0, 0};
+                sa[rr] = (int32_t)((zw[rr] >> (8 * sgrp)) & 0xFFu);
+            }
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const u4 b0 = *reinterpret_cast<const u4*>(xb + tt * 16 * LSB);
+                const u4 b1 = *reinterpret_cast<const u4*>(xb + tt * 16 * LSB + 16);
+                const i8v b = {(int32_t)b0[0], (int32_t)b0[1], (int32_t)b0[2], (int32_t)b0[3],
+                               (int32_t)b1[0], (int32_t)b1[1], (int32_t)b1[2], (int32_t)b1[3]};
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr)
+                    acc[tt][rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[rr], b, acc[tt][rr], 4, 0, 0, sa[rr],
+                                                                                  0, (int32_t)sb[tt]);
+            }
+        }
+        if (more) {
+            if (copier) {
+#pragma unroll
+                for (int c = 0; c < NCHP; ++c)
+                    if (c * 256 + tid < BM * 8) *reinterpret_cast<u4*>(&xsm[kg][buf ^ 1][xdst[c]]) = st[c];
+            }
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) {
+                qv[rr] = qn[rr];
+                zw[rr] = zn[rr];
+            }
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) sb[tt] = sbn[tt];
+        }
+        __syncthreads();
+    }
+
+    if (KS > 1) {
+        f4* red = reinterpret_cast<f4*>(smem);
+        if (kg > 0) {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) red[(((kg - 1) * TT + tt) * RR + rr) * 256 + tid] = acc[tt][rr];
+        }
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll
+        for (int k = 1; k < KS; ++k)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) acc[tt][rr] += red[(((k - 1) * TT + tt) * RR + rr) * 256 + tid];
+    }
+
+    // the correction on the fp16 projection
+    const int kofs = 8 * (lane >> 4);
+    if (args.r > 0 && M.a != nullptr) {
+        const int r = args.r, rp = args.r_pad;
+        const _Float16* R = reinterpret_cast<const _Float16*>(args.R) + (size_t)M.proj * T * rp;
+        const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int kb = 0; kb < rp / 32; ++kb) {
+            const int col = 32 * kb + kofs;
+            h8 a[RR];
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) {
+                const int row = (rt0 + rr) * 16 + (lane & 15);
+                a[rr] = (row < M.n_out && col < r) ? load_h8(M.a + (size_t)row * r + col) : zero8;
+            }
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const h8 b = (t_ok[tt] && col < rp) ? load_h8(R + (size_t)tok[tt] * rp + col) : zero8;
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = mfma16(a[rr], b, acc[tt][rr]);
+            }
+        }
+    }
+
+    const bool vec = (M.n_out & 3) == 0;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        if (!t_ok[tt]) continue;
+        _Float16* yrow = M.y + (size_t)tok[tt] * M.n_out;
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr) {
+            if (rt0 + rr >= M.n_tiles16) continue;
+            const int row0 = (rt0 + rr) * 16 + 4 * (lane >> 4);
+            const f4 v = acc[tt][rr];
+            if (vec && row0 + 3 < M.n_out) {
+                const h2 lo = {(_Float16)v[0], (_Float16)v[1]}, hi = {(_Float16)v[2], (_Float16)v[3]};
+                *reinterpret_cast<u2*>(yrow + row0) = u2{as_u32(lo), as_u32(hi)};
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (row0 + i < M.n_out) yrow[row0 + i] = (_Float16)v[i];
+            }
+        }
+    }
+}
+
+hipError_t launch_quant_mx8(const _Float16* x, int T, int d, uint8_t* xq, uint8_t* xs, hipStream_t stream) {
+    if (d % kGroup != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_mx8_kernel, dim3((unsigned)T), dim3(kMx8QuantThreads), 0, stream, x, d, xq, xs);
+    return hipGetLastError();
+}
+
+template <int TT, int RR>
+static hipError_t launch_mx8_rr(const ForwardArgs& a, hipStream_t stream) {
+    const dim3 grid(a.n_tiles);
+    switch (a.tile_ks) {
+        case 4:
+            if constexpr (TT * RR >= 8) return hipErrorInvalidValue;  // not built: register budget
+            else hipLaunchKernelGGL((mx8_kernel<TT, RR, 4>), grid, dim3(1024), 0, stream, a);
+            break;
+        case 2: hipLaunchKernelGGL((mx8_kernel<TT, RR, 2>), grid, dim3(512), 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((mx8_kernel<TT, RR, 1>), grid, dim3(256), 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int TT>
+static hipError_t launch_mx8_tt(const ForwardArgs& a, hipStream_t stream) {
+    if (a.tile_rr == 2) return launch_mx8_rr<TT, 2>(a, stream);
+    if (a.tile_rr == 1) return launch_mx8_rr<TT, 1>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mx8(const ForwardArgs& a, hipStream_t stream) {
+    switch (a.tile_tt) {
+        case 1: return launch_mx8_tt<1>(a, stream);
+        case 2: return launch_mx8_tt<2>(a, stream);
+        case 4: return launch_mx8_tt<4>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace glowq

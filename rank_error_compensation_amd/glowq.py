@@ -79,7 +79,10 @@ EXPORTS = {
     "glowq_group_forward_static": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(QWeightC), _vp,
                                                   ctypes.POINTER(_vp), _i32, _i32, ctypes.POINTER(_vp), _vp]),
     "glowq_w4a8_workspace_bytes": (_sz, [_i64, _i64, _i32]),
+    "glowq_mx8_workspace_bytes": (_sz, [_i64, _i64, _i32]),
     "glowq_group_forward_w4a8": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(QWeightC), _vp,
+                                                ctypes.POINTER(_vp), _i32, _i32, _vp, _sz, ctypes.POINTER(_vp), _vp]),
+    "glowq_group_forward_mx8": (ctypes.c_int, [_vp, _i64, _i64, _i32, ctypes.POINTER(QWeightC), _vp,
                                                 ctypes.POINTER(_vp), _i32, _i32, _vp, _sz, ctypes.POINTER(_vp), _vp]),
     "glowq_moe_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "glowq_moe_forward": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, ctypes.POINTER(MoeModuleC), _vp, _i32, _i32,
@@ -416,6 +419,31 @@ def group_forward_w4a8(x: torch.Tensor, weights: Sequence[QWeight], b: Optional[
     check(lib().glowq_group_forward_w4a8(_ptr(x), x.shape[0], x.shape[1], m, wc, _ptr(b), ac, r,
                                          int(bool(restore)), _ptr(workspace), ws_n, yc, _stream(stream)),
           "glowq_group_forward_w4a8")
+    return y
+
+
+def mx8_workspace_bytes(T: int, d: int, r: int) -> int:
+    return int(lib().glowq_mx8_workspace_bytes(T, d, r))
+
+
+def group_forward_mx8(x: torch.Tensor, weights: Sequence[QWeight], b: Optional[torch.Tensor],
+                      a: Sequence[torch.Tensor], r: int, restore: bool = True,
+                      workspace: Optional[torch.Tensor] = None, y: Optional[List[torch.Tensor]] = None,
+                      stream=None) -> List[torch.Tensor]:
+    """glowq_group_forward_mx8: MXFP4 weights against MXFP8 activations on the block-scaled matrix
+    cores, the correction on the fp16 activations."""
+    m = len(weights)
+    y = _outs(x, weights, y)
+    if workspace is None and x.shape[0] > 0:
+        n = mx8_workspace_bytes(x.shape[0], x.shape[1], r if restore else 0)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    wc = _arr(QWeightC, [w.c() for w in weights])
+    ac = _arr(_vp, [t.data_ptr() for t in a]) if a else None
+    yc = _arr(_vp, [t.data_ptr() for t in y])
+    ws_n = 0 if workspace is None else workspace.numel()
+    check(lib().glowq_group_forward_mx8(_ptr(x), x.shape[0], x.shape[1], m, wc, _ptr(b), ac, r,
+                                        int(bool(restore)), _ptr(workspace), ws_n, yc, _stream(stream)),
+          "glowq_group_forward_mx8")
     return y
 
 

@@ -359,3 +359,24 @@ def test_forward_format_validation():
     assert L.glowq_dequant(ctypes.byref(_w(fmt=9)), FAKE, 0, None) == g.ERR_INVALID_ARG
     need = L.glowq_ner_workspace_bytes(32)
     assert L.glowq_ner_sums(FAKE, ctypes.byref(_w(fmt=g.FMT_MXFP4)), FAKE, need, FAKE, None) == g.ERR_UNSUPPORTED
+
+
+def test_mx8_validation():
+    """glowq_group_forward_mx8: MXFP4 modules only; the workspace holds the codes, the block scales
+    and the projection; checks before any HIP call."""
+    L = g.lib()
+    r256 = lambda n: (n + 255) // 256 * 256
+    assert L.glowq_mx8_workspace_bytes(4, 256, 0) == r256(4 * 256) + r256(4 * 8)
+    assert L.glowq_mx8_workspace_bytes(4, 256, 8) > L.glowq_mx8_workspace_bytes(4, 256, 0)
+    assert L.glowq_mx8_workspace_bytes(0, 256, 8) == 0 and L.glowq_mx8_workspace_bytes(4, 200, 8) == 0
+    a1 = (ctypes.c_void_p * 1)(FAKE)
+    y1 = (ctypes.c_void_p * 1)(FAKE)
+    for fmt, code in ((g.FMT_INT4_G128, g.ERR_UNSUPPORTED), (g.FMT_MXFP6_E2M3, g.ERR_UNSUPPORTED),
+                      (g.FMT_MXFP6_E3M2, g.ERR_UNSUPPORTED)):
+        w1 = (g.QWeightC * 1)(_w(fmt=fmt))
+        assert L.glowq_group_forward_mx8(FAKE, 4, 256, 1, w1, FAKE, a1, 8, 1, FAKE, 1 << 24, y1, None) == code
+    w1 = (g.QWeightC * 1)(_w(fmt=g.FMT_MXFP4))
+    need = L.glowq_mx8_workspace_bytes(4, 256, 8)
+    assert L.glowq_group_forward_mx8(FAKE, 4, 256, 1, w1, FAKE, a1, 8, 1, FAKE, need - 1, y1, None) == g.ERR_WORKSPACE
+    assert L.glowq_group_forward_mx8(FAKE, 4, 256, 1, w1, FAKE, a1, 8, 1, FAKE + 16, need, y1, None) == g.ERR_ALIGN
+    assert L.glowq_group_forward_mx8(FAKE, 4, 256, 1, w1, None, a1, 8, 1, FAKE, need, y1, None) == g.ERR_INVALID_ARG
