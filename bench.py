@@ -583,6 +583,23 @@ def extra_mx(g, reps=20, copies=20):
             mx_weight_bytes(fmt, u.n_outs, 4096)
         res["qkv_T1"] = {"us_median": round(t * 1e6, 3), "alg_bytes": nb, "TB_per_s": round(nb / t / 1e12, 4),
                          "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4)}
+        if fmt == "mxfp4":
+            ws8 = torch.empty(g.mx8_workspace_bytes(1, 4096, u.r), dtype=torch.uint8, device="cuda")
+            for i in range(copies):
+                g.group_forward_mx8(u.x, sets[i], u.b, u.a, u.r, True, workspace=ws8, y=ys)
+            torch.cuda.synchronize()
+            evs = []
+            for k in range(reps * copies):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.group_forward_mx8(u.x, sets[k % copies], u.b, u.a, u.r, True, workspace=ws8, y=ys)
+                e1.record(stream)
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            t8 = statistics.median([e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs])
+            res["qkv_T1_x_mxfp8_activations"] = {"us_median": round(t8 * 1e6, 3), "TB_per_s": round(nb / t8 / 1e12, 4),
+                                                 "frac_hbm_peak": round(nb / t8 / 1e12 / 8.0, 4)}
+            del ws8
         del sets, base, ws, ys, u
         u = W.llama2_gateup_unit(2048, device="cuda", fmt=fmt)
         w = [g.QWeight.from_workload(q, device="cuda") for q in u.weights]
@@ -604,11 +621,33 @@ def extra_mx(g, reps=20, copies=20):
         fl = unit_flops(2048, 4096, u.n_outs, u.r, True)
         res["gateup_T2048"] = {"us_median": round(t * 1e6, 2), "TFLOP_per_s": round(fl / t / 1e12, 1),
                                "frac_mfma_f16_peak": round(fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+        if fmt == "mxfp4":
+            # the same weights against MXFP8 activations on the block-scaled matrix cores
+            ws8 = torch.empty(g.mx8_workspace_bytes(2048, 4096, u.r), dtype=torch.uint8, device="cuda")
+            fn8 = graphed(lambda: g.group_forward_mx8(u.x, w, u.b, u.a, u.r, True, workspace=ws8, y=ys)).replay
+            for _ in range(3):
+                fn8()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn8()
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+            t8 = statistics.median(ts)
+            res["gateup_T2048_x_mxfp8_activations"] = {
+                "us_median": round(t8 * 1e6, 2), "TFLOP_per_s": round(fl / t8 / 1e12, 1),
+                "frac_mfma_fp8_peak": round(fl / t8 / 1e12 / 5000.0, 4),
+                "how": "activations quantised to MXFP8 in the call, v_mfma_scale_f32_16x16x128_f8f6f4"}
+            del ws8
         out[fmt] = res
         del w, ws, ys, u
         torch.cuda.empty_cache()
     out["workload"] = ("llama2-7b QKV T=1 (rotating copies) and gate/up T=2048, r=64, per weight format; "
-                       "MX = OCP microscaling, 32-input blocks, E8M0 scales")
+                       "MX = OCP microscaling, 32-input blocks, E8M0 scales; x_mxfp8_activations = the MXFP4 "
+                       "weights against per-call MXFP8 activations (fp8 peak 5 PFLOP/s)")
     return out
 
 
