@@ -310,6 +310,10 @@ Call make_group(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qwei
 // that leaves fewer than 128 tiles; wave groups splitting the input groups as in the prefill
 // kernel, so that about four wavefronts share every SIMD on small grids.
 void choose_w4a8_shape(const Call& c, int& tt, int& rr, int& ks) {
+    if (c.mx8 && prefill_tiles(c, 8, 4) >= kWideMinTiles) {  // MXFP8: the wide tile on large grids
+        tt = 8, rr = 4, ks = 1;
+        return;
+    }
     tt = c.T <= 16 ? 1 : (c.T <= 32 ? 2 : 4);
     rr = 2;
     int64_t n = prefill_tiles(c, tt, rr);
@@ -321,12 +325,16 @@ void choose_w4a8_shape(const Call& c, int& tt, int& rr, int& ks) {
     if (tt == 4 && rr == 2 && ks == 4) ks = 2;  // 1024 threads would cap this tile at 128 VGPRs (spills)
 }
 
+// MXFP8 activation scales: one 512-byte record per (128-token block, input group).
+size_t mx8_scale_bytes(int64_t T, int64_t d) { return (size_t)ceil_div(T, 128) * (size_t)(d / kGroup) * 512u; }
+
 // W4A8 workspace: codes [T][d] int8 | code sums [T][G] int32 | scales [T] fp32 | for correcting
 // calls the fp16 projection [T][r_pad] and its split-K partials.
 // W4A8 and MXFP8 forms: quantise the activations into the workspace, form the projection from the
 // fp16 activations, then one GEMM launch over the prefill-style tiles.
 // W4A8 workspace: codes [T][d] int8 | code sums [T][G] int32 | scales [T] fp32 | projection;
-// MXFP8 workspace: codes [T][d] (operand order) | block scales [T][d / 32] | projection.
+// MXFP8 workspace: codes [T][d] (operand order) | block scales (512-byte records per 128 tokens and
+// group) | projection.
 int run_w4a8(const Call& c, void* workspace, hipStream_t stream) {
     if (c.T == 0) return GLOWQ_OK;
     uint8_t* base = static_cast<uint8_t*>(workspace);
@@ -338,7 +346,7 @@ int run_w4a8(const Call& c, void* workspace, hipStream_t stream) {
         x8 = base;
         base += round256((size_t)c.T * c.d);
         x8s = base;
-        base += round256((size_t)c.T * (c.d / 32));
+        base += mx8_scale_bytes(c.T, c.d);
     } else {
         xq = reinterpret_cast<int8_t*>(base);
         base += round256((size_t)c.T * c.d);
@@ -591,7 +599,7 @@ size_t glowq_w4a8_workspace_bytes(int64_t T, int64_t d, int32_t r) {
 
 size_t glowq_mx8_workspace_bytes(int64_t T, int64_t d, int32_t r) {
     if (T <= 0 || d < kGroup || d % kGroup != 0 || d > kMaxD || r < 0 || r > GLOWQ_MAX_RANK) return 0;
-    size_t n = round256((size_t)T * d) + round256((size_t)T * (d / 32));
+    size_t n = round256((size_t)T * d) + mx8_scale_bytes(T, d);
     if (r > 0) n += prefill_r_bytes(T, r, 1) + prefill_part_bytes(T, r, 1);
     return n;
 }

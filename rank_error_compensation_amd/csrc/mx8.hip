@@ -17,6 +17,13 @@
 // scale group g = 2 (p / 16) + h / 2, whose activation scale the lane l % 16 + 16 g supplies.  So the
 // activation codes of a 128-input group are stored in that order: input 32 g + n of the group at
 // byte 32 (2 (g % 2) + n / 16) + 16 (g / 2) + n % 16, and a lane reads its 32 operand bytes at 32 h.
+// The activation scales are stored so that a lane finds all the scales it needs for one group in one
+// 8-byte word: per 128-token block tb and group G a 512-byte record at (tb G_count + G) 512, the scale
+// of token t and block g of the group at byte 8 (16 g + t % 16) + (t % 128) / 16 -- lane l of the
+// step (column l % 16, scale group l / 16) reads the word at 8 l, byte j holding the scale of its
+// token in the block's 16-token tile j.
+#include <type_traits>
+
 #include "glowq_internal.h"
 
 namespace glowq {
@@ -45,6 +52,12 @@ __device__ __forceinline__ uint32_t e4m3_code(float u) {
 // i = tid, tid + 256, ...): the block's largest magnitude, its scale byte, the codes stored in the
 // operand order above (two 16-byte stores per block).
 constexpr int kMx8QuantThreads = 256;
+
+// Byte offset of the 512-byte scale record of token t's 128-token block and group G, plus the
+// token's position (t % 128) / 16 in each 8-byte word.
+__device__ __forceinline__ size_t mx8_scale_offset(int t, int G, int n_groups) {
+    return ((size_t)(t >> 7) * n_groups + G) * 512 + ((t & 127) >> 4);
+}
 
 __global__ __launch_bounds__(kMx8QuantThreads) void quant_mx8_kernel(const _Float16* __restrict__ x, int d,
                                                                    uint8_t* __restrict__ xq,
@@ -80,7 +93,7 @@ __global__ __launch_bounds__(kMx8QuantThreads) void quant_mx8_kernel(const _Floa
         uint8_t* base = xq + (size_t)t * d + (size_t)G * kGroup + 16 * (g >> 1);
         *reinterpret_cast<u4*>(base + 32 * (2 * (g & 1))) = u4{w[0], w[1], w[2], w[3]};      // n = 0 .. 15
         *reinterpret_cast<u4*>(base + 32 * (2 * (g & 1) + 1)) = u4{w[4], w[5], w[6], w[7]};  // n = 16 .. 31
-        xs[(size_t)t * nb + b] = (uint8_t)(X + 127);
+        xs[mx8_scale_offset(t, G, d / kGroup) + 8 * (16 * g + (t & 15))] = (uint8_t)(X + 127);
     }
 }
 
@@ -137,7 +150,8 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
         xsrc[c] = args.x8 + (size_t)(x_ok[c] ? t : 0) * d + col;
         xdst[c] = (idx < BM * 8 ? row : 0) * LSB + col;
     }
-    // this lane's tokens (one per token tile) and their activation-scale rows
+    // this lane's tokens (one per token tile) and their activation scales (tile m0 / 16 + tt of the
+    // scale records; a tile past T reads scales never written, feeding only outputs never stored)
     int tok[TT];
     bool t_ok[TT];
     const uint8_t* srow[TT];
@@ -145,7 +159,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
     for (int tt = 0; tt < TT; ++tt) {
         tok[tt] = m0 + 16 * tt + (lane & 15);
         t_ok[tt] = tok[tt] < T;
-        srow[tt] = args.x8scale + (size_t)(t_ok[tt] ? tok[tt] : 0) * (d / 32) + sgrp;
+        srow[tt] = args.x8scale + mx8_scale_offset(m0 + 16 * tt, 0, G) + 8 * lane;
     }
     const u4 zero4 = {0u, 0u, 0u, 0u};
     const int n_it = (G + KS - 1) / KS;
@@ -165,7 +179,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
         zw[rr] = (act0 && w_ok[rr]) ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)kg * szstride) : 0u;
     }
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) sb[tt] = act0 ? srow[tt][4 * kg] : 0u;
+    for (int tt = 0; tt < TT; ++tt) sb[tt] = act0 ? srow[tt][(size_t)kg * 512] : 0u;
     if (copier) {
 #pragma unroll
         for (int c = 0; c < NCHP; ++c)
@@ -195,7 +209,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
                 zn[rr] = w_ok[rr] ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)(g + KS) * szstride) : 0u;
             }
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) sbn[tt] = srow[tt][4 * (g + KS)];
+            for (int tt = 0; tt < TT; ++tt) sbn[tt] = srow[tt][(size_t)(g + KS) * 512];
         }
         if (act) {
             const uint8_t* xb = &xsm[kg][buf][(lane & 15) * LSB + 32 * sgrp];
@@ -298,6 +312,188 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
     }
 }
 
+// Wide tile for large grids: 128 tokens (one scale block) x 256 rows, four waves each owning 4 row
+// tiles and all 8 token tiles, so that every FP8 operand read from LDS feeds 4 block-scaled steps and
+// every weight operand 8 (32 steps per wave and group, against 8 in the tile above).  The codes of a
+// group (128 rows x 128 bytes) go HBM/L2 -> registers -> LDS (144-byte rows: the 16-byte operand
+// reads of 16 consecutive rows fall in distinct bank groups), two groups ahead in registers and
+// double-buffered in LDS; the weights (16 code bytes and the scale word per row tile) and the
+// lane's 8-byte activation-scale word come straight from HBM into registers, two groups ahead in a
+// ring of three.  The group loop is unrolled six times so that every ring slot is named statically.
+// Tokens past T read token T - 1 and row tiles past the module its last tile; neither is stored.
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+__global__ __launch_bounds__(256, 1) void mx8_wide_kernel(const ForwardArgs args) {
+    constexpr int TT = 8, RR = 4, BM = 128, LSB = 144;
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * LSB];
+
+    int mb, nbl;
+    if ((args.m_tiles & 7) == 0) {
+        // XCD x (workgroups b with b % 8 == x) owns the token blocks [x m / 8, (x + 1) m / 8) for
+        // every row block: its slice of the codes stays in its L2 while the weights stream through
+        const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3, mp = args.m_tiles >> 3;
+        nbl = local / mp;
+        mb = xcd * mp + (local - nbl * mp);
+    } else {
+        mb = (int)blockIdx.x % args.m_tiles;
+        nbl = (int)blockIdx.x / args.m_tiles;
+    }
+    const ModuleArgs M = args.mod[module_of(args, nbl)];
+    const int nb = nbl - M.tile_begin;
+    const int m0 = mb * BM;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = args.T, d = args.d, G = args.G;
+    const int NT = M.n_tiles16;
+    const int rt0 = nb * 4 * RR + wave * RR;
+    const int sgrp = lane >> 4;
+
+    // weights: this wave's row tiles (clamped to the module's last tile), the lane's 16 bytes and
+    // its row's scale word; activation scales: the lane's word of this token block's records
+    const uint8_t* qb[RR];
+    const uint8_t* zb[RR];
+#pragma unroll
+    for (int rr = 0; rr < RR; ++rr) {
+        const int rt = min(rt0 + rr, NT - 1);
+        qb[rr] = M.q + (size_t)rt * 1024 + lane * 16;
+        zb[rr] = M.sz + (size_t)rt * 64 + (lane & 15) * 4;
+    }
+    const size_t qstride = (size_t)NT * 1024, zstride = (size_t)NT * 64;
+    const uint8_t* sbb = args.x8scale + (size_t)mb * G * 512 + lane * 8;
+    // codes: thread tid copies the 16-byte chunks c = 0 .. 3 of index 256 c + tid, i.e. row
+    // (256 c + tid) / 8, column 16 ((256 c + tid) % 8)
+    const uint8_t* xsrc[4];
+    int xdst[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int idx = 256 * c + tid, row = idx >> 3, col = (idx & 7) * 16;
+        xsrc[c] = args.x8 + (size_t)min(m0 + row, T - 1) * d + col;
+        xdst[c] = row * LSB + col;
+    }
+
+    u4 xr[2][4];                           // codes of the next two groups
+    u4 qv[3][RR];                          // weight codes, ring of three groups
+    uint32_t zw[3][RR];                    // weight scale words
+    u2 sw[3];                              // activation-scale words
+    auto load_x = [&](int g, u4 (&r)[4]) {
+        const size_t o = (size_t)min(g, G - 1) * kGroup;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) r[c] = *reinterpret_cast<const u4*>(xsrc[c] + o);
+    };
+    auto load_w = [&](int g, u4 (&q)[RR], uint32_t (&z)[RR], u2& sv) {
+        const int gg = min(g, G - 1);
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr) {
+            q[rr] = *reinterpret_cast<const u4*>(qb[rr] + (size_t)gg * qstride);
+            z[rr] = *reinterpret_cast<const uint32_t*>(zb[rr] + (size_t)gg * zstride);
+        }
+        sv = *reinterpret_cast<const u2*>(sbb + (size_t)gg * 512);
+    };
+    auto store_x = [&](const u4 (&r)[4], int buf) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) *reinterpret_cast<u4*>(&xs[buf][xdst[c]]) = r[c];
+    };
+
+    f4 acc[TT][RR];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = f4{0.f, 0.f, 0.f, 0.f};
+
+    load_x(0, xr[0]);
+    load_w(0, qv[0], zw[0], sw[0]);
+    load_x(1, xr[1]);
+    load_w(1, qv[1], zw[1], sw[1]);
+    store_x(xr[0], 0);
+    __syncthreads();
+
+    // group g: LDS buffer and code registers B = g % 2, weight slot W = g % 3.  On entry the codes
+    // of g are in LDS buffer B (published by the previous barrier), those of g + 1 in registers
+    // B ^ 1, the weights of g and g + 1 in slots W and W + 1.
+    auto step = [&](int g, auto Bc, auto Wc) {
+        constexpr int B = decltype(Bc)::value, W = decltype(Wc)::value;
+        load_x(g + 2, xr[B]);  // xr[B] (the codes of g) went to LDS before the last barrier
+        load_w(g + 2, qv[(W + 2) % 3], zw[(W + 2) % 3], sw[(W + 2) % 3]);
+        i8v a[RR];
+        int32_t sa[RR];
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr) {
+            a[rr] = i8v{(int32_t)qv[W][rr][0], (int32_t)qv[W][rr][1], (int32_t)qv[W][rr][2], (int32_t)qv[W][rr][3],
+                        0, 0, 0, 0};
+            sa[rr] = (int32_t)((zw[W][rr] >> (8 * sgrp)) & 0xFFu);
+        }
+        const uint8_t* xb = &xs[B][(lane & 15) * LSB + 32 * sgrp];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const u4 b0 = *reinterpret_cast<const u4*>(xb + tt * 16 * LSB);
+            const u4 b1 = *reinterpret_cast<const u4*>(xb + tt * 16 * LSB + 16);
+            const i8v bv = {(int32_t)b0[0], (int32_t)b0[1], (int32_t)b0[2], (int32_t)b0[3],
+                            (int32_t)b1[0], (int32_t)b1[1], (int32_t)b1[2], (int32_t)b1[3]};
+            const int32_t sb = (int32_t)((sw[W][tt >> 2] >> (8 * (tt & 3))) & 0xFFu);
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr)
+                acc[tt][rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[rr], bv, acc[tt][rr], 4, 0, 0, sa[rr], 0, sb);
+        }
+        store_x(xr[B ^ 1], B ^ 1);  // the codes of g + 1; buffer B ^ 1 was last read before the last barrier
+        __syncthreads();
+    };
+    for (int g0 = 0; g0 < G; g0 += 6) {
+        step(g0, ic<0>{}, ic<0>{});
+        if (g0 + 1 < G) step(g0 + 1, ic<1>{}, ic<1>{});
+        if (g0 + 2 < G) step(g0 + 2, ic<0>{}, ic<2>{});
+        if (g0 + 3 < G) step(g0 + 3, ic<1>{}, ic<0>{});
+        if (g0 + 4 < G) step(g0 + 4, ic<0>{}, ic<1>{});
+        if (g0 + 5 < G) step(g0 + 5, ic<1>{}, ic<2>{});
+    }
+
+    // the correction on the fp16 projection: r_pad / 32 fp16 steps
+    if (args.r > 0 && M.a != nullptr) {
+        const int r = args.r, rp = args.r_pad;
+        const _Float16* R = reinterpret_cast<const _Float16*>(args.R) + (size_t)M.proj * T * rp;
+        const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+        const int kofs = 8 * (lane >> 4);
+        for (int kb = 0; kb < rp / 32; ++kb) {
+            const int col = 32 * kb + kofs;
+            h8 av[RR];
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) {
+                const int row = (rt0 + rr) * 16 + (lane & 15);
+                av[rr] = (row < M.n_out && col < r) ? load_h8(M.a + (size_t)row * r + col) : zero8;
+            }
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const int t = m0 + 16 * tt + (lane & 15);
+                const h8 bv = t < T ? load_h8(R + (size_t)t * rp + col) : zero8;
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = mfma16(av[rr], bv, acc[tt][rr]);
+            }
+        }
+    }
+
+    const bool vec = (M.n_out & 3) == 0;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const int t = m0 + 16 * tt + (lane & 15);
+        if (t >= T) continue;
+        _Float16* yrow = M.y + (size_t)t * M.n_out;
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr) {
+            if (rt0 + rr >= NT) continue;
+            const int row0 = (rt0 + rr) * 16 + 4 * (lane >> 4);
+            const f4 v = acc[tt][rr];
+            if (vec && row0 + 3 < M.n_out) {
+                const h2 lo = {(_Float16)v[0], (_Float16)v[1]}, hi = {(_Float16)v[2], (_Float16)v[3]};
+                *reinterpret_cast<u2*>(yrow + row0) = u2{as_u32(lo), as_u32(hi)};
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (row0 + i < M.n_out) yrow[row0 + i] = (_Float16)v[i];
+            }
+        }
+    }
+}
+
 hipError_t launch_quant_mx8(const _Float16* x, int T, int d, uint8_t* xq, uint8_t* xs, hipStream_t stream) {
     if (d % kGroup != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(quant_mx8_kernel, dim3((unsigned)T), dim3(kMx8QuantThreads), 0, stream, x, d, xq, xs);
@@ -327,6 +523,11 @@ static hipError_t launch_mx8_tt(const ForwardArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_mx8(const ForwardArgs& a, hipStream_t stream) {
+    if (a.tile_rr == 4) {  // the wide tile
+        if (a.tile_tt != 8 || a.tile_ks != 1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(mx8_wide_kernel, dim3(a.n_tiles), dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     switch (a.tile_tt) {
         case 1: return launch_mx8_tt<1>(a, stream);
         case 2: return launch_mx8_tt<2>(a, stream);

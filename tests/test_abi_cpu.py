@@ -366,7 +366,9 @@ def test_mx8_validation():
     and the projection; checks before any HIP call."""
     L = g.lib()
     r256 = lambda n: (n + 255) // 256 * 256
-    assert L.glowq_mx8_workspace_bytes(4, 256, 0) == r256(4 * 256) + r256(4 * 8)
+    # codes [T][d] | one 512-byte scale record per (128-token block, 128-input group)
+    assert L.glowq_mx8_workspace_bytes(4, 256, 0) == r256(4 * 256) + 1 * 2 * 512
+    assert L.glowq_mx8_workspace_bytes(129, 384, 0) == r256(129 * 384) + 2 * 3 * 512
     assert L.glowq_mx8_workspace_bytes(4, 256, 8) > L.glowq_mx8_workspace_bytes(4, 256, 0)
     assert L.glowq_mx8_workspace_bytes(0, 256, 8) == 0 and L.glowq_mx8_workspace_bytes(4, 200, 8) == 0
     a1 = (ctypes.c_void_p * 1)(FAKE)

@@ -61,13 +61,23 @@ def oracle(unit, restore=True, r=None, rows=None):
     return G.group_forward_mx8(x, w_hats, unit.b if r > 0 else None, unit.a, restore and r > 0)
 
 
+def natural_scales(raw: np.ndarray, T: int, d: int) -> np.ndarray:
+    """Undo the documented scale records: per 128-token block and group a 512-byte record, the scale
+    of token t and block g of the group at byte 8 (16 g + t % 16) + (t % 128) / 16."""
+    n_groups = d // 128
+    t = np.arange(T)[:, None]
+    b = np.arange(d // 32)[None, :]
+    pos = ((t // 128) * n_groups + b // 4) * 512 + 8 * (16 * (b % 4) + t % 16) + (t % 128) // 16
+    return raw[pos]
+
+
 def check_codes(unit, ws, rows=None):
     T, d = unit.x.shape
     x = unit.x if rows is None else unit.x[torch.as_tensor(rows, device=unit.x.device)]
     codes_ref, scales_ref = G.quantize_x_mxfp8(x)
     raw = ws.cpu().numpy()
     codes = natural_from_operand_order(raw[: T * d].reshape(T, d))
-    scales = raw[r256(T * d): r256(T * d) + T * (d // 32)].reshape(T, d // 32)
+    scales = natural_scales(raw[r256(T * d):], T, d)
     if rows is not None:
         codes, scales = codes[rows], scales[rows]
     assert np.array_equal(codes, codes_ref), np.argwhere(codes != codes_ref)[:5]
@@ -79,7 +89,10 @@ def check_codes(unit, ws, rows=None):
 SHAPES = [(1, 256, [256, 256, 256], 16), (3, 384, [40, 24], 8), (16, 1024, [520, 17], 64),
           (17, 512, [96, 64, 40], 32), (33, 640, [100], 24), (64, 1024, [1024, 512, 512], 64),
           (65, 256, [48, 32], 16), (130, 384, [300, 200], 40), (300, 512, [2048, 2048], 128),
-          (8, 2048, [64], 256)]
+          (8, 2048, [64], 256),
+          # wide tiles (128 tokens x 256 rows, at least 256 of them): ragged tokens and rows, a
+          # group count that is not a multiple of the six-group unroll, r = 0 .. 256
+          (300, 640, [11000, 10000, 1000], 64), (129, 256, [16400, 16392], 256), (520, 1408, [6000, 7000], 24)]
 
 
 @pytest.mark.parametrize("T,d,rows,r", SHAPES)
