@@ -314,17 +314,18 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
 
 // Wide tile for large grids: 128 tokens (one scale block) x 256 rows, four waves each owning 4 row
 // tiles and all 8 token tiles, so that every FP8 operand read from LDS feeds 4 block-scaled steps and
-// every weight operand 8 (32 steps per wave and group, against 8 in the tile above).  The codes of a
-// group (128 rows x 128 bytes) go HBM/L2 -> registers -> LDS (144-byte rows: the 16-byte operand
-// reads of 16 consecutive rows fall in distinct bank groups), two groups ahead in registers and
-// double-buffered in LDS; the weights (16 code bytes and the scale word per row tile) and the
-// lane's 8-byte activation-scale word come straight from HBM into registers, two groups ahead in a
-// ring of three.  The group loop is unrolled six times so that every ring slot is named statically.
-// Tokens past T read token T - 1 and row tiles past the module its last tile; neither is stored.
+// every weight operand 8 (32 steps per wave and group, against 8 in the tile above), two workgroups
+// per CU so that two waves share every SIMD (one wave's waits hide behind the other's steps; the
+// registers are budgeted for it: 128 accumulators, one group of loads ahead, 32-bit offsets).  The
+// codes of a group (128 rows x 128 bytes) go HBM/L2 -> registers -> LDS (144-byte rows: the 16-byte
+// operand reads of 16 consecutive rows fall in distinct bank groups), one group ahead, double-
+// buffered in LDS; the weights (16 code bytes and the scale word per row tile) and the lane's
+// 8-byte activation-scale word come straight from HBM into registers, one group ahead.  Tokens past
+// T read token T - 1 and row tiles past the module its last tile; neither is stored.
 template <int I>
 using ic = std::integral_constant<int, I>;
 
-__global__ __launch_bounds__(256, 1) void mx8_wide_kernel(const ForwardArgs args) {
+__global__ __launch_bounds__(256, 2) void mx8_wide_kernel(const ForwardArgs args) {
     constexpr int TT = 8, RR = 4, BM = 128, LSB = 144;
     __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * LSB];
 
@@ -349,50 +350,44 @@ __global__ __launch_bounds__(256, 1) void mx8_wide_kernel(const ForwardArgs args
     const int rt0 = nb * 4 * RR + wave * RR;
     const int sgrp = lane >> 4;
 
-    // weights: this wave's row tiles (clamped to the module's last tile), the lane's 16 bytes and
-    // its row's scale word; activation scales: the lane's word of this token block's records
-    const uint8_t* qb[RR];
-    const uint8_t* zb[RR];
+    // uniform bases plus 32-bit lane offsets (the launcher keeps T d below 2^30): weights of this
+    // wave's row tiles (clamped to the module's last tile), the activation-scale records of this
+    // token block, and the codes, thread tid copying the 16-byte chunks c = 0 .. 3 of index
+    // 256 c + tid, i.e. row (256 c + tid) / 8, column 16 ((256 c + tid) % 8)
+    int rtc[RR];
 #pragma unroll
-    for (int rr = 0; rr < RR; ++rr) {
-        const int rt = min(rt0 + rr, NT - 1);
-        qb[rr] = M.q + (size_t)rt * 1024 + lane * 16;
-        zb[rr] = M.sz + (size_t)rt * 64 + (lane & 15) * 4;
-    }
-    const size_t qstride = (size_t)NT * 1024, zstride = (size_t)NT * 64;
-    const uint8_t* sbb = args.x8scale + (size_t)mb * G * 512 + lane * 8;
-    // codes: thread tid copies the 16-byte chunks c = 0 .. 3 of index 256 c + tid, i.e. row
-    // (256 c + tid) / 8, column 16 ((256 c + tid) % 8)
-    const uint8_t* xsrc[4];
+    for (int rr = 0; rr < RR; ++rr) rtc[rr] = min(rt0 + rr, NT - 1);
+    const uint32_t qlane = lane * 16, zlane = (lane & 15) * 4, slane = lane * 8;
+    uint32_t xoff[4];
     int xdst[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int idx = 256 * c + tid, row = idx >> 3, col = (idx & 7) * 16;
-        xsrc[c] = args.x8 + (size_t)min(m0 + row, T - 1) * d + col;
+        xoff[c] = (uint32_t)(min(m0 + row, T - 1) * d + col);
         xdst[c] = row * LSB + col;
     }
 
-    u4 xr[2][4];                           // codes of the next two groups
-    u4 qv[3][RR];                          // weight codes, ring of three groups
-    uint32_t zw[3][RR];                    // weight scale words
-    u2 sw[3];                              // activation-scale words
-    auto load_x = [&](int g, u4 (&r)[4]) {
-        const size_t o = (size_t)min(g, G - 1) * kGroup;
+    u4 xr[4];         // codes of the next group
+    u4 qv[2][RR];     // weight codes of this and the next group
+    uint32_t zw[2][RR];
+    u2 sw[2];         // activation-scale words
+    auto load_x = [&](int g) {
+        const uint8_t* base = args.x8 + (size_t)min(g, G - 1) * kGroup;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) r[c] = *reinterpret_cast<const u4*>(xsrc[c] + o);
+        for (int c = 0; c < 4; ++c) xr[c] = *reinterpret_cast<const u4*>(base + xoff[c]);
     };
     auto load_w = [&](int g, u4 (&q)[RR], uint32_t (&z)[RR], u2& sv) {
-        const int gg = min(g, G - 1);
+        const size_t gg = (size_t)min(g, G - 1);
 #pragma unroll
         for (int rr = 0; rr < RR; ++rr) {
-            q[rr] = *reinterpret_cast<const u4*>(qb[rr] + (size_t)gg * qstride);
-            z[rr] = *reinterpret_cast<const uint32_t*>(zb[rr] + (size_t)gg * zstride);
+            q[rr] = *reinterpret_cast<const u4*>(M.q + (gg * NT + rtc[rr]) * 1024 + qlane);
+            z[rr] = *reinterpret_cast<const uint32_t*>(M.sz + (gg * NT + rtc[rr]) * 64 + zlane);
         }
-        sv = *reinterpret_cast<const u2*>(sbb + (size_t)gg * 512);
+        sv = *reinterpret_cast<const u2*>(args.x8scale + ((size_t)mb * G + gg) * 512 + slane);
     };
-    auto store_x = [&](const u4 (&r)[4], int buf) {
+    auto store_x = [&](int buf) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) *reinterpret_cast<u4*>(&xs[buf][xdst[c]]) = r[c];
+        for (int c = 0; c < 4; ++c) *reinterpret_cast<u4*>(&xs[buf][xdst[c]]) = xr[c];
     };
 
     f4 acc[TT][RR];
@@ -401,51 +396,56 @@ __global__ __launch_bounds__(256, 1) void mx8_wide_kernel(const ForwardArgs args
 #pragma unroll
         for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = f4{0.f, 0.f, 0.f, 0.f};
 
-    load_x(0, xr[0]);
+    load_x(0);
     load_w(0, qv[0], zw[0], sw[0]);
-    load_x(1, xr[1]);
-    load_w(1, qv[1], zw[1], sw[1]);
-    store_x(xr[0], 0);
+    store_x(0);
     __syncthreads();
 
-    // group g: LDS buffer and code registers B = g % 2, weight slot W = g % 3.  On entry the codes
-    // of g are in LDS buffer B (published by the previous barrier), those of g + 1 in registers
-    // B ^ 1, the weights of g and g + 1 in slots W and W + 1.
-    auto step = [&](int g, auto Bc, auto Wc) {
-        constexpr int B = decltype(Bc)::value, W = decltype(Wc)::value;
-        load_x(g + 2, xr[B]);  // xr[B] (the codes of g) went to LDS before the last barrier
-        load_w(g + 2, qv[(W + 2) % 3], zw[(W + 2) % 3], sw[(W + 2) % 3]);
+    // group g, S = g % 2: its codes in LDS buffer S (published by the previous barrier), its weights
+    // in slot S.  The loads of g + 1 are issued first; the FP8 operand of token tile tt + 1 is read
+    // while the four steps of tile tt issue.
+    auto step = [&](int g, auto Sc) {
+        constexpr int S = decltype(Sc)::value;
+        load_x(g + 1);  // xr (the codes of g) went to LDS before the last barrier
+        load_w(g + 1, qv[S ^ 1], zw[S ^ 1], sw[S ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* xb = &xs[S][(lane & 15) * LSB + 32 * sgrp];
+        auto bread = [&](int tt) {
+            const u4 b0 = *reinterpret_cast<const u4*>(xb + tt * 16 * LSB);
+            const u4 b1 = *reinterpret_cast<const u4*>(xb + tt * 16 * LSB + 16);
+            return i8v{(int32_t)b0[0], (int32_t)b0[1], (int32_t)b0[2], (int32_t)b0[3],
+                       (int32_t)b1[0], (int32_t)b1[1], (int32_t)b1[2], (int32_t)b1[3]};
+        };
+        i8v bq[2];
+        bq[0] = bread(0);
         i8v a[RR];
         int32_t sa[RR];
 #pragma unroll
         for (int rr = 0; rr < RR; ++rr) {
-            a[rr] = i8v{(int32_t)qv[W][rr][0], (int32_t)qv[W][rr][1], (int32_t)qv[W][rr][2], (int32_t)qv[W][rr][3],
+            a[rr] = i8v{(int32_t)qv[S][rr][0], (int32_t)qv[S][rr][1], (int32_t)qv[S][rr][2], (int32_t)qv[S][rr][3],
                         0, 0, 0, 0};
-            sa[rr] = (int32_t)((zw[W][rr] >> (8 * sgrp)) & 0xFFu);
+            sa[rr] = (int32_t)((zw[S][rr] >> (8 * sgrp)) & 0xFFu);
         }
-        const uint8_t* xb = &xs[B][(lane & 15) * LSB + 32 * sgrp];
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
-            const u4 b0 = *reinterpret_cast<const u4*>(xb + tt * 16 * LSB);
-            const u4 b1 = *reinterpret_cast<const u4*>(xb + tt * 16 * LSB + 16);
-            const i8v bv = {(int32_t)b0[0], (int32_t)b0[1], (int32_t)b0[2], (int32_t)b0[3],
-                            (int32_t)b1[0], (int32_t)b1[1], (int32_t)b1[2], (int32_t)b1[3]};
-            const int32_t sb = (int32_t)((sw[W][tt >> 2] >> (8 * (tt & 3))) & 0xFFu);
+            if (tt + 1 < TT) bq[(tt + 1) & 1] = bread(tt + 1);
+            const int32_t sb = (int32_t)((sw[S][tt >> 2] >> (8 * (tt & 3))) & 0xFFu);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr)
-                acc[tt][rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[rr], bv, acc[tt][rr], 4, 0, 0, sa[rr], 0, sb);
+                acc[tt][rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[rr], bq[tt & 1], acc[tt][rr], 4, 0, 0,
+                                                                              sa[rr], 0, sb);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        store_x(xr[B ^ 1], B ^ 1);  // the codes of g + 1; buffer B ^ 1 was last read before the last barrier
+        store_x(S ^ 1);  // the codes of g + 1; buffer S ^ 1 was last read before the last barrier
         __syncthreads();
     };
-    for (int g0 = 0; g0 < G; g0 += 6) {
-        step(g0, ic<0>{}, ic<0>{});
-        if (g0 + 1 < G) step(g0 + 1, ic<1>{}, ic<1>{});
-        if (g0 + 2 < G) step(g0 + 2, ic<0>{}, ic<2>{});
-        if (g0 + 3 < G) step(g0 + 3, ic<1>{}, ic<0>{});
-        if (g0 + 4 < G) step(g0 + 4, ic<0>{}, ic<1>{});
-        if (g0 + 5 < G) step(g0 + 5, ic<1>{}, ic<2>{});
+    int g0 = 0;
+    for (; g0 + 2 <= G; g0 += 2) {
+        step(g0, ic<0>{});
+        step(g0 + 1, ic<1>{});
     }
+    if (g0 < G) step(g0, ic<0>{});
 
     // the correction on the fp16 projection: r_pad / 32 fp16 steps
     if (args.r > 0 && M.a != nullptr) {
