@@ -310,8 +310,8 @@ Call make_group(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qwei
 // that leaves fewer than 128 tiles; wave groups splitting the input groups as in the prefill
 // kernel, so that about four wavefronts share every SIMD on small grids.
 void choose_w4a8_shape(const Call& c, int& tt, int& rr, int& ks) {
-    if (c.mx8 && prefill_tiles(c, 8, 4) >= kWideMinTiles) {  // MXFP8: the wide tile on large grids
-        tt = 8, rr = 4, ks = 1;
+    if (c.mx8 && prefill_tiles(c, 8, 8) >= kWideMinTiles) {  // MXFP8: the 128 x 512 tile on large grids
+        tt = 8, rr = 8, ks = 1;
         return;
     }
     tt = c.T <= 16 ? 1 : (c.T <= 32 ? 2 : 4);

@@ -31,26 +31,21 @@ namespace glowq {
 typedef int32_t i8v __attribute__((ext_vector_type(8)));
 
 // E4M3 code of u (exact fp32 input, |u| < 512): nearest value, ties to the even mantissa, saturating
-// at 448; subnormals below 2^-6 in steps of 2^-9.  Computed with exact operations only.
+// at 448; subnormals below 2^-6 in steps of 2^-9.  Branch-free and exact: in the normal range the
+// code is the fp32 bit pattern rounded to 3 mantissa bits (round half to even on the 20 dropped
+// bits; a mantissa carry moves into the exponent as it should) with the exponent rebased from 127
+// to 7; below 2^-6 it is the nearest multiple of 2^-9 (8 of them being the smallest normal, 0x08).
 __device__ __forceinline__ uint32_t e4m3_code(float u) {
     const float a = fminf(fabsf(u), 448.0f);
-    uint32_t code;
-    if (a < 0.015625f) {
-        code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0 .. 8; 8 is the smallest normal, code 0x08
-    } else {
-        const int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;  // floor(log2 a)
-        const float mant = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) - ((uint32_t)e << 23));
-        uint32_t q = (uint32_t)__builtin_rintf((mant - 1.0f) * 8.0f);  // 0 .. 8
-        int ee = e;
-        if (q == 8) q = 0, ++ee;
-        code = ((uint32_t)(ee + 7) << 3) | q;
-    }
+    const uint32_t b = __builtin_bit_cast(uint32_t, a);
+    const uint32_t normal = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+    const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
+    const uint32_t code = a < 0.015625f ? sub : normal;
     return (u < 0.0f && code != 0) ? (code | 0x80u) : code;
 }
 
-// One workgroup per token; each thread quantises whole 32-input blocks (block i of the row for
-// i = tid, tid + 256, ...): the block's largest magnitude, its scale byte, the codes stored in the
-// operand order above (two 16-byte stores per block).
+// One thread per (token, 32-input block) over a flat grid: the block's largest magnitude, its
+// scale byte, the codes stored in the operand order above (two 16-byte stores per block).
 constexpr int kMx8QuantThreads = 256;
 
 // Byte offset of the 512-byte scale record of token t's 128-token block and group G, plus the
@@ -59,13 +54,14 @@ __device__ __forceinline__ size_t mx8_scale_offset(int t, int G, int n_groups) {
     return ((size_t)(t >> 7) * n_groups + G) * 512 + ((t & 127) >> 4);
 }
 
-__global__ __launch_bounds__(kMx8QuantThreads) void quant_mx8_kernel(const _Float16* __restrict__ x, int d,
+__global__ __launch_bounds__(kMx8QuantThreads) void quant_mx8_kernel(const _Float16* __restrict__ x, int T, int d,
                                                                    uint8_t* __restrict__ xq,
                                                                    uint8_t* __restrict__ xs) {
-    const int t = blockIdx.x;
     const int nb = d / 32;
-    const _Float16* row = x + (size_t)t * d;
-    for (int b = threadIdx.x; b < nb; b += kMx8QuantThreads) {
+    const int64_t i = (int64_t)blockIdx.x * kMx8QuantThreads + threadIdx.x;
+    if (i < (int64_t)T * nb) {
+        const int t = (int)(i / nb), b = (int)(i - (int64_t)t * nb);
+        const _Float16* row = x + (size_t)t * d;
         h8 v[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[c] = load_h8(row + 32 * b + 8 * c);
@@ -312,30 +308,47 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
     }
 }
 
-// Wide tile for large grids: 128 tokens (one scale block) x 256 rows, four waves each owning 4 row
-// tiles and all 8 token tiles, so that every FP8 operand read from LDS feeds 4 block-scaled steps and
-// every weight operand 8 (32 steps per wave and group, against 8 in the tile above), two workgroups
-// per CU so that two waves share every SIMD (one wave's waits hide behind the other's steps; the
-// registers are budgeted for it: 128 accumulators, one group of loads ahead, 32-bit offsets).  The
-// codes of a group (128 rows x 128 bytes) go HBM/L2 -> registers -> LDS (144-byte rows: the 16-byte
-// operand reads of 16 consecutive rows fall in distinct bank groups), one group ahead, double-
-// buffered in LDS; the weights (16 code bytes and the scale word per row tile) and the lane's
-// 8-byte activation-scale word come straight from HBM into registers, one group ahead.  Tokens past
-// T read token T - 1 and row tiles past the module its last tile; neither is stored.
+// Wide tile for large grids: 128 tokens (one scale block) x 512 rows, eight waves (two per SIMD)
+// each owning 4 row tiles and all 8 token tiles, so that every FP8 operand read from LDS feeds 4
+// block-scaled steps and every weight operand 8 (32 steps per wave and group).  Nothing in flight
+// sits in registers: per group the codes (128 rows x 128 bytes, read by every wave), each wave's
+// weight blocks (4 x 1 KB, the FP4 operands as stored) and their scale words, and the token
+// block's activation-scale record are copied HBM/L2 -> LDS by the load unit (global_load_lds) into
+// a ring of three stages, two groups ahead, so that the loop carries no register loads (whose
+// waits the compiler would place conservatively at the loop head) and every wait is the explicit
+// one before each group's barrier.  In a stage, code row r keeps its 16-byte chunk c at position
+// c ^ f(r), f(r) = (r % 8) ^ ((r / 8) % 2), so that the operand reads of 16 consecutive rows fall
+// in distinct bank groups; a wave's scale words sit as [row][row tile], so that a lane reads its
+// four with one 16-byte read.  Tokens past T read token T - 1 and row tiles past the module its
+// last tile; neither is stored.
 template <int I>
 using ic = std::integral_constant<int, I>;
+typedef __attribute__((address_space(3))) void lds_void8;
 
-__global__ __launch_bounds__(256, 2) void mx8_wide_kernel(const ForwardArgs args) {
-    constexpr int TT = 8, RR = 4, BM = 128, LSB = 144;
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * LSB];
+constexpr int kMx8WideWaves = 8;
+constexpr int kMx8CodeBytes = 128 * 128;                          // codes of one group
+constexpr int kMx8WBytes = kMx8WideWaves * 4 * 1024;              // weight blocks
+constexpr int kMx8ZBytes = kMx8WideWaves * 256;                   // weight scale words
+constexpr int kMx8SBytes = kMx8WideWaves * 256;                   // activation scales (two copies per half)
+constexpr int kMx8StageBytes = kMx8CodeBytes + kMx8WBytes + kMx8ZBytes + kMx8SBytes;
+
+__global__ __launch_bounds__(512, 1) void mx8_wide_kernel(const ForwardArgs args) {
+    constexpr int TT = 8, RR = 4, BM = 128, NW = kMx8WideWaves;
+    constexpr int W_AT = kMx8CodeBytes, Z_AT = W_AT + kMx8WBytes, S_AT = Z_AT + kMx8ZBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t st0[kMx8StageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[kMx8StageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[kMx8StageBytes];
 
     int mb, nbl;
-    if ((args.m_tiles & 7) == 0) {
-        // XCD x (workgroups b with b % 8 == x) owns the token blocks [x m / 8, (x + 1) m / 8) for
-        // every row block: its slice of the codes stays in its L2 while the weights stream through
-        const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3, mp = args.m_tiles >> 3;
-        nbl = local / mp;
-        mb = xcd * mp + (local - nbl * mp);
+    if ((args.m_tiles & 3) == 0) {
+        // XCD x = 4 q + p (workgroups b with b % 8 == x) owns token blocks [p m / 4, (p + 1) m / 4)
+        // and the row blocks of parity q: four token blocks share every weight block in its L2
+        const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3, mp = args.m_tiles >> 2;
+        const int p = xcd & 3, q = xcd >> 2;
+        const int nl = local / mp;
+        nbl = 2 * nl + q;
+        mb = p * mp + (local - nl * mp);
+        if (nbl >= args.n_tiles / args.m_tiles) return;
     } else {
         mb = (int)blockIdx.x % args.m_tiles;
         nbl = (int)blockIdx.x / args.m_tiles;
@@ -347,47 +360,46 @@ __global__ __launch_bounds__(256, 2) void mx8_wide_kernel(const ForwardArgs args
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = args.T, d = args.d, G = args.G;
     const int NT = M.n_tiles16;
-    const int rt0 = nb * 4 * RR + wave * RR;
+    const int rt0 = nb * NW * RR + wave * RR;
     const int sgrp = lane >> 4;
 
-    // uniform bases plus 32-bit lane offsets (the launcher keeps T d below 2^30): weights of this
-    // wave's row tiles (clamped to the module's last tile), the activation-scale records of this
-    // token block, and the codes, thread tid copying the 16-byte chunks c = 0 .. 3 of index
-    // 256 c + tid, i.e. row (256 c + tid) / 8, column 16 ((256 c + tid) % 8)
     int rtc[RR];
 #pragma unroll
     for (int rr = 0; rr < RR; ++rr) rtc[rr] = min(rt0 + rr, NT - 1);
-    const uint32_t qlane = lane * 16, zlane = (lane & 15) * 4, slane = lane * 8;
-    uint32_t xoff[4];
-    int xdst[4];
+    // code copy: instruction i of wave w fills code rows 16 w + 8 i .. + 7 (1 KB); lane l lands at
+    // row 16 w + 8 i + l / 8, position l % 8, holding the row's chunk (l % 8) ^ f(row)
+    uint32_t xoff[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int idx = 256 * c + tid, row = idx >> 3, col = (idx & 7) * 16;
-        xoff[c] = (uint32_t)(min(m0 + row, T - 1) * d + col);
-        xdst[c] = row * LSB + col;
+    for (int i = 0; i < 2; ++i) {
+        const int row = 16 * wave + 8 * i + (lane >> 3);
+        const int f = (row & 7) ^ ((row >> 3) & 1);
+        xoff[i] = (uint32_t)(min(m0 + row, T - 1) * d + 16 * ((lane & 7) ^ f));
     }
+    // scale-word copy: lane l fetches the word of row l / 4 of row tile l % 4
+    const uint32_t zsrc = (uint32_t)(min(rt0 + (lane & 3), NT - 1) * 64 + (lane >> 2) * 4);
+    const int fr = (lane & 7) ^ ((lane >> 3) & 1);  // f of this lane's operand rows (16 tt + lane % 16)
+    const int rofs0 = (lane & 15) * 128 + 16 * ((2 * sgrp) ^ fr);
+    const int rofs1 = (lane & 15) * 128 + 16 * ((2 * sgrp + 1) ^ fr);
 
-    u4 xr[4];         // codes of the next group
-    u4 qv[2][RR];     // weight codes of this and the next group
-    uint32_t zw[2][RR];
-    u2 sw[2];         // activation-scale words
-    auto load_x = [&](int g) {
-        const uint8_t* base = args.x8 + (size_t)min(g, G - 1) * kGroup;
+    const uint32_t qlane = lane * 16, slane = (wave & 1) * 256 + lane * 4;
+    auto copy = [&](int g, uint8_t* stg) {
+        const int gg = min(g, G - 1);
+        const uint8_t* xb = args.x8 + (size_t)gg * kGroup;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) xr[c] = *reinterpret_cast<const u4*>(base + xoff[c]);
-    };
-    auto load_w = [&](int g, u4 (&q)[RR], uint32_t (&z)[RR], u2& sv) {
-        const size_t gg = (size_t)min(g, G - 1);
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(xb + xoff[i]), (lds_void8*)(stg + (16 * wave + 8 * i) * 128),
+                                             16, 0, 0);
+        const uint8_t* qb = M.q + ((size_t)gg * NT + rtc[0]) * 1024;
 #pragma unroll
-        for (int rr = 0; rr < RR; ++rr) {
-            q[rr] = *reinterpret_cast<const u4*>(M.q + (gg * NT + rtc[rr]) * 1024 + qlane);
-            z[rr] = *reinterpret_cast<const uint32_t*>(M.sz + (gg * NT + rtc[rr]) * 64 + zlane);
-        }
-        sv = *reinterpret_cast<const u2*>(args.x8scale + ((size_t)mb * G + gg) * 512 + slane);
-    };
-    auto store_x = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) *reinterpret_cast<u4*>(&xs[buf][xdst[c]]) = xr[c];
+        for (int rr = 0; rr < RR; ++rr)
+            __builtin_amdgcn_global_load_lds((const void*)(qb + (uint32_t)((rtc[rr] - rtc[0]) * 1024) + qlane),
+                                             (lds_void8*)(stg + W_AT + wave * 4096 + rr * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(M.sz + (size_t)gg * NT * 64 + zsrc),
+                                         (lds_void8*)(stg + Z_AT + wave * 256), 4, 0, 0);
+        // the activation-scale record (512 bytes): wave w copies half w % 2 (every wave issues the
+        // same copies)
+        __builtin_amdgcn_global_load_lds((const void*)(args.x8scale + ((size_t)mb * G + gg) * 512 + slane),
+                                         (lds_void8*)(stg + S_AT + wave * 256), 4, 0, 0);
     };
 
     f4 acc[TT][RR];
@@ -396,40 +408,44 @@ __global__ __launch_bounds__(256, 2) void mx8_wide_kernel(const ForwardArgs args
 #pragma unroll
         for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = f4{0.f, 0.f, 0.f, 0.f};
 
-    load_x(0);
-    load_w(0, qv[0], zw[0], sw[0]);
-    store_x(0);
-    __syncthreads();
+    // every group issues the same 8 copies per wave, so that at the end of group g the copies of
+    // g + 1 have landed once at most 8 copies (those of g + 2) are in flight
+    copy(0, st0);
+    copy(1, st1);
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    __builtin_amdgcn_s_barrier();
 
-    // group g, S = g % 2: its codes in LDS buffer S (published by the previous barrier), its weights
-    // in slot S.  The loads of g + 1 are issued first; the FP8 operand of token tile tt + 1 is read
-    // while the four steps of tile tt issue.
+    // group g, S = g % 3: its data in stage S (published by the previous barrier).  The copies of
+    // g + 2 go to stage S + 2, which every wave finished reading in group g - 1 (its operands fed
+    // steps issued before that group's barrier).
     auto step = [&](int g, auto Sc) {
         constexpr int S = decltype(Sc)::value;
-        load_x(g + 1);  // xr (the codes of g) went to LDS before the last barrier
-        load_w(g + 1, qv[S ^ 1], zw[S ^ 1], sw[S ^ 1]);
+        uint8_t* cur = S == 0 ? st0 : (S == 1 ? st1 : st2);
+        uint8_t* nx2 = S == 0 ? st2 : (S == 1 ? st0 : st1);
+        copy(g + 2, nx2);
         __builtin_amdgcn_sched_barrier(0);
-        const uint8_t* xb = &xs[S][(lane & 15) * LSB + 32 * sgrp];
         auto bread = [&](int tt) {
-            const u4 b0 = *reinterpret_cast<const u4*>(xb + tt * 16 * LSB);
-            const u4 b1 = *reinterpret_cast<const u4*>(xb + tt * 16 * LSB + 16);
+            const u4 b0 = *reinterpret_cast<const u4*>(cur + tt * 16 * 128 + rofs0);
+            const u4 b1 = *reinterpret_cast<const u4*>(cur + tt * 16 * 128 + rofs1);
             return i8v{(int32_t)b0[0], (int32_t)b0[1], (int32_t)b0[2], (int32_t)b0[3],
                        (int32_t)b1[0], (int32_t)b1[1], (int32_t)b1[2], (int32_t)b1[3]};
         };
-        i8v bq[2];
-        bq[0] = bread(0);
+        const u4 zq = *reinterpret_cast<const u4*>(cur + Z_AT + wave * 256 + (lane & 15) * 16);
+        const u2 sw = *reinterpret_cast<const u2*>(cur + S_AT + (lane >> 5) * 256 + (lane & 31) * 8);
         i8v a[RR];
         int32_t sa[RR];
 #pragma unroll
         for (int rr = 0; rr < RR; ++rr) {
-            a[rr] = i8v{(int32_t)qv[S][rr][0], (int32_t)qv[S][rr][1], (int32_t)qv[S][rr][2], (int32_t)qv[S][rr][3],
-                        0, 0, 0, 0};
-            sa[rr] = (int32_t)((zw[S][rr] >> (8 * sgrp)) & 0xFFu);
+            const u4 q = *reinterpret_cast<const u4*>(cur + W_AT + wave * 4096 + rr * 1024 + lane * 16);
+            a[rr] = i8v{(int32_t)q[0], (int32_t)q[1], (int32_t)q[2], (int32_t)q[3], 0, 0, 0, 0};
+            sa[rr] = (int32_t)((zq[rr] >> (8 * sgrp)) & 0xFFu);
         }
+        i8v bq[2];
+        bq[0] = bread(0);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
             if (tt + 1 < TT) bq[(tt + 1) & 1] = bread(tt + 1);
-            const int32_t sb = (int32_t)((sw[S][tt >> 2] >> (8 * (tt & 3))) & 0xFFu);
+            const int32_t sb = (int32_t)((sw[tt >> 2] >> (8 * (tt & 3))) & 0xFFu);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr)
@@ -437,15 +453,18 @@ __global__ __launch_bounds__(256, 2) void mx8_wide_kernel(const ForwardArgs args
                                                                               sa[rr], 0, sb);
             __builtin_amdgcn_sched_barrier(0);
         }
-        store_x(S ^ 1);  // the codes of g + 1; buffer S ^ 1 was last read before the last barrier
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): the copies of g + 1 have landed
+        __builtin_amdgcn_s_barrier();
     };
     int g0 = 0;
-    for (; g0 + 2 <= G; g0 += 2) {
+    for (; g0 + 3 <= G; g0 += 3) {
         step(g0, ic<0>{});
         step(g0 + 1, ic<1>{});
+        step(g0 + 2, ic<2>{});
     }
     if (g0 < G) step(g0, ic<0>{});
+    if (g0 + 1 < G) step(g0 + 1, ic<1>{});
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no copy may land in LDS after the workgroup ends
 
     // the correction on the fp16 projection: r_pad / 32 fp16 steps
     if (args.r > 0 && M.a != nullptr) {
@@ -496,7 +515,8 @@ __global__ __launch_bounds__(256, 2) void mx8_wide_kernel(const ForwardArgs args
 
 hipError_t launch_quant_mx8(const _Float16* x, int T, int d, uint8_t* xq, uint8_t* xs, hipStream_t stream) {
     if (d % kGroup != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(quant_mx8_kernel, dim3((unsigned)T), dim3(kMx8QuantThreads), 0, stream, x, d, xq, xs);
+    const int64_t blocks = ((int64_t)T * (d / 32) + kMx8QuantThreads - 1) / kMx8QuantThreads;
+    hipLaunchKernelGGL(quant_mx8_kernel, dim3((unsigned)blocks), dim3(kMx8QuantThreads), 0, stream, x, T, d, xq, xs);
     return hipGetLastError();
 }
 
@@ -523,9 +543,14 @@ static hipError_t launch_mx8_tt(const ForwardArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_mx8(const ForwardArgs& a, hipStream_t stream) {
-    if (a.tile_rr == 4) {  // the wide tile
+    if (a.tile_rr == 8) {  // the wide tile: 128 tokens x 512 rows
         if (a.tile_tt != 8 || a.tile_ks != 1) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(mx8_wide_kernel, dim3(a.n_tiles), dim3(256), 0, stream, a);
+        // token-block quarters x row-block parities over the eight XCDs: 8 x (m / 4) x ceil(n / 2)
+        // workgroups, those past the last row block return at once
+        const int n = a.n_tiles / a.m_tiles;
+        const unsigned grid = (a.m_tiles % 4 == 0) ? 8u * (unsigned)(a.m_tiles / 4) * (unsigned)((n + 1) / 2)
+                                                   : (unsigned)a.n_tiles;
+        hipLaunchKernelGGL(mx8_wide_kernel, dim3(grid), dim3(64 * kMx8WideWaves), 0, stream, a);
         return hipGetLastError();
     }
     switch (a.tile_tt) {

@@ -90,9 +90,12 @@ SHAPES = [(1, 256, [256, 256, 256], 16), (3, 384, [40, 24], 8), (16, 1024, [520,
           (17, 512, [96, 64, 40], 32), (33, 640, [100], 24), (64, 1024, [1024, 512, 512], 64),
           (65, 256, [48, 32], 16), (130, 384, [300, 200], 40), (300, 512, [2048, 2048], 128),
           (8, 2048, [64], 256),
-          # wide tiles (128 tokens x 256 rows, at least 256 of them): ragged tokens and rows, a
-          # group count that is not a multiple of the six-group unroll, r = 0 .. 256
-          (300, 640, [11000, 10000, 1000], 64), (129, 256, [16400, 16392], 256), (520, 1408, [6000, 7000], 24)]
+          # wide tiles (128 tokens x 512 rows, at least 256 of them): ragged tokens and rows, group
+          # counts 2, 5, 6, 11 against the three-stage ring (tails of 2, 2, 0 and 2 groups)
+          (260, 640, [22000, 21000, 1000], 64), (129, 256, [32784, 32760], 256),
+          (200, 768, [33000, 33000], 32), (520, 1408, [13000, 13600], 24),
+          # token blocks a multiple of 4 (the XCD quarter mapping), an odd number of row blocks
+          (500, 256, [16400, 16000], 16)]
 
 
 @pytest.mark.parametrize("T,d,rows,r", SHAPES)
