@@ -583,7 +583,7 @@ def extra_mx(g, reps=20, copies=20):
             mx_weight_bytes(fmt, u.n_outs, 4096)
         res["qkv_T1"] = {"us_median": round(t * 1e6, 3), "alg_bytes": nb, "TB_per_s": round(nb / t / 1e12, 4),
                          "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4)}
-        if fmt == "mxfp4":
+        if fmt in ("mxfp4", "mxfp6_e2m3"):
             ws8 = torch.empty(g.mx8_workspace_bytes(1, 4096, u.r), dtype=torch.uint8, device="cuda")
             for i in range(copies):
                 g.group_forward_mx8(u.x, sets[i], u.b, u.a, u.r, True, workspace=ws8, y=ys)
@@ -621,7 +621,7 @@ def extra_mx(g, reps=20, copies=20):
         fl = unit_flops(2048, 4096, u.n_outs, u.r, True)
         res["gateup_T2048"] = {"us_median": round(t * 1e6, 2), "TFLOP_per_s": round(fl / t / 1e12, 1),
                                "frac_mfma_f16_peak": round(fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
-        if fmt == "mxfp4":
+        if fmt in ("mxfp4", "mxfp6_e2m3"):
             # the same weights against MXFP8 activations on the block-scaled matrix cores
             ws8 = torch.empty(g.mx8_workspace_bytes(2048, 4096, u.r), dtype=torch.uint8, device="cuda")
             fn8 = graphed(lambda: g.group_forward_mx8(u.x, w, u.b, u.a, u.r, True, workspace=ws8, y=ys)).replay
@@ -646,7 +646,7 @@ def extra_mx(g, reps=20, copies=20):
         del w, ws, ys, u
         torch.cuda.empty_cache()
     out["workload"] = ("llama2-7b QKV T=1 (rotating copies) and gate/up T=2048, r=64, per weight format; "
-                       "MX = OCP microscaling, 32-input blocks, E8M0 scales; x_mxfp8_activations = the MXFP4 "
+                       "MX = OCP microscaling, 32-input blocks, E8M0 scales; x_mxfp8_activations = the same MX "
                        "weights against per-call MXFP8 activations (fp8 peak 5 PFLOP/s)")
     return out
 

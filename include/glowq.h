@@ -243,19 +243,19 @@ int glowq_group_forward_w4a8(const void* x, int64_t T, int64_t d, int32_t m, con
                              const void* b_shared, const void* const* a, int32_t r, int32_t restore,
                              void* workspace, size_t workspace_bytes, void* const* y, hipStream_t stream);
 
-/* ---------------------------------------------------------------- MXFP4 x MXFP8
+/* ---------------------------------------------------------------- MX weights x MXFP8
  * The 8-bit-activation form (GlowQ arXiv page, Tables 14-15) with the microscaling datatypes of
- * Table 13 on both operands: MXFP4 weights (glowq_repack_mx, GLOWQ_FMT_MXFP4) against activations
- * quantised per call to MXFP8 (OCP MX v1.0: per token and 32-input block an E8M0 scale
+ * Table 13 on both operands: MXFP4 or MXFP6 (E2M3 or E3M2) weights (glowq_repack_mx) against
+ * activations quantised per call to MXFP8 (OCP MX v1.0: per token and 32-input block an E8M0 scale
  * 2^(floor(log2 max|x|) - 8) and E4M3 elements, nearest value with ties to the even mantissa,
  * saturating at 448), multiplied on the gfx950 block-scaled matrix cores with both block scales
  * applied in hardware; the correction R A_i^T uses the fp16 activations (R = X B^T formed once):
  *   y_i = dequant(Xq) W_hat_i^T + [restore and r > 0] (X B^T) A_i^T.
- * Arguments, shapes and alignment as glowq_group_forward; every module must be MXFP4
- * (GLOWQ_ERR_UNSUPPORTED otherwise).  The workspace (256-byte aligned, not shared with concurrent
- * calls, contents need no initialisation) holds the activation codes and scales and, when
- * correcting, the projection: glowq_mx8_workspace_bytes(T, d, r) bytes (r = 0 when not
- * correcting; 0 for an invalid shape).  Asynchronous; allocates nothing. */
+ * Arguments, shapes and alignment as glowq_group_forward; every module must carry the same MX
+ * format (GLOWQ_ERR_UNSUPPORTED for INT4-g128 or mixed formats).  The workspace (256-byte aligned,
+ * not shared with concurrent calls, contents need no initialisation) holds the activation codes and
+ * scales and, when correcting, the projection: glowq_mx8_workspace_bytes(T, d, r) bytes (r = 0 when
+ * not correcting; 0 for an invalid shape).  Asynchronous; allocates nothing. */
 size_t glowq_mx8_workspace_bytes(int64_t T, int64_t d, int32_t r);
 int glowq_group_forward_mx8(const void* x, int64_t T, int64_t d, int32_t m, const glowq_qweight* w,
                             const void* b_shared, const void* const* a, int32_t r, int32_t restore,

@@ -94,7 +94,7 @@ int validate(const Call& c, void* workspace, size_t ws_bytes) {
     if (ceil_div(c.T, 16) * tiles16 > kMaxTiles) return GLOWQ_ERR_UNSUPPORTED;
     if (c.x != nullptr && !aligned(c.x, 16)) return GLOWQ_ERR_ALIGN;
     if (c.w4a8 && (c.d > kW4a8MaxD || c.w[0].format != GLOWQ_FMT_INT4_G128)) return GLOWQ_ERR_UNSUPPORTED;
-    if (c.mx8 && c.w[0].format != GLOWQ_FMT_MXFP4) return GLOWQ_ERR_UNSUPPORTED;
+    if (c.mx8 && c.w[0].format == GLOWQ_FMT_INT4_G128) return GLOWQ_ERR_UNSUPPORTED;  // MX weights only
     if (c.correct) {
         if (c.a == nullptr || c.b == nullptr) return GLOWQ_ERR_INVALID_ARG;
         for (int i = 0; i < c.m; ++i)

@@ -48,6 +48,24 @@ __device__ __forceinline__ uint32_t e4m3_code(float u) {
 // scale byte, the codes stored in the operand order above (two 16-byte stores per block).
 constexpr int kMx8QuantThreads = 256;
 
+// Weight format of the block-scaled step: the A operand's element code (cbsz) and the lane's operand
+// words: MXFP4 16 bytes (32 nibbles), MXFP6 24 bytes (the 16-byte plane and the 8-byte plane of the
+// device layout, element n at bits 6 n of their concatenation -- the operand order of the step, probed
+// like the FP4 one: element n of lane l pairs with the same FP8 byte as FP4 element n).
+template <int F>
+struct Mx8W {
+    static_assert(F == kFmtMxfp4 || F == kFmtMxfp6E2M3 || F == kFmtMxfp6E3M2, "MX weight format");
+    static constexpr bool six = F != kFmtMxfp4;
+    static constexpr int cbsz = F == kFmtMxfp4 ? 4 : (F == kFmtMxfp6E2M3 ? 2 : 3);
+    static constexpr int qblock = six ? 1536 : 1024;
+    static __device__ __forceinline__ i8v operand(const u4& lo, const u2& hi) {
+        if constexpr (six)
+            return i8v{(int32_t)lo[0], (int32_t)lo[1], (int32_t)lo[2], (int32_t)lo[3], (int32_t)hi[0], (int32_t)hi[1], 0, 0};
+        else
+            return i8v{(int32_t)lo[0], (int32_t)lo[1], (int32_t)lo[2], (int32_t)lo[3], 0, 0, 0, 0};
+    }
+};
+
 // Byte offset of the 512-byte scale record of token t's 128-token block and group G, plus the
 // token's position (t % 128) / 16 in each 8-byte word.
 __device__ __forceinline__ size_t mx8_scale_offset(int t, int G, int n_groups) {
@@ -100,8 +118,11 @@ __global__ __launch_bounds__(kMx8QuantThreads) void quant_mx8_kernel(const _Floa
 // operand as stored) and their scale words straight from HBM, one group ahead in registers; one
 // block-scaled matrix-core step per (row tile, token tile).  After the K loop r_pad / 32 fp16
 // matrix-core steps add R A_i^T, one rounding to fp16.
-template <int TT, int RR, int KS>
+template <int F, int TT, int RR, int KS>
 __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const ForwardArgs args) {
+    using WF = Mx8W<F>;
+    constexpr bool SIX = WF::six;
+    constexpr int QB = WF::qblock;
     constexpr int BM = 16 * TT;
     constexpr int LSB = 144;             // LDS row stride in bytes (128 + 16 padding)
     constexpr int NCH = BM * 8 / 256;    // 16-byte code chunks per thread per group (BM rows x 8)
@@ -120,8 +141,9 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = args.T, d = args.d, G = args.G;
     const int rt0 = nb * 4 * RR + wave * RR;
-    const size_t qstride = (size_t)M.n_tiles16 * 1024, szstride = (size_t)M.n_tiles16 * 64;
+    const size_t qstride = (size_t)M.n_tiles16 * QB, szstride = (size_t)M.n_tiles16 * 64;
     const int sgrp = lane >> 4;  // the lane's scale group in a 128-input group
+    const int q6ofs = 1024 + 8 * lane - 16 * lane;  // MXFP6: the lane's 8-byte plane, from its 16 bytes
 
     const uint8_t* qp[RR];
     const uint8_t* zp[RR];
@@ -130,7 +152,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
     for (int rr = 0; rr < RR; ++rr) {
         const int rt = rt0 + rr;
         w_ok[rr] = rt < M.n_tiles16;
-        qp[rr] = M.q + (size_t)(w_ok[rr] ? rt : 0) * 1024 + lane * 16;
+        qp[rr] = M.q + (size_t)(w_ok[rr] ? rt : 0) * QB + lane * 16;
         zp[rr] = M.sz + (size_t)(w_ok[rr] ? rt : 0) * 64 + (lane & 15) * 4;
     }
     // code staging: BM rows x 8 chunks of 16 bytes per group; thread tid copies chunks tid + 256 c
@@ -162,8 +184,10 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
     const bool act0 = kg < G;
     const bool copier = BM * 8 >= 256 || tid < BM * 8;  // TT = 1: 128 of 256 threads copy
 
+    const u2 zero2 = {0u, 0u};
     u4 st[NCHP];
     u4 qv[RR];
+    u2 q6[RR];
     uint32_t zw[RR];
     uint32_t sb[TT];
 #pragma unroll
@@ -172,6 +196,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
 #pragma unroll
     for (int rr = 0; rr < RR; ++rr) {
         qv[rr] = (act0 && w_ok[rr]) ? *reinterpret_cast<const u4*>(qp[rr] + (size_t)kg * qstride) : zero4;
+        q6[rr] = (SIX && act0 && w_ok[rr]) ? *reinterpret_cast<const u2*>(qp[rr] + (size_t)kg * qstride + q6ofs) : zero2;
         zw[rr] = (act0 && w_ok[rr]) ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)kg * szstride) : 0u;
     }
 #pragma unroll
@@ -194,6 +219,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
         const int buf = it & 1;
         const bool act = g < G, more = g + KS < G;
         u4 qn[RR];
+        u2 q6n[RR];
         uint32_t zn[RR], sbn[TT];
         if (more) {
 #pragma unroll
@@ -202,6 +228,8 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr) {
                 qn[rr] = w_ok[rr] ? *reinterpret_cast<const u4*>(qp[rr] + (size_t)(g + KS) * qstride) : zero4;
+                q6n[rr] = (SIX && w_ok[rr]) ? *reinterpret_cast<const u2*>(qp[rr] + (size_t)(g + KS) * qstride + q6ofs)
+                                            : zero2;
                 zn[rr] = w_ok[rr] ? *reinterpret_cast<const uint32_t*>(zp[rr] + (size_t)(g + KS) * szstride) : 0u;
             }
 #pragma unroll
@@ -213,7 +241,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
             int32_t sa[RR];
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr) {
-                a[rr] = i8v{(int32_t)qv[rr][0], (int32_t)qv[rr][1], (int32_t)qv[rr][2], (int32_t)qv[rr][3], 0, 0, 0, 0};
+                a[rr] = WF::operand(qv[rr], q6[rr]);
                 sa[rr] = (int32_t)((zw[rr] >> (8 * sgrp)) & 0xFFu);
             }
 #pragma unroll
@@ -224,8 +252,8 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
                                (int32_t)b1[0], (int32_t)b1[1], (int32_t)b1[2], (int32_t)b1[3]};
 #pragma unroll
                 for (int rr = 0; rr < RR; ++rr)
-                    acc[tt][rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[rr], b, acc[tt][rr], 4, 0, 0, sa[rr],
-                                                                                  0, (int32_t)sb[tt]);
+                    acc[tt][rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[rr], b, acc[tt][rr], WF::cbsz, 0, 0,
+                                                                                  sa[rr], 0, (int32_t)sb[tt]);
             }
         }
         if (more) {
@@ -237,6 +265,7 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr) {
                 qv[rr] = qn[rr];
+                q6[rr] = q6n[rr];
                 zw[rr] = zn[rr];
             }
 #pragma unroll
@@ -312,11 +341,12 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 ? 2 : 1)) void mx8_kernel(const 
 // each owning 4 row tiles and all 8 token tiles, so that every FP8 operand read from LDS feeds 4
 // block-scaled steps and every weight operand 8 (32 steps per wave and group).  Nothing in flight
 // sits in registers: per group the codes (128 rows x 128 bytes, read by every wave), each wave's
-// weight blocks (4 x 1 KB, the FP4 operands as stored) and their scale words, and the token
-// block's activation-scale record are copied HBM/L2 -> LDS by the load unit (global_load_lds) into
-// a ring of three stages, two groups ahead, so that the loop carries no register loads (whose
-// waits the compiler would place conservatively at the loop head) and every wait is the explicit
-// one before each group's barrier.  In a stage, code row r keeps its 16-byte chunk c at position
+// weight blocks (4 x 1 KB for MXFP4, 4 x 1.5 KB for MXFP6: the operands as stored) and their scale
+// words, and the token block's activation-scale record are copied HBM/L2 -> LDS by the load unit
+// (global_load_lds) into a ring of stages (three, two groups ahead, for MXFP4; two, one group ahead,
+// for the larger MXFP6 blocks, so that the ring fits the 160 KB of LDS), so that the loop carries no
+// register loads (whose waits the compiler would place conservatively at the loop head) and every
+// wait is the explicit one before each group's barrier.  In a stage, code row r keeps its 16-byte chunk c at position
 // c ^ f(r), f(r) = (r % 8) ^ ((r / 8) % 2), so that the operand reads of 16 consecutive rows fall
 // in distinct bank groups; a wave's scale words sit as [row][row tile], so that a lane reads its
 // four with one 16-byte read.  Tokens past T read token T - 1 and row tiles past the module its
@@ -327,17 +357,26 @@ typedef __attribute__((address_space(3))) void lds_void8;
 
 constexpr int kMx8WideWaves = 8;
 constexpr int kMx8CodeBytes = 128 * 128;                          // codes of one group
-constexpr int kMx8WBytes = kMx8WideWaves * 4 * 1024;              // weight blocks
 constexpr int kMx8ZBytes = kMx8WideWaves * 256;                   // weight scale words
 constexpr int kMx8SBytes = kMx8WideWaves * 256;                   // activation scales (two copies per half)
-constexpr int kMx8StageBytes = kMx8CodeBytes + kMx8WBytes + kMx8ZBytes + kMx8SBytes;
 
+template <int F>
 __global__ __launch_bounds__(512, 1) void mx8_wide_kernel(const ForwardArgs args) {
+    using WF = Mx8W<F>;
+    constexpr bool SIX = WF::six;
+    constexpr int QB = WF::qblock;
     constexpr int TT = 8, RR = 4, BM = 128, NW = kMx8WideWaves;
-    constexpr int W_AT = kMx8CodeBytes, Z_AT = W_AT + kMx8WBytes, S_AT = Z_AT + kMx8ZBytes;
-    __shared__ __attribute__((aligned(16))) uint8_t st0[kMx8StageBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[kMx8StageBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t st2[kMx8StageBytes];
+    constexpr int NST = SIX ? 2 : 3;                   // stages of the ring
+    constexpr int WW = RR * QB;                        // one wave's weight blocks per group
+    constexpr int NWI = WW / 1024;                     // their 1 KB copies
+    constexpr int PER = 2 + NWI + 2;                   // copies per wave and group
+    static_assert(PER < 16, "vmcnt immediate");
+    constexpr int W_AT = kMx8CodeBytes, Z_AT = W_AT + NW * WW, S_AT = Z_AT + kMx8ZBytes;
+    constexpr int SB = S_AT + kMx8SBytes;              // bytes per stage
+    static_assert(NST * SB <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t st0[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[NST == 3 ? SB : 16];
 
     int mb, nbl;
     if ((args.m_tiles & 3) == 0) {
@@ -381,7 +420,19 @@ __global__ __launch_bounds__(512, 1) void mx8_wide_kernel(const ForwardArgs args
     const int rofs0 = (lane & 15) * 128 + 16 * ((2 * sgrp) ^ fr);
     const int rofs1 = (lane & 15) * 128 + 16 * ((2 * sgrp + 1) ^ fr);
 
-    const uint32_t qlane = lane * 16, slane = (wave & 1) * 256 + lane * 4;
+    const uint32_t slane = (wave & 1) * 256 + lane * 4;
+    // weight copy i of a wave covers bytes 1024 i .. + 1023 of its RR blocks (lane l: 16 bytes at
+    // 1024 i + 16 l, in block (1024 i + 16 l) / QB), each lane's source block clamped on its own
+    uint32_t woff[NWI];
+#pragma unroll
+    for (int i = 0; i < NWI; ++i) {
+        const int b = 1024 * i + 16 * lane, rr = b / QB;
+        int rt = rtc[0];
+#pragma unroll
+        for (int k = 1; k < RR; ++k)
+            if (rr == k) rt = rtc[k];
+        woff[i] = (uint32_t)((rt - rtc[0]) * QB + (b - rr * QB));
+    }
     auto copy = [&](int g, uint8_t* stg) {
         const int gg = min(g, G - 1);
         const uint8_t* xb = args.x8 + (size_t)gg * kGroup;
@@ -389,11 +440,11 @@ __global__ __launch_bounds__(512, 1) void mx8_wide_kernel(const ForwardArgs args
         for (int i = 0; i < 2; ++i)
             __builtin_amdgcn_global_load_lds((const void*)(xb + xoff[i]), (lds_void8*)(stg + (16 * wave + 8 * i) * 128),
                                              16, 0, 0);
-        const uint8_t* qb = M.q + ((size_t)gg * NT + rtc[0]) * 1024;
+        const uint8_t* qb = M.q + ((size_t)gg * NT + rtc[0]) * QB;
 #pragma unroll
-        for (int rr = 0; rr < RR; ++rr)
-            __builtin_amdgcn_global_load_lds((const void*)(qb + (uint32_t)((rtc[rr] - rtc[0]) * 1024) + qlane),
-                                             (lds_void8*)(stg + W_AT + wave * 4096 + rr * 1024), 16, 0, 0);
+        for (int i = 0; i < NWI; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(qb + woff[i]), (lds_void8*)(stg + W_AT + wave * WW + i * 1024), 16,
+                                             0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(M.sz + (size_t)gg * NT * 64 + zsrc),
                                          (lds_void8*)(stg + Z_AT + wave * 256), 4, 0, 0);
         // the activation-scale record (512 bytes): wave w copies half w % 2 (every wave issues the
@@ -408,21 +459,27 @@ __global__ __launch_bounds__(512, 1) void mx8_wide_kernel(const ForwardArgs args
 #pragma unroll
         for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = f4{0.f, 0.f, 0.f, 0.f};
 
-    // every group issues the same 8 copies per wave, so that at the end of group g the copies of
-    // g + 1 have landed once at most 8 copies (those of g + 2) are in flight
+    // every group issues the same PER copies per wave, so that with three stages the copies of g + 1
+    // have landed at the end of group g once at most PER copies (those of g + 2) are in flight
+    // (s_waitcnt immediate: vmcnt in bits 3:0, expcnt and lgkmcnt left at their maxima)
     copy(0, st0);
-    copy(1, st1);
-    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    if constexpr (NST == 3) {
+        copy(1, st1);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | PER);
+    } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
     __builtin_amdgcn_s_barrier();
 
-    // group g, S = g % 3: its data in stage S (published by the previous barrier).  The copies of
-    // g + 2 go to stage S + 2, which every wave finished reading in group g - 1 (its operands fed
-    // steps issued before that group's barrier).
+    // group g, S = g % NST: its data in stage S (published by the previous barrier).  The copies of
+    // g + NST - 1 go to stage S + NST - 1, which every wave finished reading in group g - 1 (its
+    // operands fed steps issued before that group's barrier).
     auto step = [&](int g, auto Sc) {
         constexpr int S = decltype(Sc)::value;
+        constexpr int SN = (S + NST - 1) % NST;
         uint8_t* cur = S == 0 ? st0 : (S == 1 ? st1 : st2);
-        uint8_t* nx2 = S == 0 ? st2 : (S == 1 ? st0 : st1);
-        copy(g + 2, nx2);
+        uint8_t* nxt = SN == 0 ? st0 : (SN == 1 ? st1 : st2);
+        copy(g + NST - 1, nxt);
         __builtin_amdgcn_sched_barrier(0);
         auto bread = [&](int tt) {
             const u4 b0 = *reinterpret_cast<const u4*>(cur + tt * 16 * 128 + rofs0);
@@ -436,8 +493,10 @@ __global__ __launch_bounds__(512, 1) void mx8_wide_kernel(const ForwardArgs args
         int32_t sa[RR];
 #pragma unroll
         for (int rr = 0; rr < RR; ++rr) {
-            const u4 q = *reinterpret_cast<const u4*>(cur + W_AT + wave * 4096 + rr * 1024 + lane * 16);
-            a[rr] = i8v{(int32_t)q[0], (int32_t)q[1], (int32_t)q[2], (int32_t)q[3], 0, 0, 0, 0};
+            const uint8_t* wb = cur + W_AT + wave * WW + rr * QB;
+            const u4 q = *reinterpret_cast<const u4*>(wb + lane * 16);
+            const u2 q6 = SIX ? *reinterpret_cast<const u2*>(wb + 1024 + lane * 8) : u2{0u, 0u};
+            a[rr] = WF::operand(q, q6);
             sa[rr] = (int32_t)((zq[rr] >> (8 * sgrp)) & 0xFFu);
         }
         i8v bq[2];
@@ -449,21 +508,30 @@ __global__ __launch_bounds__(512, 1) void mx8_wide_kernel(const ForwardArgs args
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rr = 0; rr < RR; ++rr)
-                acc[tt][rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[rr], bq[tt & 1], acc[tt][rr], 4, 0, 0,
-                                                                              sa[rr], 0, sb);
+                acc[tt][rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[rr], bq[tt & 1], acc[tt][rr], WF::cbsz, 0,
+                                                                              0, sa[rr], 0, sb);
             __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): the copies of g + 1 have landed
+        // the copies of g + 1 have landed (three stages: those of g + 2 may stay in flight)
+        __builtin_amdgcn_s_waitcnt(NST == 3 ? (0x0F70 | PER) : 0x0F70);
         __builtin_amdgcn_s_barrier();
     };
     int g0 = 0;
-    for (; g0 + 3 <= G; g0 += 3) {
-        step(g0, ic<0>{});
-        step(g0 + 1, ic<1>{});
-        step(g0 + 2, ic<2>{});
+    if constexpr (NST == 3) {
+        for (; g0 + 3 <= G; g0 += 3) {
+            step(g0, ic<0>{});
+            step(g0 + 1, ic<1>{});
+            step(g0 + 2, ic<2>{});
+        }
+        if (g0 < G) step(g0, ic<0>{});
+        if (g0 + 1 < G) step(g0 + 1, ic<1>{});
+    } else {
+        for (; g0 + 2 <= G; g0 += 2) {
+            step(g0, ic<0>{});
+            step(g0 + 1, ic<1>{});
+        }
+        if (g0 < G) step(g0, ic<0>{});
     }
-    if (g0 < G) step(g0, ic<0>{});
-    if (g0 + 1 < G) step(g0 + 1, ic<1>{});
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no copy may land in LDS after the workgroup ends
 
     // the correction on the fp16 projection: r_pad / 32 fp16 steps
@@ -520,29 +588,30 @@ hipError_t launch_quant_mx8(const _Float16* x, int T, int d, uint8_t* xq, uint8_
     return hipGetLastError();
 }
 
-template <int TT, int RR>
+template <int F, int TT, int RR>
 static hipError_t launch_mx8_rr(const ForwardArgs& a, hipStream_t stream) {
     const dim3 grid(a.n_tiles);
     switch (a.tile_ks) {
         case 4:
             if constexpr (TT * RR >= 8) return hipErrorInvalidValue;  // not built: register budget
-            else hipLaunchKernelGGL((mx8_kernel<TT, RR, 4>), grid, dim3(1024), 0, stream, a);
+            else hipLaunchKernelGGL((mx8_kernel<F, TT, RR, 4>), grid, dim3(1024), 0, stream, a);
             break;
-        case 2: hipLaunchKernelGGL((mx8_kernel<TT, RR, 2>), grid, dim3(512), 0, stream, a); break;
-        case 1: hipLaunchKernelGGL((mx8_kernel<TT, RR, 1>), grid, dim3(256), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((mx8_kernel<F, TT, RR, 2>), grid, dim3(512), 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((mx8_kernel<F, TT, RR, 1>), grid, dim3(256), 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <int TT>
+template <int F, int TT>
 static hipError_t launch_mx8_tt(const ForwardArgs& a, hipStream_t stream) {
-    if (a.tile_rr == 2) return launch_mx8_rr<TT, 2>(a, stream);
-    if (a.tile_rr == 1) return launch_mx8_rr<TT, 1>(a, stream);
+    if (a.tile_rr == 2) return launch_mx8_rr<F, TT, 2>(a, stream);
+    if (a.tile_rr == 1) return launch_mx8_rr<F, TT, 1>(a, stream);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_mx8(const ForwardArgs& a, hipStream_t stream) {
+template <int F>
+static hipError_t launch_mx8_fmt(const ForwardArgs& a, hipStream_t stream) {
     if (a.tile_rr == 8) {  // the wide tile: 128 tokens x 512 rows
         if (a.tile_tt != 8 || a.tile_ks != 1) return hipErrorInvalidValue;
         // token-block quarters x row-block parities over the eight XCDs: 8 x (m / 4) x ceil(n / 2)
@@ -550,13 +619,22 @@ hipError_t launch_mx8(const ForwardArgs& a, hipStream_t stream) {
         const int n = a.n_tiles / a.m_tiles;
         const unsigned grid = (a.m_tiles % 4 == 0) ? 8u * (unsigned)(a.m_tiles / 4) * (unsigned)((n + 1) / 2)
                                                    : (unsigned)a.n_tiles;
-        hipLaunchKernelGGL(mx8_wide_kernel, dim3(grid), dim3(64 * kMx8WideWaves), 0, stream, a);
+        hipLaunchKernelGGL((mx8_wide_kernel<F>), dim3(grid), dim3(64 * kMx8WideWaves), 0, stream, a);
         return hipGetLastError();
     }
     switch (a.tile_tt) {
-        case 1: return launch_mx8_tt<1>(a, stream);
-        case 2: return launch_mx8_tt<2>(a, stream);
-        case 4: return launch_mx8_tt<4>(a, stream);
+        case 1: return launch_mx8_tt<F, 1>(a, stream);
+        case 2: return launch_mx8_tt<F, 2>(a, stream);
+        case 4: return launch_mx8_tt<F, 4>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_mx8(const ForwardArgs& a, hipStream_t stream) {
+    switch (a.fmt) {
+        case kFmtMxfp4: return launch_mx8_fmt<kFmtMxfp4>(a, stream);
+        case kFmtMxfp6E2M3: return launch_mx8_fmt<kFmtMxfp6E2M3>(a, stream);
+        case kFmtMxfp6E3M2: return launch_mx8_fmt<kFmtMxfp6E3M2>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -362,8 +362,8 @@ def test_forward_format_validation():
 
 
 def test_mx8_validation():
-    """glowq_group_forward_mx8: MXFP4 modules only; the workspace holds the codes, the block scales
-    and the projection; checks before any HIP call."""
+    """glowq_group_forward_mx8: MX weight modules only (MXFP4, MXFP6 E2M3 or E3M2); the workspace
+    holds the codes, the block scales and the projection; checks before any HIP call."""
     L = g.lib()
     r256 = lambda n: (n + 255) // 256 * 256
     # codes [T][d] | one 512-byte scale record per (128-token block, 128-input group)
@@ -373,10 +373,12 @@ def test_mx8_validation():
     assert L.glowq_mx8_workspace_bytes(0, 256, 8) == 0 and L.glowq_mx8_workspace_bytes(4, 200, 8) == 0
     a1 = (ctypes.c_void_p * 1)(FAKE)
     y1 = (ctypes.c_void_p * 1)(FAKE)
-    for fmt, code in ((g.FMT_INT4_G128, g.ERR_UNSUPPORTED), (g.FMT_MXFP6_E2M3, g.ERR_UNSUPPORTED),
-                      (g.FMT_MXFP6_E3M2, g.ERR_UNSUPPORTED)):
-        w1 = (g.QWeightC * 1)(_w(fmt=fmt))
-        assert L.glowq_group_forward_mx8(FAKE, 4, 256, 1, w1, FAKE, a1, 8, 1, FAKE, 1 << 24, y1, None) == code
+    w1 = (g.QWeightC * 1)(_w(fmt=g.FMT_INT4_G128))
+    assert L.glowq_group_forward_mx8(FAKE, 4, 256, 1, w1, FAKE, a1, 8, 1, FAKE, 1 << 24, y1, None) == g.ERR_UNSUPPORTED
+    w2 = (g.QWeightC * 2)(_w(fmt=g.FMT_MXFP4), _w(fmt=g.FMT_MXFP6_E2M3))  # one format per call
+    a2 = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    y2 = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    assert L.glowq_group_forward_mx8(FAKE, 4, 256, 2, w2, FAKE, a2, 8, 1, FAKE, 1 << 24, y2, None) == g.ERR_UNSUPPORTED
     w1 = (g.QWeightC * 1)(_w(fmt=g.FMT_MXFP4))
     need = L.glowq_mx8_workspace_bytes(4, 256, 8)
     assert L.glowq_group_forward_mx8(FAKE, 4, 256, 1, w1, FAKE, a1, 8, 1, FAKE, need - 1, y1, None) == g.ERR_WORKSPACE

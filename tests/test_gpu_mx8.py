@@ -1,10 +1,10 @@
-"""MXFP4 weights x MXFP8 activations (glowq_group_forward_mx8) against the fp64 oracle through the
-C ABI.
+"""MX weights (MXFP4, MXFP6 E2M3 / E3M2) x MXFP8 activations (glowq_group_forward_mx8) against the
+fp64 oracle through the C ABI.
 
 Bar: the E4M3 codes and E8M0 block scales the library writes to its workspace are bit-exact
 against oracle.glowq_ref.quantize_x_mxfp8 (every step of the conversion is exact on both sides);
 outputs within relative Frobenius 1e-3 and max-abs 1e-2 * max|y| of
-oracle.glowq_ref.group_forward_mx8 on the dequantised MXFP4 weights."""
+oracle.glowq_ref.group_forward_mx8 on the dequantised MX weights."""
 import numpy as np
 import pytest
 import torch
@@ -140,15 +140,32 @@ def test_mx8_zero_and_extreme_rows_rank_zero_and_empty():
     assert all(o.shape[0] == 0 for o in out)
 
 
-def test_mx8_rejects_other_formats():
+def test_mx8_rejects_int4_weights():
     g = glowq()
     keys = (62,)
     x = W.make_x(4, 256, 0.77, keys)
-    for fmt in ("int4", "mxfp6_e2m3"):
-        unit = W.make_unit("m8f", "group", x, [32], 8, keys, fmt=fmt)
-        with pytest.raises(g.GlowQError) as e:
-            run_unit(unit, True)
-        assert e.value.status == g.ERR_UNSUPPORTED
+    unit = W.make_unit("m8f", "group", x, [32], 8, keys, fmt="int4")
+    with pytest.raises(g.GlowQError) as e:
+        run_unit(unit, True)
+    assert e.value.status == g.ERR_UNSUPPORTED
+
+
+# MXFP6 weights: the 16 + 8-byte operand of the block-scaled step, small tiles and both rings of the
+# wide tile (two stages for MXFP6), ragged tokens and rows
+SHAPES6 = [("mxfp6_e2m3", 3, 384, [40, 24], 8), ("mxfp6_e2m3", 33, 640, [100], 24),
+           ("mxfp6_e2m3", 260, 640, [22000, 21000, 1000], 64), ("mxfp6_e2m3", 500, 256, [16400, 16000], 16),
+           ("mxfp6_e3m2", 17, 512, [96, 64, 40], 32), ("mxfp6_e3m2", 129, 256, [32784, 32760], 256)]
+
+
+@pytest.mark.parametrize("fmt,T,d,rows,r", SHAPES6)
+def test_mx8_mxfp6_weights_match_oracle(fmt, T, d, rows, r):
+    keys = (66, T, d)
+    x = W.make_x(T, d, 1.19, keys)
+    unit = W.make_unit("m86", "group", x, rows, r, keys, fmt=fmt)
+    ys, ws = run_unit(unit, True)
+    check_codes(unit, ws)
+    for i, (y, yr) in enumerate(zip(ys, oracle(unit, True))):
+        assert_parity(y, yr, f"mx8 {fmt} T={T} d={d} r={r} module {i}")
 
 
 @pytest.mark.parametrize("T", [1, 16, 64])
@@ -163,19 +180,20 @@ def test_mx8_llama_qkv(T):
         assert_parity(y, yr, f"mx8 qkv T={T} module {i}")
 
 
-def test_mx8_gateup_prefill_sampled():
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp6_e2m3"])
+def test_mx8_gateup_prefill_sampled(fmt):
     """LLaMA-2-7B gate/up group at T = 2048 (r = 64), 40 sampled tokens against the oracle (rows are
     independent: each token's codes, product and correction use that token alone)."""
     keys = (64,)
     T = 2048
     x = W.make_x(T, 4096, 0.77, keys, device="cuda")
-    unit = W.make_unit("m8g", "group", x, [11008, 11008], 64, keys, device="cuda", fmt="mxfp4")
+    unit = W.make_unit("m8g", "group", x, [11008, 11008], 64, keys, device="cuda", fmt=fmt)
     ys, ws = run_unit(unit, True)
     rows = np.sort(np.random.default_rng(3).choice(T, 40, replace=False))
     rows[-1] = T - 1
     ref = oracle(unit, True, rows=torch.from_numpy(rows).cuda())
     for i, (y, yr) in enumerate(zip(ys, ref)):
-        assert_parity(y[rows], yr, f"mx8 gate/up T=2048 module {i}")
+        assert_parity(y[rows], yr, f"mx8 {fmt} gate/up T=2048 module {i}")
     check_codes(unit, ws, rows=rows)
 
 
