@@ -205,9 +205,16 @@ def cpu_baseline(keep, mask):
     from oracle import glowq_ref as G
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        info = threadpool_info()
+        blas_threads = max([i.get("num_threads", 1) for i in info] + [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip() for i in info
+                                 if i.get("user_api") == "blas"})) or "unknown"
     except Exception:
-        blas_threads = 1
+        blas_threads, blas = 1, "unknown"
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
     import torch
     t_layers = []
     for l, units in keep.items():
@@ -230,7 +237,8 @@ def cpu_baseline(keep, mask):
             "kind": "oracle",
             "sample": f"fp64 numpy oracle on layers {sorted(keep)} (restored {[bool(mask[l]) for l in sorted(keep)]}) "
                       f"of the T=1 path, {t_pair:.1f}s, scaled x{32 // len(t_layers)} to the 32-layer step; "
-                      f"BLAS threads {blas_threads}, dequantisation single-threaded numpy"}
+                      f"BLAS {blas}, {blas_threads} threads; host: os.cpu_count() {os.cpu_count()}, "
+                      f"{usable} usable by this process; dequantisation single-threaded numpy"}
 
 
 # ------------------------------------------------------------------ extra measurements
