@@ -1,19 +1,20 @@
-// MXFP4 weights against MXFP8 activations on the gfx950 block-scaled matrix cores
-// (v_mfma_scale_f32_16x16x128_f8f6f4): the 8-bit-activation form of the method (GlowQ arXiv page,
-// Tables 14 and 15) with weights and activations both in the microscaling family of Table 13.
+// MX weights (MXFP4, MXFP6 E2M3 / E3M2) against MXFP8 activations on the gfx950 block-scaled matrix
+// cores (v_mfma_scale_f32_16x16x128_f8f6f4): the 8-bit-activation form of the method (GlowQ arXiv
+// page, Tables 14 and 15) with weights and activations both in the microscaling family of Table 13.
 //
 //   x8[t, k], S[t, b] = MXFP8 quantisation of X (OCP MX v1.0): per token and 32-input block b the
 //                       shared exponent floor(log2 max|x|) - 8, each element the nearest E4M3 value
 //                       (ties to even, saturating at 448)
-//   y_i[t, o]        = sum_b 2^(S_w[o, b] + S[t, b] - 254) sum_{k in b} w4[o, k] x8[t, k]
+//   y_i[t, o]        = sum_b 2^(S_w[o, b] + S[t, b] - 254) sum_{k in b} w[o, k] x8[t, k]
 //                      + R[t] . A_i[o],   R = X B^T from the fp16 X, formed once per call
-// The matrix cores apply both block scales themselves: one 16x16x128 step covers a 128-input group
-// of 16 rows and 16 tokens, four scale groups of 32 products each.
+// (w the weight element values).  The matrix cores apply both block scales themselves: one
+// 16x16x128 step covers a 128-input group of 16 rows and 16 tokens, four scale groups of 32
+// products each.
 //
-// Operand pairing of the step (measured with in-bounds probes on the device): lane l of the FP4
-// operand holds row l % 16 and the 32 products of scale group l / 16 (the weight layout's one MX
+// Operand pairing of the step (measured with in-bounds probes on the device): lane l of the weight
+// operand holds row l % 16 and the 32 elements of scale group l / 16 (the weight layout's one MX
 // block per lane; its scale is the lane's E8M0 byte); the FP8 operand's lane l holds column (token)
-// l % 16 and 32 bytes, byte p of lane group h pairing with FP4 element n = 16 (h % 2) + p % 16 of
+// l % 16 and 32 bytes, byte p of lane group h pairing with weight element n = 16 (h % 2) + p % 16 of
 // scale group g = 2 (p / 16) + h / 2, whose activation scale the lane l % 16 + 16 g supplies.  So the
 // activation codes of a 128-input group are stored in that order: input 32 g + n of the group at
 // byte 32 (2 (g % 2) + n / 16) + 16 (g / 2) + n % 16, and a lane reads its 32 operand bytes at 32 h.
@@ -114,8 +115,9 @@ __global__ __launch_bounds__(kMx8QuantThreads) void quant_mx8_kernel(const _Floa
 // GEMM tile: 16 TT tokens x 64 RR rows, four waves side by side in N (wave w owns RR row tiles of
 // 16 rows, all tokens), KS groups of four waves splitting the input groups (added through LDS in
 // wave-group order, deterministic).  Per group: the token codes (BM x 128 bytes) staged in LDS,
-// double-buffered, with each token tile's activation scales; weights (16 bytes per lane: the FP4
-// operand as stored) and their scale words straight from HBM, one group ahead in registers; one
+// double-buffered, with each token tile's activation scales; weights (16 bytes per lane for MXFP4,
+// 16 + 8 for MXFP6: the operand as stored) and their scale words straight from HBM, one group ahead
+// in registers; one
 // block-scaled matrix-core step per (row tile, token tile).  After the K loop r_pad / 32 fp16
 // matrix-core steps add R A_i^T, one rounding to fp16.
 template <int F, int TT, int RR, int KS>
