@@ -168,6 +168,65 @@ __global__ __launch_bounds__(256) void moe_proj_kernel(const MoeArgs a) {
     }
 }
 
+// Per-expert projection for few routed rows per expert (decode-sized calls): items (expert e,
+// block of 16 of its rows, 16-column tile jt of R), so that the expert's B is read by NJ workgroups
+// at once rather than streamed by one; the four waves take interleaved 32-input steps with up to
+// 16 steps of loads in flight (d <= 8192: one memory round trip per item) and add their sums through
+// LDS in wave order.
+template <int NJ>
+__global__ __launch_bounds__(256) void moe_proj_cols_kernel(const MoeArgs a) {
+    constexpr int U = 16;
+    __shared__ MoeShared s;
+    __shared__ f4 red[3][64];
+    moe_routing(a, 16, s);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int d = a.d, r = a.r, rp = a.r_pad;
+    const int kofs = 8 * (lane >> 4);
+    const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int item = blockIdx.x; item < s.total * NJ; item += gridDim.x) {
+        const int bi = item / NJ, jt = item - bi * NJ;
+        const int e = moe_expert_of(s, a.n_exp, bi);
+        const int j0 = s.off[e] + (bi - s.pre[e]) * 16;
+        const int j1 = s.end[e];
+        const int jl = j0 + (lane & 15);
+        const bool ok = jl < j1 && jl < a.n_rows;
+        const _Float16* xr = a.x + (size_t)moe_token(a, ok ? jl : j0) * d + kofs;
+        const int jj = 16 * jt + (lane & 15);
+        const bool j_ok = jj < r;
+        const _Float16* br = a.b + (size_t)e * r * d + (size_t)(j_ok ? jj : 0) * d + kofs;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int n = d / 128;  // steps of this wave: 32 inputs at 128 i + 32 wave
+        const int k0 = 32 * wave;
+        for (int c = 0; c < n; c += U) {
+            h8 xa[U], bb[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int kk = k0 + 128 * min(c + u, n - 1);
+                xa[u] = ok ? load_h8(xr + kk) : zero8;
+                bb[u] = j_ok ? load_h8(br + kk) : zero8;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c + u < n) acc = mfma16(xa[u], bb[u], acc);
+        }
+        if (wave > 0) red[wave - 1][lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+            f4 v = acc;
+#pragma unroll
+            for (int w = 0; w < 3; ++w) v += red[w][lane];
+            const int col = 16 * jt + (lane & 15);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int jrow = j0 + 4 * (lane >> 4) + i;  // output rows: tokens of the block
+                if (jrow < j1 && jrow < a.n_rows && col < rp) a.Rout[(size_t)jrow * rp + col] = (_Float16)v[i];
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // Grouped GEMM: items (expert e, row block rb of 64 RR rows of one module, block tb of 16 TT of
 // e's routed rows), in that order, so that consecutive items share the expert's weight block.
 // Per item the prefill tile: 4 waves side by side in N, the gathered activation rows staged in
@@ -491,7 +550,13 @@ __global__ __launch_bounds__(256) void moe_decode_kernel(const MoeArgs a) {
 
 template <int NJ>
 static void launch_moe_proj_nj(const MoeArgs& a, unsigned grid, hipStream_t stream) {
-    hipLaunchKernelGGL((moe_proj_kernel<NJ>), dim3(grid), dim3(256), 0, stream, a);
+    // fewer than 32 routed rows per expert on average: items per 16-column tile of R as well
+    if ((int64_t)a.n_rows < 32 * (int64_t)a.n_exp) {
+        const unsigned g2 = (unsigned)std::min<int64_t>((int64_t)grid * NJ, kMoeMaxGrid);
+        hipLaunchKernelGGL((moe_proj_cols_kernel<NJ>), dim3(g2), dim3(256), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((moe_proj_kernel<NJ>), dim3(grid), dim3(256), 0, stream, a);
+    }
 }
 
 hipError_t launch_moe_proj(const MoeArgs& a, int64_t max_items, hipStream_t stream) {

@@ -95,6 +95,18 @@ def test_moe_small_all_rows(share, T, top):
         check(case, ys, x, row_token, offsets, share, range(8), restore, f"T={T} share={share} restore={restore}")
 
 
+@pytest.mark.parametrize("r", [128, 256])
+def test_moe_projection_wide_rank_few_rows(r):
+    """Few routed rows per expert (the projection splits the rank columns over the waves) at ranks
+    that give each wave two and four 16-column tiles: every routed row against the oracle."""
+    case = MoeCase(8, 512, [96, 80], r, (73, r))
+    x = W.make_x(9, 512, 0.77, (73, r))
+    row_token, offsets = W.moe_routing(9, 8, 2, (73, r), skip=[5])
+    ys, ws = case.run(x, row_token, offsets, 0, True)
+    assert glowq().workspace_status(ws) == glowq().OK
+    check(case, ys, x, row_token, offsets, 0, range(8), True, f"few rows r={r}")
+
+
 def test_moe_down_solo_routed_order():
     """The down projection: one module per expert on its hidden rows, already in routed order
     (no token indices), 6 experts of 64 rows at d = 384, r = 24."""
