@@ -533,6 +533,9 @@ int glowq_moe_forward(const void* x, int64_t T, int64_t d, int32_t n_exp, int32_
     a.tile_tt = tt;
     a.err = static_cast<int32_t*>(workspace) + kSyncError;
     uint8_t* R = static_cast<uint8_t*>(workspace) + kWsHeader;
+    // persistent grids: (expert, block) pairs number at most n_rows / rows per block plus the active
+    // experts, and every active expert holds at least one routed row
+    const int64_t active_max = std::min<int64_t>(n_exp, n_rows);
     if (correct) {
         a.R = reinterpret_cast<const _Float16*>(R);
         if (share == GLOWQ_MOE_SHARE_ALL) {
@@ -544,10 +547,10 @@ int glowq_moe_forward(const void* x, int64_t T, int64_t d, int32_t n_exp, int32_
             a.r_by_token = 0;
             a.b = static_cast<const _Float16*>(b);
             a.Rout = reinterpret_cast<_Float16*>(R);
-            if (launch_moe_proj(a, ceil_div(n_rows, 16) + n_exp, stream) != hipSuccess) return GLOWQ_ERR_HIP;
+            if (launch_moe_proj(a, ceil_div(n_rows, 16) + active_max, stream) != hipSuccess) return GLOWQ_ERR_HIP;
         }
     }
-    if (launch_moe_gemm(a, (int64_t)rbs * (ceil_div(n_rows, rows_per_item) + n_exp), stream) != hipSuccess)
+    if (launch_moe_gemm(a, (int64_t)rbs * (ceil_div(n_rows, rows_per_item) + active_max), stream) != hipSuccess)
         return GLOWQ_ERR_HIP;
     return GLOWQ_OK;
 }
