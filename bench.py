@@ -663,9 +663,9 @@ def extra_moe(g, reps=10, copies=4):
     """Qwen1.5-MoE-A2.7B MLP: 60 experts, gate/up group 2048 -> 2 x 1408 and down 1408 -> 2048 per
     expert, top-4 routing, r = 64, one launch for all experts (plus the projection when
     correcting): per-expert shared basis and one basis for all experts, T = 1, 64 and 2048 tokens.
-    Each call is a captured HIP graph, replayed back to back between events (no host work in the
-    timed intervals); at T <= 64 the calls rotate over `copies` copies of every expert's weights and
-    factors. Bytes are the active experts' algorithmic bytes, flops the routed rows'."""
+    Calls are captured in one HIP graph (32 at T <= 64, 4 at T = 2048, rotating over `copies` copies
+    of every expert's weights and factors at T <= 64) and the graph's replay time is divided by their
+    number, as the decode path spreads its graph launch over 128 launches. Bytes are the active experts' algorithmic bytes, flops the routed rows'."""
     import torch
     import workload as W
     stream = torch.cuda.current_stream()
@@ -685,19 +685,22 @@ def extra_moe(g, reps=10, copies=4):
     sets = [(mods, b_exp, dmods, db)] + [(clone(mods), b_exp.clone(), clone(dmods), db.clone())
                                          for _ in range(copies - 1)]
 
-    def timed(fns):
-        for f in fns:
-            f()
+    def timed(calls, per_graph=32):
+        # per_graph calls (rotating over the copies) captured in one graph, so that the graph's own
+        # launch is spread over them as in the 128-launch decode path; median over replays / per_graph
+        gr = graphed(lambda: [calls[k % len(calls)]() for k in range(per_graph)])
+        for _ in range(2):
+            gr.replay()
         torch.cuda.synchronize()
         evs = []
-        for k in range(reps * len(fns)):
+        for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            fns[k % len(fns)]()
+            gr.replay()
             e1.record(stream)
             evs.append((e0, e1))
         torch.cuda.synchronize()
-        return statistics.median(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs)
+        return statistics.median(e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs) / per_graph
 
     out = {}
     for T in (1, 64, 2048):
@@ -711,31 +714,31 @@ def extra_moe(g, reps=10, copies=4):
         res = {"routed_rows": n, "active_experts": active}
         for share, tag in ((0, "gateup_per_expert"), (1, "gateup_all_experts")):
             ws = g.make_workspace(1, 8, 1, min_bytes=g.moe_workspace_bytes(n, T, r, share))
-            fns = [graphed(lambda c=c: g.moe_forward(x, E, sets[c][0], sets[c][1] if share == 0 else b_all, share, r,
-                                                     True, rt, off, n, workspace=ws, y=ys)).replay for c in range(nc)]
-            t = timed(fns)
+            calls = [lambda c=c: g.moe_forward(x, E, sets[c][0], sets[c][1] if share == 0 else b_all, share, r, True, rt,
+                                               off, n, workspace=ws, y=ys) for c in range(nc)]
+            t = timed(calls, 32 if T <= 64 else 4)
             nb = active * unit_bytes(0, d, [inter, inter], r, True, 1 if share == 0 else 0) + (
                 r * d * 2 if share == 1 else 0) + T * d * 2 + n * 2 * inter * 2
             fl = 2 * n * d * 2 * inter + (2 * n if share == 0 else 2 * T) * d * r + 2 * n * r * 2 * inter
             res[tag] = {"us": round(t * 1e6, 2), "tokens_per_s": round(T / t, 1),
                         "TB_per_s": round(nb / t / 1e12, 3), "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4),
                         "TFLOP_per_s": round(fl / t / 1e12, 1), "frac_mfma_f16_peak": round(fl / t / 1e12 / 2500.0, 4)}
-            del fns, ws
+            del calls, ws
         h = W.make_x(n, inter, 0.77, (0, 11, T), device="cuda")
         yd = [torch.empty(n, d, dtype=torch.float16, device="cuda")]
         ws = g.make_workspace(1, 8, 1, min_bytes=g.moe_workspace_bytes(n, n, r, 0))
-        fns = [graphed(lambda c=c: g.moe_forward(h, E, sets[c][2], sets[c][3], 0, r, True, None, off, n, workspace=ws,
-                                                 y=yd)).replay for c in range(nc)]
-        t = timed(fns)
+        calls = [lambda c=c: g.moe_forward(h, E, sets[c][2], sets[c][3], 0, r, True, None, off, n, workspace=ws, y=yd)
+                 for c in range(nc)]
+        t = timed(calls, 32 if T <= 64 else 4)
         nb = active * unit_bytes(0, inter, [d], r, True) + n * inter * 2 + n * d * 2
         fl = 2 * n * inter * d + 2 * n * inter * r + 2 * n * r * d
         res["down_per_expert"] = {"us": round(t * 1e6, 2), "TB_per_s": round(nb / t / 1e12, 3),
                                   "frac_hbm_peak": round(nb / t / 1e12 / 8.0, 4), "TFLOP_per_s": round(fl / t / 1e12, 1),
                                   "frac_mfma_f16_peak": round(fl / t / 1e12 / 2500.0, 4)}
         out[f"T{T}"] = res
-        del x, h, ys, yd, ws, fns
+        del x, h, ys, yd, ws, calls
     out["workload"] = ("Qwen1.5-MoE-A2.7B MLP, 60 experts, gate/up 2 x 1408 over d = 2048, down 1408 -> 2048, "
-                       "top-4, r=64; graph replays back to back; T <= 64 rotate 4 copies of all experts' weights "
+                       "top-4, r=64; 32 calls per graph (4 at T = 2048), T <= 64 rotating 4 copies of all experts' weights "
                        "(T = 64 touches ~680 MB per cycle; at T = 1 the 4 active experts' ~46 MB per cycle can "
                        "stay in the 256 MB last-level cache)")
     del sets, mods, dmods, b_exp, db
