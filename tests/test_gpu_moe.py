@@ -82,7 +82,7 @@ def check(case, ys, x, row_token, offsets, share, experts, restore=True, label="
 
 
 @pytest.mark.parametrize("share", [0, 1], ids=["per_expert", "all_experts"])
-@pytest.mark.parametrize("T,top", [(1, 2), (37, 2), (150, 3)])
+@pytest.mark.parametrize("T,top", [(1, 2), (37, 2), (150, 3), (300, 2)])
 def test_moe_small_all_rows(share, T, top):
     """8 experts (expert 2 receives no token), gate/up group of 96 + 80 rows at d = 512, r = 16:
     every routed row against the oracle, restore on and off."""
@@ -118,7 +118,7 @@ def test_moe_down_solo_routed_order():
     check(case, ys, h, None, offsets, 0, range(6), True, "down")
 
 
-@pytest.mark.parametrize("T", [1, 64, 512])
+@pytest.mark.parametrize("T", [1, 64, 512, 2048])
 def test_moe_qwen_gateup_sampled(T):
     """Qwen1.5-MoE-A2.7B MLP: 60 experts, gate/up 2 x 1408 rows over d = 2048, top-4 routing,
     r = 64, per-expert shared basis; the rows of 6 experts (the busiest, the last and some
