@@ -3,7 +3,7 @@
  * libglowq.so.  They are not part of the forward path: the benchmark uses them to measure, on
  * the GPU it runs on, the achievable peaks its kernels are compared against (an HBM streaming
  * read and a matrix-core-only loop), next to the vendor peaks, and the floor that a sequence of
- * separate launches of given sizes allows.
+ * separate launches of given sizes allows; and a check of the decode projection hand-off.
  *
  * All launch asynchronously on `stream` and return 0, or -1 for an invalid argument (checked on
  * the host before any HIP call), or -6 for a launch failure.  All pointers are device pointers
@@ -46,6 +46,30 @@ double glowq_probe_mfma_f16_flops(int64_t iters, int32_t blocks);
 int glowq_probe_mfma_shape(int32_t shape, int32_t chains, int64_t iters, void* sink_dev, int32_t blocks,
                            hipStream_t stream);
 double glowq_probe_mfma_shape_flops(int32_t shape, int32_t chains, int64_t iters, int32_t blocks);
+
+/* The decode path's projection hand-off (epoch, arrivals, tagged pairs with their bounded wait;
+ * the same device routines as the forward kernels) on its own, with producers the caller slows
+ * down or silences.  Not a measurement: a check of the protocol that the forward kernels rely on.
+ * One launch of n_prod producer and n_cons consumer workgroups (256 threads) on the workspace of
+ * glowq.h (zero-filled once by glowq_workspace_init; the epoch and counters in its header, the
+ * pairs after it):
+ *   producer p  : reads the epoch, sleeps delay * (p + 1) / n_prod times ~8128 clocks, arrives,
+ *                 then (publish == 1) writes pairs [p c, (p + 1) c) of the n_pairs (c =
+ *                 ceil(n_pairs / n_prod)) with value salt + k, tagged epoch + 1
+ *   consumer    : reads the epoch, arrives, then reads all n_pairs pairs through the bounded wait
+ *                 and adds to counts_dev[0] the values that differ from salt + k and to
+ *                 counts_dev[1] the pairs it read
+ * The launch's last arrival advances the epoch by one (skipping 2^32 - 1).  An expired wait sets
+ * the workspace error word (glowq_workspace_status reports GLOWQ_ERR_HANDOFF).
+ *   workspace_bytes >= 8192 + 8 n_pairs; workspace 256-byte aligned; counts_dev int32 [2],
+ *   16-byte aligned, accumulated into (not cleared)
+ *   1 <= n_prod <= 1024, 1 <= n_cons <= 65536, 1 <= n_pairs <= 65536, 0 <= delay <= 4096
+ *   publish 0 or 1; publish == 0 (every consumer thread waits out one full bounded wait, about a
+ *   second) needs n_pairs <= 256 and n_cons <= 64
+ * Returns -1 for an invalid argument (before any HIP call), -6 for a launch failure, else 0.
+ * Asynchronous on `stream`. */
+int glowq_probe_handoff(void* workspace, size_t workspace_bytes, int32_t n_prod, int32_t n_cons, int32_t n_pairs,
+                        int64_t delay, int32_t publish, float salt, int32_t* counts_dev, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ PROBE_LIB = os.path.join(PKG, "libglowq_probe.so")
 
 SOURCES = ["format.hip", "proj.hip", "decode.hip", "prefill.hip", "w4a8.hip", "mx8.hip", "moe.hip", "score.hip", "moment.hip", "solve.hip",
            "abi.cpp"]
-PROBE_SOURCES = ["probe.hip"]  # measurement probes, a library of their own
+PROBE_SOURCES = ["probe.hip", "handoff_probe.hip"]  # measurement and protocol probes, a library of their own
 ARCH = "gfx950"
 
 

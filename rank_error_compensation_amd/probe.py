@@ -1,5 +1,5 @@
 """ctypes binding of libglowq_probe.so (include/glowq_probe.h): the achievable-peak probes used
-by the benchmark.  Argument marshalling only."""
+by the benchmark and the hand-off protocol probe used by the tests.  Argument marshalling only."""
 from __future__ import annotations
 
 import ctypes
@@ -17,6 +17,7 @@ EXPORTS = {
     "glowq_probe_mfma_shape": (ctypes.c_int, [_i32, _i32, _i64, _vp, _i32, _vp]),
     "glowq_probe_mfma_shape_flops": (ctypes.c_double, [_i32, _i32, _i64, _i32]),
     "glowq_probe_read_sequence": (ctypes.c_int, [_vp, ctypes.POINTER(_i64), _i32, _vp, _vp]),
+    "glowq_probe_handoff": (ctypes.c_int, [_vp, _sz, _i32, _i32, _i32, _i64, _i32, ctypes.c_float, _vp, _vp]),
 }
 _lib = None
 
@@ -77,3 +78,12 @@ class ReadSequence:
         rc = lib().glowq_probe_read_sequence(src.data_ptr(), self.arr, self.n, sink.data_ptr(), _stream())
         if rc != 0:
             raise RuntimeError(f"glowq_probe_read_sequence failed ({rc})")
+
+
+def handoff(ws: torch.Tensor, n_prod: int, n_cons: int, n_pairs: int, delay: int, publish: bool, salt: float,
+            counts: torch.Tensor) -> None:
+    """One launch of the hand-off protocol probe on workspace `ws` (counts: int32 [2], accumulated)."""
+    rc = lib().glowq_probe_handoff(ws.data_ptr(), ws.numel() * ws.element_size(), n_prod, n_cons, n_pairs, delay,
+                                   int(publish), salt, counts.data_ptr(), _stream())
+    if rc != 0:
+        raise RuntimeError(f"glowq_probe_handoff failed ({rc})")

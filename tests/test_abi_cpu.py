@@ -290,6 +290,20 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert L.glowq_probe_read_sequence(FAKE, sizes, 1, FAKE, None) == -1
     assert L.glowq_probe_read_sequence(FAKE, sizes, 0, FAKE, None) == -1
 
+    def handoff(ws=FAKE, nbytes=8192 + 8 * 256, n_prod=4, n_cons=8, n_pairs=256, delay=0, publish=1, cnt=FAKE):
+        return L.glowq_probe_handoff(ws, nbytes, n_prod, n_cons, n_pairs, delay, publish, 1.0, cnt, None)
+    assert handoff(ws=None) == -1
+    assert handoff(cnt=None) == -1
+    assert handoff(ws=FAKE + 16) == -1                               # workspace not 256-byte aligned
+    assert handoff(nbytes=8192 + 8 * 255) == -1                      # pairs beyond the workspace
+    assert handoff(n_prod=0) == -1 and handoff(n_prod=1025) == -1
+    assert handoff(n_cons=0) == -1 and handoff(n_cons=65537) == -1
+    assert handoff(n_pairs=0) == -1 and handoff(n_pairs=65537, nbytes=1 << 20) == -1
+    assert handoff(delay=-1) == -1 and handoff(delay=4097) == -1
+    assert handoff(publish=2) == -1
+    assert handoff(publish=0, n_pairs=257, nbytes=1 << 20) == -1     # silent producers: one wait per thread
+    assert handoff(publish=0, n_cons=65) == -1
+
 
 def test_moe_validation_rejects_before_any_hip_call():
     L = g.lib()
