@@ -17,6 +17,7 @@
 // Workgroups are numbered XCD-aware: consecutive logical tiles (same weight block, successive
 // token blocks) land on the same XCD and share its L2.
 #include "handoff.h"
+#include "mid.h"
 
 namespace glowq {
 
@@ -35,9 +36,8 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
 // Tokens past T and ranks past r are never stored.
 constexpr int kProdMaxWaves = 16;
 
-__device__ void produce_tile(const ForwardArgs& a, int p) {
-    __shared__ f4 red[kProdMaxWaves - 1][64];
-    __shared__ uint32_t ptag;
+// The producer's LDS: red (the waves' partial tiles) and the tag, given by the caller.
+__device__ void produce_tile_in(const ForwardArgs& a, int p, f4 (*red)[64], uint32_t& ptag) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nw = (int)(blockDim.x >> 6);
@@ -102,6 +102,12 @@ __device__ void produce_tile(const ForwardArgs& a, int p) {
         }
     }
     if (tid == 0) finish(a, arrive_slot(a, arrived), epoch0);
+}
+
+__device__ void produce_tile(const ForwardArgs& a, int p) {
+    __shared__ f4 red[kProdMaxWaves - 1][64];
+    __shared__ uint32_t ptag;
+    produce_tile_in(a, p, red, ptag);
 }
 
 // Small grids: KS groups of four wavefronts per workgroup (256 KS threads) share one output tile
@@ -626,6 +632,260 @@ __global__ __launch_bounds__(256, 2) void prefill_wide_kernel(const ForwardArgs 
             }
         }
     }
+}
+
+// 17 .. 64 tokens, INT4 weights: one token block (16 TT tokens, TT = 2 or 4), so every weight byte
+// is read once, and 4 RR row tiles of 16 rows per workgroup of eight wavefronts.  Wave w owns RR row
+// tiles (row part w % 4) and all TT token tiles for half of every input group (K slices 2 (w / 4)
+// and 2 (w / 4) + 1 of 32 inputs), so every dequantised weight operand feeds TT matrix-core steps
+// (the unpacking is the costly part at this size), every activation operand read from LDS feeds RR,
+// and two wavefronts share each SIMD; the halves are added through LDS at the end, in a fixed order.
+// Per 128-input group a stage holds the activation tile (16 TT rows x 256 bytes, XOR-swizzled as in
+// the wide tile), the 4 RR weight blocks (1 KB each, operand order) and their (z, s) words, all
+// three copied HBM/L2 -> LDS by the load unit (global_load_lds, no registers); NST stages form a
+// ring, so the copies of the next NST - 1 groups are in flight while one group is multiplied, and
+// every wave issues the same PER copies per group (duplicates where fewer are needed), which lets
+// one s_waitcnt count decide when the next stage has landed.  The dequantised operands are those
+// of the other tiles (exact (q - z), one rounding by the fp16 scale).  Correcting calls only: the
+// first n_prod workgroups form R as 16 x 16 tiles (produce_tile_in) and every tile reads its rows
+// as tagged pairs for the correction, as the fused small tiles do.
+constexpr int kMidWaves = 8;
+constexpr int kMidStageMax = 160 * 1024 - 512;  // stage ring bytes (the only LDS of the kernel)
+
+template <int TT, int RR>
+struct MidShape {
+    static constexpr int RB = 4 * RR;            // row tiles per workgroup
+    static constexpr int W_AT = TT * 4096;       // activation tile: 16 TT rows x 256 bytes
+    static constexpr int Z_AT = W_AT + RB * 1024;
+    static constexpr int SB = Z_AT + 4 * 256;    // (z, s) words: 256 bytes per row part
+    static constexpr int NST = kMidStageMax / SB < 8 ? kMidStageMax / SB : 8;
+    static constexpr int XI = TT / 2;            // activation copies per wave and group
+    static constexpr int PER = XI + 2;           // copies per wave and group (one weight block, one (z, s))
+    static constexpr int WAIT = (NST - 2) * PER; // copies allowed in flight once the next stage landed
+    static_assert(RR == 2 && NST >= TT && NST >= 3 && WAIT < 64, "mid tile shape");
+    static_assert(SB - 16 >= 16 * kMaxRank * 2 && SB >= (kMidWaves - 1) * 64 * 16, "stage reuse");
+    static_assert(NST * SB >= 4 * TT * RR * 1024, "the halves' reduction fits the ring");
+};
+
+// s_waitcnt immediate: vmcnt n (bits 3:0 and 15:14), expcnt and lgkmcnt at their maxima
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+template <int TT, int RR>
+__global__ __launch_bounds__(64 * kMidWaves, 1) void mid_kernel(const ForwardArgs args) {
+    using S = MidShape<TT, RR>;
+    constexpr int RB = S::RB, NST = S::NST, SB = S::SB, W_AT = S::W_AT, Z_AT = S::Z_AT, XI = S::XI;
+    // the stage ring is the kernel's only LDS object: the compiler then leaves the ordering of the
+    // copies and the operand reads to the explicit waits below (with several objects it waits for
+    // every copy in flight before each read).  After the loop the ring holds the halves' sums, the
+    // projection rows (token tile tt in stage tt) and the tag (end of stage 0); producers keep their
+    // partial tiles in stage 0 and their tag in stage 1.
+    __shared__ __attribute__((aligned(16))) uint8_t stg[NST * SB];
+    auto sp = [&](int k) -> uint8_t* { return stg + k * SB; };
+    if ((int)blockIdx.x < args.n_prod) {
+        produce_tile_in(args, blockIdx.x, reinterpret_cast<f4(*)[64]>(stg), *reinterpret_cast<uint32_t*>(stg + SB));
+        return;
+    }
+    // thread 0's epoch read (the tag of this launch), before any arrival of this workgroup
+    uint32_t epoch0 = 0;
+    if (threadIdx.x == 0) epoch0 = load_epoch(args);
+    const int nbl = (int)blockIdx.x - args.n_prod;
+    const ModuleArgs M = args.mod[module_of(args, nbl)];
+    const int nb = nbl - M.tile_begin;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rw = wave & 3, kh = wave >> 2;  // row part, K half
+    const int T = args.T, d = args.d, G = args.G;
+    const int NT = M.n_tiles16;
+    const NibConsts nc = nib_consts();
+    const int rt0 = nb * RB + rw * RR;  // the wave's first row tile
+
+    // activation copy: instruction i of wave w fills tile rows 4 XI w + 4 i .. + 3; lane l lands at
+    // row + l / 16, 16-byte position l % 16, holding chunk (l % 16) ^ (row % 16)
+    uint32_t xoff[XI];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+        const int row = 4 * XI * wave + 4 * i + (lane >> 4);
+        xoff[i] = (uint32_t)(min(row, T - 1) * d + 8 * ((lane & 15) ^ (row & 15))) * 2u;
+    }
+    // weight copy: wave w copies block w % RB of the workgroup (waves past RB repeat a block: same
+    // bytes, same place); (z, s) copy: wave w the words of row part w % 4, lane l the word of row
+    // l % 16 of the part's row tile l / 16 (past RR: the last)
+    const int kw = wave % RB;
+    const uint32_t wsrc = (uint32_t)(min(nb * RB + kw, NT - 1) * 1024 + lane * 16);
+    const uint32_t zsrc = (uint32_t)(min(rt0 + min(lane >> 4, RR - 1), NT - 1) * 64 + (lane & 15) * 4);
+    const char* xbase = reinterpret_cast<const char*>(args.x);
+    auto copy = [&](int g, uint8_t* st) {
+        const int gg = min(g, G - 1);  // past the end: a valid group into a stage no one reads
+#pragma unroll
+        for (int i = 0; i < XI; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(xbase + (size_t)gg * kGroup * 2 + xoff[i]),
+                                             (lds_void*)(st + (4 * XI * wave + 4 * i) * 256), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(M.q + (size_t)gg * NT * 1024 + wsrc),
+                                         (lds_void*)(st + W_AT + kw * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(M.sz + (size_t)gg * NT * 64 + zsrc),
+                                         (lds_void*)(st + Z_AT + rw * 256), 4, 0, 0);
+    };
+    // operand read of slice j, token tile tt: row 16 tt + l % 16, chunk 4 j + l / 16 (swizzled)
+    uint32_t bofs[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * kh + jj;
+        bofs[jj] = (uint32_t)((lane & 15) * 256 + 16 * ((4 * j + (lane >> 4)) ^ (lane & 15)));
+    }
+
+    f4 acc[TT][RR];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = f4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k = 0; k < NST - 1; ++k) copy(k, sp(k));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::WAIT));
+    __builtin_amdgcn_s_barrier();
+    // the epoch read was thread 0's first load, so it has landed: use it now (a register load still
+    // in flight across the loop would make the compiler drain the copies at every group)
+    asm volatile("" : "+v"(epoch0));  // consumed here, so the compiler cannot sink the use past the loop
+    const uint32_t tag0 = epoch0 + 1u;
+
+    int k = 0;  // stage of group g
+    for (int g = 0; g < G; ++g) {
+        // the copies of g + NST - 1 go to the stage read in group g - 1 (done: the barrier below)
+        copy(g + NST - 1, sp(k == 0 ? NST - 1 : k - 1));
+        const uint8_t* cur = sp(k);
+        uint32_t q[RR][2];
+        h2 c1024[RR], c64[RR];
+        h8 s8[RR];
+#pragma unroll
+        for (int rr = 0; rr < RR; ++rr) {
+            const u2 qq = *reinterpret_cast<const u2*>(cur + W_AT + (RR * rw + rr) * 1024 + lane * 16 + 8 * kh);
+            q[rr][0] = qq[0];
+            q[rr][1] = qq[1];
+            const uint32_t zs = *reinterpret_cast<const uint32_t*>(cur + Z_AT + rw * 256 + rr * 64 + (lane & 15) * 4);
+            zero_consts(zs, c1024[rr], c64[rr]);
+            const _Float16 sc = as_h2(zs)[1];
+            s8[rr] = h8{sc, sc, sc, sc, sc, sc, sc, sc};
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            h8 b[TT];
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) b[tt] = *reinterpret_cast<const h8*>(cur + tt * 4096 + bofs[jj]);
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) {
+                const h8 a = nib8_minus_z(q[rr][jj], c1024[rr], c64[rr], nc) * s8[rr];
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt) acc[tt][rr] = mfma16(a, b[tt], acc[tt][rr]);
+            }
+        }
+        // the copies of g + 1 have landed once at most those of g + 2 .. g + NST - 1 are in flight
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::WAIT));
+        __builtin_amdgcn_s_barrier();
+        k = k == NST - 1 ? 0 : k + 1;
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy may land in LDS after this point
+    __syncthreads();
+
+    // the second K half hands its sums to the first through LDS; the first adds them (fixed order)
+    f4* red = reinterpret_cast<f4*>(stg);
+    if (kh == 1) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) red[((rw * TT + tt) * RR + rr) * 64 + lane] = acc[tt][rr];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) acc[tt][rr] += red[((rw * TT + tt) * RR + rr) * 64 + lane];
+    }
+    __syncthreads();  // the sums are read before the ring is reused
+
+    // thread 0 arrives (after its epoch read: the value was used before the loop) and counts its
+    // slot, and hands the tag to the workgroup through LDS
+    int arrived = 0;
+    if (threadIdx.x == 0) {
+        *reinterpret_cast<uint32_t*>(stg + SB - 4) = tag0;
+        arrived = arrive_slot(args, arrive(args));
+    }
+    {
+        __syncthreads();
+        const uint32_t tag = *reinterpret_cast<const uint32_t*>(stg + SB - 4);
+        if (M.a != nullptr) {
+            // the tile's projection rows in LDS as fp16 (the producers' pairs, waited for by all
+            // threads at once; token tile tt in stage tt), then r_pad / 32 more matrix-core steps
+            // by the first K half
+            const int r = args.r, rp = args.r_pad;
+            const u64* Rp = reinterpret_cast<const u64*>(args.R) +
+                            (size_t)(blockIdx.x & (kRReplicas - 1)) * args.n_proj * T * r + (size_t)M.proj * T * r;
+            for (int e = tid; e < 16 * TT * rp; e += 64 * kMidWaves) {
+                const int t = e / rp, col = e - t * rp;
+                _Float16* rl = reinterpret_cast<_Float16*>(sp(t >> 4));
+                rl[(t & 15) * rp + col] = (_Float16)((t < T && col < r) ? load_pair(args, Rp + (size_t)t * r + col, tag) : 0.f);
+            }
+            __syncthreads();
+            if (kh == 0) {
+                const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+                const int kofs = 8 * (lane >> 4);
+                for (int kb = 0; kb < rp / 32; ++kb) {
+                    const int col = 32 * kb + kofs;
+                    h8 av[RR];
+#pragma unroll
+                    for (int rr = 0; rr < RR; ++rr) {
+                        const int row = (rt0 + rr) * 16 + (lane & 15);
+                        av[rr] = (row < M.n_out && col < r) ? load_h8(M.a + (size_t)row * r + col) : zero8;
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < TT; ++tt) {
+                        const _Float16* rl = reinterpret_cast<const _Float16*>(sp(tt));
+                        const h8 bv = *reinterpret_cast<const h8*>(rl + (lane & 15) * rp + col);
+#pragma unroll
+                        for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = mfma16(av[rr], bv, acc[tt][rr]);
+                    }
+                }
+            }
+        }
+    }
+
+    if (kh == 0) {
+        const bool vec = (M.n_out & 3) == 0;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            const int t = 16 * tt + (lane & 15);
+            if (t >= T) continue;
+            _Float16* yrow = M.y + (size_t)t * M.n_out;
+#pragma unroll
+            for (int rr = 0; rr < RR; ++rr) {
+                if (rt0 + rr >= NT) continue;
+                const int row0 = (rt0 + rr) * 16 + 4 * (lane >> 4);
+                const f4 v = acc[tt][rr];
+                if (vec && row0 + 3 < M.n_out) {
+                    const h2 lo = {(_Float16)v[0], (_Float16)v[1]}, hi = {(_Float16)v[2], (_Float16)v[3]};
+                    *reinterpret_cast<u2*>(yrow + row0) = u2{as_u32(lo), as_u32(hi)};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (row0 + e < M.n_out) yrow[row0 + e] = (_Float16)v[e];
+                }
+            }
+        }
+    }
+    if (threadIdx.x == 0) finish(args, arrived, tag0 - 1u);
+}
+
+hipError_t launch_mid(const ForwardArgs& a, hipStream_t stream) {
+    // correcting calls only: the projection comes from the producers of the same launch
+    if (a.fmt != kFmtInt4 || a.m_tiles != 1 || a.T > 16 * a.tile_tt || a.tile_rr != 8) return hipErrorInvalidValue;
+    if (a.r <= 0 || a.n_prod <= 0) return hipErrorInvalidValue;
+    const dim3 grid(a.n_tiles + a.n_prod), block(64 * kMidWaves);
+    if (a.tile_tt == 4)
+        hipLaunchKernelGGL((mid_kernel<4, 2>), grid, block, 0, stream, a);
+    else if (a.tile_tt == 2)
+        hipLaunchKernelGGL((mid_kernel<2, 2>), grid, block, 0, stream, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 template <int F, bool FUSE>
