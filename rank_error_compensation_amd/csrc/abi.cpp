@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -42,10 +43,11 @@ constexpr size_t kDecodeAreaBytes = kDecodeAreaPairs * 8u;
 inline size_t prefill_r_bytes(int64_t T, int32_t r, int32_t n_proj) {
     return round256((size_t)T * (size_t)r_pad_of(r) * 2u * (size_t)n_proj);
 }
-// fp32 split-K partials of the prefill projection, after the fp16 projection
-inline size_t narrow_part_bytes(int64_t T) {
-    return round256((size_t)kNarrowKs * (size_t)T * (size_t)kNarrowMaxRows * 4u);
-}
+// fp32 partial outputs of a K-split call of 17 .. 64 tokens ([ranges][T][rows], ranges x rows at
+// most kNarrowPartRows), after the projection's split-K partials
+constexpr int64_t kNarrowPartRows = 28672;
+static_assert(kNarrowPartRows >= (int64_t)kNarrowKs * kNarrowMaxRows, "narrow decode partials fit");
+inline size_t narrow_part_bytes(int64_t T) { return round256((size_t)kNarrowPartRows * (size_t)T * 4u); }
 
 inline size_t prefill_part_bytes(int64_t T, int32_t r, int32_t n_proj) {
     return round256((size_t)kProjMaxSplit * (size_t)T * (size_t)r_pad_of(r) * 4u * (size_t)n_proj);
@@ -193,18 +195,47 @@ hipError_t launch_projection(const Call& c, void* R, hipStream_t stream) {
 // calls (48 such workgroups) and calls without the correction were faster on the other tiles
 // (QKV T = 64: 22.7 vs 16.3 us; gate/up without the correction: 28.2 vs 26.7 us).
 constexpr int64_t kMidMinBlocks = 160;
+// Fewer row blocks, long rows (at least kNarrowMinGroups input groups) and at least kMidSplitMinT
+// tokens: the same tile over K ranges of at least kMidMinRangeGroups input groups, about
+// kMidSplitWorkgroups workgroups in all (one per CU: the tile takes all of a CU's LDS), each range's
+// fp32 sums in the workspace, added in range order by a second launch; the producers split the
+// projection over the same ranges (partial tiles as tagged pairs after the copies of R).  Measured
+// (r = 64, weights streamed from HBM): down_proj 4096 <- 14336 at T = 64 43.1 -> 32.8 us, 4096 <-
+// 11008 39.1 -> 32.3 us against the K-split decode tile.  Where it lost it is not used: at T = 17
+// and 32 (24.2 -> 27.3 and 26.3 -> 28.7 us: the 64-token tile's cost does not shrink with T while
+// the decode tile's does) and at d = 4096 (LLaMA-3.1-8B QKV T = 64: 17.8 -> 28.8 us, ranges of 8
+// groups being mostly the ring's fill).
+constexpr int64_t kMidSplitWorkgroups = 256;
+constexpr int64_t kMidMinRangeGroups = 8;
+constexpr int64_t kMidSplitMinT = 48;
 
-bool choose_mid_shape(const Call& c, int& tt, int& rb) {
+bool choose_mid_shape(const Call& c, int& tt, int& rb, int& ks, int& gk) {
     if (!c.correct || c.T <= kDecodeWideT || c.T > kDecodeMaxT || c.w[0].format != GLOWQ_FMT_INT4_G128)
         return false;
     tt = c.T <= 32 ? 2 : 4;
     rb = 8;
-    int64_t n = 0;
-    for (int i = 0; i < c.m; ++i) n += ceil_div(ceil_div(c.w[i].n_out, 16), rb);
-    return n >= kMidMinBlocks;
+    int64_t n = 0, rows = 0;
+    for (int i = 0; i < c.m; ++i) {
+        n += ceil_div(ceil_div(c.w[i].n_out, 16), rb);
+        rows += c.w[i].n_out;
+    }
+    const int64_t G = c.d / kGroup;
+    ks = 1;
+    gk = (int)G;
+    if (n >= kMidMinBlocks) return true;
+    if (c.T < kMidSplitMinT || G < kNarrowMinGroups) return false;
+    // the decode area holds the kRReplicas copies of R and the partial tiles of ks - 1 ranges
+    const int64_t copy = (int64_t)c.n_proj * c.T * c.r;
+    const int64_t k_area = (int64_t)kDecodeAreaPairs / copy - kRReplicas + 1;
+    const int64_t k = std::min(std::min(kMidSplitWorkgroups / n, G / kMidMinRangeGroups),
+                               std::min(kNarrowPartRows / rows, k_area));
+    if (k < 2 || n * k < kMidSplitWorkgroups / 2) return false;
+    gk = (int)ceil_div(G, k);
+    ks = (int)ceil_div(G, gk);
+    return ks >= 2;
 }
 
-int run_mid(const Call& c, void* workspace, hipStream_t stream, int tt, int rb) {
+int run_mid(const Call& c, void* workspace, hipStream_t stream, int tt, int rb, int ks, int gk) {
     const int32_t rp = (int32_t)r_pad_of(c.r);
     ForwardArgs f;
     std::memset(&f, 0, sizeof(f));
@@ -222,7 +253,7 @@ int run_mid(const Call& c, void* workspace, hipStream_t stream, int tt, int rb) 
         f.R = static_cast<uint8_t*>(workspace) + kWsHeader;
         f.sync = static_cast<int32_t*>(workspace);
         for (int i = 0; i < c.n_proj; ++i) f.b[i] = static_cast<const _Float16*>(c.b[i]);
-        f.n_prod = (int32_t)(ceil_div(c.T, 16) * c.n_proj * (rp / 16));
+        f.n_prod = (int32_t)(ceil_div(c.T, 16) * c.n_proj * (rp / 16) * ks);
     }
     f.tile_tt = tt;
     f.tile_rr = rb;
@@ -245,14 +276,22 @@ int run_mid(const Call& c, void* workspace, hipStream_t stream, int tt, int rb) 
     }
     f.rows_total = (int32_t)rows;
     f.m_tiles = 1;
-    f.n_tiles = (int32_t)tiles;
+    f.dec_tiles = (int32_t)tiles;
+    f.dec_ks = ks;
+    f.dec_gk = gk;
+    f.n_tiles = (int32_t)(tiles * ks);
+    if (ks > 1)
+        f.ypart = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kWsHeader + kDecodeAreaBytes +
+                                           prefill_r_bytes(c.T, c.r, c.n_proj) +
+                                           prefill_part_bytes(c.T, c.r, c.n_proj));
     return launch_mid(f, stream) == hipSuccess ? GLOWQ_OK : GLOWQ_ERR_HIP;
 }
 
 int run(const Call& c, void* workspace, hipStream_t stream) {
     if (c.T == 0) return GLOWQ_OK;
-    int mid_tt = 0, mid_rb = 0;
-    if (choose_mid_shape(c, mid_tt, mid_rb)) return run_mid(c, workspace, stream, mid_tt, mid_rb);
+    int mid_tt = 0, mid_rb = 0, mid_ks = 1, mid_gk = 1;
+    if (choose_mid_shape(c, mid_tt, mid_rb, mid_ks, mid_gk))
+        return run_mid(c, workspace, stream, mid_tt, mid_rb, mid_ks, mid_gk);
     int64_t row_tiles = 0;
     for (int i = 0; i < c.m; ++i) row_tiles += ceil_div(c.w[i].n_out, 128);
     const bool prefill = c.T > kDecodeMaxT || (c.T > kDecodeWideT && row_tiles >= kPrefillMinRowTiles);

@@ -471,6 +471,13 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const ForwardArgs a)
     y[(size_t)t * n_out + (row - row_begin)] = (_Float16)v;
 }
 
+hipError_t launch_part_reduce(const ForwardArgs& a, hipStream_t stream) {
+    const size_t n = (size_t)a.T * a.rows_total;
+    if (n == 0 || a.ypart == nullptr || a.dec_ks < 2) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)ceil_div((int64_t)n, 256)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int F, int KW, int RT>
 static hipError_t launch_decode_kw(const ForwardArgs& a, hipStream_t stream) {
     constexpr int NTH = 64 * KW;
@@ -526,9 +533,7 @@ static hipError_t launch_decode_fmt(const ForwardArgs& a, hipStream_t stream) {
         if (a.dec_kw != 4 || a.dec_rt != kNarrowRt) return hipErrorInvalidValue;
         hipError_t e = launch_decode_kw<F, 4, kNarrowRt>(a, stream);
         if (e != hipSuccess) return e;
-        const size_t n = (size_t)a.T * a.rows_total;
-        hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)ceil_div((int64_t)n, 256)), dim3(256), 0, stream, a);
-        return hipGetLastError();
+        return launch_part_reduce(a, stream);
     }
     if (a.dec_kw == 8) return launch_decode_kw<F, 8, 1>(a, stream);
     return a.dec_rt == 2 ? launch_decode_kw<F, 4, 2>(a, stream) : launch_decode_kw<F, 4, 1>(a, stream);

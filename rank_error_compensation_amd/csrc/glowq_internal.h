@@ -328,6 +328,9 @@ hipError_t launch_repack_mx(int fmt, const uint8_t* codes, const uint8_t* scales
                             uint8_t* q_dev, uint8_t* sz_dev, int32_t* flag, hipStream_t stream);
 hipError_t launch_proj_prefill(const ProjArgs& p, hipStream_t stream);
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
+// y = the a.dec_ks fp32 partial sums at a.ypart ([dec_ks][T][rows_total]) added in range order,
+// rounded once to fp16 into the modules' outputs (the second launch of a K-split call)
+hipError_t launch_part_reduce(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_quant_mx8(const _Float16* x, int T, int d, uint8_t* xq, uint8_t* xs, hipStream_t stream);
 hipError_t launch_mx8(const ForwardArgs& a, hipStream_t stream);

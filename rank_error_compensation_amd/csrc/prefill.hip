@@ -45,7 +45,13 @@ __device__ void produce_tile_in(const ForwardArgs& a, int p, f4 (*red)[64], uint
     if (tid == 0) epoch0 = load_epoch(a);
     const int T = a.T, d = a.d, r = a.r, rp = a.r_pad;
     const int n_rt = a.n_proj * (rp / 16);  // rank tiles over the stacked projections
-    const int tt = p / n_rt, jt = p - tt * n_rt;
+    // a K-split call splits the projection over the same input ranges: producer p forms the partial
+    // tile of range kr; the producer of the last range adds the other ranges' partials to its own
+    const int pk = a.dec_ks > 1 ? a.dec_ks : 1;
+    const int n_tile = ((T + 15) >> 4) * n_rt;
+    const int kr = p / n_tile;
+    const int q = p - kr * n_tile;
+    const int tt = q / n_rt, jt = q - tt * n_rt;
     const int pi = (jt * 16) / rp, j0 = (jt * 16) - pi * rp;
     const int t0 = 16 * tt;
     const int t = t0 + (lane & 15), j = j0 + (lane & 15);
@@ -56,19 +62,20 @@ __device__ void produce_tile_in(const ForwardArgs& a, int p, f4 (*red)[64], uint
     const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
     f4 acc = {0.f, 0.f, 0.f, 0.f};
     constexpr int S = 8;
-    const int n = d / 32;  // 32-input steps; wave w takes w, w + nw, ...
-    for (int c = wave; c < n; c += S * nw) {
+    const int n = d / 32;  // 32-input steps (four per input group); wave w takes s0 + w, s0 + w + nw, ...
+    const int s0 = pk > 1 ? 4 * kr * a.dec_gk : 0, s1 = pk > 1 ? min(n, 4 * (kr + 1) * a.dec_gk) : n;
+    for (int c = s0 + wave; c < s1; c += S * nw) {
         h8 xa[S], bb[S];
 #pragma unroll
         for (int u = 0; u < S; ++u) {
             const int st = c + u * nw;
-            const int kk = 32 * (st < n ? st : c);  // steps past the end reload the first (unused)
+            const int kk = 32 * (st < s1 ? st : c);  // steps past the range reload the first (unused)
             xa[u] = t_ok ? load_h8(xr + kk) : zero8;
             bb[u] = j_ok ? load_h8(br + kk) : zero8;
         }
 #pragma unroll
         for (int u = 0; u < S; ++u)
-            if (c + u * nw < n) acc = mfma16(xa[u], bb[u], acc);
+            if (c + u * nw < s1) acc = mfma16(xa[u], bb[u], acc);
     }
     if (wave > 0) red[wave - 1][lane] = acc;
     if (tid == 0) {
@@ -80,9 +87,11 @@ __device__ void produce_tile_in(const ForwardArgs& a, int p, f4 (*red)[64], uint
     if (tid == 0) arrived = arrive(a);
     const uint32_t tag = ptag;
     u64* R = reinterpret_cast<u64*>(a.R);
+    // pairs of this call: the kRReplicas copies of R, then the partial tiles of ranges 0 .. pk - 2
+    const size_t copy = (size_t)a.n_proj * T * r;
     if (tag == 1u || tag == 0xFFFFFFFFu) {
         // first and last tag of a wrap: clear every pair of the decode area outside this call's range
-        const size_t from = (size_t)kRReplicas * a.n_proj * T * r;
+        const size_t from = (size_t)(kRReplicas + pk - 1) * copy;
         for (size_t k = from + (size_t)p * blockDim.x + tid; k < kDecodeAreaPairs; k += (size_t)a.n_prod * blockDim.x)
             R[k] = 0ull;
     }
@@ -90,14 +99,22 @@ __device__ void produce_tile_in(const ForwardArgs& a, int p, f4 (*red)[64], uint
         f4 v = acc;
         for (int w = 1; w < nw; ++w) v += red[w - 1][lane];  // fixed order: deterministic
         const int jj = j0 + (lane & 15);
-        const size_t copy = (size_t)a.n_proj * T * r;
+        u64* part = R + (size_t)kRReplicas * copy;  // partial tile of range k at part + k copy
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int ti = t0 + 4 * (lane >> 4) + i;  // output rows: tokens
             if (ti < T && jj < r) {
                 const size_t off = ((size_t)pi * T + ti) * r + jj;
+                if (kr < pk - 1) {
+                    store_pair(part + (size_t)kr * copy + off, v[i], tag);
+                } else {
+                    // ranges in order, this producer's own (the last) added last: deterministic
+                    float s = 0.f;
+                    for (int k = 0; k < pk - 1; ++k) s += load_pair(a, part + (size_t)k * copy + off, tag);
+                    const float tot = pk > 1 ? s + v[i] : v[i];
 #pragma unroll
-                for (int c = 0; c < kRReplicas; ++c) store_pair(R + c * copy + off, v[i], tag);
+                    for (int c = 0; c < kRReplicas; ++c) store_pair(R + c * copy + off, tot, tag);
+                }
             }
         }
     }
@@ -688,13 +705,18 @@ __global__ __launch_bounds__(64 * kMidWaves, 1) void mid_kernel(const ForwardArg
     // thread 0's epoch read (the tag of this launch), before any arrival of this workgroup
     uint32_t epoch0 = 0;
     if (threadIdx.x == 0) epoch0 = load_epoch(args);
-    const int nbl = (int)blockIdx.x - args.n_prod;
+    // row block nbl, K range ks_idx (groups g0 .. g1 - 1; one range unless the call splits K)
+    const int nbl_all = (int)blockIdx.x - args.n_prod;
+    const int ks_idx = nbl_all / args.dec_tiles;
+    const int nbl = nbl_all - ks_idx * args.dec_tiles;
     const ModuleArgs M = args.mod[module_of(args, nbl)];
     const int nb = nbl - M.tile_begin;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rw = wave & 3, kh = wave >> 2;  // row part, K half
     const int T = args.T, d = args.d, G = args.G;
+    const int g0 = ks_idx * args.dec_gk, g1 = min(G, g0 + args.dec_gk);
+    const bool split = args.dec_ks > 1;
     const int NT = M.n_tiles16;
     const NibConsts nc = nib_consts();
     const int rt0 = nb * RB + rw * RR;  // the wave's first row tile
@@ -715,7 +737,7 @@ __global__ __launch_bounds__(64 * kMidWaves, 1) void mid_kernel(const ForwardArg
     const uint32_t zsrc = (uint32_t)(min(rt0 + min(lane >> 4, RR - 1), NT - 1) * 64 + (lane & 15) * 4);
     const char* xbase = reinterpret_cast<const char*>(args.x);
     auto copy = [&](int g, uint8_t* st) {
-        const int gg = min(g, G - 1);  // past the end: a valid group into a stage no one reads
+        const int gg = min(g, g1 - 1);  // past the range: a valid group into a stage no one reads
 #pragma unroll
         for (int i = 0; i < XI; ++i)
             __builtin_amdgcn_global_load_lds((const void*)(xbase + (size_t)gg * kGroup * 2 + xoff[i]),
@@ -739,7 +761,7 @@ __global__ __launch_bounds__(64 * kMidWaves, 1) void mid_kernel(const ForwardArg
 #pragma unroll
         for (int rr = 0; rr < RR; ++rr) acc[tt][rr] = f4{0.f, 0.f, 0.f, 0.f};
 
-    for (int k = 0; k < NST - 1; ++k) copy(k, sp(k));
+    for (int k = 0; k < NST - 1; ++k) copy(g0 + k, sp(k));
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(S::WAIT));
     __builtin_amdgcn_s_barrier();
     // the epoch read was thread 0's first load, so it has landed: use it now (a register load still
@@ -748,7 +770,7 @@ __global__ __launch_bounds__(64 * kMidWaves, 1) void mid_kernel(const ForwardArg
     const uint32_t tag0 = epoch0 + 1u;
 
     int k = 0;  // stage of group g
-    for (int g = 0; g < G; ++g) {
+    for (int g = g0; g < g1; ++g) {
         // the copies of g + NST - 1 go to the stage read in group g - 1 (done: the barrier below)
         copy(g + NST - 1, sp(k == 0 ? NST - 1 : k - 1));
         const uint8_t* cur = sp(k);
@@ -812,7 +834,7 @@ __global__ __launch_bounds__(64 * kMidWaves, 1) void mid_kernel(const ForwardArg
     {
         __syncthreads();
         const uint32_t tag = *reinterpret_cast<const uint32_t*>(stg + SB - 4);
-        if (M.a != nullptr) {
+        if (M.a != nullptr && ks_idx == 0) {
             // the tile's projection rows in LDS as fp16 (the producers' pairs, waited for by all
             // threads at once; token tile tt in stage tt), then r_pad / 32 more matrix-core steps
             // by the first K half
@@ -860,7 +882,12 @@ __global__ __launch_bounds__(64 * kMidWaves, 1) void mid_kernel(const ForwardArg
                 if (rt0 + rr >= NT) continue;
                 const int row0 = (rt0 + rr) * 16 + 4 * (lane >> 4);
                 const f4 v = acc[tt][rr];
-                if (vec && row0 + 3 < M.n_out) {
+                if (split) {  // the range's fp32 partial sums; the reduce launch adds them in order
+                    float* pp = args.ypart + ((size_t)ks_idx * T + t) * args.rows_total + M.row_begin + row0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (row0 + e < M.n_out) pp[e] = v[e];
+                } else if (vec && row0 + 3 < M.n_out) {
                     const h2 lo = {(_Float16)v[0], (_Float16)v[1]}, hi = {(_Float16)v[2], (_Float16)v[3]};
                     *reinterpret_cast<u2*>(yrow + row0) = u2{as_u32(lo), as_u32(hi)};
                 } else {
@@ -878,6 +905,9 @@ hipError_t launch_mid(const ForwardArgs& a, hipStream_t stream) {
     // correcting calls only: the projection comes from the producers of the same launch
     if (a.fmt != kFmtInt4 || a.m_tiles != 1 || a.T > 16 * a.tile_tt || a.tile_rr != 8) return hipErrorInvalidValue;
     if (a.r <= 0 || a.n_prod <= 0) return hipErrorInvalidValue;
+    if (a.dec_ks < 1 || a.dec_gk < 1 || a.n_tiles != a.dec_tiles * a.dec_ks || (a.dec_ks - 1) * a.dec_gk >= a.G ||
+        (int64_t)a.dec_ks * a.dec_gk < a.G || (a.dec_ks > 1 && a.ypart == nullptr))
+        return hipErrorInvalidValue;
     const dim3 grid(a.n_tiles + a.n_prod), block(64 * kMidWaves);
     if (a.tile_tt == 4)
         hipLaunchKernelGGL((mid_kernel<4, 2>), grid, block, 0, stream, a);
@@ -885,7 +915,8 @@ hipError_t launch_mid(const ForwardArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((mid_kernel<2, 2>), grid, block, 0, stream, a);
     else
         return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    return a.dec_ks > 1 ? launch_part_reduce(a, stream) : hipSuccess;
 }
 
 template <int F, bool FUSE>

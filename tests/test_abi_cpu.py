@@ -47,12 +47,12 @@ def test_buffer_sizes():
     # the fixed decode area ((fp32, tag) pairs for T <= 64, r <= 256, 8 projections, 8 copies),
     # then for calls that may take the prefill path (T > 16) the projection in fp16 (r padded to
     # 32) and its fp32 split-K partials (up to 8 splits), and for 17 .. 64 tokens the fp32 partial
-    # outputs of a K-split narrow decode call (4 ranges x T x at most 40 * 128 rows)
+    # outputs of a K-split call (ranges x rows at most 28672, times T)
     area = 64 * 256 * 8 * 8 * 8
     ws = lambda T, r, p: hdr + area + (0 if T <= 16 else
                                        r256(T * ((r + 31) // 32 * 32) * 2 * p) +
                                        r256(8 * T * ((r + 31) // 32 * 32) * 4 * p) +
-                                       (r256(4 * T * 5120 * 4) if T <= 64 else 0))
+                                       (r256(28672 * T * 4) if T <= 64 else 0))
     assert L.glowq_workspace_bytes(1, 64, 1) == hdr + area
     assert L.glowq_workspace_bytes(16, 256, 8) == hdr + area
     assert L.glowq_workspace_bytes(64, 256, 8) == ws(64, 256, 8)
