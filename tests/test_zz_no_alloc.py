@@ -30,12 +30,14 @@ def test_static_rejects_calls_larger_than_the_scratch():
 
 
 # (label, T, d, module rows, r): decode (1, 4, 16 tokens), a narrow K-split call (40 tokens at
-# d = 8192), prefill (200 and 130 tokens); each followed by a smaller call of the same kind
+# d = 8192), the one-token-block tile split over K (64 and 48 tokens, 64 and 65 input groups),
+# prefill (200 and 130 tokens); each followed by a smaller call of the same kind
 CASES = [
     ("prefill", [(200, 512, [96, 64, 40], 32), (130, 384, [48, 32], 16)]),
     ("decode16", [(16, 1024, [256, 128, 128], 64), (4, 512, [64, 32, 32], 32)]),
     ("decode1", [(1, 4096, [512, 256, 256], 64), (1, 256, [40, 24], 16)]),
     ("narrow_split", [(40, 8192, [256], 64), (17, 8192, [128], 32)]),
+    ("mid_split", [(64, 8192, [2048], 64), (48, 8320, [2048], 32)]),
     ("solo", [(4, 2048, [300], 64), (1, 1024, [100], 8)]),
 ]
 
