@@ -5,8 +5,8 @@ layerwise, 32- and 64-token tiles, ragged row counts, a single input group, rank
 LLaMA-3.1-8B gate/up shape.  Calls with fewer than 160 workgroups of 128 rows, at least 48 tokens
 and at least 64 input groups split K over ranges of workgroups, the projection's producers over the
 same ranges (the ranges' fp32 sums added by a second launch): even and uneven ranges, ragged rows
-and tokens, rank 256, layerwise projections and the LLaMA-3.1-8B down_proj.  The same shapes without the correction (other tiles)
-are checked beside them.
+and tokens, ranks 24 and 256, layerwise projections and the LLaMA-3.1-8B down_proj.  The same
+shapes without the correction (other tiles) are checked beside them.
 
 Bar: relative Frobenius error <= 1e-3 and max-abs error <= 1e-2 max|y| per module."""
 import pytest
@@ -32,6 +32,7 @@ SPLIT_CASES = [
     (57, 9600, [4096], 64),              # solo, 75 groups in ranges 6 x 11 + 9; 57 tokens
     (64, 8192, [4096], 256),             # rank 256, ranges 6 x 10 + 4
     (50, 8192, [3000, 1500, 1500], 64),  # three modules (layerwise: three projections), four ranges
+    (56, 8192, [3000], 24),              # rank 24: a half-filled rank tile in every producer range
 ]
 
 
